@@ -1,0 +1,134 @@
+"""Seeded synthetic rollouts for the credit-assignment workloads.
+
+This module only draws random inputs; it holds none of the method's
+arithmetic.  The test suite and the benchmark feed the same draws to the HIP
+library and to the CPU oracle.
+
+Draws use ``numpy.random.Generator(PCG64(seed))`` in a fixed order:
+rewards, values, q_taken, exp_q_next, log_rhos, terminated, truncated,
+trunc_values.  An array that a workload does not use is not drawn, so the
+order of the draws that remain is unchanged.  Bernoulli flags are ``u < p``
+stored as ``uint8``.  bf16 inputs are rounded from the fp32 draws by torch
+(round-to-nearest-even) on the CPU, so both sides see identical bits.
+
+Workloads follow the synthetic rollout shapes the rl-triton explainer pages
+discuss (``[num_envs, seq_len]`` tensors, Technical summary: Problem; results
+quoted at 4096 envs x 128 steps).  The five named workloads below are the
+configurations this library is measured on.
+"""
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+import torch
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    algo: str                 # returns | gae | td_lambda | vtrace | retrace | vtrace+retrace
+    num_envs: int
+    T: int
+    dtype: str                # "f32" | "bf16": dtype of every floating-point input
+    seed: int
+    gamma: float
+    lam: float = 1.0
+    p_term: float = 0.0
+    p_trunc: Optional[float] = None   # None: no truncation array at all
+    reward_dist: str = "normal"       # "normal" N(0,1) | "uniform" U(-1,1)
+    log_rho_std: float = 0.5
+    clips: Dict[str, float] = field(default_factory=dict)
+
+
+WORKLOADS = {
+    "returns_4x128": Workload("returns_4x128", "returns", 4, 128, "f32", 101,
+                              gamma=0.99, p_term=0.01),
+    "gae_4096x128": Workload("gae_4096x128", "gae", 4096, 128, "f32", 102,
+                             gamma=0.99, lam=0.95, p_term=0.005, p_trunc=0.002),
+    "td_lambda_16384x256": Workload("td_lambda_16384x256", "td_lambda", 16384, 256, "f32",
+                                    103, gamma=0.995, lam=0.9, p_term=0.004,
+                                    reward_dist="uniform"),
+    "offpolicy_2048x1024": Workload("offpolicy_2048x1024", "vtrace+retrace", 2048, 1024,
+                                    "f32", 104, gamma=0.99, lam=0.95, p_term=0.002,
+                                    clips={"rho_bar": 1.0, "c_bar": 1.0, "pg_rho_bar": 1.0}),
+    "gae_bf16_256x16384": Workload("gae_bf16_256x16384", "gae", 256, 16384, "bf16", 105,
+                                   gamma=0.999, lam=0.97, p_term=0.0005, p_trunc=0.0002),
+}
+
+_NEEDS = {
+    "returns": ("rewards",),
+    "gae": ("rewards", "values"),
+    "td_lambda": ("rewards", "values"),
+    "vtrace": ("rewards", "values", "log_rhos"),
+    "retrace": ("rewards", "q_taken", "exp_q_next", "log_rhos"),
+    "vtrace+retrace": ("rewards", "values", "q_taken", "exp_q_next", "log_rhos"),
+}
+
+
+def fp32_param(x: float) -> float:
+    """The float32 value of a scalar parameter, widened back to a Python float.
+
+    The library takes gamma, lambda and the clips as float32; the oracle is fed
+    the same rounded values.
+    """
+    return float(np.float32(x))
+
+
+def make_rollout(algo: str, num_envs: int, T: int, *, seed: int, dtype: str = "f32",
+                 p_term: float = 0.0, p_trunc: Optional[float] = None,
+                 reward_dist: str = "normal", log_rho_std: float = 0.5,
+                 dense_trunc_values: bool = True) -> Dict[str, torch.Tensor]:
+    """Draw one rollout batch as CPU tensors.
+
+    Returns a dict with (as the algorithm needs) ``rewards [N,T]``,
+    ``values [N,T+1]``, ``q_taken [N,T]``, ``exp_q_next [N,T]``,
+    ``log_rhos [N,T]``, ``terminated [N,T] uint8``, ``truncated [N,T] uint8``
+    (only if ``p_trunc`` is not None) and ``trunc_values [N,T]`` (with
+    truncations, drawn densely: entries that are not truncation bootstraps are
+    never read by a correct implementation, so they hold live random values).
+    """
+    if algo not in _NEEDS:
+        raise ValueError("unknown algorithm %r" % algo)
+    if dtype not in ("f32", "bf16"):
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    g = np.random.Generator(np.random.PCG64(seed))
+    N = num_envs
+    need = _NEEDS[algo]
+    out: Dict[str, np.ndarray] = {}
+    if reward_dist == "normal":
+        out["rewards"] = g.standard_normal((N, T), dtype=np.float32)
+    elif reward_dist == "uniform":
+        out["rewards"] = g.uniform(-1.0, 1.0, (N, T)).astype(np.float32)
+    else:
+        raise ValueError("reward_dist must be 'normal' or 'uniform'")
+    if "values" in need:
+        out["values"] = g.standard_normal((N, T + 1), dtype=np.float32)
+    if "q_taken" in need:
+        out["q_taken"] = g.standard_normal((N, T), dtype=np.float32)
+        out["exp_q_next"] = g.standard_normal((N, T), dtype=np.float32)
+    if "log_rhos" in need:
+        out["log_rhos"] = (g.standard_normal((N, T), dtype=np.float32)
+                           * np.float32(log_rho_std)).astype(np.float32)
+    out["terminated"] = (g.random((N, T)) < p_term).astype(np.uint8)
+    if p_trunc is not None:
+        out["truncated"] = (g.random((N, T)) < p_trunc).astype(np.uint8)
+        if dense_trunc_values:
+            out["trunc_values"] = g.standard_normal((N, T), dtype=np.float32)
+        else:
+            out["trunc_values"] = np.zeros((N, T), np.float32)
+    res: Dict[str, torch.Tensor] = {}
+    for k, a in out.items():
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype == "bf16" and a.dtype == np.float32:
+            t = t.to(torch.bfloat16)
+        res[k] = t
+    return res
+
+
+def make_workload(w: Workload, num_envs: Optional[int] = None, T: Optional[int] = None,
+                  seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
+    """Draw the inputs of a named workload (optionally at another size or seed)."""
+    return make_rollout(w.algo, num_envs or w.num_envs, T or w.T,
+                        seed=w.seed if seed is None else seed, dtype=w.dtype,
+                        p_term=w.p_term, p_trunc=w.p_trunc, reward_dist=w.reward_dist,
+                        log_rho_std=w.log_rho_std)

@@ -1,0 +1,171 @@
+"""Forward-view (sum-form) definitions, written independently of the oracle.
+
+The oracle computes each algorithm with a backward loop.  The functions here
+compute the same quantities from the published *forward-view* sums, row by
+row and step by step, in O(T^2) float64 (or exact ``Fraction``) arithmetic.
+They share no code with ``oracle/`` and none with the HIP library.  They are
+only fast enough for tiny inputs.
+
+Notation (per row, t = 0..T-1): ``term_t``, ``trunc_t`` flags;
+``done_t = term_t or trunc_t``; a truncation that is also a termination counts
+as a termination; ``k_end(t)`` = first ``k >= t`` with ``done_k``, else
+``T-1``; the successor value of step ``k`` is 0 after a termination, the
+supplied ``trunc_values[k]`` after a truncation, ``V[k+1]`` otherwise
+(``V[T]`` closes the window).
+"""
+import math
+
+
+def _row(x, n):
+    return None if x is None else x[n]
+
+
+def _flags(term, trunc, n, T):
+    te = [bool(term[n][t]) if term is not None else False for t in range(T)]
+    tr = [bool(trunc[n][t]) if trunc is not None else False for t in range(T)]
+    return te, tr
+
+
+def _k_end(te, tr, t, T):
+    for k in range(t, T):
+        if te[k] or tr[k]:
+            return k, True
+    return T - 1, False
+
+
+def _succ(v, tv, te, tr, k, T):
+    """Successor value of step k (see module doc)."""
+    if te[k]:
+        return 0
+    if tr[k]:
+        return tv[k]
+    return v[k + 1]
+
+
+def returns(r, term, trunc, tv, bootstrap, gamma):
+    """G_t = sum_{k=t}^{k_end} gamma^{k-t} r_k + gamma^{k_end-t+1} * tail, where
+    tail = 0 (termination), tv (truncation) or the window bootstrap B."""
+    N, T = len(r), len(r[0]) if len(r) else 0
+    out = []
+    for n in range(N):
+        te, tr = _flags(term, trunc, n, T)
+        B = bootstrap[n] if bootstrap is not None else 0
+        row = []
+        for t in range(T):
+            k_end, cut = _k_end(te, tr, t, T)
+            s = sum(gamma ** (k - t) * r[n][k] for k in range(t, k_end + 1))
+            if cut:
+                tail = 0 if te[k_end] else tv[n][k_end]
+            else:
+                tail = B
+            row.append(s + gamma ** (k_end - t + 1) * tail)
+        out.append(row)
+    return out
+
+
+def _deltas(r, v, tv, te, tr, T, gamma):
+    return [r[k] + gamma * _succ(v, tv, te, tr, k, T) - v[k] for k in range(T)]
+
+
+def gae(r, v, term, trunc, tv, gamma, lam):
+    """A_t = sum_{k=t}^{k_end} (gamma*lam)^{k-t} delta_k   (Schulman et al. 2016)."""
+    N, T = len(r), len(r[0]) if len(r) else 0
+    adv = []
+    for n in range(N):
+        te, tr = _flags(term, trunc, n, T)
+        d = _deltas(r[n], v[n], _row(tv, n), te, tr, T, gamma)
+        row = []
+        for t in range(T):
+            k_end, _ = _k_end(te, tr, t, T)
+            row.append(sum((gamma * lam) ** (k - t) * d[k] for k in range(t, k_end + 1)))
+        adv.append(row)
+    return adv
+
+
+def td_lambda(r, v, term, trunc, tv, gamma, lam):
+    """Forward-view lambda-return (Sutton & Barto, sec. 12.1), truncated at the
+    episode end or the window end:
+        G^lam_t = (1-lam) sum_{n=1}^{h-1} lam^{n-1} G^(n)_t + lam^{h-1} G^(h)_t,
+    h = k_end - t + 1, G^(n)_t = sum_{i<n} gamma^i r_{t+i} + gamma^n W_n,
+    W_n = V_{t+n} for n < h and W_h = successor value of step k_end."""
+    N, T = len(r), len(r[0]) if len(r) else 0
+    out = []
+    for n in range(N):
+        te, tr = _flags(term, trunc, n, T)
+        rr, vv = r[n], v[n]
+        row = []
+        for t in range(T):
+            k_end, _ = _k_end(te, tr, t, T)
+            h = k_end - t + 1
+
+            def G(m):
+                s = sum(gamma ** i * rr[t + i] for i in range(m))
+                W = vv[t + m] if m < h else _succ(vv, _row(tv, n), te, tr, k_end, T)
+                return s + gamma ** m * W
+
+            acc = (1 - lam) * sum(lam ** (m - 1) * G(m) for m in range(1, h))
+            row.append(acc + lam ** (h - 1) * G(h))
+        out.append(row)
+    return out
+
+
+def vtrace(r, v, log_rho, term, trunc, tv, gamma, lam, rho_bar, c_bar, pg_rho_bar):
+    """IMPALA V-trace (Espeholt et al. 2018, eq. 1) with c_i = lam*min(c_bar, ratio_i):
+        vs_t = V_t + sum_{k=t}^{k_end} gamma^{k-t} (prod_{i=t}^{k-1} c_i) rho_k delta_k,
+    pg_t = min(pg_rho_bar, ratio_t) (r_t + gamma*nvs_t - V_t), nvs_t = 0 after a
+    termination, tv_t after a truncation, vs_{t+1} otherwise (V_T at t = T-1)."""
+    N, T = len(r), len(r[0]) if len(r) else 0
+    vs_all, pg_all = [], []
+    for n in range(N):
+        te, tr = _flags(term, trunc, n, T)
+        ratio = [math.exp(x) for x in log_rho[n]]
+        rho = [min(rho_bar, x) for x in ratio]
+        c = [lam * min(c_bar, x) for x in ratio]
+        d = _deltas(r[n], v[n], _row(tv, n), te, tr, T, gamma)
+        vs = []
+        for t in range(T):
+            k_end, _ = _k_end(te, tr, t, T)
+            s = 0.0
+            for k in range(t, k_end + 1):
+                p = 1.0
+                for i in range(t, k):
+                    p *= c[i]
+                s += gamma ** (k - t) * p * rho[k] * d[k]
+            vs.append(v[n][t] + s)
+        pg = []
+        for t in range(T):
+            if te[t]:
+                nvs = 0.0
+            elif tr[t]:
+                nvs = tv[n][t]
+            else:
+                nvs = vs[t + 1] if t + 1 < T else v[n][T]
+            pg.append(min(pg_rho_bar, ratio[t]) * (r[n][t] + gamma * nvs - v[n][t]))
+        vs_all.append(vs)
+        pg_all.append(pg)
+    return vs_all, pg_all
+
+
+def retrace(r, q, eq, log_rho, term, trunc, gamma, lam, c_bar):
+    """Retrace(lambda) (Munos et al. 2016):
+        Qret_t = Q_t + sum_{k=t}^{k_end} gamma^{k-t} (prod_{i=t+1}^{k} c_i)
+                          (r_k + gamma*(1-term_k)*EQ_k - Q_k),
+    c_i = lam * min(c_bar, ratio_i); EQ_k = E_pi Q(s_{k+1}, .)."""
+    N, T = len(r), len(r[0]) if len(r) else 0
+    out = []
+    for n in range(N):
+        te, tr = _flags(term, trunc, n, T)
+        c = [lam * min(c_bar, math.exp(x)) for x in log_rho[n]]
+        err = [r[n][k] + (0.0 if te[k] else gamma * eq[n][k]) - q[n][k] for k in range(T)]
+        row = []
+        for t in range(T):
+            k_end, _ = _k_end(te, tr, t, T)
+            s = 0.0
+            for k in range(t, k_end + 1):
+                p = 1.0
+                for i in range(t + 1, k + 1):
+                    p *= c[i]
+                s += gamma ** (k - t) * p * err[k]
+            row.append(q[n][t] + s)
+        out.append(row)
+    return out

@@ -1,0 +1,110 @@
+"""The oracle's pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of ``oracle/oracle.c`` (on the CPU,
+in a temporary directory), builds that copy, and runs the pin tests of
+``test_oracle_pins.py`` against it.  At least one pin must fail for every
+mutant; the unmodified copy must pass them all.
+"""
+import importlib.util
+import os
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+import test_oracle_pins as pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# (name, original text, mutated text): each a plausible slip.
+MUTANTS = [
+    ("gae_no_done_mask", "a = done ? delta : delta + gamma * lam * a;",
+     "a = delta + gamma * lam * a;"),
+    ("gae_sign_of_value", "- vt;\n            int done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);\n            a =",
+     "+ vt;\n            int done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);\n            a ="),
+    ("truncation_wins", "    if (flag_at(term, n, t, T))\n        return 0.0;\n    if (flag_at(trunc, n, t, T))\n        return AT(tv, n, t, T);",
+     "    if (flag_at(trunc, n, t, T))\n        return AT(tv, n, t, T);\n    if (flag_at(term, n, t, T))\n        return 0.0;"),
+    ("truncation_ignores_bootstrap", "        return AT(tv, n, t, T);\n    return AT(v, n, t + 1, T + 1);",
+     "        return AT(v, n, t + 1, T + 1);\n    return AT(v, n, t + 1, T + 1);"),
+    ("returns_bootstrap_dropped", "double g = bootstrap != NULL ? bootstrap[n] : 0.0;",
+     "double g = 0.0;"),
+    ("td_lambda_mix_swapped", "((1.0 - lam) * AT(v, n, t + 1, T + 1) + lam * g)",
+     "(lam * AT(v, n, t + 1, T + 1) + (1.0 - lam) * g)"),
+    ("vtrace_trace_index_shifted", "double c = lam * fmin(c_bar, ratio);",
+     "double c = lam * fmin(c_bar, t + 1 < T ? exp(AT(log_rho, n, t + 1, T)) : ratio);"),
+    ("vtrace_lambda_on_rho", "double rho = fmin(rho_bar, ratio);",
+     "double rho = lam * fmin(rho_bar, ratio);"),
+    ("vtrace_pg_uses_values", "double nvs = term_t ? 0.0 : (done ? AT(tv, n, t, T) : v_next);",
+     "double nvs = term_t ? 0.0 : (done ? AT(tv, n, t, T) : AT(v, n, t + 1, T + 1));"),
+    ("retrace_trace_index_unshifted",
+     "double c_next = lam * fmin(c_bar, exp(AT(log_rho, n, t + 1, T)));",
+     "double c_next = lam * fmin(c_bar, exp(AT(log_rho, n, t, T)));"),
+    ("retrace_keeps_eq_after_termination",
+     "(term_t ? 0.0 : gamma * AT(eq, n, t, T))", "(gamma * AT(eq, n, t, T))"),
+    ("retrace_trace_not_cut_at_truncation", "if (!done && t < T - 1) {",
+     "if (!term_t && t < T - 1) {"),
+]
+
+PIN_CASES = [
+    (pins.test_returns_constant_reward_closed_form, dict(gamma=0.99)),
+    (pins.test_returns_one_hot_and_bootstrap_closed_form, {}),
+    (pins.test_returns_no_dones_matches_discounted_sum, {}),
+    (pins.test_termination_zeroes_successor_truncation_bootstraps, {}),
+    (pins.test_gae_special_cases, {}),
+    (pins.test_td_lambda_equals_gae_plus_values, {}),
+    (pins.test_vtrace_reductions, {}),
+    (pins.test_retrace_reductions, {}),
+    (pins.test_oracle_matches_forward_views, dict(seed=21, T=12)),
+    (pins.test_trace_index_vtrace_from_t_retrace_from_t_plus_1, {}),
+    (pins.test_exhaustive_boundaries_against_forward_views, dict(T=3)),
+    (pins.test_no_leak_across_episode_boundary, dict(kind="term")),
+    (pins.test_no_leak_across_episode_boundary, dict(kind="trunc")),
+    (pins.test_window_bootstrap_counted_once_and_ignored_after_done, {}),
+    (pins.test_affine_operator_scan_equals_gae_recurrence_exactly, {}),
+]
+
+
+def _load_variant(tmp_path, name, src_text):
+    pkg = tmp_path / ("oracle_" + name)
+    shutil.copytree(os.path.join(ROOT, "oracle"), pkg,
+                    ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    (pkg / "oracle.c").write_text(src_text)
+    subprocess.run([sys.executable, str(pkg / "build.py")], check=True,
+                   stdout=subprocess.DEVNULL)
+    spec = importlib.util.spec_from_file_location("oracle_" + name, pkg / "__init__.py",
+                                                  submodule_search_locations=[str(pkg)])
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[spec.name] = mod
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def _failing_pins(monkeypatch, mod):
+    monkeypatch.setattr(pins, "oracle", mod)
+    failed = []
+    for fn, kw in PIN_CASES:
+        try:
+            fn(**kw)
+        except (AssertionError, ValueError):
+            failed.append(fn.__name__)
+    return failed
+
+
+def _source():
+    with open(os.path.join(ROOT, "oracle", "oracle.c")) as f:
+        return f.read()
+
+
+def test_unmodified_copy_passes_every_pin(tmp_path, monkeypatch):
+    mod = _load_variant(tmp_path, "clean", _source())
+    assert _failing_pins(monkeypatch, mod) == []
+
+
+@pytest.mark.parametrize("name,orig,mut", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, monkeypatch, name, orig, mut):
+    src = _source()
+    assert src.count(orig) == 1, "mutation site for %s not found exactly once" % name
+    mod = _load_variant(tmp_path, name, src.replace(orig, mut))
+    failed = _failing_pins(monkeypatch, mod)
+    assert failed, "no pin caught mutant %s" % name

@@ -1,0 +1,412 @@
+"""Pins of the fp64 oracle against facts that do not come from the oracle.
+
+Each test checks the oracle (``oracle/``) against one of:
+  * a closed form of the recurrence (constant-gamma discounted sums),
+  * a special case that reduces one algorithm to another,
+  * the forward-view sum definitions in ``bruteforce.py`` (independent code),
+  * exact rational arithmetic on the pages' affine operator,
+  * the boundary invariants the rl-triton explainer states (Technical
+    summary, Method 3): no signal crosses an episode boundary, termination
+    and truncation differ, and the window bootstrap is counted once.
+Inputs are seeded and synthetic.
+"""
+import itertools
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import bruteforce as bf
+import oracle
+
+RTOL_BF = 1e-12   # oracle vs brute force: both fp64, different summation order
+
+
+def rel_err(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    scale = max(np.max(np.abs(b)) if b.size else 0.0, 1e-300)
+    return float(np.max(np.abs(a - b)) / scale) if a.size else 0.0
+
+
+def rand_inputs(seed, N, T, p_term=0.15, p_trunc=0.1, ratio_std=0.7):
+    g = np.random.Generator(np.random.PCG64(seed))
+    d = dict(
+        r=g.standard_normal((N, T)),
+        v=g.standard_normal((N, T + 1)),
+        q=g.standard_normal((N, T)),
+        eq=g.standard_normal((N, T)),
+        lr=g.standard_normal((N, T)) * ratio_std,
+        term=(g.random((N, T)) < p_term).astype(np.uint8),
+        trunc=(g.random((N, T)) < p_trunc).astype(np.uint8),
+        tv=g.standard_normal((N, T)),
+        B=g.standard_normal(N),
+    )
+    return d
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("gamma", [0.0, 0.5, 0.99, 1.0])
+def test_returns_constant_reward_closed_form(gamma):
+    T = 37
+    r = np.ones((1, T))
+    G = oracle.returns(r, gamma=gamma)[0]
+    for t in range(T):
+        n = T - t
+        expect = n if gamma == 1.0 else (1 - gamma ** n) / (1 - gamma)
+        assert abs(G[t] - expect) <= 1e-12 * max(1.0, expect)
+
+
+def test_returns_one_hot_and_bootstrap_closed_form():
+    T, gamma, j = 20, 0.9, 13
+    r = np.zeros((1, T))
+    r[0, j] = 1.0
+    G = oracle.returns(r, bootstrap=np.array([0.0]), gamma=gamma)[0]
+    for t in range(T):
+        assert G[t] == pytest.approx(gamma ** (j - t) if t <= j else 0.0, abs=1e-15)
+    # The bootstrap B enters once, discounted by gamma^{T-t}.
+    G0 = oracle.returns(np.zeros((1, T)), bootstrap=np.array([2.0]), gamma=gamma)[0]
+    for t in range(T):
+        assert G0[t] == pytest.approx(2.0 * gamma ** (T - t), rel=1e-14)
+
+
+def test_returns_no_dones_matches_discounted_sum():
+    g = np.random.Generator(np.random.PCG64(7))
+    N, T, gamma = 5, 64, 0.97
+    r = g.standard_normal((N, T))
+    B = g.standard_normal(N)
+    G = oracle.returns(r, bootstrap=B, gamma=gamma)
+    for n in range(N):
+        for t in range(T):
+            s = math.fsum(gamma ** k * r[n, t + k] for k in range(T - t)) + gamma ** (T - t) * B[n]
+            assert abs(G[n, t] - s) <= 1e-12 * max(1.0, abs(s))
+
+
+def test_termination_zeroes_successor_truncation_bootstraps():
+    # A one-step episode after each flag: G_t = r_t (term), r_t + gamma*tv_t (trunc),
+    # and termination wins when both are set.
+    T, gamma = 4, 0.5
+    r = np.array([[1.0, 2.0, 3.0, 4.0]])
+    tv = np.array([[10.0, 20.0, 30.0, 40.0]])
+    term = np.array([[1, 0, 1, 0]], np.uint8)
+    trunc = np.array([[0, 1, 1, 0]], np.uint8)
+    G = oracle.returns(r, term, trunc, tv, np.array([100.0]), gamma=gamma)[0]
+    assert G[3] == 4.0 + 0.5 * 100.0
+    assert G[2] == 3.0                       # term and trunc: termination wins
+    assert G[1] == 2.0 + 0.5 * 20.0          # truncation: bootstrap tv_1
+    assert G[0] == 1.0                       # termination: successor value 0
+
+
+# ------------------------------------------------------- special-case reductions
+
+def test_gae_special_cases():
+    d = rand_inputs(11, 6, 40)
+    kw = dict(terminated=d["term"], truncated=d["trunc"], trunc_values=d["tv"])
+    gamma = 0.93
+    # lam = 1: GAE advantage = discounted return (bootstrap V_T, same masks) - V_t.
+    adv1, tgt1 = oracle.gae(d["r"], d["v"], gamma=gamma, lam=1.0, **kw)
+    G = oracle.returns(d["r"], d["term"], d["trunc"], d["tv"], d["v"][:, -1], gamma=gamma)
+    assert rel_err(adv1, G - d["v"][:, :-1]) < 1e-12
+    assert rel_err(tgt1, G) < 1e-12
+    # lam = 0: advantage = one-step TD error.
+    adv0, _ = oracle.gae(d["r"], d["v"], gamma=gamma, lam=0.0, **kw)
+    nv = np.where(d["term"] != 0, 0.0, np.where(d["trunc"] != 0, d["tv"], d["v"][:, 1:]))
+    assert rel_err(adv0, d["r"] + gamma * nv - d["v"][:, :-1]) < 1e-15
+    # gamma = 0: advantage = r - V.
+    advg, _ = oracle.gae(d["r"], d["v"], gamma=0.0, lam=0.7, **kw)
+    assert rel_err(advg, d["r"] - d["v"][:, :-1]) < 1e-15
+
+
+def test_td_lambda_equals_gae_plus_values():
+    # The oracle's TD(lambda) is a separate recursion (mixing V_{t+1} and G_{t+1});
+    # it must agree with GAE + V.
+    d = rand_inputs(12, 8, 50)
+    kw = dict(terminated=d["term"], truncated=d["trunc"], trunc_values=d["tv"])
+    for gamma, lam in [(0.99, 0.95), (0.5, 0.3), (1.0, 1.0), (0.9, 0.0)]:
+        adv, tgt = oracle.gae(d["r"], d["v"], gamma=gamma, lam=lam, **kw)
+        ret = oracle.td_lambda(d["r"], d["v"], gamma=gamma, lam=lam, **kw)
+        assert rel_err(ret, adv + d["v"][:, :-1]) < 1e-13
+        assert rel_err(ret, tgt) < 1e-13
+
+
+def test_vtrace_reductions():
+    d = rand_inputs(13, 6, 45)
+    kw = dict(terminated=d["term"], truncated=d["trunc"], trunc_values=d["tv"])
+    gamma, lam = 0.97, 0.8
+    # On-policy (log ratio 0, clips 1): vs = TD(lambda) returns; pg = one-step TD target - V
+    # with the next vs.
+    vs, pg = oracle.vtrace(d["r"], d["v"], np.zeros_like(d["r"]), gamma=gamma, lam=lam, **kw)
+    ret = oracle.td_lambda(d["r"], d["v"], gamma=gamma, lam=lam, **kw)
+    assert rel_err(vs, ret) < 1e-13
+    # lam = 0: vs_t = V_t + rho_t * delta_t.
+    vs0, _ = oracle.vtrace(d["r"], d["v"], d["lr"], gamma=gamma, lam=0.0, **kw)
+    rho = np.minimum(1.0, np.exp(d["lr"]))
+    nv = np.where(d["term"] != 0, 0.0, np.where(d["trunc"] != 0, d["tv"], d["v"][:, 1:]))
+    assert rel_err(vs0, d["v"][:, :-1] + rho * (d["r"] + gamma * nv - d["v"][:, :-1])) < 1e-14
+    # Clipping: any log ratio >= 0 behaves exactly like log ratio 0 with clips 1.
+    big = np.abs(d["lr"]) + 3.0
+    vsb, pgb = oracle.vtrace(d["r"], d["v"], big, gamma=gamma, lam=lam, **kw)
+    assert np.array_equal(vsb, vs) and np.array_equal(pgb, pg)
+
+
+def test_retrace_reductions():
+    d = rand_inputs(14, 6, 45)
+    gamma, lam = 0.95, 0.9
+    # lam = 0: Qret = r + gamma*(1-term)*EQ.
+    q0 = oracle.retrace(d["r"], d["q"], d["eq"], d["lr"], d["term"], d["trunc"],
+                        gamma=gamma, lam=0.0)
+    assert rel_err(q0, d["r"] + gamma * (1 - d["term"]) * d["eq"]) < 1e-15
+    # On-policy with EQ_t = Q_{t+1} (EQ_{T-1} = V_T, EQ_t = tv_t at truncations):
+    # Retrace = TD(lambda) on the values [Q_0..Q_{T-1}, V_T].
+    vals = np.concatenate([d["q"], d["v"][:, -1:]], axis=1)
+    eq = vals[:, 1:].copy()
+    eq = np.where(d["trunc"] != 0, d["tv"], eq)
+    qr = oracle.retrace(d["r"], d["q"], eq, np.zeros_like(d["r"]), d["term"], d["trunc"],
+                        gamma=gamma, lam=lam)
+    ret = oracle.td_lambda(d["r"], vals, d["term"], d["trunc"], d["tv"], gamma=gamma, lam=lam)
+    assert rel_err(qr, ret) < 1e-13
+
+
+# ------------------------------------------------- forward-view brute force
+
+@pytest.mark.parametrize("seed", [21, 22, 23])
+@pytest.mark.parametrize("T", [1, 2, 5, 12])
+def test_oracle_matches_forward_views(seed, T):
+    N = 7
+    d = rand_inputs(seed, N, T)
+    gamma, lam = 0.9, 0.8
+    tl = lambda a: a.tolist()
+    term, trunc, tv = tl(d["term"]), tl(d["trunc"]), tl(d["tv"])
+
+    G = oracle.returns(d["r"], d["term"], d["trunc"], d["tv"], d["B"], gamma=gamma)
+    assert rel_err(G, bf.returns(tl(d["r"]), term, trunc, tv, tl(d["B"]), gamma)) < RTOL_BF
+
+    adv, tgt = oracle.gae(d["r"], d["v"], d["term"], d["trunc"], d["tv"], gamma=gamma, lam=lam)
+    adv_bf = np.array(bf.gae(tl(d["r"]), tl(d["v"]), term, trunc, tv, gamma, lam))
+    assert rel_err(adv, adv_bf) < RTOL_BF
+    assert rel_err(tgt, adv_bf + d["v"][:, :-1]) < RTOL_BF
+
+    ret = oracle.td_lambda(d["r"], d["v"], d["term"], d["trunc"], d["tv"], gamma=gamma, lam=lam)
+    assert rel_err(ret, bf.td_lambda(tl(d["r"]), tl(d["v"]), term, trunc, tv, gamma, lam)) < RTOL_BF
+
+    clips = dict(rho_bar=1.1, c_bar=0.9, pg_rho_bar=1.3)
+    vs, pg = oracle.vtrace(d["r"], d["v"], d["lr"], d["term"], d["trunc"], d["tv"],
+                           gamma=gamma, lam=lam, **clips)
+    vs_bf, pg_bf = bf.vtrace(tl(d["r"]), tl(d["v"]), tl(d["lr"]), term, trunc, tv, gamma, lam,
+                             clips["rho_bar"], clips["c_bar"], clips["pg_rho_bar"])
+    assert rel_err(vs, vs_bf) < RTOL_BF
+    assert rel_err(pg, pg_bf) < RTOL_BF
+
+    qr = oracle.retrace(d["r"], d["q"], d["eq"], d["lr"], d["term"], d["trunc"],
+                        gamma=gamma, lam=lam, c_bar=0.9)
+    qr_bf = bf.retrace(tl(d["r"]), tl(d["q"]), tl(d["eq"]), tl(d["lr"]), term, trunc,
+                       gamma, lam, 0.9)
+    assert rel_err(qr, qr_bf) < RTOL_BF
+
+
+def test_trace_index_vtrace_from_t_retrace_from_t_plus_1():
+    # With traces that vary per step, V-trace's product starts at c_t and
+    # Retrace's at c_{t+1}; the brute force fixes which, the oracle must agree.
+    T, gamma, lam = 3, 1.0, 1.0
+    r = np.zeros((1, T))
+    v = np.zeros((1, T + 1))
+    v[0, T] = 1.0                      # only the window bootstrap is nonzero
+    lr = np.log(np.array([[0.5, 0.25, 0.125]]))
+    vs, _ = oracle.vtrace(r, v, lr, gamma=gamma, lam=lam, rho_bar=1.0, c_bar=1.0)
+    # delta_2 = rho_2 * V_3 = 0.125; vs_0 = c_0 c_1 delta_2 = 0.5 * 0.25 * 0.125
+    assert vs[0, 0] == pytest.approx(0.5 * 0.25 * 0.125, rel=1e-15)
+    q = np.zeros((1, T))
+    eq = np.array([[0.0, 0.0, 1.0]])
+    qr = oracle.retrace(r, q, eq, lr, gamma=gamma, lam=lam, c_bar=1.0)
+    # delta_2 = EQ_2 = 1; Qret_0 = c_1 c_2 * 1 = 0.25 * 0.125
+    assert qr[0, 0] == pytest.approx(0.25 * 0.125, rel=1e-15)
+
+
+# --------------------------------------- exhaustive boundary enumeration (T <= 6)
+
+def all_boundary_patterns(T):
+    """Every per-step state in {none, term, trunc, both}: 4^T rows."""
+    pats = np.array(list(itertools.product(range(4), repeat=T)), dtype=np.int64)
+    term = (pats & 1).astype(np.uint8)
+    trunc = ((pats >> 1) & 1).astype(np.uint8)
+    return term, trunc
+
+
+@pytest.mark.parametrize("T", [1, 3, 5])
+def test_exhaustive_boundaries_against_forward_views(T):
+    term, trunc = all_boundary_patterns(T)
+    N = term.shape[0]
+    g = np.random.Generator(np.random.PCG64(1000 + T))
+    r, v = g.standard_normal((N, T)), g.standard_normal((N, T + 1))
+    tv, lr = g.standard_normal((N, T)), g.standard_normal((N, T)) * 0.5
+    q, eq, B = g.standard_normal((N, T)), g.standard_normal((N, T)), g.standard_normal(N)
+    gamma, lam = 0.9, 0.7
+    tl = lambda a: a.tolist()
+    t_, r_ = tl(term), tl(trunc)
+    assert rel_err(oracle.returns(r, term, trunc, tv, B, gamma=gamma),
+                   bf.returns(tl(r), t_, r_, tl(tv), tl(B), gamma)) < RTOL_BF
+    adv, _ = oracle.gae(r, v, term, trunc, tv, gamma=gamma, lam=lam)
+    assert rel_err(adv, bf.gae(tl(r), tl(v), t_, r_, tl(tv), gamma, lam)) < RTOL_BF
+    assert rel_err(oracle.td_lambda(r, v, term, trunc, tv, gamma=gamma, lam=lam),
+                   bf.td_lambda(tl(r), tl(v), t_, r_, tl(tv), gamma, lam)) < RTOL_BF
+    vs, pg = oracle.vtrace(r, v, lr, term, trunc, tv, gamma=gamma, lam=lam,
+                           rho_bar=1.0, c_bar=1.0, pg_rho_bar=1.0)
+    vs_bf, pg_bf = bf.vtrace(tl(r), tl(v), tl(lr), t_, r_, tl(tv), gamma, lam, 1.0, 1.0, 1.0)
+    assert rel_err(vs, vs_bf) < RTOL_BF and rel_err(pg, pg_bf) < RTOL_BF
+    assert rel_err(oracle.retrace(r, q, eq, lr, term, trunc, gamma=gamma, lam=lam),
+                   bf.retrace(tl(r), tl(q), tl(eq), tl(lr), t_, r_, gamma, lam, 1.0)) < RTOL_BF
+
+
+# ------------------------------------------------------------------ invariants
+
+def _all_outputs(d, gamma=0.95, lam=0.9):
+    kw = dict(terminated=d["term"], truncated=d["trunc"], trunc_values=d["tv"])
+    out = {"returns": oracle.returns(d["r"], d["term"], d["trunc"], d["tv"], d["B"], gamma=gamma)}
+    out["adv"], out["tgt"] = oracle.gae(d["r"], d["v"], gamma=gamma, lam=lam, **kw)
+    out["td"] = oracle.td_lambda(d["r"], d["v"], gamma=gamma, lam=lam, **kw)
+    out["vs"], out["pg"] = oracle.vtrace(d["r"], d["v"], d["lr"], gamma=gamma, lam=lam, **kw)
+    out["qret"] = oracle.retrace(d["r"], d["q"], d["eq"], d["lr"], d["term"], d["trunc"],
+                                 gamma=gamma, lam=lam)
+    return out
+
+
+@pytest.mark.parametrize("kind", ["term", "trunc"])
+def test_no_leak_across_episode_boundary(kind):
+    # rl-triton, Method 3: signal stops at the boundary.  Perturb every input
+    # after a boundary at step s (and the window bootstrap); outputs at t <= s
+    # must be bitwise unchanged.
+    N, T, s = 4, 30, 11
+    d = rand_inputs(31, N, T, p_term=0.0, p_trunc=0.0)
+    d[kind][:, s] = 1
+    base = _all_outputs(d)
+    p = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+    g = np.random.Generator(np.random.PCG64(32))
+    for k in ("r", "q", "eq", "lr", "tv"):
+        p[k][:, s + 1:] = g.standard_normal((N, T - s - 1)) * 5
+    p["v"][:, s + 2:] = g.standard_normal((N, T - s - 1)) * 5   # V_{s+2}..V_T
+    p["B"] = p["B"] + 7.0
+    if kind == "term":
+        # After a termination even V_{s+1} and tv_s are unused.
+        p["v"][:, s + 1] += 3.0
+        p["tv"][:, s] += 3.0
+    else:
+        # After a truncation V_{s+1} belongs to the next episode and is unused.
+        p["v"][:, s + 1] += 3.0
+    pert = _all_outputs(p)
+    for name in base:
+        assert np.array_equal(base[name][:, : s + 1], pert[name][:, : s + 1]), name
+
+
+def test_window_bootstrap_counted_once_and_ignored_after_done():
+    # rl-triton, Method 3 (rollout windows): with no boundary, the bootstrap V_T
+    # enters A_{T-1} once: A_{T-1} = r + gamma*V_T - V_{T-1}.
+    N, T, gamma, lam = 3, 9, 0.9, 0.8
+    d = rand_inputs(41, N, T, p_term=0.0, p_trunc=0.0)
+    adv, _ = oracle.gae(d["r"], d["v"], gamma=gamma, lam=lam)
+    assert np.allclose(adv[:, -1], d["r"][:, -1] + gamma * d["v"][:, -1] - d["v"][:, -2],
+                       rtol=0, atol=1e-15)
+    G = oracle.returns(d["r"], bootstrap=d["B"], gamma=gamma)
+    assert np.allclose(G[:, -1], d["r"][:, -1] + gamma * d["B"], rtol=0, atol=1e-15)
+    # If the last step is a boundary, the window bootstrap has no effect.
+    for kind in ("term", "trunc"):
+        e = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in d.items()}
+        e[kind][:, -1] = 1
+        a = _all_outputs(e)
+        e["v"][:, -1] += 11.0
+        e["B"] = e["B"] - 5.0
+        b = _all_outputs(e)
+        for name in a:
+            assert np.array_equal(a[name], b[name]), (kind, name)
+
+
+def test_linearity_in_rewards_and_values():
+    # Scaling every additive input by 2 scales every output by exactly 2
+    # (powers of two are exact in binary floating point).
+    d = rand_inputs(51, 4, 33)
+    e = {k: v for k, v in d.items()}
+    for k in ("r", "v", "q", "eq", "tv", "B"):
+        e[k] = d[k] * 2.0
+    a, b = _all_outputs(d), _all_outputs(e)
+    for name in a:
+        assert np.array_equal(2.0 * a[name], b[name]), name
+
+
+def test_rows_are_independent():
+    d = rand_inputs(61, 9, 17)
+    perm = np.random.Generator(np.random.PCG64(62)).permutation(9)
+    e = {k: v[perm] for k, v in d.items()}
+    a, b = _all_outputs(d), _all_outputs(e)
+    for name in a:
+        assert np.array_equal(a[name][perm], b[name]), name
+
+
+# ------------------------------------------- the pages' affine operator, exactly
+
+def _oplus(B, A):
+    """(alpha_B, beta_B) (+) (alpha_A, beta_A) = (alpha_B + beta_B alpha_A, beta_A beta_B);
+    rl-triton, Method 1.  B is the earlier step."""
+    return (B[0] + B[1] * A[0], A[1] * B[1])
+
+
+def _tree_scan(pairs, rng):
+    """Composite of pairs[0] (+) ... (+) pairs[-1] by a random bracketing."""
+    if len(pairs) == 1:
+        return pairs[0]
+    k = rng.integers(1, len(pairs))
+    return _oplus(_tree_scan(pairs[:k], rng), _tree_scan(pairs[k:], rng))
+
+
+def test_affine_operator_scan_equals_gae_recurrence_exactly():
+    # Any bracketing of the operator gives exactly (rational arithmetic) the
+    # oracle's backward GAE recursion, with alpha_t = delta_t and
+    # beta_t = gamma*lam*(1 - done_t), carry A_T = 0.
+    rng = np.random.Generator(np.random.PCG64(71))
+    T = 9
+    gamma, lam = Fraction(9, 10), Fraction(3, 4)
+    for trial in range(20):
+        r = [Fraction(int(x), 8) for x in rng.integers(-16, 17, T)]
+        v = [Fraction(int(x), 4) for x in rng.integers(-8, 9, T + 1)]
+        tv = [Fraction(int(x), 4) for x in rng.integers(-8, 9, T)]
+        term = [int(x) for x in (rng.random(T) < 0.2)]
+        trunc = [int(x) for x in (rng.random(T) < 0.2)]
+        alpha, beta = [], []
+        for t in range(T):
+            succ = 0 if term[t] else (tv[t] if trunc[t] else v[t + 1])
+            alpha.append(r[t] + gamma * succ - v[t])
+            beta.append(gamma * lam * (0 if (term[t] or trunc[t]) else 1))
+        ref, _ = oracle.gae(np.array([[float(x) for x in r]]), np.array([[float(x) for x in v]]),
+                            np.array([term], np.uint8), np.array([trunc], np.uint8),
+                            np.array([[float(x) for x in tv]]), gamma=float(gamma), lam=float(lam))
+        for t in range(T):
+            a, b = _tree_scan(list(zip(alpha[t:], beta[t:])), rng)
+            A_t = a + b * 0           # carry A_T = 0
+            assert abs(float(A_t) - ref[0, t]) <= 1e-13 * max(1.0, abs(float(A_t)))
+
+
+# ------------------------------------------------------- regression fixture
+
+def test_oracle_regression_fixture():
+    import json
+    import os
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                        "oracle_regression.json")
+    with open(path) as f:
+        doc = json.load(f)
+    i = {k: np.array(v) for k, v in doc["inputs"].items()}
+    p = doc["params"]
+    term, trunc = i["term"].astype(np.uint8), i["trunc"].astype(np.uint8)
+    got = {"returns": oracle.returns(i["r"], term, trunc, i["tv"], i["B"], gamma=p["gamma"])}
+    got["adv"], got["tgt"] = oracle.gae(i["r"], i["v"], term, trunc, i["tv"],
+                                        gamma=p["gamma"], lam=p["lam"])
+    got["td_lambda"] = oracle.td_lambda(i["r"], i["v"], term, trunc, i["tv"],
+                                        gamma=p["gamma"], lam=p["lam"])
+    got["vs"], got["pg"] = oracle.vtrace(i["r"], i["v"], i["lr"], term, trunc, i["tv"],
+                                         gamma=p["gamma"], lam=p["lam"], rho_bar=p["rho_bar"],
+                                         c_bar=p["c_bar"], pg_rho_bar=p["pg_rho_bar"])
+    got["qret"] = oracle.retrace(i["r"], i["q"], i["eq"], i["lr"], term, trunc,
+                                 gamma=p["gamma"], lam=p["lam"], c_bar=p["c_bar"])
+    for k, rows in doc["outputs"].items():
+        want = np.array([[float.fromhex(x) for x in row] for row in rows])
+        assert rel_err(got[k], want) < 1e-15, k
