@@ -1,0 +1,286 @@
+"""Benchmark: GAE over 4096 envs x T=128 fp32 rollouts on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the hot path over one synthetic rollout batch: one
+rlca_gae call (rewards, values [N,T+1], terminated, truncated + truncation
+bootstraps -> advantages and value targets).  Inputs are drawn once (seeded),
+copied to the GPU into R rotating buffer sets whose total size exceeds the
+256 MB Infinity Cache, so every step reads its inputs from HBM.  The K timed
+steps are captured once in a HIP graph (one kernel launch per step, each on
+the next buffer set) and replayed between two events on the launch stream.
+
+Output: one JSON line with env-steps/s, the roofline of the kernel (algorithmic
+bytes per launch / average launch time against the 8 TB/s HBM peak) and the
+CPU oracle timed on the host cores on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "env-steps/sec and achieved HBM GB/s (% of peak), GAE 4096 envs × T=128 fp32"
+HBM_PEAK_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "reverse_linear_recurrence_amd", "csrc", f)
+                  for f in ("scan_kernels.hpp", "rlca.hip")]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--workload", default="gae_4096x128")
+    ap.add_argument("--rotate-mb", type=float, default=1024.0,
+                    help="total size of the rotating buffer sets (defeats the 256 MB MALL)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="approximate CPU time for the oracle baseline (0: skip)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="launch each step from Python instead of replaying a HIP graph")
+    ap.add_argument("--variant", type=int, default=-1, help="force a tiling variant")
+    return ap.parse_args()
+
+
+def algorithmic_bytes(w, N, T):
+    """Bytes the method must move per launch: one read of every input element
+    it uses and one write of every output element (truncation bootstraps,
+    read only at truncations, are not counted)."""
+    es = 2 if w.dtype == "bf16" else 4
+    if w.algo in ("gae",):
+        return (2 * es + 2 + 8) * N * T + es * N  # r, V, 2 flags, adv+targets; V_T
+    if w.algo == "td_lambda":
+        flags = 2 if w.p_trunc is not None else 1
+        return (2 * es + flags + 4) * N * T + es * N
+    if w.algo == "returns":
+        return (es + 1 + 4) * N * T
+    if w.algo == "vtrace+retrace":
+        vt = (3 * es + 1 + 8) * N * T + es * N          # r, V, log_rho, term; vs, pg
+        rt = (4 * es + 1 + 4) * N * T                  # r, Q, EQ, log_rho, term; q_ret
+        return vt + rt
+    raise ValueError(w.algo)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only; multi-GPU runs are not part of this "
+              "library (rows shard across GPUs with no communication)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import reverse_linear_recurrence_amd as rl
+    from reverse_linear_recurrence_amd.synth import WORKLOADS, fp32_param, make_workload
+
+    if not os.path.exists(rl.lib_path()):
+        from reverse_linear_recurrence_amd import build as hip_build
+        hip_build.build()
+    rl.load_library()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+
+    w = WORKLOADS[args.workload]
+    N, T = w.num_envs, w.T
+    gamma, lam = fp32_param(w.gamma), fp32_param(w.lam)
+    clips = {k: fp32_param(v) for k, v in w.clips.items()}
+    dev = torch.device("cuda:0")
+    host = make_workload(w)
+    set_bytes = sum(x.numel() * x.element_size() for x in host.values()) + 2 * 4 * N * T
+    R = max(2, int(np.ceil(args.rotate_mb * 2 ** 20 / set_bytes)))
+    print("workload %s: %d x %d %s, %d rotating sets of %.2f MB" %
+          (w.name, N, T, w.dtype, R, set_bytes / 2 ** 20), file=sys.stderr, flush=True)
+
+    sets = []
+    for _ in range(R):
+        d = {k: v.to(dev) for k, v in host.items()}
+        d["_o0"] = torch.empty(N, T, dtype=torch.float32, device=dev)
+        d["_o1"] = torch.empty(N, T, dtype=torch.float32, device=dev)
+        d["_o2"] = torch.empty(N, T, dtype=torch.float32, device=dev)
+        sets.append(d)
+    torch.cuda.synchronize()
+    rl.rlca_set_variant(args.variant)
+
+    def step(d):
+        if w.algo == "gae":
+            rl.rlca_gae(d["rewards"], d["values"], d["terminated"], d.get("truncated"),
+                        d.get("trunc_values"), gamma=gamma, lam=lam, advantages=d["_o0"],
+                        targets=d["_o1"])
+        elif w.algo == "td_lambda":
+            rl.rlca_td_lambda(d["rewards"], d["values"], d["terminated"], d.get("truncated"),
+                              d.get("trunc_values"), gamma=gamma, lam=lam, out=d["_o0"])
+        elif w.algo == "returns":
+            rl.rlca_returns(d["rewards"], d["terminated"], gamma=gamma, out=d["_o0"])
+        elif w.algo == "vtrace+retrace":
+            rl.rlca_vtrace(d["rewards"], d["values"], d["log_rhos"], d["terminated"], gamma=gamma,
+                           lam=lam, vs=d["_o0"], pg_advantages=d["_o1"], **clips)
+            rl.rlca_retrace(d["rewards"], d["q_taken"], d["exp_q_next"], d["log_rhos"],
+                            d["terminated"], gamma=gamma, lam=lam, c_bar=clips["c_bar"],
+                            out=d["_o2"])
+        else:
+            raise ValueError(w.algo)
+
+    # ---- parity of the timed configuration against the oracle (set 0)
+    import oracle
+    step(sets[0])
+    torch.cuda.synchronize()
+    if w.algo == "gae":
+        ref = oracle.gae(host["rewards"], host["values"], host["terminated"],
+                         host.get("truncated"), host.get("trunc_values"), gamma=gamma, lam=lam)
+        outs = (sets[0]["_o0"], sets[0]["_o1"])
+    elif w.algo == "td_lambda":
+        ref = (oracle.td_lambda(host["rewards"], host["values"], host["terminated"],
+                                host.get("truncated"), host.get("trunc_values"), gamma=gamma,
+                                lam=lam),)
+        outs = (sets[0]["_o0"],)
+    elif w.algo == "returns":
+        ref = (oracle.returns(host["rewards"], host["terminated"], gamma=gamma),)
+        outs = (sets[0]["_o0"],)
+    else:
+        vs, pg = oracle.vtrace(host["rewards"], host["values"], host["log_rhos"],
+                               host["terminated"], gamma=gamma, lam=lam, **clips)
+        qr = oracle.retrace(host["rewards"], host["q_taken"], host["exp_q_next"],
+                            host["log_rhos"], host["terminated"], gamma=gamma, lam=lam,
+                            c_bar=clips["c_bar"])
+        ref = (vs, pg, qr)
+        outs = (sets[0]["_o0"], sets[0]["_o1"], sets[0]["_o2"])
+    parity = max(float(np.max(np.abs(o.double().cpu().numpy() - r)) / np.max(np.abs(r)))
+                 for o, r in zip(outs, ref))
+    tol = 1e-2 if w.dtype == "bf16" else 1e-4
+    variant = rl.rlca_last_variant()
+    print("parity max|err|/max|ref| = %.3g (tolerance %g), variant %d" % (parity, tol, variant),
+          file=sys.stderr, flush=True)
+    if not parity <= tol:
+        print("parity check failed", file=sys.stderr)
+        sys.exit(1)
+
+    # ---- warmup, then K timed steps
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        step(sets[i % R])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    if args.no_graph:
+        start.record(stream)
+        for i in range(K):
+            step(sets[i % R])
+        end.record(stream)
+        torch.cuda.synchronize()
+        timing = "eager launches from Python"
+    else:
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(K):
+                    step(sets[i % R])
+        torch.cuda.synchronize()
+        g.replay()  # untimed: first replay uploads the graph
+        torch.cuda.synchronize()
+        start.record(stream)
+        g.replay()
+        end.record(stream)
+        torch.cuda.synchronize()
+        timing = "HIP graph replay of K launches"
+    elapsed_ms = start.elapsed_time(end)
+    ms_per_step = elapsed_ms / K
+    launches_per_step = 2 if w.algo == "vtrace+retrace" else 1
+    env_steps = N * T
+    value = env_steps / (ms_per_step * 1e-3)
+    bytes_per_step = algorithmic_bytes(w, N, T)
+    achieved = bytes_per_step / (ms_per_step * 1e-3) / 1e9
+
+    # ---- HBM traffic from the committed counter runs, if they match this kernel
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        entry = tr.get(w.name)
+        if entry and entry.get("kernel_source_hash") == kernel_source_hash():
+            traffic = entry.get("bytes_per_launch")
+
+    # ---- CPU oracle on the host cores (bounded sample of the same workload)
+    cpu = None
+    if args.cpu_seconds > 0:
+        h64 = {k: (v.float().numpy().astype(np.float64) if v.is_floating_point() else v.numpy())
+               for k, v in host.items()}
+
+        def oracle_step():
+            if w.algo == "gae":
+                oracle.gae(h64["rewards"], h64["values"], h64["terminated"],
+                           h64.get("truncated"), h64.get("trunc_values"), gamma=gamma, lam=lam)
+            elif w.algo == "td_lambda":
+                oracle.td_lambda(h64["rewards"], h64["values"], h64["terminated"],
+                                 h64.get("truncated"), h64.get("trunc_values"), gamma=gamma,
+                                 lam=lam)
+            elif w.algo == "returns":
+                oracle.returns(h64["rewards"], h64["terminated"], gamma=gamma)
+            else:
+                oracle.vtrace(h64["rewards"], h64["values"], h64["log_rhos"], h64["terminated"],
+                              gamma=gamma, lam=lam, **clips)
+                oracle.retrace(h64["rewards"], h64["q_taken"], h64["exp_q_next"],
+                               h64["log_rhos"], h64["terminated"], gamma=gamma, lam=lam,
+                               c_bar=clips["c_bar"])
+
+        t0 = time.perf_counter()
+        oracle_step()
+        one = time.perf_counter() - t0
+        reps = max(1, int(args.cpu_seconds / max(one, 1e-6)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            oracle_step()
+        cpu_s = time.perf_counter() - t0
+        cpu = {"value": env_steps * reps / cpu_s, "unit": "env-steps/s", "cores": 1,
+               "kind": "oracle",
+               "sample": "the whole %dx%d batch, %d repetitions (%.1f s), single-threaded "
+                         "fp64 C oracle" % (N, T, reps, cpu_s)}
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "env-steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "num_envs": N, "T": T, "input_dtype": w.dtype,
+                   "gamma": w.gamma, "lam": w.lam, "p_term": w.p_term, "p_trunc": w.p_trunc,
+                   "seed": w.seed, "rotation_sets": R, "timing": timing,
+                   "launches_per_step": launches_per_step, "variant": variant},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "algorithmic_bytes_per_launch": bytes_per_step / launches_per_step,
+                     "avg_launch_us": ms_per_step * 1e3 / launches_per_step},
+        "cpu_baseline": cpu,
+        "parity_max_rel_err": parity,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,222 @@
+/*
+ * rlca.h -- reverse linear recurrences for RL credit assignment on AMD
+ * Instinct MI355X (gfx950).  C ABI of librlca.so.
+ *
+ * Every entry point evaluates one reverse-time first-order affine recurrence
+ *
+ *     A_t = alpha_t + beta_t * A_{t+1},      t = T-1 ... 0,           (R)
+ *
+ * independently for each of num_envs rows, as stated in the rl-triton
+ * explainer pages ("rl-triton: High-Performance Triton GPU Kernels for
+ * Reinforcement Learning Credit Assignment", Zehnder 2026; Technical summary,
+ * Method 1, "Unified algebraic framework").  The GPU evaluates (R) as an
+ * associative scan over the affine pairs (alpha_t, beta_t) with the operator
+ *     (alpha_B, beta_B) (+) (alpha_A, beta_A) = (alpha_B + beta_B alpha_A, beta_A beta_B)
+ * (same section), building the pairs and the outputs in registers in a single
+ * pass over the inputs (Method 2, "Fused kernels").
+ *
+ * Episode boundaries (Method 3, "Explicit boundary semantics"), per row and
+ * step t:
+ *   term_t   terminated[t] != 0: natural end; the successor value is 0.
+ *   trunc_t  truncated[t]  != 0: time limit; the successor value is the
+ *            supplied bootstrap trunc_values[t] (the value of the true final
+ *            observation).  A step flagged both ways counts as terminated.
+ *   Either flag cuts the trace: beta_t = 0, so nothing after step t reaches
+ *   any output at or before t.
+ *   Rollout window end (t = T-1): the window bootstrap enters either
+ *   alpha_{T-1} (GAE, TD(lambda), V-trace, Retrace) or the carry A_T
+ *   (discounted returns), never both.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array pointer is a device pointer (memory the GPU of
+ *   `stream` can read or write: hipMalloc'd or torch CUDA tensors).  `stream`
+ *   is a hipStream_t passed as void*; NULL means the default stream.
+ * Layout.  Row-major [num_envs, T] (values: [num_envs, T+1]); `ld_*` is the
+ *   distance between rows in elements (>= T, or >= T+1 for values); elements
+ *   along T are contiguous.  No alignment beyond the element size is
+ *   required.  Flags are uint8 (torch.bool compatible), nonzero = true.
+ * dtype.  RLCA_F32 or RLCA_BF16 gives the type of EVERY floating-point input
+ *   of the call (rewards, values, trunc_values, log_rhos, q_taken,
+ *   exp_q_next, bootstrap).  Arithmetic is fp32; outputs are always fp32.
+ * Ownership.  The caller owns every buffer.  The library allocates no
+ *   memory, keeps no per-call state, never synchronizes, and returns as soon
+ *   as the work is enqueued on `stream`.
+ * Nullable inputs.  terminated == NULL means no terminations; truncated ==
+ *   NULL means no truncations (trunc_values is then ignored and may be NULL).
+ * Errors.  Arguments are validated before anything is enqueued; on any
+ *   non-OK status nothing is launched and no output is written.
+ *     num_envs == 0 or T == 0        -> RLCA_OK, nothing launched.
+ *     negative size, NULL required pointer, ld too small, misaligned pointer,
+ *     gamma or lam outside [0, 1] or NaN, clip <= 0 or NaN,
+ *     truncated != NULL with trunc_values == NULL  -> RLCA_EINVAL
+ *     dtype other than RLCA_F32 / RLCA_BF16 -> RLCA_EDTYPE
+ *     an output overlapping an input or another output -> RLCA_EALIAS
+ *     the HIP runtime refusing the launch -> RLCA_EHIP
+ *   rlca_last_error() returns a message for the calling thread's last
+ *   non-OK status.  Device faults are asynchronous and surface at the
+ *   caller's next synchronization with `stream`.
+ * Concurrency.  Calls are thread-safe; calls on different streams may run
+ *   concurrently if their outputs do not overlap.
+ */
+#ifndef RLCA_H
+#define RLCA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RLCA_OK = 0,
+    RLCA_EINVAL = 1,
+    RLCA_EDTYPE = 2,
+    RLCA_EALIAS = 3,
+    RLCA_EHIP = 4
+} rlca_status;
+
+typedef enum {
+    RLCA_F32 = 0,
+    RLCA_BF16 = 1
+} rlca_dtype;
+
+/*
+ * Discounted returns (Method 1, "discounted returns"):
+ *   G_t = r_t + gamma * G_{t+1}           inside an episode,
+ *   G_t = r_t                             if term_t,
+ *   G_t = r_t + gamma * trunc_values[t]   if trunc_t (and not term_t),
+ *   G_T = bootstrap[row]                  (the carry; bootstrap == NULL -> 0).
+ * As (R): alpha_t = r_t + gamma*[trunc_t & !term_t]*trunc_values[t],
+ *         beta_t = gamma*(1 - done_t).
+ * In:  rewards [N,T]; bootstrap [N] (nullable, dtype of the call).
+ * Out: returns [N,T] fp32.
+ */
+int rlca_returns(int64_t num_envs, int64_t T, int dtype,
+                 const void *rewards, int64_t ld_rewards,
+                 const uint8_t *terminated, int64_t ld_terminated,
+                 const uint8_t *truncated, int64_t ld_truncated,
+                 const void *trunc_values, int64_t ld_trunc_values,
+                 const void *bootstrap,
+                 float gamma,
+                 float *returns, int64_t ld_returns,
+                 void *stream);
+
+/*
+ * Generalized advantage estimation (Method 1, "GAE"; Schulman et al. 2016):
+ *   next_t  = 0 if term_t; trunc_values[t] if trunc_t; values[t+1] otherwise
+ *   delta_t = r_t + gamma * next_t - values[t]
+ *   A_t     = delta_t + gamma*lam*(1 - done_t) * A_{t+1},   A_T = 0
+ * values[T] (column T) is the window bootstrap and enters delta_{T-1} only.
+ * In:  rewards [N,T], values [N,T+1], trunc_values [N,T] (read only where
+ *      truncated and not terminated).
+ * Out: advantages [N,T] fp32; targets [N,T] fp32 = A_t + values[t]
+ *      (targets may be NULL).
+ */
+int rlca_gae(int64_t num_envs, int64_t T, int dtype,
+             const void *rewards, int64_t ld_rewards,
+             const void *values, int64_t ld_values,
+             const uint8_t *terminated, int64_t ld_terminated,
+             const uint8_t *truncated, int64_t ld_truncated,
+             const void *trunc_values, int64_t ld_trunc_values,
+             float gamma, float lam,
+             float *advantages, int64_t ld_advantages,
+             float *targets, int64_t ld_targets,
+             void *stream);
+
+/*
+ * TD(lambda) returns (Method 1, "TD(lambda) returns"): the lambda-return
+ *   G_t = A_t + values[t], with A_t the GAE advantage of rlca_gae on the same
+ *   inputs.  Arguments as rlca_gae.
+ * Out: lambda_returns [N,T] fp32.
+ */
+int rlca_td_lambda(int64_t num_envs, int64_t T, int dtype,
+                   const void *rewards, int64_t ld_rewards,
+                   const void *values, int64_t ld_values,
+                   const uint8_t *terminated, int64_t ld_terminated,
+                   const uint8_t *truncated, int64_t ld_truncated,
+                   const void *trunc_values, int64_t ld_trunc_values,
+                   float gamma, float lam,
+                   float *lambda_returns, int64_t ld_lambda_returns,
+                   void *stream);
+
+/*
+ * V-trace (Method 1, "V-trace"; Espeholt et al. 2018, eq. 1, with the
+ * lambda-scaled trace):
+ *   ratio_t = exp(log_rhos[t])  (log pi - log mu of the taken action)
+ *   rho_t   = min(rho_bar, ratio_t),   c_t = lam * min(c_bar, ratio_t)
+ *   A_t     = rho_t * delta_t + gamma * c_t * (1 - done_t) * A_{t+1},  A_T = 0
+ *   vs_t    = values[t] + A_t
+ *   pg_t    = min(pg_rho_bar, ratio_t) * (r_t + gamma * nvs_t - values[t]),
+ *             nvs_t = 0 if term_t; trunc_values[t] if trunc_t;
+ *                     vs_{t+1} otherwise (values[T] at t = T-1).
+ * delta_t as in rlca_gae.  Clips must be > 0 (+inf allowed: no clipping).
+ * In:  rewards [N,T], values [N,T+1], log_rhos [N,T], trunc_values [N,T].
+ * Out: vs [N,T] fp32; pg_advantages [N,T] fp32 (nullable).
+ */
+int rlca_vtrace(int64_t num_envs, int64_t T, int dtype,
+                const void *rewards, int64_t ld_rewards,
+                const void *values, int64_t ld_values,
+                const void *log_rhos, int64_t ld_log_rhos,
+                const uint8_t *terminated, int64_t ld_terminated,
+                const uint8_t *truncated, int64_t ld_truncated,
+                const void *trunc_values, int64_t ld_trunc_values,
+                float gamma, float lam, float rho_bar, float c_bar, float pg_rho_bar,
+                float *vs, int64_t ld_vs,
+                float *pg_advantages, int64_t ld_pg_advantages,
+                void *stream);
+
+/*
+ * Retrace(lambda) (Method 1, "Retrace(lambda)"; Munos et al. 2016):
+ *   c_t     = lam * min(c_bar, exp(log_rhos[t]))
+ *   delta_t = r_t + gamma * (1 - term_t) * exp_q_next[t] - q_taken[t]
+ *   A_t     = delta_t + gamma * c_{t+1} * (1 - done_t) * A_{t+1}  (t < T-1)
+ *   A_{T-1} = delta_{T-1}   (c_T and Q_T lie outside the window)
+ *   q_ret_t = q_taken[t] + A_t
+ * q_taken[t] = Q(s_t, a_t); exp_q_next[t] = E_pi Q(s_{t+1}, .), which at a
+ * truncation is the value of the true final state (kept; only the trace is
+ * cut) and after a termination is ignored.  No trunc_values argument.
+ * In:  rewards, q_taken, exp_q_next, log_rhos: [N,T].
+ * Out: q_ret [N,T] fp32.
+ */
+int rlca_retrace(int64_t num_envs, int64_t T, int dtype,
+                 const void *rewards, int64_t ld_rewards,
+                 const void *q_taken, int64_t ld_q_taken,
+                 const void *exp_q_next, int64_t ld_exp_q_next,
+                 const void *log_rhos, int64_t ld_log_rhos,
+                 const uint8_t *terminated, int64_t ld_terminated,
+                 const uint8_t *truncated, int64_t ld_truncated,
+                 float gamma, float lam, float c_bar,
+                 float *q_ret, int64_t ld_q_ret,
+                 void *stream);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char *rlca_last_error(void);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int rlca_version(void);
+
+/*
+ * Tiling variants.  A variant fixes how many consecutive steps each lane
+ * owns (K), how many lanes share one row within a wavefront, and how many
+ * wavefronts cooperate on one row.  By default each call picks one from
+ * (num_envs, T).  rlca_set_variant(v) forces variant v (0 <= v <
+ * rlca_num_variants()) for later calls on the calling thread, or restores
+ * the automatic choice with v = -1; it returns the previous setting, or -2
+ * for an unknown v (setting unchanged).  Every variant computes the same
+ * results up to rounding order.  rlca_variant_info writes K, lanes per row
+ * and wavefronts per row of variant v and returns RLCA_OK, or RLCA_EINVAL for
+ * an unknown v.  rlca_last_variant() is the variant the calling thread's
+ * last successful launch used (-1 if none).
+ */
+int rlca_num_variants(void);
+int rlca_set_variant(int variant);
+int rlca_variant_info(int variant, int *steps_per_lane, int *lanes_per_row,
+                      int *waves_per_row);
+int rlca_last_variant(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RLCA_H */

@@ -1,0 +1,36 @@
+"""Reverse linear recurrences for RL credit assignment on AMD MI355X (gfx950).
+
+Python binding of ``librlca.so`` (C ABI in ``include/rlca.h``).  This module
+only marshals arguments: it checks shapes, dtypes and devices, allocates the
+outputs with torch, and passes raw device pointers, row strides and the
+current HIP stream to the library, which does every step of the computation
+in its HIP kernels.  There is no fallback: if the library is missing or the
+tensors are not on a GPU, the call raises.
+
+Functions (same names as the C ABI):
+    rlca_returns, rlca_gae, rlca_td_lambda, rlca_vtrace, rlca_retrace
+and the tiling controls rlca_set_variant, rlca_num_variants,
+rlca_variant_info, rlca_last_variant, plus rlca_version.
+"""
+from ._binding import (  # noqa: F401
+    RLCA_BF16,
+    RLCA_EALIAS,
+    RLCA_EDTYPE,
+    RLCA_EHIP,
+    RLCA_EINVAL,
+    RLCA_F32,
+    RLCA_OK,
+    RlcaError,
+    lib_path,
+    load_library,
+    rlca_gae,
+    rlca_last_variant,
+    rlca_num_variants,
+    rlca_retrace,
+    rlca_returns,
+    rlca_set_variant,
+    rlca_td_lambda,
+    rlca_variant_info,
+    rlca_version,
+    rlca_vtrace,
+)

@@ -1,0 +1,269 @@
+"""ctypes binding of librlca.so: argument marshalling only.
+
+Each function mirrors the C entry point of the same name (include/rlca.h).
+Tensors must be 2-D CUDA (HIP) tensors, contiguous along T (any row stride),
+all floating-point inputs of one call share a dtype (float32 or bfloat16),
+flags are bool or uint8.  Outputs are float32; they are allocated here unless
+given.  The kernel is enqueued on ``stream`` (default: torch's current stream
+of the tensors' device) and the call returns without synchronizing.
+"""
+import ctypes
+import os
+
+import torch
+
+RLCA_OK, RLCA_EINVAL, RLCA_EDTYPE, RLCA_EALIAS, RLCA_EHIP = 0, 1, 2, 3, 4
+RLCA_F32, RLCA_BF16 = 0, 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librlca.so")
+_lib = None
+
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_f32 = ctypes.c_float
+_vp = ctypes.c_void_p
+
+_SIGNATURES = {
+    "rlca_returns": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                     _f32, _vp, _i64, _vp],
+    "rlca_gae": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                 _f32, _f32, _vp, _i64, _vp, _i64, _vp],
+    "rlca_td_lambda": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                       _i64, _f32, _f32, _vp, _i64, _vp],
+    "rlca_vtrace": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                    _vp, _i64, _f32, _f32, _f32, _f32, _f32, _vp, _i64, _vp, _i64, _vp],
+    "rlca_retrace": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                     _vp, _i64, _f32, _f32, _f32, _vp, _i64, _vp],
+    "rlca_last_error": [],
+    "rlca_version": [],
+    "rlca_num_variants": [],
+    "rlca_set_variant": [_int],
+    "rlca_variant_info": [_int, ctypes.POINTER(_int), ctypes.POINTER(_int),
+                          ctypes.POINTER(_int)],
+    "rlca_last_variant": [],
+}
+
+
+class RlcaError(RuntimeError):
+    """A non-OK status from librlca; ``status`` holds the rlca_status code."""
+
+    def __init__(self, status, message):
+        super().__init__("rlca status %d: %s" % (status, message))
+        self.status = status
+
+
+def lib_path():
+    return _LIB_PATH
+
+
+def load_library():
+    """Load librlca.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError("librlca.so is not built: run "
+                              "`python -m reverse_linear_recurrence_amd.build`")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, argtypes in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = argtypes
+            fn.restype = ctypes.c_char_p if name == "rlca_last_error" else ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _check(rc):
+    if rc != RLCA_OK:
+        raise RlcaError(rc, load_library().rlca_last_error().decode())
+
+
+def _float_input(name, x, dtype, shape, device):
+    if x is None:
+        return None, 0
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.dtype != dtype:
+        raise TypeError("%s has dtype %s; every float input of a call must be %s"
+                        % (name, x.dtype, dtype))
+    return _layout(name, x, shape, device)
+
+
+def _flag_input(name, x, shape, device):
+    if x is None:
+        return None, 0
+    if x.dtype not in (torch.bool, torch.uint8):
+        raise TypeError("%s must be bool or uint8, got %s" % (name, x.dtype))
+    return _layout(name, x, shape, device)
+
+
+def _layout(name, x, shape, device):
+    if x.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, x.device, device))
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(x.shape), tuple(shape)))
+    if len(shape) == 2:
+        if shape[1] > 1 and x.stride(1) != 1:
+            raise ValueError("%s must be contiguous along T (stride(1) == 1)" % name)
+        ld = x.stride(0) if shape[0] > 1 else max(shape[1], 1)
+        return x.data_ptr(), ld
+    if shape[0] > 1 and x.stride(0) != 1:
+        raise ValueError("%s must be contiguous" % name)
+    return x.data_ptr(), 1
+
+
+def _output(name, x, shape, device):
+    if x is None:
+        x = torch.empty(shape, dtype=torch.float32, device=device)
+    elif x.dtype != torch.float32:
+        raise TypeError("%s must be float32" % name)
+    ptr, ld = _layout(name, x, shape, device)
+    return x, ptr, ld
+
+
+def _common(rewards):
+    if not isinstance(rewards, torch.Tensor) or rewards.dim() != 2:
+        raise ValueError("rewards must be a 2-D tensor [num_envs, T]")
+    if rewards.device.type != "cuda":
+        raise ValueError("inputs must be on a GPU (got %s)" % rewards.device)
+    if rewards.dtype == torch.float32:
+        code = RLCA_F32
+    elif rewards.dtype == torch.bfloat16:
+        code = RLCA_BF16
+    else:
+        raise TypeError("float inputs must be float32 or bfloat16, got %s" % rewards.dtype)
+    N, T = rewards.shape
+    return N, T, code, rewards.device
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def rlca_returns(rewards, terminated=None, truncated=None, trunc_values=None, bootstrap=None,
+                 *, gamma, out=None, stream=None):
+    """Discounted returns [N, T] (float32).  bootstrap [N] is the carry G_T."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    b, _ = _float_input("bootstrap", bootstrap, dt, (N,), dev)
+    out, o, ld_o = _output("returns", out, (N, T), dev)
+    _check(load_library().rlca_returns(N, T, code, r, ld_r, te, ld_te, tr, ld_tr, tv, ld_tv, b,
+                                       gamma, o, ld_o, _stream(stream, dev)))
+    return out
+
+
+def rlca_gae(rewards, values, terminated=None, truncated=None, trunc_values=None, *, gamma, lam,
+             advantages=None, targets=None, with_targets=True, stream=None):
+    """GAE advantages and value targets, each [N, T] float32.
+
+    values is [N, T+1] (column T is the window bootstrap).  Returns
+    ``(advantages, targets)``; targets is None when ``with_targets`` is False.
+    """
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    adv, a, ld_a = _output("advantages", advantages, (N, T), dev)
+    g, ld_g = None, 0
+    if with_targets or targets is not None:
+        targets, g, ld_g = _output("targets", targets, (N, T), dev)
+    _check(load_library().rlca_gae(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr, ld_tr, tv, ld_tv,
+                                   gamma, lam, a, ld_a, g, ld_g, _stream(stream, dev)))
+    return adv, targets
+
+
+def rlca_td_lambda(rewards, values, terminated=None, truncated=None, trunc_values=None, *, gamma,
+                   lam, out=None, stream=None):
+    """TD(lambda) returns [N, T] float32; values is [N, T+1]."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    out, o, ld_o = _output("lambda_returns", out, (N, T), dev)
+    _check(load_library().rlca_td_lambda(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr, ld_tr, tv,
+                                         ld_tv, gamma, lam, o, ld_o, _stream(stream, dev)))
+    return out
+
+
+def rlca_vtrace(rewards, values, log_rhos, terminated=None, truncated=None, trunc_values=None, *,
+                gamma, lam=1.0, rho_bar=1.0, c_bar=1.0, pg_rho_bar=1.0, vs=None,
+                pg_advantages=None, with_pg=True, stream=None):
+    """V-trace targets vs and policy-gradient advantages, each [N, T] float32.
+
+    Returns ``(vs, pg_advantages)``; pg_advantages is None when ``with_pg`` is
+    False.
+    """
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    lr, ld_lr = _float_input("log_rhos", log_rhos, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    vs, o, ld_o = _output("vs", vs, (N, T), dev)
+    pg, ld_pg = None, 0
+    if with_pg or pg_advantages is not None:
+        pg_advantages, pg, ld_pg = _output("pg_advantages", pg_advantages, (N, T), dev)
+    _check(load_library().rlca_vtrace(N, T, code, r, ld_r, v, ld_v, lr, ld_lr, te, ld_te, tr,
+                                      ld_tr, tv, ld_tv, gamma, lam, rho_bar, c_bar, pg_rho_bar,
+                                      o, ld_o, pg, ld_pg, _stream(stream, dev)))
+    return vs, pg_advantages
+
+
+def rlca_retrace(rewards, q_taken, exp_q_next, log_rhos, terminated=None, truncated=None, *,
+                 gamma, lam=1.0, c_bar=1.0, out=None, stream=None):
+    """Retrace(lambda) targets Q^ret [N, T] float32."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    q, ld_q = _float_input("q_taken", q_taken, dt, (N, T), dev)
+    eq, ld_eq = _float_input("exp_q_next", exp_q_next, dt, (N, T), dev)
+    lr, ld_lr = _float_input("log_rhos", log_rhos, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    out, o, ld_o = _output("q_ret", out, (N, T), dev)
+    _check(load_library().rlca_retrace(N, T, code, r, ld_r, q, ld_q, eq, ld_eq, lr, ld_lr, te,
+                                       ld_te, tr, ld_tr, gamma, lam, c_bar, o, ld_o,
+                                       _stream(stream, dev)))
+    return out
+
+
+def rlca_version():
+    return load_library().rlca_version()
+
+
+def rlca_num_variants():
+    return load_library().rlca_num_variants()
+
+
+def rlca_set_variant(variant):
+    """Force tiling variant ``variant`` on this thread (-1: automatic); returns the previous."""
+    prev = load_library().rlca_set_variant(int(variant))
+    if prev == -2:
+        raise ValueError("unknown variant %r" % (variant,))
+    return prev
+
+
+def rlca_variant_info(variant):
+    """(steps_per_lane, lanes_per_row, waves_per_row) of a tiling variant."""
+    k, l, w = _int(), _int(), _int()
+    _check(load_library().rlca_variant_info(int(variant), ctypes.byref(k), ctypes.byref(l),
+                                            ctypes.byref(w)))
+    return k.value, l.value, w.value
+
+
+def rlca_last_variant():
+    return load_library().rlca_last_variant()

@@ -1,0 +1,560 @@
+// scan_kernels.hpp -- gfx950 (CDNA4) kernels for reverse-time affine
+// recurrences A_t = alpha_t + beta_t * A_{t+1} over [num_envs, T] rollouts.
+//
+// Source: the rl-triton explainer pages ("rl-triton: High-Performance Triton
+// GPU Kernels for Reinforcement Learning Credit Assignment", Zehnder 2026),
+// Technical summary:
+//   Method 1  every algorithm is an instance of the recurrence above and is
+//             evaluated as an associative scan over (alpha_t, beta_t) with
+//             (a_B, b_B) (+) (a_A, b_A) = (a_B + b_B a_A, b_A b_B), B earlier;
+//   Method 2  the pairs are built from the raw rollout in registers, scanned
+//             on chip, and only the final outputs are written (one read and
+//             one write of HBM per element);
+//   Method 3  termination zeroes the successor value, truncation bootstraps
+//             from a supplied value, both cut the trace; the window bootstrap
+//             enters alpha_{T-1} or the carry A_T, never both.
+//
+// Mapping onto CDNA4 (64-lane wavefronts):
+//   * A row is processed in tiles of kTile = kGroup * K steps, where kGroup
+//     lanes share the row: LPR lanes of one wavefront (16, 32 or 64), or WPR
+//     whole wavefronts of a workgroup.  Tiles are aligned to the row start
+//     and visited from the last one (latest in time) to the first, carrying
+//     the scalar A at the tile boundary.
+//   * Lane g of the group owns the K consecutive steps
+//     [tile_start + (kGroup-1-g)*K, +K): lane order is the REVERSE of time
+//     order, so the upward DPP prefix scan (row_shr, row_bcast) computes the
+//     time-suffix composite that a reverse recurrence needs.  Memory access
+//     stays coalesced: a wavefront still reads one contiguous span.
+//   * Per lane: vector loads of its K steps (4-byte aligned dwordx4 loads;
+//     bf16 and uint8 rows of any alignment are read as aligned dwords and
+//     realigned in registers), (alpha, beta) built in VGPRs, folded
+//     sequentially (K-1 FMAs), then log2(LPR) DPP levels of the operator
+//     across lanes, then (WPR > 1) one LDS exchange of per-wavefront
+//     aggregates.  Each lane then re-runs its K steps from its incoming value
+//     and writes the fused outputs with vector stores.
+//   * HBM traffic is one read of every input element the method uses (plus
+//     the V_{t+1} / log_rho_{t+1} neighbour, which hits in cache) and one
+//     write of every output element.  No intermediate touches HBM.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rlca {
+
+enum Algo : int { kReturns = 0, kGae = 1, kTdLambda = 2, kVtrace = 3, kRetrace = 4 };
+
+using bf16_t = uint16_t;  // raw bfloat16 bits
+
+// Everything a launch needs, passed by value in the kernel argument segment.
+// Row pointers are byte-exact device addresses; ld_* are row strides in
+// elements.  Field use per algorithm:
+//   r      rewards [N,T]                                  (all)
+//   v      values [N,T+1] (gae, td_lambda, vtrace) or q_taken [N,T] (retrace)
+//   lr     log importance ratios [N,T]                    (vtrace, retrace)
+//   eq     E_pi Q(s_{t+1}, .) [N,T]                        (retrace)
+//   tv     truncation bootstrap values [N,T], nullable    (not retrace)
+//   boot   window bootstrap [N], nullable                 (returns)
+//   o0     returns | advantages | lambda returns | vs | q_ret
+//   o1     targets (gae) | pg advantages (vtrace), nullable
+struct Args {
+  int64_t N, T;
+  const void *r;  int64_t ld_r;
+  const void *v;  int64_t ld_v;
+  const void *lr; int64_t ld_lr;
+  const void *eq; int64_t ld_eq;
+  const void *tv; int64_t ld_tv;
+  const void *boot;
+  const uint8_t *term;  int64_t ld_term;
+  const uint8_t *trunc; int64_t ld_trunc;
+  float *o0; int64_t ld_o0;
+  float *o1; int64_t ld_o1;
+  float gamma, lam, rho_bar, c_bar, pg_rho_bar;
+};
+
+// ------------------------------------------------------------------ loads
+
+struct __attribute__((aligned(4))) F4 { float x, y, z, w; };
+struct __attribute__((aligned(4))) U4 { uint32_t x, y, z, w; };
+struct __attribute__((aligned(4))) U2 { uint32_t x, y; };
+
+// ND consecutive dwords from a 4-byte aligned address, as dwordx4/x2/x1 loads.
+template <int ND>
+__device__ __forceinline__ void ld_dwords(const uint32_t *__restrict__ p, uint32_t (&d)[ND]) {
+#pragma unroll
+  for (int i = 0; i + 4 <= ND; i += 4) {
+    U4 q = *reinterpret_cast<const U4 *>(p + i);
+    d[i] = q.x; d[i + 1] = q.y; d[i + 2] = q.z; d[i + 3] = q.w;
+  }
+  constexpr int done4 = ND / 4 * 4;
+  if constexpr (ND - done4 >= 2) {
+    U2 q = *reinterpret_cast<const U2 *>(p + done4);
+    d[done4] = q.x; d[done4 + 1] = q.y;
+  }
+  if constexpr ((ND - done4) % 2 == 1) d[ND - 1] = p[ND - 1];
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+template <typename InT> struct Ld;
+
+template <> struct Ld<float> {
+  // K consecutive values at p (K % 4 == 0; p 4-byte aligned): K/4 dwordx4.
+  template <int K>
+  static __device__ __forceinline__ void vec(const float *__restrict__ p, float (&x)[K]) {
+    static_assert(K % 4 == 0, "K must be a multiple of 4");
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) {
+      F4 q = reinterpret_cast<const F4 *>(p)[i];
+      x[4 * i] = q.x; x[4 * i + 1] = q.y; x[4 * i + 2] = q.z; x[4 * i + 3] = q.w;
+    }
+  }
+  static __device__ __forceinline__ float one(const float *p) { return *p; }
+};
+
+template <> struct Ld<bf16_t> {
+  // K consecutive bf16 values at p (K % 4 == 0; p 2-byte aligned).  Reads the
+  // K/2 dwords starting at the dword that holds p[0], plus one more dword:
+  // the one holding p[K-1] when p is odd-aligned (it is then the dword after
+  // the K/2), else the last of the K/2 again.  Every dword read holds a
+  // requested element, and there is no branch.
+  template <int K>
+  static __device__ __forceinline__ void vec(const bf16_t *__restrict__ p, float (&x)[K]) {
+    static_assert(K % 4 == 0, "K must be a multiple of 4");
+    const int odd = static_cast<int>((reinterpret_cast<uintptr_t>(p) >> 1) & 1);
+    const uint32_t *base = reinterpret_cast<const uint32_t *>(p - odd);
+    uint32_t d[K / 2];
+    ld_dwords<K / 2>(base, d);
+    const uint32_t extra = base[K / 2 - 1 + odd];
+#pragma unroll
+    for (int e = 0; e < K; ++e) {
+      // aligned: element e is half (e&1) of dword e/2;
+      // odd:     element e is half ((e+1)&1) of dword (e+1)/2.
+      const uint32_t da = d[e / 2];
+      const uint32_t dn = (e + 1) / 2 < K / 2 ? d[(e + 1) / 2] : extra;
+      const float fa = (e & 1) ? bf16_hi(da) : bf16_lo(da);
+      const float fo = (e & 1) ? bf16_lo(dn) : bf16_hi(da);
+      x[e] = odd ? fo : fa;
+    }
+  }
+  static __device__ __forceinline__ float one(const bf16_t *p) {
+    return __uint_as_float(static_cast<uint32_t>(*p) << 16);
+  }
+};
+
+// K flag bytes at p (any alignment), loaded as raw dwords and realigned
+// later (decode), so the loads of a tile are all in flight before any use.
+// Same rule as the bf16 loader: K/4 dwords from the dword holding p[0], plus
+// the dword holding p[K-1] (a repeat of the last one when p is 4-byte
+// aligned).  After decode, byte j of the span is bits [8*(j%4), +8) of w[j/4].
+template <int K>
+struct FlagWords {
+  uint32_t d[K / 4];
+  uint32_t extra;
+  uint32_t sh;  // misalignment of p in bits
+};
+
+template <int K>
+__device__ __forceinline__ void ld_flags_raw(const uint8_t *__restrict__ p, FlagWords<K> &f) {
+  static_assert(K % 4 == 0, "K must be a multiple of 4");
+  const int mis = static_cast<int>(reinterpret_cast<uintptr_t>(p) & 3);
+  const uint32_t *base = reinterpret_cast<const uint32_t *>(p - mis);
+  ld_dwords<K / 4>(base, f.d);
+  f.extra = base[K / 4 - 1 + (mis != 0)];
+  f.sh = static_cast<uint32_t>(mis) * 8;
+}
+
+template <int K>
+__device__ __forceinline__ void decode_flags(const FlagWords<K> &f, uint32_t (&w)[K / 4]) {
+#pragma unroll
+  for (int i = 0; i < K / 4; ++i) {
+    const uint32_t hi = i + 1 < K / 4 ? f.d[i + 1] : f.extra;
+    const uint64_t pair = (static_cast<uint64_t>(hi) << 32) | f.d[i];
+    w[i] = static_cast<uint32_t>(pair >> f.sh);
+  }
+}
+
+template <int K>
+__device__ __forceinline__ bool flag(const uint32_t (&w)[K / 4], int j) {
+  return ((w[j >> 2] >> ((j & 3) * 8)) & 0xffu) != 0;
+}
+
+// Element-wise predicated loads (e < lim) for the ragged last tile of a row.
+template <typename InT, int K>
+__device__ __forceinline__ void ld_part(const InT *__restrict__ p, int64_t lim, float (&x)[K]) {
+#pragma unroll
+  for (int e = 0; e < K; ++e) x[e] = e < lim ? Ld<InT>::one(p + e) : 0.f;
+}
+
+template <int K>
+__device__ __forceinline__ void ld_flags_part(const uint8_t *__restrict__ p, int64_t lim,
+                                              uint32_t (&w)[K / 4]) {
+#pragma unroll
+  for (int i = 0; i < K / 4; ++i) w[i] = 0;
+#pragma unroll
+  for (int e = 0; e < K; ++e)
+    if (e < lim && p[e] != 0) w[e >> 2] |= 1u << ((e & 3) * 8);
+}
+
+// ------------------------------------------------------- cross-lane scan
+
+// Value of `src` in the lane selected by the DPP control CTRL (rows enabled by
+// ROW_MASK); lanes without a valid source, or in disabled rows, get `old`.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp(float src, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                     CTRL, ROW_MASK, 0xf, false));
+}
+
+// One Hillis-Steele level of the affine operator: this lane (earlier in time)
+// composes with the aggregate of a lower lane (later in time):
+//   (a, b) <- (a + b * a_src, b * b_src);  a missing source is the identity (0, 1).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void scan_level(float &a, float &b) {
+  const float a_src = dpp<CTRL, ROW_MASK>(a, 0.f);
+  const float b_src = dpp<CTRL, ROW_MASK>(b, 1.f);
+  a = fmaf(b, a_src, a);
+  b = b * b_src;
+}
+
+// Inclusive scan over aligned groups of LANES lanes (16, 32 or 64): afterwards
+// lane i holds f_i o f_{i-1} o ... o f_{group start}.
+template <int LANES>
+__device__ __forceinline__ void group_scan(float &a, float &b) {
+  static_assert(LANES == 16 || LANES == 32 || LANES == 64, "group of 16, 32 or 64 lanes");
+  scan_level<0x111, 0xf>(a, b);  // row_shr:1
+  scan_level<0x112, 0xf>(a, b);  // row_shr:2
+  scan_level<0x114, 0xf>(a, b);  // row_shr:4
+  scan_level<0x118, 0xf>(a, b);  // row_shr:8
+  if constexpr (LANES >= 32) scan_level<0x142, 0xa>(a, b);  // row_bcast:15 -> rows 1, 3
+  if constexpr (LANES >= 64) scan_level<0x143, 0xc>(a, b);  // row_bcast:31 -> rows 2, 3
+}
+
+__device__ __forceinline__ float readlane(float x, int lane) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+__device__ __forceinline__ float lane_shuffle(float x, int src_lane) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src_lane << 2, __float_as_int(x)));
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <int A> struct Uses {
+  static constexpr bool values = A == kGae || A == kTdLambda || A == kVtrace;  // V [N,T+1]
+  static constexpr bool q = A == kRetrace;
+  static constexpr bool log_rho = A == kVtrace || A == kRetrace;
+  static constexpr bool tv = A != kRetrace;
+  static constexpr bool two_outputs = A == kGae || A == kVtrace;
+};
+
+template <typename InT>
+struct RowPtrs {
+  const InT *r, *v, *lr, *eq, *tv;
+  const uint8_t *te, *tr;
+  float *o0, *o1;
+};
+
+// A lane's raw inputs for its K steps t0 .. t0+K-1 (v and lr carry the
+// step-(t0+K) neighbour in slot K; v holds q_taken for Retrace).
+template <int K>
+struct Raw {
+  float r[K], v[K + 1], lr[K + 1], eq[K], tv[K];
+  uint32_t te[K / 4], tr[K / 4];
+};
+
+// One read of the raw rollout for a lane (Method 2: on-chip construction).
+// kEdge = false: every lane of the tile lies inside its row (lim >= K), the
+// loads are unconditional vector loads.  kEdge = true: the ragged last tile,
+// element-wise loads of the steps e < lim only.
+template <int A, typename InT, int K, bool kEdge>
+__device__ __forceinline__ void load_tile(const RowPtrs<InT> &rp, bool has_term, bool has_trunc,
+                                          int64_t t0, int64_t lim, Raw<K> &x) {
+  using U = Uses<A>;
+#pragma unroll
+  for (int j = 0; j < K; ++j) { x.r[j] = 0.f; x.v[j] = 0.f; x.lr[j] = 0.f; x.eq[j] = 0.f; x.tv[j] = 0.f; }
+  x.v[K] = 0.f;
+  x.lr[K] = 0.f;
+#pragma unroll
+  for (int i = 0; i < K / 4; ++i) { x.te[i] = 0; x.tr[i] = 0; }
+
+  if constexpr (!kEdge) {
+    // Flags first, with no branch: a missing flag array is replaced by the
+    // lane's own reward bytes (the address of its reward load, so a cache
+    // hit) and masked to zero after decoding.  The truncation test below then
+    // waits for the flags only, with every other load of the tile in flight.
+    FlagWords<K> ftr, fte;
+    const uint8_t *own = reinterpret_cast<const uint8_t *>(rp.r + t0);
+    ld_flags_raw<K>(has_trunc ? rp.tr + t0 : own, ftr);
+    ld_flags_raw<K>(has_term ? rp.te + t0 : own, fte);
+    Ld<InT>::template vec<K>(rp.r + t0, x.r);
+    if constexpr (U::values || U::q) {
+      float vk[K];
+      Ld<InT>::template vec<K>(rp.v + t0, vk);
+#pragma unroll
+      for (int j = 0; j < K; ++j) x.v[j] = vk[j];
+      if constexpr (U::values) x.v[K] = Ld<InT>::one(rp.v + t0 + K);  // V_{t0+K} (<= V_T)
+    }
+    if constexpr (U::q) Ld<InT>::template vec<K>(rp.eq + t0, x.eq);
+    if constexpr (U::log_rho) {
+      float lk[K];
+      Ld<InT>::template vec<K>(rp.lr + t0, lk);
+#pragma unroll
+      for (int j = 0; j < K; ++j) x.lr[j] = lk[j];
+      if constexpr (A == kRetrace) {
+        // log_rho_{t0+K}; at the row end (lim == K) re-read the last step
+        // instead, whose value the trace then ignores.
+        x.lr[K] = Ld<InT>::one(rp.lr + t0 + (lim > K ? K : K - 1));
+      }
+    }
+    decode_flags<K>(ftr, x.tr);
+    decode_flags<K>(fte, x.te);
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) {
+      x.tr[i] = has_trunc ? x.tr[i] : 0u;
+      x.te[i] = has_term ? x.te[i] : 0u;
+    }
+  } else if (lim > 0) {
+    if (has_trunc) ld_flags_part<K>(rp.tr + t0, lim, x.tr);
+    if (has_term) ld_flags_part<K>(rp.te + t0, lim, x.te);
+    ld_part<InT, K>(rp.r + t0, lim, x.r);
+    if constexpr (U::values) {
+#pragma unroll
+      for (int e = 0; e <= K; ++e) x.v[e] = e <= lim ? Ld<InT>::one(rp.v + t0 + e) : 0.f;
+    }
+    if constexpr (U::q) {
+      float qk[K];
+      ld_part<InT, K>(rp.v + t0, lim, qk);
+#pragma unroll
+      for (int j = 0; j < K; ++j) x.v[j] = qk[j];
+      ld_part<InT, K>(rp.eq + t0, lim, x.eq);
+    }
+    if constexpr (U::log_rho) {
+#pragma unroll
+      for (int e = 0; e <= K; ++e) x.lr[e] = e < lim ? Ld<InT>::one(rp.lr + t0 + e) : 0.f;
+    }
+  }
+
+  if constexpr (U::tv) {
+    // Truncation bootstraps are read at truncated steps only (rare), never
+    // densely.  Flags of steps outside the row are zero.
+    uint32_t any_tr = 0;
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) any_tr |= x.tr[i];
+    if (any_tr != 0) {
+#pragma unroll
+      for (int j = 0; j < K; ++j)
+        if (flag<K>(x.tr, j)) x.tv[j] = Ld<InT>::one(rp.tv + t0 + j);
+    }
+  }
+}
+
+// (alpha_t, beta_t) per step (Method 1 coefficients, Method 3 masks).  Steps
+// outside the row get the identity map (0, 1).
+template <int A, int K, bool kEdge>
+__device__ __forceinline__ void coefficients(const Raw<K> &x, int64_t lim, const Args &p,
+                                             float (&al)[K], float (&be)[K], float (&ratio)[K]) {
+  const float gamma = p.gamma;
+  const float gl = p.gamma * p.lam;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const bool te = flag<K>(x.te, j);
+    const bool tr = flag<K>(x.tr, j);
+    const bool done = te || tr;
+    float a_j, b_j;
+    ratio[j] = 0.f;
+    if constexpr (A == kReturns) {
+      a_j = (tr && !te) ? fmaf(gamma, x.tv[j], x.r[j]) : x.r[j];
+      b_j = done ? 0.f : gamma;
+    } else if constexpr (A == kGae || A == kTdLambda) {
+      const float nv = te ? 0.f : (tr ? x.tv[j] : x.v[j + 1]);
+      a_j = fmaf(gamma, nv, x.r[j]) - x.v[j];
+      b_j = done ? 0.f : gl;
+    } else if constexpr (A == kVtrace) {
+      const float e = __expf(x.lr[j]);
+      ratio[j] = e;
+      const float nv = te ? 0.f : (tr ? x.tv[j] : x.v[j + 1]);
+      a_j = fminf(p.rho_bar, e) * (fmaf(gamma, nv, x.r[j]) - x.v[j]);
+      b_j = done ? 0.f : gamma * (p.lam * fminf(p.c_bar, __expf(x.lr[j])));
+    } else {  // kRetrace
+      a_j = (te ? x.r[j] : fmaf(gamma, x.eq[j], x.r[j])) - x.v[j];
+      const bool has_next = j + 1 < lim;  // step t+1 lies inside the row
+      const float c_next = p.lam * fminf(p.c_bar, __expf(x.lr[j + 1]));
+      b_j = (done || !has_next) ? 0.f : gamma * c_next;
+    }
+    const bool valid = !kEdge || j < lim;
+    al[j] = valid ? a_j : 0.f;
+    be[j] = valid ? b_j : 1.f;
+  }
+}
+
+// One tile of one row group: load, build pairs, fold, scan, carry, re-run,
+// store.  Returns the carry for the next (earlier) tile.
+template <int A, typename InT, int K, int LPR, int WPR, bool kEdge>
+__device__ __forceinline__ float do_tile(const Args &p, const RowPtrs<InT> &rp, bool row_ok,
+                                         int64_t c, bool need_carry, int g, int lane, int wave,
+                                         float carry, float2 (*s_agg)[WPR]) {
+  constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
+  constexpr int kTile = kGroup * K;
+  constexpr int kScanLanes = WPR > 1 ? 64 : LPR;
+  using U = Uses<A>;
+
+  const int64_t t0 = c * kTile + static_cast<int64_t>(kGroup - 1 - g) * K;
+  int64_t lim = p.T - t0;  // steps of this lane that lie inside the row
+  if constexpr (kEdge) lim = row_ok ? (lim > 0 ? lim : 0) : 0;
+
+  Raw<K> x;
+  load_tile<A, InT, K, kEdge>(rp, p.term != nullptr, p.trunc != nullptr, t0, lim, x);
+
+  float al[K], be[K], ratio[K];
+  coefficients<A, K, kEdge>(x, lim, p, al, be, ratio);
+
+  // Fold the lane's steps: (a, b) = f_{t0} o ... o f_{t0+K-1}.
+  float a = al[K - 1], b = be[K - 1];
+#pragma unroll
+  for (int j = K - 2; j >= 0; --j) {
+    a = fmaf(be[j], a, al[j]);
+    b = be[j] * b;
+  }
+
+  group_scan<kScanLanes>(a, b);
+
+  // Carry into this lane group's span and out of the tile.
+  float cin = carry;
+  float carry_out = 0.f;
+  if constexpr (WPR > 1) {
+    const int buf = static_cast<int>(c & 1);
+    const float wa = readlane(a, 63), wb = readlane(b, 63);  // whole-wavefront map
+    if (lane == 0) s_agg[buf][wave] = make_float2(wa, wb);
+    __syncthreads();
+    // Wavefront 0 holds the latest steps of the tile: compose downward from it.
+    float xc = carry;
+#pragma unroll
+    for (int w = 0; w < WPR; ++w) {
+      if (w == wave) cin = xc;
+      const float2 ag = s_agg[buf][w];
+      xc = fmaf(ag.y, xc, ag.x);
+    }
+    carry_out = xc;
+  }
+  // A at the earliest step of this lane's span ...
+  const float y = fmaf(b, cin, a);
+  // ... and just after its span: y of the next-later lane (lane - 1).
+  float xin = dpp<0x138, 0xf>(y, cin);  // wave_shr:1
+  if ((lane % kScanLanes) == 0) xin = cin;
+  if constexpr (WPR == 1) {
+    if (need_carry) {
+      if constexpr (LPR == 64) carry_out = readlane(y, 63);
+      else carry_out = lane_shuffle(y, (lane / LPR) * LPR + LPR - 1);
+    }
+  }
+
+  // Re-run the lane's steps from its incoming value; fused epilogue.
+  float o0[K], o1[K];
+  float xa = xin;
+#pragma unroll
+  for (int j = K - 1; j >= 0; --j) {
+    const float xn = xa;  // A_{t+1}
+    xa = fmaf(be[j], xa, al[j]);
+    o1[j] = 0.f;
+    if constexpr (A == kReturns) {
+      o0[j] = xa;
+    } else if constexpr (A == kGae) {
+      o0[j] = xa;
+      o1[j] = xa + x.v[j];
+    } else if constexpr (A == kTdLambda) {
+      o0[j] = xa + x.v[j];
+    } else if constexpr (A == kVtrace) {
+      o0[j] = x.v[j] + xa;
+      const bool te = flag<K>(x.te, j);
+      const bool tr = flag<K>(x.tr, j);
+      const float nvs = te ? 0.f : (tr ? x.tv[j] : x.v[j + 1] + xn);
+      o1[j] = fminf(p.pg_rho_bar, ratio[j]) * (fmaf(p.gamma, nvs, x.r[j]) - x.v[j]);
+    } else {  // kRetrace
+      o0[j] = x.v[j] + xa;
+    }
+  }
+
+  // One write of the outputs.
+  const bool has_o1 = U::two_outputs && p.o1 != nullptr;
+  if constexpr (!kEdge) {
+    if (row_ok) {
+#pragma unroll
+      for (int i = 0; i < K / 4; ++i)
+        reinterpret_cast<F4 *>(rp.o0 + t0)[i] =
+            F4{o0[4 * i], o0[4 * i + 1], o0[4 * i + 2], o0[4 * i + 3]};
+      if (has_o1) {
+#pragma unroll
+        for (int i = 0; i < K / 4; ++i)
+          reinterpret_cast<F4 *>(rp.o1 + t0)[i] =
+              F4{o1[4 * i], o1[4 * i + 1], o1[4 * i + 2], o1[4 * i + 3]};
+      }
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < K; ++e)
+      if (e < lim) {
+        rp.o0[t0 + e] = o0[e];
+        if (has_o1) rp.o1[t0 + e] = o1[e];
+      }
+  }
+  return carry_out;
+}
+
+// Algo A, input type InT, K steps per lane, LPR lanes per row inside one
+// wavefront (WPR == 1), or WPR wavefronts per row (then LPR must be 64).
+// Workgroup: 256 threads (WPR == 1) or 64*WPR threads (WPR > 1).
+template <int A, typename InT, int K, int LPR, int WPR>
+__global__ void __launch_bounds__(WPR > 1 ? 64 * WPR : 256)
+scan_kernel(const Args p) {
+  static_assert(WPR == 1 || LPR == 64, "multi-wavefront rows use whole wavefronts");
+  constexpr int kWaves = WPR > 1 ? WPR : 4;
+  constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
+  constexpr int kTile = kGroup * K;
+
+  __shared__ float2 s_agg[2][WPR];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  int64_t row;
+  int g;  // lane index within the row group; g = 0 owns the latest steps of a tile
+  if constexpr (WPR > 1) {
+    row = blockIdx.x;
+    g = wave * 64 + lane;
+  } else {
+    row = (static_cast<int64_t>(blockIdx.x) * kWaves + wave) * (64 / LPR) + lane / LPR;
+    g = lane % LPR;
+  }
+  // Rows past N (last workgroup only) read row 0 and store nothing; their
+  // lanes stay active because the DPP scan reads every lane of a group.
+  const bool row_ok = row < p.N;
+  const int64_t rr = row_ok ? row : 0;
+
+  RowPtrs<InT> rp;
+  rp.r = static_cast<const InT *>(p.r) + rr * p.ld_r;
+  rp.v = static_cast<const InT *>(p.v) + rr * p.ld_v;
+  rp.lr = static_cast<const InT *>(p.lr) + rr * p.ld_lr;
+  rp.eq = static_cast<const InT *>(p.eq) + rr * p.ld_eq;
+  rp.tv = static_cast<const InT *>(p.tv) + rr * p.ld_tv;
+  rp.te = p.term + rr * p.ld_term;
+  rp.tr = p.trunc + rr * p.ld_trunc;
+  rp.o0 = p.o0 + rr * p.ld_o0;
+  rp.o1 = p.o1 + rr * p.ld_o1;
+
+  float carry = 0.f;  // A at the end of the current tile (A_T for the last)
+  if constexpr (A == kReturns) {
+    if (p.boot != nullptr) carry = Ld<InT>::one(static_cast<const InT *>(p.boot) + rr);
+  }
+
+  const int64_t ntiles = (p.T + kTile - 1) / kTile;
+  int64_t c = ntiles - 1;
+  if (p.T % kTile != 0) {
+    carry = do_tile<A, InT, K, LPR, WPR, true>(p, rp, row_ok, c, c > 0, g, lane, wave, carry, s_agg);
+    --c;
+  }
+  for (; c >= 0; --c)
+    carry = do_tile<A, InT, K, LPR, WPR, false>(p, rp, row_ok, c, c > 0, g, lane, wave, carry, s_agg);
+}
+
+}  // namespace rlca

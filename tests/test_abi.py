@@ -1,0 +1,180 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+that include/rlca.h declares, and rejects bad arguments with the documented
+status before anything is enqueued (validation makes no HIP call)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+import reverse_linear_recurrence_amd as rl
+from reverse_linear_recurrence_amd import _binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rlca.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rlca_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return rl.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_binding._SIGNATURES), "binding and header disagree"
+
+
+def test_version_and_variants(lib):
+    assert rl.rlca_version() >= 100
+    nv = rl.rlca_num_variants()
+    assert nv >= 6
+    for v in range(nv):
+        k, lpr, wpr = rl.rlca_variant_info(v)
+        assert k % 4 == 0 and lpr in (16, 32, 64) or lpr % 64 == 0
+        assert wpr >= 1
+    with pytest.raises(rl.RlcaError):
+        rl.rlca_variant_info(nv)
+    assert rl.rlca_set_variant(2) == -1
+    assert rl.rlca_set_variant(-1) == 2
+    with pytest.raises(ValueError):
+        rl.rlca_set_variant(nv)
+    assert rl.rlca_set_variant(-1) == -1
+
+
+# Fake, never-dereferenced device addresses: validation fails before launch.
+BASE = 0x7F0000000000
+R, V, TE, TR, TV, ADV, TGT = (BASE + i * 0x1000000 for i in range(7))
+F32 = 0
+
+
+def gae(lib, N=4, T=8, dtype=F32, r=R, ld_r=None, v=V, ld_v=None, te=TE, tr=TR, tv=TV,
+        ld_f=None, gamma=0.99, lam=0.95, adv=ADV, ld_a=None, tgt=TGT, ld_g=None):
+    ld_r = T if ld_r is None else ld_r
+    ld_v = T + 1 if ld_v is None else ld_v
+    ld_f = T if ld_f is None else ld_f
+    ld_a = T if ld_a is None else ld_a
+    ld_g = T if ld_g is None else ld_g
+    return lib.rlca_gae(N, T, dtype, r, ld_r, v, ld_v, te, ld_f, tr, ld_f, tv, ld_f,
+                        gamma, lam, adv, ld_a, tgt, ld_g, None)
+
+
+def err(lib):
+    return lib.rlca_last_error().decode()
+
+
+def test_empty_inputs_are_ok_without_launch(lib):
+    assert gae(lib, N=0) == rl.RLCA_OK
+    assert gae(lib, T=0) == rl.RLCA_OK
+    # Nothing is read or written for an empty batch, so no pointer is needed.
+    assert gae(lib, N=0, r=None, v=None, adv=None) == rl.RLCA_OK
+    # Parameters are still validated.
+    assert gae(lib, N=0, gamma=3.0) == rl.RLCA_EINVAL
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(N=-1), rl.RLCA_EINVAL, "num_envs"),
+    (dict(T=-3), rl.RLCA_EINVAL, "T ="),
+    (dict(N=2 ** 31), rl.RLCA_EINVAL, "2^31"),
+    (dict(dtype=7), rl.RLCA_EDTYPE, "dtype"),
+    (dict(r=None), rl.RLCA_EINVAL, "rewards must not be NULL"),
+    (dict(v=None), rl.RLCA_EINVAL, "values must not be NULL"),
+    (dict(adv=None), rl.RLCA_EINVAL, "advantages must not be NULL"),
+    (dict(tv=None), rl.RLCA_EINVAL, "trunc_values is NULL"),
+    (dict(ld_r=7), rl.RLCA_EINVAL, "ld_rewards"),
+    (dict(ld_v=8), rl.RLCA_EINVAL, "ld_values"),
+    (dict(ld_f=5), rl.RLCA_EINVAL, "ld_terminated"),
+    (dict(ld_a=1), rl.RLCA_EINVAL, "ld_advantages"),
+    (dict(r=R + 2), rl.RLCA_EINVAL, "aligned"),
+    (dict(adv=ADV + 1), rl.RLCA_EINVAL, "aligned"),
+    (dict(gamma=1.5), rl.RLCA_EINVAL, "gamma"),
+    (dict(gamma=-0.1), rl.RLCA_EINVAL, "gamma"),
+    (dict(gamma=math.nan), rl.RLCA_EINVAL, "gamma"),
+    (dict(lam=math.nan), rl.RLCA_EINVAL, "lam"),
+    (dict(lam=1.01), rl.RLCA_EINVAL, "lam"),
+    (dict(ld_r=2 ** 62), rl.RLCA_EINVAL, "overflow"),
+])
+def test_gae_rejects_bad_arguments(lib, kw, status, needle):
+    assert gae(lib, **kw) == status
+    assert needle in err(lib)
+
+
+def test_aliasing_is_rejected(lib):
+    # advantages overlapping rewards, targets overlapping advantages, the last
+    # element of a strided output overlapping an input's first element.
+    assert gae(lib, adv=R + 4 * 4) == rl.RLCA_EALIAS
+    assert "advantages" in err(lib) and "rewards" in err(lib)
+    assert gae(lib, tgt=ADV + 4 * 5) == rl.RLCA_EALIAS
+    assert "targets" in err(lib)
+    span = (4 - 1) * 8 + 8  # elements of a [4, 8] array
+    assert gae(lib, adv=R - span * 4 + 4) == rl.RLCA_EALIAS
+    assert gae(lib, adv=R - span * 4) != rl.RLCA_EALIAS  # adjacent, not overlapping
+
+
+def test_truncation_without_flags_needs_no_trunc_values(lib):
+    # truncated == NULL: trunc_values is ignored; validation then proceeds to
+    # the launch, which fails without a GPU (EHIP) or succeeds with one.
+    rc = gae(lib, tr=None, tv=None, N=0)
+    assert rc == rl.RLCA_OK
+
+
+def test_other_entry_points_validate(lib):
+    assert lib.rlca_returns(4, 8, 0, None, 8, None, 8, None, 8, None, 8, None, 0.9,
+                            ADV, 8, None) == rl.RLCA_EINVAL
+    assert lib.rlca_returns(4, 8, 0, R, 8, None, 8, None, 8, None, 8, None, 1.5,
+                            ADV, 8, None) == rl.RLCA_EINVAL
+    # bootstrap overlapping the output
+    assert lib.rlca_returns(4, 8, 0, R, 8, None, 8, None, 8, None, 8, ADV + 8, 0.9,
+                            ADV, 8, None) == rl.RLCA_EALIAS
+    assert lib.rlca_td_lambda(4, 8, 0, R, 8, V, 8, None, 8, None, 8, None, 8, 0.9, 0.9,
+                              ADV, 8, None) == rl.RLCA_EINVAL  # ld_values < T+1
+    assert "ld_values" in err(lib)
+    vt = lambda **k: lib.rlca_vtrace(4, 8, 0, R, 8, V, 9, k.get("lr", TE), 8, None, 8, None, 8,
+                                      None, 8, 0.9, 0.9, k.get("rho", 1.0), k.get("c", 1.0),
+                                      k.get("pg", 1.0), ADV, 8, k.get("pgp", None), 8, None)
+    assert vt(rho=0.0) == rl.RLCA_EINVAL and "rho_bar" in err(lib)
+    assert vt(c=-1.0) == rl.RLCA_EINVAL and "c_bar" in err(lib)
+    assert vt(pg=math.nan) == rl.RLCA_EINVAL and "pg_rho_bar" in err(lib)
+    assert vt(lr=None) == rl.RLCA_EINVAL and "log_rhos" in err(lib)
+    assert vt(pgp=ADV) == rl.RLCA_EALIAS
+    rt = lambda **k: lib.rlca_retrace(4, 8, 0, R, 8, k.get("q", V), 8, k.get("eq", TV), 8, TE,
+                                       8, None, 8, None, 8, 0.9, 0.9, k.get("c", 1.0),
+                                       k.get("out", ADV), 8, None)
+    assert rt(q=None) == rl.RLCA_EINVAL and "q_taken" in err(lib)
+    assert rt(eq=None) == rl.RLCA_EINVAL and "exp_q_next" in err(lib)
+    assert rt(c=0.0) == rl.RLCA_EINVAL
+    assert rt(out=TV + 4) == rl.RLCA_EALIAS and "exp_q_next" in err(lib)
+
+
+def test_error_message_is_per_thread(lib):
+    import threading
+    assert gae(lib, gamma=2.0) == rl.RLCA_EINVAL
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.rlca_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "gamma" in err(lib)
+
+
+def test_binding_refuses_cpu_tensors():
+    r = torch.zeros(2, 4)
+    v = torch.zeros(2, 5)
+    with pytest.raises(ValueError, match="GPU"):
+        rl.rlca_gae(r, v, gamma=0.9, lam=0.9)
+    with pytest.raises(ValueError, match="2-D"):
+        rl.rlca_returns(torch.zeros(4), gamma=0.9)

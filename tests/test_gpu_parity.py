@@ -1,0 +1,266 @@
+"""GPU parity: the HIP library against the fp64 oracle, element by element, on
+the same seeded inputs.  Covers the five measured workloads at full size (in
+the tiling the benchmark uses), every tiling variant on ragged lengths, the
+exhaustive boundary enumeration, strided and misaligned rows, empty inputs,
+and bitwise invariants (no leak across a boundary, window end, determinism,
+row permutation, power-of-two scaling)."""
+import itertools
+
+import numpy as np
+import pytest
+import torch
+
+import reverse_linear_recurrence_amd as rl
+from reverse_linear_recurrence_amd.synth import WORKLOADS, fp32_param, make_workload
+from gpu_common import (ALGOS, DEFAULT_PARAMS, TOL, assert_close, params32, random_inputs,
+                        rel_err, run_gpu, run_oracle, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _auto_variant():
+    rl.rlca_set_variant(-1)
+    yield
+    rl.rlca_set_variant(-1)
+
+
+def workload_params(w):
+    p = dict(DEFAULT_PARAMS)
+    p.update(gamma=w.gamma, lam=w.lam)
+    p.update(w.clips)
+    return params32(p)
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_workload_full_size(name):
+    w = WORKLOADS[name]
+    print("workload", name, flush=True)
+    host = make_workload(w)
+    dev = to_device(host)
+    p = workload_params(w)
+    algos = ("vtrace", "retrace") if w.algo == "vtrace+retrace" else (w.algo,)
+    for algo in algos:
+        got = run_gpu(algo, dev, p)
+        ref = run_oracle(algo, host, p)
+        assert_close(got, ref, TOL[w.dtype], "%s/%s" % (name, algo))
+        errs = {k: rel_err(got[k], ref[k]) for k in ref}
+        print(name, algo, "variant", rl.rlca_last_variant(), "rel err", errs, flush=True)
+
+
+def variant_lengths(v):
+    k, lanes, _ = rl.rlca_variant_info(v)
+    tile = k * lanes
+    return sorted({1, 2, 5, tile // 2 + 3, tile - 4, tile, tile + 4, 2 * tile + 12})
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_every_variant_ragged_lengths(algo, dtype):
+    p = params32(DEFAULT_PARAMS)
+    N = 37  # not a multiple of any workgroup's row count
+    for v in range(rl.rlca_num_variants()):
+        for T in variant_lengths(v):
+            seed = 1000 * v + T
+            host = random_inputs(algo, N, T, seed, dtype)
+            dev = to_device(host)
+            rl.rlca_set_variant(v)
+            print(algo, dtype, "variant", v, "T", T, flush=True)
+            got = run_gpu(algo, dev, p)
+            assert rl.rlca_last_variant() == v
+            ref = run_oracle(algo, host, p)
+            assert_close(got, ref, TOL[dtype], "%s/%s/v%d/T%d" % (algo, dtype, v, T))
+
+
+def boundary_rows(T):
+    pats = np.array(list(itertools.product(range(4), repeat=T)), dtype=np.int64)
+    return (pats & 1).astype(np.uint8), ((pats >> 1) & 1).astype(np.uint8)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_exhaustive_boundaries(algo):
+    # Every per-step state in {none, term, trunc, both} for T = 6 (4096 rows),
+    # and the same patterns placed at the end of a longer row (T = 70), in
+    # every variant.
+    p = params32(DEFAULT_PARAMS)
+    for T, pad in ((6, 0), (70, 64)):
+        te, tr = boundary_rows(6)
+        N = te.shape[0]
+        host = random_inputs(algo, N, T, 77 + T, "f32", p_term=0.0, p_trunc=0.0)
+        term = np.zeros((N, T), np.uint8)
+        trunc = np.zeros((N, T), np.uint8)
+        term[:, pad:] = te
+        trunc[:, pad:] = tr
+        host["terminated"] = torch.from_numpy(term)
+        host["truncated"] = torch.from_numpy(trunc)
+        if algo != "retrace":
+            g = np.random.Generator(np.random.PCG64(5))
+            host["trunc_values"] = torch.from_numpy(g.standard_normal((N, T)).astype(np.float32))
+        dev = to_device(host)
+        ref = run_oracle(algo, host, p)
+        for v in range(rl.rlca_num_variants()):
+            rl.rlca_set_variant(v)
+            print(algo, "T", T, "variant", v, flush=True)
+            assert_close(run_gpu(algo, dev, p), ref, TOL["f32"], "%s/T%d/v%d" % (algo, T, v))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_strided_and_misaligned_rows(algo, dtype):
+    # Row strides larger than T, odd row strides and odd element offsets: the
+    # flag rows land at every byte alignment, bf16 rows at both half-dword
+    # positions, fp32 rows at every 4-byte position inside a 16-byte line.
+    p = params32(DEFAULT_PARAMS)
+    for T, extra, off in ((128, 3, 1), (257, 1, 3), (64, 5, 2), (1031, 2, 1)):
+        N = 29
+        host = random_inputs(algo, N, T, 4242 + T, dtype)
+        ref = run_oracle(algo, host, p)
+        # Each 2-D input is a view into a larger device buffer: row stride
+        # W + extra, first element `off` elements past the allocation start.
+        strided = {k: x.cuda() for k, x in host.items() if x.dim() == 1}
+        for k, x in host.items():
+            if x.dim() == 2:
+                buf = torch.full((off + N * (x.shape[1] + extra) + 8,), 7, dtype=x.dtype,
+                                 device="cuda")
+                view = buf[off:off + N * (x.shape[1] + extra)].view(N, x.shape[1] + extra)
+                view = view[:, :x.shape[1]]
+                view.copy_(x.cuda())
+                strided[k] = view
+        for v in (None, 1, 2, 3, 4):
+            rl.rlca_set_variant(-1 if v is None else v)
+            print(algo, dtype, "T", T, "variant", v, flush=True)
+            got = run_gpu(algo, strided, p)
+            assert_close(got, ref, TOL[dtype], "%s/%s/T%d/v%s" % (algo, dtype, T, v))
+
+
+def test_empty_and_nullable():
+    for N, T in ((0, 16), (5, 0), (0, 0)):
+        r = torch.zeros(N, T, device="cuda")
+        v = torch.zeros(N, T + 1, device="cuda")
+        adv, tgt = rl.rlca_gae(r, v, gamma=0.9, lam=0.9)
+        assert adv.shape == (N, T) and tgt.shape == (N, T)
+    host = random_inputs("gae", 9, 40, 3)
+    dev = to_device(host)
+    p = params32(DEFAULT_PARAMS)
+    adv, tgt = rl.rlca_gae(dev["rewards"], dev["values"], dev["terminated"], dev["truncated"],
+                           dev["trunc_values"], gamma=p["gamma"], lam=p["lam"],
+                           with_targets=False)
+    assert tgt is None
+    ref = run_oracle("gae", host, p)
+    assert rel_err(adv.double().cpu().numpy(), ref["advantages"]) <= TOL["f32"]
+    # No flags at all.
+    adv2, _ = rl.rlca_gae(dev["rewards"], dev["values"], gamma=p["gamma"], lam=p["lam"])
+    ref2 = run_oracle("gae", {"rewards": host["rewards"], "values": host["values"]}, p)
+    assert rel_err(adv2.double().cpu().numpy(), ref2["advantages"]) <= TOL["f32"]
+    hv = random_inputs("vtrace", 9, 40, 4)
+    dv = to_device(hv)
+    vs, pg = rl.rlca_vtrace(dv["rewards"], dv["values"], dv["log_rhos"], dv["terminated"],
+                            dv["truncated"], dv["trunc_values"], gamma=p["gamma"], lam=p["lam"],
+                            with_pg=False)
+    assert pg is None
+    assert rel_err(vs.double().cpu().numpy(), run_oracle("vtrace", hv, p)["vs"]) <= TOL["f32"]
+
+
+def test_runs_on_a_side_stream():
+    host = random_inputs("td_lambda", 300, 200, 8)
+    dev = to_device(host)
+    p = params32(DEFAULT_PARAMS)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        out = rl.rlca_td_lambda(dev["rewards"], dev["values"], dev["terminated"],
+                                dev["truncated"], dev["trunc_values"], gamma=p["gamma"],
+                                lam=p["lam"])
+    s.synchronize()
+    ref = run_oracle("td_lambda", host, p)
+    assert rel_err(out.double().cpu().numpy(), ref["lambda_returns"]) <= TOL["f32"]
+
+
+# ------------------------------------------------------------ bitwise invariants
+
+def _perturb_after(host, algo, s, kind, seed):
+    g = np.random.Generator(np.random.PCG64(seed))
+    h = {k: v.clone() for k, v in host.items()}
+    N, T = h["rewards"].shape
+    for k in ("rewards", "q_taken", "exp_q_next", "log_rhos", "trunc_values"):
+        if k in h:
+            x = h[k].float()
+            x[:, s + 1:] = torch.from_numpy(g.standard_normal((N, T - s - 1)).astype(np.float32)) * 3
+            h[k] = x.to(h[k].dtype)
+    if "values" in h:
+        x = h["values"].float()
+        x[:, s + 1:] = torch.from_numpy(g.standard_normal((N, T - s)).astype(np.float32)) * 3
+        h["values"] = x.to(h["values"].dtype)
+    if "bootstrap" in h:
+        h["bootstrap"] = h["bootstrap"] + 5
+    if kind == "term" and "trunc_values" in h:
+        x = h["trunc_values"].float()
+        x[:, s] += 3
+        h["trunc_values"] = x.to(h["trunc_values"].dtype)
+    return h
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("kind", ["term", "trunc"])
+def test_no_leak_across_boundary_bitwise(algo, kind):
+    # Method 3 of the rl-triton explainer: no signal crosses an episode
+    # boundary.  With a boundary at step s in every row, outputs at t <= s
+    # must be bitwise identical whatever follows.
+    p = params32(DEFAULT_PARAMS)
+    for T, s in ((128, 40), (1024, 700), (300, 299)):
+        host = random_inputs(algo, 64, T, 91, "f32", p_term=0.0, p_trunc=0.0)
+        host["terminated"] = torch.zeros(64, T, dtype=torch.uint8)
+        host["truncated"] = torch.zeros(64, T, dtype=torch.uint8)
+        if "trunc_values" not in host and algo != "retrace":
+            host["trunc_values"] = torch.randn(64, T)
+        host["terminated" if kind == "term" else "truncated"][:, s] = 1
+        pert = _perturb_after(host, algo, s, kind, 92)
+        for v in range(rl.rlca_num_variants()):
+            rl.rlca_set_variant(v)
+            a = run_gpu(algo, to_device(host), p)
+            b = run_gpu(algo, to_device(pert), p)
+            for k in a:
+                assert np.array_equal(a[k][:, :s + 1], b[k][:, :s + 1]), (algo, kind, T, v, k)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_determinism_permutation_and_scaling_bitwise(algo):
+    p = params32(dict(DEFAULT_PARAMS, gamma=0.95, lam=0.9))
+    host = random_inputs(algo, 200, 256, 123, "f32")
+    dev = to_device(host)
+    a = run_gpu(algo, dev, p)
+    b = run_gpu(algo, dev, p)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), ("determinism", k)
+    perm = torch.from_numpy(np.random.Generator(np.random.PCG64(1)).permutation(200))
+    hp = {k: v[perm] for k, v in host.items()}
+    c = run_gpu(algo, to_device(hp), p)
+    for k in a:
+        assert np.array_equal(a[k][perm.numpy()], c[k]), ("permutation", k)
+    hs = {k: (v * 2 if k in ("rewards", "values", "q_taken", "exp_q_next", "trunc_values",
+                             "bootstrap") else v) for k, v in host.items()}
+    d = run_gpu(algo, to_device(hs), p)
+    for k in a:
+        assert np.array_equal(2 * a[k], d[k]), ("scaling", k)
+
+
+def test_window_end_bootstrap_counted_once_bitwise():
+    # With no boundary the bootstrap V_T enters A_{T-1} once; with a boundary
+    # at T-1 it has no effect at all.
+    p = params32(DEFAULT_PARAMS)
+    for algo in ("gae", "td_lambda", "vtrace"):
+        host = random_inputs(algo, 50, 130, 5, "f32", p_term=0.0, p_trunc=0.0)
+        host["terminated"] = torch.zeros(50, 130, dtype=torch.uint8)
+        host["terminated"][:, -1] = 1
+        h2 = {k: v.clone() for k, v in host.items()}
+        h2["values"][:, -1] += 9.0
+        a = run_gpu(algo, to_device(host), p)
+        b = run_gpu(algo, to_device(h2), p)
+        for k in a:
+            assert np.array_equal(a[k], b[k]), (algo, k)
+    host = random_inputs("gae", 50, 130, 6, "f32", p_term=0.0, p_trunc=0.0)
+    host["terminated"] = torch.zeros(50, 130, dtype=torch.uint8)
+    got = run_gpu("gae", to_device(host), p)
+    r, v = host["rewards"].double().numpy(), host["values"].double().numpy()
+    expect = r[:, -1] + p["gamma"] * v[:, -1] - v[:, -2]
+    assert np.max(np.abs(got["advantages"][:, -1] - expect)) <= 1e-5 * np.max(np.abs(expect))
