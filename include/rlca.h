@@ -36,6 +36,11 @@
  *   distance between rows in elements (>= T, or >= T+1 for values); elements
  *   along T are contiguous.  No alignment beyond the element size is
  *   required.  Flags are uint8 (torch.bool compatible), nonzero = true.
+ *   Limits: num_envs <= 2^31-1, T <= 2^31-2, every ld <= 2^31-1.
+ *   trunc_values must be a valid [num_envs, T] array when truncated is
+ *   given, but only its entries at truncated (and not terminated) steps
+ *   affect any output; the others may hold anything, NaN included.  Small
+ *   batches read it in full, large ones only at truncated steps.
  * dtype.  RLCA_F32 or RLCA_BF16 gives the type of EVERY floating-point input
  *   of the call (rewards, values, trunc_values, log_rhos, q_taken,
  *   exp_q_next, bootstrap).  Arithmetic is fp32; outputs are always fp32.
@@ -108,7 +113,7 @@ int rlca_returns(int64_t num_envs, int64_t T, int dtype,
  *   delta_t = r_t + gamma * next_t - values[t]
  *   A_t     = delta_t + gamma*lam*(1 - done_t) * A_{t+1},   A_T = 0
  * values[T] (column T) is the window bootstrap and enters delta_{T-1} only.
- * In:  rewards [N,T], values [N,T+1], trunc_values [N,T] (read only where
+ * In:  rewards [N,T], values [N,T+1], trunc_values [N,T] (used only where
  *      truncated and not terminated).
  * Out: advantages [N,T] fp32; targets [N,T] fp32 = A_t + values[t]
  *      (targets may be NULL).

@@ -29,6 +29,8 @@ def build_command(out):
     return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
             # Packed fp32 ops (v_pk_*_f32) stay off: plain scalar fp32 only.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # Leading scalar kernel arguments are preloaded into SGPRs.
+            "-mllvm", "-amdgpu-kernarg-preload-count=16",
             "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC] + SOURCES + ["-o", out]
 
 

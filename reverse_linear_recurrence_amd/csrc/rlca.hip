@@ -38,36 +38,38 @@ constexpr Variant kVariants[] = {
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-template <int A, typename InT, int V>
+template <int A, typename InT, int V, bool U>
 const void *kernel_for() {
   constexpr Variant v = kVariants[V];
-  return reinterpret_cast<const void *>(&scan_kernel<A, InT, v.K, v.LPR, v.WPR>);
+  return reinterpret_cast<const void *>(&scan_kernel<A, InT, v.K, v.LPR, v.WPR, U>);
 }
 
-template <int A, typename InT>
+template <int A, typename InT, bool U>
 const void *kernel_for(int v) {
   switch (v) {
-    case 0: return kernel_for<A, InT, 0>();
-    case 1: return kernel_for<A, InT, 1>();
-    case 2: return kernel_for<A, InT, 2>();
-    case 3: return kernel_for<A, InT, 3>();
-    case 4: return kernel_for<A, InT, 4>();
-    default: return kernel_for<A, InT, 5>();
+    case 0: return kernel_for<A, InT, 0, U>();
+    case 1: return kernel_for<A, InT, 1, U>();
+    case 2: return kernel_for<A, InT, 2, U>();
+    case 3: return kernel_for<A, InT, 3, U>();
+    case 4: return kernel_for<A, InT, 4, U>();
+    default: return kernel_for<A, InT, 5, U>();
   }
 }
 
 template <int A>
-const void *kernel_for(int dtype, int v) {
-  return dtype == RLCA_BF16 ? kernel_for<A, bf16_t>(v) : kernel_for<A, float>(v);
+const void *kernel_for(int dtype, int v, bool uniform) {
+  if (dtype == RLCA_BF16)
+    return uniform ? kernel_for<A, bf16_t, true>(v) : kernel_for<A, bf16_t, false>(v);
+  return uniform ? kernel_for<A, float, true>(v) : kernel_for<A, float, false>(v);
 }
 
-const void *kernel_for(int algo, int dtype, int v) {
+const void *kernel_for(int algo, int dtype, int v, bool uniform) {
   switch (algo) {
-    case kReturns: return kernel_for<kReturns>(dtype, v);
-    case kGae: return kernel_for<kGae>(dtype, v);
-    case kTdLambda: return kernel_for<kTdLambda>(dtype, v);
-    case kVtrace: return kernel_for<kVtrace>(dtype, v);
-    default: return kernel_for<kRetrace>(dtype, v);
+    case kReturns: return kernel_for<kReturns>(dtype, v, uniform);
+    case kGae: return kernel_for<kGae>(dtype, v, uniform);
+    case kTdLambda: return kernel_for<kTdLambda>(dtype, v, uniform);
+    case kVtrace: return kernel_for<kVtrace>(dtype, v, uniform);
+    default: return kernel_for<kRetrace>(dtype, v, uniform);
   }
 }
 
@@ -129,6 +131,8 @@ int check_array(Arr &a, int64_t N) {
   if (a.ld < a.width)
     return fail(RLCA_EINVAL, "ld_%s = %lld is smaller than the row length %lld", a.name,
                 static_cast<long long>(a.ld), static_cast<long long>(a.width));
+  if (a.ld > INT32_MAX && !a.one_row)
+    return fail(RLCA_EINVAL, "ld_%s = %lld exceeds 2^31-1", a.name, static_cast<long long>(a.ld));
   // Span in elements: (N-1)*ld + width, checked against overflow.
   const int64_t lim = INT64_MAX / a.esize;
   if (N > 1 && a.ld > (lim - a.width) / (N - 1))
@@ -170,7 +174,8 @@ int check_sizes(int64_t N, int64_t T, int dtype) {
     return fail(RLCA_EINVAL, "num_envs = %lld and T = %lld must be >= 0",
                 static_cast<long long>(N), static_cast<long long>(T));
   if (N > INT32_MAX) return fail(RLCA_EINVAL, "num_envs = %lld exceeds 2^31-1", static_cast<long long>(N));
-  if (T > (int64_t(1) << 40)) return fail(RLCA_EINVAL, "T = %lld is too large", static_cast<long long>(T));
+  if (T > INT32_MAX - 1)
+    return fail(RLCA_EINVAL, "T = %lld exceeds 2^31-2", static_cast<long long>(T));
   if (dtype != RLCA_F32 && dtype != RLCA_BF16) return fail(RLCA_EDTYPE, "unknown dtype %d", dtype);
   return RLCA_OK;
 }
@@ -194,8 +199,47 @@ int launch(int algo, int dtype, const Args &args, void *stream) {
     block = dim3(256);
   }
   Args a = args;
-  void *kargs[] = {&a};
-  const hipError_t e = hipLaunchKernel(kernel_for(algo, dtype, v), grid, block, kargs, 0,
+  // Hot streams (see scan_kernels.hpp), passed again as preloaded scalars.
+  const void *hot[5] = {a.r, nullptr, nullptr, nullptr, nullptr};
+  int64_t hld[5] = {a.ld_r, 0, 0, 0, 0};  // stride of each hot [N,T] stream (0: none)
+  int64_t ldx = 0;
+  switch (algo) {
+    case kReturns:
+      hot[1] = a.term; hld[1] = a.ld_term;
+      hot[2] = a.trunc; hld[2] = a.ld_trunc;
+      hot[3] = a.tv; hld[3] = a.ld_tv;
+      hot[4] = a.boot;  // a [N] vector: no stride
+      break;
+    case kGae:
+    case kTdLambda:
+      hot[1] = a.v; ldx = a.ld_v;
+      hot[2] = a.term; hld[2] = a.ld_term;
+      hot[3] = a.trunc; hld[3] = a.ld_trunc;
+      hot[4] = a.tv; hld[4] = a.ld_tv;
+      break;
+    case kVtrace:
+      hot[1] = a.v; ldx = a.ld_v;
+      hot[2] = a.lr; hld[2] = a.ld_lr;
+      hot[3] = a.term; hld[3] = a.ld_term;
+      hot[4] = a.trunc; hld[4] = a.ld_trunc;
+      break;
+    default:  // kRetrace
+      hot[1] = a.v; hld[1] = a.ld_v;
+      hot[2] = a.eq; hld[2] = a.ld_eq;
+      hot[3] = a.lr; hld[3] = a.ld_lr;
+      hot[4] = a.term; hld[4] = a.ld_term;
+      ldx = a.trunc != nullptr ? 1 : 0;
+      break;
+  }
+  bool uniform = true;
+  for (int i = 1; i < 5; ++i)
+    if (hot[i] != nullptr && hld[i] != 0 && hld[i] != a.ld_r) uniform = false;
+  int N32 = static_cast<int>(a.N);
+  int T32 = static_cast<int>(a.T);
+  int ldT = static_cast<int>(a.ld_r);
+  int ldX = static_cast<int>(ldx);
+  void *kargs[] = {&hot[0], &hot[1], &hot[2], &hot[3], &hot[4], &N32, &T32, &ldT, &ldX, &a};
+  const hipError_t e = hipLaunchKernel(kernel_for(algo, dtype, v, uniform), grid, block, kargs, 0,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -72,11 +72,33 @@ struct Args {
   float gamma, lam, rho_bar, c_bar, pg_rho_bar;
 };
 
+// Hot streams: the (up to) five arrays each algorithm reads at the start of a
+// tile.  They are passed again as leading scalar kernel arguments h0..h4,
+// with N, T and two row strides, 14 dwords that the dispatcher preloads into
+// SGPRs: a wavefront issues its loads without first fetching the argument
+// block from memory.
+//   returns:        h = r, term, trunc, trunc_values, bootstrap
+//   gae, td_lambda: h = r, v, term, trunc, trunc_values
+//   vtrace:         h = r, v, log_rho, term, trunc     (trunc_values cold)
+//   retrace:        h = r, q, eq, log_rho, term        (trunc cold)
+// ldT is the common row stride of the hot [N,T] streams, ldX the stride of
+// values (gae, td_lambda, vtrace) or 1 if truncation flags are given
+// (retrace).  When the hot [N,T] streams do not share one stride, the
+// kUniform = false instances take every stride from Args instead.
+
+// Batches of at most this many env-steps read trunc_values as whole vectors
+// with the other loads, instead of a dependent load at truncated steps after
+// the flags arrive: at that size the kernel is latency bound and the extra
+// bytes cost less than the extra memory round trip.
+constexpr int64_t kDenseTvMaxSteps = int64_t(1) << 22;
+
 // ------------------------------------------------------------------ loads
 
 struct __attribute__((aligned(4))) F4 { float x, y, z, w; };
 struct __attribute__((aligned(4))) U4 { uint32_t x, y, z, w; };
 struct __attribute__((aligned(4))) U2 { uint32_t x, y; };
+// Four floats with 4-byte alignment, for non-temporal vector stores.
+typedef float V4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // ND consecutive dwords from a 4-byte aligned address, as dwordx4/x2/x1 loads.
 template <int ND>
@@ -241,6 +263,24 @@ __device__ __forceinline__ float lane_shuffle(float x, int src_lane) {
 
 // ------------------------------------------------------------------ kernel
 
+// Pin a value to this point of the program: nothing computed from the
+// result can be hoisted above the (empty, volatile) asm statement.  Applied
+// to kernel-argument scalars (late) and to the per-lane row index (late_v)
+// where a cold argument is first used, so that the scalar loads of the
+// argument block may be issued early but are waited for only after the
+// tile's vector loads are in flight.  Pointers are never passed through the
+// barrier, so they keep their global address space.
+template <typename V>
+__device__ __forceinline__ V late(V x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+__device__ __forceinline__ int64_t late_v(int64_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
 template <int A> struct Uses {
   static constexpr bool values = A == kGae || A == kTdLambda || A == kVtrace;  // V [N,T+1]
   static constexpr bool q = A == kRetrace;
@@ -249,11 +289,14 @@ template <int A> struct Uses {
   static constexpr bool two_outputs = A == kGae || A == kVtrace;
 };
 
+// Row pointers of the hot streams; the cold ones (outputs, and the arrays
+// marked cold above) are formed from Args at their first use (see late()).
 template <typename InT>
 struct RowPtrs {
   const InT *r, *v, *lr, *eq, *tv;
   const uint8_t *te, *tr;
-  float *o0, *o1;
+  bool has_te, has_tr, dense_tv;
+  int64_t row;  // row index used for addressing (row 0 for rows past N)
 };
 
 // A lane's raw inputs for its K steps t0 .. t0+K-1 (v and lr carry the
@@ -269,8 +312,9 @@ struct Raw {
 // loads are unconditional vector loads.  kEdge = true: the ragged last tile,
 // element-wise loads of the steps e < lim only.
 template <int A, typename InT, int K, bool kEdge>
-__device__ __forceinline__ void load_tile(const RowPtrs<InT> &rp, bool has_term, bool has_trunc,
-                                          int64_t t0, int64_t lim, Raw<K> &x) {
+__device__ __forceinline__ void load_tile(const Args &p, const RowPtrs<InT> &rp, bool has_term,
+                                          bool has_trunc, bool dense_tv, int64_t t0, int64_t lim,
+                                          Raw<K> &x) {
   using U = Uses<A>;
 #pragma unroll
   for (int j = 0; j < K; ++j) { x.r[j] = 0.f; x.v[j] = 0.f; x.lr[j] = 0.f; x.eq[j] = 0.f; x.tv[j] = 0.f; }
@@ -286,7 +330,14 @@ __device__ __forceinline__ void load_tile(const RowPtrs<InT> &rp, bool has_term,
     // waits for the flags only, with every other load of the tile in flight.
     FlagWords<K> ftr, fte;
     const uint8_t *own = reinterpret_cast<const uint8_t *>(rp.r + t0);
-    ld_flags_raw<K>(has_trunc ? rp.tr + t0 : own, ftr);
+    const uint8_t *trp = own;
+    if constexpr (A == kRetrace) {
+      // Cold stream: only a call with truncation flags waits for Args here.
+      if (has_trunc) trp = p.trunc + late_v(rp.row) * p.ld_trunc + t0;
+    } else {
+      trp = has_trunc ? rp.tr + t0 : own;
+    }
+    ld_flags_raw<K>(trp, ftr);
     ld_flags_raw<K>(has_term ? rp.te + t0 : own, fte);
     Ld<InT>::template vec<K>(rp.r + t0, x.r);
     if constexpr (U::values || U::q) {
@@ -308,6 +359,21 @@ __device__ __forceinline__ void load_tile(const RowPtrs<InT> &rp, bool has_term,
         x.lr[K] = Ld<InT>::one(rp.lr + t0 + (lim > K ? K : K - 1));
       }
     }
+    if constexpr (U::tv && A != kVtrace) {
+      // Small batches read the bootstraps as whole vectors in flight with
+      // the other loads (no dependent round trip after the flags arrive;
+      // the extra bytes cost less than the latency there).  Otherwise the
+      // lane re-reads its own rewards (a cache hit) and the bootstraps are
+      // read below at truncated steps only.
+      float tk[K];
+      Ld<InT>::template vec<K>(dense_tv ? rp.tv + t0 : rp.r + t0, tk);
+#pragma unroll
+      for (int j = 0; j < K; ++j) x.tv[j] = tk[j];
+    }
+    // Keep every load above ahead of the first use of any loaded value: the
+    // scheduler would otherwise pull the flag decoding up and wait for the
+    // flags before issuing the remaining loads.
+    __builtin_amdgcn_sched_barrier(0);
     decode_flags<K>(ftr, x.tr);
     decode_flags<K>(fte, x.te);
 #pragma unroll
@@ -316,7 +382,12 @@ __device__ __forceinline__ void load_tile(const RowPtrs<InT> &rp, bool has_term,
       x.te[i] = has_term ? x.te[i] : 0u;
     }
   } else if (lim > 0) {
-    if (has_trunc) ld_flags_part<K>(rp.tr + t0, lim, x.tr);
+    if (has_trunc) {
+      const uint8_t *trp;
+      if constexpr (A == kRetrace) trp = p.trunc + late_v(rp.row) * p.ld_trunc;
+      else trp = rp.tr;
+      ld_flags_part<K>(trp + t0, lim, x.tr);
+    }
     if (has_term) ld_flags_part<K>(rp.te + t0, lim, x.te);
     ld_part<InT, K>(rp.r + t0, lim, x.r);
     if constexpr (U::values) {
@@ -337,16 +408,26 @@ __device__ __forceinline__ void load_tile(const RowPtrs<InT> &rp, bool has_term,
   }
 
   if constexpr (U::tv) {
-    // Truncation bootstraps are read at truncated steps only (rare), never
-    // densely.  Flags of steps outside the row are zero.
+    if (!kEdge && dense_tv) return;  // already read with the other loads
+    // Read the bootstraps at truncated steps only (rare), into registers of
+    // their own (no write-after-write wait on the vector load above).  Flags
+    // of steps outside the row are zero.
     uint32_t any_tr = 0;
 #pragma unroll
     for (int i = 0; i < K / 4; ++i) any_tr |= x.tr[i];
+    float ts[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) ts[j] = 0.f;
     if (any_tr != 0) {
+      const InT *tv_row;
+      if constexpr (A == kVtrace) tv_row = static_cast<const InT *>(p.tv) + late_v(rp.row) * p.ld_tv;
+      else tv_row = rp.tv;
 #pragma unroll
       for (int j = 0; j < K; ++j)
-        if (flag<K>(x.tr, j)) x.tv[j] = Ld<InT>::one(rp.tv + t0 + j);
+        if (flag<K>(x.tr, j)) ts[j] = Ld<InT>::one(tv_row + t0 + j);
     }
+#pragma unroll
+    for (int j = 0; j < K; ++j) x.tv[j] = ts[j];
   }
 }
 
@@ -355,8 +436,11 @@ __device__ __forceinline__ void load_tile(const RowPtrs<InT> &rp, bool has_term,
 template <int A, int K, bool kEdge>
 __device__ __forceinline__ void coefficients(const Raw<K> &x, int64_t lim, const Args &p,
                                              float (&al)[K], float (&be)[K], float (&ratio)[K]) {
-  const float gamma = p.gamma;
-  const float gl = p.gamma * p.lam;
+  const float gamma = late(p.gamma);
+  const float lam = late(p.lam);
+  const float gl = gamma * lam;
+  const float rho_bar = A == kVtrace ? late(p.rho_bar) : 1.f;
+  const float c_bar = A == kVtrace || A == kRetrace ? late(p.c_bar) : 1.f;
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const bool te = flag<K>(x.te, j);
@@ -375,12 +459,12 @@ __device__ __forceinline__ void coefficients(const Raw<K> &x, int64_t lim, const
       const float e = __expf(x.lr[j]);
       ratio[j] = e;
       const float nv = te ? 0.f : (tr ? x.tv[j] : x.v[j + 1]);
-      a_j = fminf(p.rho_bar, e) * (fmaf(gamma, nv, x.r[j]) - x.v[j]);
-      b_j = done ? 0.f : gamma * (p.lam * fminf(p.c_bar, __expf(x.lr[j])));
+      a_j = fminf(rho_bar, e) * (fmaf(gamma, nv, x.r[j]) - x.v[j]);
+      b_j = done ? 0.f : gamma * (lam * fminf(c_bar, e));
     } else {  // kRetrace
       a_j = (te ? x.r[j] : fmaf(gamma, x.eq[j], x.r[j])) - x.v[j];
       const bool has_next = j + 1 < lim;  // step t+1 lies inside the row
-      const float c_next = p.lam * fminf(p.c_bar, __expf(x.lr[j + 1]));
+      const float c_next = lam * fminf(c_bar, __expf(x.lr[j + 1]));
       b_j = (done || !has_next) ? 0.f : gamma * c_next;
     }
     const bool valid = !kEdge || j < lim;
@@ -392,20 +476,20 @@ __device__ __forceinline__ void coefficients(const Raw<K> &x, int64_t lim, const
 // One tile of one row group: load, build pairs, fold, scan, carry, re-run,
 // store.  Returns the carry for the next (earlier) tile.
 template <int A, typename InT, int K, int LPR, int WPR, bool kEdge>
-__device__ __forceinline__ float do_tile(const Args &p, const RowPtrs<InT> &rp, bool row_ok,
-                                         int64_t c, bool need_carry, int g, int lane, int wave,
-                                         float carry, float2 (*s_agg)[WPR]) {
+__device__ __forceinline__ float do_tile(const Args &p, const RowPtrs<InT> &rp, int64_t T,
+                                         bool row_ok, int64_t c, bool need_carry, int g, int lane,
+                                         int wave, float carry, float2 (*s_agg)[WPR]) {
   constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
   constexpr int kTile = kGroup * K;
   constexpr int kScanLanes = WPR > 1 ? 64 : LPR;
   using U = Uses<A>;
 
   const int64_t t0 = c * kTile + static_cast<int64_t>(kGroup - 1 - g) * K;
-  int64_t lim = p.T - t0;  // steps of this lane that lie inside the row
+  int64_t lim = T - t0;  // steps of this lane that lie inside the row
   if constexpr (kEdge) lim = row_ok ? (lim > 0 ? lim : 0) : 0;
 
   Raw<K> x;
-  load_tile<A, InT, K, kEdge>(rp, p.term != nullptr, p.trunc != nullptr, t0, lim, x);
+  load_tile<A, InT, K, kEdge>(p, rp, rp.has_te, rp.has_tr, rp.dense_tv, t0, lim, x);
 
   float al[K], be[K], ratio[K];
   coefficients<A, K, kEdge>(x, lim, p, al, be, ratio);
@@ -451,6 +535,8 @@ __device__ __forceinline__ float do_tile(const Args &p, const RowPtrs<InT> &rp, 
   }
 
   // Re-run the lane's steps from its incoming value; fused epilogue.
+  const float gamma = late(p.gamma);
+  const float pg_rho_bar = A == kVtrace ? late(p.pg_rho_bar) : 1.f;
   float o0[K], o1[K];
   float xa = xin;
 #pragma unroll
@@ -470,33 +556,38 @@ __device__ __forceinline__ float do_tile(const Args &p, const RowPtrs<InT> &rp, 
       const bool te = flag<K>(x.te, j);
       const bool tr = flag<K>(x.tr, j);
       const float nvs = te ? 0.f : (tr ? x.tv[j] : x.v[j + 1] + xn);
-      o1[j] = fminf(p.pg_rho_bar, ratio[j]) * (fmaf(p.gamma, nvs, x.r[j]) - x.v[j]);
+      o1[j] = fminf(pg_rho_bar, ratio[j]) * (fmaf(gamma, nvs, x.r[j]) - x.v[j]);
     } else {  // kRetrace
       o0[j] = x.v[j] + xa;
     }
   }
 
   // One write of the outputs.
-  const bool has_o1 = U::two_outputs && p.o1 != nullptr;
+  const bool has_o1 = U::two_outputs && late(p.o1) != nullptr;
+  const int64_t orow = late_v(rp.row);
+  float *o0_row = p.o0 + orow * p.ld_o0;
+  float *o1_row = p.o1 + orow * p.ld_o1;
   if constexpr (!kEdge) {
+    // Non-temporal (streaming) dwordx4 stores: outputs are written once and
+    // not re-read by this kernel.
     if (row_ok) {
 #pragma unroll
       for (int i = 0; i < K / 4; ++i)
-        reinterpret_cast<F4 *>(rp.o0 + t0)[i] =
-            F4{o0[4 * i], o0[4 * i + 1], o0[4 * i + 2], o0[4 * i + 3]};
+        __builtin_nontemporal_store(V4{o0[4 * i], o0[4 * i + 1], o0[4 * i + 2], o0[4 * i + 3]},
+                                    reinterpret_cast<V4 *>(o0_row + t0) + i);
       if (has_o1) {
 #pragma unroll
         for (int i = 0; i < K / 4; ++i)
-          reinterpret_cast<F4 *>(rp.o1 + t0)[i] =
-              F4{o1[4 * i], o1[4 * i + 1], o1[4 * i + 2], o1[4 * i + 3]};
+          __builtin_nontemporal_store(V4{o1[4 * i], o1[4 * i + 1], o1[4 * i + 2], o1[4 * i + 3]},
+                                      reinterpret_cast<V4 *>(o1_row + t0) + i);
       }
     }
   } else {
 #pragma unroll
     for (int e = 0; e < K; ++e)
       if (e < lim) {
-        rp.o0[t0 + e] = o0[e];
-        if (has_o1) rp.o1[t0 + e] = o1[e];
+        o0_row[t0 + e] = o0[e];
+        if (has_o1) o1_row[t0 + e] = o1[e];
       }
   }
   return carry_out;
@@ -505,9 +596,12 @@ __device__ __forceinline__ float do_tile(const Args &p, const RowPtrs<InT> &rp, 
 // Algo A, input type InT, K steps per lane, LPR lanes per row inside one
 // wavefront (WPR == 1), or WPR wavefronts per row (then LPR must be 64).
 // Workgroup: 256 threads (WPR == 1) or 64*WPR threads (WPR > 1).
-template <int A, typename InT, int K, int LPR, int WPR>
+// h0..h4, N32, T32, ldT, ldX: the preloaded hot arguments (see above); they
+// duplicate fields of p.
+template <int A, typename InT, int K, int LPR, int WPR, bool kUniform>
 __global__ void __launch_bounds__(WPR > 1 ? 64 * WPR : 256)
-scan_kernel(const Args p) {
+scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
+            int N32, int T32, int ldT, int ldX, const Args p) {
   static_assert(WPR == 1 || LPR == 64, "multi-wavefront rows use whole wavefronts");
   constexpr int kWaves = WPR > 1 ? WPR : 4;
   constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
@@ -528,33 +622,77 @@ scan_kernel(const Args p) {
   }
   // Rows past N (last workgroup only) read row 0 and store nothing; their
   // lanes stay active because the DPP scan reads every lane of a group.
-  const bool row_ok = row < p.N;
+  const bool row_ok = row < N32;
   const int64_t rr = row_ok ? row : 0;
+  const int64_t T = T32;
+  // Row stride of a hot stream: the preloaded common stride, or (mixed
+  // strides) the stream's own stride from Args.
+  auto ld = [&](int64_t own_ld) -> int64_t { return kUniform ? static_cast<int64_t>(ldT) : own_ld; };
+  auto in_row = [rr](const void *base, int64_t stride) {
+    return static_cast<const InT *>(base) + rr * stride;
+  };
+  auto flag_row = [rr](const void *base, int64_t stride) {
+    return static_cast<const uint8_t *>(base) + rr * stride;
+  };
 
   RowPtrs<InT> rp;
-  rp.r = static_cast<const InT *>(p.r) + rr * p.ld_r;
-  rp.v = static_cast<const InT *>(p.v) + rr * p.ld_v;
-  rp.lr = static_cast<const InT *>(p.lr) + rr * p.ld_lr;
-  rp.eq = static_cast<const InT *>(p.eq) + rr * p.ld_eq;
-  rp.tv = static_cast<const InT *>(p.tv) + rr * p.ld_tv;
-  rp.te = p.term + rr * p.ld_term;
-  rp.tr = p.trunc + rr * p.ld_trunc;
-  rp.o0 = p.o0 + rr * p.ld_o0;
-  rp.o1 = p.o1 + rr * p.ld_o1;
+  rp.row = rr;
+  rp.r = in_row(h0, ld(p.ld_r));
+  rp.tv = nullptr;
+  if constexpr (A == kReturns) {
+    rp.te = flag_row(h1, ld(p.ld_term));
+    rp.tr = flag_row(h2, ld(p.ld_trunc));
+    rp.tv = in_row(h3, ld(p.ld_tv));
+    rp.has_te = h1 != nullptr;
+    rp.has_tr = h2 != nullptr;
+    rp.dense_tv = h3 != nullptr && static_cast<int64_t>(N32) * T <= kDenseTvMaxSteps;
+  } else if constexpr (A == kGae || A == kTdLambda) {
+    rp.v = in_row(h1, kUniform ? static_cast<int64_t>(ldX) : p.ld_v);
+    rp.te = flag_row(h2, ld(p.ld_term));
+    rp.tr = flag_row(h3, ld(p.ld_trunc));
+    rp.tv = in_row(h4, ld(p.ld_tv));
+    rp.has_te = h2 != nullptr;
+    rp.has_tr = h3 != nullptr;
+    rp.dense_tv = h4 != nullptr && static_cast<int64_t>(N32) * T <= kDenseTvMaxSteps;
+  } else if constexpr (A == kVtrace) {
+    rp.v = in_row(h1, kUniform ? static_cast<int64_t>(ldX) : p.ld_v);
+    rp.lr = in_row(h2, ld(p.ld_lr));
+    rp.te = flag_row(h3, ld(p.ld_term));
+    rp.tr = flag_row(h4, ld(p.ld_trunc));
+    rp.has_te = h3 != nullptr;
+    rp.has_tr = h4 != nullptr;
+    rp.dense_tv = false;
+  } else {  // kRetrace
+    rp.v = in_row(h1, ld(p.ld_v));
+    rp.eq = in_row(h2, ld(p.ld_eq));
+    rp.lr = in_row(h3, ld(p.ld_lr));
+    rp.te = flag_row(h4, ld(p.ld_term));
+    rp.tr = nullptr;
+    rp.has_te = h4 != nullptr;
+    rp.has_tr = ldX != 0;
+    rp.dense_tv = false;
+  }
 
   float carry = 0.f;  // A at the end of the current tile (A_T for the last)
   if constexpr (A == kReturns) {
-    if (p.boot != nullptr) carry = Ld<InT>::one(static_cast<const InT *>(p.boot) + rr);
+    if (h4 != nullptr) carry = Ld<InT>::one(static_cast<const InT *>(h4) + rr);
   }
 
-  const int64_t ntiles = (p.T + kTile - 1) / kTile;
+  const int64_t ntiles = (T + kTile - 1) / kTile;
+  if (ntiles == 1 && T == kTile) {
+    // One whole tile: straight-line code, no loop-carried waits.
+    do_tile<A, InT, K, LPR, WPR, false>(p, rp, T, row_ok, 0, false, g, lane, wave, carry, s_agg);
+    return;
+  }
   int64_t c = ntiles - 1;
-  if (p.T % kTile != 0) {
-    carry = do_tile<A, InT, K, LPR, WPR, true>(p, rp, row_ok, c, c > 0, g, lane, wave, carry, s_agg);
+  if (T % kTile != 0) {
+    carry = do_tile<A, InT, K, LPR, WPR, true>(p, rp, T, row_ok, c, c > 0, g, lane, wave, carry,
+                                               s_agg);
     --c;
   }
   for (; c >= 0; --c)
-    carry = do_tile<A, InT, K, LPR, WPR, false>(p, rp, row_ok, c, c > 0, g, lane, wave, carry, s_agg);
+    carry = do_tile<A, InT, K, LPR, WPR, false>(p, rp, T, row_ok, c, c > 0, g, lane, wave, carry,
+                                                s_agg);
 }
 
 }  // namespace rlca

@@ -102,7 +102,10 @@ def test_empty_inputs_are_ok_without_launch(lib):
     (dict(gamma=math.nan), rl.RLCA_EINVAL, "gamma"),
     (dict(lam=math.nan), rl.RLCA_EINVAL, "lam"),
     (dict(lam=1.01), rl.RLCA_EINVAL, "lam"),
-    (dict(ld_r=2 ** 62), rl.RLCA_EINVAL, "overflow"),
+    (dict(ld_r=2 ** 31), rl.RLCA_EINVAL, "exceeds 2^31-1"),
+    (dict(N=2 ** 31 - 1, ld_r=2 ** 31 - 1, ld_v=2 ** 31 - 1, ld_f=2 ** 31 - 1,
+          ld_a=2 ** 31 - 1, ld_g=2 ** 31 - 1), rl.RLCA_EINVAL, "overflow"),
+    (dict(T=2 ** 31 - 1), rl.RLCA_EINVAL, "2^31-2"),
 ])
 def test_gae_rejects_bad_arguments(lib, kw, status, needle):
     assert gae(lib, **kw) == status
