@@ -53,6 +53,11 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="launch each step from Python instead of replaying a HIP graph")
     ap.add_argument("--variant", type=int, default=-1, help="force a tiling variant")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip timing a plain copy kernel of the same byte count")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "script into profiles/traffic.json, then exit")
     return ap.parse_args()
 
 
@@ -75,8 +80,73 @@ def algorithmic_bytes(w, N, T):
     raise ValueError(w.algo)
 
 
+def launches_per_step_of(w):
+    return 2 if w.algo == "vtrace+retrace" else 1
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """Per-launch HBM traffic of each kernel from two rocprofv3 --pmc runs of
+    `bench.py --no-graph` (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+    scaled by the counter reading of the known-size copy kernel in the same
+    runs.  Writes profiles/traffic.json keyed by workload."""
+    import csv
+    import glob
+    import statistics
+
+    def per_kernel(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit("no counter_collection.csv under %s" % d)
+        vals = {}
+        for f in files:
+            for row in csv.DictReader(open(f)):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (row["Kernel_Name"], row["Grid_Size"])
+                vals.setdefault(key, []).append(float(row["Counter_Value"]))
+        return {k: statistics.median(v) for k, v in vals.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+    meta_path = os.path.join(fetch_dir, "bench_meta.json")
+    with open(meta_path) as f:
+        meta = json.load(f)
+    half = meta["copy_bytes_per_launch"] / 2
+    # The calibration copy: the runtime's copy kernel whose dispatches write
+    # exactly the known size (input uploads use the same kernel name).
+    copies = [k for k in write if "copyBuffer" in k[0] and abs(write[k] * 1024 - half) < 0.01 * half]
+    scan_name = [k for k in fetch if "scan_kernel" in k[0]]
+    if len(copies) != 1 or not scan_name:
+        raise SystemExit("expected one calibration copy and the scan kernel(s): %s" % list(write))
+    cn = copies[0]
+    f_scale = half / (fetch[cn] * 1024.0)
+    w_scale = half / (write[cn] * 1024.0)
+    traffic = sum(fetch[k] * 1024.0 * f_scale + write[k] * 1024.0 * w_scale for k in scan_name)
+    traffic /= len(scan_name)
+    out = {}
+    if os.path.exists(TRAFFIC_FILE):
+        out = json.load(open(TRAFFIC_FILE))
+    out[meta["workload"]] = {
+        "kernel_source_hash": kernel_source_hash(),
+        "bytes_per_launch": traffic,
+        "fetch_kib_per_launch": {"%s [grid %s]" % k: fetch[k] for k in scan_name},
+        "write_kib_per_launch": {"%s [grid %s]" % k: write[k] for k in scan_name},
+        "copy_kernel": "%s [grid %s]" % cn,
+        "copy_fetch_kib": fetch[cn], "copy_write_kib": write[cn],
+        "copy_bytes_read": half, "copy_bytes_written": half,
+        "fetch_scale": f_scale, "write_scale": w_scale,
+        "algorithmic_bytes_per_launch": meta["algorithmic_bytes_per_launch"],
+    }
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out[meta["workload"]], indent=1))
+
+
 def main():
     args = parse()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only; multi-GPU runs are not part of this "
               "library (rows shard across GPUs with no communication)", file=sys.stderr)
@@ -204,7 +274,49 @@ def main():
         timing = "HIP graph replay of K launches"
     elapsed_ms = start.elapsed_time(end)
     ms_per_step = elapsed_ms / K
-    launches_per_step = 2 if w.algo == "vtrace+retrace" else 1
+
+    # ---- practical ceiling: a plain copy kernel (torch's) moving the same
+    # number of bytes (half read, half written), timed the same way.  Under
+    # --no-graph it also serves as the known-size calibration kernel of the
+    # counter runs (see --summarize-pmc).
+    copy = None
+    if not args.no_copy_ceiling:
+        half = algorithmic_bytes(w, N, T) // launches_per_step_of(w) // 2 // 16 * 16
+        RC = max(2, int(np.ceil(args.rotate_mb * 2 ** 20 / (2 * half))))
+        bufs = [(torch.empty(half // 4, dtype=torch.float32, device=dev),
+                 torch.empty(half // 4, dtype=torch.float32, device=dev)) for _ in range(RC)]
+        for a, _ in bufs:
+            a.fill_(1.0)
+        KC = min(K, 1000)
+        if args.no_graph:
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            for i in range(KC):
+                bufs[i % RC][1].copy_(bufs[i % RC][0])
+            c1.record(stream)
+        else:
+            gc = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream(dev)
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                with torch.cuda.graph(gc, stream=cap):
+                    for i in range(KC):
+                        bufs[i % RC][1].copy_(bufs[i % RC][0])
+            torch.cuda.synchronize()
+            gc.replay()
+            torch.cuda.synchronize()
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            gc.replay()
+            c1.record(stream)
+        torch.cuda.synchronize()
+        cus = c0.elapsed_time(c1) * 1e3 / KC
+        copy = {"bytes_per_launch": 2 * half, "avg_launch_us": cus,
+                "GBps": 2 * half / (cus * 1e-6) / 1e9, "kernel": "torch copy_ (float32)"}
+        del bufs
+    launches_per_step = launches_per_step_of(w)
     env_steps = N * T
     value = env_steps / (ms_per_step * 1e-3)
     bytes_per_step = algorithmic_bytes(w, N, T)
@@ -255,8 +367,16 @@ def main():
                "sample": "the whole %dx%d batch, %d repetitions (%.1f s), single-threaded "
                          "fp64 C oracle" % (N, T, reps, cpu_s)}
 
+    meta_dir = os.environ.get("RLCA_BENCH_META_DIR")
+    if meta_dir:
+        os.makedirs(meta_dir, exist_ok=True)
+        with open(os.path.join(meta_dir, "bench_meta.json"), "w") as f:
+            json.dump({"workload": w.name, "algorithmic_bytes_per_launch":
+                       bytes_per_step / launches_per_step,
+                       "copy_bytes_per_launch": copy["bytes_per_launch"] if copy else None}, f)
+
     out = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "gae_4096x128" else "env-steps/sec, %s" % w.name,
         "value": value,
         "unit": "env-steps/s",
         "n_gpus": 1,
@@ -277,6 +397,7 @@ def main():
                      "algorithmic_bytes_per_launch": bytes_per_step / launches_per_step,
                      "avg_launch_us": ms_per_step * 1e3 / launches_per_step},
         "cpu_baseline": cpu,
+        "copy_ceiling": copy,
         "parity_max_rel_err": parity,
     }
     print(json.dumps(out), flush=True)

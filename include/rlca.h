@@ -203,20 +203,23 @@ int rlca_version(void);
 
 /*
  * Tiling variants.  A variant fixes how many consecutive steps each lane
- * owns (K), how many lanes share one row within a wavefront, and how many
- * wavefronts cooperate on one row.  By default each call picks one from
- * (num_envs, T).  rlca_set_variant(v) forces variant v (0 <= v <
- * rlca_num_variants()) for later calls on the calling thread, or restores
- * the automatic choice with v = -1; it returns the previous setting, or -2
- * for an unknown v (setting unchanged).  Every variant computes the same
- * results up to rounding order.  rlca_variant_info writes K, lanes per row
- * and wavefronts per row of variant v and returns RLCA_OK, or RLCA_EINVAL for
- * an unknown v.  rlca_last_variant() is the variant the calling thread's
- * last successful launch used (-1 if none).
+ * owns (one 16-byte vector of every input array: 4 fp32 or 8 bf16 steps),
+ * how many lanes share one row within a wavefront, and how many wavefronts
+ * cooperate on one row; rows longer than a tile are processed tile by tile.
+ * By default each call picks one from (num_envs, T, dtype).
+ * rlca_set_variant(v) forces variant v (0 <= v < rlca_num_variants()) for
+ * later calls on the calling thread, or restores the automatic choice with
+ * v = -1; it returns the previous setting, or -2 for an unknown v (setting
+ * unchanged).  Every variant computes the same results up to rounding order.
+ * rlca_variant_info writes the steps per lane (for `dtype`), the number of
+ * lanes that share one row (tile = steps per lane x lanes per row) and the
+ * wavefronts per row of variant v and returns RLCA_OK, or RLCA_EINVAL /
+ * RLCA_EDTYPE.  rlca_last_variant() is the variant the calling thread's last
+ * successful launch used (-1 if none).
  */
 int rlca_num_variants(void);
 int rlca_set_variant(int variant);
-int rlca_variant_info(int variant, int *steps_per_lane, int *lanes_per_row,
+int rlca_variant_info(int variant, int dtype, int *steps_per_lane, int *lanes_per_row,
                       int *waves_per_row);
 int rlca_last_variant(void);
 

@@ -39,7 +39,7 @@ _SIGNATURES = {
     "rlca_version": [],
     "rlca_num_variants": [],
     "rlca_set_variant": [_int],
-    "rlca_variant_info": [_int, ctypes.POINTER(_int), ctypes.POINTER(_int),
+    "rlca_variant_info": [_int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
                           ctypes.POINTER(_int)],
     "rlca_last_variant": [],
 }
@@ -257,11 +257,13 @@ def rlca_set_variant(variant):
     return prev
 
 
-def rlca_variant_info(variant):
-    """(steps_per_lane, lanes_per_row, waves_per_row) of a tiling variant."""
+def rlca_variant_info(variant, dtype=torch.float32):
+    """(steps_per_lane, lanes_per_row, waves_per_row) of a tiling variant for
+    inputs of ``dtype`` (torch.float32 or torch.bfloat16)."""
+    code = RLCA_BF16 if dtype in (torch.bfloat16, RLCA_BF16, "bf16") else RLCA_F32
     k, l, w = _int(), _int(), _int()
-    _check(load_library().rlca_variant_info(int(variant), ctypes.byref(k), ctypes.byref(l),
-                                            ctypes.byref(w)))
+    _check(load_library().rlca_variant_info(int(variant), code, ctypes.byref(k),
+                                            ctypes.byref(l), ctypes.byref(w)))
     return k.value, l.value, w.value
 
 

@@ -23,25 +23,40 @@ namespace {
 // ------------------------------------------------------------- variants
 
 struct Variant {
-  int K;    // consecutive steps per lane
+  int KU;   // 16-byte input vectors per lane and array: K = KU * 16 / sizeof(input)
   int LPR;  // lanes per row inside a wavefront (64 when WPR > 1)
   int WPR;  // wavefronts per row
 };
 
+// One 16-byte vector per lane and input array (K = 4 fp32 or 8 bf16 steps):
+// a wavefront's dwordx4 load then covers one contiguous 1 KB span, every
+// cache line it touches is used in full.  (Longer spans per lane split each
+// load into strided quarter-lines and cost 4x the cache-line requests.)
 constexpr Variant kVariants[] = {
-    {4, 16, 1},    // 0: tile   64, 16 rows per 256-thread workgroup
-    {4, 32, 1},    // 1: tile  128,  8 rows per workgroup
-    {4, 64, 1},    // 2: tile  256,  4 rows per workgroup
-    {16, 64, 1},   // 3: tile 1024,  4 rows per workgroup
-    {16, 64, 4},   // 4: tile 4096,  1 row per 256-thread workgroup
-    {16, 64, 16},  // 5: tile 16384, 1 row per 1024-thread workgroup
+    {1, 16, 1},   // 0: tile 16K steps, 16 rows per 256-thread workgroup
+    {1, 32, 1},   // 1: tile 32K,  8 rows per workgroup
+    {1, 64, 1},   // 2: tile 64K,  4 rows per workgroup
+    {1, 64, 4},   // 3: tile 256K, 1 row per 256-thread workgroup
+    {1, 64, 8},   // 4: tile 512K, 1 row per 512-thread workgroup
+    {1, 64, 16},  // 5: tile 1024K, 1 row per 1024-thread workgroup
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+
+template <typename InT>
+constexpr int steps_per_lane(const Variant &v) {
+  return v.KU * 16 / static_cast<int>(sizeof(InT));
+}
+
+int64_t tile_steps(const Variant &v, int dtype) {
+  const int k = dtype == RLCA_BF16 ? steps_per_lane<bf16_t>(v) : steps_per_lane<float>(v);
+  return static_cast<int64_t>(k) * v.LPR * v.WPR;
+}
 
 template <int A, typename InT, int V, bool U>
 const void *kernel_for() {
   constexpr Variant v = kVariants[V];
-  return reinterpret_cast<const void *>(&scan_kernel<A, InT, v.K, v.LPR, v.WPR, U>);
+  return reinterpret_cast<const void *>(
+      &scan_kernel<A, InT, steps_per_lane<InT>(v), v.LPR, v.WPR, U>);
 }
 
 template <int A, typename InT, bool U>
@@ -73,17 +88,19 @@ const void *kernel_for(int algo, int dtype, int v, bool uniform) {
   }
 }
 
-// Default tiling: the shortest tile that covers T for short rows; for long
-// rows, one wavefront per row when there are enough rows to fill the chip
-// (>= 2048 rows = 8 wavefronts per CU on 256 CUs), else several cooperating
-// wavefronts per row.
-int auto_variant(int64_t N, int64_t T) {
-  if (T <= 64) return 0;
-  if (T <= 128) return 1;
-  if (T <= 256) return 2;
-  if (T <= 1024 || N >= 2048) return 3;
-  if (T <= 4096 || N >= 512) return 4;
-  return 5;
+// Default tiling (measured on MI355X).  Short rows: the smallest
+// one-wavefront tile that covers T.  Long rows: about 8192 wavefronts in
+// flight (32 per CU) -- the most wavefronts per row such that N * WPR stays
+// within that and the tile is not longer than the row; from 4096 rows on,
+// one wavefront per row looping over tiles already supplies them.
+int auto_variant(int64_t N, int64_t T, int dtype) {
+  constexpr int64_t kTargetWaves = 8192;
+  for (int v = 0; v <= 2; ++v)
+    if (T <= tile_steps(kVariants[v], dtype)) return v;
+  if (N >= kTargetWaves / 2) return 2;
+  for (int v = kNumVariants - 1; v >= 3; --v)
+    if (N * kVariants[v].WPR <= kTargetWaves && tile_steps(kVariants[v], dtype) <= T) return v;
+  return tile_steps(kVariants[3], dtype) <= T ? 3 : 2;
 }
 
 // ------------------------------------------------------------- errors
@@ -187,7 +204,7 @@ int check_sizes(int64_t N, int64_t T, int dtype) {
   } while (0)
 
 int launch(int algo, int dtype, const Args &args, void *stream) {
-  const int v = t_forced_variant >= 0 ? t_forced_variant : auto_variant(args.N, args.T);
+  const int v = t_forced_variant >= 0 ? t_forced_variant : auto_variant(args.N, args.T, dtype);
   const Variant var = kVariants[v];
   dim3 grid, block;
   if (var.WPR > 1) {
@@ -445,11 +462,14 @@ int rlca_set_variant(int variant) {
   return prev;
 }
 
-int rlca_variant_info(int variant, int *steps_per_lane, int *lanes_per_row, int *waves_per_row) {
+int rlca_variant_info(int variant, int dtype, int *steps_per_lane_out, int *lanes_per_row,
+                      int *waves_per_row) {
   if (variant < 0 || variant >= kNumVariants)
     return fail(RLCA_EINVAL, "unknown variant %d", variant);
+  if (dtype != RLCA_F32 && dtype != RLCA_BF16) return fail(RLCA_EDTYPE, "unknown dtype %d", dtype);
   const Variant v = kVariants[variant];
-  if (steps_per_lane) *steps_per_lane = v.K;
+  if (steps_per_lane_out)
+    *steps_per_lane_out = dtype == RLCA_BF16 ? steps_per_lane<bf16_t>(v) : steps_per_lane<float>(v);
   if (lanes_per_row) *lanes_per_row = v.WPR > 1 ? 64 * v.WPR : v.LPR;
   if (waves_per_row) *waves_per_row = v.WPR;
   return RLCA_OK;

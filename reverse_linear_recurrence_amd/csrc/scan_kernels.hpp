@@ -90,7 +90,10 @@ struct Args {
 // with the other loads, instead of a dependent load at truncated steps after
 // the flags arrive: at that size the kernel is latency bound and the extra
 // bytes cost less than the extra memory round trip.
-constexpr int64_t kDenseTvMaxSteps = int64_t(1) << 22;
+#ifndef RLCA_DENSE_TV_MAX_STEPS
+#define RLCA_DENSE_TV_MAX_STEPS (int64_t(1) << 20)
+#endif
+constexpr int64_t kDenseTvMaxSteps = RLCA_DENSE_TV_MAX_STEPS;
 
 // ------------------------------------------------------------------ loads
 

@@ -41,8 +41,11 @@ def test_version_and_variants(lib):
     assert nv >= 6
     for v in range(nv):
         k, lpr, wpr = rl.rlca_variant_info(v)
-        assert k % 4 == 0 and lpr in (16, 32, 64) or lpr % 64 == 0
-        assert wpr >= 1
+        kb, lprb, wprb = rl.rlca_variant_info(v, torch.bfloat16)
+        assert k * 4 == kb * 2 == 16  # one 16-byte vector per lane and array
+        assert (lpr, wpr) == (lprb, wprb)
+        # lanes that share a row: part of a wavefront, or whole wavefronts
+        assert (wpr == 1 and lpr in (16, 32, 64)) or lpr == 64 * wpr
     with pytest.raises(rl.RlcaError):
         rl.rlca_variant_info(nv)
     assert rl.rlca_set_variant(2) == -1

@@ -48,8 +48,8 @@ def test_workload_full_size(name):
         print(name, algo, "variant", rl.rlca_last_variant(), "rel err", errs, flush=True)
 
 
-def variant_lengths(v):
-    k, lanes, _ = rl.rlca_variant_info(v)
+def variant_lengths(v, dtype="f32"):
+    k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32)
     tile = k * lanes
     return sorted({1, 2, 5, tile // 2 + 3, tile - 4, tile, tile + 4, 2 * tile + 12})
 
@@ -60,7 +60,7 @@ def test_every_variant_ragged_lengths(algo, dtype):
     p = params32(DEFAULT_PARAMS)
     N = 37  # not a multiple of any workgroup's row count
     for v in range(rl.rlca_num_variants()):
-        for T in variant_lengths(v):
+        for T in variant_lengths(v, dtype):
             seed = 1000 * v + T
             host = random_inputs(algo, N, T, seed, dtype)
             dev = to_device(host)
