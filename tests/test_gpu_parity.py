@@ -264,3 +264,23 @@ def test_window_end_bootstrap_counted_once_bitwise():
     r, v = host["rewards"].double().numpy(), host["values"].double().numpy()
     expect = r[:, -1] + p["gamma"] * v[:, -1] - v[:, -2]
     assert np.max(np.abs(got["advantages"][:, -1] - expect)) <= 1e-5 * np.max(np.abs(expect))
+
+
+@pytest.mark.parametrize("algo", ["returns", "gae", "td_lambda", "vtrace"])
+def test_sparse_truncation_bootstraps_large_batch(algo):
+    # Above 1M env-steps the kernels read trunc_values only at truncated
+    # steps (below, as whole vectors).  Dense truncations, fp32, every
+    # long-row tiling, against the oracle; the unused entries hold NaN.
+    p = params32(DEFAULT_PARAMS)
+    N, T = 1100, 1024
+    host = random_inputs(algo, N, T, 606, "f32", p_term=0.01, p_trunc=0.02)
+    tv = host["trunc_values"].clone()
+    keep = (host["truncated"] != 0) & (host["terminated"] == 0)
+    tv[~keep] = float("nan")
+    host["trunc_values"] = tv
+    ref = run_oracle(algo, host, p)
+    dev = to_device(host)
+    for v in (None, 2, 3, 4):
+        rl.rlca_set_variant(-1 if v is None else v)
+        print(algo, "variant", v, flush=True)
+        assert_close(run_gpu(algo, dev, p), ref, TOL["f32"], "%s/v%s" % (algo, v))
