@@ -202,10 +202,10 @@ const char *rlca_last_error(void);
 int rlca_version(void);
 
 /*
- * Tiling variants.  A variant fixes how many consecutive steps each lane
- * owns (one 16-byte vector of every input array: 4 fp32 or 8 bf16 steps),
- * how many lanes share one row within a wavefront, and how many wavefronts
- * cooperate on one row; rows longer than a tile are processed tile by tile.
+ * Tiling variants.  Each lane owns 4 consecutive steps (one 16-byte vector of
+ * every fp32 array and of every output).  A variant fixes how many lanes
+ * share one row within a wavefront and how many wavefronts cooperate on one
+ * row; rows longer than a tile are processed tile by tile.
  * By default each call picks one from (num_envs, T, dtype).
  * rlca_set_variant(v) forces variant v (0 <= v < rlca_num_variants()) for
  * later calls on the calling thread, or restores the automatic choice with

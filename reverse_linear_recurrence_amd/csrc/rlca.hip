@@ -23,40 +23,36 @@ namespace {
 // ------------------------------------------------------------- variants
 
 struct Variant {
-  int KU;   // 16-byte input vectors per lane and array: K = KU * 16 / sizeof(input)
   int LPR;  // lanes per row inside a wavefront (64 when WPR > 1)
   int WPR;  // wavefronts per row
 };
 
-// One 16-byte vector per lane and input array (K = 4 fp32 or 8 bf16 steps):
-// a wavefront's dwordx4 load then covers one contiguous 1 KB span, every
-// cache line it touches is used in full.  (Longer spans per lane split each
-// load into strided quarter-lines and cost 4x the cache-line requests.)
+// Every lane owns K = 4 consecutive steps: one 16-byte vector of each fp32
+// array (an 8-byte vector of each bf16 array) and one 16-byte vector of each
+// fp32 output, so every load and store instruction of a wavefront covers one
+// contiguous span and uses each cache line it touches in full.  (Longer spans
+// per lane split each instruction into strided partial lines: 4x the line
+// requests for 16 fp32 steps per lane, and partial-line output writes for 8
+// bf16 steps per lane.)
+constexpr int kStepsPerLane = 4;
 constexpr Variant kVariants[] = {
-    {1, 16, 1},   // 0: tile 16K steps, 16 rows per 256-thread workgroup
-    {1, 32, 1},   // 1: tile 32K,  8 rows per workgroup
-    {1, 64, 1},   // 2: tile 64K,  4 rows per workgroup
-    {1, 64, 4},   // 3: tile 256K, 1 row per 256-thread workgroup
-    {1, 64, 8},   // 4: tile 512K, 1 row per 512-thread workgroup
-    {1, 64, 16},  // 5: tile 1024K, 1 row per 1024-thread workgroup
+    {16, 1},  // 0: tile    64 steps, 16 rows per 256-thread workgroup
+    {32, 1},  // 1: tile   128,  8 rows per workgroup
+    {64, 1},  // 2: tile   256,  4 rows per workgroup
+    {64, 4},  // 3: tile  1024,  1 row per 256-thread workgroup
+    {64, 8},  // 4: tile  2048,  1 row per 512-thread workgroup
+    {64, 16}, // 5: tile  4096,  1 row per 1024-thread workgroup
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-template <typename InT>
-constexpr int steps_per_lane(const Variant &v) {
-  return v.KU * 16 / static_cast<int>(sizeof(InT));
-}
-
-int64_t tile_steps(const Variant &v, int dtype) {
-  const int k = dtype == RLCA_BF16 ? steps_per_lane<bf16_t>(v) : steps_per_lane<float>(v);
-  return static_cast<int64_t>(k) * v.LPR * v.WPR;
+int64_t tile_steps(const Variant &v, int /*dtype*/) {
+  return static_cast<int64_t>(kStepsPerLane) * v.LPR * v.WPR;
 }
 
 template <int A, typename InT, int V, bool U>
 const void *kernel_for() {
   constexpr Variant v = kVariants[V];
-  return reinterpret_cast<const void *>(
-      &scan_kernel<A, InT, steps_per_lane<InT>(v), v.LPR, v.WPR, U>);
+  return reinterpret_cast<const void *>(&scan_kernel<A, InT, kStepsPerLane, v.LPR, v.WPR, U>);
 }
 
 template <int A, typename InT, bool U>
@@ -89,15 +85,16 @@ const void *kernel_for(int algo, int dtype, int v, bool uniform) {
 }
 
 // Default tiling (measured on MI355X).  Short rows: the smallest
-// one-wavefront tile that covers T.  Long rows: about 8192 wavefronts in
-// flight (32 per CU) -- the most wavefronts per row such that N * WPR stays
-// within that and the tile is not longer than the row; from 4096 rows on,
-// one wavefront per row looping over tiles already supplies them.
+// one-wavefront tile that covers T.  Long rows (tiles loop along T, each
+// tile's loads issued while the previous one is computed): about 4096
+// wavefronts (16 per CU) -- the most wavefronts per row such that N * WPR
+// stays within that and the tile is not longer than the row; from 8192 rows
+// on, one wavefront per row.
 int auto_variant(int64_t N, int64_t T, int dtype) {
-  constexpr int64_t kTargetWaves = 8192;
+  constexpr int64_t kTargetWaves = 4096;
   for (int v = 0; v <= 2; ++v)
     if (T <= tile_steps(kVariants[v], dtype)) return v;
-  if (N >= kTargetWaves / 2) return 2;
+  if (N >= 2 * kTargetWaves) return 2;
   for (int v = kNumVariants - 1; v >= 3; --v)
     if (N * kVariants[v].WPR <= kTargetWaves && tile_steps(kVariants[v], dtype) <= T) return v;
   return tile_steps(kVariants[3], dtype) <= T ? 3 : 2;
@@ -468,8 +465,7 @@ int rlca_variant_info(int variant, int dtype, int *steps_per_lane_out, int *lane
     return fail(RLCA_EINVAL, "unknown variant %d", variant);
   if (dtype != RLCA_F32 && dtype != RLCA_BF16) return fail(RLCA_EDTYPE, "unknown dtype %d", dtype);
   const Variant v = kVariants[variant];
-  if (steps_per_lane_out)
-    *steps_per_lane_out = dtype == RLCA_BF16 ? steps_per_lane<bf16_t>(v) : steps_per_lane<float>(v);
+  if (steps_per_lane_out) *steps_per_lane_out = kStepsPerLane;
   if (lanes_per_row) *lanes_per_row = v.WPR > 1 ? 64 * v.WPR : v.LPR;
   if (waves_per_row) *waves_per_row = v.WPR;
   return RLCA_OK;

@@ -302,96 +302,170 @@ struct RowPtrs {
   int64_t row;  // row index used for addressing (row 0 for rows past N)
 };
 
-// A lane's raw inputs for its K steps t0 .. t0+K-1 (v and lr carry the
-// step-(t0+K) neighbour in slot K; v holds q_taken for Retrace).
+// A lane's inputs for its K steps t0 .. t0+K-1.  issue_tile (or load_edge)
+// fills the loaded fields; finish_tile adds the decoded flags and the
+// sparse bootstraps as new fields, never copying a loaded value, so the
+// arithmetic reads the load destinations in place and a tile's loads can be
+// in flight while the previous tile is computed.  v and lr carry the
+// step-(t0+K) neighbour in slot K; v holds q_taken for Retrace.
 template <int K>
-struct Raw {
+struct Tile {
+  // as loaded
+  FlagWords<K> ftr, fte;
   float r[K], v[K + 1], lr[K + 1], eq[K], tv[K];
-  uint32_t te[K / 4], tr[K / 4];
+  // derived
+  uint32_t te[K / 4], tr[K / 4];  // one byte per step, nonzero = flag set
+  float ts[K];                    // bootstraps read at truncated steps (Bits<> form)
+  bool dense;                     // tv[] holds the bootstraps (else ts[])
 };
 
-// One read of the raw rollout for a lane (Method 2: on-chip construction).
-// kEdge = false: every lane of the tile lies inside its row (lim >= K), the
-// loads are unconditional vector loads.  kEdge = true: the ragged last tile,
-// element-wise loads of the steps e < lim only.
-template <int A, typename InT, int K, bool kEdge>
-__device__ __forceinline__ void load_tile(const Args &p, const RowPtrs<InT> &rp, bool has_term,
-                                          bool has_trunc, bool dense_tv, int64_t t0, int64_t lim,
-                                          Raw<K> &x) {
+// One input element as loaded, widened to a float only at its use (a
+// conversion right after the load would wait for it inside the branch).
+// bf16 keeps its 16 bits zero-extended in a float register.
+template <typename InT> struct Bits;
+template <> struct Bits<float> {
+  static __device__ __forceinline__ float load(const float *p) { return *p; }
+  static __device__ __forceinline__ float to_float(float b) { return b; }
+};
+template <> struct Bits<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t *p) {
+    return __uint_as_float(static_cast<uint32_t>(*p));
+  }
+  static __device__ __forceinline__ float to_float(float b) {
+    return __uint_as_float(__float_as_uint(b) << 16);
+  }
+};
+
+// The truncation bootstrap of step j; read only where step j is truncated.
+template <typename InT, int K>
+__device__ __forceinline__ float tv_at(const Tile<K> &x, int j) {
+  return x.dense ? x.tv[j] : Bits<InT>::to_float(x.ts[j]);
+}
+
+// One read of the raw rollout for a lane of a whole tile (Method 2: on-chip
+// construction): unconditional vector loads, all issued before any use.
+template <int A, typename InT, int K>
+__device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
+                                           int64_t lim, Tile<K> &q) {
+  using U = Uses<A>;
+#pragma unroll
+  for (int j = 0; j < K; ++j) { q.v[j] = 0.f; q.lr[j] = 0.f; q.eq[j] = 0.f; q.tv[j] = 0.f; }
+  q.v[K] = 0.f;
+  q.lr[K] = 0.f;
+  // Flags first, with no branch: a missing flag array is replaced by the
+  // lane's own reward bytes (the address of its reward load, so a cache hit)
+  // and masked to zero after decoding.  The truncation test in finish_tile
+  // then waits for the flags only, with every other load in flight.
+  const uint8_t *own = reinterpret_cast<const uint8_t *>(rp.r + t0);
+  const uint8_t *trp = own;
+  if constexpr (A == kRetrace) {
+    // Cold stream: only a call with truncation flags waits for Args here.
+    if (rp.has_tr) trp = p.trunc + late_v(rp.row) * p.ld_trunc + t0;
+  } else {
+    trp = rp.has_tr ? rp.tr + t0 : own;
+  }
+  ld_flags_raw<K>(trp, q.ftr);
+  ld_flags_raw<K>(rp.has_te ? rp.te + t0 : own, q.fte);
+  Ld<InT>::template vec<K>(rp.r + t0, q.r);
+  if constexpr (U::values || U::q) {
+    float vk[K];
+    Ld<InT>::template vec<K>(rp.v + t0, vk);
+#pragma unroll
+    for (int j = 0; j < K; ++j) q.v[j] = vk[j];
+    if constexpr (U::values) q.v[K] = Ld<InT>::one(rp.v + t0 + K);  // V_{t0+K} (<= V_T)
+  }
+  if constexpr (U::q) Ld<InT>::template vec<K>(rp.eq + t0, q.eq);
+  if constexpr (U::log_rho) {
+    float lk[K];
+    Ld<InT>::template vec<K>(rp.lr + t0, lk);
+#pragma unroll
+    for (int j = 0; j < K; ++j) q.lr[j] = lk[j];
+    if constexpr (A == kRetrace) {
+      // log_rho_{t0+K}; at the row end (lim == K) re-read the last step
+      // instead, whose value the trace then ignores.
+      q.lr[K] = Ld<InT>::one(rp.lr + t0 + (lim > K ? K : K - 1));
+    }
+  }
+  q.dense = false;
+  if constexpr (U::tv && A != kVtrace) {
+    // Small batches read the bootstraps as whole vectors in flight with the
+    // other loads (no dependent round trip after the flags arrive; the extra
+    // bytes cost less than the latency there).  Otherwise the lane re-reads
+    // its own rewards (a cache hit, unused) and finish_tile reads the
+    // bootstraps at truncated steps only.
+    float tk[K];
+    Ld<InT>::template vec<K>(rp.dense_tv ? rp.tv + t0 : rp.r + t0, tk);
+#pragma unroll
+    for (int j = 0; j < K; ++j) q.tv[j] = tk[j];
+    q.dense = rp.dense_tv;
+  }
+  // Keep every load above ahead of the first use of any loaded value: the
+  // scheduler would otherwise pull the flag decoding up and wait for the
+  // flags before issuing the remaining loads.
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Truncation bootstraps at truncated steps only (rare), into registers of
+// their own.  ts[] is written only when some step of the lane is truncated;
+// every read of it is guarded by that step's truncation flag, so on other
+// paths it is never read (and not zeroed: a write there would wait for
+// loads of earlier tiles).  Flags of steps outside the row are zero.
+template <int A, typename InT, int K>
+__device__ __forceinline__ void sparse_tv(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
+                                          Tile<K> &x) {
+  if constexpr (Uses<A>::tv) {
+    if (x.dense) return;
+    uint32_t any_tr = 0;
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) any_tr |= x.tr[i];
+    if (any_tr != 0) {
+      const InT *tv_row;
+      if constexpr (A == kVtrace) tv_row = static_cast<const InT *>(p.tv) + late_v(rp.row) * p.ld_tv;
+      else tv_row = rp.tv;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        x.ts[j] = 0.f;
+        if (flag<K>(x.tr, j)) x.ts[j] = Bits<InT>::load(tv_row + t0 + j);
+      }
+    }
+  }
+}
+
+// Decode an issued tile (the first use of its loads) and issue its sparse
+// bootstrap loads.
+template <int A, typename InT, int K>
+__device__ __forceinline__ void finish_tile(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
+                                            Tile<K> &x) {
+  decode_flags<K>(x.ftr, x.tr);
+  decode_flags<K>(x.fte, x.te);
+#pragma unroll
+  for (int i = 0; i < K / 4; ++i) {
+    x.tr[i] = rp.has_tr ? x.tr[i] : 0u;
+    x.te[i] = rp.has_te ? x.te[i] : 0u;
+  }
+  sparse_tv<A, InT, K>(p, rp, t0, x);
+}
+
+// The ragged last tile of a row: element-wise loads of the steps e < lim.
+template <int A, typename InT, int K>
+__device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
+                                          int64_t lim, Tile<K> &x) {
   using U = Uses<A>;
 #pragma unroll
   for (int j = 0; j < K; ++j) { x.r[j] = 0.f; x.v[j] = 0.f; x.lr[j] = 0.f; x.eq[j] = 0.f; x.tv[j] = 0.f; }
   x.v[K] = 0.f;
   x.lr[K] = 0.f;
+  x.dense = false;
 #pragma unroll
   for (int i = 0; i < K / 4; ++i) { x.te[i] = 0; x.tr[i] = 0; }
-
-  if constexpr (!kEdge) {
-    // Flags first, with no branch: a missing flag array is replaced by the
-    // lane's own reward bytes (the address of its reward load, so a cache
-    // hit) and masked to zero after decoding.  The truncation test below then
-    // waits for the flags only, with every other load of the tile in flight.
-    FlagWords<K> ftr, fte;
-    const uint8_t *own = reinterpret_cast<const uint8_t *>(rp.r + t0);
-    const uint8_t *trp = own;
-    if constexpr (A == kRetrace) {
-      // Cold stream: only a call with truncation flags waits for Args here.
-      if (has_trunc) trp = p.trunc + late_v(rp.row) * p.ld_trunc + t0;
-    } else {
-      trp = has_trunc ? rp.tr + t0 : own;
-    }
-    ld_flags_raw<K>(trp, ftr);
-    ld_flags_raw<K>(has_term ? rp.te + t0 : own, fte);
-    Ld<InT>::template vec<K>(rp.r + t0, x.r);
-    if constexpr (U::values || U::q) {
-      float vk[K];
-      Ld<InT>::template vec<K>(rp.v + t0, vk);
-#pragma unroll
-      for (int j = 0; j < K; ++j) x.v[j] = vk[j];
-      if constexpr (U::values) x.v[K] = Ld<InT>::one(rp.v + t0 + K);  // V_{t0+K} (<= V_T)
-    }
-    if constexpr (U::q) Ld<InT>::template vec<K>(rp.eq + t0, x.eq);
-    if constexpr (U::log_rho) {
-      float lk[K];
-      Ld<InT>::template vec<K>(rp.lr + t0, lk);
-#pragma unroll
-      for (int j = 0; j < K; ++j) x.lr[j] = lk[j];
-      if constexpr (A == kRetrace) {
-        // log_rho_{t0+K}; at the row end (lim == K) re-read the last step
-        // instead, whose value the trace then ignores.
-        x.lr[K] = Ld<InT>::one(rp.lr + t0 + (lim > K ? K : K - 1));
-      }
-    }
-    if constexpr (U::tv && A != kVtrace) {
-      // Small batches read the bootstraps as whole vectors in flight with
-      // the other loads (no dependent round trip after the flags arrive;
-      // the extra bytes cost less than the latency there).  Otherwise the
-      // lane re-reads its own rewards (a cache hit) and the bootstraps are
-      // read below at truncated steps only.
-      float tk[K];
-      Ld<InT>::template vec<K>(dense_tv ? rp.tv + t0 : rp.r + t0, tk);
-#pragma unroll
-      for (int j = 0; j < K; ++j) x.tv[j] = tk[j];
-    }
-    // Keep every load above ahead of the first use of any loaded value: the
-    // scheduler would otherwise pull the flag decoding up and wait for the
-    // flags before issuing the remaining loads.
-    __builtin_amdgcn_sched_barrier(0);
-    decode_flags<K>(ftr, x.tr);
-    decode_flags<K>(fte, x.te);
-#pragma unroll
-    for (int i = 0; i < K / 4; ++i) {
-      x.tr[i] = has_trunc ? x.tr[i] : 0u;
-      x.te[i] = has_term ? x.te[i] : 0u;
-    }
-  } else if (lim > 0) {
-    if (has_trunc) {
+  if (lim > 0) {
+    if (rp.has_tr) {
       const uint8_t *trp;
       if constexpr (A == kRetrace) trp = p.trunc + late_v(rp.row) * p.ld_trunc;
       else trp = rp.tr;
       ld_flags_part<K>(trp + t0, lim, x.tr);
     }
-    if (has_term) ld_flags_part<K>(rp.te + t0, lim, x.te);
+    if (rp.has_te) ld_flags_part<K>(rp.te + t0, lim, x.te);
     ld_part<InT, K>(rp.r + t0, lim, x.r);
     if constexpr (U::values) {
 #pragma unroll
@@ -409,35 +483,13 @@ __device__ __forceinline__ void load_tile(const Args &p, const RowPtrs<InT> &rp,
       for (int e = 0; e <= K; ++e) x.lr[e] = e < lim ? Ld<InT>::one(rp.lr + t0 + e) : 0.f;
     }
   }
-
-  if constexpr (U::tv) {
-    if (!kEdge && dense_tv) return;  // already read with the other loads
-    // Read the bootstraps at truncated steps only (rare), into registers of
-    // their own (no write-after-write wait on the vector load above).  Flags
-    // of steps outside the row are zero.
-    uint32_t any_tr = 0;
-#pragma unroll
-    for (int i = 0; i < K / 4; ++i) any_tr |= x.tr[i];
-    float ts[K];
-#pragma unroll
-    for (int j = 0; j < K; ++j) ts[j] = 0.f;
-    if (any_tr != 0) {
-      const InT *tv_row;
-      if constexpr (A == kVtrace) tv_row = static_cast<const InT *>(p.tv) + late_v(rp.row) * p.ld_tv;
-      else tv_row = rp.tv;
-#pragma unroll
-      for (int j = 0; j < K; ++j)
-        if (flag<K>(x.tr, j)) ts[j] = Ld<InT>::one(tv_row + t0 + j);
-    }
-#pragma unroll
-    for (int j = 0; j < K; ++j) x.tv[j] = ts[j];
-  }
+  sparse_tv<A, InT, K>(p, rp, t0, x);
 }
 
 // (alpha_t, beta_t) per step (Method 1 coefficients, Method 3 masks).  Steps
 // outside the row get the identity map (0, 1).
-template <int A, int K, bool kEdge>
-__device__ __forceinline__ void coefficients(const Raw<K> &x, int64_t lim, const Args &p,
+template <int A, typename InT, int K, bool kEdge>
+__device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, const Args &p,
                                              float (&al)[K], float (&be)[K], float (&ratio)[K]) {
   const float gamma = late(p.gamma);
   const float lam = late(p.lam);
@@ -452,16 +504,16 @@ __device__ __forceinline__ void coefficients(const Raw<K> &x, int64_t lim, const
     float a_j, b_j;
     ratio[j] = 0.f;
     if constexpr (A == kReturns) {
-      a_j = (tr && !te) ? fmaf(gamma, x.tv[j], x.r[j]) : x.r[j];
+      a_j = (tr && !te) ? fmaf(gamma, tv_at<InT, K>(x, j), x.r[j]) : x.r[j];
       b_j = done ? 0.f : gamma;
     } else if constexpr (A == kGae || A == kTdLambda) {
-      const float nv = te ? 0.f : (tr ? x.tv[j] : x.v[j + 1]);
+      const float nv = te ? 0.f : (tr ? tv_at<InT, K>(x, j) : x.v[j + 1]);
       a_j = fmaf(gamma, nv, x.r[j]) - x.v[j];
       b_j = done ? 0.f : gl;
     } else if constexpr (A == kVtrace) {
       const float e = __expf(x.lr[j]);
       ratio[j] = e;
-      const float nv = te ? 0.f : (tr ? x.tv[j] : x.v[j + 1]);
+      const float nv = te ? 0.f : (tr ? tv_at<InT, K>(x, j) : x.v[j + 1]);
       a_j = fminf(rho_bar, e) * (fmaf(gamma, nv, x.r[j]) - x.v[j]);
       b_j = done ? 0.f : gamma * (lam * fminf(c_bar, e));
     } else {  // kRetrace
@@ -476,26 +528,18 @@ __device__ __forceinline__ void coefficients(const Raw<K> &x, int64_t lim, const
   }
 }
 
-// One tile of one row group: load, build pairs, fold, scan, carry, re-run,
-// store.  Returns the carry for the next (earlier) tile.
+// One tile of one row group, inputs already loaded: build pairs, fold, scan,
+// carry, re-run, store.  Returns the carry for the next (earlier) tile.
 template <int A, typename InT, int K, int LPR, int WPR, bool kEdge>
-__device__ __forceinline__ float do_tile(const Args &p, const RowPtrs<InT> &rp, int64_t T,
-                                         bool row_ok, int64_t c, bool need_carry, int g, int lane,
-                                         int wave, float carry, float2 (*s_agg)[WPR]) {
-  constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
-  constexpr int kTile = kGroup * K;
+__device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> &rp,
+                                              const Tile<K> &x, int64_t t0, int64_t lim,
+                                              bool row_ok, int64_t c, bool need_carry, int lane,
+                                              int wave, float carry, float2 (*s_agg)[WPR]) {
   constexpr int kScanLanes = WPR > 1 ? 64 : LPR;
   using U = Uses<A>;
 
-  const int64_t t0 = c * kTile + static_cast<int64_t>(kGroup - 1 - g) * K;
-  int64_t lim = T - t0;  // steps of this lane that lie inside the row
-  if constexpr (kEdge) lim = row_ok ? (lim > 0 ? lim : 0) : 0;
-
-  Raw<K> x;
-  load_tile<A, InT, K, kEdge>(p, rp, rp.has_te, rp.has_tr, rp.dense_tv, t0, lim, x);
-
   float al[K], be[K], ratio[K];
-  coefficients<A, K, kEdge>(x, lim, p, al, be, ratio);
+  coefficients<A, InT, K, kEdge>(x, lim, p, al, be, ratio);
 
   // Fold the lane's steps: (a, b) = f_{t0} o ... o f_{t0+K-1}.
   float a = al[K - 1], b = be[K - 1];
@@ -558,7 +602,7 @@ __device__ __forceinline__ float do_tile(const Args &p, const RowPtrs<InT> &rp, 
       o0[j] = x.v[j] + xa;
       const bool te = flag<K>(x.te, j);
       const bool tr = flag<K>(x.tr, j);
-      const float nvs = te ? 0.f : (tr ? x.tv[j] : x.v[j + 1] + xn);
+      const float nvs = te ? 0.f : (tr ? tv_at<InT, K>(x, j) : x.v[j + 1] + xn);
       o1[j] = fminf(pg_rho_bar, ratio[j]) * (fmaf(gamma, nvs, x.r[j]) - x.v[j]);
     } else {  // kRetrace
       o0[j] = x.v[j] + xa;
@@ -681,21 +725,62 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     if (h4 != nullptr) carry = Ld<InT>::one(static_cast<const InT *>(h4) + rr);
   }
 
+  // Tiles are visited from the last (latest in time) to the first.  A ragged
+  // last tile takes the element-wise path; every whole tile's loads are
+  // issued while the tile after it (in time) is being computed.
   const int64_t ntiles = (T + kTile - 1) / kTile;
+  const int64_t lane_off = static_cast<int64_t>(kGroup - 1 - g) * K;
+  auto t0_of = [&](int64_t c) { return c * kTile + lane_off; };
+
   if (ntiles == 1 && T == kTile) {
-    // One whole tile: straight-line code, no loop-carried waits.
-    do_tile<A, InT, K, LPR, WPR, false>(p, rp, T, row_ok, 0, false, g, lane, wave, carry, s_agg);
+    // One whole tile: straight-line code.
+    Tile<K> x;
+    issue_tile<A, InT, K>(p, rp, lane_off, T - lane_off, x);
+    finish_tile<A, InT, K>(p, rp, lane_off, x);
+    tile_compute<A, InT, K, LPR, WPR, false>(p, rp, x, lane_off, T - lane_off, row_ok, 0, false,
+                                             lane, wave, carry, s_agg);
     return;
   }
-  int64_t c = ntiles - 1;
-  if (T % kTile != 0) {
-    carry = do_tile<A, InT, K, LPR, WPR, true>(p, rp, T, row_ok, c, c > 0, g, lane, wave, carry,
-                                               s_agg);
+  const bool ragged = T % kTile != 0;
+  int64_t c = ragged ? ntiles - 2 : ntiles - 1;  // latest whole tile
+  // Two explicit buffers, alternating: tile c is decoded (and its sparse
+  // bootstrap loads issued) before tile c-1's loads are issued into the other
+  // buffer, then tile c is computed.  In-order load completion then lets the
+  // computation of tile c wait for tile c only, and no register copies are
+  // needed between iterations.  The prefetch is unconditional (no branch for
+  // the wait-count analysis to merge): after tile 0 it re-reads tile 0, which
+  // was just loaded (cache hits, never used).
+  Tile<K> buf_a, buf_b;
+  if (c >= 0) issue_tile<A, InT, K>(p, rp, t0_of(c), T - t0_of(c), buf_a);
+  if (ragged) {
+    const int64_t te0 = t0_of(ntiles - 1);
+    const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
+    Tile<K> x;
+    load_edge<A, InT, K>(p, rp, te0, lim, x);
+    carry = tile_compute<A, InT, K, LPR, WPR, true>(p, rp, x, te0, lim, row_ok, ntiles - 1, c >= 0,
+                                                    lane, wave, carry, s_agg);
+  }
+  if (c < 0) return;
+  for (;;) {
+    {
+      finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
+      const int64_t cn = c > 0 ? c - 1 : 0;
+      issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
+      carry = tile_compute<A, InT, K, LPR, WPR, false>(p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok,
+                                                       c, c > 0, lane, wave, carry, s_agg);
+    }
+    if (c == 0) break;
+    --c;
+    {
+      finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
+      const int64_t cn = c > 0 ? c - 1 : 0;
+      issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
+      carry = tile_compute<A, InT, K, LPR, WPR, false>(p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok,
+                                                       c, c > 0, lane, wave, carry, s_agg);
+    }
+    if (c == 0) break;
     --c;
   }
-  for (; c >= 0; --c)
-    carry = do_tile<A, InT, K, LPR, WPR, false>(p, rp, T, row_ok, c, c > 0, g, lane, wave, carry,
-                                                s_agg);
 }
 
 }  // namespace rlca

@@ -42,7 +42,7 @@ def test_version_and_variants(lib):
     for v in range(nv):
         k, lpr, wpr = rl.rlca_variant_info(v)
         kb, lprb, wprb = rl.rlca_variant_info(v, torch.bfloat16)
-        assert k * 4 == kb * 2 == 16  # one 16-byte vector per lane and array
+        assert k == kb == 4  # one 16-byte fp32 vector per lane and array
         assert (lpr, wpr) == (lprb, wprb)
         # lanes that share a row: part of a wavefront, or whole wavefronts
         assert (wpr == 1 and lpr in (16, 32, 64)) or lpr == 64 * wpr

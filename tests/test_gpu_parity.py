@@ -284,3 +284,62 @@ def test_sparse_truncation_bootstraps_large_batch(algo):
         rl.rlca_set_variant(-1 if v is None else v)
         print(algo, "variant", v, flush=True)
         assert_close(run_gpu(algo, dev, p), ref, TOL["f32"], "%s/v%s" % (algo, v))
+
+
+def test_hip_graph_replay_matches_eager():
+    # The benchmark replays captured launches; every replay, with eager work
+    # and synchronizations in between, must equal the eager call bitwise, and
+    # must see inputs updated in place.
+    host = random_inputs("gae", 300, 200, 9)
+    dev = to_device(host)
+    p = params32(DEFAULT_PARAMS)
+    args = (dev["rewards"], dev["values"], dev["terminated"], dev["truncated"],
+            dev["trunc_values"])
+    adv = torch.empty(300, 200, device="cuda")
+    tgt = torch.empty_like(adv)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            rl.rlca_gae(*args, gamma=p["gamma"], lam=p["lam"], advantages=adv, targets=tgt)
+    torch.cuda.synchronize()
+    for i in range(4):
+        if i == 2:
+            dev["rewards"].mul_(-0.5)  # in-place input update between replays
+        e_adv, e_tgt = rl.rlca_gae(*args, gamma=p["gamma"], lam=p["lam"])
+        adv.fill_(float("nan"))
+        tgt.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(adv, e_adv) and torch.equal(tgt, e_tgt), "replay %d" % i
+    ref = run_oracle("gae", {k: v.cpu() for k, v in dev.items()}, p)
+    assert rel_err(adv.double().cpu().numpy(), ref["advantages"]) <= TOL["f32"]
+
+
+def test_concurrent_calls_on_two_streams():
+    hosts = [random_inputs(a, 700, 300, 31 + i) for i, a in enumerate(("gae", "vtrace"))]
+    devs = [to_device(h) for h in hosts]
+    p = params32(DEFAULT_PARAMS)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    outs = []
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            a = rl.rlca_gae(devs[0]["rewards"], devs[0]["values"], devs[0]["terminated"],
+                            devs[0]["truncated"], devs[0]["trunc_values"], gamma=p["gamma"],
+                            lam=p["lam"])
+        with torch.cuda.stream(s2):
+            b = rl.rlca_vtrace(devs[1]["rewards"], devs[1]["values"], devs[1]["log_rhos"],
+                               devs[1]["terminated"], devs[1]["truncated"],
+                               devs[1]["trunc_values"], gamma=p["gamma"], lam=p["lam"])
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    ra = run_oracle("gae", hosts[0], p)
+    rb = run_oracle("vtrace", hosts[1], p)
+    for a, b in outs:
+        assert rel_err(a[0].double().cpu().numpy(), ra["advantages"]) <= TOL["f32"]
+        assert rel_err(b[0].double().cpu().numpy(), rb["vs"]) <= TOL["f32"]
+        assert rel_err(b[1].double().cpu().numpy(), rb["pg_advantages"]) <= TOL["f32"]
