@@ -41,8 +41,11 @@ def _load():
                                       dbl, dbl, dbl, dbl, dbl, _D, _D]
         lib.oracle_retrace.argtypes = [i64, i64, _D, _D, _D, _D, _U8, _U8,
                                        dbl, dbl, dbl, _D]
+        lib.oracle_eligibility_trace.argtypes = [i64, i64, _D, _U8, _U8, _D, dbl, dbl, _D]
+        lib.oracle_episodic_cumsum.argtypes = [i64, i64, _D, _U8, _U8, _D, _D]
         for f in (lib.oracle_returns, lib.oracle_gae, lib.oracle_td_lambda,
-                  lib.oracle_vtrace, lib.oracle_retrace):
+                  lib.oracle_vtrace, lib.oracle_retrace, lib.oracle_eligibility_trace,
+                  lib.oracle_episodic_cumsum):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -158,4 +161,30 @@ def retrace(rewards, q_taken, exp_q_next, log_rhos, terminated=None, truncated=N
     out = np.empty((N, T), np.float64)
     _check(_load().oracle_retrace(N, T, rp, qp, eqp, lrp, tep, trp, float(gamma), float(lam),
                                   float(c_bar), out.ctypes.data_as(_D)), "retrace")
+    return out
+
+
+def eligibility_trace(x, terminated=None, truncated=None, z_init=None, *, gamma, lam):
+    """Forward accumulating trace ``z [N, T]``: z_t = x_t + gamma*lam*(1-done_{t-1}) z_{t-1}."""
+    a, ap = _f64(x, np.shape(_as_numpy(x)))
+    N, T = a.shape
+    te, tep = _u8(terminated, (N, T))
+    tr, trp = _u8(truncated, (N, T))
+    z0, z0p = _f64(z_init, (N,))
+    out = np.empty((N, T), np.float64)
+    _check(_load().oracle_eligibility_trace(N, T, ap, tep, trp, z0p, float(gamma), float(lam),
+                                            out.ctypes.data_as(_D)), "eligibility_trace")
+    return out
+
+
+def episodic_cumsum(x, terminated=None, truncated=None, s_init=None):
+    """Forward episodic prefix sum ``S [N, T]``: S_t = x_t + (1-done_{t-1}) S_{t-1}."""
+    a, ap = _f64(x, np.shape(_as_numpy(x)))
+    N, T = a.shape
+    te, tep = _u8(terminated, (N, T))
+    tr, trp = _u8(truncated, (N, T))
+    s0, s0p = _f64(s_init, (N,))
+    out = np.empty((N, T), np.float64)
+    _check(_load().oracle_episodic_cumsum(N, T, ap, tep, trp, s0p, out.ctypes.data_as(_D)),
+           "episodic_cumsum")
     return out

@@ -241,3 +241,60 @@ int oracle_retrace(int64_t N, int64_t T, const double *r, const double *q,
     }
     return 0;
 }
+
+/*
+ * Forward-time recurrences (rl-triton, Method 1: eligibility traces and
+ * episodic prefix sums are the forward-time mirror of eq. R):
+ *     A_t = alpha_t + beta_t * A_{t-1},   t = 0 .. T-1.
+ * An episode boundary after step t-1 (done_{t-1}) restarts the recurrence at
+ * step t.  A_{-1} is a per-row carry from before the window (NULL: 0); it is
+ * used as given (the caller zeroes it if the previous window ended an
+ * episode).
+ */
+
+/* Accumulating eligibility trace:
+ *   z_t = x_t + gamma*lam * z_{t-1}   if not done_{t-1},
+ *   z_t = x_t                         if done_{t-1};   z_{-1} = z_init. */
+int oracle_eligibility_trace(int64_t N, int64_t T, const double *x, const uint8_t *term,
+                             const uint8_t *trunc, const double *z_init, double gamma,
+                             double lam, double *z)
+{
+    if (N < 0 || T < 0)
+        return -1;
+    if (N > 0 && T > 0 && (x == NULL || z == NULL))
+        return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        double prev = z_init != NULL ? z_init[n] : 0.0;
+        int prev_done = 0;
+        for (int64_t t = 0; t < T; ++t) {
+            double zt = AT(x, n, t, T) + (prev_done ? 0.0 : gamma * lam * prev);
+            AT(z, n, t, T) = zt;
+            prev = zt;
+            prev_done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);
+        }
+    }
+    return 0;
+}
+
+/* Episodic prefix sum:
+ *   S_t = x_t + S_{t-1}   if not done_{t-1},
+ *   S_t = x_t             if done_{t-1};   S_{-1} = s_init. */
+int oracle_episodic_cumsum(int64_t N, int64_t T, const double *x, const uint8_t *term,
+                           const uint8_t *trunc, const double *s_init, double *s)
+{
+    if (N < 0 || T < 0)
+        return -1;
+    if (N > 0 && T > 0 && (x == NULL || s == NULL))
+        return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        double prev = s_init != NULL ? s_init[n] : 0.0;
+        int prev_done = 0;
+        for (int64_t t = 0; t < T; ++t) {
+            double st = AT(x, n, t, T) + (prev_done ? 0.0 : prev);
+            AT(s, n, t, T) = st;
+            prev = st;
+            prev_done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);
+        }
+    }
+    return 0;
+}

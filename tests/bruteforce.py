@@ -169,3 +169,37 @@ def retrace(r, q, eq, log_rho, term, trunc, gamma, lam, c_bar):
             row.append(q[n][t] + s)
         out.append(row)
     return out
+
+
+def _episode_start(te, tr, t):
+    """First step of the episode that contains step t (a boundary after step
+    k-1 starts a new episode at k)."""
+    s = t
+    while s > 0 and not (te[s - 1] or tr[s - 1]):
+        s -= 1
+    return s
+
+
+def eligibility_trace(x, term, trunc, z_init, decay):
+    """z_t = sum_{k=s(t)}^{t} decay^{t-k} x_k (+ decay^{t+1} z_init if the episode
+    of step t began before the window), s(t) = first step of t's episode."""
+    N, T = len(x), len(x[0]) if len(x) else 0
+    out = []
+    for n in range(N):
+        te, tr = _flags(term, trunc, n, T)
+        z0 = z_init[n] if z_init is not None else 0
+        row = []
+        for t in range(T):
+            s = _episode_start(te, tr, t)
+            v = sum(decay ** (t - k) * x[n][k] for k in range(s, t + 1))
+            if s == 0:
+                v += decay ** (t + 1) * z0
+            row.append(v)
+        out.append(row)
+    return out
+
+
+def episodic_cumsum(x, term, trunc, s_init):
+    """S_t = sum of x over the steps of t's episode up to t (+ s_init if that
+    episode began before the window)."""
+    return eligibility_trace(x, term, trunc, s_init, 1)

@@ -46,6 +46,9 @@ def main():
                                          pg_rho_bar=p["pg_rho_bar"])
     out["qret"] = oracle.retrace(inp["r"], inp["q"], inp["eq"], inp["lr"], inp["term"],
                                  inp["trunc"], gamma=p["gamma"], lam=p["lam"], c_bar=p["c_bar"])
+    out["eligibility"] = oracle.eligibility_trace(inp["r"], inp["term"], inp["trunc"], inp["B"],
+                                                  gamma=p["gamma"], lam=p["lam"])
+    out["cumsum"] = oracle.episodic_cumsum(inp["r"], inp["term"], inp["trunc"], inp["B"])
     doc = {
         "about": "Oracle regression fixture written by tests/golden/make_regression.py "
                  "(calls only oracle/). Not an independent pin.",

@@ -44,6 +44,24 @@ MUTANTS = [
      "(term_t ? 0.0 : gamma * AT(eq, n, t, T))", "(gamma * AT(eq, n, t, T))"),
     ("retrace_trace_not_cut_at_truncation", "if (!done && t < T - 1) {",
      "if (!term_t && t < T - 1) {"),
+    ("forward_reset_on_same_step",
+     "            double zt = AT(x, n, t, T) + (prev_done ? 0.0 : gamma * lam * prev);\n"
+     "            AT(z, n, t, T) = zt;\n            prev = zt;\n"
+     "            prev_done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);",
+     "            prev_done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);\n"
+     "            double zt = AT(x, n, t, T) + (prev_done ? 0.0 : gamma * lam * prev);\n"
+     "            AT(z, n, t, T) = zt;\n            prev = zt;"),
+    ("forward_trace_ignores_lambda", "(prev_done ? 0.0 : gamma * lam * prev)",
+     "(prev_done ? 0.0 : gamma * prev)"),
+    ("cumsum_drops_carry_in", "double prev = s_init != NULL ? s_init[n] : 0.0;",
+     "double prev = 0.0;"),
+    ("cumsum_reset_ignores_truncation",
+     "            double st = AT(x, n, t, T) + (prev_done ? 0.0 : prev);\n"
+     "            AT(s, n, t, T) = st;\n            prev = st;\n"
+     "            prev_done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);",
+     "            double st = AT(x, n, t, T) + (prev_done ? 0.0 : prev);\n"
+     "            AT(s, n, t, T) = st;\n            prev = st;\n"
+     "            prev_done = flag_at(term, n, t, T);"),
 ]
 
 PIN_CASES = [
@@ -62,6 +80,11 @@ PIN_CASES = [
     (pins.test_no_leak_across_episode_boundary, dict(kind="trunc")),
     (pins.test_window_bootstrap_counted_once_and_ignored_after_done, {}),
     (pins.test_affine_operator_scan_equals_gae_recurrence_exactly, {}),
+    (pins.test_forward_recurrences_without_boundaries_are_library_cumsums, {}),
+    (pins.test_forward_boundary_restarts_next_step, {}),
+    (pins.test_forward_oracle_matches_forward_sums, dict(seed=82, T=13)),
+    (pins.test_forward_exhaustive_boundaries, {}),
+    (pins.test_forward_no_leak_bitwise, {}),
 ]
 
 

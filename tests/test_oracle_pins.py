@@ -407,6 +407,85 @@ def test_oracle_regression_fixture():
                                          c_bar=p["c_bar"], pg_rho_bar=p["pg_rho_bar"])
     got["qret"] = oracle.retrace(i["r"], i["q"], i["eq"], i["lr"], term, trunc,
                                  gamma=p["gamma"], lam=p["lam"], c_bar=p["c_bar"])
+    got["eligibility"] = oracle.eligibility_trace(i["r"], term, trunc, i["B"], gamma=p["gamma"],
+                                                  lam=p["lam"])
+    got["cumsum"] = oracle.episodic_cumsum(i["r"], term, trunc, i["B"])
     for k, rows in doc["outputs"].items():
         want = np.array([[float.fromhex(x) for x in row] for row in rows])
         assert rel_err(got[k], want) < 1e-15, k
+
+
+# -------------------------------------------- forward-time mirrors (eq. R forward)
+
+def test_forward_recurrences_without_boundaries_are_library_cumsums():
+    g = np.random.Generator(np.random.PCG64(81))
+    x = g.standard_normal((5, 40))
+    # Plain prefix sum: numpy's cumsum.
+    assert rel_err(oracle.episodic_cumsum(x), np.cumsum(x, axis=1)) < 1e-13
+    # Carry-in adds to every step of the first episode.
+    s0 = g.standard_normal(5)
+    assert rel_err(oracle.episodic_cumsum(x, s_init=s0), np.cumsum(x, axis=1) + s0[:, None]) < 1e-13
+    # Constant input, geometric decay: z_t = (1 - d^{t+1}) / (1 - d).
+    d = 0.9 * 0.8
+    z = oracle.eligibility_trace(np.ones((1, 30)), gamma=0.9, lam=0.8)[0]
+    for t in range(30):
+        assert z[t] == pytest.approx((1 - d ** (t + 1)) / (1 - d), rel=1e-14)
+    # gamma*lam = 1 reduces the trace to the prefix sum.
+    assert rel_err(oracle.eligibility_trace(x, gamma=1.0, lam=1.0), np.cumsum(x, axis=1)) < 1e-13
+
+
+def test_forward_boundary_restarts_next_step():
+    # A boundary after step 2 restarts at step 3; termination and truncation
+    # act the same for forward recurrences.
+    x = np.array([[1.0, 2.0, 3.0, 4.0, 5.0]])
+    for kind in ("term", "trunc"):
+        f = np.zeros((1, 5), np.uint8)
+        f[0, 2] = 1
+        kw = {"terminated": f} if kind == "term" else {"truncated": f}
+        s = oracle.episodic_cumsum(x, s_init=np.array([10.0]), **kw)[0]
+        assert list(s) == [11.0, 13.0, 16.0, 4.0, 9.0]
+
+
+@pytest.mark.parametrize("seed", [82, 83])
+@pytest.mark.parametrize("T", [1, 4, 13])
+def test_forward_oracle_matches_forward_sums(seed, T):
+    d = rand_inputs(seed, 6, T)
+    tl = lambda a: a.tolist()
+    z = oracle.eligibility_trace(d["r"], d["term"], d["trunc"], d["B"], gamma=0.9, lam=0.7)
+    zb = bf.eligibility_trace(tl(d["r"]), tl(d["term"]), tl(d["trunc"]), tl(d["B"]), 0.9 * 0.7)
+    assert rel_err(z, zb) < RTOL_BF
+    s = oracle.episodic_cumsum(d["r"], d["term"], d["trunc"], d["B"])
+    sb = bf.episodic_cumsum(tl(d["r"]), tl(d["term"]), tl(d["trunc"]), tl(d["B"]))
+    assert rel_err(s, sb) < RTOL_BF
+
+
+def test_forward_exhaustive_boundaries():
+    term, trunc = all_boundary_patterns(5)
+    N = term.shape[0]
+    g = np.random.Generator(np.random.PCG64(84))
+    x, z0 = g.standard_normal((N, 5)), g.standard_normal(N)
+    tl = lambda a: a.tolist()
+    assert rel_err(oracle.eligibility_trace(x, term, trunc, z0, gamma=0.95, lam=0.5),
+                   bf.eligibility_trace(tl(x), tl(term), tl(trunc), tl(z0), 0.95 * 0.5)) < RTOL_BF
+    assert rel_err(oracle.episodic_cumsum(x, term, trunc, z0),
+                   bf.episodic_cumsum(tl(x), tl(term), tl(trunc), tl(z0))) < RTOL_BF
+
+
+def test_forward_no_leak_bitwise():
+    # A boundary after step s: perturbing inputs at steps <= s (and the
+    # carry-in) leaves outputs at steps > s bitwise unchanged.
+    d = rand_inputs(85, 4, 30, p_term=0.0, p_trunc=0.0)
+    s = 12
+    for kind in ("term", "trunc"):
+        f = np.zeros((4, 30), np.uint8)
+        f[:, s] = 1
+        kw = {"terminated": f} if kind == "term" else {"truncated": f}
+        x2 = d["r"].copy()
+        x2[:, : s + 1] += 5.0
+        for fn, extra in ((oracle.episodic_cumsum, {}),
+                          (oracle.eligibility_trace, {"gamma": 0.9, "lam": 0.9})):
+            a = fn(d["r"], s_init=d["B"], **kw, **extra) if fn is oracle.episodic_cumsum else \
+                fn(d["r"], z_init=d["B"], **kw, **extra)
+            b = fn(x2, s_init=d["B"] + 3, **kw, **extra) if fn is oracle.episodic_cumsum else \
+                fn(x2, z_init=d["B"] + 3, **kw, **extra)
+            assert np.array_equal(a[:, s + 1:], b[:, s + 1:]), (kind, fn.__name__)
