@@ -77,6 +77,9 @@ def algorithmic_bytes(w, N, T):
         vt = (3 * es + 1 + 8) * N * T + es * N          # r, V, log_rho, term; vs, pg
         rt = (4 * es + 1 + 4) * N * T                  # r, Q, EQ, log_rho, term; q_ret
         return vt + rt
+    if w.algo in ("eligibility", "cumsum"):
+        flags = 2 if w.p_trunc is not None else 1
+        return (es + flags + 4) * N * T                # x, flags; output
     raise ValueError(w.algo)
 
 
@@ -197,6 +200,12 @@ def main():
                               d.get("trunc_values"), gamma=gamma, lam=lam, out=d["_o0"])
         elif w.algo == "returns":
             rl.rlca_returns(d["rewards"], d["terminated"], gamma=gamma, out=d["_o0"])
+        elif w.algo == "eligibility":
+            rl.rlca_eligibility_trace(d["rewards"], d["terminated"], d.get("truncated"),
+                                      gamma=gamma, lam=lam, out=d["_o0"])
+        elif w.algo == "cumsum":
+            rl.rlca_episodic_cumsum(d["rewards"], d["terminated"], d.get("truncated"),
+                                    out=d["_o0"])
         elif w.algo == "vtrace+retrace":
             rl.rlca_vtrace(d["rewards"], d["values"], d["log_rhos"], d["terminated"], gamma=gamma,
                            lam=lam, vs=d["_o0"], pg_advantages=d["_o1"], **clips)
@@ -221,6 +230,13 @@ def main():
         outs = (sets[0]["_o0"],)
     elif w.algo == "returns":
         ref = (oracle.returns(host["rewards"], host["terminated"], gamma=gamma),)
+        outs = (sets[0]["_o0"],)
+    elif w.algo == "eligibility":
+        ref = (oracle.eligibility_trace(host["rewards"], host["terminated"], host.get("truncated"),
+                                        gamma=gamma, lam=lam),)
+        outs = (sets[0]["_o0"],)
+    elif w.algo == "cumsum":
+        ref = (oracle.episodic_cumsum(host["rewards"], host["terminated"], host.get("truncated")),)
         outs = (sets[0]["_o0"],)
     else:
         vs, pg = oracle.vtrace(host["rewards"], host["values"], host["log_rhos"],
@@ -347,6 +363,11 @@ def main():
                                  lam=lam)
             elif w.algo == "returns":
                 oracle.returns(h64["rewards"], h64["terminated"], gamma=gamma)
+            elif w.algo == "eligibility":
+                oracle.eligibility_trace(h64["rewards"], h64["terminated"], h64.get("truncated"),
+                                         gamma=gamma, lam=lam)
+            elif w.algo == "cumsum":
+                oracle.episodic_cumsum(h64["rewards"], h64["terminated"], h64.get("truncated"))
             else:
                 oracle.vtrace(h64["rewards"], h64["values"], h64["log_rhos"], h64["terminated"],
                               gamma=gamma, lam=lam, **clips)

@@ -195,6 +195,43 @@ int rlca_retrace(int64_t num_envs, int64_t T, int dtype,
                  float *q_ret, int64_t ld_q_ret,
                  void *stream);
 
+/*
+ * Forward-time mirrors of (R) (Method 1: "eligibility traces" and "episodic
+ * prefix sums", computed forward in time):
+ *     A_t = alpha_t + beta_t * A_{t-1},   t = 0 .. T-1,
+ * with alpha_t = x_t.  A boundary after step t-1 (done_{t-1} = terminated or
+ * truncated at t-1; the two are not distinguished here) restarts the
+ * recurrence at step t: beta_t = 0.  A_{-1} is the per-row carry-in
+ * (`z_init` / `s_init`, [N] in the call's dtype, NULL: 0), used as given
+ * (zero it if the previous window ended an episode).
+ *
+ * Accumulating eligibility trace: beta_t = gamma * lam * (1 - done_{t-1}),
+ *   z_t = x_t + gamma*lam*(1 - done_{t-1}) * z_{t-1}.
+ * In:  x [N,T].  Out: traces [N,T] fp32.
+ */
+int rlca_eligibility_trace(int64_t num_envs, int64_t T, int dtype,
+                           const void *x, int64_t ld_x,
+                           const uint8_t *terminated, int64_t ld_terminated,
+                           const uint8_t *truncated, int64_t ld_truncated,
+                           const void *z_init,
+                           float gamma, float lam,
+                           float *traces, int64_t ld_traces,
+                           void *stream);
+
+/*
+ * Episodic prefix sum: beta_t = 1 - done_{t-1},
+ *   S_t = x_t + (1 - done_{t-1}) * S_{t-1}   (the running sum of x within
+ *   each episode, e.g. the return so far).
+ * In:  x [N,T].  Out: sums [N,T] fp32.
+ */
+int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype,
+                         const void *x, int64_t ld_x,
+                         const uint8_t *terminated, int64_t ld_terminated,
+                         const uint8_t *truncated, int64_t ld_truncated,
+                         const void *s_init,
+                         float *sums, int64_t ld_sums,
+                         void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *rlca_last_error(void);
 

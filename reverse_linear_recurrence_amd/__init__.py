@@ -8,7 +8,8 @@ in its HIP kernels.  There is no fallback: if the library is missing or the
 tensors are not on a GPU, the call raises.
 
 Functions (same names as the C ABI):
-    rlca_returns, rlca_gae, rlca_td_lambda, rlca_vtrace, rlca_retrace
+    rlca_returns, rlca_gae, rlca_td_lambda, rlca_vtrace, rlca_retrace,
+    rlca_eligibility_trace, rlca_episodic_cumsum
 and the tiling controls rlca_set_variant, rlca_num_variants,
 rlca_variant_info, rlca_last_variant, plus rlca_version.
 """
@@ -23,6 +24,8 @@ from ._binding import (  # noqa: F401
     RlcaError,
     lib_path,
     load_library,
+    rlca_eligibility_trace,
+    rlca_episodic_cumsum,
     rlca_gae,
     rlca_last_variant,
     rlca_num_variants,

@@ -35,6 +35,10 @@ _SIGNATURES = {
                     _vp, _i64, _f32, _f32, _f32, _f32, _f32, _vp, _i64, _vp, _i64, _vp],
     "rlca_retrace": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                      _vp, _i64, _f32, _f32, _f32, _vp, _i64, _vp],
+    "rlca_eligibility_trace": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _f32,
+                               _f32, _vp, _i64, _vp],
+    "rlca_episodic_cumsum": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64,
+                             _vp],
     "rlca_last_error": [],
     "rlca_version": [],
     "rlca_num_variants": [],
@@ -123,7 +127,7 @@ def _output(name, x, shape, device):
 
 def _common(rewards):
     if not isinstance(rewards, torch.Tensor) or rewards.dim() != 2:
-        raise ValueError("rewards must be a 2-D tensor [num_envs, T]")
+        raise ValueError("inputs must be 2-D tensors [num_envs, T]")
     if rewards.device.type != "cuda":
         raise ValueError("inputs must be on a GPU (got %s)" % rewards.device)
     if rewards.dtype == torch.float32:
@@ -238,6 +242,38 @@ def rlca_retrace(rewards, q_taken, exp_q_next, log_rhos, terminated=None, trunca
     _check(load_library().rlca_retrace(N, T, code, r, ld_r, q, ld_q, eq, ld_eq, lr, ld_lr, te,
                                        ld_te, tr, ld_tr, gamma, lam, c_bar, o, ld_o,
                                        _stream(stream, dev)))
+    return out
+
+
+def rlca_eligibility_trace(x, terminated=None, truncated=None, z_init=None, *, gamma, lam,
+                           out=None, stream=None):
+    """Forward accumulating trace [N, T] float32:
+    z_t = x_t + gamma*lam*(1-done_{t-1}) z_{t-1}, z_{-1} = z_init [N] (None: 0)."""
+    N, T, code, dev = _common(x)
+    dt = x.dtype
+    a, ld_a = _float_input("x", x, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    z0, _ = _float_input("z_init", z_init, dt, (N,), dev)
+    out, o, ld_o = _output("traces", out, (N, T), dev)
+    _check(load_library().rlca_eligibility_trace(N, T, code, a, ld_a, te, ld_te, tr, ld_tr, z0,
+                                                 gamma, lam, o, ld_o, _stream(stream, dev)))
+    return out
+
+
+def rlca_episodic_cumsum(x, terminated=None, truncated=None, s_init=None, *, out=None,
+                         stream=None):
+    """Forward episodic prefix sum [N, T] float32:
+    S_t = x_t + (1-done_{t-1}) S_{t-1}, S_{-1} = s_init [N] (None: 0)."""
+    N, T, code, dev = _common(x)
+    dt = x.dtype
+    a, ld_a = _float_input("x", x, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    s0, _ = _float_input("s_init", s_init, dt, (N,), dev)
+    out, o, ld_o = _output("sums", out, (N, T), dev)
+    _check(load_library().rlca_episodic_cumsum(N, T, code, a, ld_a, te, ld_te, tr, ld_tr, s0, o,
+                                               ld_o, _stream(stream, dev)))
     return out
 
 

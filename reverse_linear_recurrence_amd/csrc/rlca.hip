@@ -80,7 +80,9 @@ const void *kernel_for(int algo, int dtype, int v, bool uniform) {
     case kGae: return kernel_for<kGae>(dtype, v, uniform);
     case kTdLambda: return kernel_for<kTdLambda>(dtype, v, uniform);
     case kVtrace: return kernel_for<kVtrace>(dtype, v, uniform);
-    default: return kernel_for<kRetrace>(dtype, v, uniform);
+    case kRetrace: return kernel_for<kRetrace>(dtype, v, uniform);
+    case kEligibility: return kernel_for<kEligibility>(dtype, v, uniform);
+    default: return kernel_for<kCumsum>(dtype, v, uniform);
   }
 }
 
@@ -237,12 +239,17 @@ int launch(int algo, int dtype, const Args &args, void *stream) {
       hot[3] = a.term; hld[3] = a.ld_term;
       hot[4] = a.trunc; hld[4] = a.ld_trunc;
       break;
-    default:  // kRetrace
+    case kRetrace:
       hot[1] = a.v; hld[1] = a.ld_v;
       hot[2] = a.eq; hld[2] = a.ld_eq;
       hot[3] = a.lr; hld[3] = a.ld_lr;
       hot[4] = a.term; hld[4] = a.ld_term;
       ldx = a.trunc != nullptr ? 1 : 0;
+      break;
+    default:  // kEligibility, kCumsum
+      hot[1] = a.term; hld[1] = a.ld_term;
+      hot[2] = a.trunc; hld[2] = a.ld_trunc;
+      hot[3] = a.boot;  // initial carry, a [N] vector: no stride
       break;
   }
   bool uniform = true;
@@ -444,6 +451,54 @@ int rlca_retrace(int64_t num_envs, int64_t T, int dtype, const void *rewards, in
   a.o0 = q_ret; a.ld_o0 = ld_q_ret;
   a.gamma = gamma; a.lam = lam; a.rho_bar = 1.f; a.c_bar = c_bar; a.pg_rho_bar = 1.f;
   return launch(kRetrace, dtype, a, stream);
+}
+
+static int forward_like(int algo, int64_t num_envs, int64_t T, int dtype, const void *x,
+                        int64_t ld_x, const uint8_t *terminated, int64_t ld_terminated,
+                        const uint8_t *truncated, int64_t ld_truncated, const void *init,
+                        float gamma, float lam, float *out, int64_t ld_out, const char *init_name,
+                        const char *out_name, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  const int64_t es = esize_of(dtype);
+  Arr arrs[] = {
+      {"x", x, ld_x, T, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {init_name, init, num_envs, num_envs, es, false, false, true},
+      {out_name, out, ld_out, T, 4, true, true},
+  };
+  if (num_envs == 0 || T == 0) return RLCA_OK;
+  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
+  RLCA_TRY(check_aliasing(arrs, 5));
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = x; a.ld_r = ld_x;
+  a.boot = init;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = out; a.ld_o0 = ld_out;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
+  return launch(algo, dtype, a, stream);
+}
+
+int rlca_eligibility_trace(int64_t num_envs, int64_t T, int dtype, const void *x, int64_t ld_x,
+                           const uint8_t *terminated, int64_t ld_terminated,
+                           const uint8_t *truncated, int64_t ld_truncated, const void *z_init,
+                           float gamma, float lam, float *traces, int64_t ld_traces,
+                           void *stream) {
+  return forward_like(kEligibility, num_envs, T, dtype, x, ld_x, terminated, ld_terminated,
+                      truncated, ld_truncated, z_init, gamma, lam, traces, ld_traces, "z_init",
+                      "traces", stream);
+}
+
+int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype, const void *x, int64_t ld_x,
+                         const uint8_t *terminated, int64_t ld_terminated,
+                         const uint8_t *truncated, int64_t ld_truncated, const void *s_init,
+                         float *sums, int64_t ld_sums, void *stream) {
+  return forward_like(kCumsum, num_envs, T, dtype, x, ld_x, terminated, ld_terminated, truncated,
+                      ld_truncated, s_init, 1.f, 1.f, sums, ld_sums, "s_init", "sums", stream);
 }
 
 const char *rlca_last_error(void) { return t_last_error.c_str(); }

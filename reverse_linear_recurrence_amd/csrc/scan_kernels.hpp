@@ -42,7 +42,11 @@
 
 namespace rlca {
 
-enum Algo : int { kReturns = 0, kGae = 1, kTdLambda = 2, kVtrace = 3, kRetrace = 4 };
+enum Algo : int {
+  kReturns = 0, kGae = 1, kTdLambda = 2, kVtrace = 3, kRetrace = 4,
+  // forward-time mirrors: A_t = alpha_t + beta_t * A_{t-1}
+  kEligibility = 5, kCumsum = 6
+};
 
 using bf16_t = uint16_t;  // raw bfloat16 bits
 
@@ -81,6 +85,7 @@ struct Args {
 //   gae, td_lambda: h = r, v, term, trunc, trunc_values
 //   vtrace:         h = r, v, log_rho, term, trunc     (trunc_values cold)
 //   retrace:        h = r, q, eq, log_rho, term        (trunc cold)
+//   eligibility, cumsum: h = x (in r), term, trunc, initial carry [N], -
 // ldT is the common row stride of the hot [N,T] streams, ldX the stride of
 // values (gae, td_lambda, vtrace) or 1 if truncation flags are given
 // (retrace).  When the hot [N,T] streams do not share one stride, the
@@ -285,10 +290,11 @@ __device__ __forceinline__ int64_t late_v(int64_t x) {
 }
 
 template <int A> struct Uses {
+  static constexpr bool forward = A == kEligibility || A == kCumsum;
   static constexpr bool values = A == kGae || A == kTdLambda || A == kVtrace;  // V [N,T+1]
   static constexpr bool q = A == kRetrace;
   static constexpr bool log_rho = A == kVtrace || A == kRetrace;
-  static constexpr bool tv = A != kRetrace;
+  static constexpr bool tv = A == kReturns || A == kGae || A == kTdLambda || A == kVtrace;
   static constexpr bool two_outputs = A == kGae || A == kVtrace;
 };
 
@@ -315,6 +321,8 @@ struct Tile {
   float r[K], v[K + 1], lr[K + 1], eq[K], tv[K];
   // derived
   uint32_t te[K / 4], tr[K / 4];  // one byte per step, nonzero = flag set
+                                  // (forward: the flag of the step before)
+  bool at_start;                  // forward: the lane's span starts at t = 0
   float ts[K];                    // bootstraps read at truncated steps (Bits<> form)
   bool dense;                     // tv[] holds the bootstraps (else ts[])
 };
@@ -356,16 +364,21 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
   // lane's own reward bytes (the address of its reward load, so a cache hit)
   // and masked to zero after decoding.  The truncation test in finish_tile
   // then waits for the flags only, with every other load in flight.
+  // Forward recurrences use the flag of the step before each step: read the
+  // K bytes from t0 - 1 (from t0 at the row start; finish_tile then shifts
+  // in "no boundary" before step 0).
+  const int64_t f0 = Uses<A>::forward ? (t0 > 0 ? t0 - 1 : 0) : t0;
+  q.at_start = Uses<A>::forward && t0 == 0;
   const uint8_t *own = reinterpret_cast<const uint8_t *>(rp.r + t0);
   const uint8_t *trp = own;
   if constexpr (A == kRetrace) {
     // Cold stream: only a call with truncation flags waits for Args here.
     if (rp.has_tr) trp = p.trunc + late_v(rp.row) * p.ld_trunc + t0;
   } else {
-    trp = rp.has_tr ? rp.tr + t0 : own;
+    trp = rp.has_tr ? rp.tr + f0 : own;
   }
   ld_flags_raw<K>(trp, q.ftr);
-  ld_flags_raw<K>(rp.has_te ? rp.te + t0 : own, q.fte);
+  ld_flags_raw<K>(rp.has_te ? rp.te + f0 : own, q.fte);
   Ld<InT>::template vec<K>(rp.r + t0, q.r);
   if constexpr (U::values || U::q) {
     float vk[K];
@@ -438,6 +451,15 @@ __device__ __forceinline__ void finish_tile(const Args &p, const RowPtrs<InT> &r
                                             Tile<K> &x) {
   decode_flags<K>(x.ftr, x.tr);
   decode_flags<K>(x.fte, x.te);
+  if constexpr (Uses<A>::forward) {
+    if (x.at_start) {  // bytes t0 .. t0+K-1 were read: shift by one step
+#pragma unroll
+      for (int i = K / 4 - 1; i >= 0; --i) {
+        x.tr[i] = (x.tr[i] << 8) | (i > 0 ? x.tr[i - 1] >> 24 : 0u);
+        x.te[i] = (x.te[i] << 8) | (i > 0 ? x.te[i - 1] >> 24 : 0u);
+      }
+    }
+  }
 #pragma unroll
   for (int i = 0; i < K / 4; ++i) {
     x.tr[i] = rp.has_tr ? x.tr[i] : 0u;
@@ -458,14 +480,25 @@ __device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp,
   x.dense = false;
 #pragma unroll
   for (int i = 0; i < K / 4; ++i) { x.te[i] = 0; x.tr[i] = 0; }
+  x.at_start = false;
   if (lim > 0) {
-    if (rp.has_tr) {
-      const uint8_t *trp;
-      if constexpr (A == kRetrace) trp = p.trunc + late_v(rp.row) * p.ld_trunc;
-      else trp = rp.tr;
-      ld_flags_part<K>(trp + t0, lim, x.tr);
+    if constexpr (Uses<A>::forward) {
+      // The flag of the step before each step (none before t = 0).
+#pragma unroll
+      for (int e = 0; e < K; ++e) {
+        const bool in = e < lim && t0 + e > 0;
+        if (in && rp.has_tr && rp.tr[t0 + e - 1] != 0) x.tr[e >> 2] |= 1u << ((e & 3) * 8);
+        if (in && rp.has_te && rp.te[t0 + e - 1] != 0) x.te[e >> 2] |= 1u << ((e & 3) * 8);
+      }
+    } else {
+      if (rp.has_tr) {
+        const uint8_t *trp;
+        if constexpr (A == kRetrace) trp = p.trunc + late_v(rp.row) * p.ld_trunc;
+        else trp = rp.tr;
+        ld_flags_part<K>(trp + t0, lim, x.tr);
+      }
+      if (rp.has_te) ld_flags_part<K>(rp.te + t0, lim, x.te);
     }
-    if (rp.has_te) ld_flags_part<K>(rp.te + t0, lim, x.te);
     ld_part<InT, K>(rp.r + t0, lim, x.r);
     if constexpr (U::values) {
 #pragma unroll
@@ -516,6 +549,10 @@ __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, cons
       const float nv = te ? 0.f : (tr ? tv_at<InT, K>(x, j) : x.v[j + 1]);
       a_j = fminf(rho_bar, e) * (fmaf(gamma, nv, x.r[j]) - x.v[j]);
       b_j = done ? 0.f : gamma * (lam * fminf(c_bar, e));
+    } else if constexpr (Uses<A>::forward) {
+      // te, tr: flags of step t-1; a boundary there restarts at step t.
+      a_j = x.r[j];
+      b_j = done ? 0.f : (A == kCumsum ? 1.f : gl);
     } else {  // kRetrace
       a_j = (te ? x.r[j] : fmaf(gamma, x.eq[j], x.r[j])) - x.v[j];
       const bool has_next = j + 1 < lim;  // step t+1 lies inside the row
@@ -541,12 +578,25 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
   float al[K], be[K], ratio[K];
   coefficients<A, InT, K, kEdge>(x, lim, p, al, be, ratio);
 
-  // Fold the lane's steps: (a, b) = f_{t0} o ... o f_{t0+K-1}.
-  float a = al[K - 1], b = be[K - 1];
+  // Fold the lane's steps into one map of the incoming value: reverse,
+  // (a, b) = f_{t0} o ... o f_{t0+K-1}; forward, f_{t0+K-1} o ... o f_{t0}.
+  float a, b;
+  if constexpr (U::forward) {
+    a = al[0];
+    b = be[0];
 #pragma unroll
-  for (int j = K - 2; j >= 0; --j) {
-    a = fmaf(be[j], a, al[j]);
-    b = be[j] * b;
+    for (int j = 1; j < K; ++j) {
+      a = fmaf(be[j], a, al[j]);
+      b = be[j] * b;
+    }
+  } else {
+    a = al[K - 1];
+    b = be[K - 1];
+#pragma unroll
+    for (int j = K - 2; j >= 0; --j) {
+      a = fmaf(be[j], a, al[j]);
+      b = be[j] * b;
+    }
   }
 
   group_scan<kScanLanes>(a, b);
@@ -559,7 +609,8 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
     const float wa = readlane(a, 63), wb = readlane(b, 63);  // whole-wavefront map
     if (lane == 0) s_agg[buf][wave] = make_float2(wa, wb);
     __syncthreads();
-    // Wavefront 0 holds the latest steps of the tile: compose downward from it.
+    // Wavefront 0 holds the first span of the tile in scan order (reverse:
+    // the latest steps; forward: the earliest): compose from it onward.
     float xc = carry;
 #pragma unroll
     for (int w = 0; w < WPR; ++w) {
@@ -569,9 +620,12 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
     }
     carry_out = xc;
   }
-  // A at the earliest step of this lane's span ...
+  // A at the far end of this lane's span (reverse: its earliest step;
+  // forward: its latest) ...
   const float y = fmaf(b, cin, a);
-  // ... and just after its span: y of the next-later lane (lane - 1).
+  // ... and the value entering the lane's span: y of the previous lane in
+  // scan order (lane - 1), the next-later (reverse) or next-earlier (forward)
+  // span.
   float xin = dpp<0x138, 0xf>(y, cin);  // wave_shr:1
   if ((lane % kScanLanes) == 0) xin = cin;
   if constexpr (WPR == 1) {
@@ -586,8 +640,17 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
   const float pg_rho_bar = A == kVtrace ? late(p.pg_rho_bar) : 1.f;
   float o0[K], o1[K];
   float xa = xin;
+  if constexpr (U::forward) {
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+      xa = fmaf(be[j], xa, al[j]);
+      o0[j] = xa;
+      o1[j] = 0.f;
+    }
+  }
 #pragma unroll
   for (int j = K - 1; j >= 0; --j) {
+    if constexpr (U::forward) break;
     const float xn = xa;  // A_{t+1}
     xa = fmaf(be[j], xa, al[j]);
     o1[j] = 0.f;
@@ -709,6 +772,12 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     rp.has_te = h3 != nullptr;
     rp.has_tr = h4 != nullptr;
     rp.dense_tv = false;
+  } else if constexpr (Uses<A>::forward) {
+    rp.te = flag_row(h1, ld(p.ld_term));
+    rp.tr = flag_row(h2, ld(p.ld_trunc));
+    rp.has_te = h1 != nullptr;
+    rp.has_tr = h2 != nullptr;
+    rp.dense_tv = false;
   } else {  // kRetrace
     rp.v = in_row(h1, ld(p.ld_v));
     rp.eq = in_row(h2, ld(p.ld_eq));
@@ -720,16 +789,23 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     rp.dense_tv = false;
   }
 
-  float carry = 0.f;  // A at the end of the current tile (A_T for the last)
+  // The value entering the current tile: A_T before the last tile (reverse),
+  // A_{-1} before the first (forward).
+  float carry = 0.f;
   if constexpr (A == kReturns) {
     if (h4 != nullptr) carry = Ld<InT>::one(static_cast<const InT *>(h4) + rr);
+  } else if constexpr (Uses<A>::forward) {
+    if (h3 != nullptr) carry = Ld<InT>::one(static_cast<const InT *>(h3) + rr);
   }
 
   // Tiles are visited from the last (latest in time) to the first.  A ragged
   // last tile takes the element-wise path; every whole tile's loads are
   // issued while the tile after it (in time) is being computed.
   const int64_t ntiles = (T + kTile - 1) / kTile;
-  const int64_t lane_off = static_cast<int64_t>(kGroup - 1 - g) * K;
+  // Lane g's span in a tile: reverse recurrences scan lanes against time
+  // (g = 0 owns the latest steps), forward ones along it.
+  const int64_t lane_off =
+      static_cast<int64_t>(Uses<A>::forward ? g : kGroup - 1 - g) * K;
   auto t0_of = [&](int64_t c) { return c * kTile + lane_off; };
 
   if (ntiles == 1 && T == kTile) {
@@ -742,6 +818,45 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     return;
   }
   const bool ragged = T % kTile != 0;
+  if constexpr (Uses<A>::forward) {
+    // Tiles from the first to the last; the ragged one comes last.  Same
+    // two-buffer pipeline as below, in increasing c.
+    const int64_t nwhole = ragged ? ntiles - 1 : ntiles;
+    Tile<K> buf_a, buf_b;
+    int64_t c = 0;
+    if (nwhole > 0) {
+      issue_tile<A, InT, K>(p, rp, t0_of(0), T - t0_of(0), buf_a);
+      for (;;) {
+        {
+          finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
+          const int64_t cn = c + 1 < nwhole ? c + 1 : c;
+          issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
+          carry = tile_compute<A, InT, K, LPR, WPR, false>(p, rp, buf_a, t0_of(c), T - t0_of(c),
+                                                           row_ok, c, c + 1 < ntiles, lane, wave,
+                                                           carry, s_agg);
+        }
+        if (++c == nwhole) break;
+        {
+          finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
+          const int64_t cn = c + 1 < nwhole ? c + 1 : c;
+          issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
+          carry = tile_compute<A, InT, K, LPR, WPR, false>(p, rp, buf_b, t0_of(c), T - t0_of(c),
+                                                           row_ok, c, c + 1 < ntiles, lane, wave,
+                                                           carry, s_agg);
+        }
+        if (++c == nwhole) break;
+      }
+    }
+    if (ragged) {
+      const int64_t te0 = t0_of(ntiles - 1);
+      const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
+      Tile<K> x;
+      load_edge<A, InT, K>(p, rp, te0, lim, x);
+      tile_compute<A, InT, K, LPR, WPR, true>(p, rp, x, te0, lim, row_ok, ntiles - 1, false, lane,
+                                              wave, carry, s_agg);
+    }
+    return;
+  }
   int64_t c = ragged ? ntiles - 2 : ntiles - 1;  // latest whole tile
   // Two explicit buffers, alternating: tile c is decoded (and its sparse
   // bootstrap loads issued) before tile c-1's loads are issued into the other

@@ -53,6 +53,11 @@ WORKLOADS = {
                                     clips={"rho_bar": 1.0, "c_bar": 1.0, "pg_rho_bar": 1.0}),
     "gae_bf16_256x16384": Workload("gae_bf16_256x16384", "gae", 256, 16384, "bf16", 105,
                                    gamma=0.999, lam=0.97, p_term=0.0005, p_trunc=0.0002),
+    # Forward-time mirrors, at the GAE workload's shape and boundary rates.
+    "eligibility_4096x128": Workload("eligibility_4096x128", "eligibility", 4096, 128, "f32",
+                                     106, gamma=0.99, lam=0.95, p_term=0.005, p_trunc=0.002),
+    "cumsum_4096x128": Workload("cumsum_4096x128", "cumsum", 4096, 128, "f32", 107,
+                                gamma=1.0, lam=1.0, p_term=0.005, p_trunc=0.002),
 }
 
 _NEEDS = {
@@ -62,7 +67,11 @@ _NEEDS = {
     "vtrace": ("rewards", "values", "log_rhos"),
     "retrace": ("rewards", "q_taken", "exp_q_next", "log_rhos"),
     "vtrace+retrace": ("rewards", "values", "q_taken", "exp_q_next", "log_rhos"),
+    # forward-time algorithms: the per-step input x is drawn as "rewards"
+    "eligibility": ("rewards",),
+    "cumsum": ("rewards",),
 }
+_FORWARD = ("eligibility", "cumsum")
 
 
 def fp32_param(x: float) -> float:
@@ -112,7 +121,9 @@ def make_rollout(algo: str, num_envs: int, T: int, *, seed: int, dtype: str = "f
     out["terminated"] = (g.random((N, T)) < p_term).astype(np.uint8)
     if p_trunc is not None:
         out["truncated"] = (g.random((N, T)) < p_trunc).astype(np.uint8)
-        if dense_trunc_values:
+        if algo in _FORWARD:
+            pass  # no bootstrap values: forward recurrences only restart
+        elif dense_trunc_values:
             out["trunc_values"] = g.standard_normal((N, T), dtype=np.float32)
         else:
             out["trunc_values"] = np.zeros((N, T), np.float32)

@@ -11,7 +11,8 @@ from reverse_linear_recurrence_amd.synth import fp32_param
 
 TOL = {"f32": 1e-4, "bf16": 1e-2}
 
-ALGOS = ("returns", "gae", "td_lambda", "vtrace", "retrace")
+ALGOS = ("returns", "gae", "td_lambda", "vtrace", "retrace", "eligibility", "cumsum")
+FORWARD = ("eligibility", "cumsum")
 
 DEFAULT_PARAMS = dict(gamma=0.97, lam=0.9, rho_bar=1.0, c_bar=1.0, pg_rho_bar=1.0)
 
@@ -49,6 +50,13 @@ def run_gpu(algo, d, p, **kw):
         res = {"q_ret": rl.rlca_retrace(g("rewards"), g("q_taken"), g("exp_q_next"),
                                         g("log_rhos"), g("terminated"), g("truncated"),
                                         gamma=p["gamma"], lam=p["lam"], c_bar=p["c_bar"], **kw)}
+    elif algo == "eligibility":
+        res = {"traces": rl.rlca_eligibility_trace(g("rewards"), g("terminated"), g("truncated"),
+                                                   g("bootstrap"), gamma=p["gamma"],
+                                                   lam=p["lam"], **kw)}
+    elif algo == "cumsum":
+        res = {"sums": rl.rlca_episodic_cumsum(g("rewards"), g("terminated"), g("truncated"),
+                                               g("bootstrap"), **kw)}
     else:
         raise ValueError(algo)
     torch.cuda.synchronize()
@@ -78,6 +86,13 @@ def run_oracle(algo, d, p):
         return {"q_ret": oracle.retrace(g("rewards"), g("q_taken"), g("exp_q_next"), g("log_rhos"),
                                         g("terminated"), g("truncated"), gamma=p["gamma"],
                                         lam=p["lam"], c_bar=p["c_bar"])}
+    if algo == "eligibility":
+        return {"traces": oracle.eligibility_trace(g("rewards"), g("terminated"), g("truncated"),
+                                                   g("bootstrap"), gamma=p["gamma"],
+                                                   lam=p["lam"])}
+    if algo == "cumsum":
+        return {"sums": oracle.episodic_cumsum(g("rewards"), g("terminated"), g("truncated"),
+                                               g("bootstrap"))}
     raise ValueError(algo)
 
 
@@ -110,7 +125,7 @@ def random_inputs(algo, N, T, seed, dtype="f32", p_term=0.05, p_trunc=0.05, boot
     if algo == "retrace" and p_trunc:
         g = np.random.Generator(np.random.PCG64(seed + 7))
         d["truncated"] = torch.from_numpy((g.random((N, T)) < p_trunc).astype(np.uint8))
-    if algo == "returns" and bootstrap:
+    if algo in ("returns",) + FORWARD and bootstrap:
         g = np.random.Generator(np.random.PCG64(seed + 11))
         b = torch.from_numpy(g.standard_normal(N).astype(np.float32))
         d["bootstrap"] = b.to(torch.bfloat16) if dtype == "bf16" else b
