@@ -14,6 +14,12 @@ Flags are ``uint8``/``bool`` arrays of shape ``[N, T]``; ``None`` means "never".
 ``values`` has shape ``[N, T+1]``: column ``T`` is the window-end bootstrap.
 ``trunc_values`` ``[N, T]`` is read only where a truncation is not also a
 termination (termination wins).
+
+Window carries: ``carry_in [N]`` (None: 0) is the scan state just past the
+window end (reverse recurrences; ``bootstrap`` for returns) or just before its
+start (forward ones; ``z_init`` / ``s_init``).  With ``chunk=True`` a function
+also returns ``carry_out [N]`` (the neighbouring window's carry_in) and
+``carry_map [N, 2]`` = (a, b) with carry_out = a + b * carry_in.
 """
 import ctypes
 import os
@@ -34,18 +40,23 @@ def _load():
             build_oracle()
         lib = ctypes.CDLL(LIB)
         i64, dbl = ctypes.c_int64, ctypes.c_double
-        lib.oracle_returns.argtypes = [i64, i64, _D, _U8, _U8, _D, _D, dbl, _D]
-        lib.oracle_gae.argtypes = [i64, i64, _D, _D, _U8, _U8, _D, dbl, dbl, _D, _D]
-        lib.oracle_td_lambda.argtypes = [i64, i64, _D, _D, _U8, _U8, _D, dbl, dbl, _D]
+        lib.oracle_returns.argtypes = [i64, i64, _D, _U8, _U8, _D, _D, dbl, _D, _D, _D]
+        lib.oracle_gae.argtypes = [i64, i64, _D, _D, _U8, _U8, _D, dbl, dbl, _D, _D,
+                                   _D, _D, _D]
+        lib.oracle_td_lambda.argtypes = [i64, i64, _D, _D, _U8, _U8, _D, dbl, dbl, _D,
+                                         _D, _D, _D]
         lib.oracle_vtrace.argtypes = [i64, i64, _D, _D, _D, _U8, _U8, _D,
-                                      dbl, dbl, dbl, dbl, dbl, _D, _D]
+                                      dbl, dbl, dbl, dbl, dbl, _D, _D, _D, _D, _D]
         lib.oracle_retrace.argtypes = [i64, i64, _D, _D, _D, _D, _U8, _U8,
-                                       dbl, dbl, dbl, _D]
-        lib.oracle_eligibility_trace.argtypes = [i64, i64, _D, _U8, _U8, _D, dbl, dbl, _D]
-        lib.oracle_episodic_cumsum.argtypes = [i64, i64, _D, _U8, _U8, _D, _D]
+                                       dbl, dbl, dbl, _D, _D, _D, _D]
+        lib.oracle_eligibility_trace.argtypes = [i64, i64, _D, _U8, _U8, _D, dbl, dbl, _D,
+                                                 _D, _D]
+        lib.oracle_episodic_cumsum.argtypes = [i64, i64, _D, _U8, _U8, _D, _D, _D, _D]
+        lib.oracle_affine_scan.argtypes = [i64, i64, _D, _D, _U8, ctypes.c_int, _D,
+                                           _D, _D, _D]
         for f in (lib.oracle_returns, lib.oracle_gae, lib.oracle_td_lambda,
                   lib.oracle_vtrace, lib.oracle_retrace, lib.oracle_eligibility_trace,
-                  lib.oracle_episodic_cumsum):
+                  lib.oracle_episodic_cumsum, lib.oracle_affine_scan):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -84,9 +95,21 @@ def _check(rc, name):
         raise ValueError("oracle %s rejected its arguments" % name)
 
 
+class _Carry:
+    """carry_out [N] and carry map [N, 2] buffers of one call."""
+
+    def __init__(self, N):
+        self.out = np.empty(N, np.float64)
+        self.map = np.empty((N, 2), np.float64)
+        self.out_p = self.out.ctypes.data_as(_D)
+        self.map_p = self.map.ctypes.data_as(_D)
+
+
 def returns(rewards, terminated=None, truncated=None, trunc_values=None,
-            bootstrap=None, *, gamma):
-    """Discounted returns ``G [N, T]``; ``bootstrap [N]`` is the carry ``G_T`` (None: 0)."""
+            bootstrap=None, *, gamma, chunk=False):
+    """Discounted returns ``G [N, T]``; ``bootstrap [N]`` is the carry ``G_T`` (None: 0).
+
+    chunk=True: ``(G, carry_out, carry_map)``, carry_out = G_0."""
     r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
     N, T = r.shape
     te, tep = _u8(terminated, (N, T))
@@ -94,14 +117,18 @@ def returns(rewards, terminated=None, truncated=None, trunc_values=None,
     tv, tvp = _f64(trunc_values, (N, T))
     b, bp = _f64(bootstrap, (N,))
     out = np.empty((N, T), np.float64)
+    c = _Carry(N)
     _check(_load().oracle_returns(N, T, rp, tep, trp, tvp, bp, float(gamma),
-                                  out.ctypes.data_as(_D)), "returns")
-    return out
+                                  out.ctypes.data_as(_D), c.out_p, c.map_p), "returns")
+    return (out, c.out, c.map) if chunk else out
 
 
 def gae(rewards, values, terminated=None, truncated=None, trunc_values=None, *,
-        gamma, lam):
-    """GAE: returns ``(advantages, targets)``, each ``[N, T]``."""
+        gamma, lam, carry_in=None, chunk=False):
+    """GAE: returns ``(advantages, targets)``, each ``[N, T]``.
+
+    carry_in: A_T (advantage of the step after the window).  chunk=True adds
+    ``carry_out`` (= A_0) and ``carry_map``."""
     r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
     N, T = r.shape
     v, vp = _f64(values, (N, T + 1))
@@ -110,14 +137,20 @@ def gae(rewards, values, terminated=None, truncated=None, trunc_values=None, *,
     tv, tvp = _f64(trunc_values, (N, T))
     adv = np.empty((N, T), np.float64)
     tgt = np.empty((N, T), np.float64)
+    ci, cip = _f64(carry_in, (N,))
+    c = _Carry(N)
     _check(_load().oracle_gae(N, T, rp, vp, tep, trp, tvp, float(gamma), float(lam),
-                              adv.ctypes.data_as(_D), tgt.ctypes.data_as(_D)), "gae")
-    return adv, tgt
+                              adv.ctypes.data_as(_D), tgt.ctypes.data_as(_D), cip, c.out_p,
+                              c.map_p), "gae")
+    return (adv, tgt, c.out, c.map) if chunk else (adv, tgt)
 
 
 def td_lambda(rewards, values, terminated=None, truncated=None, trunc_values=None, *,
-              gamma, lam):
-    """TD(lambda) returns ``[N, T]``."""
+              gamma, lam, carry_in=None, chunk=False):
+    """TD(lambda) returns ``[N, T]``.
+
+    carry_in: G_T - V_T of the step after the window.  chunk=True adds
+    ``carry_out`` (= G_0 - V_0) and ``carry_map``."""
     r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
     N, T = r.shape
     v, vp = _f64(values, (N, T + 1))
@@ -125,14 +158,20 @@ def td_lambda(rewards, values, terminated=None, truncated=None, trunc_values=Non
     tr, trp = _u8(truncated, (N, T))
     tv, tvp = _f64(trunc_values, (N, T))
     out = np.empty((N, T), np.float64)
+    ci, cip = _f64(carry_in, (N,))
+    c = _Carry(N)
     _check(_load().oracle_td_lambda(N, T, rp, vp, tep, trp, tvp, float(gamma), float(lam),
-                                    out.ctypes.data_as(_D)), "td_lambda")
-    return out
+                                    out.ctypes.data_as(_D), cip, c.out_p, c.map_p), "td_lambda")
+    return (out, c.out, c.map) if chunk else out
 
 
 def vtrace(rewards, values, log_rhos, terminated=None, truncated=None, trunc_values=None,
-           *, gamma, lam, rho_bar=1.0, c_bar=1.0, pg_rho_bar=1.0):
-    """V-trace: returns ``(vs, pg_advantages)``, each ``[N, T]``."""
+           *, gamma, lam, rho_bar=1.0, c_bar=1.0, pg_rho_bar=1.0, carry_in=None,
+           chunk=False):
+    """V-trace: returns ``(vs, pg_advantages)``, each ``[N, T]``.
+
+    carry_in: vs_T - V_T of the step after the window.  chunk=True adds
+    ``carry_out`` (= vs_0 - V_0) and ``carry_map``."""
     r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
     N, T = r.shape
     v, vp = _f64(values, (N, T + 1))
@@ -142,15 +181,21 @@ def vtrace(rewards, values, log_rhos, terminated=None, truncated=None, trunc_val
     tv, tvp = _f64(trunc_values, (N, T))
     vs = np.empty((N, T), np.float64)
     pg = np.empty((N, T), np.float64)
+    ci, cip = _f64(carry_in, (N,))
+    c = _Carry(N)
     _check(_load().oracle_vtrace(N, T, rp, vp, lrp, tep, trp, tvp, float(gamma), float(lam),
                                  float(rho_bar), float(c_bar), float(pg_rho_bar),
-                                 vs.ctypes.data_as(_D), pg.ctypes.data_as(_D)), "vtrace")
-    return vs, pg
+                                 vs.ctypes.data_as(_D), pg.ctypes.data_as(_D), cip, c.out_p,
+                                 c.map_p), "vtrace")
+    return (vs, pg, c.out, c.map) if chunk else (vs, pg)
 
 
 def retrace(rewards, q_taken, exp_q_next, log_rhos, terminated=None, truncated=None, *,
-            gamma, lam, c_bar=1.0):
-    """Retrace(lambda) targets ``Q^ret [N, T]``."""
+            gamma, lam, c_bar=1.0, carry_in=None, chunk=False):
+    """Retrace(lambda) targets ``Q^ret [N, T]``.
+
+    carry_in: c_T * (Qret_T - Q_T) of the step after the window.  chunk=True
+    adds ``carry_out`` (= c_0 * (Qret_0 - Q_0)) and ``carry_map``."""
     r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
     N, T = r.shape
     q, qp = _f64(q_taken, (N, T))
@@ -159,32 +204,61 @@ def retrace(rewards, q_taken, exp_q_next, log_rhos, terminated=None, truncated=N
     te, tep = _u8(terminated, (N, T))
     tr, trp = _u8(truncated, (N, T))
     out = np.empty((N, T), np.float64)
+    ci, cip = _f64(carry_in, (N,))
+    c = _Carry(N)
     _check(_load().oracle_retrace(N, T, rp, qp, eqp, lrp, tep, trp, float(gamma), float(lam),
-                                  float(c_bar), out.ctypes.data_as(_D)), "retrace")
-    return out
+                                  float(c_bar), out.ctypes.data_as(_D), cip, c.out_p, c.map_p),
+           "retrace")
+    return (out, c.out, c.map) if chunk else out
 
 
-def eligibility_trace(x, terminated=None, truncated=None, z_init=None, *, gamma, lam):
-    """Forward accumulating trace ``z [N, T]``: z_t = x_t + gamma*lam*(1-done_{t-1}) z_{t-1}."""
+def eligibility_trace(x, terminated=None, truncated=None, z_init=None, *, gamma, lam,
+                      chunk=False):
+    """Forward accumulating trace ``z [N, T]``: z_t = x_t + gamma*lam*(1-done_{t-1}) z_{t-1}.
+
+    chunk=True adds ``carry_out`` (= z_{T-1}, 0 if done_{T-1}) and ``carry_map``."""
     a, ap = _f64(x, np.shape(_as_numpy(x)))
     N, T = a.shape
     te, tep = _u8(terminated, (N, T))
     tr, trp = _u8(truncated, (N, T))
     z0, z0p = _f64(z_init, (N,))
     out = np.empty((N, T), np.float64)
+    c = _Carry(N)
     _check(_load().oracle_eligibility_trace(N, T, ap, tep, trp, z0p, float(gamma), float(lam),
-                                            out.ctypes.data_as(_D)), "eligibility_trace")
-    return out
+                                            out.ctypes.data_as(_D), c.out_p, c.map_p),
+           "eligibility_trace")
+    return (out, c.out, c.map) if chunk else out
 
 
-def episodic_cumsum(x, terminated=None, truncated=None, s_init=None):
-    """Forward episodic prefix sum ``S [N, T]``: S_t = x_t + (1-done_{t-1}) S_{t-1}."""
+def episodic_cumsum(x, terminated=None, truncated=None, s_init=None, *, chunk=False):
+    """Forward episodic prefix sum ``S [N, T]``: S_t = x_t + (1-done_{t-1}) S_{t-1}.
+
+    chunk=True adds ``carry_out`` (= S_{T-1}, 0 if done_{T-1}) and ``carry_map``."""
     a, ap = _f64(x, np.shape(_as_numpy(x)))
     N, T = a.shape
     te, tep = _u8(terminated, (N, T))
     tr, trp = _u8(truncated, (N, T))
     s0, s0p = _f64(s_init, (N,))
     out = np.empty((N, T), np.float64)
-    _check(_load().oracle_episodic_cumsum(N, T, ap, tep, trp, s0p, out.ctypes.data_as(_D)),
-           "episodic_cumsum")
-    return out
+    c = _Carry(N)
+    _check(_load().oracle_episodic_cumsum(N, T, ap, tep, trp, s0p, out.ctypes.data_as(_D),
+                                          c.out_p, c.map_p), "episodic_cumsum")
+    return (out, c.out, c.map) if chunk else out
+
+
+def affine_scan(alpha, beta, reset=None, carry_in=None, *, reverse=True):
+    """Segmented affine scan ``A [N, T]`` with ``carry_out [N]`` and ``carry_map [N, 2]``.
+
+    reverse: A_t = alpha_t + beta'_t A_{t+1} (A_T = carry_in); else
+    A_t = alpha_t + beta'_t A_{t-1} (A_{-1} = carry_in); beta'_t = 0 where
+    reset_t, else beta_t.  Returns ``(A, carry_out, carry_map)``."""
+    a, ap = _f64(alpha, np.shape(_as_numpy(alpha)))
+    N, T = a.shape
+    b, bp = _f64(beta, (N, T))
+    rs, rsp = _u8(reset, (N, T))
+    ci, cip = _f64(carry_in, (N,))
+    out = np.empty((N, T), np.float64)
+    c = _Carry(N)
+    _check(_load().oracle_affine_scan(N, T, ap, bp, rsp, 1 if reverse else 0, cip,
+                                      out.ctypes.data_as(_D), c.out_p, c.map_p), "affine_scan")
+    return out, c.out, c.map

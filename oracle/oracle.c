@@ -35,6 +35,25 @@
  *       tv_t              if boot_t   (value of the true final observation)
  *       V_{t+1}           otherwise   (V has T+1 columns; V_T closes the window)
  *
+ * Window carries (rl-triton, Method 3 "rollout windows"; Method 1: the
+ * operator is associative, so a rollout may be cut along time).  A rollout
+ * longer than one window is processed as consecutive windows.  Per row:
+ *   carry_in   the scan state just past the window end (reverse recurrences)
+ *              or just before its start (forward ones), in the units each
+ *              function states; NULL means 0, the plain windowed result.
+ *              (returns: the bootstrap; forward mirrors: the initial value.)
+ *   carry_out  [N], NULL = not wanted: the value the neighbouring window
+ *              (the earlier one for reverse recurrences, the later one for
+ *              forward ones) takes as its carry_in, so that consecutive
+ *              windows reproduce the result of one long window.
+ *   map_out    [N, 2], NULL = not wanted: (a, b) with
+ *              carry_out = a + b * carry_in for every carry_in.  a is
+ *              carry_out computed from carry 0 (a second copy of the state,
+ *              suffix 0, run from 0 beside the real one); b is its derivative
+ *              with respect to carry_in (forward-mode differentiation of the
+ *              same loop: a variable prefixed d, updated beside the state).
+ *              Windows evaluated independently chain through these maps.
+ *
  * Every function returns 0 on success and -1 on a NULL required pointer or a
  * negative size.
  */
@@ -47,6 +66,18 @@
 static int flag_at(const uint8_t *f, int64_t n, int64_t t, int64_t T)
 {
     return f != NULL && AT(f, n, t, T) != 0;
+}
+
+/* Store the carry and the carry map of row n (either pointer may be NULL). */
+static void put_carry(double *carry_out, double *map_out, int64_t n, double carry,
+                      double a, double b)
+{
+    if (carry_out != NULL)
+        carry_out[n] = carry;
+    if (map_out != NULL) {
+        map_out[2 * n] = a;
+        map_out[2 * n + 1] = b;
+    }
 }
 
 /* Successor value of step t (see the header).  v is [N, T+1]. */
@@ -66,28 +97,37 @@ static double next_value(const double *v, const double *tv, const uint8_t *term,
  *   G_t = r_t                      after a termination,
  *   G_t = r_t + gamma * tv_t       after a truncation,
  *   G_T = B                        per-row window bootstrap (NULL: 0).
- * Here the window bootstrap lives in the carry A_T (Method 3, rollout windows).
+ * Here the window bootstrap lives in the carry A_T (Method 3, rollout windows):
+ * carry_in is B, carry_out is G_0.
  */
 int oracle_returns(int64_t N, int64_t T, const double *r, const uint8_t *term,
                    const uint8_t *trunc, const double *tv, const double *bootstrap,
-                   double gamma, double *G)
+                   double gamma, double *G, double *carry_out, double *map_out)
 {
     if (N < 0 || T < 0 || (N > 0 && T > 0 && (r == NULL || G == NULL)) ||
         (trunc != NULL && tv == NULL))
         return -1;
     for (int64_t n = 0; n < N; ++n) {
         double g = bootstrap != NULL ? bootstrap[n] : 0.0;
+        double g0 = 0.0, dg = 1.0;
         for (int64_t t = T - 1; t >= 0; --t) {
-            double succ;
-            if (flag_at(term, n, t, T))
-                succ = 0.0;
-            else if (flag_at(trunc, n, t, T))
-                succ = AT(tv, n, t, T);
-            else
+            double succ, succ0, dsucc;
+            if (flag_at(term, n, t, T)) {
+                succ = succ0 = dsucc = 0.0;
+            } else if (flag_at(trunc, n, t, T)) {
+                succ = succ0 = AT(tv, n, t, T);
+                dsucc = 0.0;
+            } else {
                 succ = g;
+                succ0 = g0;
+                dsucc = dg;
+            }
             g = AT(r, n, t, T) + gamma * succ;
+            g0 = AT(r, n, t, T) + gamma * succ0;
+            dg = gamma * dsucc;
             AT(G, n, t, T) = g;
         }
+        put_carry(carry_out, map_out, n, g, g0, dg);
     }
     return 0;
 }
@@ -98,28 +138,35 @@ int oracle_returns(int64_t N, int64_t T, const double *r, const uint8_t *term,
  *   delta_t = r_t + gamma * next_value_t - V_t
  *   A_t     = delta_t + gamma*lam * A_{t+1}    if not done_t
  *   A_t     = delta_t                          if done_t
- *   A_T     = 0: the window bootstrap V_T enters through delta_{T-1}.
+ *   A_T     = carry_in (NULL: 0): the window bootstrap V_T enters through
+ *             delta_{T-1}; carry_in is the advantage A_T of the step after
+ *             the window, and carry_out is A_0.
  *   targets_t = A_t + V_t.
  */
 int oracle_gae(int64_t N, int64_t T, const double *r, const double *v,
                const uint8_t *term, const uint8_t *trunc, const double *tv,
-               double gamma, double lam, double *adv, double *targets)
+               double gamma, double lam, double *adv, double *targets,
+               const double *carry_in, double *carry_out, double *map_out)
 {
     if (N < 0 || T < 0 || (trunc != NULL && tv == NULL))
         return -1;
     if (N > 0 && T > 0 && (r == NULL || v == NULL || adv == NULL))
         return -1;
     for (int64_t n = 0; n < N; ++n) {
-        double a = 0.0;
+        double a = carry_in != NULL ? carry_in[n] : 0.0;
+        double a0 = 0.0, da = 1.0;
         for (int64_t t = T - 1; t >= 0; --t) {
             double vt = AT(v, n, t, T + 1);
             double delta = AT(r, n, t, T) + gamma * next_value(v, tv, term, trunc, n, t, T) - vt;
             int done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);
             a = done ? delta : delta + gamma * lam * a;
+            a0 = done ? delta : delta + gamma * lam * a0;
+            da = done ? 0.0 : gamma * lam * da;
             AT(adv, n, t, T) = a;
             if (targets != NULL)
                 AT(targets, n, t, T) = a + vt;
         }
+        put_carry(carry_out, map_out, n, a, a0, da);
     }
     return 0;
 }
@@ -129,29 +176,39 @@ int oracle_gae(int64_t N, int64_t T, const double *r, const double *v,
  * (recursive) lambda-return of Sutton & Barto with episode cuts:
  *   G_t = r_t + gamma * next_value_t                                if done_t
  *   G_t = r_t + gamma * ((1 - lam) * V_{t+1} + lam * G_{t+1})       otherwise
- *   G_T = V_T (the window bootstrap; equivalently (1-lam)V_T + lam V_T).
- * This form is independent of the GAE function above; the two agree as
- * G_t = A_t + V_t only in exact arithmetic.
+ *   G_T = V_T + carry_in (the window bootstrap, plus the lambda-return
+ *         excess G_T - V_T of the step after the window; NULL: 0).
+ * carry_out is G_0 - V_0.  This form is independent of the GAE function
+ * above; the two agree as G_t = A_t + V_t only in exact arithmetic.
  */
 int oracle_td_lambda(int64_t N, int64_t T, const double *r, const double *v,
                      const uint8_t *term, const uint8_t *trunc, const double *tv,
-                     double gamma, double lam, double *ret)
+                     double gamma, double lam, double *ret,
+                     const double *carry_in, double *carry_out, double *map_out)
 {
     if (N < 0 || T < 0 || (trunc != NULL && tv == NULL))
         return -1;
     if (N > 0 && T > 0 && (r == NULL || v == NULL || ret == NULL))
         return -1;
     for (int64_t n = 0; n < N; ++n) {
-        double g = AT(v, n, T, T + 1);
+        double g = AT(v, n, T, T + 1) + (carry_in != NULL ? carry_in[n] : 0.0);
+        double g0 = AT(v, n, T, T + 1), dg = 1.0;
         for (int64_t t = T - 1; t >= 0; --t) {
             int done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);
             double rt = AT(r, n, t, T);
-            if (done)
+            if (done) {
                 g = rt + gamma * next_value(v, tv, term, trunc, n, t, T);
-            else
+                g0 = g;
+                dg = 0.0;
+            } else {
                 g = rt + gamma * ((1.0 - lam) * AT(v, n, t + 1, T + 1) + lam * g);
+                g0 = rt + gamma * ((1.0 - lam) * AT(v, n, t + 1, T + 1) + lam * g0);
+                dg = gamma * lam * dg;
+            }
             AT(ret, n, t, T) = g;
         }
+        double v0 = AT(v, n, 0, T + 1);
+        put_carry(carry_out, map_out, n, g - v0, g0 - v0, dg);
     }
     return 0;
 }
@@ -164,22 +221,26 @@ int oracle_td_lambda(int64_t N, int64_t T, const double *r, const double *v,
  *   v_t    = V_t + rho_t * (r_t + gamma * next_value_t - V_t)
  *                + gamma * c_t * (v_{t+1} - V_{t+1})      (the last term only
  *                                                          if not done_t)
- *   v_T    = V_T (window end: the correction beyond the window is zero).
+ *   v_T    = V_T + carry_in (window end: the correction v_T - V_T beyond
+ *            the window, zero when carry_in is NULL).
  *   pg_t   = min(pg_rho_bar, exp(log_rho_t)) * (r_t + gamma * nv_t - V_t),
  *            nv_t = 0 if term_t, tv_t if a truncation, v_{t+1} otherwise.
- * pg may be NULL.
+ * pg may be NULL.  carry_out is v_0 - V_0.
  */
 int oracle_vtrace(int64_t N, int64_t T, const double *r, const double *v,
                   const double *log_rho, const uint8_t *term, const uint8_t *trunc,
                   const double *tv, double gamma, double lam, double rho_bar,
-                  double c_bar, double pg_rho_bar, double *vs, double *pg)
+                  double c_bar, double pg_rho_bar, double *vs, double *pg,
+                  const double *carry_in, double *carry_out, double *map_out)
 {
     if (N < 0 || T < 0 || (trunc != NULL && tv == NULL))
         return -1;
     if (N > 0 && T > 0 && (r == NULL || v == NULL || log_rho == NULL || vs == NULL))
         return -1;
     for (int64_t n = 0; n < N; ++n) {
-        double v_next = AT(v, n, T, T + 1); /* v_{t+1}, starting with v_T = V_T */
+        /* v_{t+1}, starting with v_T */
+        double v_next = AT(v, n, T, T + 1) + (carry_in != NULL ? carry_in[n] : 0.0);
+        double v_next0 = AT(v, n, T, T + 1), dv_next = 1.0;
         for (int64_t t = T - 1; t >= 0; --t) {
             double ratio = exp(AT(log_rho, n, t, T));
             double rho = fmin(rho_bar, ratio);
@@ -190,15 +251,23 @@ int oracle_vtrace(int64_t N, int64_t T, const double *r, const double *v,
             int done = term_t || flag_at(trunc, n, t, T);
             double nv = next_value(v, tv, term, trunc, n, t, T);
             double vs_t = vt + rho * (rt + gamma * nv - vt);
-            if (!done)
+            double vs0_t = vs_t, dvs_t = 0.0;
+            if (!done) {
                 vs_t += gamma * c * (v_next - AT(v, n, t + 1, T + 1));
+                vs0_t += gamma * c * (v_next0 - AT(v, n, t + 1, T + 1));
+                dvs_t = gamma * c * dv_next;
+            }
             if (pg != NULL) {
                 double nvs = term_t ? 0.0 : (done ? AT(tv, n, t, T) : v_next);
                 AT(pg, n, t, T) = fmin(pg_rho_bar, ratio) * (rt + gamma * nvs - vt);
             }
             AT(vs, n, t, T) = vs_t;
             v_next = vs_t;
+            v_next0 = vs0_t;
+            dv_next = dvs_t;
         }
+        double v0 = AT(v, n, 0, T + 1);
+        put_carry(carry_out, map_out, n, v_next - v0, v_next0 - v0, dv_next);
     }
     return 0;
 }
@@ -212,31 +281,51 @@ int oracle_vtrace(int64_t N, int64_t T, const double *r, const double *v,
  *                                                           and t < T-1)
  * where Q_t = Q(s_t, a_t) and EQ_t = E_pi Q(s_{t+1}, .).  At a truncation the
  * supplied EQ_t (value of the true final state) is kept and only the trace is
- * cut; at a termination EQ_t is dropped.  At t = T-1 the correction term is
- * absent because c_T and Q_T lie outside the window: EQ_{T-1} is the window
- * bootstrap, in alpha_{T-1} (Method 3, rollout windows).
+ * cut; at a termination EQ_t is dropped.  At t = T-1 the correction
+ * c_T * (Qret_T - Q_T) involves the step after the window: it is carry_in
+ * (NULL: 0, the plain window, where EQ_{T-1} is the window bootstrap, in
+ * alpha_{T-1}; Method 3, rollout windows).  carry_out is the same quantity
+ * for the window's first step, c_0 * (Qret_0 - Q_0).
  */
 int oracle_retrace(int64_t N, int64_t T, const double *r, const double *q,
                    const double *eq, const double *log_rho, const uint8_t *term,
                    const uint8_t *trunc, double gamma, double lam, double c_bar,
-                   double *qret)
+                   double *qret, const double *carry_in, double *carry_out,
+                   double *map_out)
 {
     if (N < 0 || T < 0)
         return -1;
     if (N > 0 && T > 0 && (r == NULL || q == NULL || eq == NULL || log_rho == NULL || qret == NULL))
         return -1;
     for (int64_t n = 0; n < N; ++n) {
-        double qret_next = 0.0;
+        double qret_next = 0.0, qret_next0 = 0.0, dqret_next = 0.0;
+        double carry = carry_in != NULL ? carry_in[n] : 0.0;
         for (int64_t t = T - 1; t >= 0; --t) {
             int term_t = flag_at(term, n, t, T);
             int done = term_t || flag_at(trunc, n, t, T);
             double target = AT(r, n, t, T) + (term_t ? 0.0 : gamma * AT(eq, n, t, T));
+            double target0 = target, dtarget = 0.0;
             if (!done && t < T - 1) {
                 double c_next = lam * fmin(c_bar, exp(AT(log_rho, n, t + 1, T)));
                 target += gamma * c_next * (qret_next - AT(q, n, t + 1, T));
+                target0 += gamma * c_next * (qret_next0 - AT(q, n, t + 1, T));
+                dtarget = gamma * c_next * dqret_next;
+            } else if (!done) { /* t = T-1: the correction from the step after the window */
+                target += gamma * carry;
+                dtarget = gamma;
             }
             AT(qret, n, t, T) = target;
             qret_next = target;
+            qret_next0 = target0;
+            dqret_next = dtarget;
+        }
+        if (T > 0) {
+            double c0 = lam * fmin(c_bar, exp(AT(log_rho, n, 0, T)));
+            double q0 = AT(q, n, 0, T);
+            put_carry(carry_out, map_out, n, c0 * (qret_next - q0), c0 * (qret_next0 - q0),
+                      c0 * dqret_next);
+        } else {
+            put_carry(carry_out, map_out, n, carry, 0.0, 1.0);
         }
     }
     return 0;
@@ -248,8 +337,8 @@ int oracle_retrace(int64_t N, int64_t T, const double *r, const double *q,
  *     A_t = alpha_t + beta_t * A_{t-1},   t = 0 .. T-1.
  * An episode boundary after step t-1 (done_{t-1}) restarts the recurrence at
  * step t.  A_{-1} is a per-row carry from before the window (NULL: 0); it is
- * used as given (the caller zeroes it if the previous window ended an
- * episode).
+ * used as given.  carry_out is what the next window's first step receives:
+ * A_{T-1}, or 0 if the episode ends after step T-1 (done_{T-1}).
  */
 
 /* Accumulating eligibility trace:
@@ -257,7 +346,7 @@ int oracle_retrace(int64_t N, int64_t T, const double *r, const double *q,
  *   z_t = x_t                         if done_{t-1};   z_{-1} = z_init. */
 int oracle_eligibility_trace(int64_t N, int64_t T, const double *x, const uint8_t *term,
                              const uint8_t *trunc, const double *z_init, double gamma,
-                             double lam, double *z)
+                             double lam, double *z, double *carry_out, double *map_out)
 {
     if (N < 0 || T < 0)
         return -1;
@@ -265,13 +354,22 @@ int oracle_eligibility_trace(int64_t N, int64_t T, const double *x, const uint8_
         return -1;
     for (int64_t n = 0; n < N; ++n) {
         double prev = z_init != NULL ? z_init[n] : 0.0;
+        double prev0 = 0.0, dprev = 1.0;
         int prev_done = 0;
         for (int64_t t = 0; t < T; ++t) {
+            double z0t = AT(x, n, t, T) + (prev_done ? 0.0 : gamma * lam * prev0);
+            double dzt = prev_done ? 0.0 : gamma * lam * dprev;
+            prev0 = z0t;
+            dprev = dzt;
             double zt = AT(x, n, t, T) + (prev_done ? 0.0 : gamma * lam * prev);
             AT(z, n, t, T) = zt;
             prev = zt;
             prev_done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);
         }
+        if (prev_done)
+            put_carry(carry_out, map_out, n, 0.0, 0.0, 0.0);
+        else
+            put_carry(carry_out, map_out, n, prev, prev0, dprev);
     }
     return 0;
 }
@@ -280,7 +378,8 @@ int oracle_eligibility_trace(int64_t N, int64_t T, const double *x, const uint8_
  *   S_t = x_t + S_{t-1}   if not done_{t-1},
  *   S_t = x_t             if done_{t-1};   S_{-1} = s_init. */
 int oracle_episodic_cumsum(int64_t N, int64_t T, const double *x, const uint8_t *term,
-                           const uint8_t *trunc, const double *s_init, double *s)
+                           const uint8_t *trunc, const double *s_init, double *s,
+                           double *carry_out, double *map_out)
 {
     if (N < 0 || T < 0)
         return -1;
@@ -288,13 +387,54 @@ int oracle_episodic_cumsum(int64_t N, int64_t T, const double *x, const uint8_t 
         return -1;
     for (int64_t n = 0; n < N; ++n) {
         double prev = s_init != NULL ? s_init[n] : 0.0;
+        double prev0 = 0.0, dprev = 1.0;
         int prev_done = 0;
         for (int64_t t = 0; t < T; ++t) {
+            double s0t = AT(x, n, t, T) + (prev_done ? 0.0 : prev0);
+            double dst = prev_done ? 0.0 : dprev;
+            prev0 = s0t;
+            dprev = dst;
             double st = AT(x, n, t, T) + (prev_done ? 0.0 : prev);
             AT(s, n, t, T) = st;
             prev = st;
             prev_done = flag_at(term, n, t, T) || flag_at(trunc, n, t, T);
         }
+        double keep = prev_done ? 0.0 : 1.0; /* nothing crosses an episode end */
+        put_carry(carry_out, map_out, n, keep * prev, keep * prev0, keep * dprev);
+    }
+    return 0;
+}
+
+/*
+ * Generic segmented affine scan (rl-triton, Method 1: eq. R with arbitrary
+ * coefficient sequences, of which every algorithm above is an instance).
+ *   reverse != 0:  A_t = alpha_t + beta'_t * A_{t+1},  t = T-1 .. 0,  A_T = carry_in
+ *   reverse == 0:  A_t = alpha_t + beta'_t * A_{t-1},  t = 0 .. T-1,  A_{-1} = carry_in
+ * with beta'_t = 0 where reset_t is set (step t starts a segment: nothing
+ * flows into it from its neighbour) and beta_t elsewhere; reset NULL: never.
+ * carry_in NULL: 0.  carry_out is the last state computed: A_0 (reverse) or
+ * A_{T-1} (forward); a reset in the next window is that window's own flag.
+ */
+int oracle_affine_scan(int64_t N, int64_t T, const double *alpha, const double *beta,
+                       const uint8_t *reset, int reverse, const double *carry_in,
+                       double *out, double *carry_out, double *map_out)
+{
+    if (N < 0 || T < 0)
+        return -1;
+    if (N > 0 && T > 0 && (alpha == NULL || beta == NULL || out == NULL))
+        return -1;
+    for (int64_t n = 0; n < N; ++n) {
+        double a = carry_in != NULL ? carry_in[n] : 0.0;
+        double a0 = 0.0, da = 1.0;
+        for (int64_t i = 0; i < T; ++i) {
+            int64_t t = reverse ? T - 1 - i : i;
+            double b = flag_at(reset, n, t, T) ? 0.0 : AT(beta, n, t, T);
+            a = AT(alpha, n, t, T) + b * a;
+            a0 = AT(alpha, n, t, T) + b * a0;
+            da = b * da;
+            AT(out, n, t, T) = a;
+        }
+        put_carry(carry_out, map_out, n, a, a0, da);
     }
     return 0;
 }

@@ -203,3 +203,32 @@ def episodic_cumsum(x, term, trunc, s_init):
     """S_t = sum of x over the steps of t's episode up to t (+ s_init if that
     episode began before the window)."""
     return eligibility_trace(x, term, trunc, s_init, 1)
+
+
+def affine_scan(alpha, beta, reset, carry, reverse):
+    """Sum form of the segmented affine scan, row by row.
+
+    Reverse:  A_t = sum_{k=t}^{T-1} (prod_{j=t}^{k-1} b_j) alpha_k
+                    + (prod_{j=t}^{T-1} b_j) carry
+    Forward:  A_t = sum_{k=0}^{t} (prod_{j=k+1}^{t} b_j) alpha_k
+                    + (prod_{j=0}^{t} b_j) carry
+    with b_j = 0 where reset_j is set, beta_j otherwise.  Every product is
+    formed afresh for every (t, k): O(T^3), tiny inputs only.
+    """
+    out = []
+    for n in range(len(alpha)):
+        T = len(alpha[n])
+        b = [0 if (reset is not None and reset[n][j]) else beta[n][j] for j in range(T)]
+        c = 0 if carry is None else carry[n]
+        row = []
+        for t in range(T):
+            ks = range(t, T) if reverse else range(0, t + 1)
+            total = 0
+            for k in ks:
+                js = range(t, k) if reverse else range(k + 1, t + 1)
+                total += math.prod(b[j] for j in js) * alpha[n][k]
+            js = range(t, T) if reverse else range(0, t + 1)
+            total += math.prod(b[j] for j in js) * c
+            row.append(total)
+        out.append(row)
+    return out

@@ -62,6 +62,33 @@ MUTANTS = [
      "            double st = AT(x, n, t, T) + (prev_done ? 0.0 : prev);\n"
      "            AT(s, n, t, T) = st;\n            prev = st;\n"
      "            prev_done = flag_at(term, n, t, T);"),
+    # window carries and the generic affine scan
+    ("gae_carry_in_dropped",
+     "double a = carry_in != NULL ? carry_in[n] : 0.0;\n        double a0 = 0.0, da = 1.0;\n"
+     "        for (int64_t t = T - 1;",
+     "double a = 0.0;\n        double a0 = 0.0, da = 1.0;\n        for (int64_t t = T - 1;"),
+    ("gae_map_derivative_ignores_done", "da = done ? 0.0 : gamma * lam * da;",
+     "da = gamma * lam * da;"),
+    ("td_lambda_carry_out_keeps_value", "put_carry(carry_out, map_out, n, g - v0, g0 - v0, dg);",
+     "put_carry(carry_out, map_out, n, g, g0 - v0, dg);"),
+    ("vtrace_pg_ignores_carry", "double nvs = term_t ? 0.0 : (done ? AT(tv, n, t, T) : v_next);",
+     "double nvs = term_t ? 0.0 : (done ? AT(tv, n, t, T) : v_next0);"),
+    ("vtrace_map_trace_unclipped", "dvs_t = gamma * c * dv_next;", "dvs_t = gamma * lam * dv_next;"),
+    ("retrace_carry_out_without_trace", "c0 * (qret_next - q0), c0 * (qret_next0 - q0),",
+     "(qret_next - q0), c0 * (qret_next0 - q0),"),
+    ("retrace_carry_undiscounted", "target += gamma * carry;", "target += carry;"),
+    ("returns_map_keeps_truncated_carry",
+     "succ = succ0 = AT(tv, n, t, T);\n                dsucc = 0.0;",
+     "succ = succ0 = AT(tv, n, t, T);\n                dsucc = dg;"),
+    ("eligibility_carry_out_unmasked",
+     "        if (prev_done)\n            put_carry(carry_out, map_out, n, 0.0, 0.0, 0.0);\n"
+     "        else\n            put_carry", "        put_carry"),
+    ("cumsum_carry_out_unmasked", "double keep = prev_done ? 0.0 : 1.0;", "double keep = 1.0;"),
+    ("affine_reset_ignored", "double b = flag_at(reset, n, t, T) ? 0.0 : AT(beta, n, t, T);",
+     "double b = AT(beta, n, t, T);"),
+    ("affine_direction_swapped", "int64_t t = reverse ? T - 1 - i : i;",
+     "int64_t t = reverse ? i : T - 1 - i;"),
+    ("affine_map_from_carry", "a0 = AT(alpha, n, t, T) + b * a0;", "a0 = AT(alpha, n, t, T) + b * a;"),
 ]
 
 PIN_CASES = [
@@ -85,6 +112,17 @@ PIN_CASES = [
     (pins.test_forward_oracle_matches_forward_sums, dict(seed=82, T=13)),
     (pins.test_forward_exhaustive_boundaries, {}),
     (pins.test_forward_no_leak_bitwise, {}),
+] + [(pins.test_window_split_reproduces_one_long_window, dict(kind=k, seed=91))
+     for k in pins.CARRY_KINDS] + [
+    (pins.test_carry_map_is_the_affine_map_of_the_carry, dict(kind=k)) for k in pins.CARRY_KINDS
+] + [(pins.test_carry_map_closed_forms, dict(kind=k)) for k in pins.CARRY_KINDS] + [
+    (pins.test_carry_closed_forms_one_step, {}),
+    (pins.test_affine_scan_constant_beta_is_a_first_order_iir_filter, dict(reverse=True)),
+    (pins.test_affine_scan_constant_beta_is_a_first_order_iir_filter, dict(reverse=False)),
+    (pins.test_affine_scan_unit_beta_is_cumsum, {}),
+    (pins.test_affine_scan_matches_sum_form, dict(reverse=True, seed=100, T=6)),
+    (pins.test_affine_scan_matches_sum_form, dict(reverse=False, seed=100, T=6)),
+    (pins.test_affine_scan_exact_in_rationals, {}),
 ]
 
 

@@ -489,3 +489,255 @@ def test_forward_no_leak_bitwise():
             b = fn(x2, s_init=d["B"] + 3, **kw, **extra) if fn is oracle.episodic_cumsum else \
                 fn(x2, z_init=d["B"] + 3, **kw, **extra)
             assert np.array_equal(a[:, s + 1:], b[:, s + 1:]), (kind, fn.__name__)
+
+
+# ------------------------------------- window carries (Method 3, rollout windows)
+
+CARRY_KINDS = ("returns", "gae", "td_lambda", "vtrace", "retrace", "eligibility", "cumsum")
+FORWARD_KINDS = ("eligibility", "cumsum")
+WP = dict(gamma=0.93, lam=0.85, rho_bar=1.1, c_bar=0.9, pg_rho_bar=1.3)
+
+
+def run_window(kind, d, lo, hi, carry, p=WP):
+    """One window [lo, hi) of the rollout in ``d``: (outputs, carry_out, carry_map)."""
+    s = slice(lo, hi)
+    r, te, tr, tv = d["r"][:, s], d["term"][:, s], d["trunc"][:, s], d["tv"][:, s]
+    v = d["v"][:, lo:hi + 1]
+    g, lam = p["gamma"], p["lam"]
+    if kind == "returns":
+        G, co, cm = oracle.returns(r, te, tr, tv, carry, gamma=g, chunk=True)
+        return (G,), co, cm
+    if kind == "gae":
+        a, tg, co, cm = oracle.gae(r, v, te, tr, tv, gamma=g, lam=lam, carry_in=carry, chunk=True)
+        return (a, tg), co, cm
+    if kind == "td_lambda":
+        G, co, cm = oracle.td_lambda(r, v, te, tr, tv, gamma=g, lam=lam, carry_in=carry,
+                                     chunk=True)
+        return (G,), co, cm
+    if kind == "vtrace":
+        vs, pg, co, cm = oracle.vtrace(r, v, d["lr"][:, s], te, tr, tv, gamma=g, lam=lam,
+                                       rho_bar=p["rho_bar"], c_bar=p["c_bar"],
+                                       pg_rho_bar=p["pg_rho_bar"], carry_in=carry, chunk=True)
+        return (vs, pg), co, cm
+    if kind == "retrace":
+        q, co, cm = oracle.retrace(r, d["q"][:, s], d["eq"][:, s], d["lr"][:, s], te, tr,
+                                   gamma=g, lam=lam, c_bar=p["c_bar"], carry_in=carry, chunk=True)
+        return (q,), co, cm
+    if kind == "eligibility":
+        z, co, cm = oracle.eligibility_trace(r, te, tr, carry, gamma=g, lam=lam, chunk=True)
+        return (z,), co, cm
+    S, co, cm = oracle.episodic_cumsum(r, te, tr, carry, chunk=True)
+    return (S,), co, cm
+
+
+def _boundaries_at(d, k):
+    """Force each kind of boundary right before and at the cut k."""
+    d = {key: (val.copy() if hasattr(val, "copy") else val) for key, val in d.items()}
+    d["term"][0, k - 1], d["trunc"][0, k - 1] = 1, 0
+    d["term"][1, k - 1], d["trunc"][1, k - 1] = 0, 1
+    d["term"][2, k], d["trunc"][2, k] = 1, 0
+    d["term"][3, k], d["trunc"][3, k] = 0, 1
+    d["term"][4, k - 1: k + 1] = 0
+    d["trunc"][4, k - 1: k + 1] = 0
+    return d
+
+
+@pytest.mark.parametrize("kind", CARRY_KINDS)
+@pytest.mark.parametrize("seed", [91, 92])
+def test_window_split_reproduces_one_long_window(kind, seed):
+    # Cutting a rollout at k and chaining the two windows through
+    # carry_out -> carry_in gives the result of the uncut window (whose
+    # definition the pins above fix).
+    N, T = 8, 23
+    for k in (1, 7, 22):
+        d = _boundaries_at(rand_inputs(seed, N, T), k)
+        first = d["B"] if kind in FORWARD_KINDS else None
+        whole, whole_co, _ = run_window(kind, d, 0, T, first)
+        if kind in FORWARD_KINDS:
+            e_out, e_co, _ = run_window(kind, d, 0, k, first)
+            l_out, l_co, _ = run_window(kind, d, k, T, e_co)
+            chained_co = l_co
+        else:
+            l_out, l_co, _ = run_window(kind, d, k, T, None)
+            e_out, e_co, _ = run_window(kind, d, 0, k, l_co)
+            chained_co = e_co
+        for w, e, l in zip(whole, e_out, l_out):
+            assert rel_err(np.concatenate([e, l], axis=1), w) < 1e-12, (kind, k)
+        assert rel_err(chained_co, whole_co) < 1e-12, (kind, k)
+
+
+@pytest.mark.parametrize("kind", CARRY_KINDS)
+def test_carry_map_is_the_affine_map_of_the_carry(kind):
+    # Few boundaries, so that most rows carry through the whole window.
+    d = rand_inputs(93, 6, 17, p_term=0.03, p_trunc=0.02)
+    _, co0, m0 = run_window(kind, d, 0, 17, None)
+    assert np.array_equal(m0[:, 0], co0)  # a = carry_out from carry 0
+    for x in (0.75, -1.5, 40.0):
+        c = np.full(6, x) + d["B"]
+        _, co, m = run_window(kind, d, 0, 17, c)
+        assert np.array_equal(m, m0)  # the map does not depend on the carry
+        assert rel_err(co, m[:, 0] + m[:, 1] * c) < 1e-12
+
+
+@pytest.mark.parametrize("kind", CARRY_KINDS)
+def test_carry_map_closed_forms(kind):
+    # No boundaries, log-ratios 0 (every clipped ratio is 1, c_t = lam):
+    # b is the product of the per-step factors, (gamma*lam)^T, gamma^T for
+    # returns and 1 for the plain prefix sum.
+    N, T = 3, 9
+    d = rand_inputs(94, N, T, p_term=0.0, p_trunc=0.0)
+    d["lr"][:] = 0.0
+    g, lam = WP["gamma"], WP["lam"]
+    want_b = {"returns": g ** T, "cumsum": 1.0}.get(kind, (g * lam) ** T)
+    _, _, m = run_window(kind, d, 0, T, None, p=dict(WP, c_bar=1.0, rho_bar=1.0))
+    assert np.allclose(m[:, 1], want_b, rtol=1e-13, atol=0)
+    # A boundary anywhere before the window's last step cuts the carry: b = 0
+    # (reverse: any step; forward: any step but the last) ...
+    for j in (0, 4, T - 1):
+        for flag in ("term", "trunc"):
+            e = {key: (val.copy() if hasattr(val, "copy") else val) for key, val in d.items()}
+            e[flag][:, j] = 1
+            _, co, m = run_window(kind, e, 0, T, None)
+            assert np.all(m[:, 1] == 0.0), (kind, j, flag)
+            if kind in FORWARD_KINDS and j == T - 1:
+                # ... and a boundary after the last step passes nothing on.
+                assert np.all(co == 0.0) and np.all(m == 0.0)
+
+
+def test_carry_closed_forms_one_step():
+    # T = 1, no boundary: the carry enters exactly where the published
+    # recursions put the quantity of the step after the window.
+    g, lam = WP["gamma"], WP["lam"]
+    d = rand_inputs(95, 5, 1, p_term=0.0, p_trunc=0.0)
+    c = np.array([0.3, -1.2, 2.0, 0.0, 5.5])
+    r, v0, v1 = d["r"][:, 0], d["v"][:, 0], d["v"][:, 1]
+    (a, tg), co, _ = run_window("gae", d, 0, 1, c)
+    assert rel_err(a[:, 0], r + g * v1 - v0 + g * lam * c) < 1e-14
+    assert rel_err(co, a[:, 0]) == 0
+    (G,), co, _ = run_window("td_lambda", d, 0, 1, c)
+    assert rel_err(G[:, 0], r + g * ((1 - lam) * v1 + lam * (v1 + c))) < 1e-14
+    assert rel_err(co, G[:, 0] - v0) < 1e-14
+    ratio = np.exp(d["lr"][:, 0])
+    rho, cc = np.minimum(WP["rho_bar"], ratio), lam * np.minimum(WP["c_bar"], ratio)
+    (vs, pg), co, _ = run_window("vtrace", d, 0, 1, c)
+    assert rel_err(vs[:, 0], v0 + rho * (r + g * v1 - v0) + g * cc * c) < 1e-14
+    assert rel_err(pg[:, 0], np.minimum(WP["pg_rho_bar"], ratio) * (r + g * (v1 + c) - v0)) < 1e-14
+    assert rel_err(co, vs[:, 0] - v0) < 1e-14
+    (Q,), co, _ = run_window("retrace", d, 0, 1, c)
+    assert rel_err(Q[:, 0], r + g * d["eq"][:, 0] + g * c) < 1e-14
+    assert rel_err(co, cc * (Q[:, 0] - d["q"][:, 0])) < 1e-14
+    (z,), co, _ = run_window("eligibility", d, 0, 1, c)
+    assert rel_err(z[:, 0], r + g * lam * c) < 1e-14 and rel_err(co, z[:, 0]) == 0
+
+
+@pytest.mark.parametrize("kind", CARRY_KINDS)
+def test_windows_evaluated_apart_chain_through_their_maps(kind):
+    # The T-split: every window runs from carry 0 and reports its map; the
+    # maps, composed from the far end, give each window's true carry; a second
+    # pass with those carries reproduces the uncut window.
+    N, T = 7, 40
+    d = rand_inputs(96, N, T, p_term=0.04, p_trunc=0.03)
+    cuts = [0, 9, 10, 26, 40]
+    first = d["B"] if kind in FORWARD_KINDS else None
+    whole, whole_co, _ = run_window(kind, d, 0, T, first)
+    wins = list(zip(cuts[:-1], cuts[1:]))
+    maps = [run_window(kind, d, lo, hi, None)[2] for lo, hi in wins]
+    carries = [None] * len(wins)
+    order = range(len(wins)) if kind in FORWARD_KINDS else range(len(wins) - 1, -1, -1)
+    c = first if first is not None else np.zeros(N)
+    for i in order:
+        carries[i] = c
+        c = maps[i][:, 0] + maps[i][:, 1] * c
+    assert rel_err(c, whole_co) < 1e-12
+    outs = [run_window(kind, d, lo, hi, carries[i])[0] for i, (lo, hi) in enumerate(wins)]
+    for j, w in enumerate(whole):
+        assert rel_err(np.concatenate([o[j] for o in outs], axis=1), w) < 1e-12, kind
+
+
+# ------------------------------------------ generic segmented affine scan (eq. R)
+
+@pytest.mark.parametrize("reverse", [True, False])
+def test_affine_scan_constant_beta_is_a_first_order_iir_filter(reverse):
+    # y_t = x_t + b y_{t-1} is scipy's lfilter([1], [1, -b]); the carry is the
+    # filter state y_{-1}, i.e. initial condition zi = b * carry.
+    from scipy.signal import lfilter
+    g = np.random.Generator(np.random.PCG64(97))
+    N, T, b = 4, 50, 0.97
+    x, c = g.standard_normal((N, T)), g.standard_normal(N)
+    A, co, m = oracle.affine_scan(x, np.full((N, T), b), carry_in=c, reverse=reverse)
+    for n in range(N):
+        xs = x[n, ::-1] if reverse else x[n]
+        y, _ = lfilter([1.0], [1.0, -b], xs, zi=[b * c[n]])
+        want = y[::-1] if reverse else y
+        assert rel_err(A[n], want) < 1e-13
+    assert rel_err(co, A[:, 0] if reverse else A[:, -1]) == 0
+    assert np.allclose(m[:, 1], b ** T, rtol=1e-13, atol=0)
+
+
+def test_affine_scan_unit_beta_is_cumsum():
+    g = np.random.Generator(np.random.PCG64(98))
+    x, c = g.standard_normal((3, 31)), g.standard_normal(3)
+    A, _, _ = oracle.affine_scan(x, np.ones((3, 31)), carry_in=c, reverse=False)
+    assert rel_err(A, np.cumsum(x, axis=1) + c[:, None]) < 1e-13
+    A, _, _ = oracle.affine_scan(x, np.ones((3, 31)), carry_in=c, reverse=True)
+    assert rel_err(A, np.cumsum(x[:, ::-1], axis=1)[:, ::-1] + c[:, None]) < 1e-13
+
+
+@pytest.mark.parametrize("reverse", [True, False])
+@pytest.mark.parametrize("seed,T", [(99, 1), (100, 6), (101, 15)])
+def test_affine_scan_matches_sum_form(reverse, seed, T):
+    g = np.random.Generator(np.random.PCG64(seed))
+    N = 5
+    al, be = g.standard_normal((N, T)), g.uniform(-1.2, 1.2, (N, T))
+    rs = (g.random((N, T)) < 0.2).astype(np.uint8)
+    c = g.standard_normal(N)
+    A, co, m = oracle.affine_scan(al, be, rs, c, reverse=reverse)
+    want = bf.affine_scan(al.tolist(), be.tolist(), rs.tolist(), c.tolist(), reverse)
+    assert rel_err(A, want) < RTOL_BF
+    want0 = bf.affine_scan(al.tolist(), be.tolist(), rs.tolist(), None, reverse)
+    assert rel_err(m[:, 0], [row[0] if reverse else row[-1] for row in want0]) < RTOL_BF
+
+
+@pytest.mark.parametrize("reverse", [True, False])
+def test_affine_scan_exhaustive_resets(reverse):
+    T = 5
+    pats = np.array(list(itertools.product([0, 1], repeat=T)), np.uint8)
+    N = len(pats)
+    g = np.random.Generator(np.random.PCG64(102))
+    al, be, c = g.standard_normal((N, T)), g.uniform(0.5, 1.5, (N, T)), g.standard_normal(N)
+    A, _, _ = oracle.affine_scan(al, be, pats, c, reverse=reverse)
+    assert rel_err(A, bf.affine_scan(al.tolist(), be.tolist(), pats.tolist(), c.tolist(),
+                                     reverse)) < RTOL_BF
+
+
+def test_affine_scan_exact_in_rationals():
+    # Small integer/dyadic inputs: the fp64 result is exact and equals the
+    # sum form evaluated in Fractions.
+    al = [[3, -1, 4, 1, -5, 9]]
+    be = [[0.5, 0.25, 2.0, -1.0, 0.5, 1.0]]
+    rs = [[0, 0, 1, 0, 0, 0]]
+    for reverse in (True, False):
+        A, _, _ = oracle.affine_scan(np.array(al, float), np.array(be), np.array(rs, np.uint8),
+                                     np.array([2.0]), reverse=reverse)
+        want = bf.affine_scan([[Fraction(x) for x in al[0]]],
+                              [[Fraction(x) for x in be[0]]], rs, [Fraction(2)], reverse)
+        assert [Fraction(x) for x in A[0]] == want[0]
+
+
+def test_affine_scan_instances_of_the_algorithms():
+    # GAE is the reverse scan with alpha = delta and beta = gamma*lam cut at
+    # done; the eligibility trace is the forward scan cut after done_{t-1}.
+    d = rand_inputs(103, 6, 20)
+    g, lam = 0.95, 0.9
+    te, tr = d["term"].astype(bool), d["trunc"].astype(bool)
+    nv = np.where(te, 0.0, np.where(tr, d["tv"], d["v"][:, 1:]))
+    delta = d["r"] + g * nv - d["v"][:, :-1]
+    A, _, _ = oracle.affine_scan(delta, np.full((6, 20), g * lam), (te | tr).astype(np.uint8))
+    assert rel_err(A, oracle.gae(d["r"], d["v"], d["term"], d["trunc"], d["tv"], gamma=g,
+                                 lam=lam)[0]) < 1e-13
+    prev_done = np.zeros_like(te)
+    prev_done[:, 1:] = (te | tr)[:, :-1]
+    Z, _, _ = oracle.affine_scan(d["r"], np.full((6, 20), g * lam), prev_done.astype(np.uint8),
+                                 d["B"], reverse=False)
+    assert rel_err(Z, oracle.eligibility_trace(d["r"], d["term"], d["trunc"], d["B"], gamma=g,
+                                               lam=lam)) < 1e-13
