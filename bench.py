@@ -13,6 +13,9 @@ the next buffer set) and replayed between two events on the launch stream.
 Output: one JSON line with env-steps/s, the roofline of the kernel (algorithmic
 bytes per launch / average launch time against the 8 TB/s HBM peak) and the
 CPU oracle timed on the host cores on a bounded sample.
+
+--window times the window form of the same call (rlca_X_chunk: a per-row
+carry read, the outgoing carry and the carry map written) on the same inputs.
 """
 import argparse
 import hashlib
@@ -29,7 +32,8 @@ METRIC = "env-steps/sec and achieved HBM GB/s (% of peak), GAE 4096 envs × T=12
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "reverse_linear_recurrence_amd", "csrc", f)
-                  for f in ("scan_kernels.hpp", "rlca.hip")]
+                  for f in ("scan_kernels.hpp", "kernel_table.hpp", "variants.hpp",
+                            "kernels_plain.hip", "kernels_window.hip", "rlca.hip")]
 
 
 def kernel_source_hash():
@@ -53,6 +57,8 @@ def parse():
     ap.add_argument("--no-graph", action="store_true",
                     help="launch each step from Python instead of replaying a HIP graph")
     ap.add_argument("--variant", type=int, default=-1, help="force a tiling variant")
+    ap.add_argument("--window", action="store_true",
+                    help="time the window entry point (carry in; carry and carry map out)")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip timing a plain copy kernel of the same byte count")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -61,10 +67,13 @@ def parse():
     return ap.parse_args()
 
 
-def algorithmic_bytes(w, N, T):
-    """Bytes the method must move per launch: one read of every input element
+def algorithmic_bytes(w, N, T, window=False):
+    """Bytes the method must move per step: one read of every input element
     it uses and one write of every output element (truncation bootstraps,
-    read only at truncations, are not counted)."""
+    read only at truncations, are not counted).  A window call adds its
+    per-row carry in (4 B), carry out (4 B) and carry map (8 B) per launch."""
+    if window:
+        return algorithmic_bytes(w, N, T) + 16 * N * launches_per_step_of(w)
     es = 2 if w.dtype == "bf16" else 4
     if w.algo in ("gae",):
         return (2 * es + 2 + 8) * N * T + es * N  # r, V, 2 flags, adv+targets; V_T
@@ -180,17 +189,57 @@ def main():
     print("workload %s: %d x %d %s, %d rotating sets of %.2f MB" %
           (w.name, N, T, w.dtype, R, set_bytes / 2 ** 20), file=sys.stderr, flush=True)
 
+    # Window calls: a seeded per-row carry entering every window.
+    carry_in = torch.from_numpy(np.random.Generator(np.random.PCG64(w.seed + 1))
+                                .standard_normal(N).astype(np.float32))
     sets = []
     for _ in range(R):
         d = {k: v.to(dev) for k, v in host.items()}
         d["_o0"] = torch.empty(N, T, dtype=torch.float32, device=dev)
         d["_o1"] = torch.empty(N, T, dtype=torch.float32, device=dev)
         d["_o2"] = torch.empty(N, T, dtype=torch.float32, device=dev)
+        d["_cin"] = carry_in.to(dev)
+        d["_cout"] = torch.empty(N, dtype=torch.float32, device=dev)
+        d["_cmap"] = torch.empty(N, 2, dtype=torch.float32, device=dev)
+        d["_cout2"] = torch.empty(N, dtype=torch.float32, device=dev)
+        d["_cmap2"] = torch.empty(N, 2, dtype=torch.float32, device=dev)
         sets.append(d)
     torch.cuda.synchronize()
     rl.rlca_set_variant(args.variant)
 
+    def window_step(d):
+        c = dict(carry_in=d["_cin"], carry_out=d["_cout"], carry_map=d["_cmap"])
+        if w.algo == "gae":
+            rl.rlca_gae_chunk(d["rewards"], d["values"], d["terminated"], d.get("truncated"),
+                              d.get("trunc_values"), gamma=gamma, lam=lam, advantages=d["_o0"],
+                              targets=d["_o1"], **c)
+        elif w.algo == "td_lambda":
+            rl.rlca_td_lambda_chunk(d["rewards"], d["values"], d["terminated"],
+                                    d.get("truncated"), d.get("trunc_values"), gamma=gamma,
+                                    lam=lam, out=d["_o0"], **c)
+        elif w.algo == "returns":
+            rl.rlca_returns_chunk(d["rewards"], d["terminated"], gamma=gamma, out=d["_o0"], **c)
+        elif w.algo == "eligibility":
+            rl.rlca_eligibility_trace_chunk(d["rewards"], d["terminated"], d.get("truncated"),
+                                            gamma=gamma, lam=lam, out=d["_o0"], **c)
+        elif w.algo == "cumsum":
+            rl.rlca_episodic_cumsum_chunk(d["rewards"], d["terminated"], d.get("truncated"),
+                                          out=d["_o0"], **c)
+        elif w.algo == "vtrace+retrace":
+            rl.rlca_vtrace_chunk(d["rewards"], d["values"], d["log_rhos"], d["terminated"],
+                                 gamma=gamma, lam=lam, vs=d["_o0"], pg_advantages=d["_o1"],
+                                 **clips, **c)
+            rl.rlca_retrace_chunk(d["rewards"], d["q_taken"], d["exp_q_next"], d["log_rhos"],
+                                  d["terminated"], gamma=gamma, lam=lam, c_bar=clips["c_bar"],
+                                  out=d["_o2"], carry_in=d["_cin"], carry_out=d["_cout2"],
+                                  carry_map=d["_cmap2"])
+        else:
+            raise ValueError(w.algo)
+
     def step(d):
+        if args.window:
+            window_step(d)
+            return
         if w.algo == "gae":
             rl.rlca_gae(d["rewards"], d["values"], d["terminated"], d.get("truncated"),
                         d.get("trunc_values"), gamma=gamma, lam=lam, advantages=d["_o0"],
@@ -219,33 +268,51 @@ def main():
     import oracle
     step(sets[0])
     torch.cuda.synchronize()
+    win = dict(carry_in=carry_in, chunk=True) if args.window else {}
+    if args.window and w.algo in ("returns",):
+        win = dict(chunk=True)
     if w.algo == "gae":
         ref = oracle.gae(host["rewards"], host["values"], host["terminated"],
-                         host.get("truncated"), host.get("trunc_values"), gamma=gamma, lam=lam)
+                         host.get("truncated"), host.get("trunc_values"), gamma=gamma, lam=lam,
+                         **win)
         outs = (sets[0]["_o0"], sets[0]["_o1"])
     elif w.algo == "td_lambda":
-        ref = (oracle.td_lambda(host["rewards"], host["values"], host["terminated"],
-                                host.get("truncated"), host.get("trunc_values"), gamma=gamma,
-                                lam=lam),)
+        ref = oracle.td_lambda(host["rewards"], host["values"], host["terminated"],
+                               host.get("truncated"), host.get("trunc_values"), gamma=gamma,
+                               lam=lam, **win)
         outs = (sets[0]["_o0"],)
     elif w.algo == "returns":
-        ref = (oracle.returns(host["rewards"], host["terminated"], gamma=gamma),)
+        ref = oracle.returns(host["rewards"], host["terminated"],
+                             bootstrap=carry_in if args.window else None, gamma=gamma, **win)
         outs = (sets[0]["_o0"],)
     elif w.algo == "eligibility":
-        ref = (oracle.eligibility_trace(host["rewards"], host["terminated"], host.get("truncated"),
-                                        gamma=gamma, lam=lam),)
+        ref = oracle.eligibility_trace(host["rewards"], host["terminated"], host.get("truncated"),
+                                       carry_in if args.window else None, gamma=gamma, lam=lam,
+                                       **({"chunk": True} if args.window else {}))
         outs = (sets[0]["_o0"],)
     elif w.algo == "cumsum":
-        ref = (oracle.episodic_cumsum(host["rewards"], host["terminated"], host.get("truncated")),)
+        ref = oracle.episodic_cumsum(host["rewards"], host["terminated"], host.get("truncated"),
+                                     carry_in if args.window else None,
+                                     **({"chunk": True} if args.window else {}))
         outs = (sets[0]["_o0"],)
     else:
-        vs, pg = oracle.vtrace(host["rewards"], host["values"], host["log_rhos"],
-                               host["terminated"], gamma=gamma, lam=lam, **clips)
+        vs = oracle.vtrace(host["rewards"], host["values"], host["log_rhos"], host["terminated"],
+                           gamma=gamma, lam=lam, **clips, **win)
         qr = oracle.retrace(host["rewards"], host["q_taken"], host["exp_q_next"],
                             host["log_rhos"], host["terminated"], gamma=gamma, lam=lam,
-                            c_bar=clips["c_bar"])
-        ref = (vs, pg, qr)
+                            c_bar=clips["c_bar"], **win)
         outs = (sets[0]["_o0"], sets[0]["_o1"], sets[0]["_o2"])
+        if args.window:
+            ref = (vs[0], vs[1], vs[2], vs[3], qr[0], qr[1], qr[2])
+            outs = (sets[0]["_o0"], sets[0]["_o1"], sets[0]["_cout"], sets[0]["_cmap"],
+                    sets[0]["_o2"], sets[0]["_cout2"], sets[0]["_cmap2"])
+        else:
+            ref = (vs[0], vs[1], qr)
+    if not isinstance(ref, tuple):
+        ref = (ref,)
+    if args.window and w.algo != "vtrace+retrace":
+        # outputs, then carry_out [N] and carry map [N, 2]
+        outs = outs + (sets[0]["_cout"], sets[0]["_cmap"])
     parity = max(float(np.max(np.abs(o.double().cpu().numpy() - r)) / np.max(np.abs(r)))
                  for o, r in zip(outs, ref))
     tol = 1e-2 if w.dtype == "bf16" else 1e-4
@@ -297,7 +364,7 @@ def main():
     # counter runs (see --summarize-pmc).
     copy = None
     if not args.no_copy_ceiling:
-        half = algorithmic_bytes(w, N, T) // launches_per_step_of(w) // 2 // 16 * 16
+        half = algorithmic_bytes(w, N, T, args.window) // launches_per_step_of(w) // 2 // 16 * 16
         RC = max(2, int(np.ceil(args.rotate_mb * 2 ** 20 / (2 * half))))
         bufs = [(torch.empty(half // 4, dtype=torch.float32, device=dev),
                  torch.empty(half // 4, dtype=torch.float32, device=dev)) for _ in range(RC)]
@@ -335,7 +402,8 @@ def main():
     launches_per_step = launches_per_step_of(w)
     env_steps = N * T
     value = env_steps / (ms_per_step * 1e-3)
-    bytes_per_step = algorithmic_bytes(w, N, T)
+    bytes_per_step = algorithmic_bytes(w, N, T, args.window)
+    traffic_key = w.name + ("/window" if args.window else "")
     achieved = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
     # ---- HBM traffic from the committed counter runs, if they match this kernel
@@ -343,7 +411,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        entry = tr.get(w.name)
+        entry = tr.get(traffic_key)
         if entry and entry.get("kernel_source_hash") == kernel_source_hash():
             traffic = entry.get("bytes_per_launch")
 
@@ -392,7 +460,7 @@ def main():
     if meta_dir:
         os.makedirs(meta_dir, exist_ok=True)
         with open(os.path.join(meta_dir, "bench_meta.json"), "w") as f:
-            json.dump({"workload": w.name, "algorithmic_bytes_per_launch":
+            json.dump({"workload": traffic_key, "algorithmic_bytes_per_launch":
                        bytes_per_step / launches_per_step,
                        "copy_bytes_per_launch": copy["bytes_per_launch"] if copy else None}, f)
 
@@ -412,7 +480,9 @@ def main():
         "config": {"workload": w.name, "num_envs": N, "T": T, "input_dtype": w.dtype,
                    "gamma": w.gamma, "lam": w.lam, "p_term": w.p_term, "p_trunc": w.p_trunc,
                    "seed": w.seed, "rotation_sets": R, "timing": timing,
-                   "launches_per_step": launches_per_step, "variant": variant},
+                   "launches_per_step": launches_per_step, "variant": variant,
+                   "entry": "window (carry in; carry and carry map out)" if args.window
+                   else "plain"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": bytes_per_step / launches_per_step,

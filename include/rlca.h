@@ -232,6 +232,148 @@ int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype,
                          float *sums, int64_t ld_sums,
                          void *stream);
 
+/*
+ * Window entry points (Method 3, "rollout windows"; Method 1: the operator is
+ * associative, so a rollout can be cut along time and the pieces chained).
+ * A rollout longer than one call -- streamed as it is collected, or cut into
+ * pieces evaluated apart -- is processed as consecutive windows of one
+ * rollout.  Each rlca_X_chunk call takes the arguments of rlca_X (the
+ * per-row bootstrap / initial value of returns and of the forward mirrors is
+ * replaced by carry_in) plus three per-row fp32 vectors, whatever `dtype`:
+ *
+ *   carry_in  [num_envs], nullable (0): the scan state A entering the window
+ *             from the neighbouring window -- the later one for reverse
+ *             recurrences (A_T), the earlier one for forward ones (A_{-1}).
+ *   carry_out [num_envs], nullable: the value to pass as carry_in to the
+ *             window on the other side (earlier for reverse, later for
+ *             forward).  Like every output it must not overlap an input,
+ *             carry_in included (RLCA_EALIAS): stream through two carry
+ *             vectors used in turn.
+ *   carry_map [num_envs, 2] (row-major pairs (a, b)), nullable: the affine
+ *             map carry_out = a + b * carry_in of the window, whatever
+ *             carry_in is.  With it, windows can be evaluated in parallel
+ *             from carry 0 and joined afterwards: compose the maps from the
+ *             far end to get each window's true carry_in, then evaluate the
+ *             windows again with it.
+ *
+ * What the carry is, per algorithm (A as in each entry point above):
+ *   returns       A = G.  carry_in = G_T (the bootstrap); carry_out = G_0.
+ *   gae           A = advantage.  carry_in = A_T, the advantage of the step
+ *                 after the window; carry_out = A_0.  values keeps its T+1
+ *                 columns: V_T is the first value of the next window.
+ *   td_lambda     A = G^lambda - V.  carry_in = G^lambda_T - V_T;
+ *                 carry_out = G^lambda_0 - V_0 (= lambda_returns[0] - V_0).
+ *   vtrace        A = vs - V.  carry_in = vs_T - V_T, which also enters pg at
+ *                 step T-1 through vs_T; carry_out = vs_0 - V_0.
+ *   retrace       A = q_ret - q_taken; the trace factor c_{t+1} multiplies
+ *                 A_{t+1}, so the carry holds it: carry_in =
+ *                 c_T (q_ret_T - q_taken_T) with c_T = lam min(c_bar,
+ *                 exp(log_rho_T)) of the next window's first step, and
+ *                 carry_out = c_0 (q_ret_0 - q_taken_0).  With carry_in NULL
+ *                 the result equals rlca_retrace's.
+ *   eligibility_trace, episodic_cumsum
+ *                 carry_in = A_{-1} (z_init / s_init as fp32); carry_out =
+ *                 A_{T-1}, or 0 if an episode ends after step T-1.
+ * Splitting a rollout at any step and chaining the windows this way
+ * reproduces the one-window result up to fp32 rounding.  Errors and
+ * everything else as for rlca_X.
+ */
+int rlca_returns_chunk(int64_t num_envs, int64_t T, int dtype,
+                       const void *rewards, int64_t ld_rewards,
+                       const uint8_t *terminated, int64_t ld_terminated,
+                       const uint8_t *truncated, int64_t ld_truncated,
+                       const void *trunc_values, int64_t ld_trunc_values,
+                       const float *carry_in, float gamma,
+                       float *returns, int64_t ld_returns,
+                       float *carry_out, float *carry_map,
+                       void *stream);
+int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype,
+                   const void *rewards, int64_t ld_rewards,
+                   const void *values, int64_t ld_values,
+                   const uint8_t *terminated, int64_t ld_terminated,
+                   const uint8_t *truncated, int64_t ld_truncated,
+                   const void *trunc_values, int64_t ld_trunc_values,
+                   float gamma, float lam,
+                   float *advantages, int64_t ld_advantages,
+                   float *targets, int64_t ld_targets,
+                   const float *carry_in, float *carry_out, float *carry_map,
+                   void *stream);
+int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype,
+                         const void *rewards, int64_t ld_rewards,
+                         const void *values, int64_t ld_values,
+                         const uint8_t *terminated, int64_t ld_terminated,
+                         const uint8_t *truncated, int64_t ld_truncated,
+                         const void *trunc_values, int64_t ld_trunc_values,
+                         float gamma, float lam,
+                         float *lambda_returns, int64_t ld_lambda_returns,
+                         const float *carry_in, float *carry_out, float *carry_map,
+                         void *stream);
+int rlca_vtrace_chunk(int64_t num_envs, int64_t T, int dtype,
+                      const void *rewards, int64_t ld_rewards,
+                      const void *values, int64_t ld_values,
+                      const void *log_rhos, int64_t ld_log_rhos,
+                      const uint8_t *terminated, int64_t ld_terminated,
+                      const uint8_t *truncated, int64_t ld_truncated,
+                      const void *trunc_values, int64_t ld_trunc_values,
+                      float gamma, float lam, float rho_bar, float c_bar, float pg_rho_bar,
+                      float *vs, int64_t ld_vs,
+                      float *pg_advantages, int64_t ld_pg_advantages,
+                      const float *carry_in, float *carry_out, float *carry_map,
+                      void *stream);
+int rlca_retrace_chunk(int64_t num_envs, int64_t T, int dtype,
+                       const void *rewards, int64_t ld_rewards,
+                       const void *q_taken, int64_t ld_q_taken,
+                       const void *exp_q_next, int64_t ld_exp_q_next,
+                       const void *log_rhos, int64_t ld_log_rhos,
+                       const uint8_t *terminated, int64_t ld_terminated,
+                       const uint8_t *truncated, int64_t ld_truncated,
+                       float gamma, float lam, float c_bar,
+                       float *q_ret, int64_t ld_q_ret,
+                       const float *carry_in, float *carry_out, float *carry_map,
+                       void *stream);
+int rlca_eligibility_trace_chunk(int64_t num_envs, int64_t T, int dtype,
+                                 const void *x, int64_t ld_x,
+                                 const uint8_t *terminated, int64_t ld_terminated,
+                                 const uint8_t *truncated, int64_t ld_truncated,
+                                 const float *carry_in,
+                                 float gamma, float lam,
+                                 float *traces, int64_t ld_traces,
+                                 float *carry_out, float *carry_map,
+                                 void *stream);
+int rlca_episodic_cumsum_chunk(int64_t num_envs, int64_t T, int dtype,
+                               const void *x, int64_t ld_x,
+                               const uint8_t *terminated, int64_t ld_terminated,
+                               const uint8_t *truncated, int64_t ld_truncated,
+                               const float *carry_in,
+                               float *sums, int64_t ld_sums,
+                               float *carry_out, float *carry_map,
+                               void *stream);
+
+/*
+ * Generic segmented affine scan: (R) itself with caller-given coefficients
+ * (Method 1: every entry point above is an instance of it; the pages'
+ * "Significance and claims" section names long-context LLM post-training and
+ * spiking neural networks as further uses of the same fused scan).
+ *   reverse = 1:  A_t = alpha_t + beta'_t * A_{t+1},  t = T-1 .. 0,  A_T = carry_in
+ *   reverse = 0:  A_t = alpha_t + beta'_t * A_{t-1},  t = 0 .. T-1,  A_{-1} = carry_in
+ * beta'_t = 0 where reset[t] != 0 (step t starts a segment: nothing flows in
+ * from its neighbour), beta_t elsewhere; reset NULL: no resets.
+ * In:  alpha, beta [N,T] (dtype), reset [N,T] uint8 (nullable).
+ * Out: out [N,T] fp32 (= A).  carry_in, carry_out, carry_map as for the
+ * window entry points: carry_out is A_0 (reverse) or A_{T-1} (forward), as
+ * is; a reset at the next window's first step belongs to that window.
+ * reverse other than 0 or 1 -> RLCA_EINVAL.
+ */
+int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype,
+                     const void *alpha, int64_t ld_alpha,
+                     const void *beta, int64_t ld_beta,
+                     const uint8_t *reset, int64_t ld_reset,
+                     int reverse,
+                     const float *carry_in,
+                     float *out, int64_t ld_out,
+                     float *carry_out, float *carry_map,
+                     void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *rlca_last_error(void);
 

@@ -9,8 +9,9 @@ tensors are not on a GPU, the call raises.
 
 Functions (same names as the C ABI):
     rlca_returns, rlca_gae, rlca_td_lambda, rlca_vtrace, rlca_retrace,
-    rlca_eligibility_trace, rlca_episodic_cumsum
-and the tiling controls rlca_set_variant, rlca_num_variants,
+    rlca_eligibility_trace, rlca_episodic_cumsum,
+their window forms (carry in; carry and carry map out) with the suffix
+_chunk, the generic segmented scan rlca_affine_scan, and the tiling controls rlca_set_variant, rlca_num_variants,
 rlca_variant_info, rlca_last_variant, plus rlca_version.
 """
 from ._binding import (  # noqa: F401
@@ -24,16 +25,24 @@ from ._binding import (  # noqa: F401
     RlcaError,
     lib_path,
     load_library,
+    rlca_affine_scan,
     rlca_eligibility_trace,
+    rlca_eligibility_trace_chunk,
     rlca_episodic_cumsum,
+    rlca_episodic_cumsum_chunk,
     rlca_gae,
+    rlca_gae_chunk,
     rlca_last_variant,
     rlca_num_variants,
     rlca_retrace,
+    rlca_retrace_chunk,
     rlca_returns,
+    rlca_returns_chunk,
     rlca_set_variant,
     rlca_td_lambda,
+    rlca_td_lambda_chunk,
     rlca_variant_info,
     rlca_version,
     rlca_vtrace,
+    rlca_vtrace_chunk,
 )

@@ -39,6 +39,23 @@ _SIGNATURES = {
                                _f32, _vp, _i64, _vp],
     "rlca_episodic_cumsum": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64,
                              _vp],
+    "rlca_returns_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                           _f32, _vp, _i64, _vp, _vp, _vp],
+    "rlca_gae_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                       _f32, _f32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
+    "rlca_td_lambda_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                             _i64, _f32, _f32, _vp, _i64, _vp, _vp, _vp, _vp],
+    "rlca_vtrace_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                          _i64, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _vp, _i64, _vp, _i64,
+                          _vp, _vp, _vp, _vp],
+    "rlca_retrace_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                           _i64, _vp, _i64, _f32, _f32, _f32, _vp, _i64, _vp, _vp, _vp, _vp],
+    "rlca_eligibility_trace_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                     _f32, _f32, _vp, _i64, _vp, _vp, _vp],
+    "rlca_episodic_cumsum_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp,
+                                   _i64, _vp, _vp, _vp],
+    "rlca_affine_scan": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _int, _vp, _vp, _i64,
+                         _vp, _vp, _vp],
     "rlca_last_error": [],
     "rlca_version": [],
     "rlca_num_variants": [],
@@ -275,6 +292,217 @@ def rlca_episodic_cumsum(x, terminated=None, truncated=None, s_init=None, *, out
     _check(load_library().rlca_episodic_cumsum(N, T, code, a, ld_a, te, ld_te, tr, ld_tr, s0, o,
                                                ld_o, _stream(stream, dev)))
     return out
+
+
+# ------------------------------------------------------------ window calls
+#
+# Each rlca_X_chunk takes the arguments of rlca_X (the bootstrap / initial
+# value replaced by ``carry_in``) and returns the outputs of rlca_X followed by
+# ``carry_out`` [N] and ``carry_map`` [N, 2] (float32).  carry_in [N] float32
+# (None: 0) is the scan state entering from the neighbouring window;
+# carry_out must not overlap carry_in (use two vectors in turn).
+# ``with_carry_out`` / ``with_map`` False pass NULL for that output (returned
+# as None).
+
+
+def _carry_in(carry_in, N, device):
+    if carry_in is None:
+        return None
+    if not isinstance(carry_in, torch.Tensor) or carry_in.dtype != torch.float32:
+        raise TypeError("carry_in must be a float32 tensor")
+    ptr, _ = _layout("carry_in", carry_in, (N,), device)
+    return ptr
+
+
+def _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, device):
+    co = cm = None
+    co_p = cm_p = None
+    if with_carry_out or carry_out is not None:
+        carry_out, co_p, _ = _output("carry_out", carry_out, (N,), device)
+        co = carry_out
+    if with_map or carry_map is not None:
+        if carry_map is None:
+            carry_map = torch.empty((N, 2), dtype=torch.float32, device=device)
+        if carry_map.dtype != torch.float32 or not carry_map.is_contiguous():
+            raise TypeError("carry_map must be a contiguous float32 tensor")
+        _layout("carry_map", carry_map, (N, 2), device)
+        cm, cm_p = carry_map, carry_map.data_ptr()
+    return co, cm, co_p, cm_p
+
+
+def rlca_returns_chunk(rewards, terminated=None, truncated=None, trunc_values=None, *, gamma,
+                       carry_in=None, out=None, carry_out=None, carry_map=None,
+                       with_carry_out=True, with_map=True, stream=None):
+    """Window of discounted returns: ``(returns, carry_out, carry_map)``;
+    carry_in is G_T, carry_out is G_0."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    out, o, ld_o = _output("returns", out, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_returns_chunk(N, T, code, r, ld_r, te, ld_te, tr, ld_tr, tv, ld_tv,
+                                             ci, gamma, o, ld_o, co_p, cm_p,
+                                             _stream(stream, dev)))
+    return out, co, cm
+
+
+def rlca_gae_chunk(rewards, values, terminated=None, truncated=None, trunc_values=None, *,
+                   gamma, lam, carry_in=None, advantages=None, targets=None, with_targets=True,
+                   carry_out=None, carry_map=None, with_carry_out=True, with_map=True,
+                   stream=None):
+    """Window of GAE: ``(advantages, targets, carry_out, carry_map)``; carry_in
+    is the advantage A_T of the step after the window, carry_out is A_0."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    adv, a, ld_a = _output("advantages", advantages, (N, T), dev)
+    g, ld_g = None, 0
+    if with_targets or targets is not None:
+        targets, g, ld_g = _output("targets", targets, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_gae_chunk(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr, ld_tr, tv,
+                                         ld_tv, gamma, lam, a, ld_a, g, ld_g, ci, co_p, cm_p,
+                                         _stream(stream, dev)))
+    return adv, targets, co, cm
+
+
+def rlca_td_lambda_chunk(rewards, values, terminated=None, truncated=None, trunc_values=None, *,
+                         gamma, lam, carry_in=None, out=None, carry_out=None, carry_map=None,
+                         with_carry_out=True, with_map=True, stream=None):
+    """Window of TD(lambda) returns: ``(lambda_returns, carry_out, carry_map)``;
+    the carry is G^lambda - V (carry_in at step T, carry_out at step 0)."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    out, o, ld_o = _output("lambda_returns", out, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_td_lambda_chunk(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr, ld_tr,
+                                               tv, ld_tv, gamma, lam, o, ld_o, ci, co_p, cm_p,
+                                               _stream(stream, dev)))
+    return out, co, cm
+
+
+def rlca_vtrace_chunk(rewards, values, log_rhos, terminated=None, truncated=None,
+                      trunc_values=None, *, gamma, lam=1.0, rho_bar=1.0, c_bar=1.0,
+                      pg_rho_bar=1.0, carry_in=None, vs=None, pg_advantages=None, with_pg=True,
+                      carry_out=None, carry_map=None, with_carry_out=True, with_map=True,
+                      stream=None):
+    """Window of V-trace: ``(vs, pg_advantages, carry_out, carry_map)``; the
+    carry is vs - V (carry_in at step T, carry_out at step 0)."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    lr, ld_lr = _float_input("log_rhos", log_rhos, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    vs, o, ld_o = _output("vs", vs, (N, T), dev)
+    pg, ld_pg = None, 0
+    if with_pg or pg_advantages is not None:
+        pg_advantages, pg, ld_pg = _output("pg_advantages", pg_advantages, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_vtrace_chunk(N, T, code, r, ld_r, v, ld_v, lr, ld_lr, te, ld_te,
+                                            tr, ld_tr, tv, ld_tv, gamma, lam, rho_bar, c_bar,
+                                            pg_rho_bar, o, ld_o, pg, ld_pg, ci, co_p, cm_p,
+                                            _stream(stream, dev)))
+    return vs, pg_advantages, co, cm
+
+
+def rlca_retrace_chunk(rewards, q_taken, exp_q_next, log_rhos, terminated=None, truncated=None,
+                       *, gamma, lam=1.0, c_bar=1.0, carry_in=None, out=None, carry_out=None,
+                       carry_map=None, with_carry_out=True, with_map=True, stream=None):
+    """Window of Retrace(lambda): ``(q_ret, carry_out, carry_map)``; the carry
+    is c_t (q_ret_t - q_taken_t) (carry_in at step T, carry_out at step 0)."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    q, ld_q = _float_input("q_taken", q_taken, dt, (N, T), dev)
+    eq, ld_eq = _float_input("exp_q_next", exp_q_next, dt, (N, T), dev)
+    lr, ld_lr = _float_input("log_rhos", log_rhos, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    out, o, ld_o = _output("q_ret", out, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_retrace_chunk(N, T, code, r, ld_r, q, ld_q, eq, ld_eq, lr, ld_lr,
+                                             te, ld_te, tr, ld_tr, gamma, lam, c_bar, o, ld_o, ci,
+                                             co_p, cm_p, _stream(stream, dev)))
+    return out, co, cm
+
+
+def rlca_eligibility_trace_chunk(x, terminated=None, truncated=None, *, gamma, lam,
+                                 carry_in=None, out=None, carry_out=None, carry_map=None,
+                                 with_carry_out=True, with_map=True, stream=None):
+    """Window of the eligibility trace: ``(traces, carry_out, carry_map)``;
+    carry_in is z_{-1}, carry_out is z_{T-1} (0 if an episode ends there)."""
+    N, T, code, dev = _common(x)
+    dt = x.dtype
+    a, ld_a = _float_input("x", x, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    out, o, ld_o = _output("traces", out, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_eligibility_trace_chunk(N, T, code, a, ld_a, te, ld_te, tr, ld_tr,
+                                                       ci, gamma, lam, o, ld_o, co_p, cm_p,
+                                                       _stream(stream, dev)))
+    return out, co, cm
+
+
+def rlca_episodic_cumsum_chunk(x, terminated=None, truncated=None, *, carry_in=None, out=None,
+                               carry_out=None, carry_map=None, with_carry_out=True,
+                               with_map=True, stream=None):
+    """Window of the episodic prefix sum: ``(sums, carry_out, carry_map)``;
+    carry_in is S_{-1}, carry_out is S_{T-1} (0 if an episode ends there)."""
+    N, T, code, dev = _common(x)
+    dt = x.dtype
+    a, ld_a = _float_input("x", x, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    out, o, ld_o = _output("sums", out, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_episodic_cumsum_chunk(N, T, code, a, ld_a, te, ld_te, tr, ld_tr,
+                                                     ci, o, ld_o, co_p, cm_p,
+                                                     _stream(stream, dev)))
+    return out, co, cm
+
+
+def rlca_affine_scan(alpha, beta, reset=None, *, reverse=True, carry_in=None, out=None,
+                     carry_out=None, carry_map=None, with_carry_out=True, with_map=True,
+                     stream=None):
+    """Segmented affine scan: ``(A, carry_out, carry_map)`` with
+    A_t = alpha_t + beta'_t A_{t+1} (reverse; A_T = carry_in) or
+    A_t = alpha_t + beta'_t A_{t-1} (forward; A_{-1} = carry_in),
+    beta'_t = 0 where reset_t, else beta_t."""
+    N, T, code, dev = _common(alpha)
+    dt = alpha.dtype
+    a, ld_a = _float_input("alpha", alpha, dt, (N, T), dev)
+    b, ld_b = _float_input("beta", beta, dt, (N, T), dev)
+    rs, ld_rs = _flag_input("reset", reset, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    out, o, ld_o = _output("out", out, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_affine_scan(N, T, code, a, ld_a, b, ld_b, rs, ld_rs,
+                                           1 if reverse else 0, ci, o, ld_o, co_p, cm_p,
+                                           _stream(stream, dev)))
+    return out, co, cm
 
 
 def rlca_version():

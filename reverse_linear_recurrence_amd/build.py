@@ -8,14 +8,17 @@ the Python binding loads it.
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librlca.so")
-SOURCES = [os.path.join(CSRC, "rlca.hip")]
-DEPS = SOURCES + [os.path.join(CSRC, "scan_kernels.hpp"), os.path.join(INCLUDE, "rlca.h")]
+# Host code and the two kernel tables, compiled in parallel.
+SOURCES = [os.path.join(CSRC, n) for n in ("rlca.hip", "kernels_plain.hip", "kernels_window.hip")]
+DEPS = SOURCES + [os.path.join(CSRC, n) for n in ("scan_kernels.hpp", "kernel_table.hpp",
+                                                   "variants.hpp")] + [os.path.join(INCLUDE, "rlca.h")]
 ARCH = "gfx950"
 
 
@@ -25,13 +28,25 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def build_command(out):
-    return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+def compile_command(src, obj):
+    return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-c",
             # Packed fp32 ops (v_pk_*_f32) stay off: plain scalar fp32 only.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # Leading scalar kernel arguments are preloaded into SGPRs.
             "-mllvm", "-amdgpu-kernarg-preload-count=16",
-            "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC] + SOURCES + ["-o", out]
+            "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC, src, "-o", obj]
+
+
+def link_command(objs, out):
+    return [hipcc(), "--offload-arch=" + ARCH, "-fPIC", "-shared"] + objs + ["-o", out]
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature.
+    out = "\n".join(l for l in res.stdout.splitlines()
+                    if "packed-fp32-ops" not in l and "hip-link" not in l)
+    return res.returncode, out
 
 
 def up_to_date():
@@ -43,19 +58,29 @@ def up_to_date():
 
 def build(verbose=False):
     """Compile librlca.so (always) and return its path."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = build_command(tmp)
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
-    # hipcc's host pass warns that it does not know the packed-fp32 feature.
-    out = "\n".join(l for l in res.stdout.splitlines()
-                    if "packed-fp32-ops" not in l and "hip-link" not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed (%d):\n%s" % (res.returncode, out))
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, LIB)
+    tag = ".tmp%d" % os.getpid()
+    objs = [os.path.join(PKG, os.path.basename(src).replace(".hip", tag + ".o")) for src in SOURCES]
+    cmds = [compile_command(src, obj) for src, obj in zip(SOURCES, objs)]
+    tmp = LIB + tag
+    try:
+        if verbose:
+            for c in cmds:
+                print(" ".join(c), flush=True)
+        with ThreadPoolExecutor(len(cmds)) as ex:
+            results = list(ex.map(_run, cmds))
+        for (rc, out), src in zip(results, SOURCES):
+            if rc != 0:
+                raise RuntimeError("hipcc failed on %s (%d):\n%s" % (src, rc, out))
+            if verbose and out.strip():
+                print(out)
+        rc, out = _run(link_command(objs, tmp))
+        if rc != 0:
+            raise RuntimeError("hipcc link failed (%d):\n%s" % (rc, out))
+        os.replace(tmp, LIB)
+    finally:
+        for f in objs + [tmp]:
+            if os.path.exists(f):
+                os.remove(f)
     return LIB
 
 

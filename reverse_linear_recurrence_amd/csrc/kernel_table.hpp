@@ -1,0 +1,37 @@
+// kernel_table.hpp -- instantiation of scan_kernel over variants, dtypes and
+// stride modes for one algorithm; included by the kernel translation units.
+#pragma once
+
+#include "rlca.h"
+#include "scan_kernels.hpp"
+#include "variants.hpp"
+
+namespace rlca {
+
+template <int A, typename InT, int V, bool U, bool C>
+const void *kernel_ptr() {
+  constexpr Variant v = kVariants[V];
+  return reinterpret_cast<const void *>(&scan_kernel<A, InT, kStepsPerLane, v.LPR, v.WPR, U, C>);
+}
+
+template <int A, typename InT, bool U, bool C>
+const void *kernel_ptr(int v) {
+  static_assert(kNumVariants == 6, "one case per variant");
+  switch (v) {
+    case 0: return kernel_ptr<A, InT, 0, U, C>();
+    case 1: return kernel_ptr<A, InT, 1, U, C>();
+    case 2: return kernel_ptr<A, InT, 2, U, C>();
+    case 3: return kernel_ptr<A, InT, 3, U, C>();
+    case 4: return kernel_ptr<A, InT, 4, U, C>();
+    default: return kernel_ptr<A, InT, 5, U, C>();
+  }
+}
+
+template <int A, bool C>
+const void *kernel_ptr(int dtype, int v, bool uniform) {
+  if (dtype == RLCA_BF16)
+    return uniform ? kernel_ptr<A, bf16_t, true, C>(v) : kernel_ptr<A, bf16_t, false, C>(v);
+  return uniform ? kernel_ptr<A, float, true, C>(v) : kernel_ptr<A, float, false, C>(v);
+}
+
+}  // namespace rlca

@@ -2,8 +2,9 @@
 // kernel launch for the C ABI declared in include/rlca.h.
 //
 // Nothing here touches element data: every step of the computation runs in
-// the kernels of scan_kernels.hpp.  A call validates its arguments, picks a
-// tiling variant, and enqueues exactly one kernel on the caller's stream.
+// the kernels of scan_kernels.hpp (instantiated in kernels_plain.hip and
+// kernels_window.hip).  A call validates its arguments, picks a tiling
+// variant, and enqueues exactly one kernel on the caller's stream.
 
 #include <hip/hip_runtime.h>
 
@@ -16,75 +17,10 @@
 
 #include "rlca.h"
 #include "scan_kernels.hpp"
+#include "variants.hpp"
 
 namespace rlca {
 namespace {
-
-// ------------------------------------------------------------- variants
-
-struct Variant {
-  int LPR;  // lanes per row inside a wavefront (64 when WPR > 1)
-  int WPR;  // wavefronts per row
-};
-
-// Every lane owns K = 4 consecutive steps: one 16-byte vector of each fp32
-// array (an 8-byte vector of each bf16 array) and one 16-byte vector of each
-// fp32 output, so every load and store instruction of a wavefront covers one
-// contiguous span and uses each cache line it touches in full.  (Longer spans
-// per lane split each instruction into strided partial lines: 4x the line
-// requests for 16 fp32 steps per lane, and partial-line output writes for 8
-// bf16 steps per lane.)
-constexpr int kStepsPerLane = 4;
-constexpr Variant kVariants[] = {
-    {16, 1},  // 0: tile    64 steps, 16 rows per 256-thread workgroup
-    {32, 1},  // 1: tile   128,  8 rows per workgroup
-    {64, 1},  // 2: tile   256,  4 rows per workgroup
-    {64, 4},  // 3: tile  1024,  1 row per 256-thread workgroup
-    {64, 8},  // 4: tile  2048,  1 row per 512-thread workgroup
-    {64, 16}, // 5: tile  4096,  1 row per 1024-thread workgroup
-};
-constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
-
-int64_t tile_steps(const Variant &v, int /*dtype*/) {
-  return static_cast<int64_t>(kStepsPerLane) * v.LPR * v.WPR;
-}
-
-template <int A, typename InT, int V, bool U>
-const void *kernel_for() {
-  constexpr Variant v = kVariants[V];
-  return reinterpret_cast<const void *>(&scan_kernel<A, InT, kStepsPerLane, v.LPR, v.WPR, U>);
-}
-
-template <int A, typename InT, bool U>
-const void *kernel_for(int v) {
-  switch (v) {
-    case 0: return kernel_for<A, InT, 0, U>();
-    case 1: return kernel_for<A, InT, 1, U>();
-    case 2: return kernel_for<A, InT, 2, U>();
-    case 3: return kernel_for<A, InT, 3, U>();
-    case 4: return kernel_for<A, InT, 4, U>();
-    default: return kernel_for<A, InT, 5, U>();
-  }
-}
-
-template <int A>
-const void *kernel_for(int dtype, int v, bool uniform) {
-  if (dtype == RLCA_BF16)
-    return uniform ? kernel_for<A, bf16_t, true>(v) : kernel_for<A, bf16_t, false>(v);
-  return uniform ? kernel_for<A, float, true>(v) : kernel_for<A, float, false>(v);
-}
-
-const void *kernel_for(int algo, int dtype, int v, bool uniform) {
-  switch (algo) {
-    case kReturns: return kernel_for<kReturns>(dtype, v, uniform);
-    case kGae: return kernel_for<kGae>(dtype, v, uniform);
-    case kTdLambda: return kernel_for<kTdLambda>(dtype, v, uniform);
-    case kVtrace: return kernel_for<kVtrace>(dtype, v, uniform);
-    case kRetrace: return kernel_for<kRetrace>(dtype, v, uniform);
-    case kEligibility: return kernel_for<kEligibility>(dtype, v, uniform);
-    default: return kernel_for<kCumsum>(dtype, v, uniform);
-  }
-}
 
 // Default tiling (measured on MI355X).  Short rows: the smallest
 // one-wavefront tile that covers T.  Long rows (tiles loop along T, each
@@ -92,14 +28,14 @@ const void *kernel_for(int algo, int dtype, int v, bool uniform) {
 // wavefronts (16 per CU) -- the most wavefronts per row such that N * WPR
 // stays within that and the tile is not longer than the row; from 8192 rows
 // on, one wavefront per row.
-int auto_variant(int64_t N, int64_t T, int dtype) {
+int auto_variant(int64_t N, int64_t T) {
   constexpr int64_t kTargetWaves = 4096;
   for (int v = 0; v <= 2; ++v)
-    if (T <= tile_steps(kVariants[v], dtype)) return v;
+    if (T <= tile_steps(kVariants[v])) return v;
   if (N >= 2 * kTargetWaves) return 2;
   for (int v = kNumVariants - 1; v >= 3; --v)
-    if (N * kVariants[v].WPR <= kTargetWaves && tile_steps(kVariants[v], dtype) <= T) return v;
-  return tile_steps(kVariants[3], dtype) <= T ? 3 : 2;
+    if (N * kVariants[v].WPR <= kTargetWaves && tile_steps(kVariants[v]) <= T) return v;
+  return tile_steps(kVariants[3]) <= T ? 3 : 2;
 }
 
 // ------------------------------------------------------------- errors
@@ -202,8 +138,9 @@ int check_sizes(int64_t N, int64_t T, int dtype) {
     if (rc_ != RLCA_OK) return rc_; \
   } while (0)
 
-int launch(int algo, int dtype, const Args &args, void *stream) {
-  const int v = t_forced_variant >= 0 ? t_forced_variant : auto_variant(args.N, args.T, dtype);
+// window: the instance with carry vectors (Args::cin, cout, cmap).
+int launch(int algo, int dtype, const Args &args, void *stream, bool window = false) {
+  const int v = t_forced_variant >= 0 ? t_forced_variant : auto_variant(args.N, args.T);
   const Variant var = kVariants[v];
   dim3 grid, block;
   if (var.WPR > 1) {
@@ -246,6 +183,11 @@ int launch(int algo, int dtype, const Args &args, void *stream) {
       hot[4] = a.term; hld[4] = a.ld_term;
       ldx = a.trunc != nullptr ? 1 : 0;
       break;
+    case kAffine:
+    case kAffineFwd:
+      hot[1] = a.v; hld[1] = a.ld_v;  // beta
+      hot[2] = a.term; hld[2] = a.ld_term;  // reset flags
+      break;
     default:  // kEligibility, kCumsum
       hot[1] = a.term; hld[1] = a.ld_term;
       hot[2] = a.trunc; hld[2] = a.ld_trunc;
@@ -260,7 +202,10 @@ int launch(int algo, int dtype, const Args &args, void *stream) {
   int ldT = static_cast<int>(a.ld_r);
   int ldX = static_cast<int>(ldx);
   void *kargs[] = {&hot[0], &hot[1], &hot[2], &hot[3], &hot[4], &N32, &T32, &ldT, &ldX, &a};
-  const hipError_t e = hipLaunchKernel(kernel_for(algo, dtype, v, uniform), grid, block, kargs, 0,
+  const void *kernel = window ? window_kernel(algo, dtype, v, uniform)
+                              : plain_kernel(algo, dtype, v, uniform);
+  if (kernel == nullptr) return fail(RLCA_EINVAL, "no kernel for algorithm %d", algo);
+  const hipError_t e = hipLaunchKernel(kernel, grid, block, kargs, 0,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess)
     return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
@@ -269,6 +214,201 @@ int launch(int algo, int dtype, const Args &args, void *stream) {
 }
 
 int64_t esize_of(int dtype) { return dtype == RLCA_BF16 ? 2 : 4; }
+
+// The carry vectors of a window call (all NULL and off for the plain calls).
+struct Window {
+  bool on;
+  const float *cin;
+  float *cout;
+  float *cmap;
+};
+constexpr Window kNoWindow{false, nullptr, nullptr, nullptr};
+
+// Validate the arrays of a call (plus the window's carry vectors), then fill
+// the window fields of Args and launch.  arrs has room for n + 3 entries.
+int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const Window &w,
+                        Args &a, void *stream) {
+  if (w.on) {
+    arrs[n++] = Arr{"carry_in", w.cin, N, N, 4, false, false, true};
+    arrs[n++] = Arr{"carry_out", w.cout, N, N, 4, false, true, true};
+    arrs[n++] = Arr{"carry_map", w.cmap, 2 * N, 2 * N, 4, false, true, true};
+  }
+  if (N == 0 || a.T == 0) return RLCA_OK;
+  for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], N));
+  RLCA_TRY(check_aliasing(arrs, n));
+  a.cin = w.cin;
+  a.cout = w.cout;
+  a.cmap = w.cmap;
+  return launch(algo, dtype, a, stream, w.on);
+}
+
+int returns_impl(int64_t num_envs, int64_t T, int dtype, const void *rewards, int64_t ld_rewards,
+                 const uint8_t *terminated, int64_t ld_terminated, const uint8_t *truncated,
+                 int64_t ld_truncated, const void *trunc_values, int64_t ld_trunc_values,
+                 const void *bootstrap, float gamma, float *returns, int64_t ld_returns,
+                 const Window &w, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_unit("gamma", gamma));
+  if (truncated != nullptr && trunc_values == nullptr)
+    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
+  const int64_t es = esize_of(dtype);
+  const bool tv_used = truncated != nullptr;
+  Arr arrs[9] = {
+      {"rewards", rewards, ld_rewards, T, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
+      {"bootstrap", bootstrap, num_envs, num_envs, es, false, false, true},
+      {"returns", returns, ld_returns, T, 4, true, true},
+  };
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = rewards; a.ld_r = ld_rewards;
+  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
+  a.boot = bootstrap;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = returns; a.ld_o0 = ld_returns;
+  a.gamma = gamma; a.lam = 1.f; a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
+  return validate_and_launch(kReturns, dtype, num_envs, arrs, 6, w, a, stream);
+}
+
+int gae_like(int algo, int64_t num_envs, int64_t T, int dtype, const void *rewards,
+             int64_t ld_rewards, const void *values, int64_t ld_values,
+             const uint8_t *terminated, int64_t ld_terminated, const uint8_t *truncated,
+             int64_t ld_truncated, const void *trunc_values, int64_t ld_trunc_values,
+             float gamma, float lam, float *out0, int64_t ld_out0, float *out1,
+             int64_t ld_out1, const char *name0, const char *name1, const Window &w,
+             void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  if (truncated != nullptr && trunc_values == nullptr)
+    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
+  const int64_t es = esize_of(dtype);
+  const bool tv_used = truncated != nullptr;
+  Arr arrs[10] = {
+      {"rewards", rewards, ld_rewards, T, es, true, false},
+      {"values", values, ld_values, T + 1, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
+      {name0, out0, ld_out0, T, 4, true, true},
+      {name1, out1, ld_out1, T, 4, false, true},
+  };
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = rewards; a.ld_r = ld_rewards;
+  a.v = values; a.ld_v = ld_values;
+  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = out0; a.ld_o0 = ld_out0;
+  a.o1 = out1; a.ld_o1 = ld_out1;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
+  return validate_and_launch(algo, dtype, num_envs, arrs, 7, w, a, stream);
+}
+
+int vtrace_impl(int64_t num_envs, int64_t T, int dtype, const void *rewards, int64_t ld_rewards,
+                const void *values, int64_t ld_values, const void *log_rhos,
+                int64_t ld_log_rhos, const uint8_t *terminated, int64_t ld_terminated,
+                const uint8_t *truncated, int64_t ld_truncated, const void *trunc_values,
+                int64_t ld_trunc_values, float gamma, float lam, float rho_bar, float c_bar,
+                float pg_rho_bar, float *vs, int64_t ld_vs, float *pg_advantages,
+                int64_t ld_pg_advantages, const Window &w, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  RLCA_TRY(check_clip("rho_bar", rho_bar));
+  RLCA_TRY(check_clip("c_bar", c_bar));
+  RLCA_TRY(check_clip("pg_rho_bar", pg_rho_bar));
+  if (truncated != nullptr && trunc_values == nullptr)
+    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
+  const int64_t es = esize_of(dtype);
+  const bool tv_used = truncated != nullptr;
+  Arr arrs[11] = {
+      {"rewards", rewards, ld_rewards, T, es, true, false},
+      {"values", values, ld_values, T + 1, es, true, false},
+      {"log_rhos", log_rhos, ld_log_rhos, T, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
+      {"vs", vs, ld_vs, T, 4, true, true},
+      {"pg_advantages", pg_advantages, ld_pg_advantages, T, 4, false, true},
+  };
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = rewards; a.ld_r = ld_rewards;
+  a.v = values; a.ld_v = ld_values;
+  a.lr = log_rhos; a.ld_lr = ld_log_rhos;
+  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = vs; a.ld_o0 = ld_vs;
+  a.o1 = pg_advantages; a.ld_o1 = ld_pg_advantages;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = rho_bar; a.c_bar = c_bar; a.pg_rho_bar = pg_rho_bar;
+  return validate_and_launch(kVtrace, dtype, num_envs, arrs, 8, w, a, stream);
+}
+
+int retrace_impl(int64_t num_envs, int64_t T, int dtype, const void *rewards, int64_t ld_rewards,
+                 const void *q_taken, int64_t ld_q_taken, const void *exp_q_next,
+                 int64_t ld_exp_q_next, const void *log_rhos, int64_t ld_log_rhos,
+                 const uint8_t *terminated, int64_t ld_terminated, const uint8_t *truncated,
+                 int64_t ld_truncated, float gamma, float lam, float c_bar, float *q_ret,
+                 int64_t ld_q_ret, const Window &w, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  RLCA_TRY(check_clip("c_bar", c_bar));
+  const int64_t es = esize_of(dtype);
+  Arr arrs[10] = {
+      {"rewards", rewards, ld_rewards, T, es, true, false},
+      {"q_taken", q_taken, ld_q_taken, T, es, true, false},
+      {"exp_q_next", exp_q_next, ld_exp_q_next, T, es, true, false},
+      {"log_rhos", log_rhos, ld_log_rhos, T, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {"q_ret", q_ret, ld_q_ret, T, 4, true, true},
+  };
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = rewards; a.ld_r = ld_rewards;
+  a.v = q_taken; a.ld_v = ld_q_taken;
+  a.eq = exp_q_next; a.ld_eq = ld_exp_q_next;
+  a.lr = log_rhos; a.ld_lr = ld_log_rhos;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = q_ret; a.ld_o0 = ld_q_ret;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = 1.f; a.c_bar = c_bar; a.pg_rho_bar = 1.f;
+  return validate_and_launch(kRetrace, dtype, num_envs, arrs, 7, w, a, stream);
+}
+
+int forward_like(int algo, int64_t num_envs, int64_t T, int dtype, const void *x, int64_t ld_x,
+                 const uint8_t *terminated, int64_t ld_terminated, const uint8_t *truncated,
+                 int64_t ld_truncated, const void *init, float gamma, float lam, float *out,
+                 int64_t ld_out, const char *init_name, const char *out_name, const Window &w,
+                 void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  const int64_t es = esize_of(dtype);
+  Arr arrs[8] = {
+      {"x", x, ld_x, T, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {init_name, init, num_envs, num_envs, es, false, false, true},
+      {out_name, out, ld_out, T, 4, true, true},
+  };
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = x; a.ld_r = ld_x;
+  a.boot = init;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = out; a.ld_o0 = ld_out;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
+  return validate_and_launch(algo, dtype, num_envs, arrs, 5, w, a, stream);
+}
 
 }  // namespace
 }  // namespace rlca
@@ -282,71 +422,9 @@ int rlca_returns(int64_t num_envs, int64_t T, int dtype, const void *rewards, in
                  int64_t ld_truncated, const void *trunc_values, int64_t ld_trunc_values,
                  const void *bootstrap, float gamma, float *returns, int64_t ld_returns,
                  void *stream) {
-  RLCA_TRY(check_sizes(num_envs, T, dtype));
-  RLCA_TRY(check_unit("gamma", gamma));
-  if (truncated != nullptr && trunc_values == nullptr)
-    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
-  const int64_t es = esize_of(dtype);
-  const bool tv_used = truncated != nullptr;
-  Arr arrs[] = {
-      {"rewards", rewards, ld_rewards, T, es, true, false},
-      {"terminated", terminated, ld_terminated, T, 1, false, false},
-      {"truncated", truncated, ld_truncated, T, 1, false, false},
-      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
-      {"bootstrap", bootstrap, num_envs, num_envs, es, false, false, true},
-      {"returns", returns, ld_returns, T, 4, true, true},
-  };
-  if (num_envs == 0 || T == 0) return RLCA_OK;
-  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
-  RLCA_TRY(check_aliasing(arrs, 6));
-  Args a{};
-  a.N = num_envs; a.T = T;
-  a.r = rewards; a.ld_r = ld_rewards;
-  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
-  a.boot = bootstrap;
-  a.term = terminated; a.ld_term = ld_terminated;
-  a.trunc = truncated; a.ld_trunc = ld_truncated;
-  a.o0 = returns; a.ld_o0 = ld_returns;
-  a.gamma = gamma; a.lam = 1.f; a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
-  return launch(kReturns, dtype, a, stream);
-}
-
-static int gae_like(int algo, int64_t num_envs, int64_t T, int dtype, const void *rewards,
-                    int64_t ld_rewards, const void *values, int64_t ld_values,
-                    const uint8_t *terminated, int64_t ld_terminated, const uint8_t *truncated,
-                    int64_t ld_truncated, const void *trunc_values, int64_t ld_trunc_values,
-                    float gamma, float lam, float *out0, int64_t ld_out0, float *out1,
-                    int64_t ld_out1, const char *name0, const char *name1, void *stream) {
-  RLCA_TRY(check_sizes(num_envs, T, dtype));
-  RLCA_TRY(check_unit("gamma", gamma));
-  RLCA_TRY(check_unit("lam", lam));
-  if (truncated != nullptr && trunc_values == nullptr)
-    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
-  const int64_t es = esize_of(dtype);
-  const bool tv_used = truncated != nullptr;
-  Arr arrs[] = {
-      {"rewards", rewards, ld_rewards, T, es, true, false},
-      {"values", values, ld_values, T + 1, es, true, false},
-      {"terminated", terminated, ld_terminated, T, 1, false, false},
-      {"truncated", truncated, ld_truncated, T, 1, false, false},
-      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
-      {name0, out0, ld_out0, T, 4, true, true},
-      {name1, out1, ld_out1, T, 4, false, true},
-  };
-  if (num_envs == 0 || T == 0) return RLCA_OK;
-  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
-  RLCA_TRY(check_aliasing(arrs, 7));
-  Args a{};
-  a.N = num_envs; a.T = T;
-  a.r = rewards; a.ld_r = ld_rewards;
-  a.v = values; a.ld_v = ld_values;
-  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
-  a.term = terminated; a.ld_term = ld_terminated;
-  a.trunc = truncated; a.ld_trunc = ld_truncated;
-  a.o0 = out0; a.ld_o0 = ld_out0;
-  a.o1 = out1; a.ld_o1 = ld_out1;
-  a.gamma = gamma; a.lam = lam; a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
-  return launch(algo, dtype, a, stream);
+  return returns_impl(num_envs, T, dtype, rewards, ld_rewards, terminated, ld_terminated,
+                      truncated, ld_truncated, trunc_values, ld_trunc_values, bootstrap, gamma,
+                      returns, ld_returns, kNoWindow, stream);
 }
 
 int rlca_gae(int64_t num_envs, int64_t T, int dtype, const void *rewards, int64_t ld_rewards,
@@ -358,7 +436,7 @@ int rlca_gae(int64_t num_envs, int64_t T, int dtype, const void *rewards, int64_
   return gae_like(kGae, num_envs, T, dtype, rewards, ld_rewards, values, ld_values, terminated,
                   ld_terminated, truncated, ld_truncated, trunc_values, ld_trunc_values, gamma,
                   lam, advantages, ld_advantages, targets, ld_targets, "advantages", "targets",
-                  stream);
+                  kNoWindow, stream);
 }
 
 int rlca_td_lambda(int64_t num_envs, int64_t T, int dtype, const void *rewards,
@@ -370,7 +448,7 @@ int rlca_td_lambda(int64_t num_envs, int64_t T, int dtype, const void *rewards,
   return gae_like(kTdLambda, num_envs, T, dtype, rewards, ld_rewards, values, ld_values,
                   terminated, ld_terminated, truncated, ld_truncated, trunc_values,
                   ld_trunc_values, gamma, lam, lambda_returns, ld_lambda_returns, nullptr, 0,
-                  "lambda_returns", "unused", stream);
+                  "lambda_returns", "unused", kNoWindow, stream);
 }
 
 int rlca_vtrace(int64_t num_envs, int64_t T, int dtype, const void *rewards, int64_t ld_rewards,
@@ -380,41 +458,10 @@ int rlca_vtrace(int64_t num_envs, int64_t T, int dtype, const void *rewards, int
                 int64_t ld_trunc_values, float gamma, float lam, float rho_bar, float c_bar,
                 float pg_rho_bar, float *vs, int64_t ld_vs, float *pg_advantages,
                 int64_t ld_pg_advantages, void *stream) {
-  RLCA_TRY(check_sizes(num_envs, T, dtype));
-  RLCA_TRY(check_unit("gamma", gamma));
-  RLCA_TRY(check_unit("lam", lam));
-  RLCA_TRY(check_clip("rho_bar", rho_bar));
-  RLCA_TRY(check_clip("c_bar", c_bar));
-  RLCA_TRY(check_clip("pg_rho_bar", pg_rho_bar));
-  if (truncated != nullptr && trunc_values == nullptr)
-    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
-  const int64_t es = esize_of(dtype);
-  const bool tv_used = truncated != nullptr;
-  Arr arrs[] = {
-      {"rewards", rewards, ld_rewards, T, es, true, false},
-      {"values", values, ld_values, T + 1, es, true, false},
-      {"log_rhos", log_rhos, ld_log_rhos, T, es, true, false},
-      {"terminated", terminated, ld_terminated, T, 1, false, false},
-      {"truncated", truncated, ld_truncated, T, 1, false, false},
-      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
-      {"vs", vs, ld_vs, T, 4, true, true},
-      {"pg_advantages", pg_advantages, ld_pg_advantages, T, 4, false, true},
-  };
-  if (num_envs == 0 || T == 0) return RLCA_OK;
-  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
-  RLCA_TRY(check_aliasing(arrs, 8));
-  Args a{};
-  a.N = num_envs; a.T = T;
-  a.r = rewards; a.ld_r = ld_rewards;
-  a.v = values; a.ld_v = ld_values;
-  a.lr = log_rhos; a.ld_lr = ld_log_rhos;
-  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
-  a.term = terminated; a.ld_term = ld_terminated;
-  a.trunc = truncated; a.ld_trunc = ld_truncated;
-  a.o0 = vs; a.ld_o0 = ld_vs;
-  a.o1 = pg_advantages; a.ld_o1 = ld_pg_advantages;
-  a.gamma = gamma; a.lam = lam; a.rho_bar = rho_bar; a.c_bar = c_bar; a.pg_rho_bar = pg_rho_bar;
-  return launch(kVtrace, dtype, a, stream);
+  return vtrace_impl(num_envs, T, dtype, rewards, ld_rewards, values, ld_values, log_rhos,
+                     ld_log_rhos, terminated, ld_terminated, truncated, ld_truncated,
+                     trunc_values, ld_trunc_values, gamma, lam, rho_bar, c_bar, pg_rho_bar, vs,
+                     ld_vs, pg_advantages, ld_pg_advantages, kNoWindow, stream);
 }
 
 int rlca_retrace(int64_t num_envs, int64_t T, int dtype, const void *rewards, int64_t ld_rewards,
@@ -423,64 +470,10 @@ int rlca_retrace(int64_t num_envs, int64_t T, int dtype, const void *rewards, in
                  const uint8_t *terminated, int64_t ld_terminated, const uint8_t *truncated,
                  int64_t ld_truncated, float gamma, float lam, float c_bar, float *q_ret,
                  int64_t ld_q_ret, void *stream) {
-  RLCA_TRY(check_sizes(num_envs, T, dtype));
-  RLCA_TRY(check_unit("gamma", gamma));
-  RLCA_TRY(check_unit("lam", lam));
-  RLCA_TRY(check_clip("c_bar", c_bar));
-  const int64_t es = esize_of(dtype);
-  Arr arrs[] = {
-      {"rewards", rewards, ld_rewards, T, es, true, false},
-      {"q_taken", q_taken, ld_q_taken, T, es, true, false},
-      {"exp_q_next", exp_q_next, ld_exp_q_next, T, es, true, false},
-      {"log_rhos", log_rhos, ld_log_rhos, T, es, true, false},
-      {"terminated", terminated, ld_terminated, T, 1, false, false},
-      {"truncated", truncated, ld_truncated, T, 1, false, false},
-      {"q_ret", q_ret, ld_q_ret, T, 4, true, true},
-  };
-  if (num_envs == 0 || T == 0) return RLCA_OK;
-  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
-  RLCA_TRY(check_aliasing(arrs, 7));
-  Args a{};
-  a.N = num_envs; a.T = T;
-  a.r = rewards; a.ld_r = ld_rewards;
-  a.v = q_taken; a.ld_v = ld_q_taken;
-  a.eq = exp_q_next; a.ld_eq = ld_exp_q_next;
-  a.lr = log_rhos; a.ld_lr = ld_log_rhos;
-  a.term = terminated; a.ld_term = ld_terminated;
-  a.trunc = truncated; a.ld_trunc = ld_truncated;
-  a.o0 = q_ret; a.ld_o0 = ld_q_ret;
-  a.gamma = gamma; a.lam = lam; a.rho_bar = 1.f; a.c_bar = c_bar; a.pg_rho_bar = 1.f;
-  return launch(kRetrace, dtype, a, stream);
-}
-
-static int forward_like(int algo, int64_t num_envs, int64_t T, int dtype, const void *x,
-                        int64_t ld_x, const uint8_t *terminated, int64_t ld_terminated,
-                        const uint8_t *truncated, int64_t ld_truncated, const void *init,
-                        float gamma, float lam, float *out, int64_t ld_out, const char *init_name,
-                        const char *out_name, void *stream) {
-  RLCA_TRY(check_sizes(num_envs, T, dtype));
-  RLCA_TRY(check_unit("gamma", gamma));
-  RLCA_TRY(check_unit("lam", lam));
-  const int64_t es = esize_of(dtype);
-  Arr arrs[] = {
-      {"x", x, ld_x, T, es, true, false},
-      {"terminated", terminated, ld_terminated, T, 1, false, false},
-      {"truncated", truncated, ld_truncated, T, 1, false, false},
-      {init_name, init, num_envs, num_envs, es, false, false, true},
-      {out_name, out, ld_out, T, 4, true, true},
-  };
-  if (num_envs == 0 || T == 0) return RLCA_OK;
-  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
-  RLCA_TRY(check_aliasing(arrs, 5));
-  Args a{};
-  a.N = num_envs; a.T = T;
-  a.r = x; a.ld_r = ld_x;
-  a.boot = init;
-  a.term = terminated; a.ld_term = ld_terminated;
-  a.trunc = truncated; a.ld_trunc = ld_truncated;
-  a.o0 = out; a.ld_o0 = ld_out;
-  a.gamma = gamma; a.lam = lam; a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
-  return launch(algo, dtype, a, stream);
+  return retrace_impl(num_envs, T, dtype, rewards, ld_rewards, q_taken, ld_q_taken, exp_q_next,
+                      ld_exp_q_next, log_rhos, ld_log_rhos, terminated, ld_terminated,
+                      truncated, ld_truncated, gamma, lam, c_bar, q_ret, ld_q_ret, kNoWindow,
+                      stream);
 }
 
 int rlca_eligibility_trace(int64_t num_envs, int64_t T, int dtype, const void *x, int64_t ld_x,
@@ -490,7 +483,7 @@ int rlca_eligibility_trace(int64_t num_envs, int64_t T, int dtype, const void *x
                            void *stream) {
   return forward_like(kEligibility, num_envs, T, dtype, x, ld_x, terminated, ld_terminated,
                       truncated, ld_truncated, z_init, gamma, lam, traces, ld_traces, "z_init",
-                      "traces", stream);
+                      "traces", kNoWindow, stream);
 }
 
 int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype, const void *x, int64_t ld_x,
@@ -498,12 +491,128 @@ int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype, const void *x, 
                          const uint8_t *truncated, int64_t ld_truncated, const void *s_init,
                          float *sums, int64_t ld_sums, void *stream) {
   return forward_like(kCumsum, num_envs, T, dtype, x, ld_x, terminated, ld_terminated, truncated,
-                      ld_truncated, s_init, 1.f, 1.f, sums, ld_sums, "s_init", "sums", stream);
+                      ld_truncated, s_init, 1.f, 1.f, sums, ld_sums, "s_init", "sums", kNoWindow,
+                      stream);
+}
+
+// ------------------------------------------------------ window entry points
+
+int rlca_returns_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                       int64_t ld_rewards, const uint8_t *terminated, int64_t ld_terminated,
+                       const uint8_t *truncated, int64_t ld_truncated, const void *trunc_values,
+                       int64_t ld_trunc_values, const float *carry_in, float gamma,
+                       float *returns, int64_t ld_returns, float *carry_out, float *carry_map,
+                       void *stream) {
+  return returns_impl(num_envs, T, dtype, rewards, ld_rewards, terminated, ld_terminated,
+                      truncated, ld_truncated, trunc_values, ld_trunc_values, nullptr, gamma,
+                      returns, ld_returns, Window{true, carry_in, carry_out, carry_map}, stream);
+}
+
+int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                   int64_t ld_rewards, const void *values, int64_t ld_values,
+                   const uint8_t *terminated, int64_t ld_terminated, const uint8_t *truncated,
+                   int64_t ld_truncated, const void *trunc_values, int64_t ld_trunc_values,
+                   float gamma, float lam, float *advantages, int64_t ld_advantages,
+                   float *targets, int64_t ld_targets, const float *carry_in, float *carry_out,
+                   float *carry_map, void *stream) {
+  return gae_like(kGae, num_envs, T, dtype, rewards, ld_rewards, values, ld_values, terminated,
+                  ld_terminated, truncated, ld_truncated, trunc_values, ld_trunc_values, gamma,
+                  lam, advantages, ld_advantages, targets, ld_targets, "advantages", "targets",
+                  Window{true, carry_in, carry_out, carry_map}, stream);
+}
+
+int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                         int64_t ld_rewards, const void *values, int64_t ld_values,
+                         const uint8_t *terminated, int64_t ld_terminated,
+                         const uint8_t *truncated, int64_t ld_truncated,
+                         const void *trunc_values, int64_t ld_trunc_values, float gamma,
+                         float lam, float *lambda_returns, int64_t ld_lambda_returns,
+                         const float *carry_in, float *carry_out, float *carry_map,
+                         void *stream) {
+  return gae_like(kTdLambda, num_envs, T, dtype, rewards, ld_rewards, values, ld_values,
+                  terminated, ld_terminated, truncated, ld_truncated, trunc_values,
+                  ld_trunc_values, gamma, lam, lambda_returns, ld_lambda_returns, nullptr, 0,
+                  "lambda_returns", "unused", Window{true, carry_in, carry_out, carry_map},
+                  stream);
+}
+
+int rlca_vtrace_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                      int64_t ld_rewards, const void *values, int64_t ld_values,
+                      const void *log_rhos, int64_t ld_log_rhos, const uint8_t *terminated,
+                      int64_t ld_terminated, const uint8_t *truncated, int64_t ld_truncated,
+                      const void *trunc_values, int64_t ld_trunc_values, float gamma, float lam,
+                      float rho_bar, float c_bar, float pg_rho_bar, float *vs, int64_t ld_vs,
+                      float *pg_advantages, int64_t ld_pg_advantages, const float *carry_in,
+                      float *carry_out, float *carry_map, void *stream) {
+  return vtrace_impl(num_envs, T, dtype, rewards, ld_rewards, values, ld_values, log_rhos,
+                     ld_log_rhos, terminated, ld_terminated, truncated, ld_truncated,
+                     trunc_values, ld_trunc_values, gamma, lam, rho_bar, c_bar, pg_rho_bar, vs,
+                     ld_vs, pg_advantages, ld_pg_advantages,
+                     Window{true, carry_in, carry_out, carry_map}, stream);
+}
+
+int rlca_retrace_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                       int64_t ld_rewards, const void *q_taken, int64_t ld_q_taken,
+                       const void *exp_q_next, int64_t ld_exp_q_next, const void *log_rhos,
+                       int64_t ld_log_rhos, const uint8_t *terminated, int64_t ld_terminated,
+                       const uint8_t *truncated, int64_t ld_truncated, float gamma, float lam,
+                       float c_bar, float *q_ret, int64_t ld_q_ret, const float *carry_in,
+                       float *carry_out, float *carry_map, void *stream) {
+  return retrace_impl(num_envs, T, dtype, rewards, ld_rewards, q_taken, ld_q_taken, exp_q_next,
+                      ld_exp_q_next, log_rhos, ld_log_rhos, terminated, ld_terminated,
+                      truncated, ld_truncated, gamma, lam, c_bar, q_ret, ld_q_ret,
+                      Window{true, carry_in, carry_out, carry_map}, stream);
+}
+
+int rlca_eligibility_trace_chunk(int64_t num_envs, int64_t T, int dtype, const void *x,
+                                 int64_t ld_x, const uint8_t *terminated, int64_t ld_terminated,
+                                 const uint8_t *truncated, int64_t ld_truncated,
+                                 const float *carry_in, float gamma, float lam, float *traces,
+                                 int64_t ld_traces, float *carry_out, float *carry_map,
+                                 void *stream) {
+  return forward_like(kEligibility, num_envs, T, dtype, x, ld_x, terminated, ld_terminated,
+                      truncated, ld_truncated, nullptr, gamma, lam, traces, ld_traces, "z_init",
+                      "traces", Window{true, carry_in, carry_out, carry_map}, stream);
+}
+
+int rlca_episodic_cumsum_chunk(int64_t num_envs, int64_t T, int dtype, const void *x,
+                               int64_t ld_x, const uint8_t *terminated, int64_t ld_terminated,
+                               const uint8_t *truncated, int64_t ld_truncated,
+                               const float *carry_in, float *sums, int64_t ld_sums,
+                               float *carry_out, float *carry_map, void *stream) {
+  return forward_like(kCumsum, num_envs, T, dtype, x, ld_x, terminated, ld_terminated, truncated,
+                      ld_truncated, nullptr, 1.f, 1.f, sums, ld_sums, "s_init", "sums",
+                      Window{true, carry_in, carry_out, carry_map}, stream);
+}
+
+int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype, const void *alpha,
+                     int64_t ld_alpha, const void *beta, int64_t ld_beta, const uint8_t *reset,
+                     int64_t ld_reset, int reverse, const float *carry_in, float *out,
+                     int64_t ld_out, float *carry_out, float *carry_map, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  if (reverse != 0 && reverse != 1)
+    return fail(RLCA_EINVAL, "reverse = %d must be 0 or 1", reverse);
+  const int64_t es = esize_of(dtype);
+  Arr arrs[7] = {
+      {"alpha", alpha, ld_alpha, T, es, true, false},
+      {"beta", beta, ld_beta, T, es, true, false},
+      {"reset", reset, ld_reset, T, 1, false, false},
+      {"out", out, ld_out, T, 4, true, true},
+  };
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = alpha; a.ld_r = ld_alpha;
+  a.v = beta; a.ld_v = ld_beta;
+  a.term = reset; a.ld_term = ld_reset;
+  a.o0 = out; a.ld_o0 = ld_out;
+  a.gamma = a.lam = a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
+  return validate_and_launch(reverse ? kAffine : kAffineFwd, dtype, num_envs, arrs, 4,
+                            Window{true, carry_in, carry_out, carry_map}, a, stream);
 }
 
 const char *rlca_last_error(void) { return t_last_error.c_str(); }
 
-int rlca_version(void) { return 100; }  // 0.1.0
+int rlca_version(void) { return 200; }  // 0.2.0: window entry points, affine scan
 
 int rlca_num_variants(void) { return kNumVariants; }
 

@@ -35,6 +35,12 @@
 //   * HBM traffic is one read of every input element the method uses (plus
 //     the V_{t+1} / log_rho_{t+1} neighbour, which hits in cache) and one
 //     write of every output element.  No intermediate touches HBM.
+//   * Window instances (kChunk): the carry entering the window is read from a
+//     per-row vector, and the row's outgoing carry and the affine map from
+//     the incoming to the outgoing carry (the composite of every step, kept
+//     beside the scalar carry from tile to tile) are written per row, so that
+//     consecutive windows of one rollout chain exactly (Method 3, rollout
+//     windows; the operator is associative).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -45,7 +51,10 @@ namespace rlca {
 enum Algo : int {
   kReturns = 0, kGae = 1, kTdLambda = 2, kVtrace = 3, kRetrace = 4,
   // forward-time mirrors: A_t = alpha_t + beta_t * A_{t-1}
-  kEligibility = 5, kCumsum = 6
+  kEligibility = 5, kCumsum = 6,
+  // the generic segmented scan over caller-given (alpha, beta), reverse and
+  // forward in time
+  kAffine = 7, kAffineFwd = 8
 };
 
 using bf16_t = uint16_t;  // raw bfloat16 bits
@@ -61,6 +70,9 @@ using bf16_t = uint16_t;  // raw bfloat16 bits
 //   boot   window bootstrap [N], nullable                 (returns)
 //   o0     returns | advantages | lambda returns | vs | q_ret
 //   o1     targets (gae) | pg advantages (vtrace), nullable
+// Generic scan: r = alpha, v = beta [N,T], term = reset flags, o0 = A.
+// Window instances only: cin [N] incoming carry (nullable: 0), cout [N]
+// outgoing carry, cmap [N,2] carry map, both nullable.
 struct Args {
   int64_t N, T;
   const void *r;  int64_t ld_r;
@@ -74,6 +86,9 @@ struct Args {
   float *o0; int64_t ld_o0;
   float *o1; int64_t ld_o1;
   float gamma, lam, rho_bar, c_bar, pg_rho_bar;
+  const float *cin;
+  float *cout;
+  float *cmap;
 };
 
 // Hot streams: the (up to) five arrays each algorithm reads at the start of a
@@ -86,6 +101,7 @@ struct Args {
 //   vtrace:         h = r, v, log_rho, term, trunc     (trunc_values cold)
 //   retrace:        h = r, q, eq, log_rho, term        (trunc cold)
 //   eligibility, cumsum: h = x (in r), term, trunc, initial carry [N], -
+//   affine (both directions): h = alpha, beta, reset, -, -
 // ldT is the common row stride of the hot [N,T] streams, ldX the stride of
 // values (gae, td_lambda, vtrace) or 1 if truncation flags are given
 // (retrace).  When the hot [N,T] streams do not share one stride, the
@@ -290,7 +306,11 @@ __device__ __forceinline__ int64_t late_v(int64_t x) {
 }
 
 template <int A> struct Uses {
-  static constexpr bool forward = A == kEligibility || A == kCumsum;
+  static constexpr bool forward = A == kEligibility || A == kCumsum || A == kAffineFwd;
+  // Reset by the flags of the step before (an episode that ended after step
+  // t-1 restarts at t); the generic scan uses the flag of the step itself.
+  static constexpr bool prev_flags = A == kEligibility || A == kCumsum;
+  static constexpr bool affine = A == kAffine || A == kAffineFwd;  // beta [N,T] in v
   static constexpr bool values = A == kGae || A == kTdLambda || A == kVtrace;  // V [N,T+1]
   static constexpr bool q = A == kRetrace;
   static constexpr bool log_rho = A == kVtrace || A == kRetrace;
@@ -367,8 +387,8 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
   // Forward recurrences use the flag of the step before each step: read the
   // K bytes from t0 - 1 (from t0 at the row start; finish_tile then shifts
   // in "no boundary" before step 0).
-  const int64_t f0 = Uses<A>::forward ? (t0 > 0 ? t0 - 1 : 0) : t0;
-  q.at_start = Uses<A>::forward && t0 == 0;
+  const int64_t f0 = Uses<A>::prev_flags ? (t0 > 0 ? t0 - 1 : 0) : t0;
+  q.at_start = Uses<A>::prev_flags && t0 == 0;
   const uint8_t *own = reinterpret_cast<const uint8_t *>(rp.r + t0);
   const uint8_t *trp = own;
   if constexpr (A == kRetrace) {
@@ -380,7 +400,7 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
   ld_flags_raw<K>(trp, q.ftr);
   ld_flags_raw<K>(rp.has_te ? rp.te + f0 : own, q.fte);
   Ld<InT>::template vec<K>(rp.r + t0, q.r);
-  if constexpr (U::values || U::q) {
+  if constexpr (U::values || U::q || U::affine) {
     float vk[K];
     Ld<InT>::template vec<K>(rp.v + t0, vk);
 #pragma unroll
@@ -451,7 +471,7 @@ __device__ __forceinline__ void finish_tile(const Args &p, const RowPtrs<InT> &r
                                             Tile<K> &x) {
   decode_flags<K>(x.ftr, x.tr);
   decode_flags<K>(x.fte, x.te);
-  if constexpr (Uses<A>::forward) {
+  if constexpr (Uses<A>::prev_flags) {
     if (x.at_start) {  // bytes t0 .. t0+K-1 were read: shift by one step
 #pragma unroll
       for (int i = K / 4 - 1; i >= 0; --i) {
@@ -482,7 +502,7 @@ __device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp,
   for (int i = 0; i < K / 4; ++i) { x.te[i] = 0; x.tr[i] = 0; }
   x.at_start = false;
   if (lim > 0) {
-    if constexpr (Uses<A>::forward) {
+    if constexpr (Uses<A>::prev_flags) {
       // The flag of the step before each step (none before t = 0).
 #pragma unroll
       for (int e = 0; e < K; ++e) {
@@ -504,12 +524,12 @@ __device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp,
 #pragma unroll
       for (int e = 0; e <= K; ++e) x.v[e] = e <= lim ? Ld<InT>::one(rp.v + t0 + e) : 0.f;
     }
-    if constexpr (U::q) {
+    if constexpr (U::q || U::affine) {
       float qk[K];
       ld_part<InT, K>(rp.v + t0, lim, qk);
 #pragma unroll
       for (int j = 0; j < K; ++j) x.v[j] = qk[j];
-      ld_part<InT, K>(rp.eq + t0, lim, x.eq);
+      if constexpr (U::q) ld_part<InT, K>(rp.eq + t0, lim, x.eq);
     }
     if constexpr (U::log_rho) {
 #pragma unroll
@@ -521,7 +541,7 @@ __device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp,
 
 // (alpha_t, beta_t) per step (Method 1 coefficients, Method 3 masks).  Steps
 // outside the row get the identity map (0, 1).
-template <int A, typename InT, int K, bool kEdge>
+template <int A, typename InT, int K, bool kEdge, bool kChunk>
 __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, const Args &p,
                                              float (&al)[K], float (&be)[K], float (&ratio)[K]) {
   const float gamma = late(p.gamma);
@@ -549,6 +569,10 @@ __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, cons
       const float nv = te ? 0.f : (tr ? tv_at<InT, K>(x, j) : x.v[j + 1]);
       a_j = fminf(rho_bar, e) * (fmaf(gamma, nv, x.r[j]) - x.v[j]);
       b_j = done ? 0.f : gamma * (lam * fminf(c_bar, e));
+    } else if constexpr (Uses<A>::affine) {
+      // te: reset flag of step t itself.
+      a_j = x.r[j];
+      b_j = te ? 0.f : x.v[j];
     } else if constexpr (Uses<A>::forward) {
       // te, tr: flags of step t-1; a boundary there restarts at step t.
       a_j = x.r[j];
@@ -557,7 +581,13 @@ __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, cons
       a_j = (te ? x.r[j] : fmaf(gamma, x.eq[j], x.r[j])) - x.v[j];
       const bool has_next = j + 1 < lim;  // step t+1 lies inside the row
       const float c_next = lam * fminf(c_bar, __expf(x.lr[j + 1]));
-      b_j = (done || !has_next) ? 0.f : gamma * c_next;
+      if constexpr (kChunk) {
+        // Window: the carry is c_T * (Qret_T - Q_T) of the step after the
+        // window, so the last step's factor is gamma alone.
+        b_j = done ? 0.f : gamma * (has_next ? c_next : 1.f);
+      } else {
+        b_j = (done || !has_next) ? 0.f : gamma * c_next;
+      }
     }
     const bool valid = !kEdge || j < lim;
     al[j] = valid ? a_j : 0.f;
@@ -565,18 +595,74 @@ __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, cons
   }
 }
 
+// The row's carry map (a, b), carry = a + b * (carry entering the window),
+// kept beside the scalar carry by the window instances.
+struct CarryMap {
+  float a, b;
+};
+
+// Window instances: what the outgoing carry needs besides the scan, read
+// with the carry entering the window once the row's first tile of loads is
+// in flight (so that no wait for the argument block or for these loads comes
+// before them): Retrace's log_rho_0 and the forward mirrors' flags of step
+// T-1.
+struct WindowIn {
+  float lr0;
+  bool done_last;
+};
+
+template <int A, typename InT>
+__device__ __forceinline__ WindowIn window_in(const Args &p, const RowPtrs<InT> &rp, int64_t T,
+                                              float &carry) {
+  WindowIn w{0.f, false};
+  const int64_t row = late_v(rp.row);
+  if (p.cin != nullptr) carry = p.cin[row];
+  if constexpr (A == kRetrace) w.lr0 = Ld<InT>::one(rp.lr);
+  if constexpr (Uses<A>::prev_flags)
+    w.done_last = (rp.has_te && rp.te[T - 1] != 0) || (rp.has_tr && rp.tr[T - 1] != 0);
+  return w;
+}
+
+// The window instances' per-row results, written after the row's last tile
+// by the group's last lane in scan order: the carry the neighbouring window
+// takes and the map from this window's incoming carry to it.  Reverse
+// recurrences hand on A_0 (Retrace: c_0 * A_0, the trace factor of step 0
+// applied); forward mirrors hand on A_{T-1}, or nothing when an episode ends
+// after step T-1; the generic scan hands on its last state unchanged.
+template <int A, typename InT>
+__device__ __forceinline__ void window_out(const Args &p, const RowPtrs<InT> &rp,
+                                           const WindowIn &w, bool write, float carry,
+                                           CarryMap m) {
+  if (!write) return;
+  float f = 1.f;
+  if constexpr (A == kRetrace) f = p.lam * fminf(p.c_bar, __expf(w.lr0));
+  if constexpr (Uses<A>::prev_flags) f = w.done_last ? 0.f : 1.f;
+  if (p.cout != nullptr) p.cout[rp.row] = f * carry;
+  if (p.cmap != nullptr) {
+    p.cmap[2 * rp.row] = f * m.a;
+    p.cmap[2 * rp.row + 1] = f * m.b;
+  }
+}
+
 // One tile of one row group, inputs already loaded: build pairs, fold, scan,
-// carry, re-run, store.  Returns the carry for the next (earlier) tile.
-template <int A, typename InT, int K, int LPR, int WPR, bool kEdge>
+// carry, re-run, store.  Returns the carry for the next tile in scan order
+// (in every lane when need_carry; need_carry is false for the row's last
+// tile).  Window instances also fold the tile's composite into m in the
+// group's last lane in scan order, whose inclusive scan is that composite,
+// and after the row's last tile that lane writes the window results
+// (window_out) before the tile's outputs are stored.
+template <int A, typename InT, int K, int LPR, int WPR, bool kEdge, bool kChunk>
 __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> &rp,
                                               const Tile<K> &x, int64_t t0, int64_t lim,
                                               bool row_ok, int64_t c, bool need_carry, int lane,
-                                              int wave, float carry, float2 (*s_agg)[WPR]) {
+                                              int wave, float carry, float2 (*s_agg)[WPR],
+                                              CarryMap &m, const WindowIn &win,
+                                              bool write_window) {
   constexpr int kScanLanes = WPR > 1 ? 64 : LPR;
   using U = Uses<A>;
 
   float al[K], be[K], ratio[K];
-  coefficients<A, InT, K, kEdge>(x, lim, p, al, be, ratio);
+  coefficients<A, InT, K, kEdge, kChunk>(x, lim, p, al, be, ratio);
 
   // Fold the lane's steps into one map of the incoming value: reverse,
   // (a, b) = f_{t0} o ... o f_{t0+K-1}; forward, f_{t0+K-1} o ... o f_{t0}.
@@ -612,13 +698,23 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
     // Wavefront 0 holds the first span of the tile in scan order (reverse:
     // the latest steps; forward: the earliest): compose from it onward.
     float xc = carry;
+    CarryMap tm{0.f, 1.f};  // the tile's composite
 #pragma unroll
     for (int w = 0; w < WPR; ++w) {
       if (w == wave) cin = xc;
       const float2 ag = s_agg[buf][w];
       xc = fmaf(ag.y, xc, ag.x);
+      if constexpr (kChunk) {
+        tm.a = fmaf(ag.y, tm.a, ag.x);
+        tm.b = ag.y * tm.b;
+      }
     }
     carry_out = xc;
+    if constexpr (kChunk) {
+      m.a = fmaf(tm.b, m.a, tm.a);
+      m.b = tm.b * m.b;
+      if (!need_carry) window_out<A, InT>(p, rp, win, write_window, xc, m);
+    }
   }
   // A at the far end of this lane's span (reverse: its earliest step;
   // forward: its latest) ...
@@ -632,6 +728,12 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
     if (need_carry) {
       if constexpr (LPR == 64) carry_out = readlane(y, 63);
       else carry_out = lane_shuffle(y, (lane / LPR) * LPR + LPR - 1);
+    }
+    if constexpr (kChunk) {
+      // Meaningful in the group's last lane only (see above).
+      m.a = fmaf(b, m.a, a);
+      m.b = b * m.b;
+      if (!need_carry) window_out<A, InT>(p, rp, win, write_window, y, m);
     }
   }
 
@@ -654,7 +756,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
     const float xn = xa;  // A_{t+1}
     xa = fmaf(be[j], xa, al[j]);
     o1[j] = 0.f;
-    if constexpr (A == kReturns) {
+    if constexpr (A == kReturns || A == kAffine) {
       o0[j] = xa;
     } else if constexpr (A == kGae) {
       o0[j] = xa;
@@ -707,8 +809,9 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 // wavefront (WPR == 1), or WPR wavefronts per row (then LPR must be 64).
 // Workgroup: 256 threads (WPR == 1) or 64*WPR threads (WPR > 1).
 // h0..h4, N32, T32, ldT, ldX: the preloaded hot arguments (see above); they
-// duplicate fields of p.
-template <int A, typename InT, int K, int LPR, int WPR, bool kUniform>
+// duplicate fields of p.  kChunk: window instance (carry vector in, carry and
+// carry map out).
+template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk>
 __global__ void __launch_bounds__(WPR > 1 ? 64 * WPR : 256)
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
             int N32, int T32, int ldT, int ldX, const Args p) {
@@ -772,6 +875,13 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     rp.has_te = h3 != nullptr;
     rp.has_tr = h4 != nullptr;
     rp.dense_tv = false;
+  } else if constexpr (Uses<A>::affine) {
+    rp.v = in_row(h1, ld(p.ld_v));
+    rp.te = flag_row(h2, ld(p.ld_term));
+    rp.tr = nullptr;
+    rp.has_te = h2 != nullptr;
+    rp.has_tr = false;
+    rp.dense_tv = false;
   } else if constexpr (Uses<A>::forward) {
     rp.te = flag_row(h1, ld(p.ld_term));
     rp.tr = flag_row(h2, ld(p.ld_trunc));
@@ -792,11 +902,16 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
   // The value entering the current tile: A_T before the last tile (reverse),
   // A_{-1} before the first (forward).
   float carry = 0.f;
-  if constexpr (A == kReturns) {
+  if constexpr (kChunk) {
+    // read by window_in after the first loads are issued
+  } else if constexpr (A == kReturns) {
     if (h4 != nullptr) carry = Ld<InT>::one(static_cast<const InT *>(h4) + rr);
   } else if constexpr (Uses<A>::forward) {
     if (h3 != nullptr) carry = Ld<InT>::one(static_cast<const InT *>(h3) + rr);
   }
+  CarryMap m{0.f, 1.f};
+  WindowIn win{0.f, false};
+  const bool write_window = row_ok && g == kGroup - 1;
 
   // Tiles are visited from the last (latest in time) to the first.  A ragged
   // last tile takes the element-wise path; every whole tile's loads are
@@ -812,9 +927,11 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     // One whole tile: straight-line code.
     Tile<K> x;
     issue_tile<A, InT, K>(p, rp, lane_off, T - lane_off, x);
+    if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
     finish_tile<A, InT, K>(p, rp, lane_off, x);
-    tile_compute<A, InT, K, LPR, WPR, false>(p, rp, x, lane_off, T - lane_off, row_ok, 0, false,
-                                             lane, wave, carry, s_agg);
+    tile_compute<A, InT, K, LPR, WPR, false, kChunk>(p, rp, x, lane_off, T - lane_off, row_ok, 0,
+                                                     false, lane, wave, carry, s_agg, m, win,
+                                                     write_window);
     return;
   }
   const bool ragged = T % kTile != 0;
@@ -826,23 +943,24 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     int64_t c = 0;
     if (nwhole > 0) {
       issue_tile<A, InT, K>(p, rp, t0_of(0), T - t0_of(0), buf_a);
+      if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
       for (;;) {
         {
           finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
           const int64_t cn = c + 1 < nwhole ? c + 1 : c;
           issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
-          carry = tile_compute<A, InT, K, LPR, WPR, false>(p, rp, buf_a, t0_of(c), T - t0_of(c),
-                                                           row_ok, c, c + 1 < ntiles, lane, wave,
-                                                           carry, s_agg);
+          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+              p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
+              s_agg, m, win, write_window);
         }
         if (++c == nwhole) break;
         {
           finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
           const int64_t cn = c + 1 < nwhole ? c + 1 : c;
           issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
-          carry = tile_compute<A, InT, K, LPR, WPR, false>(p, rp, buf_b, t0_of(c), T - t0_of(c),
-                                                           row_ok, c, c + 1 < ntiles, lane, wave,
-                                                           carry, s_agg);
+          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+              p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
+              s_agg, m, win, write_window);
         }
         if (++c == nwhole) break;
       }
@@ -852,8 +970,12 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
       const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
       Tile<K> x;
       load_edge<A, InT, K>(p, rp, te0, lim, x);
-      tile_compute<A, InT, K, LPR, WPR, true>(p, rp, x, te0, lim, row_ok, ntiles - 1, false, lane,
-                                              wave, carry, s_agg);
+      if constexpr (kChunk) {
+        if (nwhole == 0) win = window_in<A, InT>(p, rp, T, carry);
+      }
+      tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok, ntiles - 1,
+                                                      false, lane, wave, carry, s_agg, m, win,
+                                                      write_window);
     }
     return;
   }
@@ -872,8 +994,12 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
     Tile<K> x;
     load_edge<A, InT, K>(p, rp, te0, lim, x);
-    carry = tile_compute<A, InT, K, LPR, WPR, true>(p, rp, x, te0, lim, row_ok, ntiles - 1, c >= 0,
-                                                    lane, wave, carry, s_agg);
+    if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
+    carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok,
+                                                            ntiles - 1, c >= 0, lane, wave, carry,
+                                                            s_agg, m, win, write_window);
+  } else {
+    if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
   }
   if (c < 0) return;
   for (;;) {
@@ -881,8 +1007,9 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
       finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
       const int64_t cn = c > 0 ? c - 1 : 0;
       issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
-      carry = tile_compute<A, InT, K, LPR, WPR, false>(p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok,
-                                                       c, c > 0, lane, wave, carry, s_agg);
+      carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+          p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
+          win, write_window);
     }
     if (c == 0) break;
     --c;
@@ -890,8 +1017,9 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
       finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
       const int64_t cn = c > 0 ? c - 1 : 0;
       issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
-      carry = tile_compute<A, InT, K, LPR, WPR, false>(p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok,
-                                                       c, c > 0, lane, wave, carry, s_agg);
+      carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+          p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
+          win, write_window);
     }
     if (c == 0) break;
     --c;

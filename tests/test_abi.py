@@ -184,3 +184,57 @@ def test_binding_refuses_cpu_tensors():
         rl.rlca_gae(r, v, gamma=0.9, lam=0.9)
     with pytest.raises(ValueError, match="2-D"):
         rl.rlca_returns(torch.zeros(4), gamma=0.9)
+
+
+# Window entry points: the carry vectors are validated like every array.
+C_IN, C_OUT, C_MAP = (BASE + (8 + i) * 0x1000000 for i in range(3))
+
+
+def gae_chunk(lib, N=4, T=8, cin=C_IN, cout=C_OUT, cmap=C_MAP, adv=ADV, r=R):
+    return lib.rlca_gae_chunk(N, T, F32, r, T, V, T + 1, TE, T, TR, T, TV, T, 0.9, 0.9,
+                              adv, T, TGT, T, cin, cout, cmap, None)
+
+
+def test_window_entry_points_validate_carry_vectors(lib):
+    assert gae_chunk(lib, N=0) == rl.RLCA_OK
+    assert gae_chunk(lib, cin=C_IN + 2) == rl.RLCA_EINVAL and "carry_in" in err(lib)
+    assert gae_chunk(lib, cout=C_OUT + 1) == rl.RLCA_EINVAL and "carry_out" in err(lib)
+    # carry_out overlapping carry_in (no in-place update), carry_map
+    # overlapping carry_out, a carry output overlapping an input array.
+    assert gae_chunk(lib, cout=C_IN + 4) == rl.RLCA_EALIAS and "carry_in" in err(lib)
+    assert gae_chunk(lib, cout=C_IN) == rl.RLCA_EALIAS
+    assert gae_chunk(lib, cmap=C_OUT + 12) == rl.RLCA_EALIAS and "carry_map" in err(lib)
+    assert gae_chunk(lib, cmap=R + 8) == rl.RLCA_EALIAS and "rewards" in err(lib)
+    # The map holds 2 floats per row: one float past the carry vector's end
+    # is still an overlap for the map, not for the carry.
+    assert gae_chunk(lib, cmap=C_OUT - 2 * 4 * 4 + 4) == rl.RLCA_EALIAS
+    ret = lambda **k: lib.rlca_returns_chunk(4, 8, F32, R, 8, None, 8, None, 8, None, 8,
+                                              k.get("cin", C_IN), k.get("gamma", 0.9), ADV, 8,
+                                              k.get("cout", C_OUT), None, None)
+    assert ret(gamma=1.5) == rl.RLCA_EINVAL
+    assert ret(cout=ADV + 4) == rl.RLCA_EALIAS
+    el = lambda **k: lib.rlca_eligibility_trace_chunk(4, 8, F32, R, 8, None, 8, None, 8,
+                                                       k.get("cin", C_IN), 0.9, k.get("lam", 0.9),
+                                                       ADV, 8, C_OUT, C_MAP, None)
+    assert el(lam=2.0) == rl.RLCA_EINVAL and "lam" in err(lib)
+    assert el(cin=ADV) == rl.RLCA_EALIAS
+
+
+def test_affine_scan_validates(lib):
+    aff = lambda **k: lib.rlca_affine_scan(k.get("N", 4), 8, k.get("dtype", F32), k.get("a", R),
+                                           8, k.get("b", V), 8, k.get("rs", None), 8,
+                                           k.get("rev", 1), None, k.get("out", ADV), 8, None,
+                                           None, None)
+    assert aff(N=0) == rl.RLCA_OK
+    assert aff(rev=2) == rl.RLCA_EINVAL and "reverse" in err(lib)
+    assert aff(b=None) == rl.RLCA_EINVAL and "beta" in err(lib)
+    assert aff(a=None) == rl.RLCA_EINVAL and "alpha" in err(lib)
+    assert aff(out=None) == rl.RLCA_EINVAL and "out" in err(lib)
+    assert aff(dtype=5) == rl.RLCA_EDTYPE
+    assert aff(out=V + 4) == rl.RLCA_EALIAS and "beta" in err(lib)
+    assert aff(rs=ADV + 3) == rl.RLCA_EALIAS and "reset" in err(lib)
+
+
+def test_binding_refuses_bad_carry_vectors():
+    with pytest.raises(ValueError, match="GPU"):
+        rl.rlca_affine_scan(torch.zeros(2, 4), torch.zeros(2, 4))
