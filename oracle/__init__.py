@@ -54,9 +54,15 @@ def _load():
         lib.oracle_episodic_cumsum.argtypes = [i64, i64, _D, _U8, _U8, _D, _D, _D, _D]
         lib.oracle_affine_scan.argtypes = [i64, i64, _D, _D, _U8, ctypes.c_int, _D,
                                            _D, _D, _D]
+        _I32 = ctypes.POINTER(ctypes.c_int32)
+        lib.oracle_retrace_probs.argtypes = [i64, i64, i64, _D, _D, _I32, _D, _D, _U8, _U8, _D,
+                                             dbl, dbl, dbl, _D, _D, _D, _D]
+        lib.oracle_vtrace_probs.argtypes = [i64, i64, i64, _D, _D, _I32, _D, _D, _U8, _U8, _D,
+                                            dbl, dbl, dbl, dbl, dbl, _D, _D, _D, _D, _D]
         for f in (lib.oracle_returns, lib.oracle_gae, lib.oracle_td_lambda,
                   lib.oracle_vtrace, lib.oracle_retrace, lib.oracle_eligibility_trace,
-                  lib.oracle_episodic_cumsum, lib.oracle_affine_scan):
+                  lib.oracle_episodic_cumsum, lib.oracle_affine_scan,
+                  lib.oracle_retrace_probs, lib.oracle_vtrace_probs):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -262,3 +268,63 @@ def affine_scan(alpha, beta, reset=None, carry_in=None, *, reverse=True):
     _check(_load().oracle_affine_scan(N, T, ap, bp, rsp, 1 if reverse else 0, cip,
                                       out.ctypes.data_as(_D), c.out_p, c.map_p), "affine_scan")
     return out, c.out, c.map
+
+
+def _i32(x, shape):
+    a = np.ascontiguousarray(_as_numpy(x)).astype(np.int32, copy=False)
+    if a.shape != shape:
+        raise ValueError("expected shape %s, got %s" % (shape, a.shape))
+    return a, a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def retrace_probs(rewards, q_values, actions, log_pi, log_mu, terminated=None, truncated=None,
+                  trunc_eq=None, *, gamma, lam, c_bar=1.0, carry_in=None, chunk=False):
+    """Retrace(lambda) from tables: q_values and log_pi ``[N, T+1, A]``,
+    log_mu ``[N, T, A]``, actions ``[N, T]``; trunc_eq ``[N, T]`` is
+    E_pi Q at the true final state of truncated steps.  Returns ``Q^ret``
+    (chunk=True: also carry_out and carry_map)."""
+    r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
+    N, T = r.shape
+    A = np.shape(_as_numpy(q_values))[2]
+    q, qp = _f64(q_values, (N, T + 1, A))
+    ac, acp = _i32(actions, (N, T))
+    lp, lpp = _f64(log_pi, (N, T + 1, A))
+    lm, lmp = _f64(log_mu, (N, T, A))
+    te, tep = _u8(terminated, (N, T))
+    tr, trp = _u8(truncated, (N, T))
+    te2, te2p = _f64(trunc_eq, (N, T))
+    ci, cip = _f64(carry_in, (N,))
+    out = np.empty((N, T), np.float64)
+    c = _Carry(N)
+    _check(_load().oracle_retrace_probs(N, T, A, rp, qp, acp, lpp, lmp, tep, trp, te2p,
+                                        float(gamma), float(lam), float(c_bar),
+                                        out.ctypes.data_as(_D), cip, c.out_p, c.map_p),
+           "retrace_probs")
+    return (out, c.out, c.map) if chunk else out
+
+
+def vtrace_probs(rewards, values, actions, log_pi, log_mu, terminated=None, truncated=None,
+                 trunc_values=None, *, gamma, lam, rho_bar=1.0, c_bar=1.0, pg_rho_bar=1.0,
+                 carry_in=None, chunk=False):
+    """V-trace from tables: log_pi and log_mu ``[N, T, A]``, actions ``[N, T]``.
+    Returns ``(vs, pg_advantages)`` (chunk=True: also carry_out, carry_map)."""
+    r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
+    N, T = r.shape
+    A = np.shape(_as_numpy(log_pi))[2]
+    v, vp = _f64(values, (N, T + 1))
+    ac, acp = _i32(actions, (N, T))
+    lp, lpp = _f64(log_pi, (N, T, A))
+    lm, lmp = _f64(log_mu, (N, T, A))
+    te, tep = _u8(terminated, (N, T))
+    tr, trp = _u8(truncated, (N, T))
+    tv, tvp = _f64(trunc_values, (N, T))
+    ci, cip = _f64(carry_in, (N,))
+    vs = np.empty((N, T), np.float64)
+    pg = np.empty((N, T), np.float64)
+    c = _Carry(N)
+    _check(_load().oracle_vtrace_probs(N, T, A, rp, vp, acp, lpp, lmp, tep, trp, tvp,
+                                       float(gamma), float(lam), float(rho_bar), float(c_bar),
+                                       float(pg_rho_bar), vs.ctypes.data_as(_D),
+                                       pg.ctypes.data_as(_D), cip, c.out_p, c.map_p),
+           "vtrace_probs")
+    return (vs, pg, c.out, c.map) if chunk else (vs, pg)

@@ -60,6 +60,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #define AT(p, n, t, ld) ((p)[(size_t)(n) * (size_t)(ld) + (size_t)(t)])
 
@@ -437,4 +438,108 @@ int oracle_affine_scan(int64_t N, int64_t T, const double *alpha, const double *
         put_carry(carry_out, map_out, n, a, a0, da);
     }
     return 0;
+}
+
+/*
+ * Retrace(lambda) and V-trace from the policies' log-probability tables
+ * (rl-triton, Results: the heavier Retrace workload loads the action
+ * probabilities at every step).  Per row, with A actions and a_t the action
+ * taken at step t (0 <= a_t < A):
+ *   log_rho_t = log_pi[t][a_t] - log_mu[t][a_t]      target over behaviour
+ * Retrace also reads action values and the target policy one step ahead:
+ *   q       [N, T+1, A]   Q(s_t, a); slice T is the state after the window
+ *   log_pi  [N, T+1, A]   log pi(a | s_t); slice T likewise
+ *   q_taken_t = q[t][a_t]
+ *   EQ_t      = sum over a of exp(log_pi[t+1][a]) * q[t+1][a]   (E_pi Q(s_{t+1}, .))
+ *   except after a truncation that is not a termination, where s_{t+1} in the
+ *   tables is the next episode's first state: EQ_t = trunc_eq[t], the same
+ *   expectation at the true final state, supplied by the caller.
+ * V-trace reads log_pi [N, T, A] (no slice T).  log_mu is [N, T, A] for both.
+ * With these [N, T] quantities the result is that of oracle_retrace /
+ * oracle_vtrace above (window carries passed through).  An action outside
+ * [0, A) is rejected (-1).
+ */
+static int derive_probs(int64_t N, int64_t T, int64_t A, int pi_slices, const int32_t *actions,
+                        const double *log_pi, const double *log_mu, double *log_rho)
+{
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t t = 0; t < T; ++t) {
+            int32_t a = actions[n * T + t];
+            if (a < 0 || a >= A)
+                return -1;
+            double lp = log_pi[((size_t)n * (size_t)(T + pi_slices) + (size_t)t) * (size_t)A + (size_t)a];
+            double lm = log_mu[((size_t)n * (size_t)T + (size_t)t) * (size_t)A + (size_t)a];
+            log_rho[n * T + t] = lp - lm;
+        }
+    return 0;
+}
+
+int oracle_retrace_probs(int64_t N, int64_t T, int64_t A, const double *r, const double *q,
+                         const int32_t *actions, const double *log_pi, const double *log_mu,
+                         const uint8_t *term, const uint8_t *trunc, const double *trunc_eq,
+                         double gamma, double lam, double c_bar, double *qret,
+                         const double *carry_in, double *carry_out, double *map_out)
+{
+    if (N < 0 || T < 0 || A < 1 || (trunc != NULL && trunc_eq == NULL))
+        return -1;
+    if (N == 0 || T == 0)
+        return oracle_retrace(N, T, r, NULL, NULL, NULL, term, trunc, gamma, lam, c_bar, qret,
+                              carry_in, carry_out, map_out);
+    if (r == NULL || q == NULL || actions == NULL || log_pi == NULL || log_mu == NULL ||
+        qret == NULL)
+        return -1;
+    size_t nt = (size_t)N * (size_t)T;
+    double *q_taken = malloc(nt * sizeof(double));
+    double *eq = malloc(nt * sizeof(double));
+    double *log_rho = malloc(nt * sizeof(double));
+    int rc = -1;
+    if (q_taken == NULL || eq == NULL || log_rho == NULL)
+        goto out;
+    if (derive_probs(N, T, A, 1, actions, log_pi, log_mu, log_rho) != 0)
+        goto out;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t t = 0; t < T; ++t) {
+            size_t here = ((size_t)n * (size_t)(T + 1) + (size_t)t) * (size_t)A;
+            size_t next = here + (size_t)A;
+            q_taken[n * T + t] = q[here + (size_t)actions[n * T + t]];
+            if (flag_at(trunc, n, t, T) && !flag_at(term, n, t, T)) {
+                eq[n * T + t] = AT(trunc_eq, n, t, T);
+            } else {
+                double e = 0.0;
+                for (int64_t b = 0; b < A; ++b)
+                    e += exp(log_pi[next + (size_t)b]) * q[next + (size_t)b];
+                eq[n * T + t] = e;
+            }
+        }
+    rc = oracle_retrace(N, T, r, q_taken, eq, log_rho, term, trunc, gamma, lam, c_bar, qret,
+                        carry_in, carry_out, map_out);
+out:
+    free(q_taken);
+    free(eq);
+    free(log_rho);
+    return rc;
+}
+
+int oracle_vtrace_probs(int64_t N, int64_t T, int64_t A, const double *r, const double *v,
+                        const int32_t *actions, const double *log_pi, const double *log_mu,
+                        const uint8_t *term, const uint8_t *trunc, const double *tv,
+                        double gamma, double lam, double rho_bar, double c_bar,
+                        double pg_rho_bar, double *vs, double *pg, const double *carry_in,
+                        double *carry_out, double *map_out)
+{
+    if (N < 0 || T < 0 || A < 1 || (trunc != NULL && tv == NULL))
+        return -1;
+    if (N == 0 || T == 0)
+        return oracle_vtrace(N, T, r, v, NULL, term, trunc, tv, gamma, lam, rho_bar, c_bar,
+                             pg_rho_bar, vs, pg, carry_in, carry_out, map_out);
+    if (r == NULL || v == NULL || actions == NULL || log_pi == NULL || log_mu == NULL ||
+        vs == NULL)
+        return -1;
+    double *log_rho = malloc((size_t)N * (size_t)T * sizeof(double));
+    int rc = -1;
+    if (log_rho != NULL && derive_probs(N, T, A, 0, actions, log_pi, log_mu, log_rho) == 0)
+        rc = oracle_vtrace(N, T, r, v, log_rho, term, trunc, tv, gamma, lam, rho_bar, c_bar,
+                           pg_rho_bar, vs, pg, carry_in, carry_out, map_out);
+    free(log_rho);
+    return rc;
 }

@@ -89,6 +89,22 @@ MUTANTS = [
     ("affine_direction_swapped", "int64_t t = reverse ? T - 1 - i : i;",
      "int64_t t = reverse ? i : T - 1 - i;"),
     ("affine_map_from_carry", "a0 = AT(alpha, n, t, T) + b * a0;", "a0 = AT(alpha, n, t, T) + b * a;"),
+    # Retrace and V-trace from policy tables
+    ("probs_expectation_from_current_state", "size_t next = here + (size_t)A;",
+     "size_t next = here;"),
+    ("probs_q_taken_from_next_state", "q_taken[n * T + t] = q[here + (size_t)actions[n * T + t]];",
+     "q_taken[n * T + t] = q[next + (size_t)actions[n * T + t]];"),
+    ("probs_ratio_inverted", "log_rho[n * T + t] = lp - lm;", "log_rho[n * T + t] = lm - lp;"),
+    ("probs_log_prob_used_as_prob", "e += exp(log_pi[next + (size_t)b]) * q[next + (size_t)b];",
+     "e += log_pi[next + (size_t)b] * q[next + (size_t)b];"),
+    ("probs_truncation_uses_table",
+     "if (flag_at(trunc, n, t, T) && !flag_at(term, n, t, T)) {\n                eq[n * T + t]",
+     "if (0) {\n                eq[n * T + t]"),
+    ("probs_behaviour_from_next_step",
+     "double lm = log_mu[((size_t)n * (size_t)T + (size_t)t) * (size_t)A + (size_t)a];",
+     "double lm = log_mu[((size_t)n * (size_t)T + (size_t)(t + 1 < T ? t + 1 : t)) * (size_t)A + (size_t)a];"),
+    ("vtrace_probs_table_stride", "derive_probs(N, T, A, 0, actions, log_pi, log_mu, log_rho) == 0",
+     "derive_probs(N, T, A, 1, actions, log_pi, log_mu, log_rho) == 0"),
 ]
 
 PIN_CASES = [
@@ -123,6 +139,11 @@ PIN_CASES = [
     (pins.test_affine_scan_matches_sum_form, dict(reverse=True, seed=100, T=6)),
     (pins.test_affine_scan_matches_sum_form, dict(reverse=False, seed=100, T=6)),
     (pins.test_affine_scan_exact_in_rationals, {}),
+    (pins.test_retrace_probs_is_retrace_of_the_table_quantities, dict(seed=113, A=18)),
+    (pins.test_vtrace_probs_is_vtrace_of_the_table_ratio, dict(seed=115, A=6)),
+    (pins.test_retrace_probs_single_action_and_greedy_target, {}),
+    (pins.test_probs_action_relabeling_is_invariant, {}),
+    (pins.test_probs_tables_are_read_only_where_the_definition_reads_them, {}),
 ]
 
 

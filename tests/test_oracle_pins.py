@@ -741,3 +741,133 @@ def test_affine_scan_instances_of_the_algorithms():
                                  d["B"], reverse=False)
     assert rel_err(Z, oracle.eligibility_trace(d["r"], d["term"], d["trunc"], d["B"], gamma=g,
                                                lam=lam)) < 1e-13
+
+
+# --------------------- Retrace and V-trace from policy tables (Results section)
+
+def _log_softmax(x):
+    m = x.max(-1, keepdims=True)
+    return x - m - np.log(np.exp(x - m).sum(-1, keepdims=True))
+
+
+def prob_tables(seed, N, T, A, p_term=0.1, p_trunc=0.1):
+    d = rand_inputs(seed, N, T, p_term=p_term, p_trunc=p_trunc)
+    g = np.random.Generator(np.random.PCG64(seed + 1000))
+    d["Q"] = g.standard_normal((N, T + 1, A))
+    d["logpi"] = _log_softmax(g.standard_normal((N, T + 1, A)))
+    d["logmu"] = _log_softmax(g.standard_normal((N, T, A)))
+    d["act"] = g.integers(0, A, (N, T)).astype(np.int32)
+    d["teq"] = g.standard_normal((N, T))
+    return d
+
+
+def _taken(table, act):
+    return np.take_along_axis(table, act[..., None].astype(np.int64), -1)[..., 0]
+
+
+PP = dict(gamma=0.95, lam=0.9, c_bar=0.9)
+
+
+def _retrace_probs(d, **kw):
+    return oracle.retrace_probs(d["r"], d["Q"], d["act"], d["logpi"], d["logmu"], d["term"],
+                                d["trunc"], d["teq"], **dict(PP, **kw))
+
+
+@pytest.mark.parametrize("seed,A", [(111, 1), (112, 4), (113, 18)])
+def test_retrace_probs_is_retrace_of_the_table_quantities(seed, A):
+    # q_taken, E_pi Q(s_{t+1}) and the log-ratio formed here with numpy from
+    # their definitions, then the (pinned) Retrace oracle.
+    N, T = 5, 21
+    d = prob_tables(seed, N, T, A)
+    T_ = d["r"].shape[1]
+    q_taken = _taken(d["Q"][:, :T_], d["act"])
+    eq = (np.exp(d["logpi"][:, 1:]) * d["Q"][:, 1:]).sum(-1)
+    trunc_only = d["trunc"].astype(bool) & ~d["term"].astype(bool)
+    eq = np.where(trunc_only, d["teq"], eq)
+    lr = _taken(d["logpi"][:, :T_], d["act"]) - _taken(d["logmu"], d["act"])
+    want = oracle.retrace(d["r"], q_taken, eq, lr, d["term"], d["trunc"], **PP)
+    assert rel_err(_retrace_probs(d), want) < 1e-13
+
+
+@pytest.mark.parametrize("seed,A", [(114, 1), (115, 6)])
+def test_vtrace_probs_is_vtrace_of_the_table_ratio(seed, A):
+    N, T = 4, 17
+    d = prob_tables(seed, N, T, A)
+    lr = _taken(d["logpi"][:, :T], d["act"]) - _taken(d["logmu"], d["act"])
+    kw = dict(gamma=0.97, lam=0.9, rho_bar=1.2, c_bar=0.8, pg_rho_bar=1.1)
+    want = oracle.vtrace(d["r"], d["v"], lr, d["term"], d["trunc"], d["tv"], **kw)
+    got = oracle.vtrace_probs(d["r"], d["v"], d["act"], d["logpi"][:, :T], d["logmu"],
+                              d["term"], d["trunc"], d["tv"], **kw)
+    for a, b in zip(got, want):
+        assert rel_err(a, b) < 1e-13
+
+
+def test_retrace_probs_single_action_and_greedy_target():
+    # One action: pi = 1, so E_pi Q(s_{t+1}) = Q(s_{t+1}, 0) and the ratio is
+    # 1 / mu.  A greedy target policy makes E_pi Q the maximum over actions.
+    N, T = 3, 12
+    d = prob_tables(116, N, T, 1, p_term=0.0, p_trunc=0.0)
+    d["logpi"][:] = 0.0
+    d["logmu"][:] = np.log(0.5)
+    lam_c = min(0.9, 2.0) * 0.9
+    want = oracle.retrace(d["r"], d["Q"][:, :T, 0], d["Q"][:, 1:, 0],
+                          np.full((N, T), np.log(2.0)), **PP)
+    assert rel_err(_retrace_probs(d), want) < 1e-13
+    d = prob_tables(117, N, T, 7, p_term=0.0, p_trunc=0.0)
+    best = d["Q"].argmax(-1)
+    with np.errstate(divide="ignore"):
+        d["logpi"] = np.where(np.arange(7) == best[..., None], 0.0, -np.inf)
+    q_taken = _taken(d["Q"][:, :T], d["act"])
+    lr = _taken(d["logpi"][:, :T], d["act"]) - _taken(d["logmu"], d["act"])
+    want = oracle.retrace(d["r"], q_taken, d["Q"][:, 1:].max(-1), lr, **PP)
+    got = _retrace_probs(d)
+    assert np.all(np.isfinite(got)) and rel_err(got, want) < 1e-13
+    assert lam_c > 0
+
+
+def test_probs_action_relabeling_is_invariant():
+    N, T, A = 4, 15, 9
+    d = prob_tables(118, N, T, A)
+    perm = np.random.Generator(np.random.PCG64(119)).permutation(A)
+    inv = np.argsort(perm)
+    e = dict(d, Q=d["Q"][..., perm], logpi=d["logpi"][..., perm], logmu=d["logmu"][..., perm],
+             act=inv[d["act"]].astype(np.int32))
+    assert rel_err(_retrace_probs(e), _retrace_probs(d)) < 1e-14
+    kw = dict(gamma=0.9, lam=0.95)
+    a = oracle.vtrace_probs(d["r"], d["v"], d["act"], d["logpi"][:, :T], d["logmu"], **kw)
+    b = oracle.vtrace_probs(e["r"], e["v"], e["act"], e["logpi"][:, :T], e["logmu"], **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_probs_tables_are_read_only_where_the_definition_reads_them():
+    N, T, A = 3, 10, 5
+    d = prob_tables(120, N, T, A, p_term=0.0, p_trunc=0.0)
+    base = _retrace_probs(d)
+    # Slice 0 enters only through the taken action (q_taken_0, log_rho_0).
+    e = {k: (v.copy() if hasattr(v, "copy") else v) for k, v in d.items()}
+    others = np.arange(A)[None, :] != d["act"][:, :1]
+    e["Q"][:, 0][others] += 7.0
+    e["logpi"][:, 0][others] -= 3.0
+    e["logmu"][others[:, None, :].repeat(T, 1) & (np.arange(T)[None, :, None] == 0)] += 1.0
+    assert np.array_equal(_retrace_probs(e), base)
+    # After a truncation at step s the expectation comes from trunc_eq, and
+    # the trace is cut: slice s+1 then reaches no output at or before s.
+    # (Without the truncation the same change moves step s.)
+    s = 4
+    noise = np.random.Generator(np.random.PCG64(122)).standard_normal((N, A))
+    e = {k: (v.copy() if hasattr(v, "copy") else v) for k, v in d.items()}
+    e["Q"][:, s + 1] += 5.0
+    e["logpi"][:, s + 1] = _log_softmax(e["logpi"][:, s + 1] + noise)
+    assert not np.array_equal(_retrace_probs(e)[:, s], _retrace_probs(d)[:, s])
+    d["trunc"][:, s] = 1
+    e["trunc"] = d["trunc"]
+    assert np.array_equal(_retrace_probs(e)[:, : s + 1], _retrace_probs(d)[:, : s + 1])
+
+
+def test_probs_reject_actions_out_of_range():
+    d = prob_tables(121, 2, 5, 3)
+    for bad in (-1, 3):
+        e = dict(d, act=d["act"].copy())
+        e["act"][1, 2] = bad
+        with pytest.raises(ValueError):
+            _retrace_probs(e)
