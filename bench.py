@@ -33,7 +33,8 @@ HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "reverse_linear_recurrence_amd", "csrc", f)
                   for f in ("scan_kernels.hpp", "kernel_table.hpp", "variants.hpp",
-                            "kernels_plain.hip", "kernels_window.hip", "rlca.hip")]
+                            "kernels_plain.hip", "kernels_window.hip", "probs_kernels.hpp",
+                            "kernels_probs.hip", "rlca.hip")]
 
 
 def kernel_source_hash():
@@ -89,6 +90,16 @@ def algorithmic_bytes(w, N, T, window=False):
     if w.algo in ("eligibility", "cumsum"):
         flags = 2 if w.p_trunc is not None else 1
         return (es + flags + 4) * N * T                # x, flags; output
+    flags = 2 if w.p_trunc is not None else 1
+    A = w.num_actions
+    if w.algo == "retrace_probs":
+        # r, action, the taken behaviour entry, flags, q_ret per step; every
+        # entry of the q and log_pi slices 1..T (E_pi Q), and the taken entries
+        # of slice 0.
+        return (es + 4 + es + flags + 4 + 2 * A * es) * N * T + 2 * es * N
+    if w.algo == "vtrace_probs":
+        # r, V, action, the two taken entries, flags, vs + pg per step; V_T.
+        return (2 * es + 4 + 2 * es + flags + 8) * N * T + es * N
     raise ValueError(w.algo)
 
 
@@ -127,9 +138,10 @@ def summarize_pmc(fetch_dir, write_dir):
     # The calibration copy: the runtime's copy kernel whose dispatches write
     # exactly the known size (input uploads use the same kernel name).
     copies = [k for k in write if "copyBuffer" in k[0] and abs(write[k] * 1024 - half) < 0.01 * half]
-    scan_name = [k for k in fetch if "scan_kernel" in k[0]]
+    scan_name = [k for k in fetch if "rlca::" in k[0]]
     if len(copies) != 1 or not scan_name:
-        raise SystemExit("expected one calibration copy and the scan kernel(s): %s" % list(write))
+        raise SystemExit("expected one calibration copy and the library's kernel(s): %s"
+                         % list(write))
     cn = copies[0]
     f_scale = half / (fetch[cn] * 1024.0)
     w_scale = half / (write[cn] * 1024.0)
@@ -240,6 +252,17 @@ def main():
         if args.window:
             window_step(d)
             return
+        if w.algo == "retrace_probs":
+            rl.rlca_retrace_probs(d["rewards"], d["q_values"], d["actions"], d["log_pi"],
+                                  d["log_mu"], d["terminated"], d.get("truncated"),
+                                  d.get("trunc_eq"), gamma=gamma, lam=lam, out=d["_o0"], **clips)
+            return
+        if w.algo == "vtrace_probs":
+            rl.rlca_vtrace_probs(d["rewards"], d["values"], d["actions"], d["log_pi"],
+                                 d["log_mu"], d["terminated"], d.get("truncated"),
+                                 d.get("trunc_values"), gamma=gamma, lam=lam, vs=d["_o0"],
+                                 pg_advantages=d["_o1"], **clips)
+            return
         if w.algo == "gae":
             rl.rlca_gae(d["rewards"], d["values"], d["terminated"], d.get("truncated"),
                         d.get("trunc_values"), gamma=gamma, lam=lam, advantages=d["_o0"],
@@ -271,7 +294,22 @@ def main():
     win = dict(carry_in=carry_in, chunk=True) if args.window else {}
     if args.window and w.algo in ("returns",):
         win = dict(chunk=True)
-    if w.algo == "gae":
+    if w.algo in ("retrace_probs", "vtrace_probs") and args.window:
+        print("the policy-table calls have no window form", file=sys.stderr)
+        sys.exit(2)
+    if w.algo == "retrace_probs":
+        ref = oracle.retrace_probs(host["rewards"], host["q_values"], host["actions"],
+                                   host["log_pi"], host["log_mu"], host["terminated"],
+                                   host.get("truncated"), host.get("trunc_eq"), gamma=gamma,
+                                   lam=lam, **clips)
+        outs = (sets[0]["_o0"],)
+    elif w.algo == "vtrace_probs":
+        ref = oracle.vtrace_probs(host["rewards"], host["values"], host["actions"],
+                                  host["log_pi"], host["log_mu"], host["terminated"],
+                                  host.get("truncated"), host.get("trunc_values"), gamma=gamma,
+                                  lam=lam, **clips)
+        outs = (sets[0]["_o0"], sets[0]["_o1"])
+    elif w.algo == "gae":
         ref = oracle.gae(host["rewards"], host["values"], host["terminated"],
                          host.get("truncated"), host.get("trunc_values"), gamma=gamma, lam=lam,
                          **win)
@@ -422,7 +460,16 @@ def main():
                for k, v in host.items()}
 
         def oracle_step():
-            if w.algo == "gae":
+            if w.algo == "retrace_probs":
+                oracle.retrace_probs(h64["rewards"], h64["q_values"], h64["actions"],
+                                     h64["log_pi"], h64["log_mu"], h64["terminated"],
+                                     h64.get("truncated"), h64.get("trunc_eq"), gamma=gamma,
+                                     lam=lam, **clips)
+            elif w.algo == "vtrace_probs":
+                oracle.vtrace_probs(h64["rewards"], h64["values"], h64["actions"], h64["log_pi"],
+                                    h64["log_mu"], h64["terminated"], h64.get("truncated"),
+                                    h64.get("trunc_values"), gamma=gamma, lam=lam, **clips)
+            elif w.algo == "gae":
                 oracle.gae(h64["rewards"], h64["values"], h64["terminated"],
                            h64.get("truncated"), h64.get("trunc_values"), gamma=gamma, lam=lam)
             elif w.algo == "td_lambda":

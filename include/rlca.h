@@ -374,6 +374,66 @@ int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype,
                      float *carry_out, float *carry_map,
                      void *stream);
 
+/*
+ * Retrace(lambda) and V-trace from the policies' log-probability tables
+ * (Results: the heavier Retrace workload loads the action probabilities at
+ * every step).  With A = num_actions and a_t = actions[t] (int32, the action
+ * taken at step t):
+ *   log_rho_t = log_pi[t][a_t] - log_mu[t][a_t]
+ * replaces the log_rhos input of rlca_retrace / rlca_vtrace, and Retrace
+ * forms its other per-step inputs on chip:
+ *   q_taken_t  = q_values[t][a_t]
+ *   exp_q_next_t = sum over a of exp(log_pi[t+1][a]) * q_values[t+1][a]
+ *                  (E_pi Q(s_{t+1}, .)), except after a truncation that is not
+ *                  a termination, where the tables' slice t+1 is the next
+ *                  episode's first state: trunc_eq[t] (E_pi Q at the true final
+ *                  state, supplied; read only there).
+ * Everything else is as for rlca_retrace / rlca_vtrace (same outputs, same
+ * boundary rules, same tolerances).
+ * Layout.  A table is row-major [num_envs, S, A] with S slices per row, A
+ *   entries per slice contiguous; ld_* is the distance between rows in
+ *   elements (>= S * A).  Retrace: q_values and log_pi have S = T + 1 (slice
+ *   T is the state after the window), log_mu S = T.  V-trace: log_pi and
+ *   log_mu have S = T.  actions is [num_envs, T] int32.  log_mu_taken = 1:
+ *   log_mu is instead [num_envs, T] (row stride ld_log_mu >= T) holding
+ *   log mu(a_t | s_t) of the taken actions only, the form replay buffers
+ *   usually keep; the full table costs a whole read of it.  0 or 1, else
+ *   RLCA_EINVAL.
+ * Errors.  As for the other entry points; also num_actions outside
+ *   [1, 65536] -> RLCA_EINVAL, and (Retrace) truncated != NULL with
+ *   trunc_eq == NULL -> RLCA_EINVAL.  An action outside [0, A) is not
+ *   detected before launch and reads no memory outside the tables: its step
+ *   and every earlier step of its row come out NaN (the scan cuts episodes
+ *   by a zero factor, which does not stop a NaN), later steps are unaffected.
+ * Each row is processed by one 256-thread workgroup, 1024 steps per tile;
+ * the tiling controls do not apply (rlca_last_variant() reports -1).
+ */
+int rlca_retrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                       const void *rewards, int64_t ld_rewards,
+                       const void *q_values, int64_t ld_q_values,
+                       const int32_t *actions, int64_t ld_actions,
+                       const void *log_pi, int64_t ld_log_pi,
+                       const void *log_mu, int64_t ld_log_mu, int log_mu_taken,
+                       const uint8_t *terminated, int64_t ld_terminated,
+                       const uint8_t *truncated, int64_t ld_truncated,
+                       const void *trunc_eq, int64_t ld_trunc_eq,
+                       float gamma, float lam, float c_bar,
+                       float *q_ret, int64_t ld_q_ret,
+                       void *stream);
+int rlca_vtrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                      const void *rewards, int64_t ld_rewards,
+                      const void *values, int64_t ld_values,
+                      const int32_t *actions, int64_t ld_actions,
+                      const void *log_pi, int64_t ld_log_pi,
+                      const void *log_mu, int64_t ld_log_mu, int log_mu_taken,
+                      const uint8_t *terminated, int64_t ld_terminated,
+                      const uint8_t *truncated, int64_t ld_truncated,
+                      const void *trunc_values, int64_t ld_trunc_values,
+                      float gamma, float lam, float rho_bar, float c_bar, float pg_rho_bar,
+                      float *vs, int64_t ld_vs,
+                      float *pg_advantages, int64_t ld_pg_advantages,
+                      void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *rlca_last_error(void);
 

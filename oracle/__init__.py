@@ -55,10 +55,11 @@ def _load():
         lib.oracle_affine_scan.argtypes = [i64, i64, _D, _D, _U8, ctypes.c_int, _D,
                                            _D, _D, _D]
         _I32 = ctypes.POINTER(ctypes.c_int32)
-        lib.oracle_retrace_probs.argtypes = [i64, i64, i64, _D, _D, _I32, _D, _D, _U8, _U8, _D,
-                                             dbl, dbl, dbl, _D, _D, _D, _D]
-        lib.oracle_vtrace_probs.argtypes = [i64, i64, i64, _D, _D, _I32, _D, _D, _U8, _U8, _D,
-                                            dbl, dbl, dbl, dbl, dbl, _D, _D, _D, _D, _D]
+        ci = ctypes.c_int
+        lib.oracle_retrace_probs.argtypes = [i64, i64, i64, _D, _D, _I32, _D, _D, ci, _U8, _U8,
+                                             _D, dbl, dbl, dbl, _D, _D, _D, _D]
+        lib.oracle_vtrace_probs.argtypes = [i64, i64, i64, _D, _D, _I32, _D, _D, ci, _U8, _U8,
+                                            _D, dbl, dbl, dbl, dbl, dbl, _D, _D, _D, _D, _D]
         for f in (lib.oracle_returns, lib.oracle_gae, lib.oracle_td_lambda,
                   lib.oracle_vtrace, lib.oracle_retrace, lib.oracle_eligibility_trace,
                   lib.oracle_episodic_cumsum, lib.oracle_affine_scan,
@@ -280,23 +281,26 @@ def _i32(x, shape):
 def retrace_probs(rewards, q_values, actions, log_pi, log_mu, terminated=None, truncated=None,
                   trunc_eq=None, *, gamma, lam, c_bar=1.0, carry_in=None, chunk=False):
     """Retrace(lambda) from tables: q_values and log_pi ``[N, T+1, A]``,
-    log_mu ``[N, T, A]``, actions ``[N, T]``; trunc_eq ``[N, T]`` is
-    E_pi Q at the true final state of truncated steps.  Returns ``Q^ret``
-    (chunk=True: also carry_out and carry_map)."""
+    log_mu ``[N, T, A]`` (or ``[N, T]``: the taken actions' entries only),
+    actions ``[N, T]``; trunc_eq ``[N, T]`` is E_pi Q at the true final state
+    of truncated steps.  Returns ``Q^ret`` (chunk=True: also carry_out and
+    carry_map)."""
     r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
     N, T = r.shape
     A = np.shape(_as_numpy(q_values))[2]
     q, qp = _f64(q_values, (N, T + 1, A))
     ac, acp = _i32(actions, (N, T))
     lp, lpp = _f64(log_pi, (N, T + 1, A))
-    lm, lmp = _f64(log_mu, (N, T, A))
+    mu_taken = len(np.shape(_as_numpy(log_mu))) == 2
+    lm, lmp = _f64(log_mu, (N, T) if mu_taken else (N, T, A))
     te, tep = _u8(terminated, (N, T))
     tr, trp = _u8(truncated, (N, T))
     te2, te2p = _f64(trunc_eq, (N, T))
     ci, cip = _f64(carry_in, (N,))
     out = np.empty((N, T), np.float64)
     c = _Carry(N)
-    _check(_load().oracle_retrace_probs(N, T, A, rp, qp, acp, lpp, lmp, tep, trp, te2p,
+    _check(_load().oracle_retrace_probs(N, T, A, rp, qp, acp, lpp, lmp, int(mu_taken), tep,
+                                        trp, te2p,
                                         float(gamma), float(lam), float(c_bar),
                                         out.ctypes.data_as(_D), cip, c.out_p, c.map_p),
            "retrace_probs")
@@ -306,7 +310,8 @@ def retrace_probs(rewards, q_values, actions, log_pi, log_mu, terminated=None, t
 def vtrace_probs(rewards, values, actions, log_pi, log_mu, terminated=None, truncated=None,
                  trunc_values=None, *, gamma, lam, rho_bar=1.0, c_bar=1.0, pg_rho_bar=1.0,
                  carry_in=None, chunk=False):
-    """V-trace from tables: log_pi and log_mu ``[N, T, A]``, actions ``[N, T]``.
+    """V-trace from tables: log_pi and log_mu ``[N, T, A]`` (log_mu may be
+    ``[N, T]``: the taken actions' entries only), actions ``[N, T]``.
     Returns ``(vs, pg_advantages)`` (chunk=True: also carry_out, carry_map)."""
     r, rp = _f64(rewards, np.shape(_as_numpy(rewards)))
     N, T = r.shape
@@ -314,7 +319,8 @@ def vtrace_probs(rewards, values, actions, log_pi, log_mu, terminated=None, trun
     v, vp = _f64(values, (N, T + 1))
     ac, acp = _i32(actions, (N, T))
     lp, lpp = _f64(log_pi, (N, T, A))
-    lm, lmp = _f64(log_mu, (N, T, A))
+    mu_taken = len(np.shape(_as_numpy(log_mu))) == 2
+    lm, lmp = _f64(log_mu, (N, T) if mu_taken else (N, T, A))
     te, tep = _u8(terminated, (N, T))
     tr, trp = _u8(truncated, (N, T))
     tv, tvp = _f64(trunc_values, (N, T))
@@ -322,7 +328,8 @@ def vtrace_probs(rewards, values, actions, log_pi, log_mu, terminated=None, trun
     vs = np.empty((N, T), np.float64)
     pg = np.empty((N, T), np.float64)
     c = _Carry(N)
-    _check(_load().oracle_vtrace_probs(N, T, A, rp, vp, acp, lpp, lmp, tep, trp, tvp,
+    _check(_load().oracle_vtrace_probs(N, T, A, rp, vp, acp, lpp, lmp, int(mu_taken), tep, trp,
+                                       tvp,
                                        float(gamma), float(lam), float(rho_bar), float(c_bar),
                                        float(pg_rho_bar), vs.ctypes.data_as(_D),
                                        pg.ctypes.data_as(_D), cip, c.out_p, c.map_p),

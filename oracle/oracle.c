@@ -454,13 +454,15 @@ int oracle_affine_scan(int64_t N, int64_t T, const double *alpha, const double *
  *   except after a truncation that is not a termination, where s_{t+1} in the
  *   tables is the next episode's first state: EQ_t = trunc_eq[t], the same
  *   expectation at the true final state, supplied by the caller.
- * V-trace reads log_pi [N, T, A] (no slice T).  log_mu is [N, T, A] for both.
- * With these [N, T] quantities the result is that of oracle_retrace /
- * oracle_vtrace above (window carries passed through).  An action outside
- * [0, A) is rejected (-1).
+ * V-trace reads log_pi [N, T, A] (no slice T).  log_mu is [N, T, A] for both,
+ * or, with mu_taken != 0, [N, T] holding log mu(a_t | s_t) of the taken
+ * actions only.  With these [N, T] quantities the result is that of
+ * oracle_retrace / oracle_vtrace above (window carries passed through).  An
+ * action outside [0, A) is rejected (-1).
  */
 static int derive_probs(int64_t N, int64_t T, int64_t A, int pi_slices, const int32_t *actions,
-                        const double *log_pi, const double *log_mu, double *log_rho)
+                        const double *log_pi, const double *log_mu, int mu_taken,
+                        double *log_rho)
 {
     for (int64_t n = 0; n < N; ++n)
         for (int64_t t = 0; t < T; ++t) {
@@ -468,7 +470,8 @@ static int derive_probs(int64_t N, int64_t T, int64_t A, int pi_slices, const in
             if (a < 0 || a >= A)
                 return -1;
             double lp = log_pi[((size_t)n * (size_t)(T + pi_slices) + (size_t)t) * (size_t)A + (size_t)a];
-            double lm = log_mu[((size_t)n * (size_t)T + (size_t)t) * (size_t)A + (size_t)a];
+            double lm = mu_taken ? log_mu[n * T + t]
+                                 : log_mu[((size_t)n * (size_t)T + (size_t)t) * (size_t)A + (size_t)a];
             log_rho[n * T + t] = lp - lm;
         }
     return 0;
@@ -476,7 +479,8 @@ static int derive_probs(int64_t N, int64_t T, int64_t A, int pi_slices, const in
 
 int oracle_retrace_probs(int64_t N, int64_t T, int64_t A, const double *r, const double *q,
                          const int32_t *actions, const double *log_pi, const double *log_mu,
-                         const uint8_t *term, const uint8_t *trunc, const double *trunc_eq,
+                         int mu_taken, const uint8_t *term, const uint8_t *trunc,
+                         const double *trunc_eq,
                          double gamma, double lam, double c_bar, double *qret,
                          const double *carry_in, double *carry_out, double *map_out)
 {
@@ -495,7 +499,7 @@ int oracle_retrace_probs(int64_t N, int64_t T, int64_t A, const double *r, const
     int rc = -1;
     if (q_taken == NULL || eq == NULL || log_rho == NULL)
         goto out;
-    if (derive_probs(N, T, A, 1, actions, log_pi, log_mu, log_rho) != 0)
+    if (derive_probs(N, T, A, 1, actions, log_pi, log_mu, mu_taken, log_rho) != 0)
         goto out;
     for (int64_t n = 0; n < N; ++n)
         for (int64_t t = 0; t < T; ++t) {
@@ -522,7 +526,8 @@ out:
 
 int oracle_vtrace_probs(int64_t N, int64_t T, int64_t A, const double *r, const double *v,
                         const int32_t *actions, const double *log_pi, const double *log_mu,
-                        const uint8_t *term, const uint8_t *trunc, const double *tv,
+                        int mu_taken, const uint8_t *term, const uint8_t *trunc,
+                        const double *tv,
                         double gamma, double lam, double rho_bar, double c_bar,
                         double pg_rho_bar, double *vs, double *pg, const double *carry_in,
                         double *carry_out, double *map_out)
@@ -537,7 +542,7 @@ int oracle_vtrace_probs(int64_t N, int64_t T, int64_t A, const double *r, const 
         return -1;
     double *log_rho = malloc((size_t)N * (size_t)T * sizeof(double));
     int rc = -1;
-    if (log_rho != NULL && derive_probs(N, T, A, 0, actions, log_pi, log_mu, log_rho) == 0)
+    if (log_rho != NULL && derive_probs(N, T, A, 0, actions, log_pi, log_mu, mu_taken, log_rho) == 0)
         rc = oracle_vtrace(N, T, r, v, log_rho, term, trunc, tv, gamma, lam, rho_bar, c_bar,
                            pg_rho_bar, vs, pg, carry_in, carry_out, map_out);
     free(log_rho);

@@ -11,7 +11,9 @@ Functions (same names as the C ABI):
     rlca_returns, rlca_gae, rlca_td_lambda, rlca_vtrace, rlca_retrace,
     rlca_eligibility_trace, rlca_episodic_cumsum,
 their window forms (carry in; carry and carry map out) with the suffix
-_chunk, the generic segmented scan rlca_affine_scan, and the tiling controls rlca_set_variant, rlca_num_variants,
+_chunk, the generic segmented scan rlca_affine_scan, Retrace and V-trace from
+policy log-probability tables (rlca_retrace_probs, rlca_vtrace_probs), and the
+tiling controls rlca_set_variant, rlca_num_variants,
 rlca_variant_info, rlca_last_variant, plus rlca_version.
 """
 from ._binding import (  # noqa: F401
@@ -36,6 +38,7 @@ from ._binding import (  # noqa: F401
     rlca_num_variants,
     rlca_retrace,
     rlca_retrace_chunk,
+    rlca_retrace_probs,
     rlca_returns,
     rlca_returns_chunk,
     rlca_set_variant,
@@ -45,4 +48,5 @@ from ._binding import (  # noqa: F401
     rlca_version,
     rlca_vtrace,
     rlca_vtrace_chunk,
+    rlca_vtrace_probs,
 )

@@ -56,6 +56,12 @@ _SIGNATURES = {
                                    _i64, _vp, _vp, _vp],
     "rlca_affine_scan": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _int, _vp, _vp, _i64,
                          _vp, _vp, _vp],
+    "rlca_retrace_probs": [_i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                           _vp, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f32, _f32, _f32,
+                           _vp, _i64, _vp],
+    "rlca_vtrace_probs": [_i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                          _vp, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f32, _f32, _f32,
+                          _f32, _f32, _vp, _i64, _vp, _i64, _vp],
     "rlca_last_error": [],
     "rlca_version": [],
     "rlca_num_variants": [],
@@ -503,6 +509,100 @@ def rlca_affine_scan(alpha, beta, reset=None, *, reverse=True, carry_in=None, ou
                                            1 if reverse else 0, ci, o, ld_o, co_p, cm_p,
                                            _stream(stream, dev)))
     return out, co, cm
+
+
+# ------------------------------------------------------ policy-table calls
+
+
+def _table(name, x, dtype, N, S, A, device):
+    """A [N, S, A] table, contiguous within a row: (pointer, row stride in elements)."""
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if x.dtype != dtype:
+        raise TypeError("%s has dtype %s; every float input of a call must be %s"
+                        % (name, x.dtype, dtype))
+    if x.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, x.device, device))
+    if tuple(x.shape) != (N, S, A):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(x.shape), (N, S, A)))
+    if (A > 1 and x.stride(2) != 1) or (S > 1 and x.stride(1) != A):
+        raise ValueError("%s must be contiguous within a row ([N, S, A] with strides (ld, A, 1))"
+                         % name)
+    ld = x.stride(0) if N > 1 else max(S * A, 1)
+    return x.data_ptr(), ld
+
+
+def _actions(x, N, T, device):
+    if not isinstance(x, torch.Tensor) or x.dtype != torch.int32:
+        raise TypeError("actions must be an int32 tensor")
+    return _layout("actions", x, (N, T), device)
+
+
+def _log_mu(log_mu, dtype, N, T, A, device):
+    """log_mu as a [N, T, A] table, or [N, T]: the taken actions' entries."""
+    if isinstance(log_mu, torch.Tensor) and log_mu.dim() == 2:
+        ptr, ld = _float_input("log_mu", log_mu, dtype, (N, T), device)
+        return ptr, ld, 1
+    ptr, ld = _table("log_mu", log_mu, dtype, N, T, A, device)
+    return ptr, ld, 0
+
+
+def rlca_retrace_probs(rewards, q_values, actions, log_pi, log_mu, terminated=None,
+                       truncated=None, trunc_eq=None, *, gamma, lam=1.0, c_bar=1.0, out=None,
+                       stream=None):
+    """Retrace(lambda) targets [N, T] float32 from q_values and log_pi
+    [N, T+1, A], log_mu [N, T, A] (or [N, T]: the taken actions' entries) and
+    int32 actions [N, T]; trunc_eq [N, T] (E_pi Q at the true final state) is
+    read at truncations."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    if not isinstance(q_values, torch.Tensor) or q_values.dim() != 3:
+        raise ValueError("q_values must be a 3-D tensor [N, T+1, A]")
+    A = q_values.shape[2]
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    q, ld_q = _table("q_values", q_values, dt, N, T + 1, A, dev)
+    ac, ld_ac = _actions(actions, N, T, dev)
+    lp, ld_lp = _table("log_pi", log_pi, dt, N, T + 1, A, dev)
+    lm, ld_lm, mu_taken = _log_mu(log_mu, dt, N, T, A, dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    teq, ld_teq = _float_input("trunc_eq", trunc_eq, dt, (N, T), dev)
+    out, o, ld_o = _output("q_ret", out, (N, T), dev)
+    _check(load_library().rlca_retrace_probs(N, T, A, code, r, ld_r, q, ld_q, ac, ld_ac, lp, ld_lp,
+                                             lm, ld_lm, mu_taken, te, ld_te, tr, ld_tr, teq,
+                                             ld_teq, gamma, lam, c_bar, o, ld_o,
+                                             _stream(stream, dev)))
+    return out
+
+
+def rlca_vtrace_probs(rewards, values, actions, log_pi, log_mu, terminated=None, truncated=None,
+                      trunc_values=None, *, gamma, lam=1.0, rho_bar=1.0, c_bar=1.0,
+                      pg_rho_bar=1.0, vs=None, pg_advantages=None, with_pg=True, stream=None):
+    """V-trace from log_pi [N, T, A], log_mu [N, T, A] (or [N, T]: the taken
+    actions' entries) and int32 actions [N, T]: ``(vs, pg_advantages)``,
+    each [N, T] float32."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    if not isinstance(log_pi, torch.Tensor) or log_pi.dim() != 3:
+        raise ValueError("log_pi must be a 3-D tensor [N, T, A]")
+    A = log_pi.shape[2]
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    ac, ld_ac = _actions(actions, N, T, dev)
+    lp, ld_lp = _table("log_pi", log_pi, dt, N, T, A, dev)
+    lm, ld_lm, mu_taken = _log_mu(log_mu, dt, N, T, A, dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    vs, o, ld_o = _output("vs", vs, (N, T), dev)
+    pg, ld_pg = None, 0
+    if with_pg or pg_advantages is not None:
+        pg_advantages, pg, ld_pg = _output("pg_advantages", pg_advantages, (N, T), dev)
+    _check(load_library().rlca_vtrace_probs(N, T, A, code, r, ld_r, v, ld_v, ac, ld_ac, lp, ld_lp,
+                                            lm, ld_lm, mu_taken, te, ld_te, tr, ld_tr, tv, ld_tv,
+                                            gamma, lam, rho_bar, c_bar, pg_rho_bar, o, ld_o, pg,
+                                            ld_pg, _stream(stream, dev)))
+    return vs, pg_advantages
 
 
 def rlca_version():

@@ -15,10 +15,12 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librlca.so")
-# Host code and the two kernel tables, compiled in parallel.
-SOURCES = [os.path.join(CSRC, n) for n in ("rlca.hip", "kernels_plain.hip", "kernels_window.hip")]
+# Host code and the kernel tables, compiled in parallel.
+SOURCES = [os.path.join(CSRC, n) for n in ("rlca.hip", "kernels_plain.hip", "kernels_window.hip",
+                                           "kernels_probs.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, n) for n in ("scan_kernels.hpp", "kernel_table.hpp",
-                                                   "variants.hpp")] + [os.path.join(INCLUDE, "rlca.h")]
+                                                   "variants.hpp", "probs_kernels.hpp")] + [
+    os.path.join(INCLUDE, "rlca.h")]
 ARCH = "gfx950"
 
 

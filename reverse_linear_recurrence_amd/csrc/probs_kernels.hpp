@@ -1,0 +1,311 @@
+// probs_kernels.hpp -- Retrace(lambda) and V-trace from the policies'
+// log-probability tables (rl-triton, Results: the heavier Retrace workload
+// loads the action probabilities at every step).
+//
+// The per-step quantities the scan needs are formed on chip from [N, T(+1), A]
+// tables, then the scan core of scan_kernels.hpp (tile_compute) runs as for
+// rlca_retrace / rlca_vtrace:
+//   log_rho_t = log_pi[t][a_t] - log_mu[t][a_t]
+//   Retrace: q_taken_t = q[t][a_t] and
+//            EQ_t = sum over a of exp(log_pi[t+1][a]) * q[t+1][a]
+//            (after a truncation that is not a termination: trunc_eq[t]).
+//
+// Mapping.  One 256-thread workgroup (4 wavefronts) per row; each thread owns
+// K = 4 consecutive steps of a 1024-step tile, tiles visited from the last to
+// the first, with the multi-wavefront scan of scan_kernels.hpp.  For each
+// tile the workgroup first streams the tables' slices with coalesced 16-byte
+// loads (thread i taking elements 4i .. 4i+3, 4(i+256) .., and so on), keeps
+// the taken action's entries in LDS and, for Retrace, adds each run of a
+// thread's elements that share a slice into that slice's LDS accumulator of
+// exp(log_pi) * q.  Streaming whole tables moves fewer bytes than gathering
+// one entry per slice would, because every gathered entry costs a whole
+// memory line.  Each thread then reads its steps' quantities from LDS.
+#pragma once
+
+#include "scan_kernels.hpp"
+
+namespace rlca {
+
+// The tables of the policy-table entry points.  Row strides ld_* are in
+// elements; a table row holds its slices contiguously, A entries each.
+struct TableArgs {
+  int64_t A;
+  const void *q;       int64_t ld_q;    // [N, T+1, A]            (Retrace)
+  const int32_t *act;  int64_t ld_act;  // [N, T]
+  const void *lpi;     int64_t ld_lpi;  // [N, T+1, A] Retrace, [N, T, A] V-trace
+  const void *lmu;     int64_t ld_lmu;  // [N, T, A], or [N, T] when mu_taken
+  const void *teq;     int64_t ld_teq;  // [N, T], read at truncations (Retrace)
+  int mu_taken;                         // log_mu holds the taken actions' entries only
+};
+
+constexpr int kProbsK = 4;
+constexpr int kProbsWaves = 4;                      // wavefronts per row (one row per block)
+constexpr int kProbsGroup = 64 * kProbsWaves;       // threads per row
+constexpr int kProbsTile = kProbsGroup * kProbsK;   // steps per tile
+constexpr int kProbsUnroll = 4;                     // table chunks in flight per thread
+
+// Slice and entry of element e of a tile's table span (A entries per slice):
+// a float reciprocal estimate, corrected to the exact quotient.
+__device__ __forceinline__ void slice_of(int64_t e, int64_t A, float inv_a, int &sl, int &a) {
+  int q = static_cast<int>((static_cast<float>(e) + 0.5f) * inv_a);
+  int r = static_cast<int>(e - static_cast<int64_t>(q) * A);
+  if (r < 0) {
+    --q;
+    r += static_cast<int>(A);
+  } else if (r >= A) {
+    ++q;
+    r -= static_cast<int>(A);
+  }
+  sl = q;
+  a = r;
+}
+
+// Stream slices [0, nsl) of one table row span (tile-relative), A entries
+// each, with the whole workgroup; kOther: a second table over the same span
+// alongside.  Every element whose entry is the slice's taken action is
+// stored to taken[slice] (and the second table's to taken_other[slice]);
+// with kSum, exp(this table's entry) times the second table's entry is added
+// into acc[slice - 1] (the expectation of the step before the slice), each
+// thread adding its runs of same-slice elements with one LDS atomic per run.
+template <typename InT, bool kOther, bool kSum>
+__device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, int nsl,
+                                              int64_t A, float inv_a, const int *acts,
+                                              float *taken, float *taken_other, float *acc,
+                                              int tid) {
+  static_assert(kOther || !kSum, "the sum needs the second table");
+  const int64_t nel = static_cast<int64_t>(nsl) * A;
+  const int64_t nvec = nel / 4;
+  auto take = [&](int sl, int a, float v, float o) {
+    if (a == acts[sl]) {
+      taken[sl] = v;
+      if constexpr (kOther) taken_other[sl] = o;
+    }
+  };
+  for (int64_t i0 = tid; i0 < nvec; i0 += kProbsGroup * kProbsUnroll) {
+    float tv[kProbsUnroll][4], ov[kProbsUnroll][4];
+#pragma unroll
+    for (int u = 0; u < kProbsUnroll; ++u) {
+      const int64_t idx = i0 + kProbsGroup * u < nvec ? i0 + kProbsGroup * u : i0;  // in range
+      Ld<InT>::template vec<4>(tab + 4 * idx, tv[u]);
+      if constexpr (kOther) Ld<InT>::template vec<4>(other + 4 * idx, ov[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kProbsUnroll; ++u) {
+      if (i0 + kProbsGroup * u < nvec) {
+        int sl, a;
+        slice_of(4 * (i0 + kProbsGroup * u), A, inv_a, sl, a);
+        int cur = sl;
+        float run = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          if constexpr (kSum) {
+            if (sl != cur) {
+              if (cur >= 1) atomicAdd(&acc[cur - 1], run);
+              run = 0.f;
+              cur = sl;
+            }
+            run = fmaf(__expf(tv[u][k]), ov[u][k], run);
+          }
+          take(sl, a, tv[u][k], kOther ? ov[u][k] : 0.f);
+          if (++a == A) {
+            a = 0;
+            ++sl;
+          }
+        }
+        if constexpr (kSum) {
+          if (cur >= 1) atomicAdd(&acc[cur - 1], run);
+        }
+      }
+    }
+  }
+  for (int64_t e = 4 * nvec + tid; e < nel; e += kProbsGroup) {
+    int sl, a;
+    slice_of(e, A, inv_a, sl, a);
+    const float v = Ld<InT>::one(tab + e);
+    float o = 0.f;
+    if constexpr (kOther) o = Ld<InT>::one(other + e);
+    if constexpr (kSum) {
+      if (sl >= 1) atomicAdd(&acc[sl - 1], __expf(v) * o);
+    }
+    take(sl, a, v, o);
+  }
+}
+
+template <int Algo, typename InT>
+__global__ void __launch_bounds__(kProbsGroup)
+probs_kernel(const Args p, const TableArgs ta) {
+  static_assert(Algo == kRetrace || Algo == kVtrace, "policy tables: Retrace or V-trace");
+  constexpr int K = kProbsK;
+  constexpr int kTile = kProbsTile;
+  constexpr int WPR = kProbsWaves;
+  // Per tile slice (slot kTile: the slice after the tile): the expectation,
+  // the taken q, log_pi and log_mu, and the action.
+  __shared__ float s_eq[kTile + 1];
+  __shared__ float s_qt[kTile + 1];
+  __shared__ float s_lp[kTile + 1];
+  __shared__ float s_lm[kTile + 1];
+  __shared__ int s_act[kTile + 1];
+  __shared__ float2 s_agg[2][WPR];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int64_t T = p.T, A = ta.A;
+  const int64_t rr = blockIdx.x;  // one row per workgroup; the grid is N
+  const bool row_ok = true;
+
+  RowPtrs<InT> rp;
+  rp.row = rr;
+  rp.r = static_cast<const InT *>(p.r) + rr * p.ld_r;
+  rp.v = Algo == kVtrace ? static_cast<const InT *>(p.v) + rr * p.ld_v : nullptr;
+  rp.lr = rp.eq = rp.tv = nullptr;
+  rp.te = p.term + rr * p.ld_term;
+  rp.tr = p.trunc + rr * p.ld_trunc;
+  rp.has_te = p.term != nullptr;
+  rp.has_tr = p.trunc != nullptr;
+  rp.dense_tv = false;
+  const int32_t *act_row = ta.act + rr * ta.ld_act;
+  const InT *lpi_row = static_cast<const InT *>(ta.lpi) + rr * ta.ld_lpi;
+  const InT *lmu_row = static_cast<const InT *>(ta.lmu) + rr * ta.ld_lmu;
+  const InT *q_row = Algo == kRetrace ? static_cast<const InT *>(ta.q) + rr * ta.ld_q : nullptr;
+  const float nan = __int_as_float(0x7fc00000);
+  const float inv_a = 1.f / static_cast<float>(A);
+
+  const int64_t ntiles = (T + kTile - 1) / kTile;
+  const int lane_off = (kProbsGroup - 1 - tid) * K;  // reverse: thread 0 owns the latest steps
+  float carry = 0.f;
+  CarryMap m{0.f, 1.f};
+  const WindowIn win{0.f, false};
+
+  for (int64_t c = ntiles - 1; c >= 0; --c) {
+    const int64_t ts = c * kTile;
+    const int64_t t0 = ts + lane_off;
+    const int64_t lim = T - t0 > 0 ? T - t0 : 0;
+    const bool whole = ts + kTile <= T;
+    // Slices of the tile (Retrace: and the slice after it, at most slice T).
+    const int nsteps = static_cast<int>(T - ts < kTile ? T - ts : kTile);
+    const int nsl = Algo == kRetrace ? nsteps + 1 : nsteps;
+
+    __syncthreads();  // the previous tile's reads of the LDS arrays are done
+    for (int i = tid; i < nsl; i += kProbsGroup) {
+      const int64_t t = ts + i;
+      s_act[i] = t < T ? act_row[t] : -1;
+      s_eq[i] = 0.f;
+      s_qt[i] = nan;  // taken entries stay NaN for an action outside [0, A)
+      s_lp[i] = nan;
+      s_lm[i] = nan;
+    }
+    __syncthreads();
+    if constexpr (Algo == kRetrace) {
+      stream_slices<InT, true, true>(lpi_row + ts * A, q_row + ts * A, nsl, A, inv_a, s_act,
+                                     s_lp, s_qt, s_eq, tid);
+      // A log_mu table: its slices below T (the slice after the window has
+      // no action).
+      const int nsl_mu = static_cast<int>(T - ts < nsl ? T - ts : nsl);
+      if (!ta.mu_taken)
+        stream_slices<InT, false, false>(lmu_row + ts * A, nullptr, nsl_mu, A, inv_a, s_act,
+                                         s_lm, nullptr, nullptr, tid);
+    } else {
+      if (ta.mu_taken)
+        stream_slices<InT, false, false>(lpi_row + ts * A, nullptr, nsl, A, inv_a, s_act, s_lp,
+                                         nullptr, nullptr, tid);
+      else
+        stream_slices<InT, true, false>(lpi_row + ts * A, lmu_row + ts * A, nsl, A, inv_a, s_act,
+                                        s_lp, s_lm, nullptr, tid);
+    }
+    __syncthreads();
+
+    // The thread's rewards, flags and (V-trace) values.
+    Tile<K> x;
+#pragma unroll
+    for (int j = 0; j < K; ++j) { x.r[j] = 0.f; x.v[j] = 0.f; x.lr[j] = 0.f; x.eq[j] = 0.f; x.tv[j] = 0.f; }
+    x.v[K] = 0.f;
+    x.lr[K] = 0.f;
+    x.dense = false;
+    x.at_start = false;
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i) { x.te[i] = 0; x.tr[i] = 0; }
+    if (whole) {
+      Ld<InT>::template vec<K>(rp.r + t0, x.r);
+      const uint8_t *own = reinterpret_cast<const uint8_t *>(rp.r + t0);
+      ld_flags_raw<K>(rp.has_te ? rp.te + t0 : own, x.fte);
+      ld_flags_raw<K>(rp.has_tr ? rp.tr + t0 : own, x.ftr);
+      if constexpr (Algo == kVtrace) {
+        float vk[K];
+        Ld<InT>::template vec<K>(rp.v + t0, vk);
+#pragma unroll
+        for (int j = 0; j < K; ++j) x.v[j] = vk[j];
+        x.v[K] = Ld<InT>::one(rp.v + t0 + K);
+      }
+      decode_flags<K>(x.fte, x.te);
+      decode_flags<K>(x.ftr, x.tr);
+#pragma unroll
+      for (int i = 0; i < K / 4; ++i) {
+        x.te[i] = rp.has_te ? x.te[i] : 0u;
+        x.tr[i] = rp.has_tr ? x.tr[i] : 0u;
+      }
+    } else if (lim > 0) {
+      ld_part<InT, K>(rp.r + t0, lim, x.r);
+      if (rp.has_te) ld_flags_part<K>(rp.te + t0, lim, x.te);
+      if (rp.has_tr) ld_flags_part<K>(rp.tr + t0, lim, x.tr);
+      if constexpr (Algo == kVtrace) {
+#pragma unroll
+        for (int e = 0; e <= K; ++e) x.v[e] = e <= lim ? Ld<InT>::one(rp.v + t0 + e) : 0.f;
+      }
+    }
+
+    // Behaviour entries given per step (mu_taken): read like the rewards.
+    float lmk[K + 1];
+#pragma unroll
+    for (int j = 0; j <= K; ++j) lmk[j] = 0.f;
+    if (ta.mu_taken) {
+      if (whole) {
+        float v4[K];
+        Ld<InT>::template vec<K>(lmu_row + t0, v4);
+#pragma unroll
+        for (int j = 0; j < K; ++j) lmk[j] = v4[j];
+      } else {
+        float v4[K];
+        ld_part<InT, K>(lmu_row + t0, lim, v4);
+#pragma unroll
+        for (int j = 0; j < K; ++j) lmk[j] = v4[j];
+      }
+      if (Algo == kRetrace && lim > K) lmk[K] = Ld<InT>::one(lmu_row + t0 + K);
+    }
+
+    // The per-step quantities from LDS: log_rho (and Retrace's neighbour
+    // log_rho_{t0+K}, q_taken and the expectation, or the truncation value).
+    const int s0 = lane_off;
+    const InT *teq_row =
+        Algo == kRetrace ? static_cast<const InT *>(ta.teq) + late_v(rr) * ta.ld_teq : nullptr;
+#pragma unroll
+    for (int j = 0; j <= K; ++j) {
+      const bool step = j < lim;
+      const bool next = Algo == kRetrace && j == K && lim > K;
+      if (step || next) {
+        const int s = s0 + j;
+        x.lr[j] = s_lp[s] - (ta.mu_taken ? lmk[j] : s_lm[s]);
+        if (j < K) {
+          if constexpr (Algo == kRetrace) {
+            x.v[j] = s_qt[s];
+            const bool trunc_only = flag<K>(x.tr, j) && !flag<K>(x.te, j);
+            x.eq[j] = trunc_only ? Ld<InT>::one(teq_row + t0 + j) : s_eq[s];
+          }
+        }
+      }
+    }
+    if constexpr (Algo == kVtrace) sparse_tv<kVtrace, InT, K>(p, rp, t0, x);
+
+    if (whole) {
+      carry = tile_compute<Algo, InT, K, 64, WPR, false, false>(p, rp, x, t0, T - t0, row_ok, c,
+                                                                c > 0, lane, wave, carry, s_agg,
+                                                                m, win, false);
+    } else {
+      carry = tile_compute<Algo, InT, K, 64, WPR, true, false>(p, rp, x, t0, lim, row_ok, c,
+                                                               c > 0, lane, wave, carry, s_agg, m,
+                                                               win, false);
+    }
+  }
+}
+
+}  // namespace rlca

@@ -3,8 +3,9 @@
 //
 // Nothing here touches element data: every step of the computation runs in
 // the kernels of scan_kernels.hpp (instantiated in kernels_plain.hip and
-// kernels_window.hip).  A call validates its arguments, picks a tiling
-// variant, and enqueues exactly one kernel on the caller's stream.
+// kernels_window.hip) and probs_kernels.hpp (kernels_probs.hip).  A call
+// validates its arguments, picks a tiling variant, and enqueues exactly one
+// kernel on the caller's stream.
 
 #include <hip/hip_runtime.h>
 
@@ -15,6 +16,7 @@
 #include <cstring>
 #include <string>
 
+#include "probs_kernels.hpp"
 #include "rlca.h"
 #include "scan_kernels.hpp"
 #include "variants.hpp"
@@ -240,6 +242,32 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const 
   a.cout = w.cout;
   a.cmap = w.cmap;
   return launch(algo, dtype, a, stream, w.on);
+}
+
+// The policy-table kernels: one tiling (a 256-thread workgroup per row),
+// arguments by value.
+int launch_probs(int algo, int dtype, const Args &args, const TableArgs &tables, void *stream) {
+  const void *kernel = probs_kernel_for(algo, dtype);
+  if (kernel == nullptr) return fail(RLCA_EINVAL, "no policy-table kernel for algorithm %d", algo);
+  Args a = args;
+  TableArgs ta = tables;
+  const dim3 grid(static_cast<unsigned>(a.N));
+  const dim3 block(kProbsThreads);
+  void *kargs[] = {&a, &ta};
+  const hipError_t e =
+      hipLaunchKernel(kernel, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  t_last_variant = -1;
+  return RLCA_OK;
+}
+
+constexpr int64_t kMaxActions = 65536;
+
+int check_actions(int64_t A) {
+  if (A < 1 || A > kMaxActions)
+    return fail(RLCA_EINVAL, "num_actions = %lld must lie in [1, %lld]", static_cast<long long>(A),
+                static_cast<long long>(kMaxActions));
+  return RLCA_OK;
 }
 
 int returns_impl(int64_t num_envs, int64_t T, int dtype, const void *rewards, int64_t ld_rewards,
@@ -610,9 +638,121 @@ int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype, const void *alpha,
                             Window{true, carry_in, carry_out, carry_map}, a, stream);
 }
 
+// ------------------------------------------------ policy-table entry points
+
+int rlca_retrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                       const void *rewards, int64_t ld_rewards, const void *q_values,
+                       int64_t ld_q_values, const int32_t *actions, int64_t ld_actions,
+                       const void *log_pi, int64_t ld_log_pi, const void *log_mu,
+                       int64_t ld_log_mu, int log_mu_taken, const uint8_t *terminated,
+                       int64_t ld_terminated, const uint8_t *truncated, int64_t ld_truncated,
+                       const void *trunc_eq,
+                       int64_t ld_trunc_eq, float gamma, float lam, float c_bar, float *q_ret,
+                       int64_t ld_q_ret, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_actions(num_actions));
+  if (log_mu_taken != 0 && log_mu_taken != 1)
+    return fail(RLCA_EINVAL, "log_mu_taken = %d must be 0 or 1", log_mu_taken);
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  RLCA_TRY(check_clip("c_bar", c_bar));
+  if (truncated != nullptr && trunc_eq == nullptr)
+    return fail(RLCA_EINVAL, "truncated is given but trunc_eq is NULL");
+  const int64_t es = esize_of(dtype);
+  const int64_t A = num_actions;
+  Arr arrs[] = {
+      {"rewards", rewards, ld_rewards, T, es, true, false},
+      {"q_values", q_values, ld_q_values, (T + 1) * A, es, true, false},
+      {"actions", actions, ld_actions, T, 4, true, false},
+      {"log_pi", log_pi, ld_log_pi, (T + 1) * A, es, true, false},
+      {"log_mu", log_mu, ld_log_mu, log_mu_taken ? T : T * A, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {"trunc_eq", truncated != nullptr ? trunc_eq : nullptr, ld_trunc_eq, T, es, false, false},
+      {"q_ret", q_ret, ld_q_ret, T, 4, true, true},
+  };
+  if (num_envs == 0 || T == 0) return RLCA_OK;
+  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
+  RLCA_TRY(check_aliasing(arrs, 9));
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = rewards; a.ld_r = ld_rewards;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = q_ret; a.ld_o0 = ld_q_ret;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = 1.f; a.c_bar = c_bar; a.pg_rho_bar = 1.f;
+  TableArgs ta{};
+  ta.A = A;
+  ta.q = q_values; ta.ld_q = ld_q_values;
+  ta.act = actions; ta.ld_act = ld_actions;
+  ta.lpi = log_pi; ta.ld_lpi = ld_log_pi;
+  ta.lmu = log_mu; ta.ld_lmu = ld_log_mu;
+  ta.mu_taken = log_mu_taken;
+  ta.teq = truncated != nullptr ? trunc_eq : nullptr; ta.ld_teq = ld_trunc_eq;
+  return launch_probs(kRetrace, dtype, a, ta, stream);
+}
+
+int rlca_vtrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                      const void *rewards, int64_t ld_rewards, const void *values,
+                      int64_t ld_values, const int32_t *actions, int64_t ld_actions,
+                      const void *log_pi, int64_t ld_log_pi, const void *log_mu,
+                      int64_t ld_log_mu, int log_mu_taken, const uint8_t *terminated,
+                      int64_t ld_terminated, const uint8_t *truncated, int64_t ld_truncated,
+                      const void *trunc_values,
+                      int64_t ld_trunc_values, float gamma, float lam, float rho_bar,
+                      float c_bar, float pg_rho_bar, float *vs, int64_t ld_vs,
+                      float *pg_advantages, int64_t ld_pg_advantages, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_actions(num_actions));
+  if (log_mu_taken != 0 && log_mu_taken != 1)
+    return fail(RLCA_EINVAL, "log_mu_taken = %d must be 0 or 1", log_mu_taken);
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  RLCA_TRY(check_clip("rho_bar", rho_bar));
+  RLCA_TRY(check_clip("c_bar", c_bar));
+  RLCA_TRY(check_clip("pg_rho_bar", pg_rho_bar));
+  if (truncated != nullptr && trunc_values == nullptr)
+    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
+  const int64_t es = esize_of(dtype);
+  const int64_t A = num_actions;
+  const bool tv_used = truncated != nullptr;
+  Arr arrs[] = {
+      {"rewards", rewards, ld_rewards, T, es, true, false},
+      {"values", values, ld_values, T + 1, es, true, false},
+      {"actions", actions, ld_actions, T, 4, true, false},
+      {"log_pi", log_pi, ld_log_pi, T * A, es, true, false},
+      {"log_mu", log_mu, ld_log_mu, log_mu_taken ? T : T * A, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
+      {"vs", vs, ld_vs, T, 4, true, true},
+      {"pg_advantages", pg_advantages, ld_pg_advantages, T, 4, false, true},
+  };
+  if (num_envs == 0 || T == 0) return RLCA_OK;
+  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
+  RLCA_TRY(check_aliasing(arrs, 10));
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = rewards; a.ld_r = ld_rewards;
+  a.v = values; a.ld_v = ld_values;
+  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = vs; a.ld_o0 = ld_vs;
+  a.o1 = pg_advantages; a.ld_o1 = ld_pg_advantages;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = rho_bar; a.c_bar = c_bar; a.pg_rho_bar = pg_rho_bar;
+  TableArgs ta{};
+  ta.A = A;
+  ta.act = actions; ta.ld_act = ld_actions;
+  ta.lpi = log_pi; ta.ld_lpi = ld_log_pi;
+  ta.lmu = log_mu; ta.ld_lmu = ld_log_mu;
+  ta.mu_taken = log_mu_taken;
+  return launch_probs(kVtrace, dtype, a, ta, stream);
+}
+
 const char *rlca_last_error(void) { return t_last_error.c_str(); }
 
-int rlca_version(void) { return 200; }  // 0.2.0: window entry points, affine scan
+int rlca_version(void) { return 300; }  // 0.3.0: policy-table Retrace and V-trace
 
 int rlca_num_variants(void) { return kNumVariants; }
 

@@ -39,5 +39,9 @@ inline int64_t tile_steps(const Variant &v) {
 // window_kernel: carry vector in, carry and carry map out (every Algo).
 const void *plain_kernel(int algo, int dtype, int variant, bool uniform);
 const void *window_kernel(int algo, int dtype, int variant, bool uniform);
+// The policy-table kernels (Retrace, V-trace): one tiling, one row per
+// 256-thread workgroup.
+const void *probs_kernel_for(int algo, int dtype);
+constexpr int kProbsThreads = 256;
 
 }  // namespace rlca

@@ -14,7 +14,8 @@ stored as ``uint8``.  bf16 inputs are rounded from the fp32 draws by torch
 Workloads follow the synthetic rollout shapes the rl-triton explainer pages
 discuss (``[num_envs, seq_len]`` tensors, Technical summary: Problem; results
 quoted at 4096 envs x 128 steps).  The five named workloads below are the
-configurations this library is measured on.
+configurations this library is measured on; the policy-table workloads draw
+their tables with ``make_tables``.
 """
 from dataclasses import dataclass, field
 from typing import Dict, Optional
@@ -38,6 +39,8 @@ class Workload:
     reward_dist: str = "normal"       # "normal" N(0,1) | "uniform" U(-1,1)
     log_rho_std: float = 0.5
     clips: Dict[str, float] = field(default_factory=dict)
+    num_actions: int = 0              # policy-table workloads: actions per step
+    mu_taken: bool = False            # log_mu as the taken actions' entries [N, T]
 
 
 WORKLOADS = {
@@ -58,6 +61,18 @@ WORKLOADS = {
                                      106, gamma=0.99, lam=0.95, p_term=0.005, p_trunc=0.002),
     "cumsum_4096x128": Workload("cumsum_4096x128", "cumsum", 4096, 128, "f32", 107,
                                 gamma=1.0, lam=1.0, p_term=0.005, p_trunc=0.002),
+    # Retrace and V-trace from policy tables, at the off-policy workload's
+    # shape with 18 actions (the size of a full Atari action set).
+    "retrace_probs_2048x1024x18": Workload("retrace_probs_2048x1024x18", "retrace_probs", 2048,
+                                           1024, "f32", 108, gamma=0.99, lam=0.95,
+                                           p_term=0.002, p_trunc=0.001,
+                                           clips={"c_bar": 1.0}, num_actions=18,
+                                           mu_taken=True),
+    "vtrace_probs_2048x1024x18": Workload("vtrace_probs_2048x1024x18", "vtrace_probs", 2048,
+                                          1024, "f32", 109, gamma=0.99, lam=0.95,
+                                          p_term=0.002, p_trunc=0.001,
+                                          clips={"rho_bar": 1.0, "c_bar": 1.0, "pg_rho_bar": 1.0},
+                                          num_actions=18),
 }
 
 _NEEDS = {
@@ -136,9 +151,68 @@ def make_rollout(algo: str, num_envs: int, T: int, *, seed: int, dtype: str = "f
     return res
 
 
+def _log_probs(g: np.random.Generator, shape, scale: float) -> np.ndarray:
+    """Log-probability tables of random policies: N(0, scale^2) logits,
+    normalized over the last axis (in float64, then rounded to float32)."""
+    z = g.standard_normal(shape) * scale
+    z = z - z.max(-1, keepdims=True)
+    return (z - np.log(np.exp(z).sum(-1, keepdims=True))).astype(np.float32)
+
+
+def make_tables(algo: str, num_envs: int, T: int, num_actions: int, *, seed: int,
+                dtype: str = "f32", p_term: float = 0.0, p_trunc: Optional[float] = None,
+                logit_scale: float = 1.0, mu_taken: bool = False) -> Dict[str, torch.Tensor]:
+    """Draw one batch for the policy-table entry points as CPU tensors.
+
+    Draw order: rewards [N,T]; values [N,T+1] (vtrace_probs) or q_values
+    [N,T+1,A] (retrace_probs); target log-probabilities log_pi ([N,T+1,A]
+    for Retrace, [N,T,A] for V-trace); behaviour log-probabilities log_mu
+    [N,T,A]; actions [N,T] int32, sampled from the behaviour policy by
+    inverse CDF of uniform draws; terminated; truncated (if p_trunc is not
+    None) with trunc_eq (Retrace) or trunc_values (V-trace) [N,T], drawn
+    densely as N(0,1).  mu_taken: log_mu is returned as the taken actions'
+    entries [N,T] (the same draws).
+    """
+    if algo not in ("retrace_probs", "vtrace_probs"):
+        raise ValueError("unknown policy-table algorithm %r" % algo)
+    g = np.random.Generator(np.random.PCG64(seed))
+    N, A = num_envs, num_actions
+    retrace = algo == "retrace_probs"
+    out: Dict[str, np.ndarray] = {"rewards": g.standard_normal((N, T), dtype=np.float32)}
+    if retrace:
+        out["q_values"] = g.standard_normal((N, T + 1, A), dtype=np.float32)
+        out["log_pi"] = _log_probs(g, (N, T + 1, A), logit_scale)
+    else:
+        out["values"] = g.standard_normal((N, T + 1), dtype=np.float32)
+        out["log_pi"] = _log_probs(g, (N, T, A), logit_scale)
+    out["log_mu"] = _log_probs(g, (N, T, A), logit_scale)
+    cdf = np.cumsum(np.exp(out["log_mu"].astype(np.float64)), axis=-1)
+    u = g.random((N, T, 1)) * cdf[..., -1:]
+    out["actions"] = np.minimum((cdf < u).sum(-1), A - 1).astype(np.int32)
+    if mu_taken:
+        out["log_mu"] = np.take_along_axis(out["log_mu"], out["actions"][..., None].astype(np.int64),
+                                           -1)[..., 0]
+    out["terminated"] = (g.random((N, T)) < p_term).astype(np.uint8)
+    if p_trunc is not None:
+        out["truncated"] = (g.random((N, T)) < p_trunc).astype(np.uint8)
+        out["trunc_eq" if retrace else "trunc_values"] = g.standard_normal((N, T),
+                                                                           dtype=np.float32)
+    res: Dict[str, torch.Tensor] = {}
+    for k, a in out.items():
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        if dtype == "bf16" and a.dtype == np.float32:
+            t = t.to(torch.bfloat16)
+        res[k] = t
+    return res
+
+
 def make_workload(w: Workload, num_envs: Optional[int] = None, T: Optional[int] = None,
                   seed: Optional[int] = None) -> Dict[str, torch.Tensor]:
     """Draw the inputs of a named workload (optionally at another size or seed)."""
+    if w.algo in ("retrace_probs", "vtrace_probs"):
+        return make_tables(w.algo, num_envs or w.num_envs, T or w.T, w.num_actions,
+                           seed=w.seed if seed is None else seed, dtype=w.dtype,
+                           p_term=w.p_term, p_trunc=w.p_trunc, mu_taken=w.mu_taken)
     return make_rollout(w.algo, num_envs or w.num_envs, T or w.T,
                         seed=w.seed if seed is None else seed, dtype=w.dtype,
                         p_term=w.p_term, p_trunc=w.p_trunc, reward_dist=w.reward_dist,

@@ -238,3 +238,29 @@ def test_affine_scan_validates(lib):
 def test_binding_refuses_bad_carry_vectors():
     with pytest.raises(ValueError, match="GPU"):
         rl.rlca_affine_scan(torch.zeros(2, 4), torch.zeros(2, 4))
+
+
+def test_policy_table_entry_points_validate(lib):
+    Q, ACT, LP, LM = (BASE + (12 + i) * 0x1000000 for i in range(4))
+    rp = lambda **k: lib.rlca_retrace_probs(
+        4, 8, k.get("A", 5), F32, R, 8, k.get("q", Q), k.get("ld_q", 45), k.get("act", ACT), 8,
+        LP, k.get("ld_lp", 45), LM, k.get("ld_lm", 40), k.get("taken", 0), None, 8,
+        k.get("tr", None), 8,
+        k.get("teq", None), 8, 0.9, 0.9, 1.0, k.get("out", ADV), 8, None)
+    assert rp(A=0) == rl.RLCA_EINVAL and "num_actions" in err(lib)
+    assert rp(A=65537) == rl.RLCA_EINVAL
+    assert rp(ld_q=44) == rl.RLCA_EINVAL and "ld_q_values" in err(lib)   # needs (T+1)*A
+    assert rp(ld_lp=40) == rl.RLCA_EINVAL and "ld_log_pi" in err(lib)
+    assert rp(ld_lm=39) == rl.RLCA_EINVAL and "ld_log_mu" in err(lib)
+    assert rp(taken=2) == rl.RLCA_EINVAL and "log_mu_taken" in err(lib)
+    assert rp(ld_lm=7, taken=1) == rl.RLCA_EINVAL and "ld_log_mu" in err(lib)
+    assert rp(act=ACT + 2) == rl.RLCA_EINVAL and "actions" in err(lib)
+    assert rp(q=None) == rl.RLCA_EINVAL and "q_values" in err(lib)
+    assert rp(tr=TR) == rl.RLCA_EINVAL and "trunc_eq" in err(lib)
+    assert rp(out=Q + 4) == rl.RLCA_EALIAS and "q_values" in err(lib)
+    vt = lambda **k: lib.rlca_vtrace_probs(
+        4, 8, 5, F32, R, 8, V, 9, ACT, 8, LP, k.get("ld_lp", 40), LM, 40, 0, None, 8, None, 8,
+        None, 8, 0.9, 0.9, k.get("rho", 1.0), 1.0, 1.0, ADV, 8, k.get("pg", None), 8, None)
+    assert vt(ld_lp=39) == rl.RLCA_EINVAL and "ld_log_pi" in err(lib)
+    assert vt(rho=0.0) == rl.RLCA_EINVAL and "rho_bar" in err(lib)
+    assert vt(pg=ACT) == rl.RLCA_EALIAS and "actions" in err(lib)

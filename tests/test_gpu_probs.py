@@ -1,0 +1,145 @@
+"""GPU parity of Retrace and V-trace from policy log-probability tables
+(rlca_retrace_probs, rlca_vtrace_probs) against the oracle.
+
+The tables are [N, T(+1), A] (rl-triton, Results: the heavier Retrace workload
+loads the action probabilities at every step).  Cases cover one to 257
+actions, row lengths around the 256-step tile, workgroups with rows past N,
+row strides larger than a row, both input dtypes, the full-size workload, and
+out-of-range actions (NaN at that step and every earlier step of the row).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import reverse_linear_recurrence_amd as rl
+from gpu_common import TOL, rel_err
+from reverse_linear_recurrence_amd.synth import WORKLOADS, fp32_param, make_tables, make_workload
+
+pytestmark = pytest.mark.gpu
+
+RP = dict(gamma=fp32_param(0.97), lam=fp32_param(0.9), c_bar=fp32_param(0.95))
+VP = dict(gamma=fp32_param(0.97), lam=fp32_param(0.9), rho_bar=fp32_param(1.05),
+          c_bar=fp32_param(0.95), pg_rho_bar=fp32_param(1.1))
+
+
+def gpu_retrace(d, **kw):
+    g = lambda k: None if d.get(k) is None else d[k].cuda()
+    out = rl.rlca_retrace_probs(g("rewards"), g("q_values"), g("actions"), g("log_pi"),
+                                g("log_mu"), g("terminated"), g("truncated"), g("trunc_eq"),
+                                **dict(RP, **kw))
+    torch.cuda.synchronize()
+    return out.double().cpu().numpy()
+
+
+def ref_retrace(d, **kw):
+    return oracle.retrace_probs(d["rewards"], d["q_values"], d["actions"], d["log_pi"],
+                                d["log_mu"], d.get("terminated"), d.get("truncated"),
+                                d.get("trunc_eq"), **dict(RP, **kw))
+
+
+def gpu_vtrace(d, **kw):
+    g = lambda k: None if d.get(k) is None else d[k].cuda()
+    vs, pg = rl.rlca_vtrace_probs(g("rewards"), g("values"), g("actions"), g("log_pi"),
+                                  g("log_mu"), g("terminated"), g("truncated"),
+                                  g("trunc_values"), **dict(VP, **kw))
+    torch.cuda.synchronize()
+    return vs.double().cpu().numpy(), pg.double().cpu().numpy()
+
+
+def ref_vtrace(d, **kw):
+    return oracle.vtrace_probs(d["rewards"], d["values"], d["actions"], d["log_pi"], d["log_mu"],
+                               d.get("terminated"), d.get("truncated"), d.get("trunc_values"),
+                               **dict(VP, **kw))
+
+
+CASES = [(1, 1, 1), (5, 7, 3), (9, 255, 18), (4, 256, 18), (6, 257, 18), (3, 700, 5),
+         (2, 1024, 18), (2, 1027, 18), (3, 2100, 4), (5, 300, 64), (2, 260, 257)]
+
+
+@pytest.mark.parametrize("mu_taken", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,T,A", CASES)
+def test_retrace_probs_parity(N, T, A, dtype, mu_taken):
+    for p_term, p_trunc in ((0.05, 0.05), (0.0, None)):
+        d = make_tables("retrace_probs", N, T, A, seed=N * 1000 + T + A, dtype=dtype,
+                        p_term=p_term, p_trunc=p_trunc, mu_taken=mu_taken)
+        got, ref = gpu_retrace(d), ref_retrace(d)
+        assert np.all(np.isfinite(got))
+        assert rel_err(got, ref) <= TOL[dtype], (N, T, A, p_trunc, rel_err(got, ref))
+
+
+@pytest.mark.parametrize("mu_taken", [False, True])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,T,A", CASES)
+def test_vtrace_probs_parity(N, T, A, dtype, mu_taken):
+    for p_term, p_trunc in ((0.05, 0.05), (0.0, None)):
+        d = make_tables("vtrace_probs", N, T, A, seed=N * 1000 + T + A + 1, dtype=dtype,
+                        p_term=p_term, p_trunc=p_trunc, mu_taken=mu_taken)
+        got, ref = gpu_vtrace(d), ref_vtrace(d)
+        for a, b in zip(got, ref):
+            assert np.all(np.isfinite(a))
+            assert rel_err(a, b) <= TOL[dtype], (N, T, A, p_trunc, rel_err(a, b))
+
+
+@pytest.mark.parametrize("name", ["retrace_probs_2048x1024x18", "vtrace_probs_2048x1024x18"])
+def test_full_size_workloads(name):
+    w = WORKLOADS[name]
+    d = make_workload(w)
+    kw = {k: fp32_param(v) for k, v in w.clips.items()}
+    kw.update(gamma=fp32_param(w.gamma), lam=fp32_param(w.lam))
+    if w.algo == "retrace_probs":
+        got, ref = gpu_retrace(d, **kw), ref_retrace(d, **kw)
+        assert rel_err(got, ref) <= TOL["f32"]
+    else:
+        for a, b in zip(gpu_vtrace(d, **kw), ref_vtrace(d, **kw)):
+            assert rel_err(a, b) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("mu_taken", [False, True])
+def test_strided_tables_and_rows(mu_taken):
+    # Rows of every array further apart than one row; results unchanged.
+    N, T, A = 5, 300, 7
+    d = make_tables("retrace_probs", N, T, A, seed=5, p_term=0.05, p_trunc=0.05,
+                    mu_taken=mu_taken)
+    ref = ref_retrace(d)
+    wide = {}
+    for k, v in d.items():
+        pad = list(v.shape)
+        pad[1] += 3
+        big = torch.zeros(pad, dtype=v.dtype)
+        big[:, : v.shape[1]] = v
+        wide[k] = big[:, : v.shape[1]]
+    assert wide["q_values"].stride(0) == (T + 4) * A
+    assert rel_err(gpu_retrace(wide), ref) <= TOL["f32"]
+
+
+def test_out_of_range_action_gives_nan_where_it_reaches():
+    N, T, A = 3, 40, 4
+    d = make_tables("retrace_probs", N, T, A, seed=6, p_term=0.0, p_trunc=None)
+    d["terminated"] = torch.zeros(N, T, dtype=torch.uint8)
+    d["terminated"][1, 19] = 1          # row 1: episode ends after step 19
+    d["actions"][1, 30] = A              # out of range at step 30 of row 1
+    got = gpu_retrace(d)
+    ok = oracle.retrace_probs(d["rewards"][[0, 2]], d["q_values"][[0, 2]], d["actions"][[0, 2]],
+                              d["log_pi"][[0, 2]], d["log_mu"][[0, 2]], gamma=RP["gamma"],
+                              lam=RP["lam"], c_bar=RP["c_bar"])
+    assert rel_err(got[[0, 2]], ok) <= TOL["f32"]          # other rows unaffected
+    # The step and every earlier step of its row: the scan cuts an episode by a
+    # zero factor, and 0 * NaN is NaN, so the boundary after step 19 does not
+    # stop it.  Later steps are untouched.
+    assert np.all(np.isnan(got[1, :31]))
+    assert np.all(np.isfinite(got[1, 31:]))
+
+
+def test_empty_and_validation():
+    d = make_tables("retrace_probs", 2, 3, 4, seed=7, p_trunc=0.1)
+    g = {k: v.cuda() for k, v in d.items()}
+    with pytest.raises(rl.RlcaError) as e:
+        rl.rlca_retrace_probs(g["rewards"], g["q_values"], g["actions"], g["log_pi"],
+                              g["log_mu"], g["terminated"], g["truncated"], None, gamma=0.9)
+    assert e.value.status == rl.RLCA_EINVAL
+    z = {k: v[:0] for k, v in g.items()}
+    out = rl.rlca_retrace_probs(z["rewards"], z["q_values"], z["actions"], z["log_pi"],
+                                z["log_mu"], gamma=0.9)
+    assert out.shape == (0, 3)

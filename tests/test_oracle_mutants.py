@@ -101,10 +101,13 @@ MUTANTS = [
      "if (flag_at(trunc, n, t, T) && !flag_at(term, n, t, T)) {\n                eq[n * T + t]",
      "if (0) {\n                eq[n * T + t]"),
     ("probs_behaviour_from_next_step",
-     "double lm = log_mu[((size_t)n * (size_t)T + (size_t)t) * (size_t)A + (size_t)a];",
-     "double lm = log_mu[((size_t)n * (size_t)T + (size_t)(t + 1 < T ? t + 1 : t)) * (size_t)A + (size_t)a];"),
-    ("vtrace_probs_table_stride", "derive_probs(N, T, A, 0, actions, log_pi, log_mu, log_rho) == 0",
-     "derive_probs(N, T, A, 1, actions, log_pi, log_mu, log_rho) == 0"),
+     ": log_mu[((size_t)n * (size_t)T + (size_t)t) * (size_t)A + (size_t)a];",
+     ": log_mu[((size_t)n * (size_t)T + (size_t)(t + 1 < T ? t + 1 : t)) * (size_t)A + (size_t)a];"),
+    ("probs_taken_behaviour_shifted", "double lm = mu_taken ? log_mu[n * T + t]",
+     "double lm = mu_taken ? log_mu[n * T + (t + 1 < T ? t + 1 : t)]"),
+    ("vtrace_probs_table_stride",
+     "derive_probs(N, T, A, 0, actions, log_pi, log_mu, mu_taken, log_rho) == 0",
+     "derive_probs(N, T, A, 1, actions, log_pi, log_mu, mu_taken, log_rho) == 0"),
 ]
 
 PIN_CASES = [
@@ -144,6 +147,7 @@ PIN_CASES = [
     (pins.test_retrace_probs_single_action_and_greedy_target, {}),
     (pins.test_probs_action_relabeling_is_invariant, {}),
     (pins.test_probs_tables_are_read_only_where_the_definition_reads_them, {}),
+    (pins.test_probs_taken_behaviour_entries_equal_the_table_form, {}),
 ]
 
 

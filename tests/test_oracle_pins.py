@@ -871,3 +871,20 @@ def test_probs_reject_actions_out_of_range():
         e["act"][1, 2] = bad
         with pytest.raises(ValueError):
             _retrace_probs(e)
+
+
+def test_probs_taken_behaviour_entries_equal_the_table_form():
+    # log_mu given as the taken actions' entries [N, T] equals the table form
+    # bitwise (the same numbers enter); the table's other entries are unread.
+    N, T, A = 4, 13, 6
+    d = prob_tables(123, N, T, A)
+    taken = _taken(d["logmu"], d["act"])
+    e = dict(d, logmu=taken)
+    assert np.array_equal(_retrace_probs(e), _retrace_probs(d))
+    kw = dict(gamma=0.9, lam=0.95)
+    a = oracle.vtrace_probs(d["r"], d["v"], d["act"], d["logpi"][:, :T], d["logmu"], **kw)
+    b = oracle.vtrace_probs(d["r"], d["v"], d["act"], d["logpi"][:, :T], taken, **kw)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # A wrong layout of the taken entries is not the table form.
+    assert not np.array_equal(_retrace_probs(dict(d, logmu=taken[:, ::-1].copy())),
+                              _retrace_probs(d))
