@@ -31,16 +31,26 @@ if ROOT not in sys.path:
 METRIC = "env-steps/sec and achieved HBM GB/s (% of peak), GAE 4096 envs × T=128 fp32"
 HBM_PEAK_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "reverse_linear_recurrence_amd", "csrc", f)
-                  for f in ("scan_kernels.hpp", "kernel_table.hpp", "variants.hpp",
-                            "kernels_plain.hip", "kernels_window.hip", "probs_kernels.hpp",
-                            "kernels_probs.hip", "rlca.hip")]
+# The sources each kernel family is built from (with the host code that picks
+# its launch configuration): a committed traffic figure is used only while
+# these are unchanged.
+_CSRC = os.path.join(ROOT, "reverse_linear_recurrence_amd", "csrc")
+KERNEL_SOURCES = {
+    "scan": ("scan_kernels.hpp", "kernel_table.hpp", "variants.hpp", "kernels_plain.hip",
+             "kernels_window.hip", "rlca.hip"),
+    "probs": ("scan_kernels.hpp", "probs_kernels.hpp", "variants.hpp", "kernels_probs.hip",
+              "rlca.hip"),
+}
 
 
-def kernel_source_hash():
+def kernel_family(workload_key):
+    return "probs" if "_probs_" in workload_key else "scan"
+
+
+def kernel_source_hash(family="scan"):
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
+    for f in KERNEL_SOURCES[family]:
+        with open(os.path.join(_CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -151,7 +161,7 @@ def summarize_pmc(fetch_dir, write_dir):
     if os.path.exists(TRAFFIC_FILE):
         out = json.load(open(TRAFFIC_FILE))
     out[meta["workload"]] = {
-        "kernel_source_hash": kernel_source_hash(),
+        "kernel_source_hash": kernel_source_hash(kernel_family(meta["workload"])),
         "bytes_per_launch": traffic,
         "fetch_kib_per_launch": {"%s [grid %s]" % k: fetch[k] for k in scan_name},
         "write_kib_per_launch": {"%s [grid %s]" % k: write[k] for k in scan_name},
@@ -450,7 +460,7 @@ def main():
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
         entry = tr.get(traffic_key)
-        if entry and entry.get("kernel_source_hash") == kernel_source_hash():
+        if entry and entry.get("kernel_source_hash") == kernel_source_hash(kernel_family(traffic_key)):
             traffic = entry.get("bytes_per_launch")
 
     # ---- CPU oracle on the host cores (bounded sample of the same workload)
