@@ -34,7 +34,8 @@ def workload_params(w):
     return params32(p)
 
 
-@pytest.mark.parametrize("name", list(WORKLOADS))
+# (The policy-table workloads have their own file, test_gpu_probs.py.)
+@pytest.mark.parametrize("name", [n for n, w in WORKLOADS.items() if not w.algo.endswith("_probs")])
 def test_workload_full_size(name):
     w = WORKLOADS[name]
     print("workload", name, flush=True)
