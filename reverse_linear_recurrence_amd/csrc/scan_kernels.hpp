@@ -488,10 +488,17 @@ __device__ __forceinline__ void finish_tile(const Args &p, const RowPtrs<InT> &r
   sparse_tv<A, InT, K>(p, rp, t0, x);
 }
 
-// The ragged last tile of a row: element-wise loads of the steps e < lim.
+// The ragged last tile of a row.  A lane whose K steps all lie in the row
+// (lim >= K) loads them as in a whole tile; the lane holding the row's end
+// loads the steps e < lim one by one; lanes past the end load nothing.
 template <int A, typename InT, int K>
 __device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
                                           int64_t lim, Tile<K> &x) {
+  if (lim >= K) {
+    issue_tile<A, InT, K>(p, rp, t0, lim, x);
+    finish_tile<A, InT, K>(p, rp, t0, x);
+    return;
+  }
   using U = Uses<A>;
 #pragma unroll
   for (int j = 0; j < K; ++j) { x.r[j] = 0.f; x.v[j] = 0.f; x.lr[j] = 0.f; x.eq[j] = 0.f; x.tv[j] = 0.f; }
@@ -793,6 +800,18 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
           __builtin_nontemporal_store(V4{o1[4 * i], o1[4 * i + 1], o1[4 * i + 2], o1[4 * i + 3]},
                                       reinterpret_cast<V4 *>(o1_row + t0) + i);
       }
+    }
+  } else if (lim >= K) {
+    // Ragged tile, a lane whose steps all lie in the row: as above.
+#pragma unroll
+    for (int i = 0; i < K / 4; ++i)
+      __builtin_nontemporal_store(V4{o0[4 * i], o0[4 * i + 1], o0[4 * i + 2], o0[4 * i + 3]},
+                                  reinterpret_cast<V4 *>(o0_row + t0) + i);
+    if (has_o1) {
+#pragma unroll
+      for (int i = 0; i < K / 4; ++i)
+        __builtin_nontemporal_store(V4{o1[4 * i], o1[4 * i + 1], o1[4 * i + 2], o1[4 * i + 3]},
+                                    reinterpret_cast<V4 *>(o1_row + t0) + i);
     }
   } else {
 #pragma unroll

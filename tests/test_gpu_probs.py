@@ -143,3 +143,43 @@ def test_empty_and_validation():
     out = rl.rlca_retrace_probs(z["rewards"], z["q_values"], z["actions"], z["log_pi"],
                                 z["log_mu"], gamma=0.9)
     assert out.shape == (0, 3)
+
+
+def test_policy_table_calls_in_a_hip_graph():
+    # Replays agree with eager calls (Retrace up to the order of the LDS sums
+    # of the expectation; V-trace bitwise), with inputs changed in place.
+    d = make_tables("retrace_probs", 9, 700, 18, seed=8, p_term=0.01, p_trunc=0.01)
+    v = make_tables("vtrace_probs", 9, 700, 18, seed=9, p_term=0.01, p_trunc=0.01)
+    g_ = {k: x.cuda() for k, x in d.items()}
+    h_ = {k: x.cuda() for k, x in v.items()}
+    q_out = torch.empty(9, 700, device="cuda")
+    vs_out, pg_out = torch.empty(9, 700, device="cuda"), torch.empty(9, 700, device="cuda")
+
+    def calls(q, vs, pg):
+        rl.rlca_retrace_probs(g_["rewards"], g_["q_values"], g_["actions"], g_["log_pi"],
+                              g_["log_mu"], g_["terminated"], g_["truncated"], g_["trunc_eq"],
+                              out=q, **RP)
+        rl.rlca_vtrace_probs(h_["rewards"], h_["values"], h_["actions"], h_["log_pi"],
+                             h_["log_mu"], h_["terminated"], h_["truncated"], h_["trunc_values"],
+                             vs=vs, pg_advantages=pg, **VP)
+
+    graph = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(graph, stream=s):
+            calls(q_out, vs_out, pg_out)
+    torch.cuda.synchronize()
+    for i in range(3):
+        if i == 1:
+            g_["rewards"].mul_(-0.5)
+            h_["rewards"].mul_(-0.5)
+        e = [torch.empty(9, 700, device="cuda") for _ in range(3)]
+        calls(*e)
+        for x in (q_out, vs_out, pg_out):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert float((q_out - e[0]).abs().max()) <= 1e-5 * float(e[0].abs().max())
+        assert torch.equal(vs_out, e[1]) and torch.equal(pg_out, e[2])

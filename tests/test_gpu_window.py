@@ -320,3 +320,49 @@ def test_affine_scan_reproduces_gae_and_eligibility_calls():
     ref = oracle.eligibility_trace(d["rewards"], d["terminated"], d["truncated"], z0,
                                    gamma=p["gamma"], lam=p["lam"])
     assert rel_err(Z.double().cpu().numpy(), ref) <= TOL["f32"]
+
+
+def test_window_calls_in_a_hip_graph_chain_like_eager_calls():
+    # A captured chain of two windows (the carry passed on device between
+    # them) replays like the eager chain, with eager work and
+    # synchronizations between replays and inputs changed in place.
+    p = params32(DEFAULT_PARAMS)
+    N, T = 40, 300
+    d = to_device(random_inputs("gae", N, T, 91, p_term=0.003, p_trunc=0.003, bootstrap=False))
+    late, early = _slice("gae", d, 150, T), _slice("gae", d, 0, 150)
+    c0 = torch.randn(N, device="cuda")
+    c1 = torch.empty(N, device="cuda")
+    c2 = torch.empty(N, device="cuda")
+    a_late, t_late = torch.empty(N, T - 150, device="cuda"), torch.empty(N, T - 150, device="cuda")
+    a_early, t_early = torch.empty(N, 150, device="cuda"), torch.empty(N, 150, device="cuda")
+
+    def chain(outs):
+        rl.rlca_gae_chunk(late["rewards"], late["values"], late["terminated"], late["truncated"],
+                          late["trunc_values"], gamma=p["gamma"], lam=p["lam"], carry_in=c0,
+                          advantages=outs[0], targets=outs[1], carry_out=c1, with_map=False)
+        rl.rlca_gae_chunk(early["rewards"], early["values"], early["terminated"],
+                          early["truncated"], early["trunc_values"], gamma=p["gamma"],
+                          lam=p["lam"], carry_in=c1, advantages=outs[2], targets=outs[3],
+                          carry_out=c2, with_map=False)
+
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            chain((a_late, t_late, a_early, t_early))
+    torch.cuda.synchronize()
+    for i in range(4):
+        if i == 2:
+            d["rewards"].mul_(-0.5)
+        eager = [torch.empty_like(x) for x in (a_late, t_late, a_early, t_early)]
+        chain(eager)
+        e_c2 = c2.clone()
+        for x in (a_late, t_late, a_early, t_early, c1, c2):
+            x.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((a_late, t_late, a_early, t_early), eager):
+            assert torch.equal(got, want), "replay %d" % i
+        assert torch.equal(c2, e_c2)
