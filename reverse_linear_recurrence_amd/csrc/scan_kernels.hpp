@@ -464,11 +464,9 @@ __device__ __forceinline__ void sparse_tv(const Args &p, const RowPtrs<InT> &rp,
   }
 }
 
-// Decode an issued tile (the first use of its loads) and issue its sparse
-// bootstrap loads.
+// Decode an issued tile's flags (the first use of its loads).
 template <int A, typename InT, int K>
-__device__ __forceinline__ void finish_tile(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
-                                            Tile<K> &x) {
+__device__ __forceinline__ void decode_tile(const RowPtrs<InT> &rp, Tile<K> &x) {
   decode_flags<K>(x.ftr, x.tr);
   decode_flags<K>(x.fte, x.te);
   if constexpr (Uses<A>::prev_flags) {
@@ -485,18 +483,67 @@ __device__ __forceinline__ void finish_tile(const Args &p, const RowPtrs<InT> &r
     x.tr[i] = rp.has_tr ? x.tr[i] : 0u;
     x.te[i] = rp.has_te ? x.te[i] : 0u;
   }
+}
+
+// Decode an issued tile and issue its sparse bootstrap loads.
+template <int A, typename InT, int K>
+__device__ __forceinline__ void finish_tile(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
+                                            Tile<K> &x) {
+  decode_tile<A, InT, K>(rp, x);
   sparse_tv<A, InT, K>(p, rp, t0, x);
 }
 
-// The ragged last tile of a row.  A lane whose K steps all lie in the row
-// (lim >= K) loads them as in a whole tile; the lane holding the row's end
-// loads the steps e < lim one by one; lanes past the end load nothing.
+// Move a lane's per-step values d steps down (x[j] <- x[j + d], zero past the
+// end), d the same for every field of the lane.
+template <int N>
+__device__ __forceinline__ void shift_down(float (&x)[N], int d) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    float v = 0.f;
+#pragma unroll
+    for (int k = 1; j + k < N; ++k) v = d == k ? x[j + k] : v;
+    x[j] = d == 0 ? x[j] : v;
+  }
+}
+
+template <int K>
+__device__ __forceinline__ void shift_flags_down(uint32_t (&w)[K / 4], int d) {
+  uint32_t out[K / 4];
+#pragma unroll
+  for (int i = 0; i < K / 4; ++i) out[i] = 0u;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    uint32_t b = 0u;
+#pragma unroll
+    for (int k = 0; j + k < K; ++k) b = d == k ? (w[(j + k) >> 2] >> (((j + k) & 3) * 8)) & 0xffu : b;
+    out[j >> 2] |= b << ((j & 3) * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < K / 4; ++i) w[i] = out[i];
+}
+
+// The ragged last tile of a row.  Rows of at least K steps: every lane loads
+// K steps as in a whole tile, a lane whose span runs past the row's end the
+// row's last K steps [T - K, T), and then moves its values down so that slot
+// j holds step t0 + j (slots past the end are zero and masked later).  No
+// lane branches, so every load of the tile is in flight together.  Shorter
+// rows load the steps e < lim one by one.
 template <int A, typename InT, int K>
 __device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
-                                          int64_t lim, Tile<K> &x) {
-  if (lim >= K) {
-    issue_tile<A, InT, K>(p, rp, t0, lim, x);
-    finish_tile<A, InT, K>(p, rp, t0, x);
+                                          int64_t lim, int64_t T, Tile<K> &x) {
+  if (T >= K) {
+    const int64_t tb = t0 < T - K ? t0 : T - K;
+    const int d = static_cast<int>(t0 - tb < K ? t0 - tb : K);
+    issue_tile<A, InT, K>(p, rp, tb, T - tb, x);
+    decode_tile<A, InT, K>(rp, x);
+    shift_down(x.r, d);
+    shift_down(x.v, d);
+    shift_down(x.lr, d);
+    shift_down(x.eq, d);
+    shift_down(x.tv, d);
+    shift_flags_down<K>(x.te, d);
+    shift_flags_down<K>(x.tr, d);
+    sparse_tv<A, InT, K>(p, rp, t0, x);
     return;
   }
   using U = Uses<A>;
@@ -988,7 +1035,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
       const int64_t te0 = t0_of(ntiles - 1);
       const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
       Tile<K> x;
-      load_edge<A, InT, K>(p, rp, te0, lim, x);
+      load_edge<A, InT, K>(p, rp, te0, lim, T, x);
       if constexpr (kChunk) {
         if (nwhole == 0) win = window_in<A, InT>(p, rp, T, carry);
       }
@@ -1012,7 +1059,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     const int64_t te0 = t0_of(ntiles - 1);
     const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
     Tile<K> x;
-    load_edge<A, InT, K>(p, rp, te0, lim, x);
+    load_edge<A, InT, K>(p, rp, te0, lim, T, x);
     if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
     carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok,
                                                             ntiles - 1, c >= 0, lane, wave, carry,

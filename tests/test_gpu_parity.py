@@ -54,7 +54,10 @@ def test_workload_full_size(name):
 def variant_lengths(v, dtype="f32"):
     k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32)
     tile = k * lanes
-    return sorted({1, 2, 5, tile // 2 + 3, tile - 4, tile, tile + 4, 2 * tile + 12})
+    # every residue of T mod 4 (the lane holding a row's end has 1..3 steps),
+    # rows shorter than one lane's span, one tile, and several tiles
+    return sorted({1, 2, 3, 5, 6, 7, tile // 2 + 3, tile - 4, tile - 2, tile - 1, tile,
+                   tile + 1, tile + 4, 2 * tile + 12, 2 * tile + 14})
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])

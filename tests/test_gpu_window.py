@@ -133,7 +133,7 @@ def window_inputs(algo, N, T, seed, dtype, sparse):
 def variant_lengths(v):
     _, lanes, _ = rl.rlca_variant_info(v)
     tile = 4 * lanes
-    return sorted({1, tile - 3, tile, 2 * tile + 5})
+    return sorted({1, 3, 6, tile - 3, tile - 2, tile, 2 * tile + 5, 2 * tile + 7})
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
