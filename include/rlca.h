@@ -405,8 +405,10 @@ int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype,
  *   detected before launch and reads no memory outside the tables: its step
  *   and every earlier step of its row come out NaN (the scan cuts episodes
  *   by a zero factor, which does not stop a NaN), later steps are unaffected.
- * Each row is processed by one 256-thread workgroup, 1024 steps per tile;
- * the tiling controls do not apply (rlca_last_variant() reports -1).
+ * Rows of more than 256 steps are processed by one 256-thread workgroup
+ * each, 1024 steps per tile; shorter rows by one wavefront each, four rows
+ * per workgroup.  The tiling controls do not apply (rlca_last_variant()
+ * reports -1).
  */
 int rlca_retrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
                        const void *rewards, int64_t ld_rewards,

@@ -39,10 +39,11 @@ struct TableArgs {
 };
 
 constexpr int kProbsK = 4;
-constexpr int kProbsWaves = 4;                      // wavefronts per row (one row per block)
-constexpr int kProbsGroup = 64 * kProbsWaves;       // threads per row
-constexpr int kProbsTile = kProbsGroup * kProbsK;   // steps per tile
+constexpr int kProbsThreads = 256;                  // threads per workgroup
 constexpr int kProbsUnroll = 4;                     // table chunks in flight per thread
+// Two tilings: WPR = 4 wavefronts share one row (1024-step tiles, one row per
+// workgroup) for long rows; WPR = 1, one wavefront per row (256-step tiles,
+// four rows per workgroup) for rows of at most 256 steps.
 
 // Slice and entry of element e of a tile's table span (A entries per slice):
 // a float reciprocal estimate, corrected to the exact quotient.
@@ -67,7 +68,7 @@ __device__ __forceinline__ void slice_of(int64_t e, int64_t A, float inv_a, int 
 // with kSum, exp(this table's entry) times the second table's entry is added
 // into acc[slice - 1] (the expectation of the step before the slice), each
 // thread adding its runs of same-slice elements with one LDS atomic per run.
-template <typename InT, bool kOther, bool kSum>
+template <int kGroup, typename InT, bool kOther, bool kSum>
 __device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, int nsl,
                                               int64_t A, float inv_a, const int *acts,
                                               float *taken, float *taken_other, float *acc,
@@ -81,21 +82,22 @@ __device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, 
       if constexpr (kOther) taken_other[sl] = o;
     }
   };
-  for (int64_t i0 = tid; i0 < nvec; i0 += kProbsGroup * kProbsUnroll) {
+  for (int64_t i0 = tid; i0 < nvec; i0 += kGroup * kProbsUnroll) {
     float tv[kProbsUnroll][4], ov[kProbsUnroll][4];
 #pragma unroll
     for (int u = 0; u < kProbsUnroll; ++u) {
-      const int64_t idx = i0 + kProbsGroup * u < nvec ? i0 + kProbsGroup * u : i0;  // in range
+      const int64_t idx = i0 + kGroup * u < nvec ? i0 + kGroup * u : i0;  // in range
       Ld<InT>::template vec<4>(tab + 4 * idx, tv[u]);
       if constexpr (kOther) Ld<InT>::template vec<4>(other + 4 * idx, ov[u]);
     }
 #pragma unroll
     for (int u = 0; u < kProbsUnroll; ++u) {
-      if (i0 + kProbsGroup * u < nvec) {
+      if (i0 + kGroup * u < nvec) {
         int sl, a;
-        slice_of(4 * (i0 + kProbsGroup * u), A, inv_a, sl, a);
+        slice_of(4 * (i0 + kGroup * u), A, inv_a, sl, a);
         int cur = sl;
         float run = 0.f;
+        int act = acts[sl];  // the current slice's taken action, read once per slice
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           if constexpr (kSum) {
@@ -106,10 +108,14 @@ __device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, 
             }
             run = fmaf(__expf(tv[u][k]), ov[u][k], run);
           }
-          take(sl, a, tv[u][k], kOther ? ov[u][k] : 0.f);
+          if (a == act) {
+            taken[sl] = tv[u][k];
+            if constexpr (kOther) taken_other[sl] = ov[u][k];
+          }
           if (++a == A) {
             a = 0;
             ++sl;
+            if (k < 3) act = acts[sl];
           }
         }
         if constexpr (kSum) {
@@ -118,7 +124,7 @@ __device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, 
       }
     }
   }
-  for (int64_t e = 4 * nvec + tid; e < nel; e += kProbsGroup) {
+  for (int64_t e = 4 * nvec + tid; e < nel; e += kGroup) {
     int sl, a;
     slice_of(e, A, inv_a, sl, a);
     const float v = Ld<InT>::one(tab + e);
@@ -131,28 +137,39 @@ __device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, 
   }
 }
 
-template <int Algo, typename InT>
-__global__ void __launch_bounds__(kProbsGroup)
+template <int Algo, typename InT, int WPR>
+__global__ void __launch_bounds__(kProbsThreads)
 probs_kernel(const Args p, const TableArgs ta) {
   static_assert(Algo == kRetrace || Algo == kVtrace, "policy tables: Retrace or V-trace");
+  static_assert(WPR == 1 || WPR == 4, "one or four wavefronts per row");
   constexpr int K = kProbsK;
-  constexpr int kTile = kProbsTile;
-  constexpr int WPR = kProbsWaves;
-  // Per tile slice (slot kTile: the slice after the tile): the expectation,
-  // the taken q, log_pi and log_mu, and the action.
-  __shared__ float s_eq[kTile + 1];
-  __shared__ float s_qt[kTile + 1];
-  __shared__ float s_lp[kTile + 1];
-  __shared__ float s_lm[kTile + 1];
-  __shared__ int s_act[kTile + 1];
+  constexpr int kGroup = 64 * WPR;            // threads per row
+  constexpr int kTile = kGroup * K;           // steps per tile
+  constexpr int kRows = kProbsThreads / kGroup;  // rows per workgroup
+  // Per row and tile slice (slot kTile: the slice after the tile): the
+  // expectation, the taken q, log_pi and log_mu, and the action.
+  __shared__ float s_eq_all[kRows][kTile + 1];
+  __shared__ float s_qt_all[kRows][kTile + 1];
+  __shared__ float s_lp_all[kRows][kTile + 1];
+  __shared__ float s_lm_all[kRows][kTile + 1];
+  __shared__ int s_act_all[kRows][kTile + 1];
   __shared__ float2 s_agg[2][WPR];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int64_t T = p.T, A = ta.A;
-  const int64_t rr = blockIdx.x;  // one row per workgroup; the grid is N
-  const bool row_ok = true;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int tid = WPR > 1 ? static_cast<int>(threadIdx.x) : lane;  // thread within the row
+  const int slot = WPR > 1 ? 0 : wave;                               // the row's LDS arrays
+  float *s_eq = s_eq_all[slot];
+  float *s_qt = s_qt_all[slot];
+  float *s_lp = s_lp_all[slot];
+  float *s_lm = s_lm_all[slot];
+  int *s_act = s_act_all[slot];
+  const int64_t N = p.N, T = p.T, A = ta.A;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kRows + (WPR > 1 ? 0 : wave);
+  // Rows past N (last workgroup) read row 0 and store nothing; they take part
+  // in every barrier.
+  const bool row_ok = row < N;
+  const int64_t rr = row_ok ? row : 0;
 
   RowPtrs<InT> rp;
   rp.row = rr;
@@ -172,7 +189,7 @@ probs_kernel(const Args p, const TableArgs ta) {
   const float inv_a = 1.f / static_cast<float>(A);
 
   const int64_t ntiles = (T + kTile - 1) / kTile;
-  const int lane_off = (kProbsGroup - 1 - tid) * K;  // reverse: thread 0 owns the latest steps
+  const int lane_off = (kGroup - 1 - tid) * K;  // reverse: thread 0 owns the latest steps
   float carry = 0.f;
   CarryMap m{0.f, 1.f};
   const WindowIn win{0.f, false};
@@ -180,14 +197,14 @@ probs_kernel(const Args p, const TableArgs ta) {
   for (int64_t c = ntiles - 1; c >= 0; --c) {
     const int64_t ts = c * kTile;
     const int64_t t0 = ts + lane_off;
-    const int64_t lim = T - t0 > 0 ? T - t0 : 0;
+    const int64_t lim = row_ok ? (T - t0 > 0 ? T - t0 : 0) : 0;
     const bool whole = ts + kTile <= T;
     // Slices of the tile (Retrace: and the slice after it, at most slice T).
     const int nsteps = static_cast<int>(T - ts < kTile ? T - ts : kTile);
     const int nsl = Algo == kRetrace ? nsteps + 1 : nsteps;
 
     __syncthreads();  // the previous tile's reads of the LDS arrays are done
-    for (int i = tid; i < nsl; i += kProbsGroup) {
+    for (int i = tid; i < nsl; i += kGroup) {
       const int64_t t = ts + i;
       s_act[i] = t < T ? act_row[t] : -1;
       s_eq[i] = 0.f;
@@ -197,20 +214,20 @@ probs_kernel(const Args p, const TableArgs ta) {
     }
     __syncthreads();
     if constexpr (Algo == kRetrace) {
-      stream_slices<InT, true, true>(lpi_row + ts * A, q_row + ts * A, nsl, A, inv_a, s_act,
+      stream_slices<kGroup, InT, true, true>(lpi_row + ts * A, q_row + ts * A, nsl, A, inv_a, s_act,
                                      s_lp, s_qt, s_eq, tid);
       // A log_mu table: its slices below T (the slice after the window has
       // no action).
       const int nsl_mu = static_cast<int>(T - ts < nsl ? T - ts : nsl);
       if (!ta.mu_taken)
-        stream_slices<InT, false, false>(lmu_row + ts * A, nullptr, nsl_mu, A, inv_a, s_act,
+        stream_slices<kGroup, InT, false, false>(lmu_row + ts * A, nullptr, nsl_mu, A, inv_a, s_act,
                                          s_lm, nullptr, nullptr, tid);
     } else {
       if (ta.mu_taken)
-        stream_slices<InT, false, false>(lpi_row + ts * A, nullptr, nsl, A, inv_a, s_act, s_lp,
+        stream_slices<kGroup, InT, false, false>(lpi_row + ts * A, nullptr, nsl, A, inv_a, s_act, s_lp,
                                          nullptr, nullptr, tid);
       else
-        stream_slices<InT, true, false>(lpi_row + ts * A, lmu_row + ts * A, nsl, A, inv_a, s_act,
+        stream_slices<kGroup, InT, true, false>(lpi_row + ts * A, lmu_row + ts * A, nsl, A, inv_a, s_act,
                                         s_lp, s_lm, nullptr, tid);
     }
     __syncthreads();

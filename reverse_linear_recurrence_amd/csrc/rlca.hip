@@ -244,15 +244,18 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const 
   return launch(algo, dtype, a, stream, w.on);
 }
 
-// The policy-table kernels: one tiling (a 256-thread workgroup per row),
+// The policy-table kernels: a 256-thread workgroup per row for long rows,
+// one wavefront per row (four per workgroup) for rows of at most 256 steps;
 // arguments by value.
 int launch_probs(int algo, int dtype, const Args &args, const TableArgs &tables, void *stream) {
-  const void *kernel = probs_kernel_for(algo, dtype);
+  const int wpr = args.T <= kProbsShortRow ? 1 : 4;
+  const void *kernel = probs_kernel_for(algo, dtype, wpr);
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no policy-table kernel for algorithm %d", algo);
   Args a = args;
   TableArgs ta = tables;
-  const dim3 grid(static_cast<unsigned>(a.N));
-  const dim3 block(kProbsThreads);
+  const int64_t rows_per_block = 4 / wpr;
+  const dim3 grid(static_cast<unsigned>((a.N + rows_per_block - 1) / rows_per_block));
+  const dim3 block(kProbsBlock);
   void *kargs[] = {&a, &ta};
   const hipError_t e =
       hipLaunchKernel(kernel, grid, block, kargs, 0, static_cast<hipStream_t>(stream));

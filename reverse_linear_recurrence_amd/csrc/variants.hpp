@@ -39,9 +39,11 @@ inline int64_t tile_steps(const Variant &v) {
 // window_kernel: carry vector in, carry and carry map out (every Algo).
 const void *plain_kernel(int algo, int dtype, int variant, bool uniform);
 const void *window_kernel(int algo, int dtype, int variant, bool uniform);
-// The policy-table kernels (Retrace, V-trace): one tiling, one row per
-// 256-thread workgroup.
-const void *probs_kernel_for(int algo, int dtype);
-constexpr int kProbsThreads = 256;
+// The policy-table kernels (Retrace, V-trace), 256-thread workgroups: 4
+// wavefronts per row (1024-step tiles, one row per workgroup) or 1 (256-step
+// tiles, four rows per workgroup).
+const void *probs_kernel_for(int algo, int dtype, int waves_per_row);
+constexpr int kProbsBlock = 256;
+constexpr int64_t kProbsShortRow = 256;  // rows up to this long: one wavefront each
 
 }  // namespace rlca
