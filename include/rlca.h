@@ -2,11 +2,14 @@
  * rlca.h -- reverse linear recurrences for RL credit assignment on AMD
  * Instinct MI355X (gfx950).  C ABI of librlca.so.
  *
- * Every entry point evaluates one reverse-time first-order affine recurrence
+ * Every entry point evaluates one first-order affine recurrence, in reverse
+ * time
  *
  *     A_t = alpha_t + beta_t * A_{t+1},      t = T-1 ... 0,           (R)
  *
- * independently for each of num_envs rows, as stated in the rl-triton
+ * (the forward-time mirrors and the generic scan also run it forward,
+ * A_t = alpha_t + beta_t * A_{t-1}), independently for each of num_envs rows,
+ * as stated in the rl-triton
  * explainer pages ("rl-triton: High-Performance Triton GPU Kernels for
  * Reinforcement Learning Credit Assignment", Zehnder 2026; Technical summary,
  * Method 1, "Unified algebraic framework").  The GPU evaluates (R) as an
@@ -42,8 +45,11 @@
  *   affect any output; the others may hold anything, NaN included.  Small
  *   batches read it in full, large ones only at truncated steps.
  * dtype.  RLCA_F32 or RLCA_BF16 gives the type of EVERY floating-point input
- *   of the call (rewards, values, trunc_values, log_rhos, q_taken,
- *   exp_q_next, bootstrap).  Arithmetic is fp32; outputs are always fp32.
+ *   array of the call (rewards, values, trunc_values, log_rhos, q_taken,
+ *   exp_q_next, bootstrap, z_init, s_init, x, alpha, beta, q_values, log_pi,
+ *   log_mu, trunc_eq), except the window calls' carry vectors, which are
+ *   always fp32.  Arithmetic is fp32; outputs are always fp32.  Actions are
+ *   int32.
  * Ownership.  The caller owns every buffer.  The library allocates no
  *   memory, keeps no per-call state, never synchronizes, and returns as soon
  *   as the work is enqueued on `stream`.
