@@ -442,6 +442,40 @@ int rlca_vtrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dtyp
                       float *pg_advantages, int64_t ld_pg_advantages,
                       void *stream);
 
+/*
+ * Window forms of the two policy-table calls: the arguments of
+ * rlca_retrace_probs / rlca_vtrace_probs followed by carry_in, carry_out and
+ * carry_map, with the meanings of the window entry points above (Retrace:
+ * c_T (q_ret_T - q_taken_T); V-trace: vs_T - V_T).
+ */
+int rlca_retrace_probs_chunk(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                             const void *rewards, int64_t ld_rewards,
+                             const void *q_values, int64_t ld_q_values,
+                             const int32_t *actions, int64_t ld_actions,
+                             const void *log_pi, int64_t ld_log_pi,
+                             const void *log_mu, int64_t ld_log_mu, int log_mu_taken,
+                             const uint8_t *terminated, int64_t ld_terminated,
+                             const uint8_t *truncated, int64_t ld_truncated,
+                             const void *trunc_eq, int64_t ld_trunc_eq,
+                             float gamma, float lam, float c_bar,
+                             float *q_ret, int64_t ld_q_ret,
+                             const float *carry_in, float *carry_out, float *carry_map,
+                             void *stream);
+int rlca_vtrace_probs_chunk(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                            const void *rewards, int64_t ld_rewards,
+                            const void *values, int64_t ld_values,
+                            const int32_t *actions, int64_t ld_actions,
+                            const void *log_pi, int64_t ld_log_pi,
+                            const void *log_mu, int64_t ld_log_mu, int log_mu_taken,
+                            const uint8_t *terminated, int64_t ld_terminated,
+                            const uint8_t *truncated, int64_t ld_truncated,
+                            const void *trunc_values, int64_t ld_trunc_values,
+                            float gamma, float lam, float rho_bar, float c_bar, float pg_rho_bar,
+                            float *vs, int64_t ld_vs,
+                            float *pg_advantages, int64_t ld_pg_advantages,
+                            const float *carry_in, float *carry_out, float *carry_map,
+                            void *stream);
+
 /* Message for the calling thread's last non-OK status ("" if none). */
 const char *rlca_last_error(void);
 

@@ -39,6 +39,7 @@ from ._binding import (  # noqa: F401
     rlca_retrace,
     rlca_retrace_chunk,
     rlca_retrace_probs,
+    rlca_retrace_probs_chunk,
     rlca_returns,
     rlca_returns_chunk,
     rlca_set_variant,
@@ -49,4 +50,5 @@ from ._binding import (  # noqa: F401
     rlca_vtrace,
     rlca_vtrace_chunk,
     rlca_vtrace_probs,
+    rlca_vtrace_probs_chunk,
 )

@@ -62,6 +62,13 @@ _SIGNATURES = {
     "rlca_vtrace_probs": [_i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                           _vp, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f32, _f32, _f32,
                           _f32, _f32, _vp, _i64, _vp, _i64, _vp],
+    "rlca_retrace_probs_chunk": [_i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                 _i64, _vp, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f32,
+                                 _f32, _f32, _vp, _i64, _vp, _vp, _vp, _vp],
+    "rlca_vtrace_probs_chunk": [_i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                                _i64, _vp, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f32,
+                                _f32, _f32, _f32, _f32, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
+                                _vp],
     "rlca_last_error": [],
     "rlca_version": [],
     "rlca_num_variants": [],
@@ -603,6 +610,68 @@ def rlca_vtrace_probs(rewards, values, actions, log_pi, log_mu, terminated=None,
                                             gamma, lam, rho_bar, c_bar, pg_rho_bar, o, ld_o, pg,
                                             ld_pg, _stream(stream, dev)))
     return vs, pg_advantages
+
+
+def rlca_retrace_probs_chunk(rewards, q_values, actions, log_pi, log_mu, terminated=None,
+                             truncated=None, trunc_eq=None, *, gamma, lam=1.0, c_bar=1.0,
+                             carry_in=None, out=None, carry_out=None, carry_map=None,
+                             with_carry_out=True, with_map=True, stream=None):
+    """Window of rlca_retrace_probs: ``(q_ret, carry_out, carry_map)``; the
+    carry is c_t (q_ret_t - q_taken_t) (carry_in at step T, carry_out at 0)."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    if not isinstance(q_values, torch.Tensor) or q_values.dim() != 3:
+        raise ValueError("q_values must be a 3-D tensor [N, T+1, A]")
+    A = q_values.shape[2]
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    q, ld_q = _table("q_values", q_values, dt, N, T + 1, A, dev)
+    ac, ld_ac = _actions(actions, N, T, dev)
+    lp, ld_lp = _table("log_pi", log_pi, dt, N, T + 1, A, dev)
+    lm, ld_lm, mu_taken = _log_mu(log_mu, dt, N, T, A, dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    teq, ld_teq = _float_input("trunc_eq", trunc_eq, dt, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    out, o, ld_o = _output("q_ret", out, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_retrace_probs_chunk(
+        N, T, A, code, r, ld_r, q, ld_q, ac, ld_ac, lp, ld_lp, lm, ld_lm, mu_taken, te, ld_te,
+        tr, ld_tr, teq, ld_teq, gamma, lam, c_bar, o, ld_o, ci, co_p, cm_p,
+        _stream(stream, dev)))
+    return out, co, cm
+
+
+def rlca_vtrace_probs_chunk(rewards, values, actions, log_pi, log_mu, terminated=None,
+                            truncated=None, trunc_values=None, *, gamma, lam=1.0, rho_bar=1.0,
+                            c_bar=1.0, pg_rho_bar=1.0, carry_in=None, vs=None,
+                            pg_advantages=None, with_pg=True, carry_out=None, carry_map=None,
+                            with_carry_out=True, with_map=True, stream=None):
+    """Window of rlca_vtrace_probs: ``(vs, pg_advantages, carry_out, carry_map)``;
+    the carry is vs - V (carry_in at step T, carry_out at step 0)."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    if not isinstance(log_pi, torch.Tensor) or log_pi.dim() != 3:
+        raise ValueError("log_pi must be a 3-D tensor [N, T, A]")
+    A = log_pi.shape[2]
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    ac, ld_ac = _actions(actions, N, T, dev)
+    lp, ld_lp = _table("log_pi", log_pi, dt, N, T, A, dev)
+    lm, ld_lm, mu_taken = _log_mu(log_mu, dt, N, T, A, dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    vs, o, ld_o = _output("vs", vs, (N, T), dev)
+    pg, ld_pg = None, 0
+    if with_pg or pg_advantages is not None:
+        pg_advantages, pg, ld_pg = _output("pg_advantages", pg_advantages, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_vtrace_probs_chunk(
+        N, T, A, code, r, ld_r, v, ld_v, ac, ld_ac, lp, ld_lp, lm, ld_lm, mu_taken, te, ld_te,
+        tr, ld_tr, tv, ld_tv, gamma, lam, rho_bar, c_bar, pg_rho_bar, o, ld_o, pg, ld_pg, ci,
+        co_p, cm_p, _stream(stream, dev)))
+    return vs, pg_advantages, co, cm
 
 
 def rlca_version():

@@ -137,7 +137,9 @@ __device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, 
   }
 }
 
-template <int Algo, typename InT, int WPR>
+// kChunk: window instance (carry vector in; carry and carry map out, as in
+// scan_kernel).
+template <int Algo, typename InT, int WPR, bool kChunk>
 __global__ void __launch_bounds__(kProbsThreads)
 probs_kernel(const Args p, const TableArgs ta) {
   static_assert(Algo == kRetrace || Algo == kVtrace, "policy tables: Retrace or V-trace");
@@ -191,8 +193,14 @@ probs_kernel(const Args p, const TableArgs ta) {
   const int64_t ntiles = (T + kTile - 1) / kTile;
   const int lane_off = (kGroup - 1 - tid) * K;  // reverse: thread 0 owns the latest steps
   float carry = 0.f;
+  if constexpr (kChunk) {
+    if (p.cin != nullptr) carry = p.cin[rr];
+  }
   CarryMap m{0.f, 1.f};
-  const WindowIn win{0.f, false};
+  WindowIn win{0.f, false};
+  // The window results come from the row's last thread in scan order, which
+  // owns the row's first steps (its log_rho_0 gives Retrace's c_0).
+  const bool write_window = kChunk && row_ok && tid == kGroup - 1;
 
   for (int64_t c = ntiles - 1; c >= 0; --c) {
     const int64_t ts = c * kTile;
@@ -313,14 +321,17 @@ probs_kernel(const Args p, const TableArgs ta) {
     }
     if constexpr (Algo == kVtrace) sparse_tv<kVtrace, InT, K>(p, rp, t0, x);
 
+    if constexpr (kChunk && Algo == kRetrace) {
+      if (c == 0) win.lr0 = x.lr[0];
+    }
     if (whole) {
-      carry = tile_compute<Algo, InT, K, 64, WPR, false, false>(p, rp, x, t0, T - t0, row_ok, c,
-                                                                c > 0, lane, wave, carry, s_agg,
-                                                                m, win, false);
+      carry = tile_compute<Algo, InT, K, 64, WPR, false, kChunk>(p, rp, x, t0, T - t0, row_ok, c,
+                                                                 c > 0, lane, wave, carry, s_agg,
+                                                                 m, win, write_window);
     } else {
-      carry = tile_compute<Algo, InT, K, 64, WPR, true, false>(p, rp, x, t0, lim, row_ok, c,
-                                                               c > 0, lane, wave, carry, s_agg, m,
-                                                               win, false);
+      carry = tile_compute<Algo, InT, K, 64, WPR, true, kChunk>(p, rp, x, t0, lim, row_ok, c,
+                                                                c > 0, lane, wave, carry, s_agg, m,
+                                                                win, write_window);
     }
   }
 }

@@ -226,15 +226,22 @@ struct Window {
 };
 constexpr Window kNoWindow{false, nullptr, nullptr, nullptr};
 
-// Validate the arrays of a call (plus the window's carry vectors), then fill
-// the window fields of Args and launch.  arrs has room for n + 3 entries.
-int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const Window &w,
-                        Args &a, void *stream) {
+// Append the window's carry vectors to a call's arrays (arrs has room for
+// n + 3 entries); returns the new count.
+int add_window(Arr *arrs, int n, const Window &w, int64_t N) {
   if (w.on) {
     arrs[n++] = Arr{"carry_in", w.cin, N, N, 4, false, false, true};
     arrs[n++] = Arr{"carry_out", w.cout, N, N, 4, false, true, true};
     arrs[n++] = Arr{"carry_map", w.cmap, 2 * N, 2 * N, 4, false, true, true};
   }
+  return n;
+}
+
+// Validate the arrays of a call (plus the window's carry vectors), then fill
+// the window fields of Args and launch.  arrs has room for n + 3 entries.
+int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const Window &w,
+                        Args &a, void *stream) {
+  n = add_window(arrs, n, w, N);
   if (N == 0 || a.T == 0) return RLCA_OK;
   for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], N));
   RLCA_TRY(check_aliasing(arrs, n));
@@ -247,9 +254,10 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const 
 // The policy-table kernels: a 256-thread workgroup per row for long rows,
 // one wavefront per row (four per workgroup) for rows of at most 256 steps;
 // arguments by value.
-int launch_probs(int algo, int dtype, const Args &args, const TableArgs &tables, void *stream) {
+int launch_probs(int algo, int dtype, const Args &args, const TableArgs &tables, void *stream,
+                 bool window) {
   const int wpr = args.T <= kProbsShortRow ? 1 : 4;
-  const void *kernel = probs_kernel_for(algo, dtype, wpr);
+  const void *kernel = probs_kernel_for(algo, dtype, wpr, window);
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no policy-table kernel for algorithm %d", algo);
   Args a = args;
   TableArgs ta = tables;
@@ -439,6 +447,121 @@ int forward_like(int algo, int64_t num_envs, int64_t T, int dtype, const void *x
   a.o0 = out; a.ld_o0 = ld_out;
   a.gamma = gamma; a.lam = lam; a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
   return validate_and_launch(algo, dtype, num_envs, arrs, 5, w, a, stream);
+}
+
+int retrace_probs_impl(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                       const void *rewards, int64_t ld_rewards, const void *q_values,
+                       int64_t ld_q_values, const int32_t *actions, int64_t ld_actions,
+                       const void *log_pi, int64_t ld_log_pi, const void *log_mu,
+                       int64_t ld_log_mu, int log_mu_taken, const uint8_t *terminated,
+                       int64_t ld_terminated, const uint8_t *truncated, int64_t ld_truncated,
+                       const void *trunc_eq,
+                       int64_t ld_trunc_eq, float gamma, float lam, float c_bar, float *q_ret,
+                       int64_t ld_q_ret, const Window &w, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_actions(num_actions));
+  if (log_mu_taken != 0 && log_mu_taken != 1)
+    return fail(RLCA_EINVAL, "log_mu_taken = %d must be 0 or 1", log_mu_taken);
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  RLCA_TRY(check_clip("c_bar", c_bar));
+  if (truncated != nullptr && trunc_eq == nullptr)
+    return fail(RLCA_EINVAL, "truncated is given but trunc_eq is NULL");
+  const int64_t es = esize_of(dtype);
+  const int64_t A = num_actions;
+  Arr arrs[12] = {
+      {"rewards", rewards, ld_rewards, T, es, true, false},
+      {"q_values", q_values, ld_q_values, (T + 1) * A, es, true, false},
+      {"actions", actions, ld_actions, T, 4, true, false},
+      {"log_pi", log_pi, ld_log_pi, (T + 1) * A, es, true, false},
+      {"log_mu", log_mu, ld_log_mu, log_mu_taken ? T : T * A, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {"trunc_eq", truncated != nullptr ? trunc_eq : nullptr, ld_trunc_eq, T, es, false, false},
+      {"q_ret", q_ret, ld_q_ret, T, 4, true, true},
+  };
+  const int n = add_window(arrs, 9, w, num_envs);
+  if (num_envs == 0 || T == 0) return RLCA_OK;
+  for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], num_envs));
+  RLCA_TRY(check_aliasing(arrs, n));
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = rewards; a.ld_r = ld_rewards;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = q_ret; a.ld_o0 = ld_q_ret;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = 1.f; a.c_bar = c_bar; a.pg_rho_bar = 1.f;
+  TableArgs ta{};
+  ta.A = A;
+  ta.q = q_values; ta.ld_q = ld_q_values;
+  ta.act = actions; ta.ld_act = ld_actions;
+  ta.lpi = log_pi; ta.ld_lpi = ld_log_pi;
+  ta.lmu = log_mu; ta.ld_lmu = ld_log_mu;
+  ta.mu_taken = log_mu_taken;
+  ta.teq = truncated != nullptr ? trunc_eq : nullptr; ta.ld_teq = ld_trunc_eq;
+  a.cin = w.cin; a.cout = w.cout; a.cmap = w.cmap;
+  return launch_probs(kRetrace, dtype, a, ta, stream, w.on);
+}
+
+int vtrace_probs_impl(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                      const void *rewards, int64_t ld_rewards, const void *values,
+                      int64_t ld_values, const int32_t *actions, int64_t ld_actions,
+                      const void *log_pi, int64_t ld_log_pi, const void *log_mu,
+                      int64_t ld_log_mu, int log_mu_taken, const uint8_t *terminated,
+                      int64_t ld_terminated, const uint8_t *truncated, int64_t ld_truncated,
+                      const void *trunc_values,
+                      int64_t ld_trunc_values, float gamma, float lam, float rho_bar,
+                      float c_bar, float pg_rho_bar, float *vs, int64_t ld_vs,
+                      float *pg_advantages, int64_t ld_pg_advantages, const Window &w,
+                      void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  RLCA_TRY(check_actions(num_actions));
+  if (log_mu_taken != 0 && log_mu_taken != 1)
+    return fail(RLCA_EINVAL, "log_mu_taken = %d must be 0 or 1", log_mu_taken);
+  RLCA_TRY(check_unit("gamma", gamma));
+  RLCA_TRY(check_unit("lam", lam));
+  RLCA_TRY(check_clip("rho_bar", rho_bar));
+  RLCA_TRY(check_clip("c_bar", c_bar));
+  RLCA_TRY(check_clip("pg_rho_bar", pg_rho_bar));
+  if (truncated != nullptr && trunc_values == nullptr)
+    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
+  const int64_t es = esize_of(dtype);
+  const int64_t A = num_actions;
+  const bool tv_used = truncated != nullptr;
+  Arr arrs[13] = {
+      {"rewards", rewards, ld_rewards, T, es, true, false},
+      {"values", values, ld_values, T + 1, es, true, false},
+      {"actions", actions, ld_actions, T, 4, true, false},
+      {"log_pi", log_pi, ld_log_pi, T * A, es, true, false},
+      {"log_mu", log_mu, ld_log_mu, log_mu_taken ? T : T * A, es, true, false},
+      {"terminated", terminated, ld_terminated, T, 1, false, false},
+      {"truncated", truncated, ld_truncated, T, 1, false, false},
+      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
+      {"vs", vs, ld_vs, T, 4, true, true},
+      {"pg_advantages", pg_advantages, ld_pg_advantages, T, 4, false, true},
+  };
+  const int n = add_window(arrs, 10, w, num_envs);
+  if (num_envs == 0 || T == 0) return RLCA_OK;
+  for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], num_envs));
+  RLCA_TRY(check_aliasing(arrs, n));
+  Args a{};
+  a.N = num_envs; a.T = T;
+  a.r = rewards; a.ld_r = ld_rewards;
+  a.v = values; a.ld_v = ld_values;
+  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
+  a.term = terminated; a.ld_term = ld_terminated;
+  a.trunc = truncated; a.ld_trunc = ld_truncated;
+  a.o0 = vs; a.ld_o0 = ld_vs;
+  a.o1 = pg_advantages; a.ld_o1 = ld_pg_advantages;
+  a.gamma = gamma; a.lam = lam; a.rho_bar = rho_bar; a.c_bar = c_bar; a.pg_rho_bar = pg_rho_bar;
+  TableArgs ta{};
+  ta.A = A;
+  ta.act = actions; ta.ld_act = ld_actions;
+  ta.lpi = log_pi; ta.ld_lpi = ld_log_pi;
+  ta.lmu = log_mu; ta.ld_lmu = ld_log_mu;
+  ta.mu_taken = log_mu_taken;
+  a.cin = w.cin; a.cout = w.cout; a.cmap = w.cmap;
+  return launch_probs(kVtrace, dtype, a, ta, stream, w.on);
 }
 
 }  // namespace
@@ -649,50 +772,13 @@ int rlca_retrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dty
                        const void *log_pi, int64_t ld_log_pi, const void *log_mu,
                        int64_t ld_log_mu, int log_mu_taken, const uint8_t *terminated,
                        int64_t ld_terminated, const uint8_t *truncated, int64_t ld_truncated,
-                       const void *trunc_eq,
-                       int64_t ld_trunc_eq, float gamma, float lam, float c_bar, float *q_ret,
-                       int64_t ld_q_ret, void *stream) {
-  RLCA_TRY(check_sizes(num_envs, T, dtype));
-  RLCA_TRY(check_actions(num_actions));
-  if (log_mu_taken != 0 && log_mu_taken != 1)
-    return fail(RLCA_EINVAL, "log_mu_taken = %d must be 0 or 1", log_mu_taken);
-  RLCA_TRY(check_unit("gamma", gamma));
-  RLCA_TRY(check_unit("lam", lam));
-  RLCA_TRY(check_clip("c_bar", c_bar));
-  if (truncated != nullptr && trunc_eq == nullptr)
-    return fail(RLCA_EINVAL, "truncated is given but trunc_eq is NULL");
-  const int64_t es = esize_of(dtype);
-  const int64_t A = num_actions;
-  Arr arrs[] = {
-      {"rewards", rewards, ld_rewards, T, es, true, false},
-      {"q_values", q_values, ld_q_values, (T + 1) * A, es, true, false},
-      {"actions", actions, ld_actions, T, 4, true, false},
-      {"log_pi", log_pi, ld_log_pi, (T + 1) * A, es, true, false},
-      {"log_mu", log_mu, ld_log_mu, log_mu_taken ? T : T * A, es, true, false},
-      {"terminated", terminated, ld_terminated, T, 1, false, false},
-      {"truncated", truncated, ld_truncated, T, 1, false, false},
-      {"trunc_eq", truncated != nullptr ? trunc_eq : nullptr, ld_trunc_eq, T, es, false, false},
-      {"q_ret", q_ret, ld_q_ret, T, 4, true, true},
-  };
-  if (num_envs == 0 || T == 0) return RLCA_OK;
-  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
-  RLCA_TRY(check_aliasing(arrs, 9));
-  Args a{};
-  a.N = num_envs; a.T = T;
-  a.r = rewards; a.ld_r = ld_rewards;
-  a.term = terminated; a.ld_term = ld_terminated;
-  a.trunc = truncated; a.ld_trunc = ld_truncated;
-  a.o0 = q_ret; a.ld_o0 = ld_q_ret;
-  a.gamma = gamma; a.lam = lam; a.rho_bar = 1.f; a.c_bar = c_bar; a.pg_rho_bar = 1.f;
-  TableArgs ta{};
-  ta.A = A;
-  ta.q = q_values; ta.ld_q = ld_q_values;
-  ta.act = actions; ta.ld_act = ld_actions;
-  ta.lpi = log_pi; ta.ld_lpi = ld_log_pi;
-  ta.lmu = log_mu; ta.ld_lmu = ld_log_mu;
-  ta.mu_taken = log_mu_taken;
-  ta.teq = truncated != nullptr ? trunc_eq : nullptr; ta.ld_teq = ld_trunc_eq;
-  return launch_probs(kRetrace, dtype, a, ta, stream);
+                       const void *trunc_eq, int64_t ld_trunc_eq, float gamma, float lam,
+                       float c_bar, float *q_ret, int64_t ld_q_ret, void *stream) {
+  return retrace_probs_impl(num_envs, T, num_actions, dtype, rewards, ld_rewards, q_values,
+                            ld_q_values, actions, ld_actions, log_pi, ld_log_pi, log_mu,
+                            ld_log_mu, log_mu_taken, terminated, ld_terminated, truncated,
+                            ld_truncated, trunc_eq, ld_trunc_eq, gamma, lam, c_bar, q_ret,
+                            ld_q_ret, kNoWindow, stream);
 }
 
 int rlca_vtrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
@@ -701,56 +787,51 @@ int rlca_vtrace_probs(int64_t num_envs, int64_t T, int64_t num_actions, int dtyp
                       const void *log_pi, int64_t ld_log_pi, const void *log_mu,
                       int64_t ld_log_mu, int log_mu_taken, const uint8_t *terminated,
                       int64_t ld_terminated, const uint8_t *truncated, int64_t ld_truncated,
-                      const void *trunc_values,
-                      int64_t ld_trunc_values, float gamma, float lam, float rho_bar,
-                      float c_bar, float pg_rho_bar, float *vs, int64_t ld_vs,
+                      const void *trunc_values, int64_t ld_trunc_values, float gamma, float lam,
+                      float rho_bar, float c_bar, float pg_rho_bar, float *vs, int64_t ld_vs,
                       float *pg_advantages, int64_t ld_pg_advantages, void *stream) {
-  RLCA_TRY(check_sizes(num_envs, T, dtype));
-  RLCA_TRY(check_actions(num_actions));
-  if (log_mu_taken != 0 && log_mu_taken != 1)
-    return fail(RLCA_EINVAL, "log_mu_taken = %d must be 0 or 1", log_mu_taken);
-  RLCA_TRY(check_unit("gamma", gamma));
-  RLCA_TRY(check_unit("lam", lam));
-  RLCA_TRY(check_clip("rho_bar", rho_bar));
-  RLCA_TRY(check_clip("c_bar", c_bar));
-  RLCA_TRY(check_clip("pg_rho_bar", pg_rho_bar));
-  if (truncated != nullptr && trunc_values == nullptr)
-    return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
-  const int64_t es = esize_of(dtype);
-  const int64_t A = num_actions;
-  const bool tv_used = truncated != nullptr;
-  Arr arrs[] = {
-      {"rewards", rewards, ld_rewards, T, es, true, false},
-      {"values", values, ld_values, T + 1, es, true, false},
-      {"actions", actions, ld_actions, T, 4, true, false},
-      {"log_pi", log_pi, ld_log_pi, T * A, es, true, false},
-      {"log_mu", log_mu, ld_log_mu, log_mu_taken ? T : T * A, es, true, false},
-      {"terminated", terminated, ld_terminated, T, 1, false, false},
-      {"truncated", truncated, ld_truncated, T, 1, false, false},
-      {"trunc_values", tv_used ? trunc_values : nullptr, ld_trunc_values, T, es, false, false},
-      {"vs", vs, ld_vs, T, 4, true, true},
-      {"pg_advantages", pg_advantages, ld_pg_advantages, T, 4, false, true},
-  };
-  if (num_envs == 0 || T == 0) return RLCA_OK;
-  for (Arr &a : arrs) RLCA_TRY(check_array(a, num_envs));
-  RLCA_TRY(check_aliasing(arrs, 10));
-  Args a{};
-  a.N = num_envs; a.T = T;
-  a.r = rewards; a.ld_r = ld_rewards;
-  a.v = values; a.ld_v = ld_values;
-  a.tv = tv_used ? trunc_values : nullptr; a.ld_tv = ld_trunc_values;
-  a.term = terminated; a.ld_term = ld_terminated;
-  a.trunc = truncated; a.ld_trunc = ld_truncated;
-  a.o0 = vs; a.ld_o0 = ld_vs;
-  a.o1 = pg_advantages; a.ld_o1 = ld_pg_advantages;
-  a.gamma = gamma; a.lam = lam; a.rho_bar = rho_bar; a.c_bar = c_bar; a.pg_rho_bar = pg_rho_bar;
-  TableArgs ta{};
-  ta.A = A;
-  ta.act = actions; ta.ld_act = ld_actions;
-  ta.lpi = log_pi; ta.ld_lpi = ld_log_pi;
-  ta.lmu = log_mu; ta.ld_lmu = ld_log_mu;
-  ta.mu_taken = log_mu_taken;
-  return launch_probs(kVtrace, dtype, a, ta, stream);
+  return vtrace_probs_impl(num_envs, T, num_actions, dtype, rewards, ld_rewards, values, ld_values,
+                           actions, ld_actions, log_pi, ld_log_pi, log_mu, ld_log_mu,
+                           log_mu_taken, terminated, ld_terminated, truncated, ld_truncated,
+                           trunc_values, ld_trunc_values, gamma, lam, rho_bar, c_bar, pg_rho_bar,
+                           vs, ld_vs, pg_advantages, ld_pg_advantages, kNoWindow, stream);
+}
+
+int rlca_retrace_probs_chunk(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                             const void *rewards, int64_t ld_rewards, const void *q_values,
+                             int64_t ld_q_values, const int32_t *actions, int64_t ld_actions,
+                             const void *log_pi, int64_t ld_log_pi, const void *log_mu,
+                             int64_t ld_log_mu, int log_mu_taken, const uint8_t *terminated,
+                             int64_t ld_terminated, const uint8_t *truncated,
+                             int64_t ld_truncated, const void *trunc_eq, int64_t ld_trunc_eq,
+                             float gamma, float lam, float c_bar, float *q_ret,
+                             int64_t ld_q_ret, const float *carry_in, float *carry_out,
+                             float *carry_map, void *stream) {
+  return retrace_probs_impl(num_envs, T, num_actions, dtype, rewards, ld_rewards, q_values,
+                            ld_q_values, actions, ld_actions, log_pi, ld_log_pi, log_mu,
+                            ld_log_mu, log_mu_taken, terminated, ld_terminated, truncated,
+                            ld_truncated, trunc_eq, ld_trunc_eq, gamma, lam, c_bar, q_ret,
+                            ld_q_ret, Window{true, carry_in, carry_out, carry_map}, stream);
+}
+
+int rlca_vtrace_probs_chunk(int64_t num_envs, int64_t T, int64_t num_actions, int dtype,
+                            const void *rewards, int64_t ld_rewards, const void *values,
+                            int64_t ld_values, const int32_t *actions, int64_t ld_actions,
+                            const void *log_pi, int64_t ld_log_pi, const void *log_mu,
+                            int64_t ld_log_mu, int log_mu_taken, const uint8_t *terminated,
+                            int64_t ld_terminated, const uint8_t *truncated,
+                            int64_t ld_truncated, const void *trunc_values,
+                            int64_t ld_trunc_values, float gamma, float lam, float rho_bar,
+                            float c_bar, float pg_rho_bar, float *vs, int64_t ld_vs,
+                            float *pg_advantages, int64_t ld_pg_advantages,
+                            const float *carry_in, float *carry_out, float *carry_map,
+                            void *stream) {
+  return vtrace_probs_impl(num_envs, T, num_actions, dtype, rewards, ld_rewards, values, ld_values,
+                           actions, ld_actions, log_pi, ld_log_pi, log_mu, ld_log_mu,
+                           log_mu_taken, terminated, ld_terminated, truncated, ld_truncated,
+                           trunc_values, ld_trunc_values, gamma, lam, rho_bar, c_bar, pg_rho_bar,
+                           vs, ld_vs, pg_advantages, ld_pg_advantages,
+                           Window{true, carry_in, carry_out, carry_map}, stream);
 }
 
 const char *rlca_last_error(void) { return t_last_error.c_str(); }

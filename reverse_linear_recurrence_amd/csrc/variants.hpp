@@ -42,7 +42,7 @@ const void *window_kernel(int algo, int dtype, int variant, bool uniform);
 // The policy-table kernels (Retrace, V-trace), 256-thread workgroups: 4
 // wavefronts per row (1024-step tiles, one row per workgroup) or 1 (256-step
 // tiles, four rows per workgroup).
-const void *probs_kernel_for(int algo, int dtype, int waves_per_row);
+const void *probs_kernel_for(int algo, int dtype, int waves_per_row, bool window);
 constexpr int kProbsBlock = 256;
 constexpr int64_t kProbsShortRow = 256;  // rows up to this long: one wavefront each
 

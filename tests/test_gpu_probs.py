@@ -183,3 +183,79 @@ def test_policy_table_calls_in_a_hip_graph():
         torch.cuda.synchronize()
         assert float((q_out - e[0]).abs().max()) <= 1e-5 * float(e[0].abs().max())
         assert torch.equal(vs_out, e[1]) and torch.equal(pg_out, e[2])
+
+
+def _slice_tables(d, lo, hi, algo):
+    out = {}
+    for k, v in d.items():
+        if k in ("q_values",) or (k == "log_pi" and algo == "retrace_probs") or k == "values":
+            out[k] = v[:, lo:hi + 1]
+        else:
+            out[k] = v[:, lo:hi]
+    return out
+
+
+def gpu_window(algo, d, carry, **kw):
+    g = lambda k: None if d.get(k) is None else d[k].cuda()
+    c = None if carry is None else carry.cuda()
+    if algo == "retrace_probs":
+        q, co, cm = rl.rlca_retrace_probs_chunk(g("rewards"), g("q_values"), g("actions"),
+                                                g("log_pi"), g("log_mu"), g("terminated"),
+                                                g("truncated"), g("trunc_eq"), carry_in=c, **RP,
+                                                **kw)
+        outs = (q,)
+    else:
+        vs, pg, co, cm = rl.rlca_vtrace_probs_chunk(g("rewards"), g("values"), g("actions"),
+                                                    g("log_pi"), g("log_mu"), g("terminated"),
+                                                    g("truncated"), g("trunc_values"), carry_in=c,
+                                                    **VP, **kw)
+        outs = (vs, pg)
+    torch.cuda.synchronize()
+    return [o.double().cpu().numpy() for o in outs], co, cm
+
+
+@pytest.mark.parametrize("algo", ["retrace_probs", "vtrace_probs"])
+@pytest.mark.parametrize("N,T,A", [(5, 7, 3), (6, 300, 18), (3, 1500, 5)])
+def test_policy_table_windows_match_the_oracle_window_forms(algo, N, T, A):
+    d = make_tables(algo, N, T, A, seed=N + T + A, p_term=0.005, p_trunc=0.005,
+                    mu_taken=(T % 2 == 0))
+    c = torch.from_numpy(np.random.Generator(np.random.PCG64(T)).standard_normal(N)
+                         .astype(np.float32))
+    outs, co, cm = gpu_window(algo, d, c)
+    if algo == "retrace_probs":
+        q, rco, rcm = oracle.retrace_probs(d["rewards"], d["q_values"], d["actions"],
+                                           d["log_pi"], d["log_mu"], d["terminated"],
+                                           d["truncated"], d["trunc_eq"], carry_in=c, chunk=True,
+                                           **RP)
+        refs = (q,)
+    else:
+        vs, pg, rco, rcm = oracle.vtrace_probs(d["rewards"], d["values"], d["actions"],
+                                               d["log_pi"], d["log_mu"], d["terminated"],
+                                               d["truncated"], d["trunc_values"], carry_in=c,
+                                               chunk=True, **VP)
+        refs = (vs, pg)
+    for a, b in zip(outs, refs):
+        assert rel_err(a, b) <= TOL["f32"]
+    assert rel_err(co.double().cpu().numpy(), rco) <= TOL["f32"]
+    assert rel_err(cm[:, 0].double().cpu().numpy(), rcm[:, 0]) <= TOL["f32"]
+    eb = np.max(np.abs(cm[:, 1].double().cpu().numpy() - rcm[:, 1])) / max(
+        np.max(np.abs(rcm[:, 1])), 1e-3)
+    assert eb <= 1e-4
+
+
+@pytest.mark.parametrize("algo", ["retrace_probs", "vtrace_probs"])
+def test_policy_table_windows_chain_like_one_window(algo):
+    N, T, A = 7, 1300, 9
+    d = make_tables(algo, N, T, A, seed=77, p_term=0.002, p_trunc=0.002)
+    whole = gpu_retrace(d) if algo == "retrace_probs" else gpu_vtrace(d)
+    whole = whole if isinstance(whole, tuple) else (whole,)
+    cuts = [0, 200, 1100, 1300]
+    carry = None
+    pieces = {}
+    for lo, hi in reversed(list(zip(cuts[:-1], cuts[1:]))):
+        outs, co, _ = gpu_window(algo, _slice_tables(d, lo, hi, algo), carry, with_map=False)
+        carry = co.cpu()
+        pieces[lo] = outs
+    for j, w in enumerate(whole):
+        got = np.concatenate([pieces[lo][j] for lo in cuts[:-1]], axis=1)
+        assert rel_err(got, w) <= TOL["f32"], (algo, j, rel_err(got, w))
