@@ -46,55 +46,154 @@ constexpr int kProbsUnroll = 4;                     // table chunks in flight pe
 // four rows per workgroup) for rows of at most 256 steps.
 
 // Slice and entry of element e of a tile's table span (A entries per slice):
-// a float reciprocal estimate, corrected to the exact quotient.
-__device__ __forceinline__ void slice_of(int64_t e, int64_t A, float inv_a, int &sl, int &a) {
-  int q = static_cast<int>((static_cast<float>(e) + 0.5f) * inv_a);
-  int r = static_cast<int>(e - static_cast<int64_t>(q) * A);
-  if (r < 0) {
-    --q;
-    r += static_cast<int>(A);
-  } else if (r >= A) {
-    ++q;
-    r -= static_cast<int>(A);
-  }
-  sl = q;
-  a = r;
+// a float reciprocal estimate, corrected to the exact quotient.  A span holds
+// at most 1025 slices of at most 65536 entries, so e fits in 32 bits; the
+// estimate is within one of the quotient.
+__device__ __forceinline__ void slice_of(int e, int A, float inv_a, int &sl, int &a) {
+  const int q = static_cast<int>((static_cast<float>(e) + 0.5f) * inv_a);
+  const int r = e - q * A;
+  const bool lo = r < 0, hi = r >= A;
+  sl = lo ? q - 1 : (hi ? q + 1 : q);
+  a = lo ? r + A : (hi ? r - A : r);
 }
 
-// Stream slices [0, nsl) of one table row span (tile-relative), A entries
-// each, with the whole workgroup; kOther: a second table over the same span
-// alongside.  Every element whose entry is the slice's taken action is
-// stored to taken[slice] (and the second table's to taken_other[slice]);
-// with kSum, exp(this table's entry) times the second table's entry is added
-// into acc[slice - 1] (the expectation of the step before the slice), each
-// thread adding its runs of same-slice elements with one LDS atomic per run.
-template <int kGroup, typename InT, bool kOther, bool kSum>
-__device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, int nsl,
-                                              int64_t A, float inv_a, const int *acts,
-                                              float *taken, float *taken_other, float *acc,
-                                              int tid) {
-  static_assert(kOther || !kSum, "the sum needs the second table");
-  const int64_t nel = static_cast<int64_t>(nsl) * A;
-  const int64_t nvec = nel / 4;
-  auto take = [&](int sl, int a, float v, float o) {
-    if (a == acts[sl]) {
-      taken[sl] = v;
-      if constexpr (kOther) taken_other[sl] = o;
-    }
+// Entry k (0..3) of a chunk of four, k a run-time value, as a select chain.
+__device__ __forceinline__ float pick4(float v0, float v1, float v2, float v3, int k) {
+  float r = v0;
+  r = k == 1 ? v1 : r;
+  r = k == 2 ? v2 : r;
+  r = k == 3 ? v3 : r;
+  return r;
+}
+
+// Pass four register values through an empty asm.  The compiler then treats
+// them as opaque, so select chains over them stay selects: otherwise a chain
+// indexed by a run-time value can become an indexed load from a private
+// array, which lives in scratch memory.
+__device__ __forceinline__ void opaque4(float &v0, float &v1, float &v2, float &v3) {
+  asm("" : "+v"(v0), "+v"(v1), "+v"(v2), "+v"(v3));
+}
+
+// DPP row_shr:D within 16-lane rows: lane l of a row gets lane l - D's
+// value, lanes without a source get `old`.
+template <int D>
+__device__ __forceinline__ float row_shr(float src, float old) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src),
+                                                     0x110 + D, 0xf, 0xf, false));
+}
+template <int D>
+__device__ __forceinline__ int row_shr(int src, int old) {
+  return __builtin_amdgcn_update_dpp(old, src, 0x110 + D, 0xf, 0xf, false);
+}
+
+// One level of the segmented inclusive sum within 16-lane rows: slices never
+// decrease across lanes, so a lane D below with the same slice heads a run of
+// lanes that all share it.
+template <int D>
+__device__ __forceinline__ void seg_level(float &run, int key) {
+  const float v = row_shr<D>(run, 0.f);
+  const int k = row_shr<D>(key, -1);
+  run = k == key ? run + v : run;
+}
+
+// The vector part of stream_slices: chunks of four consecutive elements.
+// Each thread keeps kProbsUnroll chunks in flight: as soon as it has used a
+// chunk it issues the load of the chunk one round later into the same
+// registers (past the end, a re-read of chunk 0, unused).  Rounds are counted
+// per wavefront, so every lane of a wavefront runs every round (lanes past
+// the end with nothing to add).
+//
+// kWide (A >= 4): a chunk holds the end of at most one slice, so it is handled
+// without branches per element: the slice sl of its first entry a0 covers
+// entries k < A - a0 and slice sl + 1 the rest; each slice's taken entry sits
+// at a known position in the chunk (or outside it).  With kSum, a lane's part
+// of slice sl + 1 moves to the next lane (which starts in that slice), the
+// parts of each slice are summed across the lanes of a 16-lane row (DPP), and
+// only the row's last lane of each slice adds into LDS: adjacent lanes share
+// slices, and LDS atomics on one address serialize.  Otherwise (A < 4) the
+// chunk walks its elements one by one with one LDS atomic per run.
+template <int kGroup, typename InT, bool kOther, bool kSum, bool kWide>
+__device__ __forceinline__ void stream_chunks(const InT *tab, const InT *other, int nvec, int A,
+                                              float inv_a, const int *acts, float *taken,
+                                              float *taken_other, float *acc, int tid) {
+  if (nvec == 0) return;
+  constexpr int kRound = kGroup * kProbsUnroll;  // chunks per round of the workgroup
+  const int lane = tid & 63;
+  const bool row_end = (lane & 15) == 15;
+  float tv[kProbsUnroll][4], ov[kProbsUnroll][4] = {};  // ov: the second table (kOther)
+  auto issue = [&](int u, int c) {
+    const int idx = c < nvec ? c : 0;  // in range
+    Ld<InT>::template vec<4>(tab + 4 * static_cast<int64_t>(idx), tv[u]);
+    if constexpr (kOther) Ld<InT>::template vec<4>(other + 4 * static_cast<int64_t>(idx), ov[u]);
   };
-  for (int64_t i0 = tid; i0 < nvec; i0 += kGroup * kProbsUnroll) {
-    float tv[kProbsUnroll][4], ov[kProbsUnroll][4];
+#pragma unroll
+  for (int u = 0; u < kProbsUnroll; ++u) issue(u, tid + kGroup * u);
+  for (int i0 = tid; i0 - lane < nvec; i0 += kRound) {
 #pragma unroll
     for (int u = 0; u < kProbsUnroll; ++u) {
-      const int64_t idx = i0 + kGroup * u < nvec ? i0 + kGroup * u : i0;  // in range
-      Ld<InT>::template vec<4>(tab + 4 * idx, tv[u]);
-      if constexpr (kOther) Ld<InT>::template vec<4>(other + 4 * idx, ov[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < kProbsUnroll; ++u) {
-      if (i0 + kGroup * u < nvec) {
+      const int c = i0 + kGroup * u;
+      const bool live = c < nvec;
+      if constexpr (kWide) {
+        int sl = -1, split = 4;
+        float run0 = 0.f, run1 = 0.f;
+        if (live) {
+          int a;
+          slice_of(4 * c, A, inv_a, sl, a);
+          float t0 = tv[u][0], t1 = tv[u][1], t2 = tv[u][2], t3 = tv[u][3];
+          float o0 = ov[u][0], o1 = ov[u][1], o2 = ov[u][2], o3 = ov[u][3];
+          opaque4(t0, t1, t2, t3);
+          if constexpr (kOther) opaque4(o0, o1, o2, o3);
+          split = A - a;               // entries k < split belong to slice sl
+          const bool two = split < 4;  // slice sl + 1 starts inside the chunk
+          // Position in the chunk of each slice's taken entry; an action
+          // outside [0, A) lands outside the slice's range and stores nothing.
+          const int k0 = acts[sl] - a;
+          int k1 = 4;
+          if (two) k1 = split + acts[sl + 1];
+          if (k0 >= 0 && k0 < split && k0 < 4) {
+            taken[sl] = pick4(t0, t1, t2, t3, k0);
+            if constexpr (kOther) taken_other[sl] = pick4(o0, o1, o2, o3, k0);
+          }
+          if (k1 >= split && k1 < 4) {
+            taken[sl + 1] = pick4(t0, t1, t2, t3, k1);
+            if constexpr (kOther) taken_other[sl + 1] = pick4(o0, o1, o2, o3, k1);
+          }
+          if constexpr (kSum) {
+            // Each slice's part summed in element order.
+            auto add = [&](float t, float o, int k) {
+              const float e = __expf(t);
+              const float f0 = fmaf(e, o, run0);
+              const float f1 = fmaf(e, o, run1);
+              const bool first = k < split;
+              run0 = first ? f0 : run0;
+              run1 = first ? run1 : f1;
+            };
+            add(t0, o0, 0);
+            add(t1, o1, 1);
+            add(t2, o2, 2);
+            add(t3, o3, 3);
+          }
+        }
+        if constexpr (kSum) {
+          // Every lane of the wavefront is active here.  A lane whose chunk
+          // ends inside slice sl + 1 hands that part to the next lane, which
+          // starts in slice sl + 1, unless the next lane is in the next row
+          // or past the end.
+          const bool next_live = c + 1 < nvec;
+          const bool keep1 = split < 4 && (row_end || !next_live);
+          run0 += row_shr<1>(split < 4 ? run1 : 0.f, 0.f);
+          if (A + 3 > 4) seg_level<1>(run0, sl);
+          if (A + 3 > 8) seg_level<2>(run0, sl);
+          if (A + 3 > 16) seg_level<4>(run0, sl);
+          if (A + 3 > 32) seg_level<8>(run0, sl);
+          // The last lane of its slice in the row adds the row's part.
+          const bool tail = live && (split <= 4 || row_end || !next_live);
+          if (tail && sl >= 1) atomicAdd(&acc[sl - 1], run0);
+          if (live && keep1) atomicAdd(&acc[sl], run1);
+        }
+      } else if (live) {
         int sl, a;
-        slice_of(4 * (i0 + kGroup * u), A, inv_a, sl, a);
+        slice_of(4 * c, A, inv_a, sl, a);
         int cur = sl;
         float run = 0.f;
         int act = acts[sl];  // the current slice's taken action, read once per slice
@@ -122,18 +221,46 @@ __device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, 
           if (cur >= 1) atomicAdd(&acc[cur - 1], run);
         }
       }
+      issue(u, c + kRound);
     }
   }
-  for (int64_t e = 4 * nvec + tid; e < nel; e += kGroup) {
+}
+
+// Stream slices [0, nsl) of one table row span (tile-relative), A entries
+// each, with the whole workgroup; kOther: a second table over the same span
+// alongside.  Every element whose entry is the slice's taken action is
+// stored to taken[slice] (and the second table's to taken_other[slice]);
+// with kSum, exp(this table's entry) times the second table's entry is added
+// into acc[slice - 1] (the expectation of the step before the slice), each
+// thread adding its runs of same-slice elements with one LDS atomic per run.
+template <int kGroup, typename InT, bool kOther, bool kSum>
+__device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, int nsl,
+                                              int64_t A, float inv_a, const int *acts,
+                                              float *taken, float *taken_other, float *acc,
+                                              int tid) {
+  static_assert(kOther || !kSum, "the sum needs the second table");
+  const int A32 = static_cast<int>(A);
+  const int nel = nsl * A32;  // at most 1025 * 65536 < 2^31
+  const int nvec = nel / 4;
+  if (A32 >= 4)
+    stream_chunks<kGroup, InT, kOther, kSum, true>(tab, other, nvec, A32, inv_a, acts, taken,
+                                                   taken_other, acc, tid);
+  else
+    stream_chunks<kGroup, InT, kOther, kSum, false>(tab, other, nvec, A32, inv_a, acts, taken,
+                                                    taken_other, acc, tid);
+  for (int e = 4 * nvec + tid; e < nel; e += kGroup) {
     int sl, a;
-    slice_of(e, A, inv_a, sl, a);
+    slice_of(e, A32, inv_a, sl, a);
     const float v = Ld<InT>::one(tab + e);
     float o = 0.f;
     if constexpr (kOther) o = Ld<InT>::one(other + e);
     if constexpr (kSum) {
       if (sl >= 1) atomicAdd(&acc[sl - 1], __expf(v) * o);
     }
-    take(sl, a, v, o);
+    if (a == acts[sl]) {
+      taken[sl] = v;
+      if constexpr (kOther) taken_other[sl] = o;
+    }
   }
 }
 

@@ -53,8 +53,9 @@ def ref_vtrace(d, **kw):
                                **dict(VP, **kw))
 
 
-CASES = [(1, 1, 1), (5, 7, 3), (9, 255, 18), (4, 256, 18), (6, 257, 18), (3, 700, 5),
-         (2, 1024, 18), (2, 1027, 18), (3, 2100, 4), (5, 300, 64), (2, 260, 257)]
+CASES = [(1, 1, 1), (7, 33, 2), (5, 7, 3), (11, 100, 4), (4, 129, 7), (9, 255, 18),
+         (4, 256, 18), (6, 257, 18), (3, 700, 5), (2, 1024, 18), (2, 1027, 18), (3, 2100, 4),
+         (5, 300, 64), (2, 260, 257)]
 
 
 @pytest.mark.parametrize("mu_taken", [False, True])
