@@ -15,9 +15,10 @@
 // the first, with the multi-wavefront scan of scan_kernels.hpp.  For each
 // tile the workgroup first streams the tables' slices with coalesced 16-byte
 // loads (thread i taking elements 4i .. 4i+3, 4(i+256) .., and so on), keeps
-// the taken action's entries in LDS and, for Retrace, adds each run of a
-// thread's elements that share a slice into that slice's LDS accumulator of
-// exp(log_pi) * q.  Streaming whole tables moves fewer bytes than gathering
+// the taken action's entries in LDS and, for Retrace, sums exp(log_pi) * q per
+// slice: each lane's parts are combined with its neighbours' across a 16-lane
+// row (DPP) and one lane per slice and row adds the result into that slice's
+// LDS accumulator.  Streaming whole tables moves fewer bytes than gathering
 // one entry per slice would, because every gathered entry costs a whole
 // memory line.  Each thread then reads its steps' quantities from LDS.
 #pragma once
@@ -40,7 +41,7 @@ struct TableArgs {
 
 constexpr int kProbsK = 4;
 constexpr int kProbsThreads = 256;                  // threads per workgroup
-constexpr int kProbsUnroll = 4;                     // table chunks in flight per thread
+constexpr int kProbsUnroll = 2;                     // table chunks in flight per thread
 // Two tilings: WPR = 4 wavefronts share one row (1024-step tiles, one row per
 // workgroup) for long rows; WPR = 1, one wavefront per row (256-step tiles,
 // four rows per workgroup) for rows of at most 256 steps.
