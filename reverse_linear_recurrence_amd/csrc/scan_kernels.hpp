@@ -173,15 +173,18 @@ template <> struct Ld<bf16_t> {
     uint32_t d[K / 2];
     ld_dwords<K / 2>(base, d);
     const uint32_t extra = base[K / 2 - 1 + odd];
+    // In the byte pair {dn : da} (da = dword e/2 in bytes 0-3, dn = the next
+    // dword in bytes 4-7), element e starts at byte 2 * ((e & 1) + odd).
+    // One v_perm_b32 moves its two bytes to the top half of the result and
+    // zeros the bottom half (selector byte 0x0c), which is the element as a
+    // float.
+    const uint32_t sel_even = odd ? 0x03020c0cu : 0x01000c0cu;
+    const uint32_t sel_odd = odd ? 0x05040c0cu : 0x03020c0cu;
 #pragma unroll
     for (int e = 0; e < K; ++e) {
-      // aligned: element e is half (e&1) of dword e/2;
-      // odd:     element e is half ((e+1)&1) of dword (e+1)/2.
       const uint32_t da = d[e / 2];
-      const uint32_t dn = (e + 1) / 2 < K / 2 ? d[(e + 1) / 2] : extra;
-      const float fa = (e & 1) ? bf16_hi(da) : bf16_lo(da);
-      const float fo = (e & 1) ? bf16_lo(dn) : bf16_hi(da);
-      x[e] = odd ? fo : fa;
+      const uint32_t dn = e / 2 + 1 < K / 2 ? d[e / 2 + 1] : extra;
+      x[e] = __uint_as_float(__builtin_amdgcn_perm(dn, da, (e & 1) ? sel_odd : sel_even));
     }
   }
   static __device__ __forceinline__ float one(const bf16_t *p) {
@@ -255,26 +258,31 @@ __device__ __forceinline__ float dpp(float src, float old) {
 
 // One Hillis-Steele level of the affine operator: this lane (earlier in time)
 // composes with the aggregate of a lower lane (later in time):
-//   (a, b) <- (a + b * a_src, b * b_src);  a missing source is the identity (0, 1).
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ void scan_level(float &a, float &b) {
-  const float a_src = dpp<CTRL, ROW_MASK>(a, 0.f);
-  const float b_src = dpp<CTRL, ROW_MASK>(b, 1.f);
-  a = fmaf(b, a_src, a);
-  b = b * b_src;
-}
+//   (a, b) <- (a + b * a_src, b * b_src).
+// Two DPP instructions: v_fmac_f32_dpp (a += a_src * b) and v_mul_f32_dpp
+// (b *= b_src).  Without bound_ctrl a lane whose source is outside its row
+// (or in a row the mask leaves out) is not written, which is exactly the
+// identity (0, 1).  The compiler's hazard check does not see into asm, so the
+// block starts with the two wait states a DPP read needs after a VALU write
+// of its source; the second DPP read (of b) follows its last write by three.
+#define RLCA_SCAN_LEVEL(a, b, CTRL, ROW_MASK)                                          \
+  asm("s_nop 1\n\t"                                                                \
+      "v_fmac_f32_dpp %0, %0, %1 " CTRL " row_mask:" ROW_MASK " bank_mask:0xf\n\t"   \
+      "v_mul_f32_dpp %1, %1, %1 " CTRL " row_mask:" ROW_MASK " bank_mask:0xf"          \
+      : "+v"(a), "+v"(b))
 
-// Inclusive scan over aligned groups of LANES lanes (16, 32 or 64): afterwards
-// lane i holds f_i o f_{i-1} o ... o f_{group start}.
+// Inclusive scan over aligned groups of LANES lanes (4, 8, 16, 32 or 64):
+// afterwards lane i holds f_i o f_{i-1} o ... o f_{group start}.
 template <int LANES>
 __device__ __forceinline__ void group_scan(float &a, float &b) {
-  static_assert(LANES == 16 || LANES == 32 || LANES == 64, "group of 16, 32 or 64 lanes");
-  scan_level<0x111, 0xf>(a, b);  // row_shr:1
-  scan_level<0x112, 0xf>(a, b);  // row_shr:2
-  scan_level<0x114, 0xf>(a, b);  // row_shr:4
-  scan_level<0x118, 0xf>(a, b);  // row_shr:8
-  if constexpr (LANES >= 32) scan_level<0x142, 0xa>(a, b);  // row_bcast:15 -> rows 1, 3
-  if constexpr (LANES >= 64) scan_level<0x143, 0xc>(a, b);  // row_bcast:31 -> rows 2, 3
+  static_assert(LANES == 4 || LANES == 8 || LANES == 16 || LANES == 32 || LANES == 64,
+                "group of 4, 8, 16, 32 or 64 lanes");
+  RLCA_SCAN_LEVEL(a, b, "row_shr:1", "0xf");
+  RLCA_SCAN_LEVEL(a, b, "row_shr:2", "0xf");
+  if constexpr (LANES >= 8) RLCA_SCAN_LEVEL(a, b, "row_shr:4", "0xf");
+  if constexpr (LANES >= 16) RLCA_SCAN_LEVEL(a, b, "row_shr:8", "0xf");
+  if constexpr (LANES >= 32) RLCA_SCAN_LEVEL(a, b, "row_bcast:15", "0xa");  // -> rows 1, 3
+  if constexpr (LANES >= 64) RLCA_SCAN_LEVEL(a, b, "row_bcast:31", "0xc");  // -> rows 2, 3
 }
 
 __device__ __forceinline__ float readlane(float x, int lane) {
@@ -751,18 +759,18 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
     __syncthreads();
     // Wavefront 0 holds the first span of the tile in scan order (reverse:
     // the latest steps; forward: the earliest): compose from it onward.
-    float xc = carry;
-    CarryMap tm{0.f, 1.f};  // the tile's composite
-#pragma unroll
-    for (int w = 0; w < WPR; ++w) {
-      if (w == wave) cin = xc;
-      const float2 ag = s_agg[buf][w];
-      xc = fmaf(ag.y, xc, ag.x);
-      if constexpr (kChunk) {
-        tm.a = fmaf(ag.y, tm.a, ag.x);
-        tm.b = ag.y * tm.b;
-      }
-    }
+    // Lane w < WPR of every wavefront takes wavefront w's map, and a scan
+    // over those lanes leaves in lane w the composite of wavefronts 0 .. w.
+    const float2 ag = lane < WPR ? s_agg[buf][lane] : make_float2(0.f, 1.f);
+    float sa = ag.x, sb = ag.y;
+    group_scan<WPR>(sa, sb);
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    const int wp = w > 0 ? w - 1 : 0;
+    const float pa = readlane(sa, wp), pb = readlane(sb, wp);  // wavefronts 0 .. w-1
+    if (w > 0) cin = fmaf(pb, carry, pa);
+    const float ta = readlane(sa, WPR - 1), tb = readlane(sb, WPR - 1);
+    const float xc = fmaf(tb, carry, ta);
+    CarryMap tm{ta, tb};  // the tile's composite
     carry_out = xc;
     if constexpr (kChunk) {
       m.a = fmaf(tm.b, m.a, tm.a);
