@@ -19,6 +19,7 @@ carry read, the outgoing carry and the carry map written) on the same inputs.
 """
 import argparse
 import hashlib
+import re
 import json
 import os
 import sys
@@ -47,11 +48,21 @@ def kernel_family(workload_key):
     return "probs" if "_probs_" in workload_key else "scan"
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_text(src):
+    """C++ source with comments removed and whitespace runs collapsed: what a
+    comment-only edit leaves unchanged.  (No kernel source puts // or /* in a
+    string literal.)"""
+    return " ".join(_COMMENT.sub(" ", src).split())
+
+
 def kernel_source_hash(family="scan"):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
-        with open(os.path.join(_CSRC, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(_CSRC, f), encoding="utf-8") as fh:
+            h.update(code_text(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -232,8 +232,9 @@ __device__ __forceinline__ void stream_chunks(const InT *tab, const InT *other, 
 // alongside.  Every element whose entry is the slice's taken action is
 // stored to taken[slice] (and the second table's to taken_other[slice]);
 // with kSum, exp(this table's entry) times the second table's entry is added
-// into acc[slice - 1] (the expectation of the step before the slice), each
-// thread adding its runs of same-slice elements with one LDS atomic per run.
+// into acc[slice - 1] (the expectation of the step before the slice); the
+// parts are combined across lanes first (stream_chunks), so that few LDS
+// atomics go out per slice.
 template <int kGroup, typename InT, bool kOther, bool kSum>
 __device__ __forceinline__ void stream_slices(const InT *tab, const InT *other, int nsl,
                                               int64_t A, float inv_a, const int *acts,

@@ -29,9 +29,10 @@
 //     bf16 and uint8 rows of any alignment are read as aligned dwords and
 //     realigned in registers), (alpha, beta) built in VGPRs, folded
 //     sequentially (K-1 FMAs), then log2(LPR) DPP levels of the operator
-//     across lanes, then (WPR > 1) one LDS exchange of per-wavefront
-//     aggregates.  Each lane then re-runs its K steps from its incoming value
-//     and writes the fused outputs with vector stores.
+//     across lanes (two DPP instructions each), then (WPR > 1) one LDS
+//     exchange of per-wavefront aggregates, scanned across lanes.  Each lane
+//     then re-runs its K steps from its incoming value and writes the fused
+//     outputs with vector stores.
 //   * HBM traffic is one read of every input element the method uses (plus
 //     the V_{t+1} / log_rho_{t+1} neighbour, which hits in cache) and one
 //     write of every output element.  No intermediate touches HBM.
