@@ -1,8 +1,8 @@
 """GPU parity: the HIP library against the fp64 oracle, element by element, on
 the same seeded inputs.  Covers the five measured workloads at full size (in
 the tiling the benchmark uses), every tiling variant on ragged lengths, the
-exhaustive boundary enumeration, strided and misaligned rows, empty inputs,
-and bitwise invariants (no leak across a boundary, window end, determinism,
+exhaustive boundary enumeration, strided and misaligned rows, rows that
+start past element 2^31 of their buffer, empty inputs, and bitwise invariants (no leak across a boundary, window end, determinism,
 row permutation, power-of-two scaling)."""
 import itertools
 
@@ -137,6 +137,44 @@ def test_strided_and_misaligned_rows(algo, dtype):
             print(algo, dtype, "T", T, "variant", v, flush=True)
             got = run_gpu(algo, strided, p)
             assert_close(got, ref, TOL[dtype], "%s/%s/T%d/v%s" % (algo, dtype, T, v))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ["gae", "vtrace"])
+def test_rows_past_element_2_to_the_31(algo, dtype):
+    # Row offsets need 64 bits: four rows 2^30 elements apart, so the last row
+    # starts at element 3 * 2^30.  Every 2-D input is a strided view into one
+    # of two large buffers (floats, flags) left uninitialized outside the
+    # rows; inputs sit at different offsets inside each row slot.  One tile
+    # per row (T = 128) and a ragged multi-tile row (T = 4100).
+    p = params32(DEFAULT_PARAMS)
+    N, LD = 4, 1 << 30
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for T in (128, 4100):
+        host = random_inputs(algo, N, T, 31 + T, dtype, p_term=0.01, p_trunc=0.01)
+        ref = run_oracle(algo, host, p)
+        two_d = {k: x for k, x in host.items() if x.dim() == 2}
+        offs, off_f, off_b = {}, 0, 0
+        for k, x in two_d.items():
+            if x.dtype == torch.uint8:
+                offs[k] = off_b + 1  # odd byte offsets: flag rows at every alignment
+                off_b += x.shape[1] + 64
+            else:
+                offs[k] = off_f + 1  # odd element offsets
+                off_f += x.shape[1] + 64
+        fbuf = torch.empty((N - 1) * LD + off_f + 8, dtype=tdt, device="cuda")
+        bbuf = torch.empty((N - 1) * LD + off_b + 8, dtype=torch.uint8, device="cuda")
+        dev = {}
+        for k, x in two_d.items():
+            buf = bbuf if x.dtype == torch.uint8 else fbuf
+            view = buf.as_strided((N, x.shape[1]), (LD, 1), offs[k])
+            view.copy_(x.cuda())
+            dev[k] = view
+        print(algo, dtype, "T", T, "last row at element", (N - 1) * LD, flush=True)
+        got = run_gpu(algo, dev, p)
+        del dev, fbuf, bbuf
+        torch.cuda.empty_cache()
+        assert_close(got, ref, TOL[dtype], "%s/%s/T%d" % (algo, dtype, T))
 
 
 def test_empty_and_nullable():
