@@ -4,8 +4,9 @@
 The tables are [N, T(+1), A] (rl-triton, Results: the heavier Retrace workload
 loads the action probabilities at every step).  Cases cover one to 257
 actions, row lengths around the 256-step tile, workgroups with rows past N,
-row strides larger than a row, both input dtypes, the full-size workload, and
-out-of-range actions (NaN at that step and every earlier step of the row).
+row strides larger than a row, table rows past element 2^31 of their buffer,
+both input dtypes, the full-size workload, and out-of-range actions (NaN at
+that step and every earlier step of the row).
 """
 import numpy as np
 import pytest
@@ -113,6 +114,42 @@ def test_strided_tables_and_rows(mu_taken):
         wide[k] = big[:, : v.shape[1]]
     assert wide["q_values"].stride(0) == (T + 4) * A
     assert rel_err(gpu_retrace(wide), ref) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ["retrace_probs", "vtrace_probs"])
+def test_table_rows_past_element_2_to_the_31(algo, dtype):
+    # Table row offsets need 64 bits: three rows 2^30 elements apart, so the
+    # last table row starts at element 2^31.  The tables are strided views
+    # into one large buffer, uninitialized outside the rows, each at its own
+    # odd offset inside a row slot.  Short rows (one wavefront per row) and
+    # long rows (one workgroup per row).
+    N, LD, A = 3, 1 << 30, 18
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for T in (100, 300):
+        d = make_tables(algo, N, T, A, seed=900 + T, dtype=dtype, p_term=0.01, p_trunc=0.01)
+        ref = ref_retrace(d) if algo == "retrace_probs" else ref_vtrace(d)
+        tables = {k: x for k, x in d.items() if x is not None and x.dim() == 3}
+        offs, off = {}, 0
+        for k, x in tables.items():
+            offs[k] = off + 1
+            off += x.shape[1] * x.shape[2] + 64
+        buf = torch.empty((N - 1) * LD + off + 8, dtype=tdt, device="cuda")
+        dev = {k: (None if x is None else x.cuda()) for k, x in d.items()}
+        for k, x in tables.items():
+            view = buf.as_strided(tuple(x.shape), (LD, x.shape[2], 1), offs[k])
+            view.copy_(x.cuda())
+            dev[k] = view
+        print(algo, dtype, "T", T, "last table row at element", (N - 1) * LD, flush=True)
+        if algo == "retrace_probs":
+            got = gpu_retrace(dev)
+            assert rel_err(got, ref) <= TOL[dtype], (algo, dtype, T, rel_err(got, ref))
+        else:
+            got = gpu_vtrace(dev)
+            for a, b in zip(got, ref):
+                assert rel_err(a, b) <= TOL[dtype], (algo, dtype, T, rel_err(a, b))
+        del dev, buf
+        torch.cuda.empty_cache()
 
 
 def test_out_of_range_action_gives_nan_where_it_reaches():
