@@ -264,3 +264,26 @@ def test_policy_table_entry_points_validate(lib):
     assert vt(ld_lp=39) == rl.RLCA_EINVAL and "ld_log_pi" in err(lib)
     assert vt(rho=0.0) == rl.RLCA_EINVAL and "rho_bar" in err(lib)
     assert vt(pg=ACT) == rl.RLCA_EALIAS and "actions" in err(lib)
+
+
+def test_policy_table_window_entry_points_validate(lib):
+    # The window forms check their per-row carry vectors like rlca_gae_chunk.
+    Q, ACT, LP, LM = (BASE + (12 + i) * 0x1000000 for i in range(4))
+    rpc = lambda **k: lib.rlca_retrace_probs_chunk(
+        k.get("N", 4), 8, 5, F32, R, 8, Q, 45, ACT, 8, LP, 45, LM, 40, 0, None, 8, None, 8,
+        None, 8, 0.9, 0.9, 1.0, ADV, 8, k.get("cin", C_IN), k.get("cout", C_OUT),
+        k.get("cmap", C_MAP), None)
+    assert rpc(N=0) == rl.RLCA_OK
+    assert rpc(cin=C_IN + 2) == rl.RLCA_EINVAL and "carry_in" in err(lib)
+    assert rpc(cout=C_OUT + 1) == rl.RLCA_EINVAL and "carry_out" in err(lib)
+    assert rpc(cout=C_IN) == rl.RLCA_EALIAS and "carry_in" in err(lib)
+    assert rpc(cmap=Q + 8) == rl.RLCA_EALIAS and "q_values" in err(lib)
+    assert rpc(cmap=ADV) == rl.RLCA_EALIAS
+    vtc = lambda **k: lib.rlca_vtrace_probs_chunk(
+        k.get("N", 4), 8, 5, F32, R, 8, V, 9, ACT, 8, LP, 40, LM, 40, 0, None, 8, None, 8,
+        None, 8, 0.9, 0.9, 1.0, 1.0, 1.0, ADV, 8, None, 8, k.get("cin", C_IN),
+        k.get("cout", C_OUT), k.get("cmap", C_MAP), None)
+    assert vtc(N=0) == rl.RLCA_OK
+    assert vtc(cmap=C_MAP + 2) == rl.RLCA_EINVAL and "carry_map" in err(lib)
+    assert vtc(cout=LP + 16) == rl.RLCA_EALIAS and "log_pi" in err(lib)
+    assert vtc(cmap=C_OUT) == rl.RLCA_EALIAS and "carry_out" in err(lib)
