@@ -330,6 +330,24 @@ def test_sparse_truncation_bootstraps_large_batch(algo):
         assert_close(run_gpu(algo, dev, p), ref, TOL["f32"], "%s/v%s" % (algo, v))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_many_workgroups_and_a_partial_last_one(algo, dtype):
+    # 20003 rows of exactly one tile, in each short-row tiling: thousands of
+    # workgroups (several rounds of the chip), the last with rows past N.
+    p = params32(DEFAULT_PARAMS)
+    N = 20003
+    for v in (0, 1, 2):
+        k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32)
+        T = k * lanes
+        host = random_inputs(algo, N, T, 7000 + v, dtype, p_term=0.01, p_trunc=0.01)
+        ref = run_oracle(algo, host, p)
+        rl.rlca_set_variant(v)
+        print(algo, dtype, "variant", v, "T", T, flush=True)
+        assert_close(run_gpu(algo, to_device(host), p), ref, TOL[dtype],
+                     "%s/%s/v%d" % (algo, dtype, v))
+
+
 def test_hip_graph_replay_matches_eager():
     # The benchmark replays captured launches; every replay, with eager work
     # and synchronizations in between, must equal the eager call bitwise, and
