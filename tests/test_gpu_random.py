@@ -1,7 +1,10 @@
-"""GPU parity on randomly drawn cases: algorithm, input dtype, N, T, tiling
-variant, row stride, start offset and boundary density, each checked element
-by element against the oracle.  The draws are derandomized (a fixed sequence
-of cases), so every run tests the same cases and a failure names its inputs.
+"""GPU parity on randomly drawn cases, each checked element by element against
+the oracle: the plain calls (algorithm, input dtype, N, T, tiling variant, row
+stride, start offset, boundary density), the window calls with a random
+carry_in, and the policy-table calls (A, row length on both sides of the
+256-step tiling switch, log_mu as table or taken entries).  The draws are
+derandomized (a fixed sequence of cases), so every run tests the same cases
+and a failure names its inputs.
 """
 import pytest
 import torch
@@ -55,3 +58,65 @@ def test_random_cases_match_the_oracle(case):
     finally:
         rl.rlca_set_variant(-1)
     assert_close(got, ref, TOL[case["dtype"]], str(case))
+
+
+WINDOW_CASE = st.fixed_dictionaries({
+    "algo": st.sampled_from(ALGOS),
+    "dtype": st.sampled_from(["f32", "bf16"]),
+    "N": st.integers(1, 30),
+    "T": st.one_of(st.integers(1, 70), st.integers(100, 300), st.integers(900, 2600)),
+    "variant": st.integers(-1, 5),
+    "sparse": st.booleans(),
+})
+
+
+@settings(max_examples=40, derandomize=True, deadline=None, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(case=WINDOW_CASE)
+def test_random_window_calls_match_the_oracle(case):
+    # The window form with a random carry_in: outputs, carry_out and map.
+    from test_gpu_window import check_window, run_gpu_chunk, run_oracle_chunk, window_inputs
+    p = params32(DEFAULT_PARAMS)
+    d, c = window_inputs(case["algo"], case["N"], case["T"], case["N"] * 31 + case["T"],
+                         case["dtype"], case["sparse"])
+    ref = run_oracle_chunk(case["algo"], d, p, c)
+    rl.rlca_set_variant(case["variant"])
+    try:
+        print("window case", case, flush=True)
+        got = run_gpu_chunk(case["algo"], {k: v.cuda() for k, v in d.items()}, p, c.cuda())
+    finally:
+        rl.rlca_set_variant(-1)
+    check_window(got, ref, case["dtype"], str(case))
+
+
+TABLE_CASE = st.fixed_dictionaries({
+    "algo": st.sampled_from(["retrace_probs", "vtrace_probs"]),
+    "dtype": st.sampled_from(["f32", "bf16"]),
+    "N": st.integers(1, 12),
+    # one wavefront per row up to 256 steps, one workgroup per row beyond
+    "T": st.one_of(st.integers(1, 40), st.integers(200, 300), st.integers(1000, 1100)),
+    "A": st.one_of(st.integers(1, 8), st.integers(9, 70)),
+    "mu_taken": st.booleans(),
+    "p_done": st.sampled_from([0.0, 0.01, 0.1]),
+})
+
+
+@settings(max_examples=40, derandomize=True, deadline=None, database=None,
+          suppress_health_check=[HealthCheck.too_slow])
+@given(case=TABLE_CASE)
+def test_random_policy_table_cases_match_the_oracle(case):
+    from test_gpu_probs import gpu_retrace, gpu_vtrace, ref_retrace, ref_vtrace
+    from gpu_common import rel_err
+    from reverse_linear_recurrence_amd.synth import make_tables
+    d = make_tables(case["algo"], case["N"], case["T"], case["A"],
+                    seed=case["N"] * 101 + case["T"] * 7 + case["A"], dtype=case["dtype"],
+                    p_term=case["p_done"], p_trunc=case["p_done"] or None,
+                    mu_taken=case["mu_taken"])
+    print("table case", case, flush=True)
+    tol = TOL[case["dtype"]]
+    if case["algo"] == "retrace_probs":
+        got, ref = gpu_retrace(d), ref_retrace(d)
+        assert rel_err(got, ref) <= tol, (case, rel_err(got, ref))
+    else:
+        for a, b in zip(gpu_vtrace(d), ref_vtrace(d)):
+            assert rel_err(a, b) <= tol, (case, rel_err(a, b))
