@@ -124,8 +124,8 @@ __device__ __forceinline__ void stream_chunks(const InT *tab, const InT *other, 
   float tv[kProbsUnroll][4], ov[kProbsUnroll][4] = {};  // ov: the second table (kOther)
   auto issue = [&](int u, int c) {
     const int idx = c < nvec ? c : 0;  // in range
-    Ld<InT>::template vec<4>(tab + 4 * static_cast<int64_t>(idx), tv[u]);
-    if constexpr (kOther) Ld<InT>::template vec<4>(other + 4 * static_cast<int64_t>(idx), ov[u]);
+    Ld<InT>::template vec<4, true>(tab + 4 * static_cast<int64_t>(idx), tv[u]);
+    if constexpr (kOther) Ld<InT>::template vec<4, true>(other + 4 * static_cast<int64_t>(idx), ov[u]);
   };
 #pragma unroll
   for (int u = 0; u < kProbsUnroll; ++u) issue(u, tid + kGroup * u);

@@ -126,19 +126,37 @@ struct __attribute__((aligned(4))) U2 { uint32_t x, y; };
 typedef float V4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // ND consecutive dwords from a 4-byte aligned address, as dwordx4/x2/x1 loads.
-template <int ND>
+// Vector types for the loads below (4-byte alignment is all they assume).
+typedef uint32_t NU4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t NU2 __attribute__((ext_vector_type(2), aligned(4)));
+typedef float NF4 __attribute__((ext_vector_type(4), aligned(4)));
+
+// kNT: non-temporal loads, for streams that nothing reads again (flags, the
+// truncation bootstraps, Retrace's expectations, the policy tables).  The
+// rewards, values and log-ratios stay ordinary loads: the step-(t0+K)
+// neighbour of values and log-ratios, and a missing flag array's stand-in
+// (the lane's own reward bytes), re-read lines they bring in, and measured
+// slower (TD(lambda) 16384x256 +5%) when those streams were non-temporal too.
+template <int ND, bool kNT = false>
 __device__ __forceinline__ void ld_dwords(const uint32_t *__restrict__ p, uint32_t (&d)[ND]) {
 #pragma unroll
   for (int i = 0; i + 4 <= ND; i += 4) {
-    U4 q = *reinterpret_cast<const U4 *>(p + i);
+    NU4 q;
+    if constexpr (kNT) q = __builtin_nontemporal_load(reinterpret_cast<const NU4 *>(p + i));
+    else q = *reinterpret_cast<const NU4 *>(p + i);
     d[i] = q.x; d[i + 1] = q.y; d[i + 2] = q.z; d[i + 3] = q.w;
   }
   constexpr int done4 = ND / 4 * 4;
   if constexpr (ND - done4 >= 2) {
-    U2 q = *reinterpret_cast<const U2 *>(p + done4);
+    NU2 q;
+    if constexpr (kNT) q = __builtin_nontemporal_load(reinterpret_cast<const NU2 *>(p + done4));
+    else q = *reinterpret_cast<const NU2 *>(p + done4);
     d[done4] = q.x; d[done4 + 1] = q.y;
   }
-  if constexpr ((ND - done4) % 2 == 1) d[ND - 1] = p[ND - 1];
+  if constexpr ((ND - done4) % 2 == 1) {
+    if constexpr (kNT) d[ND - 1] = __builtin_nontemporal_load(p + ND - 1);
+    else d[ND - 1] = p[ND - 1];
+  }
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -148,12 +166,14 @@ template <typename InT> struct Ld;
 
 template <> struct Ld<float> {
   // K consecutive values at p (K % 4 == 0; p 4-byte aligned): K/4 dwordx4.
-  template <int K>
+  template <int K, bool kNT = false>
   static __device__ __forceinline__ void vec(const float *__restrict__ p, float (&x)[K]) {
     static_assert(K % 4 == 0, "K must be a multiple of 4");
 #pragma unroll
     for (int i = 0; i < K / 4; ++i) {
-      F4 q = reinterpret_cast<const F4 *>(p)[i];
+      NF4 q;
+      if constexpr (kNT) q = __builtin_nontemporal_load(reinterpret_cast<const NF4 *>(p) + i);
+      else q = reinterpret_cast<const NF4 *>(p)[i];
       x[4 * i] = q.x; x[4 * i + 1] = q.y; x[4 * i + 2] = q.z; x[4 * i + 3] = q.w;
     }
   }
@@ -166,13 +186,13 @@ template <> struct Ld<bf16_t> {
   // the one holding p[K-1] when p is odd-aligned (it is then the dword after
   // the K/2), else the last of the K/2 again.  Every dword read holds a
   // requested element, and there is no branch.
-  template <int K>
+  template <int K, bool kNT = false>
   static __device__ __forceinline__ void vec(const bf16_t *__restrict__ p, float (&x)[K]) {
     static_assert(K % 4 == 0, "K must be a multiple of 4");
     const int odd = static_cast<int>((reinterpret_cast<uintptr_t>(p) >> 1) & 1);
     const uint32_t *base = reinterpret_cast<const uint32_t *>(p - odd);
     uint32_t d[K / 2];
-    ld_dwords<K / 2>(base, d);
+    ld_dwords<K / 2, kNT>(base, d);
     const uint32_t extra = base[K / 2 - 1 + odd];
     // In the byte pair {dn : da} (da = dword e/2 in bytes 0-3, dn = the next
     // dword in bytes 4-7), element e starts at byte 2 * ((e & 1) + odd).
@@ -210,7 +230,7 @@ __device__ __forceinline__ void ld_flags_raw(const uint8_t *__restrict__ p, Flag
   static_assert(K % 4 == 0, "K must be a multiple of 4");
   const int mis = static_cast<int>(reinterpret_cast<uintptr_t>(p) & 3);
   const uint32_t *base = reinterpret_cast<const uint32_t *>(p - mis);
-  ld_dwords<K / 4>(base, f.d);
+  ld_dwords<K / 4, true>(base, f.d);
   f.extra = base[K / 4 - 1 + (mis != 0)];
   f.sh = static_cast<uint32_t>(mis) * 8;
 }
@@ -416,7 +436,7 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
     for (int j = 0; j < K; ++j) q.v[j] = vk[j];
     if constexpr (U::values) q.v[K] = Ld<InT>::one(rp.v + t0 + K);  // V_{t0+K} (<= V_T)
   }
-  if constexpr (U::q) Ld<InT>::template vec<K>(rp.eq + t0, q.eq);
+  if constexpr (U::q) Ld<InT>::template vec<K, true>(rp.eq + t0, q.eq);
   if constexpr (U::log_rho) {
     float lk[K];
     Ld<InT>::template vec<K>(rp.lr + t0, lk);
@@ -436,7 +456,7 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
     // its own rewards (a cache hit, unused) and finish_tile reads the
     // bootstraps at truncated steps only.
     float tk[K];
-    Ld<InT>::template vec<K>(rp.dense_tv ? rp.tv + t0 : rp.r + t0, tk);
+    Ld<InT>::template vec<K, true>(rp.dense_tv ? rp.tv + t0 : rp.r + t0, tk);
 #pragma unroll
     for (int j = 0; j < K; ++j) q.tv[j] = tk[j];
     q.dense = rp.dense_tv;
