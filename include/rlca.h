@@ -395,7 +395,10 @@ int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype,
  *                  episode's first state: trunc_eq[t] (E_pi Q at the true final
  *                  state, supplied; read only there).
  * Everything else is as for rlca_retrace / rlca_vtrace (same outputs, same
- * boundary rules, same tolerances).
+ * boundary rules, same tolerances).  Determinism: V-trace is bit-reproducible
+ * run to run; Retrace's expectation is summed in an order that can vary
+ * between runs (on-chip atomic adds), so its outputs can differ in the last
+ * bits between otherwise identical calls.
  * Layout.  A table is row-major [num_envs, S, A] with S slices per row, A
  *   entries per slice contiguous; ld_* is the distance between rows in
  *   elements (>= S * A).  Retrace: q_values and log_pi have S = T + 1 (slice
