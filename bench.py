@@ -187,6 +187,26 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(out[meta["workload"]], indent=1))
 
 
+def host_threads():
+    """Host cores this process may run on, capped at 16 (one GPU's share)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def main():
     args = parse()
     if args.summarize_pmc:
@@ -480,52 +500,94 @@ def main():
         h64 = {k: (v.float().numpy().astype(np.float64) if v.is_floating_point() else v.numpy())
                for k, v in host.items()}
 
-        def oracle_step():
+        def oracle_step(h):
             if w.algo == "retrace_probs":
-                oracle.retrace_probs(h64["rewards"], h64["q_values"], h64["actions"],
-                                     h64["log_pi"], h64["log_mu"], h64["terminated"],
-                                     h64.get("truncated"), h64.get("trunc_eq"), gamma=gamma,
+                oracle.retrace_probs(h["rewards"], h["q_values"], h["actions"],
+                                     h["log_pi"], h["log_mu"], h["terminated"],
+                                     h.get("truncated"), h.get("trunc_eq"), gamma=gamma,
                                      lam=lam, **clips)
             elif w.algo == "vtrace_probs":
-                oracle.vtrace_probs(h64["rewards"], h64["values"], h64["actions"], h64["log_pi"],
-                                    h64["log_mu"], h64["terminated"], h64.get("truncated"),
-                                    h64.get("trunc_values"), gamma=gamma, lam=lam, **clips)
+                oracle.vtrace_probs(h["rewards"], h["values"], h["actions"], h["log_pi"],
+                                    h["log_mu"], h["terminated"], h.get("truncated"),
+                                    h.get("trunc_values"), gamma=gamma, lam=lam, **clips)
             elif w.algo == "gae":
-                oracle.gae(h64["rewards"], h64["values"], h64["terminated"],
-                           h64.get("truncated"), h64.get("trunc_values"), gamma=gamma, lam=lam)
+                oracle.gae(h["rewards"], h["values"], h["terminated"],
+                           h.get("truncated"), h.get("trunc_values"), gamma=gamma, lam=lam)
             elif w.algo == "td_lambda":
-                oracle.td_lambda(h64["rewards"], h64["values"], h64["terminated"],
-                                 h64.get("truncated"), h64.get("trunc_values"), gamma=gamma,
+                oracle.td_lambda(h["rewards"], h["values"], h["terminated"],
+                                 h.get("truncated"), h.get("trunc_values"), gamma=gamma,
                                  lam=lam)
             elif w.algo == "returns":
-                oracle.returns(h64["rewards"], h64["terminated"], gamma=gamma)
+                oracle.returns(h["rewards"], h["terminated"], gamma=gamma)
             elif w.algo == "eligibility":
-                oracle.eligibility_trace(h64["rewards"], h64["terminated"], h64.get("truncated"),
+                oracle.eligibility_trace(h["rewards"], h["terminated"], h.get("truncated"),
                                          gamma=gamma, lam=lam)
             elif w.algo == "cumsum":
-                oracle.episodic_cumsum(h64["rewards"], h64["terminated"], h64.get("truncated"))
+                oracle.episodic_cumsum(h["rewards"], h["terminated"], h.get("truncated"))
             else:
-                oracle.vtrace(h64["rewards"], h64["values"], h64["log_rhos"], h64["terminated"],
+                oracle.vtrace(h["rewards"], h["values"], h["log_rhos"], h["terminated"],
                               gamma=gamma, lam=lam, **clips)
-                oracle.retrace(h64["rewards"], h64["q_taken"], h64["exp_q_next"],
-                               h64["log_rhos"], h64["terminated"], gamma=gamma, lam=lam,
+                oracle.retrace(h["rewards"], h["q_taken"], h["exp_q_next"],
+                               h["log_rhos"], h["terminated"], gamma=gamma, lam=lam,
                                c_bar=clips["c_bar"])
 
-        oracle_step()  # first touch of the inputs, untimed
-        # Whole batches until the time budget is spent (the first call is slower
-        # than the rest, so a repetition count taken from it falls short).
-        reps = 0
-        t0 = time.perf_counter()
-        while True:
-            oracle_step()
-            reps += 1
-            cpu_s = time.perf_counter() - t0
-            if cpu_s >= args.cpu_seconds:
-                break
+        def timed(step, budget):
+            """Whole batches until the time budget is spent (the first call,
+            untimed, is slower than the rest, so a repetition count taken from
+            it falls short)."""
+            step()
+            reps, t0 = 0, time.perf_counter()
+            while True:
+                step()
+                reps += 1
+                spent = time.perf_counter() - t0
+                if spent >= budget:
+                    return reps, spent
+
+        reps, cpu_s = timed(lambda: oracle_step(h64), args.cpu_seconds)
         cpu = {"value": env_steps * reps / cpu_s, "unit": "env-steps/s", "cores": 1,
                "kind": "oracle",
                "sample": "the whole %dx%d batch, %d repetitions (%.1f s), single-threaded "
-                         "fp64 C oracle" % (N, T, reps, cpu_s)}
+                         "fp64 C oracle" % (N, T, reps, cpu_s),
+               "cpu_model": cpu_model()}
+        # The same oracle on every host core this process may use (at most 16,
+        # the host share of one GPU): one contiguous slice of rows per thread,
+        # each thread repeating its slice until the budget is spent.  The C
+        # oracle runs without the interpreter lock, so the threads run in
+        # parallel.
+        nthreads = host_threads()
+        if nthreads > 1 and N >= nthreads:
+            import threading
+            bounds = [N * i // nthreads for i in range(nthreads + 1)]
+            slices = [{k: np.ascontiguousarray(v[a:b]) for k, v in h64.items()}
+                      for a, b in zip(bounds[:-1], bounds[1:])]
+            done = [0] * nthreads
+            go = threading.Barrier(nthreads + 1, timeout=120)
+            stop = [0.0]
+
+            def worker(i):
+                oracle_step(slices[i])  # first touch, untimed
+                go.wait()
+                while time.perf_counter() < stop[0]:
+                    oracle_step(slices[i])
+                    done[i] += 1
+
+            threads = [threading.Thread(target=worker, args=(i,)) for i in range(nthreads)]
+            for th in threads:
+                th.start()
+            stop[0] = time.perf_counter() + 1e9
+            go.wait()
+            t0 = time.perf_counter()
+            stop[0] = t0 + args.cpu_seconds / 2
+            for th in threads:
+                th.join()
+            cpu_m = time.perf_counter() - t0
+            rows_done = sum(done[i] * (bounds[i + 1] - bounds[i]) for i in range(nthreads))
+            cpu["all_cores"] = {
+                "value": rows_done * T / cpu_m, "unit": "env-steps/s", "cores": nthreads,
+                "sample": "the %dx%d batch in %d row slices, one thread each repeating its "
+                          "slice for %.1f s (%.1f batches in all)"
+                          % (N, T, nthreads, cpu_m, rows_done / N)}
 
     meta_dir = os.environ.get("RLCA_BENCH_META_DIR")
     if meta_dir:

@@ -68,3 +68,14 @@ def test_more_than_one_gpu_is_refused():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr
+
+
+def test_host_threads_is_bounded_by_affinity_and_one_gpu_share():
+    n = bench.host_threads()
+    assert 1 <= n <= 16
+    assert n <= len(os.sched_getaffinity(0))
+
+
+def test_cpu_model_is_text_or_absent():
+    m = bench.cpu_model()
+    assert m is None or (isinstance(m, str) and m)
