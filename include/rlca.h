@@ -486,24 +486,41 @@ const char *rlca_last_error(void);
 int rlca_version(void);
 
 /*
- * Tiling variants.  Each lane owns 4 consecutive steps (one 16-byte vector of
- * every fp32 array and of every output).  A variant fixes how many lanes
- * share one row within a wavefront and how many wavefronts cooperate on one
- * row; rows longer than a tile are processed tile by tile.
+ * Tiling variants.  Each lane owns K consecutive steps.  K = 4 everywhere
+ * (one 16-byte vector of every fp32 array and of every output), except the
+ * tilings with whole wavefronts per row (waves_per_row > 1) on bf16 inputs,
+ * where K = 8 (one 16-byte vector of every bf16 array) for every algorithm
+ * but V-trace.  A variant fixes how many lanes share one row within a
+ * wavefront and how many wavefronts cooperate on one row; rows longer than a
+ * tile are processed tile by tile.
  * By default each call picks one from (num_envs, T, dtype).
  * rlca_set_variant(v) forces variant v (0 <= v < rlca_num_variants()) for
  * later calls on the calling thread, or restores the automatic choice with
  * v = -1; it returns the previous setting, or -2 for an unknown v (setting
  * unchanged).  Every variant computes the same results up to rounding order.
- * rlca_variant_info writes the steps per lane (for `dtype`), the number of
- * lanes that share one row (tile = steps per lane x lanes per row) and the
- * wavefronts per row of variant v and returns RLCA_OK, or RLCA_EINVAL /
- * RLCA_EDTYPE.  rlca_last_variant() is the variant the calling thread's last
- * successful launch used (-1 if none).
+ * rlca_variant_info writes the steps per lane K of variant v for the
+ * algorithm `algo` (an rlca_algo; a window form takes its algorithm's, the
+ * affine scan RLCA_ALGO_AFFINE in either direction) and `dtype`, the number
+ * of lanes that share one row (tile = K x lanes per row) and the wavefronts
+ * per row, and returns RLCA_OK, or RLCA_EINVAL (unknown variant or
+ * algorithm) / RLCA_EDTYPE.  rlca_last_variant() is the variant the calling
+ * thread's last successful launch used (-1 if none).  The policy-table entry
+ * points have their own tiling and are not described by these calls.
  */
+typedef enum {
+  RLCA_ALGO_RETURNS = 0,
+  RLCA_ALGO_GAE = 1,
+  RLCA_ALGO_TD_LAMBDA = 2,
+  RLCA_ALGO_VTRACE = 3,
+  RLCA_ALGO_RETRACE = 4,
+  RLCA_ALGO_ELIGIBILITY = 5,
+  RLCA_ALGO_CUMSUM = 6,
+  RLCA_ALGO_AFFINE = 7
+} rlca_algo;
+
 int rlca_num_variants(void);
 int rlca_set_variant(int variant);
-int rlca_variant_info(int variant, int dtype, int *steps_per_lane, int *lanes_per_row,
+int rlca_variant_info(int variant, int algo, int dtype, int *steps_per_lane, int *lanes_per_row,
                       int *waves_per_row);
 int rlca_last_variant(void);
 

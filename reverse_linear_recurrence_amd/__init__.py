@@ -17,6 +17,7 @@ tiling controls rlca_set_variant, rlca_num_variants,
 rlca_variant_info, rlca_last_variant, plus rlca_version.
 """
 from ._binding import (  # noqa: F401
+    ALGO_CODES,
     RLCA_BF16,
     RLCA_EALIAS,
     RLCA_EDTYPE,

@@ -73,7 +73,7 @@ _SIGNATURES = {
     "rlca_version": [],
     "rlca_num_variants": [],
     "rlca_set_variant": [_int],
-    "rlca_variant_info": [_int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
+    "rlca_variant_info": [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
                           ctypes.POINTER(_int)],
     "rlca_last_variant": [],
 }
@@ -690,13 +690,22 @@ def rlca_set_variant(variant):
     return prev
 
 
-def rlca_variant_info(variant, dtype=torch.float32):
+# Algorithm codes of rlca_variant_info (rlca_algo); a window form takes its
+# algorithm's code, the affine scan "affine" in either direction.
+ALGO_CODES = {"returns": 0, "gae": 1, "td_lambda": 2, "vtrace": 3, "retrace": 4,
+              "eligibility": 5, "cumsum": 6, "affine": 7}
+
+
+def rlca_variant_info(variant, dtype=torch.float32, algo="gae"):
     """(steps_per_lane, lanes_per_row, waves_per_row) of a tiling variant for
-    inputs of ``dtype`` (torch.float32 or torch.bfloat16)."""
+    the algorithm ``algo`` (a key of ALGO_CODES) on inputs of ``dtype``
+    (torch.float32 or torch.bfloat16)."""
     code = RLCA_BF16 if dtype in (torch.bfloat16, RLCA_BF16, "bf16") else RLCA_F32
+    if algo not in ALGO_CODES:
+        raise ValueError("unknown algorithm %r" % (algo,))
     k, l, w = _int(), _int(), _int()
-    _check(load_library().rlca_variant_info(int(variant), code, ctypes.byref(k),
-                                            ctypes.byref(l), ctypes.byref(w)))
+    _check(load_library().rlca_variant_info(int(variant), ALGO_CODES[algo], code,
+                                            ctypes.byref(k), ctypes.byref(l), ctypes.byref(w)))
     return k.value, l.value, w.value
 
 

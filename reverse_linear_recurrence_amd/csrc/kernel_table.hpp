@@ -11,7 +11,8 @@ namespace rlca {
 template <int A, typename InT, int V, bool U, bool C>
 const void *kernel_ptr() {
   constexpr Variant v = kVariants[V];
-  return reinterpret_cast<const void *>(&scan_kernel<A, InT, kStepsPerLane, v.LPR, v.WPR, U, C>);
+  constexpr int K = steps_per_lane(v, sizeof(InT) == 2, A == kVtrace);
+  return reinterpret_cast<const void *>(&scan_kernel<A, InT, K, v.LPR, v.WPR, U, C>);
 }
 
 template <int A, typename InT, bool U, bool C>

@@ -22,6 +22,13 @@
 #include "variants.hpp"
 
 namespace rlca {
+
+// The public algorithm codes of rlca_variant_info are the kernels' own.
+static_assert(RLCA_ALGO_RETURNS == kReturns && RLCA_ALGO_GAE == kGae &&
+                  RLCA_ALGO_TD_LAMBDA == kTdLambda && RLCA_ALGO_VTRACE == kVtrace &&
+                  RLCA_ALGO_RETRACE == kRetrace && RLCA_ALGO_ELIGIBILITY == kEligibility &&
+                  RLCA_ALGO_CUMSUM == kCumsum && RLCA_ALGO_AFFINE == kAffine,
+              "rlca_algo and Algo disagree");
 namespace {
 
 // Default tiling (measured on MI355X).  Short rows: the smallest
@@ -30,14 +37,15 @@ namespace {
 // wavefronts (16 per CU) -- the most wavefronts per row such that N * WPR
 // stays within that and the tile is not longer than the row; from 8192 rows
 // on, one wavefront per row.
-int auto_variant(int64_t N, int64_t T) {
+int auto_variant(int64_t N, int64_t T, bool bf16, bool vtrace) {
   constexpr int64_t kTargetWaves = 4096;
+  auto tile = [&](int v) { return tile_steps(kVariants[v], bf16, vtrace); };
   for (int v = 0; v <= 2; ++v)
-    if (T <= tile_steps(kVariants[v])) return v;
+    if (T <= tile(v)) return v;
   if (N >= 2 * kTargetWaves) return 2;
   for (int v = kNumVariants - 1; v >= 3; --v)
-    if (N * kVariants[v].WPR <= kTargetWaves && tile_steps(kVariants[v]) <= T) return v;
-  return tile_steps(kVariants[3]) <= T ? 3 : 2;
+    if (N * kVariants[v].WPR <= kTargetWaves && tile(v) <= T) return v;
+  return tile(3) <= T ? 3 : 2;
 }
 
 // ------------------------------------------------------------- errors
@@ -142,7 +150,9 @@ int check_sizes(int64_t N, int64_t T, int dtype) {
 
 // window: the instance with carry vectors (Args::cin, cout, cmap).
 int launch(int algo, int dtype, const Args &args, void *stream, bool window = false) {
-  const int v = t_forced_variant >= 0 ? t_forced_variant : auto_variant(args.N, args.T);
+  const int v = t_forced_variant >= 0
+                    ? t_forced_variant
+                    : auto_variant(args.N, args.T, dtype == RLCA_BF16, algo == kVtrace);
   const Variant var = kVariants[v];
   dim3 grid, block;
   if (var.WPR > 1) {
@@ -836,7 +846,7 @@ int rlca_vtrace_probs_chunk(int64_t num_envs, int64_t T, int64_t num_actions, in
 
 const char *rlca_last_error(void) { return t_last_error.c_str(); }
 
-int rlca_version(void) { return 300; }  // 0.3.0: policy-table Retrace and V-trace
+int rlca_version(void) { return 400; }  // 0.4.0: bf16 long rows at 8 steps per lane; rlca_variant_info takes the algorithm
 
 int rlca_num_variants(void) { return kNumVariants; }
 
@@ -847,13 +857,16 @@ int rlca_set_variant(int variant) {
   return prev;
 }
 
-int rlca_variant_info(int variant, int dtype, int *steps_per_lane_out, int *lanes_per_row,
-                      int *waves_per_row) {
+int rlca_variant_info(int variant, int algo, int dtype, int *steps_per_lane_out,
+                      int *lanes_per_row, int *waves_per_row) {
   if (variant < 0 || variant >= kNumVariants)
     return fail(RLCA_EINVAL, "unknown variant %d", variant);
+  if (algo < RLCA_ALGO_RETURNS || algo > RLCA_ALGO_AFFINE)
+    return fail(RLCA_EINVAL, "unknown algorithm %d", algo);
   if (dtype != RLCA_F32 && dtype != RLCA_BF16) return fail(RLCA_EDTYPE, "unknown dtype %d", dtype);
   const Variant v = kVariants[variant];
-  if (steps_per_lane_out) *steps_per_lane_out = kStepsPerLane;
+  if (steps_per_lane_out)
+    *steps_per_lane_out = steps_per_lane(v, dtype == RLCA_BF16, algo == RLCA_ALGO_VTRACE);
   if (lanes_per_row) *lanes_per_row = v.WPR > 1 ? 64 * v.WPR : v.LPR;
   if (waves_per_row) *waves_per_row = v.WPR;
   return RLCA_OK;

@@ -11,26 +11,30 @@ struct Variant {
   int WPR;  // wavefronts per row
 };
 
-// Every lane owns K = 4 consecutive steps: one 16-byte vector of each fp32
-// array (an 8-byte vector of each bf16 array) and one 16-byte vector of each
-// fp32 output, so every load and store instruction of a wavefront covers one
-// contiguous span and uses each cache line it touches in full.  (Longer spans
-// per lane split each instruction into strided partial lines: 4x the line
-// requests for 16 fp32 steps per lane, and partial-line output writes for 8
-// bf16 steps per lane.)
-constexpr int kStepsPerLane = 4;
 constexpr Variant kVariants[] = {
-    {16, 1},  // 0: tile    64 steps, 16 rows per 256-thread workgroup
+    {16, 1},  // 0: tile    64 steps (K = 4), 16 rows per 256-thread workgroup
     {32, 1},  // 1: tile   128,  8 rows per workgroup
     {64, 1},  // 2: tile   256,  4 rows per workgroup
-    {64, 4},  // 3: tile  1024,  1 row per 256-thread workgroup
-    {64, 8},  // 4: tile  2048,  1 row per 512-thread workgroup
-    {64, 16}, // 5: tile  4096,  1 row per 1024-thread workgroup
+    {64, 4},  // 3: tile  1024 (bf16, K = 8: 2048), 1 row per 256-thread workgroup
+    {64, 8},  // 4: tile  2048 (4096),  1 row per 512-thread workgroup
+    {64, 16}, // 5: tile  4096 (8192),  1 row per 1024-thread workgroup
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 
-inline int64_t tile_steps(const Variant &v) {
-  return static_cast<int64_t>(kStepsPerLane) * v.LPR * v.WPR;
+// Every lane owns K consecutive steps, one 16-byte vector of each input
+// array: K = 4 for fp32, and for bf16 when a row is shared by lanes of one
+// wavefront; K = 8 for bf16 rows of whole wavefronts, which halves the tiles
+// (and the workgroup barriers) per row and doubles the bytes each tile has in
+// flight.  V-trace keeps K = 4 there: its 1024-thread instance would spill.
+// Each load and store instruction of a wavefront then covers one contiguous
+// span.  (Longer fp32 spans per lane split each instruction into strided
+// partial lines: 4x the line requests for 16 fp32 steps per lane.)
+constexpr int steps_per_lane(const Variant &v, bool bf16, bool vtrace) {
+  return bf16 && v.WPR > 1 && !vtrace ? 8 : 4;
+}
+
+inline int64_t tile_steps(const Variant &v, bool bf16, bool vtrace) {
+  return static_cast<int64_t>(steps_per_lane(v, bf16, vtrace)) * v.LPR * v.WPR;
 }
 
 // Host-side address of the kernel instance for an algorithm (Algo), input

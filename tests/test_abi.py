@@ -40,14 +40,25 @@ def test_version_and_variants(lib):
     nv = rl.rlca_num_variants()
     assert nv >= 6
     for v in range(nv):
-        k, lpr, wpr = rl.rlca_variant_info(v)
-        kb, lprb, wprb = rl.rlca_variant_info(v, torch.bfloat16)
-        assert k == kb == 4  # one 16-byte fp32 vector per lane and array
-        assert (lpr, wpr) == (lprb, wprb)
-        # lanes that share a row: part of a wavefront, or whole wavefronts
-        assert (wpr == 1 and lpr in (16, 32, 64)) or lpr == 64 * wpr
+        for algo in rl.ALGO_CODES:
+            k, lpr, wpr = rl.rlca_variant_info(v, torch.float32, algo)
+            kb, lprb, wprb = rl.rlca_variant_info(v, torch.bfloat16, algo)
+            assert k == 4  # one 16-byte fp32 vector per lane and array
+            # bf16: one 16-byte vector per lane on rows of whole wavefronts
+            # (V-trace keeps 4 steps), 4 steps where lanes of one wavefront
+            # share a row
+            assert kb == (8 if wpr > 1 and algo != "vtrace" else 4)
+            assert (lpr, wpr) == (lprb, wprb)
+            # lanes that share a row: part of a wavefront, or whole wavefronts
+            assert (wpr == 1 and lpr in (16, 32, 64)) or lpr == 64 * wpr
     with pytest.raises(rl.RlcaError):
         rl.rlca_variant_info(nv)
+    with pytest.raises(ValueError):
+        rl.rlca_variant_info(0, torch.float32, "sarsa")
+    lib = rl.load_library()
+    k = ctypes.c_int()
+    assert lib.rlca_variant_info(0, 8, 0, ctypes.byref(k), None, None) == rl.RLCA_EINVAL
+    assert lib.rlca_variant_info(0, -1, 0, ctypes.byref(k), None, None) == rl.RLCA_EINVAL
     assert rl.rlca_set_variant(2) == -1
     assert rl.rlca_set_variant(-1) == 2
     with pytest.raises(ValueError):

@@ -51,8 +51,9 @@ def test_workload_full_size(name):
         print(name, algo, "variant", rl.rlca_last_variant(), "rel err", errs, flush=True)
 
 
-def variant_lengths(v, dtype="f32"):
-    k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32)
+def variant_lengths(v, dtype="f32", algo="gae"):
+    k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                       algo)
     tile = k * lanes
     # every residue of T mod 4 (the lane holding a row's end has 1..3 steps),
     # rows shorter than one lane's span, one tile, and several tiles
@@ -66,7 +67,7 @@ def test_every_variant_ragged_lengths(algo, dtype):
     p = params32(DEFAULT_PARAMS)
     N = 37  # not a multiple of any workgroup's row count
     for v in range(rl.rlca_num_variants()):
-        for T in variant_lengths(v, dtype):
+        for T in variant_lengths(v, dtype, algo):
             seed = 1000 * v + T
             host = random_inputs(algo, N, T, seed, dtype)
             dev = to_device(host)
@@ -338,7 +339,8 @@ def test_many_workgroups_and_a_partial_last_one(algo, dtype):
     p = params32(DEFAULT_PARAMS)
     N = 20003
     for v in (0, 1, 2):
-        k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32)
+        k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                           algo)
         T = k * lanes
         host = random_inputs(algo, N, T, 7000 + v, dtype, p_term=0.01, p_trunc=0.01)
         ref = run_oracle(algo, host, p)

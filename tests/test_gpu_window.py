@@ -130,9 +130,10 @@ def window_inputs(algo, N, T, seed, dtype, sparse):
     return d, c
 
 
-def variant_lengths(v):
-    _, lanes, _ = rl.rlca_variant_info(v)
-    tile = 4 * lanes
+def variant_lengths(v, dtype, algo):
+    k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32,
+                                       algo)
+    tile = k * lanes
     return sorted({1, 3, 6, tile - 3, tile - 2, tile, 2 * tile + 5, 2 * tile + 7})
 
 
@@ -141,7 +142,7 @@ def variant_lengths(v):
 def test_window_parity_every_variant(algo, dtype):
     p = params32(dict(DEFAULT_PARAMS, c_bar=0.95, rho_bar=1.05))
     for v in range(rl.rlca_num_variants()):
-        for T in variant_lengths(v):
+        for T in variant_lengths(v, dtype, algo):
             for sparse in (False, True):
                 N = 37 if T < 4096 else 5
                 d, c = window_inputs(algo, N, T, 1000 + 7 * v + T, dtype, sparse)
@@ -274,7 +275,7 @@ def affine_inputs(N, T, seed, dtype, p_reset):
 @pytest.mark.parametrize("reverse", [True, False])
 def test_affine_scan_parity_every_variant(reverse, dtype):
     for v in range(rl.rlca_num_variants()):
-        for T in variant_lengths(v):
+        for T in variant_lengths(v, dtype, "affine"):
             for p_reset, with_reset in ((0.0, False), (0.01, True), (0.2, True)):
                 N = 29 if T < 4096 else 4
                 al, be, rs, c = affine_inputs(N, T, 3000 + v * 13 + T, dtype, p_reset)
