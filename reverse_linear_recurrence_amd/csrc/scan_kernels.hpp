@@ -865,7 +865,38 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
   if constexpr (!kEdge) {
     // Non-temporal (streaming) dwordx4 stores: outputs are written once and
     // not re-read by this kernel.
-    if (row_ok) {
+    if constexpr (K == 8 && WPR > 1) {
+      // Eight steps per lane: a lane's 32 output bytes would be two 16-byte
+      // stores, each instruction writing every other 16-byte piece of the
+      // wavefront's span.  Stage the outputs through this wavefront's part
+      // of LDS instead, in time order, and store them back as two
+      // instructions that each write one contiguous half of the span.
+      // (Whole tiles only: every lane of the wavefront holds K steps.)
+      __shared__ float4 s_stage[WPR][2 * 64];
+      const int pos = U::forward ? lane : 63 - lane;  // the lane's span in the wavefront's
+      const int64_t ws = t0 - static_cast<int64_t>(pos) * K;  // the wavefront's first step
+      float4 *st = s_stage[wave];
+      auto put = [&](float *row, const float (&o)[K]) {
+        st[2 * pos] = make_float4(o[0], o[1], o[2], o[3]);
+        st[2 * pos + 1] = make_float4(o[4], o[5], o[6], o[7]);
+        // The wavefront's LDS operations complete in order; this keeps the
+        // compiler from moving the reads of other lanes' values above.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float4 lo = st[lane], hi = st[64 + lane];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        V4 *dst = reinterpret_cast<V4 *>(row + ws);
+        __builtin_nontemporal_store(V4{lo.x, lo.y, lo.z, lo.w}, dst + lane);
+        __builtin_nontemporal_store(V4{hi.x, hi.y, hi.z, hi.w}, dst + 64 + lane);
+      };
+      if (row_ok) {
+        put(o0_row, o0);
+        if (has_o1) put(o1_row, o1);
+      }
+    } else if (row_ok) {
 #pragma unroll
       for (int i = 0; i < K / 4; ++i)
         __builtin_nontemporal_store(V4{o0[4 * i], o0[4 * i + 1], o0[4 * i + 2], o0[4 * i + 3]},

@@ -26,8 +26,8 @@ constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
 // wavefront; K = 8 for bf16 rows of whole wavefronts, which halves the tiles
 // (and the workgroup barriers) per row and doubles the bytes each tile has in
 // flight.  V-trace keeps K = 4 there: its 1024-thread instance would spill.
-// Each load and store instruction of a wavefront then covers one contiguous
-// span.  (Longer fp32 spans per lane split each instruction into strided
+// Each load instruction of a wavefront then covers one contiguous span, and
+// so does each output store (at K = 8 after staging through LDS).  (Longer fp32 spans per lane split each instruction into strided
 // partial lines: 4x the line requests for 16 fp32 steps per lane.)
 constexpr int steps_per_lane(const Variant &v, bool bf16, bool vtrace) {
   return bf16 && v.WPR > 1 && !vtrace ? 8 : 4;
