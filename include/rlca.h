@@ -486,14 +486,16 @@ const char *rlca_last_error(void);
 int rlca_version(void);
 
 /*
- * Tiling variants.  Each lane owns K consecutive steps.  K = 4 everywhere
- * (one 16-byte vector of every fp32 array and of every output), except the
- * tilings with whole wavefronts per row (waves_per_row > 1) on bf16 inputs,
- * where K = 8 (one 16-byte vector of every bf16 array) for every algorithm
- * but V-trace.  A variant fixes how many lanes share one row within a
- * wavefront and how many wavefronts cooperate on one row; rows longer than a
- * tile are processed tile by tile.
- * By default each call picks one from (num_envs, T, dtype).
+ * Tiling variants.  Each lane owns K consecutive steps.  K = 4 (one 16-byte
+ * vector of every fp32 array and of every output) except in the wide
+ * variants on bf16 inputs, where K = 8 (one 16-byte vector of every bf16
+ * array) for every algorithm but V-trace; on fp32 inputs and for V-trace a
+ * wide variant runs the same kernel as its narrow twin.  A variant fixes how
+ * many lanes share one row within a wavefront, how many wavefronts cooperate
+ * on one row, and whether it is wide; rows longer than a tile are processed
+ * tile by tile.  Variants 0-2: 16, 32 or 64 lanes of one wavefront per row;
+ * 3-5: 4, 8 or 16 wavefronts per row; 6-8: 3-5, wide.
+ * By default each call picks one from (num_envs, T, dtype, algorithm).
  * rlca_set_variant(v) forces variant v (0 <= v < rlca_num_variants()) for
  * later calls on the calling thread, or restores the automatic choice with
  * v = -1; it returns the previous setting, or -2 for an unknown v (setting

@@ -17,14 +17,17 @@ const void *kernel_ptr() {
 
 template <int A, typename InT, bool U, bool C>
 const void *kernel_ptr(int v) {
-  static_assert(kNumVariants == 6, "one case per variant");
+  static_assert(kNumVariants == 9, "one case per variant");
   switch (v) {
     case 0: return kernel_ptr<A, InT, 0, U, C>();
     case 1: return kernel_ptr<A, InT, 1, U, C>();
     case 2: return kernel_ptr<A, InT, 2, U, C>();
     case 3: return kernel_ptr<A, InT, 3, U, C>();
     case 4: return kernel_ptr<A, InT, 4, U, C>();
-    default: return kernel_ptr<A, InT, 5, U, C>();
+    case 5: return kernel_ptr<A, InT, 5, U, C>();
+    case 6: return kernel_ptr<A, InT, 6, U, C>();
+    case 7: return kernel_ptr<A, InT, 7, U, C>();
+    default: return kernel_ptr<A, InT, 8, U, C>();
   }
 }
 

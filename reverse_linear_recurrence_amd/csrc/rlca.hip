@@ -36,16 +36,21 @@ namespace {
 // tile's loads issued while the previous one is computed): about 4096
 // wavefronts (16 per CU) -- the most wavefronts per row such that N * WPR
 // stays within that and the tile is not longer than the row; from 8192 rows
-// on, one wavefront per row.
+// on, one wavefront per row.  On bf16 inputs a long-row choice then takes its
+// wide twin (8 steps per lane) when the row holds one of its tiles.
 int auto_variant(int64_t N, int64_t T, bool bf16, bool vtrace) {
   constexpr int64_t kTargetWaves = 4096;
   auto tile = [&](int v) { return tile_steps(kVariants[v], bf16, vtrace); };
+  auto widen = [&](int v) {
+    const int w = v - 3 + kFirstWide;
+    return steps_per_lane(kVariants[w], bf16, vtrace) == 8 && tile(w) <= T ? w : v;
+  };
   for (int v = 0; v <= 2; ++v)
     if (T <= tile(v)) return v;
   if (N >= 2 * kTargetWaves) return 2;
-  for (int v = kNumVariants - 1; v >= 3; --v)
-    if (N * kVariants[v].WPR <= kTargetWaves && tile(v) <= T) return v;
-  return tile(3) <= T ? 3 : 2;
+  for (int v = 5; v >= 3; --v)
+    if (N * kVariants[v].WPR <= kTargetWaves && tile(v) <= T) return widen(v);
+  return tile(3) <= T ? widen(3) : 2;
 }
 
 // ------------------------------------------------------------- errors

@@ -7,30 +7,37 @@
 namespace rlca {
 
 struct Variant {
-  int LPR;  // lanes per row inside a wavefront (64 when WPR > 1)
-  int WPR;  // wavefronts per row
+  int LPR;    // lanes per row inside a wavefront (64 when WPR > 1)
+  int WPR;    // wavefronts per row
+  bool wide;  // 8 steps per lane on bf16 inputs (see steps_per_lane)
 };
 
 constexpr Variant kVariants[] = {
-    {16, 1},  // 0: tile    64 steps (K = 4), 16 rows per 256-thread workgroup
-    {32, 1},  // 1: tile   128,  8 rows per workgroup
-    {64, 1},  // 2: tile   256,  4 rows per workgroup
-    {64, 4},  // 3: tile  1024 (bf16, K = 8: 2048), 1 row per 256-thread workgroup
-    {64, 8},  // 4: tile  2048 (4096),  1 row per 512-thread workgroup
-    {64, 16}, // 5: tile  4096 (8192),  1 row per 1024-thread workgroup
+    {16, 1, false},  // 0: tile    64 steps, 16 rows per 256-thread workgroup
+    {32, 1, false},  // 1: tile   128,  8 rows per workgroup
+    {64, 1, false},  // 2: tile   256,  4 rows per workgroup
+    {64, 4, false},  // 3: tile  1024,  1 row per 256-thread workgroup
+    {64, 8, false},  // 4: tile  2048,  1 row per 512-thread workgroup
+    {64, 16, false}, // 5: tile  4096,  1 row per 1024-thread workgroup
+    {64, 4, true},   // 6: as 3, bf16 tile 2048
+    {64, 8, true},   // 7: as 4, bf16 tile 4096
+    {64, 16, true},  // 8: as 5, bf16 tile 8192
 };
 constexpr int kNumVariants = sizeof(kVariants) / sizeof(kVariants[0]);
+constexpr int kFirstWide = 6;  // variants kFirstWide + i are variants 3 + i, wide
 
 // Every lane owns K consecutive steps, one 16-byte vector of each input
-// array: K = 4 for fp32, and for bf16 when a row is shared by lanes of one
-// wavefront; K = 8 for bf16 rows of whole wavefronts, which halves the tiles
-// (and the workgroup barriers) per row and doubles the bytes each tile has in
-// flight.  V-trace keeps K = 4 there: its 1024-thread instance would spill.
-// Each load instruction of a wavefront then covers one contiguous span, and
-// so does each output store (at K = 8 after staging through LDS).  (Longer fp32 spans per lane split each instruction into strided
-// partial lines: 4x the line requests for 16 fp32 steps per lane.)
+// array: K = 4 everywhere except the wide variants on bf16 inputs, where
+// K = 8 (one 16-byte vector of each bf16 array).  That halves the tiles (and
+// the workgroup barriers) per row and doubles the bytes each tile has in
+// flight.  V-trace keeps K = 4 there: its 1024-thread instance would spill;
+// on fp32 inputs and for V-trace a wide variant is the same kernel as its
+// narrow twin.  Each load instruction of a wavefront covers one contiguous
+// span, and so does each output store (at K = 8 after staging through LDS).
+// (Longer fp32 spans per lane split each instruction into strided partial
+// lines: 4x the line requests for 16 fp32 steps per lane.)
 constexpr int steps_per_lane(const Variant &v, bool bf16, bool vtrace) {
-  return bf16 && v.WPR > 1 && !vtrace ? 8 : 4;
+  return v.wide && bf16 && !vtrace ? 8 : 4;
 }
 
 inline int64_t tile_steps(const Variant &v, bool bf16, bool vtrace) {

@@ -38,17 +38,18 @@ def test_library_exports_every_declared_symbol(lib):
 def test_version_and_variants(lib):
     assert rl.rlca_version() >= 100
     nv = rl.rlca_num_variants()
-    assert nv >= 6
+    assert nv == 9
     for v in range(nv):
         for algo in rl.ALGO_CODES:
             k, lpr, wpr = rl.rlca_variant_info(v, torch.float32, algo)
             kb, lprb, wprb = rl.rlca_variant_info(v, torch.bfloat16, algo)
             assert k == 4  # one 16-byte fp32 vector per lane and array
-            # bf16: one 16-byte vector per lane on rows of whole wavefronts
-            # (V-trace keeps 4 steps), 4 steps where lanes of one wavefront
-            # share a row
-            assert kb == (8 if wpr > 1 and algo != "vtrace" else 4)
+            # bf16: one 16-byte vector per lane in the wide variants 6-8
+            # (V-trace keeps 4 steps), 4 steps elsewhere
+            assert kb == (8 if v >= 6 and algo != "vtrace" else 4)
             assert (lpr, wpr) == (lprb, wprb)
+            if v >= 6:  # the wide twins of variants 3-5
+                assert (lpr, wpr) == rl.rlca_variant_info(v - 3, torch.float32, algo)[1:]
             # lanes that share a row: part of a wavefront, or whole wavefronts
             assert (wpr == 1 and lpr in (16, 32, 64)) or lpr == 64 * wpr
     with pytest.raises(rl.RlcaError):
