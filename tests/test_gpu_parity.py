@@ -350,6 +350,30 @@ def test_many_workgroups_and_a_partial_last_one(algo, dtype):
                      "%s/%s/v%d" % (algo, dtype, v))
 
 
+@pytest.mark.parametrize("algo", ALGOS)
+def test_wide_variants_on_fp32_are_their_narrow_twins(algo):
+    # Variants 6-8 take 8 steps per lane on bf16 only; on fp32 inputs (and for
+    # V-trace on bf16) they run the kernels of variants 3-5, so the outputs
+    # are equal bitwise.
+    p = params32(DEFAULT_PARAMS)
+    cases = [("f32", algo)] + ([("bf16", algo)] if algo == "vtrace" else [])
+    for dtype, a in cases:
+        host = random_inputs(a, 9, 5000, 4242, dtype)
+        dev = to_device(host)
+        for v in (3, 4, 5):
+            assert rl.rlca_variant_info(v + 3, torch.bfloat16 if dtype == "bf16"
+                                        else torch.float32, a)[0] == 4
+            rl.rlca_set_variant(v)
+            try:
+                narrow = run_gpu(a, dev, p)
+                rl.rlca_set_variant(v + 3)
+                wide = run_gpu(a, dev, p)
+            finally:
+                rl.rlca_set_variant(-1)
+            for k in narrow:
+                assert np.array_equal(narrow[k], wide[k]), "%s/%s/v%d/%s" % (a, dtype, v, k)
+
+
 def test_hip_graph_replay_matches_eager():
     # The benchmark replays captured launches; every replay, with eager work
     # and synchronizations in between, must equal the eager call bitwise, and
