@@ -374,6 +374,24 @@ def test_wide_variants_on_fp32_are_their_narrow_twins(algo):
                 assert np.array_equal(narrow[k], wide[k]), "%s/%s/v%d/%s" % (a, dtype, v, k)
 
 
+def test_default_tiling_choice():
+    # The default variant for a few shapes: one-wavefront tiles for short
+    # rows, whole wavefronts per row for long ones, and on bf16 the wide twin
+    # (8 steps per lane) only when the row holds one wide tile; never for
+    # fp32 or V-trace.  (The choice depends on the shape, not on the data.)
+    p = params32(DEFAULT_PARAMS)
+    cases = [("gae", "f32", 4096, 128, 1), ("gae", "f32", 16384, 256, 2),
+             ("gae", "f32", 256, 16384, 5), ("gae", "bf16", 256, 16384, 8),
+             ("gae", "bf16", 512, 8192, 7), ("gae", "bf16", 1024, 2048, 6),
+             ("gae", "bf16", 2048, 1024, 3), ("vtrace", "bf16", 256, 16384, 5),
+             ("retrace", "bf16", 1024, 2048, 6), ("td_lambda", "f32", 2048, 1024, 3)]
+    assert rl.rlca_set_variant(-1) == -1
+    for algo, dtype, N, T, want in cases:
+        dev = to_device(random_inputs(algo, N, T, 11, dtype))
+        run_gpu(algo, dev, p)
+        assert rl.rlca_last_variant() == want, (algo, dtype, N, T, rl.rlca_last_variant())
+
+
 def test_hip_graph_replay_matches_eager():
     # The benchmark replays captured launches; every replay, with eager work
     # and synchronizations in between, must equal the eager call bitwise, and
