@@ -81,6 +81,9 @@ def parse():
     ap.add_argument("--variant", type=int, default=-1, help="force a tiling variant")
     ap.add_argument("--window", action="store_true",
                     help="time the window entry point (carry in; carry and carry map out)")
+    ap.add_argument("--split", action="store_true",
+                    help="give the library a workspace, so that calls on few long rows "
+                         "split every row into segments (rlca_set_workspace)")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip timing a plain copy kernel of the same byte count")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -259,6 +262,11 @@ def main():
         sets.append(d)
     torch.cuda.synchronize()
     rl.rlca_set_variant(args.variant)
+    split_segments = 1
+    if args.split:
+        split_segments = rl.rlca_split_segments(N, T)
+        workspace = torch.empty(3 * N * split_segments, dtype=torch.float32, device=dev)
+        rl.rlca_set_workspace(workspace)
 
     def window_step(d):
         c = dict(carry_in=d["_cin"], carry_out=d["_cout"], carry_map=d["_cmap"])
@@ -478,7 +486,7 @@ def main():
         copy = {"bytes_per_launch": 2 * half, "avg_launch_us": cus,
                 "GBps": 2 * half / (cus * 1e-6) / 1e9, "kernel": "torch copy_ (float32)"}
         del bufs
-    launches_per_step = launches_per_step_of(w)
+    launches_per_step = launches_per_step_of(w) * (3 if split_segments > 1 else 1)
     env_steps = N * T
     value = env_steps / (ms_per_step * 1e-3)
     bytes_per_step = algorithmic_bytes(w, N, T, args.window)
@@ -614,6 +622,7 @@ def main():
                    "gamma": w.gamma, "lam": w.lam, "p_term": w.p_term, "p_trunc": w.p_trunc,
                    "seed": w.seed, "rotation_sets": R, "timing": timing,
                    "launches_per_step": launches_per_step, "variant": variant,
+                   "split_segments": split_segments,
                    "entry": "window (carry in; carry and carry map out)" if args.window
                    else "plain"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",

@@ -520,6 +520,38 @@ typedef enum {
   RLCA_ALGO_AFFINE = 7
 } rlca_algo;
 
+/*
+ * Split calls: few long rows.  With one workgroup per row, a plain call
+ * (rlca_returns, rlca_gae, rlca_td_lambda, rlca_vtrace, rlca_retrace,
+ * rlca_eligibility_trace, rlca_episodic_cumsum) on at most 64 rows of at
+ * least 32768 steps leaves most compute units idle.  When the calling thread has set a
+ * workspace, such a call cuts every row into S = rlca_split_segments(N, T)
+ * segments of T / S steps and runs three launches on the same stream: the
+ * segments from carry 0, writing only their carry maps to the workspace; a
+ * small kernel composing, per row, the carry that enters each segment; and
+ * the segments again from those carries, writing the outputs.  It is the
+ * window calls' split along T (their carry and carry-map conventions) done
+ * inside the library; it reads the inputs twice and computes the same
+ * results up to rounding order.
+ *
+ * rlca_set_workspace(ptr, bytes) sets the calling thread's workspace: device
+ * memory owned by the caller, 4-byte aligned; NULL switches split calls off
+ * (the default).  A call splits only when bytes >= 12 * N * S (3 floats per
+ * segment); otherwise, or when S = 1, it runs unsplit.  The workspace must
+ * not overlap the call's arrays (RLCA_EALIAS), and calls that use one
+ * workspace must be ordered, for instance issued to one stream: the library
+ * does not synchronize.  Returns RLCA_OK, or RLCA_EINVAL (negative size,
+ * misaligned pointer).
+ *
+ * rlca_split_segments(num_envs, T) returns S (1: no split): the smallest
+ * power of two with num_envs * S >= 256, T divisible by S and T / S >= 4096,
+ * stopping where either condition would fail; 1 for more than 64 rows and
+ * for rows shorter than 32768 steps; -1 (with a message for rlca_last_error) for
+ * negative sizes.
+ */
+int rlca_set_workspace(void *workspace, int64_t bytes);
+int rlca_split_segments(int64_t num_envs, int64_t T);
+
 int rlca_num_variants(void);
 int rlca_set_variant(int variant);
 int rlca_variant_info(int variant, int algo, int dtype, int *steps_per_lane, int *lanes_per_row,

@@ -44,6 +44,8 @@ from ._binding import (  # noqa: F401
     rlca_returns,
     rlca_returns_chunk,
     rlca_set_variant,
+    rlca_set_workspace,
+    rlca_split_segments,
     rlca_td_lambda,
     rlca_td_lambda_chunk,
     rlca_variant_info,

@@ -9,6 +9,7 @@ of the tensors' device) and the call returns without synchronizing.
 """
 import ctypes
 import os
+import threading
 
 import torch
 
@@ -71,6 +72,8 @@ _SIGNATURES = {
                                 _vp],
     "rlca_last_error": [],
     "rlca_version": [],
+    "rlca_set_workspace": [_vp, _i64],
+    "rlca_split_segments": [_i64, _i64],
     "rlca_num_variants": [],
     "rlca_set_variant": [_int],
     "rlca_variant_info": [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
@@ -707,6 +710,34 @@ def rlca_variant_info(variant, dtype=torch.float32, algo="gae"):
     _check(load_library().rlca_variant_info(int(variant), ALGO_CODES[algo], code,
                                             ctypes.byref(k), ctypes.byref(l), ctypes.byref(w)))
     return k.value, l.value, w.value
+
+
+_ws_local = threading.local()
+
+
+def rlca_set_workspace(workspace):
+    """Set the calling thread's workspace for split calls (few long rows):
+    a contiguous tensor on the GPU, or None to switch split calls off.  The
+    tensor is kept alive here until the next call replaces it."""
+    lib = load_library()
+    if workspace is None:
+        _check(lib.rlca_set_workspace(None, 0))
+    else:
+        if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda
+                and workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous tensor on a GPU")
+        _check(lib.rlca_set_workspace(workspace.data_ptr(),
+                                      workspace.numel() * workspace.element_size()))
+    _ws_local.tensor = workspace
+
+
+def rlca_split_segments(num_envs, T):
+    """Segments per row a call of num_envs rows of T steps is split into
+    when a workspace is set (1: not split)."""
+    s = load_library().rlca_split_segments(int(num_envs), int(T))
+    if s < 0:
+        raise ValueError(load_library().rlca_last_error().decode())
+    return s
 
 
 def rlca_last_variant():

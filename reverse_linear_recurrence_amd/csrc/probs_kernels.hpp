@@ -304,6 +304,8 @@ probs_kernel(const Args p, const TableArgs ta) {
 
   RowPtrs<InT> rp;
   rp.row = rr;
+  rp.src = rr;
+  rp.seg_off = 0;
   rp.r = static_cast<const InT *>(p.r) + rr * p.ld_r;
   rp.v = Algo == kVtrace ? static_cast<const InT *>(p.v) + rr * p.ld_v : nullptr;
   rp.lr = rp.eq = rp.tv = nullptr;

@@ -58,6 +58,9 @@ int auto_variant(int64_t N, int64_t T, bool bf16, bool vtrace) {
 thread_local std::string t_last_error;
 thread_local int t_forced_variant = -1;
 thread_local int t_last_variant = -1;
+// The caller's workspace for split calls (rlca_set_workspace), in floats.
+thread_local float *t_ws = nullptr;
+thread_local int64_t t_ws_floats = 0;
 
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char *fmt, ...) {
@@ -154,7 +157,9 @@ int check_sizes(int64_t N, int64_t T, int dtype) {
   } while (0)
 
 // window: the instance with carry vectors (Args::cin, cout, cmap).
-int launch(int algo, int dtype, const Args &args, void *stream, bool window = false) {
+// S > 1: segment view (window instances): args.N rows of args.T steps, row r
+// being segment r % S of row r / S of the caller's arrays.
+int launch(int algo, int dtype, const Args &args, void *stream, bool window = false, int S = 1) {
   const int v = t_forced_variant >= 0
                     ? t_forced_variant
                     : auto_variant(args.N, args.T, dtype == RLCA_BF16, algo == kVtrace);
@@ -218,7 +223,8 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
   int T32 = static_cast<int>(a.T);
   int ldT = static_cast<int>(a.ld_r);
   int ldX = static_cast<int>(ldx);
-  void *kargs[] = {&hot[0], &hot[1], &hot[2], &hot[3], &hot[4], &N32, &T32, &ldT, &ldX, &a};
+  int S32 = S;
+  void *kargs[] = {&hot[0], &hot[1], &hot[2], &hot[3], &hot[4], &N32, &T32, &ldT, &ldX, &S32, &a};
   const void *kernel = window ? window_kernel(algo, dtype, v, uniform)
                               : plain_kernel(algo, dtype, v, uniform);
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no kernel for algorithm %d", algo);
@@ -252,18 +258,99 @@ int add_window(Arr *arrs, int n, const Window &w, int64_t N) {
   return n;
 }
 
+// ------------------------------------------------------------- split calls
+//
+// Few long rows leave most CUs idle with one workgroup per row.  A plain call
+// with at most kSplitMaxRows rows then cuts every row into S segments of
+// T / S steps and runs them as N * S rows of the window kernels, the T-split
+// of the window calls done inside the library:
+//   1. every segment from carry 0, writing only its carry map (a, b);
+//   2. per row, the maps composed from the row's end (forward mirrors: its
+//      start) into the carry entering each segment (compose_carries);
+//   3. every segment again from that carry, writing the outputs.
+// The inputs are read twice.  Used only while the caller has set a workspace
+// of 3 * N * S floats (rlca_set_workspace).
+
+constexpr int64_t kSplitMaxRows = 64;    // split calls with at most this many rows
+constexpr int64_t kSplitMinRow = 32768;  // and rows at least this long
+constexpr int64_t kSplitTarget = 256;    // into about this many segments (one per CU)
+constexpr int64_t kSplitMinLen = 4096;   // of at least this many steps
+
+// Segments per row for a plain call of N rows of T steps (1: no split): the
+// smallest power of two with N * S >= kSplitTarget, T % S == 0 and
+// T / S >= kSplitMinLen, stopping early where either no longer holds.  Below
+// kSplitMinRow steps a row takes one workgroup too little time to repay the
+// two extra launches and the second read (bf16 96x16384: 9.9 us unsplit,
+// 12.1 us split into 4), and above kSplitMaxRows rows the unsplit call
+// already nears the bandwidth the split reaches (bf16 96x32768: 18.5 us
+// unsplit, 20.5 us split into 4; 64x65536: 32.4 against 22.8 us).
+int64_t split_count(int64_t N, int64_t T) {
+  if (N > kSplitMaxRows || T < kSplitMinRow) return 1;
+  int64_t S = 1;
+  while (N * S < kSplitTarget && T % (2 * S) == 0 && T / (2 * S) >= kSplitMinLen) S *= 2;
+  return S;
+}
+
+// The carry entering each segment, from the segments' maps: reverse
+// recurrences compose from the row's last segment (whose carry is the row's
+// bootstrap, or 0), forward ones from its first (the row's initial value).
+template <typename InT>
+__global__ void compose_carries(const float *__restrict__ map, const InT *__restrict__ init,
+                                float *__restrict__ cin, int64_t N, int S, bool forward) {
+  const int64_t n = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (n >= N) return;
+  float c = init != nullptr ? Bits<InT>::to_float(Bits<InT>::load(init + n)) : 0.f;
+  for (int i = 0; i < S; ++i) {
+    const int64_t seg = n * S + (forward ? i : S - 1 - i);
+    cin[seg] = c;
+    c = fmaf(map[2 * seg + 1], c, map[2 * seg]);
+  }
+}
+
 // Validate the arrays of a call (plus the window's carry vectors), then fill
 // the window fields of Args and launch.  arrs has room for n + 3 entries.
 int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const Window &w,
                         Args &a, void *stream) {
   n = add_window(arrs, n, w, N);
   if (N == 0 || a.T == 0) return RLCA_OK;
+  const int64_t S = w.on || algo == kAffine || algo == kAffineFwd ? 1 : split_count(N, a.T);
+  const bool split = S > 1 && t_ws != nullptr && t_ws_floats >= 3 * N * S;
+  if (split) arrs[n++] = Arr{"workspace", t_ws, 3 * N * S, 3 * N * S, 4, false, true, true};
   for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], N));
   RLCA_TRY(check_aliasing(arrs, n));
   a.cin = w.cin;
   a.cout = w.cout;
   a.cmap = w.cmap;
-  return launch(algo, dtype, a, stream, w.on);
+  if (!split) return launch(algo, dtype, a, stream, w.on);
+
+  float *maps = t_ws, *cins = t_ws + 2 * N * S;
+  Args a1 = a;  // 1. maps only
+  a1.N = N * S;
+  a1.T = a.T / S;
+  a1.o0 = nullptr;
+  a1.o1 = nullptr;
+  a1.cin = nullptr;
+  a1.cout = nullptr;
+  a1.cmap = maps;
+  RLCA_TRY(launch(algo, dtype, a1, stream, true, static_cast<int>(S)));
+  const bool forward = algo == kEligibility || algo == kCumsum;  // 2. compose
+  const void *init = algo == kReturns || forward ? a.boot : nullptr;
+  const dim3 grid(static_cast<unsigned>((N + 255) / 256)), block(256);
+  if (dtype == RLCA_BF16)
+    compose_carries<bf16_t><<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
+        maps, static_cast<const bf16_t *>(init), cins, N, static_cast<int>(S), forward);
+  else
+    compose_carries<float><<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
+        maps, static_cast<const float *>(init), cins, N, static_cast<int>(S), forward);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  Args a2 = a;  // 3. outputs
+  a2.N = N * S;
+  a2.T = a.T / S;
+  a2.cin = cins;
+  a2.cout = nullptr;
+  a2.cmap = nullptr;
+  return launch(algo, dtype, a2, stream, true, static_cast<int>(S));
 }
 
 // The policy-table kernels: a 256-thread workgroup per row for long rows,
@@ -852,6 +939,28 @@ int rlca_vtrace_probs_chunk(int64_t num_envs, int64_t T, int64_t num_actions, in
 const char *rlca_last_error(void) { return t_last_error.c_str(); }
 
 int rlca_version(void) { return 400; }  // 0.4.0: bf16 long rows at 8 steps per lane; rlca_variant_info takes the algorithm
+
+int rlca_set_workspace(void *workspace, int64_t bytes) {
+  if (workspace == nullptr) {
+    t_ws = nullptr;
+    t_ws_floats = 0;
+    return RLCA_OK;
+  }
+  if (bytes < 0) return fail(RLCA_EINVAL, "workspace size %lld is negative", static_cast<long long>(bytes));
+  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
+    return fail(RLCA_EINVAL, "workspace is not 4-byte aligned");
+  t_ws = static_cast<float *>(workspace);
+  t_ws_floats = bytes / 4;
+  return RLCA_OK;
+}
+
+int rlca_split_segments(int64_t num_envs, int64_t T) {
+  if (num_envs < 0 || T < 0) {
+    fail(RLCA_EINVAL, "num_envs and T must be >= 0");
+    return -1;
+  }
+  return static_cast<int>(split_count(num_envs, T));
+}
 
 int rlca_num_variants(void) { return kNumVariants; }
 

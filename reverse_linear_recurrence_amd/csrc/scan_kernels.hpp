@@ -354,7 +354,9 @@ struct RowPtrs {
   const InT *r, *v, *lr, *eq, *tv;
   const uint8_t *te, *tr;
   bool has_te, has_tr, dense_tv;
-  int64_t row;  // row index used for addressing (row 0 for rows past N)
+  int64_t row;      // row index of the launch (row 0 for rows past N): carry vectors
+  int64_t src;      // the row of the caller's arrays that holds it
+  int64_t seg_off;  // and the offset of its first step there (segment view)
 };
 
 // A lane's inputs for its K steps t0 .. t0+K-1.  issue_tile (or load_edge)
@@ -422,7 +424,7 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
   const uint8_t *trp = own;
   if constexpr (A == kRetrace) {
     // Cold stream: only a call with truncation flags waits for Args here.
-    if (rp.has_tr) trp = p.trunc + late_v(rp.row) * p.ld_trunc + t0;
+    if (rp.has_tr) trp = p.trunc + late_v(rp.src) * p.ld_trunc + rp.seg_off + t0;
   } else {
     trp = rp.has_tr ? rp.tr + f0 : own;
   }
@@ -482,7 +484,8 @@ __device__ __forceinline__ void sparse_tv(const Args &p, const RowPtrs<InT> &rp,
     for (int i = 0; i < K / 4; ++i) any_tr |= x.tr[i];
     if (any_tr != 0) {
       const InT *tv_row;
-      if constexpr (A == kVtrace) tv_row = static_cast<const InT *>(p.tv) + late_v(rp.row) * p.ld_tv;
+      if constexpr (A == kVtrace)
+        tv_row = static_cast<const InT *>(p.tv) + late_v(rp.src) * p.ld_tv + rp.seg_off;
       else tv_row = rp.tv;
 #pragma unroll
       for (int j = 0; j < K; ++j) {
@@ -596,7 +599,7 @@ __device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp,
     } else {
       if (rp.has_tr) {
         const uint8_t *trp;
-        if constexpr (A == kRetrace) trp = p.trunc + late_v(rp.row) * p.ld_trunc;
+        if constexpr (A == kRetrace) trp = p.trunc + late_v(rp.src) * p.ld_trunc + rp.seg_off;
         else trp = rp.tr;
         ld_flags_part<K>(trp + t0, lim, x.tr);
       }
@@ -859,9 +862,12 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 
   // One write of the outputs.
   const bool has_o1 = U::two_outputs && late(p.o1) != nullptr;
-  const int64_t orow = late_v(rp.row);
-  float *o0_row = p.o0 + orow * p.ld_o0;
-  float *o1_row = p.o1 + orow * p.ld_o1;
+  const int64_t orow = late_v(rp.src);
+  float *o0_row = p.o0 + orow * p.ld_o0 + rp.seg_off;
+  float *o1_row = p.o1 + orow * p.ld_o1 + rp.seg_off;
+  // Window instances with no outputs (the first pass of a split call) write
+  // only the carry vectors.
+  const bool store = row_ok && (!kChunk || late(p.o0) != nullptr);
   if constexpr (!kEdge) {
     // Non-temporal (streaming) dwordx4 stores: outputs are written once and
     // not re-read by this kernel.
@@ -892,11 +898,11 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
         __builtin_nontemporal_store(V4{lo.x, lo.y, lo.z, lo.w}, dst + lane);
         __builtin_nontemporal_store(V4{hi.x, hi.y, hi.z, hi.w}, dst + 64 + lane);
       };
-      if (row_ok) {
+      if (store) {
         put(o0_row, o0);
         if (has_o1) put(o1_row, o1);
       }
-    } else if (row_ok) {
+    } else if (store) {
 #pragma unroll
       for (int i = 0; i < K / 4; ++i)
         __builtin_nontemporal_store(V4{o0[4 * i], o0[4 * i + 1], o0[4 * i + 2], o0[4 * i + 3]},
@@ -908,7 +914,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
                                       reinterpret_cast<V4 *>(o1_row + t0) + i);
       }
     }
-  } else if (lim >= K) {
+  } else if (lim >= K && store) {
     // Ragged tile, a lane whose steps all lie in the row: as above.
 #pragma unroll
     for (int i = 0; i < K / 4; ++i)
@@ -920,7 +926,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
         __builtin_nontemporal_store(V4{o1[4 * i], o1[4 * i + 1], o1[4 * i + 2], o1[4 * i + 3]},
                                     reinterpret_cast<V4 *>(o1_row + t0) + i);
     }
-  } else {
+  } else if (store) {
 #pragma unroll
     for (int e = 0; e < K; ++e)
       if (e < lim) {
@@ -940,7 +946,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk>
 __global__ void __launch_bounds__(WPR > 1 ? 64 * WPR : 256)
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
-            int N32, int T32, int ldT, int ldX, const Args p) {
+            int N32, int T32, int ldT, int ldX, int S32, const Args p) {
   static_assert(WPR == 1 || LPR == 64, "multi-wavefront rows use whole wavefronts");
   constexpr int kWaves = WPR > 1 ? WPR : 4;
   constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
@@ -964,18 +970,31 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
   const bool row_ok = row < N32;
   const int64_t rr = row_ok ? row : 0;
   const int64_t T = T32;
+  // Segment view (window instances, S32 > 1): row rr is segment rr % S32,
+  // T steps long, of row rr / S32 of the caller's arrays.
+  int64_t src = rr, seg_off = 0;
+  if constexpr (kChunk) {
+    if (S32 > 1) {
+      const int v = static_cast<int>(rr);
+      const int n = v / S32;
+      src = n;
+      seg_off = static_cast<int64_t>(v - n * S32) * T;
+    }
+  }
   // Row stride of a hot stream: the preloaded common stride, or (mixed
   // strides) the stream's own stride from Args.
   auto ld = [&](int64_t own_ld) -> int64_t { return kUniform ? static_cast<int64_t>(ldT) : own_ld; };
-  auto in_row = [rr](const void *base, int64_t stride) {
-    return static_cast<const InT *>(base) + rr * stride;
+  auto in_row = [src, seg_off](const void *base, int64_t stride) {
+    return static_cast<const InT *>(base) + src * stride + seg_off;
   };
-  auto flag_row = [rr](const void *base, int64_t stride) {
-    return static_cast<const uint8_t *>(base) + rr * stride;
+  auto flag_row = [src, seg_off](const void *base, int64_t stride) {
+    return static_cast<const uint8_t *>(base) + src * stride + seg_off;
   };
 
   RowPtrs<InT> rp;
   rp.row = rr;
+  rp.src = src;
+  rp.seg_off = seg_off;
   rp.r = in_row(h0, ld(p.ld_r));
   rp.tv = nullptr;
   if constexpr (A == kReturns) {

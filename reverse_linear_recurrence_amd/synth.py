@@ -56,6 +56,10 @@ WORKLOADS = {
                                     clips={"rho_bar": 1.0, "c_bar": 1.0, "pg_rho_bar": 1.0}),
     "gae_bf16_256x16384": Workload("gae_bf16_256x16384", "gae", 256, 16384, "bf16", 105,
                                    gamma=0.999, lam=0.97, p_term=0.0005, p_trunc=0.0002),
+    # Few long rows (split calls when a workspace is set), at the long-horizon
+    # workload's rates.
+    "gae_bf16_16x262144": Workload("gae_bf16_16x262144", "gae", 16, 262144, "bf16", 110,
+                                   gamma=0.999, lam=0.97, p_term=0.0005, p_trunc=0.0002),
     # Forward-time mirrors, at the GAE workload's shape and boundary rates.
     "eligibility_4096x128": Workload("eligibility_4096x128", "eligibility", 4096, 128, "f32",
                                      106, gamma=0.99, lam=0.95, p_term=0.005, p_trunc=0.002),

@@ -299,3 +299,36 @@ def test_policy_table_window_entry_points_validate(lib):
     assert vtc(cmap=C_MAP + 2) == rl.RLCA_EINVAL and "carry_map" in err(lib)
     assert vtc(cout=LP + 16) == rl.RLCA_EALIAS and "log_pi" in err(lib)
     assert vtc(cmap=C_OUT) == rl.RLCA_EALIAS and "carry_out" in err(lib)
+
+
+def test_split_segments_rule(lib):
+    # the smallest power of two S with N * S >= 256, T % S == 0 and
+    # T / S >= 4096, stopping where either would fail; no split above 64 rows
+    # or below 32768 steps per row
+    cases = {(64, 65536): 4, (16, 262144): 16, (1, 32768): 8, (1, 1 << 20): 256,
+             (3, 32768): 8, (65, 65536): 1, (127, 65536): 1, (128, 32768): 1,
+             (3, 16384): 1, (100, 16384): 1, (8, 4096): 1, (2, 3 * 16384): 8,
+             (2, 32769): 1, (2, 2 * 32769): 2, (0, 0): 1}
+    for (N, T), S in cases.items():
+        assert rl.rlca_split_segments(N, T) == S, (N, T)
+    with pytest.raises(ValueError):
+        rl.rlca_split_segments(-1, 8)
+    assert lib.rlca_split_segments(4, -8) == -1 and "T" in err(lib)
+
+
+def test_workspace_is_validated(lib):
+    try:
+        assert lib.rlca_set_workspace(BASE + 0x8000002, 64) == rl.RLCA_EINVAL
+        assert "aligned" in err(lib)
+        assert lib.rlca_set_workspace(BASE + 0x8000000, -4) == rl.RLCA_EINVAL
+        # A call that splits (16 rows of 65536 steps: 16 segments each) checks
+        # its 3 * 16 * 16 floats of workspace against its arrays before any
+        # launch.
+        assert lib.rlca_set_workspace(ADV + 64, 1 << 20) == rl.RLCA_OK
+        assert gae(lib, N=16, T=65536) == rl.RLCA_EALIAS and "workspace" in err(lib)
+        assert lib.rlca_set_workspace(R + 4 * 65536 * 16 - 8, 1 << 20) == rl.RLCA_OK
+        assert gae(lib, N=16, T=65536) == rl.RLCA_EALIAS and "rewards" in err(lib)
+        with pytest.raises(ValueError):
+            rl.rlca_set_workspace(torch.empty(16))  # not on a GPU
+    finally:
+        assert lib.rlca_set_workspace(None, 0) == rl.RLCA_OK
