@@ -1,9 +1,9 @@
 """Split calls (few long rows) on the GPU against the oracle.
 
 With a workspace set, a plain call on at most 64 rows of at least 32768 steps
-cuts each row into
-S segments and runs them as N * S rows of the window kernels (maps only,
-compose, outputs): the window calls' split along T inside one library call.
+cuts each row into S segments and runs them as N * S rows of the window
+kernels (maps only, compose, outputs): the window calls' split along T inside
+one library call.
 The results must match the oracle to the same tolerance as an unsplit call,
 for every algorithm, with episode boundaries that fall inside and across
 segment borders and with carries that cross every border (no boundaries).
