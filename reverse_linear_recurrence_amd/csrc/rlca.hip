@@ -294,16 +294,58 @@ int64_t split_count(int64_t N, int64_t T) {
 // The carry entering each segment, from the segments' maps: reverse
 // recurrences compose from the row's last segment (whose carry is the row's
 // bootstrap, or 0), forward ones from its first (the row's initial value).
+// One wavefront per row.  Its lanes load the maps of 64 consecutive segments
+// at once (every chunk's loads are issued before the first is used), and a
+// shuffle scan composes them: lane j ends with the composite of the chunk's
+// maps from its own to the chunk's end in composition order.  Chunks are
+// taken in that order, each starting from the carry the previous one hands
+// on.
 template <typename InT>
-__global__ void compose_carries(const float *__restrict__ map, const InT *__restrict__ init,
-                                float *__restrict__ cin, int64_t N, int S, bool forward) {
-  const int64_t n = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (n >= N) return;
+__global__ void __launch_bounds__(64)
+compose_carries(const float *__restrict__ map, const InT *__restrict__ init,
+                float *__restrict__ cin, int S, bool forward) {
+  constexpr int kMaxChunks = 4;
+  static_assert(kSplitTarget <= 64 * kMaxChunks, "S <= kSplitTarget segments per row");
+  const int64_t n = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int nchunks = (S + 63) / 64;
+  // chunk k, lane j: the segment j-th in composition order within the chunk
+  auto seg_of = [&](int k, int j) {
+    const int i = 64 * k + j;  // position in composition order
+    return forward ? i : S - 1 - i;
+  };
+  float ma[kMaxChunks], mb[kMaxChunks];
+#pragma unroll
+  for (int k = 0; k < kMaxChunks; ++k) {
+    ma[k] = 0.f;
+    mb[k] = 1.f;  // identity past the row's segments
+    if (k < nchunks && 64 * k + lane < S) {
+      const int64_t e = n * S + seg_of(k, lane);
+      ma[k] = map[2 * e];
+      mb[k] = map[2 * e + 1];
+    }
+  }
   float c = init != nullptr ? Bits<InT>::to_float(Bits<InT>::load(init + n)) : 0.f;
-  for (int i = 0; i < S; ++i) {
-    const int64_t seg = n * S + (forward ? i : S - 1 - i);
-    cin[seg] = c;
-    c = fmaf(map[2 * seg + 1], c, map[2 * seg]);
+  for (int k = 0; k < nchunks; ++k) {
+    // Inclusive scan in composition order: after it, lane j holds
+    // f_j o f_{j-1} o ... o f_0 (f_0 applied first).
+    float a = ma[k], b = mb[k];
+#pragma unroll
+    for (int d = 1; d < 64; d *= 2) {
+      const float pa = __shfl_up(a, d), pb = __shfl_up(b, d);
+      if (lane >= d) {
+        a = fmaf(b, pa, a);
+        b = b * pb;
+      }
+    }
+    // The carry entering lane j's segment: lanes 0 .. j-1 applied to c.
+    float ea = __shfl_up(a, 1), eb = __shfl_up(b, 1);
+    if (lane == 0) {
+      ea = 0.f;
+      eb = 1.f;
+    }
+    if (64 * k + lane < S) cin[n * S + seg_of(k, lane)] = fmaf(eb, c, ea);
+    c = fmaf(__shfl(b, 63), c, __shfl(a, 63));
   }
 }
 
@@ -335,13 +377,13 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const 
   RLCA_TRY(launch(algo, dtype, a1, stream, true, static_cast<int>(S)));
   const bool forward = algo == kEligibility || algo == kCumsum;  // 2. compose
   const void *init = algo == kReturns || forward ? a.boot : nullptr;
-  const dim3 grid(static_cast<unsigned>((N + 255) / 256)), block(256);
+  const dim3 grid(static_cast<unsigned>(N)), block(64);
   if (dtype == RLCA_BF16)
     compose_carries<bf16_t><<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
-        maps, static_cast<const bf16_t *>(init), cins, N, static_cast<int>(S), forward);
+        maps, static_cast<const bf16_t *>(init), cins, static_cast<int>(S), forward);
   else
     compose_carries<float><<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
-        maps, static_cast<const float *>(init), cins, N, static_cast<int>(S), forward);
+        maps, static_cast<const float *>(init), cins, static_cast<int>(S), forward);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   Args a2 = a;  // 3. outputs
