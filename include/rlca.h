@@ -521,14 +521,16 @@ typedef enum {
 } rlca_algo;
 
 /*
- * Split calls: few long rows.  With one workgroup per row, a plain call
- * (rlca_returns, rlca_gae, rlca_td_lambda, rlca_vtrace, rlca_retrace,
- * rlca_eligibility_trace, rlca_episodic_cumsum) on at most 64 rows of at
- * least 32768 steps leaves most compute units idle.  When the calling thread has set a
- * workspace, such a call cuts every row into S = rlca_split_segments(N, T)
+ * Split calls: few long rows.  With one workgroup per row, a call on at
+ * most 64 rows of at least 32768 steps leaves most compute units idle.  When
+ * the calling thread has set a workspace, such a call of the scan family (the
+ * seven algorithms, their window forms rlca_*_chunk and rlca_affine_scan; not
+ * the policy-table calls) cuts every row into S = rlca_split_segments(N, T)
  * segments of T / S steps and runs three launches on the same stream: the
  * segments from carry 0, writing only their carry maps to the workspace; a
- * small kernel composing, per row, the carry that enters each segment; and
+ * small kernel composing, per row, the carry that enters each segment from
+ * the row's starting carry (carry_in, or the bootstrap or initial value of a
+ * plain call) and, for window calls, the row's carry_out and carry_map; and
  * the segments again from those carries, writing the outputs.  It is the
  * window calls' split along T (their carry and carry-map conventions) done
  * inside the library; it reads the inputs twice and computes the same

@@ -247,8 +247,12 @@ struct Window {
 };
 constexpr Window kNoWindow{false, nullptr, nullptr, nullptr};
 
+// Room a call's argument table keeps after its own arrays: the window's
+// three carry vectors and a split call's workspace.
+constexpr int kExtraArrs = 4;
+
 // Append the window's carry vectors to a call's arrays (arrs has room for
-// n + 3 entries); returns the new count.
+// them); returns the new count.
 int add_window(Arr *arrs, int n, const Window &w, int64_t N) {
   if (w.on) {
     arrs[n++] = Arr{"carry_in", w.cin, N, N, 4, false, false, true};
@@ -260,13 +264,14 @@ int add_window(Arr *arrs, int n, const Window &w, int64_t N) {
 
 // ------------------------------------------------------------- split calls
 //
-// Few long rows leave most CUs idle with one workgroup per row.  A plain call
-// with at most kSplitMaxRows rows then cuts every row into S segments of
-// T / S steps and runs them as N * S rows of the window kernels, the T-split
-// of the window calls done inside the library:
+// Few long rows leave most CUs idle with one workgroup per row.  A call (plain,
+// window form or generic scan) with at most kSplitMaxRows rows then cuts every
+// row into S segments of T / S steps and runs them as N * S rows of the
+// window kernels, the T-split of the window calls done inside the library:
 //   1. every segment from carry 0, writing only its carry map (a, b);
 //   2. per row, the maps composed from the row's end (forward mirrors: its
-//      start) into the carry entering each segment (compose_carries);
+//      start) into the carry entering each segment, and for window calls the
+//      row's carry out and carry map (compose_carries);
 //   3. every segment again from that carry, writing the outputs.
 // The inputs are read twice.  Used only while the caller has set a workspace
 // of 3 * N * S floats (rlca_set_workspace).
@@ -276,7 +281,7 @@ constexpr int64_t kSplitMinRow = 32768;  // and rows at least this long
 constexpr int64_t kSplitTarget = 256;    // into about this many segments (one per CU)
 constexpr int64_t kSplitMinLen = 4096;   // of at least this many steps
 
-// Segments per row for a plain call of N rows of T steps (1: no split): the
+// Segments per row for a call of N rows of T steps (1: no split): the
 // smallest power of two with N * S >= kSplitTarget, T % S == 0 and
 // T / S >= kSplitMinLen, stopping early where either no longer holds.  Below
 // kSplitMinRow steps a row takes one workgroup too little time to repay the
@@ -294,6 +299,10 @@ int64_t split_count(int64_t N, int64_t T) {
 // The carry entering each segment, from the segments' maps: reverse
 // recurrences compose from the row's last segment (whose carry is the row's
 // bootstrap, or 0), forward ones from its first (the row's initial value).
+// The row's starting carry is the caller's carry_in (window calls, fp32) or
+// the plain call's bootstrap or initial value (input dtype), else 0.  Window
+// calls also get the row's carry_out (the last segment's outgoing carry in
+// composition order) and its carry map (the composite of every segment map).
 // One wavefront per row.  Its lanes load the maps of 64 consecutive segments
 // at once (every chunk's loads are issued before the first is used), and a
 // shuffle scan composes them: lane j ends with the composite of the chunk's
@@ -303,7 +312,8 @@ int64_t split_count(int64_t N, int64_t T) {
 template <typename InT>
 __global__ void __launch_bounds__(64)
 compose_carries(const float *__restrict__ map, const InT *__restrict__ init,
-                float *__restrict__ cin, int S, bool forward) {
+                const float *__restrict__ init_f32, float *__restrict__ cin, int S,
+                bool forward, float *__restrict__ cout, float *__restrict__ cmap) {
   constexpr int kMaxChunks = 4;
   static_assert(kSplitTarget <= 64 * kMaxChunks, "S <= kSplitTarget segments per row");
   const int64_t n = blockIdx.x;
@@ -325,7 +335,10 @@ compose_carries(const float *__restrict__ map, const InT *__restrict__ init,
       mb[k] = map[2 * e + 1];
     }
   }
-  float c = init != nullptr ? Bits<InT>::to_float(Bits<InT>::load(init + n)) : 0.f;
+  float c = init_f32 != nullptr ? init_f32[n]
+             : init != nullptr  ? Bits<InT>::to_float(Bits<InT>::load(init + n))
+                                : 0.f;
+  float ta = 0.f, tb = 1.f;  // the composite of the chunks so far
   for (int k = 0; k < nchunks; ++k) {
     // Inclusive scan in composition order: after it, lane j holds
     // f_j o f_{j-1} o ... o f_0 (f_0 applied first).
@@ -345,17 +358,30 @@ compose_carries(const float *__restrict__ map, const InT *__restrict__ init,
       eb = 1.f;
     }
     if (64 * k + lane < S) cin[n * S + seg_of(k, lane)] = fmaf(eb, c, ea);
-    c = fmaf(__shfl(b, 63), c, __shfl(a, 63));
+    const float ka = __shfl(a, 63), kb = __shfl(b, 63);
+    c = fmaf(kb, c, ka);
+    ta = fmaf(kb, ta, ka);
+    tb = kb * tb;
+  }
+  if (lane == 0) {
+    if (cout != nullptr) cout[n] = c;
+    if (cmap != nullptr) {
+      cmap[2 * n] = ta;
+      cmap[2 * n + 1] = tb;
+    }
   }
 }
 
-// Validate the arrays of a call (plus the window's carry vectors), then fill
-// the window fields of Args and launch.  arrs has room for n + 3 entries.
-int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const Window &w,
-                        Args &a, void *stream) {
+// Validate the arrays of a call (plus the window's carry vectors and a split
+// call's workspace), then fill the window fields of Args and launch.  The
+// call's n arrays come first in arrs, which has room for kExtraArrs more.
+template <int kCap>
+int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n,
+                        const Window &w, Args &a, void *stream) {
+  if (n + kExtraArrs > kCap) return fail(RLCA_EINVAL, "internal: argument table too small");
   n = add_window(arrs, n, w, N);
   if (N == 0 || a.T == 0) return RLCA_OK;
-  const int64_t S = w.on || algo == kAffine || algo == kAffineFwd ? 1 : split_count(N, a.T);
+  const int64_t S = split_count(N, a.T);
   const bool split = S > 1 && t_ws != nullptr && t_ws_floats >= 3 * N * S;
   if (split) arrs[n++] = Arr{"workspace", t_ws, 3 * N * S, 3 * N * S, 4, false, true, true};
   for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], N));
@@ -375,15 +401,19 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr *arrs, int n, const 
   a1.cout = nullptr;
   a1.cmap = maps;
   RLCA_TRY(launch(algo, dtype, a1, stream, true, static_cast<int>(S)));
-  const bool forward = algo == kEligibility || algo == kCumsum;  // 2. compose
-  const void *init = algo == kReturns || forward ? a.boot : nullptr;
+  // 2. compose: from the caller's carry_in (window calls), or the bootstrap of
+  // returns or initial value of the forward mirrors (plain calls)
+  const bool forward = algo == kEligibility || algo == kCumsum || algo == kAffineFwd;
+  const void *init = !w.on && (algo == kReturns || forward) ? a.boot : nullptr;
   const dim3 grid(static_cast<unsigned>(N)), block(64);
   if (dtype == RLCA_BF16)
     compose_carries<bf16_t><<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
-        maps, static_cast<const bf16_t *>(init), cins, static_cast<int>(S), forward);
+        maps, static_cast<const bf16_t *>(init), w.cin, cins, static_cast<int>(S), forward,
+        w.cout, w.cmap);
   else
     compose_carries<float><<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
-        maps, static_cast<const float *>(init), cins, static_cast<int>(S), forward);
+        maps, static_cast<const float *>(init), w.cin, cins, static_cast<int>(S), forward,
+        w.cout, w.cmap);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   Args a2 = a;  // 3. outputs
@@ -436,7 +466,7 @@ int returns_impl(int64_t num_envs, int64_t T, int dtype, const void *rewards, in
     return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
   const int64_t es = esize_of(dtype);
   const bool tv_used = truncated != nullptr;
-  Arr arrs[9] = {
+  Arr arrs[6 + kExtraArrs] = {
       {"rewards", rewards, ld_rewards, T, es, true, false},
       {"terminated", terminated, ld_terminated, T, 1, false, false},
       {"truncated", truncated, ld_truncated, T, 1, false, false},
@@ -470,7 +500,7 @@ int gae_like(int algo, int64_t num_envs, int64_t T, int dtype, const void *rewar
     return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
   const int64_t es = esize_of(dtype);
   const bool tv_used = truncated != nullptr;
-  Arr arrs[10] = {
+  Arr arrs[7 + kExtraArrs] = {
       {"rewards", rewards, ld_rewards, T, es, true, false},
       {"values", values, ld_values, T + 1, es, true, false},
       {"terminated", terminated, ld_terminated, T, 1, false, false},
@@ -509,7 +539,7 @@ int vtrace_impl(int64_t num_envs, int64_t T, int dtype, const void *rewards, int
     return fail(RLCA_EINVAL, "truncated is given but trunc_values is NULL");
   const int64_t es = esize_of(dtype);
   const bool tv_used = truncated != nullptr;
-  Arr arrs[11] = {
+  Arr arrs[8 + kExtraArrs] = {
       {"rewards", rewards, ld_rewards, T, es, true, false},
       {"values", values, ld_values, T + 1, es, true, false},
       {"log_rhos", log_rhos, ld_log_rhos, T, es, true, false},
@@ -544,7 +574,7 @@ int retrace_impl(int64_t num_envs, int64_t T, int dtype, const void *rewards, in
   RLCA_TRY(check_unit("lam", lam));
   RLCA_TRY(check_clip("c_bar", c_bar));
   const int64_t es = esize_of(dtype);
-  Arr arrs[10] = {
+  Arr arrs[7 + kExtraArrs] = {
       {"rewards", rewards, ld_rewards, T, es, true, false},
       {"q_taken", q_taken, ld_q_taken, T, es, true, false},
       {"exp_q_next", exp_q_next, ld_exp_q_next, T, es, true, false},
@@ -575,7 +605,7 @@ int forward_like(int algo, int64_t num_envs, int64_t T, int dtype, const void *x
   RLCA_TRY(check_unit("gamma", gamma));
   RLCA_TRY(check_unit("lam", lam));
   const int64_t es = esize_of(dtype);
-  Arr arrs[8] = {
+  Arr arrs[5 + kExtraArrs] = {
       {"x", x, ld_x, T, es, true, false},
       {"terminated", terminated, ld_terminated, T, 1, false, false},
       {"truncated", truncated, ld_truncated, T, 1, false, false},
@@ -891,7 +921,7 @@ int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype, const void *alpha,
   if (reverse != 0 && reverse != 1)
     return fail(RLCA_EINVAL, "reverse = %d must be 0 or 1", reverse);
   const int64_t es = esize_of(dtype);
-  Arr arrs[7] = {
+  Arr arrs[4 + kExtraArrs] = {
       {"alpha", alpha, ld_alpha, T, es, true, false},
       {"beta", beta, ld_beta, T, es, true, false},
       {"reset", reset, ld_reset, T, 1, false, false},

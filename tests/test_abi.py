@@ -332,3 +332,21 @@ def test_workspace_is_validated(lib):
             rl.rlca_set_workspace(torch.empty(16))  # not on a GPU
     finally:
         assert lib.rlca_set_workspace(None, 0) == rl.RLCA_OK
+
+
+def test_split_window_call_validates_its_workspace(lib):
+    # A window call that splits checks the window's three carry vectors and
+    # the workspace, all beside its own arrays (the argument table has room
+    # for four more entries), before any launch.
+    N, T = 16, 65536
+    try:
+        assert lib.rlca_set_workspace(R + 64, 1 << 20) == rl.RLCA_OK
+        for _ in range(3):
+            assert gae_chunk(lib, N=N, T=T, r=R) == rl.RLCA_EALIAS
+            assert "workspace" in err(lib)
+            assert lib.rlca_returns_chunk(N, T, F32, R, T, None, T, None, T, None, T, C_IN, 0.9,
+                                          ADV, T, C_OUT, C_MAP, None) == rl.RLCA_EALIAS
+        assert lib.rlca_set_workspace(C_MAP + 8, 1 << 20) == rl.RLCA_OK
+        assert gae_chunk(lib, N=N, T=T) == rl.RLCA_EALIAS and "carry_map" in err(lib)
+    finally:
+        assert lib.rlca_set_workspace(None, 0) == rl.RLCA_OK

@@ -1,9 +1,10 @@
 """Split calls (few long rows) on the GPU against the oracle.
 
-With a workspace set, a plain call on at most 64 rows of at least 32768 steps
-cuts each row into S segments and runs them as N * S rows of the window
-kernels (maps only, compose, outputs): the window calls' split along T inside
-one library call.
+With a workspace set, a call (plain, window form or generic scan) on at most
+64 rows of at least 32768 steps cuts each row into S segments and runs them as
+N * S rows of the window kernels (maps only, compose, outputs): the window
+calls' split along T inside one library call.  Window calls also get the
+row's carry_out and carry map from the composition.
 The results must match the oracle to the same tolerance as an unsplit call,
 for every algorithm, with episode boundaries that fall inside and across
 segment borders and with carries that cross every border (no boundaries).
@@ -12,9 +13,12 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import reverse_linear_recurrence_amd as rl
 from gpu_common import (ALGOS, DEFAULT_PARAMS, TOL, assert_close, params32, random_inputs,
                         run_gpu, run_oracle, to_device)
+from test_gpu_window import (affine_inputs, check_window, run_gpu_chunk, run_oracle_chunk,
+                             window_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -108,3 +112,40 @@ def test_split_and_unsplit_calls_agree():
     finally:
         rl.rlca_set_workspace(None)
     assert_close(split, plain, TOL["f32"], "td_lambda/split vs unsplit")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_split_window_call_matches_oracle(algo, dtype, workspace):
+    # carry in from the caller; carry out and carry map of the whole row
+    p = params32(dict(DEFAULT_PARAMS, c_bar=0.95, rho_bar=1.05))
+    N, T = 3, 32768
+    S = rl.rlca_split_segments(N, T)
+    for sparse in (False, True):
+        d, c = window_inputs(algo, N, T, 501 + sparse, dtype, sparse)
+        workspace.fill_(float("nan"))
+        print(algo, dtype, "window N", N, "T", T, "S", S, "sparse", sparse, flush=True)
+        got = run_gpu_chunk(algo, to_device(d), p, c.cuda())
+        assert np.all(np.isfinite(workspace[:2 * N * S].cpu().numpy())), "did not split"
+        check_window(got, run_oracle_chunk(algo, d, p, c), dtype,
+                     "%s/%s split window sparse=%s" % (algo, dtype, sparse))
+
+
+@pytest.mark.parametrize("reverse", [True, False])
+def test_split_affine_scan_matches_oracle(reverse, workspace):
+    N, T = 2, 65536
+    S = rl.rlca_split_segments(N, T)
+    assert S == 16
+    for p_reset, with_reset in ((0.0, False), (0.001, True)):
+        al, be, rs, c = affine_inputs(N, T, 601, "f32", p_reset)
+        workspace.fill_(float("nan"))
+        A, co, cm = rl.rlca_affine_scan(al.cuda(), be.cuda(), rs.cuda() if with_reset else None,
+                                        reverse=reverse, carry_in=c.cuda())
+        torch.cuda.synchronize()
+        assert np.all(np.isfinite(workspace[:2 * N * S].cpu().numpy())), "did not split"
+        rA, rco, rcm = oracle.affine_scan(al, be, rs if with_reset else None, c,
+                                          reverse=reverse)
+        got = ({"A": A.double().cpu().numpy()}, co.double().cpu().numpy(),
+               cm.double().cpu().numpy())
+        check_window(got, ({"A": rA}, rco, rcm), "f32",
+                     "affine split rev=%s p_reset=%g" % (reverse, p_reset))
