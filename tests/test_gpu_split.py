@@ -149,3 +149,37 @@ def test_split_affine_scan_matches_oracle(reverse, workspace):
                cm.double().cpu().numpy())
         check_window(got, ({"A": rA}, rco, rcm), "f32",
                      "affine split rev=%s p_reset=%g" % (reverse, p_reset))
+
+
+def test_split_call_in_a_hip_graph_replays_like_eager_calls(workspace):
+    # The three launches of a split call (both passes and the compose kernel)
+    # captured once; every replay, with eager split calls and in-place input
+    # updates in between, equals the eager call bitwise.
+    p = params32(DEFAULT_PARAMS)
+    N, T = 4, 65536
+    assert rl.rlca_split_segments(N, T) == 16
+    dev = to_device(random_inputs("gae", N, T, 701, "f32", p_term=0.0005, p_trunc=0.0005))
+    args = (dev["rewards"], dev["values"], dev["terminated"], dev["truncated"],
+            dev["trunc_values"])
+    adv = torch.empty(N, T, device="cuda")
+    tgt = torch.empty_like(adv)
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            rl.rlca_gae(*args, gamma=p["gamma"], lam=p["lam"], advantages=adv, targets=tgt)
+    torch.cuda.synchronize()
+    for i in range(4):
+        if i == 2:
+            dev["rewards"].mul_(-0.5)
+        e_adv, e_tgt = rl.rlca_gae(*args, gamma=p["gamma"], lam=p["lam"])
+        adv.fill_(float("nan"))
+        tgt.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(adv, e_adv) and torch.equal(tgt, e_tgt), "replay %d" % i
+    ref = run_oracle("gae", {k: v.cpu() for k, v in dev.items()}, p)
+    assert_close({"advantages": adv.double().cpu().numpy()}, {"advantages": ref["advantages"]},
+                 TOL["f32"], "gae/split graph")
