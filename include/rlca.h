@@ -534,7 +534,11 @@ typedef enum {
  * the segments again from those carries, writing the outputs.  It is the
  * window calls' split along T (their carry and carry-map conventions) done
  * inside the library; it reads the inputs twice and computes the same
- * results up to rounding order.
+ * results up to rounding order.  Validation is the same as unsplit, all of it
+ * before the first launch; should the runtime refuse the second or third
+ * launch (RLCA_EHIP), the earlier ones stay enqueued, the workspace and (for
+ * window calls) carry_out and carry_map may hold partial results, and the
+ * outputs are not written.
  *
  * rlca_set_workspace(ptr, bytes) sets the calling thread's workspace: device
  * memory owned by the caller, 4-byte aligned; NULL switches split calls off

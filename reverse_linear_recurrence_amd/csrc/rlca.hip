@@ -403,18 +403,16 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   RLCA_TRY(launch(algo, dtype, a1, stream, true, static_cast<int>(S)));
   // 2. compose: from the caller's carry_in (window calls), or the bootstrap of
   // returns or initial value of the forward mirrors (plain calls)
-  const bool forward = algo == kEligibility || algo == kCumsum || algo == kAffineFwd;
+  bool forward = algo == kEligibility || algo == kCumsum || algo == kAffineFwd;
   const void *init = !w.on && (algo == kReturns || forward) ? a.boot : nullptr;
-  const dim3 grid(static_cast<unsigned>(N)), block(64);
-  if (dtype == RLCA_BF16)
-    compose_carries<bf16_t><<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
-        maps, static_cast<const bf16_t *>(init), w.cin, cins, static_cast<int>(S), forward,
-        w.cout, w.cmap);
-  else
-    compose_carries<float><<<grid, block, 0, static_cast<hipStream_t>(stream)>>>(
-        maps, static_cast<const float *>(init), w.cin, cins, static_cast<int>(S), forward,
-        w.cout, w.cmap);
-  const hipError_t e = hipGetLastError();
+  const float *cmaps = maps, *init_f32 = w.cin;
+  float *cout = w.cout, *cmap = w.cmap;
+  int S32 = static_cast<int>(S);
+  void *kargs[] = {&cmaps, &init, &init_f32, &cins, &S32, &forward, &cout, &cmap};
+  const void *kernel = dtype == RLCA_BF16 ? reinterpret_cast<const void *>(&compose_carries<bf16_t>)
+                                          : reinterpret_cast<const void *>(&compose_carries<float>);
+  const hipError_t e = hipLaunchKernel(kernel, dim3(static_cast<unsigned>(N)), dim3(64), kargs, 0,
+                                       static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   Args a2 = a;  // 3. outputs
   a2.N = N * S;
