@@ -50,9 +50,10 @@
  *   log_mu, trunc_eq), except the window calls' carry vectors, which are
  *   always fp32.  Arithmetic is fp32; outputs are always fp32.  Actions are
  *   int32.
- * Ownership.  The caller owns every buffer.  The library allocates no
- *   memory, keeps no per-call state, never synchronizes, and returns as soon
- *   as the work is enqueued on `stream`.
+ * Ownership.  The caller owns every buffer, the split calls' workspace
+ *   included.  The library allocates no memory, keeps no per-call state,
+ *   never synchronizes, and returns as soon as the work is enqueued on
+ *   `stream`.
  * Nullable inputs.  terminated == NULL means no terminations; truncated ==
  *   NULL means no truncations (trunc_values is then ignored and may be NULL).
  * Errors.  Arguments are validated before anything is enqueued; on any

@@ -4,8 +4,8 @@
 // Nothing here touches element data: every step of the computation runs in
 // the kernels of scan_kernels.hpp (instantiated in kernels_plain.hip and
 // kernels_window.hip) and probs_kernels.hpp (kernels_probs.hip).  A call
-// validates its arguments, picks a tiling variant, and enqueues exactly one
-// kernel on the caller's stream.
+// validates its arguments, picks a tiling variant, and enqueues one kernel on
+// the caller's stream (a split call on a few long rows: three, see below).
 
 #include <hip/hip_runtime.h>
 
