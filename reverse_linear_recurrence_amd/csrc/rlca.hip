@@ -157,23 +157,27 @@ int check_sizes(int64_t N, int64_t T, int dtype) {
   } while (0)
 
 // window: the instance with carry vectors (Args::cin, cout, cmap).
-// S > 1: segment view (window instances): args.N rows of args.T steps, row r
-// being segment r % S of row r / S of the caller's arrays.
+// S > 1: segment view (window instances): each of the args.N rows is cut
+// into S segments of args.T steps, segment y taken by grid row y.
 int launch(int algo, int dtype, const Args &args, void *stream, bool window = false, int S = 1) {
   const int v = t_forced_variant >= 0
                     ? t_forced_variant
-                    : auto_variant(args.N, args.T, dtype == RLCA_BF16, algo == kVtrace);
+                    : auto_variant(args.N * S, args.T, dtype == RLCA_BF16, algo == kVtrace);
   const Variant var = kVariants[v];
   dim3 grid, block;
   if (var.WPR > 1) {
-    grid = dim3(static_cast<unsigned>(args.N));
+    grid = dim3(static_cast<unsigned>(args.N), static_cast<unsigned>(S));
     block = dim3(64 * var.WPR);
   } else {
     const int64_t rows_per_wg = 4 * (64 / var.LPR);
-    grid = dim3(static_cast<unsigned>((args.N + rows_per_wg - 1) / rows_per_wg));
+    grid = dim3(static_cast<unsigned>((args.N + rows_per_wg - 1) / rows_per_wg),
+                static_cast<unsigned>(S));
     block = dim3(256);
   }
   Args a = args;
+  a.seg_count = S;
+  // Truncation bootstraps of the whole call: dense reads for small batches.
+  const bool dense_tv = args.N * S * args.T <= kDenseTvMaxSteps;
   // Hot streams (see scan_kernels.hpp), passed again as preloaded scalars.
   const void *hot[5] = {a.r, nullptr, nullptr, nullptr, nullptr};
   int64_t hld[5] = {a.ld_r, 0, 0, 0, 0};  // stride of each hot [N,T] stream (0: none)
@@ -182,7 +186,7 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
     case kReturns:
       hot[1] = a.term; hld[1] = a.ld_term;
       hot[2] = a.trunc; hld[2] = a.ld_trunc;
-      hot[3] = a.tv; hld[3] = a.ld_tv;
+      hot[3] = dense_tv ? a.tv : nullptr; hld[3] = a.ld_tv;
       hot[4] = a.boot;  // a [N] vector: no stride
       break;
     case kGae:
@@ -190,7 +194,7 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
       hot[1] = a.v; ldx = a.ld_v;
       hot[2] = a.term; hld[2] = a.ld_term;
       hot[3] = a.trunc; hld[3] = a.ld_trunc;
-      hot[4] = a.tv; hld[4] = a.ld_tv;
+      hot[4] = dense_tv ? a.tv : nullptr; hld[4] = a.ld_tv;
       break;
     case kVtrace:
       hot[1] = a.v; ldx = a.ld_v;
@@ -223,8 +227,7 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
   int T32 = static_cast<int>(a.T);
   int ldT = static_cast<int>(a.ld_r);
   int ldX = static_cast<int>(ldx);
-  int S32 = S;
-  void *kargs[] = {&hot[0], &hot[1], &hot[2], &hot[3], &hot[4], &N32, &T32, &ldT, &ldX, &S32, &a};
+  void *kargs[] = {&hot[0], &hot[1], &hot[2], &hot[3], &hot[4], &N32, &T32, &ldT, &ldX, &a};
   const void *kernel = window ? window_kernel(algo, dtype, v, uniform)
                               : plain_kernel(algo, dtype, v, uniform);
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no kernel for algorithm %d", algo);
@@ -393,7 +396,6 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
 
   float *maps = t_ws, *cins = t_ws + 2 * N * S;
   Args a1 = a;  // 1. maps only
-  a1.N = N * S;
   a1.T = a.T / S;
   a1.o0 = nullptr;
   a1.o1 = nullptr;
@@ -415,7 +417,6 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   Args a2 = a;  // 3. outputs
-  a2.N = N * S;
   a2.T = a.T / S;
   a2.cin = cins;
   a2.cout = nullptr;

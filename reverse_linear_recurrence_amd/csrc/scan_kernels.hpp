@@ -90,6 +90,7 @@ struct Args {
   const float *cin;
   float *cout;
   float *cmap;
+  int seg_count = 1;  // window instances: segments per row (gridDim.y; 1 unless split)
 };
 
 // Hot streams: the (up to) five arrays each algorithm reads at the start of a
@@ -111,7 +112,9 @@ struct Args {
 // Batches of at most this many env-steps read trunc_values as whole vectors
 // with the other loads, instead of a dependent load at truncated steps after
 // the flags arrive: at that size the kernel is latency bound and the extra
-// bytes cost less than the extra memory round trip.
+// bytes cost less than the extra memory round trip.  The host decides (for
+// the whole call, split or not) and passes the hot bootstrap pointer only
+// for dense reads; sparse reads take the bootstraps' own pointer from Args.
 #ifndef RLCA_DENSE_TV_MAX_STEPS
 #define RLCA_DENSE_TV_MAX_STEPS (int64_t(1) << 20)
 #endif
@@ -354,9 +357,9 @@ struct RowPtrs {
   const InT *r, *v, *lr, *eq, *tv;
   const uint8_t *te, *tr;
   bool has_te, has_tr, dense_tv;
-  int64_t row;      // row index of the launch (row 0 for rows past N): carry vectors
-  int64_t src;      // the row of the caller's arrays that holds it
-  int64_t seg_off;  // and the offset of its first step there (segment view)
+  int64_t row;      // row index (row 0 for rows past N)
+  int64_t src;      // the row of the caller's arrays holding the data (= row)
+  int64_t seg_off;  // the offset of the first step there (segment view)
 };
 
 // A lane's inputs for its K steps t0 .. t0+K-1.  issue_tile (or load_edge)
@@ -483,10 +486,10 @@ __device__ __forceinline__ void sparse_tv(const Args &p, const RowPtrs<InT> &rp,
 #pragma unroll
     for (int i = 0; i < K / 4; ++i) any_tr |= x.tr[i];
     if (any_tr != 0) {
-      const InT *tv_row;
-      if constexpr (A == kVtrace)
-        tv_row = static_cast<const InT *>(p.tv) + late_v(rp.src) * p.ld_tv + rp.seg_off;
-      else tv_row = rp.tv;
+      // The bootstraps' own row pointer (the hot one is null when they are
+      // read sparsely).
+      const InT *tv_row =
+          static_cast<const InT *>(p.tv) + late_v(rp.src) * p.ld_tv + rp.seg_off;
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         x.ts[j] = 0.f;
@@ -701,7 +704,8 @@ template <int A, typename InT>
 __device__ __forceinline__ WindowIn window_in(const Args &p, const RowPtrs<InT> &rp, int64_t T,
                                               float &carry) {
   WindowIn w{0.f, false};
-  const int64_t row = late_v(rp.row);
+  // The carry vectors hold one entry per segment (row-major over segments).
+  const int64_t row = late_v(rp.row) * late(p.seg_count) + blockIdx.y;
   if (p.cin != nullptr) carry = p.cin[row];
   if constexpr (A == kRetrace) w.lr0 = Ld<InT>::one(rp.lr);
   if constexpr (Uses<A>::prev_flags)
@@ -723,10 +727,11 @@ __device__ __forceinline__ void window_out(const Args &p, const RowPtrs<InT> &rp
   float f = 1.f;
   if constexpr (A == kRetrace) f = p.lam * fminf(p.c_bar, __expf(w.lr0));
   if constexpr (Uses<A>::prev_flags) f = w.done_last ? 0.f : 1.f;
-  if (p.cout != nullptr) p.cout[rp.row] = f * carry;
+  const int64_t row = late_v(rp.row) * late(p.seg_count) + blockIdx.y;
+  if (p.cout != nullptr) p.cout[row] = f * carry;
   if (p.cmap != nullptr) {
-    p.cmap[2 * rp.row] = f * m.a;
-    p.cmap[2 * rp.row + 1] = f * m.b;
+    p.cmap[2 * row] = f * m.a;
+    p.cmap[2 * row + 1] = f * m.b;
   }
 }
 
@@ -946,7 +951,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk>
 __global__ void __launch_bounds__(WPR > 1 ? 64 * WPR : 256)
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
-            int N32, int T32, int ldT, int ldX, int S32, const Args p) {
+            int N32, int T32, int ldT, int ldX, const Args p) {
   static_assert(WPR == 1 || LPR == 64, "multi-wavefront rows use whole wavefronts");
   constexpr int kWaves = WPR > 1 ? WPR : 4;
   constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
@@ -970,17 +975,11 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
   const bool row_ok = row < N32;
   const int64_t rr = row_ok ? row : 0;
   const int64_t T = T32;
-  // Segment view (window instances, S32 > 1): row rr is segment rr % S32,
-  // T steps long, of row rr / S32 of the caller's arrays.
-  int64_t src = rr, seg_off = 0;
-  if constexpr (kChunk) {
-    if (S32 > 1) {
-      const int v = static_cast<int>(rr);
-      const int n = v / S32;
-      src = n;
-      seg_off = static_cast<int64_t>(v - n * S32) * T;
-    }
-  }
+  // Segment view (window instances of a split call): the launch has one
+  // grid row per segment, and workgroups of grid row y take segment y, T
+  // steps long, of their rows (no argument is read before the loads).
+  const int64_t src = rr;
+  const int64_t seg_off = kChunk ? static_cast<int64_t>(blockIdx.y) * T : 0;
   // Row stride of a hot stream: the preloaded common stride, or (mixed
   // strides) the stream's own stride from Args.
   auto ld = [&](int64_t own_ld) -> int64_t { return kUniform ? static_cast<int64_t>(ldT) : own_ld; };
@@ -1003,7 +1002,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     rp.tv = in_row(h3, ld(p.ld_tv));
     rp.has_te = h1 != nullptr;
     rp.has_tr = h2 != nullptr;
-    rp.dense_tv = h3 != nullptr && static_cast<int64_t>(N32) * T <= kDenseTvMaxSteps;
+    rp.dense_tv = h3 != nullptr;
   } else if constexpr (A == kGae || A == kTdLambda) {
     rp.v = in_row(h1, kUniform ? static_cast<int64_t>(ldX) : p.ld_v);
     rp.te = flag_row(h2, ld(p.ld_term));
@@ -1011,7 +1010,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     rp.tv = in_row(h4, ld(p.ld_tv));
     rp.has_te = h2 != nullptr;
     rp.has_tr = h3 != nullptr;
-    rp.dense_tv = h4 != nullptr && static_cast<int64_t>(N32) * T <= kDenseTvMaxSteps;
+    rp.dense_tv = h4 != nullptr;
   } else if constexpr (A == kVtrace) {
     rp.v = in_row(h1, kUniform ? static_cast<int64_t>(ldX) : p.ld_v);
     rp.lr = in_row(h2, ld(p.ld_lr));
