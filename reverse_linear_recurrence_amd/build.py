@@ -36,6 +36,10 @@ def compile_command(src, obj):
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # Leading scalar kernel arguments are preloaded into SGPRs.
             "-mllvm", "-amdgpu-kernarg-preload-count=16",
+            # Host code: a stack guard after local arrays, so that a write past
+            # an argument table aborts (in the CPU tests) instead of corrupting
+            # the caller's stack.
+            "-Xarch_host", "-fstack-protector-strong",
             "-Wall", "-Wextra", "-I", INCLUDE, "-I", CSRC, src, "-o", obj]
 
 

@@ -983,10 +983,10 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
   // Row stride of a hot stream: the preloaded common stride, or (mixed
   // strides) the stream's own stride from Args.
   auto ld = [&](int64_t own_ld) -> int64_t { return kUniform ? static_cast<int64_t>(ldT) : own_ld; };
-  auto in_row = [src, seg_off](const void *base, int64_t stride) {
+  auto in_row = [&](const void *base, int64_t stride) {
     return static_cast<const InT *>(base) + src * stride + seg_off;
   };
-  auto flag_row = [src, seg_off](const void *base, int64_t stride) {
+  auto flag_row = [&](const void *base, int64_t stride) {
     return static_cast<const uint8_t *>(base) + src * stride + seg_off;
   };
 
