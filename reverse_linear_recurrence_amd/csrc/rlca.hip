@@ -24,10 +24,12 @@
 namespace rlca {
 
 // The public algorithm codes of rlca_variant_info are the kernels' own.
-static_assert(RLCA_ALGO_RETURNS == kReturns && RLCA_ALGO_GAE == kGae &&
-                  RLCA_ALGO_TD_LAMBDA == kTdLambda && RLCA_ALGO_VTRACE == kVtrace &&
-                  RLCA_ALGO_RETRACE == kRetrace && RLCA_ALGO_ELIGIBILITY == kEligibility &&
-                  RLCA_ALGO_CUMSUM == kCumsum && RLCA_ALGO_AFFINE == kAffine,
+constexpr bool same_code(int public_code, int kernel_code) { return public_code == kernel_code; }
+static_assert(same_code(RLCA_ALGO_RETURNS, kReturns) && same_code(RLCA_ALGO_GAE, kGae) &&
+                  same_code(RLCA_ALGO_TD_LAMBDA, kTdLambda) &&
+                  same_code(RLCA_ALGO_VTRACE, kVtrace) && same_code(RLCA_ALGO_RETRACE, kRetrace) &&
+                  same_code(RLCA_ALGO_ELIGIBILITY, kEligibility) &&
+                  same_code(RLCA_ALGO_CUMSUM, kCumsum) && same_code(RLCA_ALGO_AFFINE, kAffine),
               "rlca_algo and Algo disagree");
 namespace {
 
