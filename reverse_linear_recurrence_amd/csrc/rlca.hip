@@ -167,15 +167,15 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
                     : auto_variant(args.N * S, args.T, dtype == RLCA_BF16, algo == kVtrace);
   const Variant var = kVariants[v];
   dim3 grid, block;
+  const int waves = short_row_waves(var.WPR, var.LPR, window);
   if (var.WPR > 1) {
     grid = dim3(static_cast<unsigned>(args.N), static_cast<unsigned>(S));
-    block = dim3(64 * var.WPR);
   } else {
-    const int64_t rows_per_wg = 4 * (64 / var.LPR);
+    const int64_t rows_per_wg = waves * (64 / var.LPR);
     grid = dim3(static_cast<unsigned>((args.N + rows_per_wg - 1) / rows_per_wg),
                 static_cast<unsigned>(S));
-    block = dim3(256);
   }
+  block = dim3(64 * waves);
   Args a = args;
   a.seg_count = S;
   // Truncation bootstraps of the whole call: dense reads for small batches.

@@ -47,6 +47,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "variants.hpp"
+
 namespace rlca {
 
 enum Algo : int {
@@ -944,16 +946,16 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 
 // Algo A, input type InT, K steps per lane, LPR lanes per row inside one
 // wavefront (WPR == 1), or WPR wavefronts per row (then LPR must be 64).
-// Workgroup: 256 threads (WPR == 1) or 64*WPR threads (WPR > 1).
+// Workgroup: 64 * short_row_waves(WPR, LPR, kChunk) threads.
 // h0..h4, N32, T32, ldT, ldX: the preloaded hot arguments (see above); they
 // duplicate fields of p.  kChunk: window instance (carry vector in, carry and
 // carry map out).
 template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk>
-__global__ void __launch_bounds__(WPR > 1 ? 64 * WPR : 256)
+__global__ void __launch_bounds__(64 * short_row_waves(WPR, LPR, kChunk))
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
             int N32, int T32, int ldT, int ldX, const Args p) {
   static_assert(WPR == 1 || LPR == 64, "multi-wavefront rows use whole wavefronts");
-  constexpr int kWaves = WPR > 1 ? WPR : 4;
+  constexpr int kWaves = short_row_waves(WPR, LPR, kChunk);
   constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
   constexpr int kTile = kGroup * K;
 

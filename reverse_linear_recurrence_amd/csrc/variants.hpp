@@ -13,8 +13,8 @@ struct Variant {
 };
 
 constexpr Variant kVariants[] = {
-    {16, 1, false},  // 0: tile    64 steps, 16 rows per 256-thread workgroup
-    {32, 1, false},  // 1: tile   128,  8 rows per workgroup
+    {16, 1, false},  // 0: tile    64 steps, 16 rows per 256-thread workgroup (window: 32 per 512)
+    {32, 1, false},  // 1: tile   128,  8 rows per workgroup (window: 16 per 512 threads)
     {64, 1, false},  // 2: tile   256,  4 rows per workgroup
     {64, 4, false},  // 3: tile  1024,  1 row per 256-thread workgroup
     {64, 8, false},  // 4: tile  2048,  1 row per 512-thread workgroup
@@ -38,6 +38,17 @@ constexpr int kFirstWide = 6;  // variants kFirstWide + i are variants 3 + i, wi
 // lines: 4x the line requests for 16 fp32 steps per lane.)
 constexpr int steps_per_lane(const Variant &v, bool bf16, bool vtrace) {
   return v.wide && bf16 && !vtrace ? 8 : 4;
+}
+
+// Wavefronts per workgroup: WPR for rows of whole wavefronts; otherwise 4,
+// or 8 for window instances whose rows take part of a wavefront (LPR < 64).
+// Larger workgroups write the per-row carry vectors in longer runs: the GAE
+// 4096x128 window call took 3.66 instead of 3.97 us, eligibility 2.91
+// instead of 2.99; with one row per wavefront they were slower (TD(lambda)
+// 16384x256 window 11.93 against 11.52 us), and the plain calls gained
+// nothing.
+constexpr int short_row_waves(int WPR, int LPR, bool window) {
+  return WPR > 1 ? WPR : (window && LPR < 64 ? 8 : 4);
 }
 
 inline int64_t tile_steps(const Variant &v, bool bf16, bool vtrace) {
