@@ -339,6 +339,15 @@ __device__ __forceinline__ int64_t late_v(int64_t x) {
   return x;
 }
 
+// A row index pinned the same way, in scalar registers when the whole
+// workgroup shares the row (kU: rows of whole wavefronts), so that the
+// addresses formed from it stay scalar.
+template <bool kU>
+__device__ __forceinline__ int64_t late_row(int64_t x) {
+  if constexpr (kU) return late(x);
+  else return late_v(x);
+}
+
 template <int A> struct Uses {
   static constexpr bool forward = A == kEligibility || A == kCumsum || A == kAffineFwd;
   // Reset by the flags of the step before (an episode that ended after step
@@ -702,12 +711,12 @@ struct WindowIn {
   bool done_last;
 };
 
-template <int A, typename InT>
+template <int A, typename InT, bool kU = false>
 __device__ __forceinline__ WindowIn window_in(const Args &p, const RowPtrs<InT> &rp, int64_t T,
                                               float &carry) {
   WindowIn w{0.f, false};
   // The carry vectors hold one entry per segment (row-major over segments).
-  const int64_t row = late_v(rp.row) * late(p.seg_count) + blockIdx.y;
+  const int64_t row = late_row<kU>(rp.row) * late(p.seg_count) + blockIdx.y;
   if (p.cin != nullptr) carry = p.cin[row];
   if constexpr (A == kRetrace) w.lr0 = Ld<InT>::one(rp.lr);
   if constexpr (Uses<A>::prev_flags)
@@ -721,7 +730,7 @@ __device__ __forceinline__ WindowIn window_in(const Args &p, const RowPtrs<InT> 
 // recurrences hand on A_0 (Retrace: c_0 * A_0, the trace factor of step 0
 // applied); forward mirrors hand on A_{T-1}, or nothing when an episode ends
 // after step T-1; the generic scan hands on its last state unchanged.
-template <int A, typename InT>
+template <int A, typename InT, bool kU = false>
 __device__ __forceinline__ void window_out(const Args &p, const RowPtrs<InT> &rp,
                                            const WindowIn &w, bool write, float carry,
                                            CarryMap m) {
@@ -729,7 +738,7 @@ __device__ __forceinline__ void window_out(const Args &p, const RowPtrs<InT> &rp
   float f = 1.f;
   if constexpr (A == kRetrace) f = p.lam * fminf(p.c_bar, __expf(w.lr0));
   if constexpr (Uses<A>::prev_flags) f = w.done_last ? 0.f : 1.f;
-  const int64_t row = late_v(rp.row) * late(p.seg_count) + blockIdx.y;
+  const int64_t row = late_row<kU>(rp.row) * late(p.seg_count) + blockIdx.y;
   if (p.cout != nullptr) p.cout[row] = f * carry;
   if (p.cmap != nullptr) {
     p.cmap[2 * row] = f * m.a;
@@ -806,7 +815,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
     if constexpr (kChunk) {
       m.a = fmaf(tm.b, m.a, tm.a);
       m.b = tm.b * m.b;
-      if (!need_carry) window_out<A, InT>(p, rp, win, write_window, xc, m);
+      if (!need_carry) window_out<A, InT, (WPR > 1)>(p, rp, win, write_window, xc, m);
     }
   }
   // A at the far end of this lane's span (reverse: its earliest step;
@@ -826,7 +835,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
       // Meaningful in the group's last lane only (see above).
       m.a = fmaf(b, m.a, a);
       m.b = b * m.b;
-      if (!need_carry) window_out<A, InT>(p, rp, win, write_window, y, m);
+      if (!need_carry) window_out<A, InT, (WPR > 1)>(p, rp, win, write_window, y, m);
     }
   }
 
@@ -869,12 +878,12 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 
   // One write of the outputs.
   const bool has_o1 = U::two_outputs && late(p.o1) != nullptr;
-  const int64_t orow = late_v(rp.src);
+  const int64_t orow = late_row<(WPR > 1)>(rp.src);
   float *o0_row = p.o0 + orow * p.ld_o0 + rp.seg_off;
   float *o1_row = p.o1 + orow * p.ld_o1 + rp.seg_off;
   // Window instances with no outputs (the first pass of a split call) write
   // only the carry vectors.
-  const bool store = row_ok && (!kChunk || late(p.o0) != nullptr);
+  const bool store = row_ok && (!kChunk || p.o0 != nullptr);
   if constexpr (!kEdge) {
     // Non-temporal (streaming) dwordx4 stores: outputs are written once and
     // not re-read by this kernel.
@@ -1073,7 +1082,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     // One whole tile: straight-line code.
     Tile<K> x;
     issue_tile<A, InT, K>(p, rp, lane_off, T - lane_off, x);
-    if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
+    if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
     finish_tile<A, InT, K>(p, rp, lane_off, x);
     tile_compute<A, InT, K, LPR, WPR, false, kChunk>(p, rp, x, lane_off, T - lane_off, row_ok, 0,
                                                      false, lane, wave, carry, s_agg, m, win,
@@ -1089,7 +1098,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     int64_t c = 0;
     if (nwhole > 0) {
       issue_tile<A, InT, K>(p, rp, t0_of(0), T - t0_of(0), buf_a);
-      if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
+      if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
       for (;;) {
         {
           finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
@@ -1117,7 +1126,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
       Tile<K> x;
       load_edge<A, InT, K>(p, rp, te0, lim, T, x);
       if constexpr (kChunk) {
-        if (nwhole == 0) win = window_in<A, InT>(p, rp, T, carry);
+        if (nwhole == 0) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
       }
       tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok, ntiles - 1,
                                                       false, lane, wave, carry, s_agg, m, win,
@@ -1140,12 +1149,12 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
     Tile<K> x;
     load_edge<A, InT, K>(p, rp, te0, lim, T, x);
-    if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
+    if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
     carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok,
                                                             ntiles - 1, c >= 0, lane, wave, carry,
                                                             s_agg, m, win, write_window);
   } else {
-    if constexpr (kChunk) win = window_in<A, InT>(p, rp, T, carry);
+    if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
   }
   if (c < 0) return;
   for (;;) {
