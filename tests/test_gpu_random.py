@@ -21,9 +21,11 @@ CASE = st.fixed_dictionaries({
     "algo": st.sampled_from(ALGOS),
     "dtype": st.sampled_from(["f32", "bf16"]),
     "N": st.integers(1, 40),
-    # short rows, one tile, several tiles and ragged tails
-    "T": st.one_of(st.integers(1, 70), st.integers(100, 300), st.integers(900, 2600)),
-    "variant": st.integers(-1, 5),
+    # short rows, one tile, several tiles and ragged tails (up to two 8192-step
+    # tiles of the widest tiling)
+    "T": st.one_of(st.integers(1, 70), st.integers(100, 300), st.integers(900, 2600),
+                   st.integers(8000, 17000)),
+    "variant": st.integers(-1, 8),  # the default, or any of the 9 tilings
     "extra": st.integers(0, 5),      # row stride beyond the row length
     "off": st.integers(0, 3),        # elements before the first row
     "p_done": st.sampled_from([0.0, 0.01, 0.2]),
@@ -64,8 +66,9 @@ WINDOW_CASE = st.fixed_dictionaries({
     "algo": st.sampled_from(ALGOS),
     "dtype": st.sampled_from(["f32", "bf16"]),
     "N": st.integers(1, 30),
-    "T": st.one_of(st.integers(1, 70), st.integers(100, 300), st.integers(900, 2600)),
-    "variant": st.integers(-1, 5),
+    "T": st.one_of(st.integers(1, 70), st.integers(100, 300), st.integers(900, 2600),
+                   st.integers(8000, 17000)),
+    "variant": st.integers(-1, 8),  # the default, or any of the 9 tilings
     "sparse": st.booleans(),
 })
 
