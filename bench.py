@@ -84,6 +84,9 @@ def parse():
     ap.add_argument("--split", action="store_true",
                     help="give the library a workspace, so that calls on few long rows "
                          "split every row into segments (rlca_set_workspace)")
+    ap.add_argument("--spread-replays", type=int, default=11,
+                    help="after the timed region, replay the graph this many more times, "
+                         "each timed alone, for median / p10 / p90 launch times (0: skip)")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip timing a plain copy kernel of the same byte count")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -445,6 +448,28 @@ def main():
     elapsed_ms = start.elapsed_time(end)
     ms_per_step = elapsed_ms / K
 
+    # ---- spread: after the timed region, replay the same graph a few more
+    # times, each replay timed alone; the average step time of each replay
+    # gives median / p10 / p90 over replays.  (Per-dispatch spreads come from
+    # the kernel trace; single launches are too short to time with events.)
+    spread = None
+    if not args.no_graph and args.spread_replays > 0:
+        per = []
+        for _ in range(args.spread_replays):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            b.synchronize()
+            per.append(a.elapsed_time(b) * 1e3 / K)
+        per.sort()
+
+        def pick(f):
+            return per[min(len(per) - 1, int(f * len(per)))]
+        spread = {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9),
+                  "replays": len(per), "steps_per_replay": K}
+
     # ---- practical ceiling: a plain copy kernel (torch's) moving the same
     # number of bytes (half read, half written), timed the same way.  Under
     # --no-graph it also serves as the known-size calibration kernel of the
@@ -631,6 +656,7 @@ def main():
                      "avg_launch_us": ms_per_step * 1e3 / launches_per_step},
         "cpu_baseline": cpu,
         "copy_ceiling": copy,
+        "replay_us_per_step": spread,
         "parity_max_rel_err": parity,
     }
     print(json.dumps(out), flush=True)
