@@ -403,8 +403,9 @@ def main():
     if args.window and w.algo != "vtrace+retrace":
         # outputs, then carry_out [N] and carry map [N, 2]
         outs = outs + (sets[0]["_cout"], sets[0]["_cmap"])
-    parity = max(float(np.max(np.abs(o.double().cpu().numpy() - r)) / np.max(np.abs(r)))
-                 for o, r in zip(outs, ref))
+    per_output = [float(np.max(np.abs(o.double().cpu().numpy() - r)) / np.max(np.abs(r)))
+                  for o, r in zip(outs, ref)]
+    parity = max(per_output)
     tol = 1e-2 if w.dtype == "bf16" else 1e-4
     variant = rl.rlca_last_variant()
     print("parity max|err|/max|ref| = %.3g (tolerance %g), variant %d" % (parity, tol, variant),
@@ -658,6 +659,8 @@ def main():
         "copy_ceiling": copy,
         "replay_us_per_step": spread,
         "parity_max_rel_err": parity,
+        "parity": {"max_rel_err_per_output": per_output, "tolerance": tol,
+                   "pass": parity <= tol},
     }
     print(json.dumps(out), flush=True)
 
