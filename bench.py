@@ -566,23 +566,26 @@ def main():
                                c_bar=clips["c_bar"])
 
         def timed(step, budget):
-            """Whole batches until the time budget is spent (the first call,
-            untimed, is slower than the rest, so a repetition count taken from
-            it falls short)."""
+            """Whole batches until the time budget is spent and at least five
+            ran (the first call, untimed, is slower than the rest, so a
+            repetition count taken from it falls short).  Returns the
+            repetitions, the time spent and each batch's time."""
             step()
-            reps, t0 = 0, time.perf_counter()
+            each, t0 = [], time.perf_counter()
             while True:
+                t1 = time.perf_counter()
                 step()
-                reps += 1
+                each.append(time.perf_counter() - t1)
                 spent = time.perf_counter() - t0
-                if spent >= budget:
-                    return reps, spent
+                if spent >= budget and len(each) >= 5:
+                    return len(each), spent, sorted(each)
 
-        reps, cpu_s = timed(lambda: oracle_step(h64), args.cpu_seconds)
+        reps, cpu_s, each = timed(lambda: oracle_step(h64), args.cpu_seconds)
         cpu = {"value": env_steps * reps / cpu_s, "unit": "env-steps/s", "cores": 1,
                "kind": "oracle",
                "sample": "the whole %dx%d batch, %d repetitions (%.1f s), single-threaded "
                          "fp64 C oracle" % (N, T, reps, cpu_s),
+               "median_ms_per_batch": each[len(each) // 2] * 1e3,
                "cpu_model": cpu_model()}
         # The same oracle on every host core this process may use (at most 16,
         # the host share of one GPU): one contiguous slice of rows per thread,
