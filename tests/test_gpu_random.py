@@ -45,7 +45,7 @@ def strided(host, extra, off):
     return dev
 
 
-@settings(max_examples=80, derandomize=True, deadline=None, database=None,
+@settings(max_examples=300, derandomize=True, deadline=None, database=None,
           suppress_health_check=[HealthCheck.too_slow])
 @given(case=CASE)
 def test_random_cases_match_the_oracle(case):
@@ -73,7 +73,7 @@ WINDOW_CASE = st.fixed_dictionaries({
 })
 
 
-@settings(max_examples=40, derandomize=True, deadline=None, database=None,
+@settings(max_examples=150, derandomize=True, deadline=None, database=None,
           suppress_health_check=[HealthCheck.too_slow])
 @given(case=WINDOW_CASE)
 def test_random_window_calls_match_the_oracle(case):
@@ -104,7 +104,7 @@ TABLE_CASE = st.fixed_dictionaries({
 })
 
 
-@settings(max_examples=40, derandomize=True, deadline=None, database=None,
+@settings(max_examples=150, derandomize=True, deadline=None, database=None,
           suppress_health_check=[HealthCheck.too_slow])
 @given(case=TABLE_CASE)
 def test_random_policy_table_cases_match_the_oracle(case):
