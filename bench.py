@@ -82,8 +82,9 @@ def parse():
     ap.add_argument("--window", action="store_true",
                     help="time the window entry point (carry in; carry and carry map out)")
     ap.add_argument("--split", action="store_true",
-                    help="give the library a workspace, so that calls on few long rows "
-                         "split every row into segments (rlca_set_workspace)")
+                    help="call the window form with a workspace (and, without --window, no "
+                         "carries), so that calls on few long rows split every row into "
+                         "segments")
     ap.add_argument("--spread-replays", type=int, default=11,
                     help="after the timed region, replay the graph this many more times, "
                          "each timed alone, for median / p10 / p90 launch times (0: skip)")
@@ -266,13 +267,20 @@ def main():
     torch.cuda.synchronize()
     rl.rlca_set_variant(args.variant)
     split_segments = 1
+    workspace = None
     if args.split:
+        if w.algo in ("retrace_probs", "vtrace_probs", "vtrace+retrace"):
+            print("--split: the workload must be one call of the scan family", file=sys.stderr)
+            sys.exit(2)
         split_segments = rl.rlca_split_segments(N, T)
-        workspace = torch.empty(3 * N * split_segments, dtype=torch.float32, device=dev)
-        rl.rlca_set_workspace(workspace)
+        workspace = rl.split_workspace(N, T, dev)
 
     def window_step(d):
-        c = dict(carry_in=d["_cin"], carry_out=d["_cout"], carry_map=d["_cmap"])
+        if args.window:
+            c = dict(carry_in=d["_cin"], carry_out=d["_cout"], carry_map=d["_cmap"])
+        else:  # --split alone: the plain call's results through the window form
+            c = dict(with_carry_out=False, with_map=False)
+        c["workspace"] = workspace
         if w.algo == "gae":
             rl.rlca_gae_chunk(d["rewards"], d["values"], d["terminated"], d.get("truncated"),
                               d.get("trunc_values"), gamma=gamma, lam=lam, advantages=d["_o0"],
@@ -301,7 +309,7 @@ def main():
             raise ValueError(w.algo)
 
     def step(d):
-        if args.window:
+        if args.window or args.split:
             window_step(d)
             return
         if w.algo == "retrace_probs":
@@ -528,103 +536,56 @@ def main():
         if entry and entry.get("kernel_source_hash") == kernel_source_hash(kernel_family(traffic_key)):
             traffic = entry.get("bytes_per_launch")
 
-    # ---- CPU oracle on the host cores (bounded sample of the same workload)
+    # ---- CPU oracle on the host cores (bounded sample of the same workload):
+    # the fp64 C oracle over the whole batch, first on one thread, then on
+    # every host core this process may use (at most 16, one GPU's share), one
+    # contiguous slice of rows per OpenMP thread (oracle_rows.c).  Each leg
+    # repeats whole batches until its time budget is spent.
     cpu = None
     if args.cpu_seconds > 0:
-        h64 = {k: (v.float().numpy().astype(np.float64) if v.is_floating_point() else v.numpy())
-               for k, v in host.items()}
+        params = dict(gamma=gamma, lam=lam, **clips)
+        algos = {"vtrace+retrace": ("vtrace", "retrace"), "eligibility": ("eligibility_trace",),
+                 "cumsum": ("episodic_cumsum",)}.get(w.algo, (w.algo,))
 
-        def oracle_step(h):
-            if w.algo == "retrace_probs":
-                oracle.retrace_probs(h["rewards"], h["q_values"], h["actions"],
-                                     h["log_pi"], h["log_mu"], h["terminated"],
-                                     h.get("truncated"), h.get("trunc_eq"), gamma=gamma,
-                                     lam=lam, **clips)
-            elif w.algo == "vtrace_probs":
-                oracle.vtrace_probs(h["rewards"], h["values"], h["actions"], h["log_pi"],
-                                    h["log_mu"], h["terminated"], h.get("truncated"),
-                                    h.get("trunc_values"), gamma=gamma, lam=lam, **clips)
-            elif w.algo == "gae":
-                oracle.gae(h["rewards"], h["values"], h["terminated"],
-                           h.get("truncated"), h.get("trunc_values"), gamma=gamma, lam=lam)
-            elif w.algo == "td_lambda":
-                oracle.td_lambda(h["rewards"], h["values"], h["terminated"],
-                                 h.get("truncated"), h.get("trunc_values"), gamma=gamma,
-                                 lam=lam)
-            elif w.algo == "returns":
-                oracle.returns(h["rewards"], h["terminated"], gamma=gamma)
-            elif w.algo == "eligibility":
-                oracle.eligibility_trace(h["rewards"], h["terminated"], h.get("truncated"),
-                                         gamma=gamma, lam=lam)
-            elif w.algo == "cumsum":
-                oracle.episodic_cumsum(h["rewards"], h["terminated"], h.get("truncated"))
-            else:
-                oracle.vtrace(h["rewards"], h["values"], h["log_rhos"], h["terminated"],
-                              gamma=gamma, lam=lam, **clips)
-                oracle.retrace(h["rewards"], h["q_taken"], h["exp_q_next"],
-                               h["log_rhos"], h["terminated"], gamma=gamma, lam=lam,
-                               c_bar=clips["c_bar"])
+        def runner(threads):
+            runs = [oracle.batch_runner(a, host, params, threads) for a in algos]
 
-        def timed(step, budget):
+            def run():
+                for r in runs:
+                    r()
+            return run
+
+        def timed(run, budget):
             """Whole batches until the time budget is spent and at least five
-            ran (the first call, untimed, is slower than the rest, so a
-            repetition count taken from it falls short).  Returns the
-            repetitions, the time spent and each batch's time."""
-            step()
+            ran (the first call, untimed, touches the memory).  Returns the
+            repetitions, the time spent and each batch's time, sorted."""
+            run()
             each, t0 = [], time.perf_counter()
             while True:
                 t1 = time.perf_counter()
-                step()
+                run()
                 each.append(time.perf_counter() - t1)
                 spent = time.perf_counter() - t0
                 if spent >= budget and len(each) >= 5:
                     return len(each), spent, sorted(each)
 
-        reps, cpu_s, each = timed(lambda: oracle_step(h64), args.cpu_seconds)
+        reps, cpu_s, each = timed(runner(1), args.cpu_seconds / 2)
         cpu = {"value": env_steps * reps / cpu_s, "unit": "env-steps/s", "cores": 1,
                "kind": "oracle",
                "sample": "the whole %dx%d batch, %d repetitions (%.1f s), single-threaded "
                          "fp64 C oracle" % (N, T, reps, cpu_s),
                "median_ms_per_batch": each[len(each) // 2] * 1e3,
                "cpu_model": cpu_model()}
-        # The same oracle on every host core this process may use (at most 16,
-        # the host share of one GPU): one contiguous slice of rows per thread,
-        # each thread repeating its slice until the budget is spent.  The C
-        # oracle runs without the interpreter lock, so the threads run in
-        # parallel.
         nthreads = host_threads()
-        if nthreads > 1 and N >= nthreads:
-            import threading
-            bounds = [N * i // nthreads for i in range(nthreads + 1)]
-            slices = [{k: np.ascontiguousarray(v[a:b]) for k, v in h64.items()}
-                      for a, b in zip(bounds[:-1], bounds[1:])]
-            done = [0] * nthreads
-            go = threading.Barrier(nthreads + 1, timeout=120)
-            stop = [0.0]
-
-            def worker(i):
-                oracle_step(slices[i])  # first touch, untimed
-                go.wait()
-                while time.perf_counter() < stop[0]:
-                    oracle_step(slices[i])
-                    done[i] += 1
-
-            threads = [threading.Thread(target=worker, args=(i,)) for i in range(nthreads)]
-            for th in threads:
-                th.start()
-            stop[0] = time.perf_counter() + 1e9
-            go.wait()
-            t0 = time.perf_counter()
-            stop[0] = t0 + args.cpu_seconds / 2
-            for th in threads:
-                th.join()
-            cpu_m = time.perf_counter() - t0
-            rows_done = sum(done[i] * (bounds[i + 1] - bounds[i]) for i in range(nthreads))
+        if nthreads > 1:
+            reps_m, cpu_m, each_m = timed(runner(nthreads), args.cpu_seconds / 2)
             cpu["all_cores"] = {
-                "value": rows_done * T / cpu_m, "unit": "env-steps/s", "cores": nthreads,
-                "sample": "the %dx%d batch in %d row slices, one thread each repeating its "
-                          "slice for %.1f s (%.1f batches in all)"
-                          % (N, T, nthreads, cpu_m, rows_done / N)}
+                "value": env_steps * reps_m / cpu_m, "unit": "env-steps/s", "cores": nthreads,
+                "sample": "the whole %dx%d batch, %d repetitions (%.1f s), the same oracle on "
+                          "%d OpenMP threads, one contiguous slice of rows each"
+                          % (N, T, reps_m, cpu_m, nthreads),
+                "median_ms_per_batch": each_m[len(each_m) // 2] * 1e3,
+                "speedup_over_one_thread": (reps_m / cpu_m) / (reps / cpu_s)}
 
     meta_dir = os.environ.get("RLCA_BENCH_META_DIR")
     if meta_dir:

@@ -51,15 +51,18 @@
  *   always fp32.  Arithmetic is fp32; outputs are always fp32.  Actions are
  *   int32.
  * Ownership.  The caller owns every buffer, the split calls' workspace
- *   included.  The library allocates no memory, keeps no per-call state,
- *   never synchronizes, and returns as soon as the work is enqueued on
- *   `stream`.
+ *   included.  The library allocates no memory, keeps no state between calls
+ *   (a per-thread tiling override, rlca_set_variant, aside), never
+ *   synchronizes, and returns as soon as the work is enqueued on `stream`.
  * Nullable inputs.  terminated == NULL means no terminations; truncated ==
  *   NULL means no truncations (trunc_values is then ignored and may be NULL).
  * Errors.  Arguments are validated before anything is enqueued; on any
- *   non-OK status nothing is launched and no output is written.
- *     num_envs == 0 or T == 0        -> RLCA_OK, nothing launched.
- *     negative size, NULL required pointer, ld too small, misaligned pointer,
+ *   non-OK status nothing is launched and no output is written (the one
+ *   exception, a launch refused in the middle of a split call, is stated
+ *   with the split calls below).
+ *     T < 1                          -> RLCA_EINVAL (also when num_envs == 0).
+ *     num_envs == 0                  -> RLCA_OK, nothing launched.
+ *     negative num_envs, NULL required pointer, ld too small, misaligned pointer,
  *     gamma or lam outside [0, 1] or NaN, clip <= 0 or NaN,
  *     truncated != NULL with trunc_values == NULL  -> RLCA_EINVAL
  *     dtype other than RLCA_F32 / RLCA_BF16 -> RLCA_EDTYPE
@@ -246,7 +249,9 @@ int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype,
  * pieces evaluated apart -- is processed as consecutive windows of one
  * rollout.  Each rlca_X_chunk call takes the arguments of rlca_X (the
  * per-row bootstrap / initial value of returns and of the forward mirrors is
- * replaced by carry_in) plus three per-row fp32 vectors, whatever `dtype`:
+ * replaced by carry_in) plus three per-row fp32 vectors, whatever `dtype`,
+ * and an optional workspace (workspace, workspace_bytes; NULL, 0: none) that
+ * lets a call on few long rows run split (see "Split calls" below):
  *
  *   carry_in  [num_envs], nullable (0): the scan state A entering the window
  *             from the neighbouring window -- the later one for reverse
@@ -283,7 +288,9 @@ int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype,
  *                 A_{T-1}, or 0 if an episode ends after step T-1.
  * Splitting a rollout at any step and chaining the windows this way
  * reproduces the one-window result up to fp32 rounding.  Errors and
- * everything else as for rlca_X.
+ * everything else as for rlca_X.  A window call with carry_in, carry_out and
+ * carry_map all NULL computes what rlca_X computes (returns and the forward
+ * mirrors: with a zero bootstrap / initial value).
  */
 int rlca_returns_chunk(int64_t num_envs, int64_t T, int dtype,
                        const void *rewards, int64_t ld_rewards,
@@ -293,6 +300,7 @@ int rlca_returns_chunk(int64_t num_envs, int64_t T, int dtype,
                        const float *carry_in, float gamma,
                        float *returns, int64_t ld_returns,
                        float *carry_out, float *carry_map,
+                       void *workspace, int64_t workspace_bytes,
                        void *stream);
 int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype,
                    const void *rewards, int64_t ld_rewards,
@@ -304,6 +312,7 @@ int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype,
                    float *advantages, int64_t ld_advantages,
                    float *targets, int64_t ld_targets,
                    const float *carry_in, float *carry_out, float *carry_map,
+                   void *workspace, int64_t workspace_bytes,
                    void *stream);
 int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype,
                          const void *rewards, int64_t ld_rewards,
@@ -314,6 +323,7 @@ int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype,
                          float gamma, float lam,
                          float *lambda_returns, int64_t ld_lambda_returns,
                          const float *carry_in, float *carry_out, float *carry_map,
+                         void *workspace, int64_t workspace_bytes,
                          void *stream);
 int rlca_vtrace_chunk(int64_t num_envs, int64_t T, int dtype,
                       const void *rewards, int64_t ld_rewards,
@@ -326,6 +336,7 @@ int rlca_vtrace_chunk(int64_t num_envs, int64_t T, int dtype,
                       float *vs, int64_t ld_vs,
                       float *pg_advantages, int64_t ld_pg_advantages,
                       const float *carry_in, float *carry_out, float *carry_map,
+                      void *workspace, int64_t workspace_bytes,
                       void *stream);
 int rlca_retrace_chunk(int64_t num_envs, int64_t T, int dtype,
                        const void *rewards, int64_t ld_rewards,
@@ -337,6 +348,7 @@ int rlca_retrace_chunk(int64_t num_envs, int64_t T, int dtype,
                        float gamma, float lam, float c_bar,
                        float *q_ret, int64_t ld_q_ret,
                        const float *carry_in, float *carry_out, float *carry_map,
+                       void *workspace, int64_t workspace_bytes,
                        void *stream);
 int rlca_eligibility_trace_chunk(int64_t num_envs, int64_t T, int dtype,
                                  const void *x, int64_t ld_x,
@@ -346,6 +358,7 @@ int rlca_eligibility_trace_chunk(int64_t num_envs, int64_t T, int dtype,
                                  float gamma, float lam,
                                  float *traces, int64_t ld_traces,
                                  float *carry_out, float *carry_map,
+                                 void *workspace, int64_t workspace_bytes,
                                  void *stream);
 int rlca_episodic_cumsum_chunk(int64_t num_envs, int64_t T, int dtype,
                                const void *x, int64_t ld_x,
@@ -354,6 +367,7 @@ int rlca_episodic_cumsum_chunk(int64_t num_envs, int64_t T, int dtype,
                                const float *carry_in,
                                float *sums, int64_t ld_sums,
                                float *carry_out, float *carry_map,
+                               void *workspace, int64_t workspace_bytes,
                                void *stream);
 
 /*
@@ -366,9 +380,10 @@ int rlca_episodic_cumsum_chunk(int64_t num_envs, int64_t T, int dtype,
  * beta'_t = 0 where reset[t] != 0 (step t starts a segment: nothing flows in
  * from its neighbour), beta_t elsewhere; reset NULL: no resets.
  * In:  alpha, beta [N,T] (dtype), reset [N,T] uint8 (nullable).
- * Out: out [N,T] fp32 (= A).  carry_in, carry_out, carry_map as for the
- * window entry points: carry_out is A_0 (reverse) or A_{T-1} (forward), as
- * is; a reset at the next window's first step belongs to that window.
+ * Out: out [N,T] fp32 (= A).  carry_in, carry_out, carry_map and the
+ * workspace as for the window entry points: carry_out is A_0 (reverse) or
+ * A_{T-1} (forward), as is; a reset at the next window's first step belongs
+ * to that window.
  * reverse other than 0 or 1 -> RLCA_EINVAL.
  */
 int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype,
@@ -379,6 +394,7 @@ int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype,
                      const float *carry_in,
                      float *out, int64_t ld_out,
                      float *carry_out, float *carry_map,
+                     void *workspace, int64_t workspace_bytes,
                      void *stream);
 
 /*
@@ -522,42 +538,47 @@ typedef enum {
 } rlca_algo;
 
 /*
- * Split calls: few long rows.  With one workgroup per row, a call on at
- * most 64 rows of at least 32768 steps leaves most compute units idle.  When
- * the calling thread has set a workspace, such a call of the scan family (the
- * seven algorithms, their window forms rlca_*_chunk and rlca_affine_scan; not
- * the policy-table calls) cuts every row into S = rlca_split_segments(N, T)
- * segments of T / S steps and runs three launches on the same stream: the
- * segments from carry 0, writing only their carry maps to the workspace; a
- * small kernel composing, per row, the carry that enters each segment from
- * the row's starting carry (carry_in, or the bootstrap or initial value of a
- * plain call) and, for window calls, the row's carry_out and carry_map; and
- * the segments again from those carries, writing the outputs.  It is the
- * window calls' split along T (their carry and carry-map conventions) done
- * inside the library; it reads the inputs twice and computes the same
- * results up to rounding order.  Validation is the same as unsplit, all of it
- * before the first launch; should the runtime refuse the second or third
- * launch (RLCA_EHIP), the earlier ones stay enqueued, the workspace and (for
- * window calls) carry_out and carry_map may hold partial results, and the
- * outputs are not written.
+ * Split calls: few long rows (Method 1: the operator is associative, so a
+ * row can be cut along time, its pieces scanned apart and joined by their
+ * carry maps).  With one workgroup per row, a call on at most 64 rows of at
+ * least 32768 steps leaves most compute units idle.  A window call of the
+ * scan family (rlca_*_chunk of the seven algorithms and rlca_affine_scan; not
+ * the policy-table calls) given a workspace then cuts every row into
+ * S = rlca_split_segments(N, T) segments of T / S steps and runs three
+ * launches on `stream`: the segments from carry 0, writing only their carry
+ * maps to the workspace; a small kernel composing, per row, the carry that
+ * enters each segment from carry_in, and the row's carry_out and carry_map;
+ * and the segments again from those carries, writing the outputs.  It reads
+ * the inputs twice and computes the same results up to rounding order.  The
+ * plain entry points (rlca_gae, ...) never split: for the same result on few
+ * long rows call the window form with NULL carries and a workspace.
  *
- * rlca_set_workspace(ptr, bytes) sets the calling thread's workspace: device
- * memory owned by the caller, 4-byte aligned; NULL switches split calls off
- * (the default).  A call splits only when bytes >= 12 * N * S (3 floats per
- * segment); otherwise, or when S = 1, it runs unsplit.  The workspace must
- * not overlap the call's arrays (RLCA_EALIAS), and calls that use one
- * workspace must be ordered, for instance issued to one stream: the library
- * does not synchronize.  Returns RLCA_OK, or RLCA_EINVAL (negative size,
- * misaligned pointer).
+ * Workspace.  Device memory owned by the caller, 4-byte aligned, at least
+ * rlca_split_workspace_bytes(N, T) bytes; it must not overlap the call's
+ * arrays (RLCA_EALIAS).  It is used only when S > 1 (otherwise the call runs
+ * unsplit and never touches it); then a smaller size is RLCA_EINVAL.  Calls
+ * that share a workspace must be ordered, for instance issued to one stream:
+ * the library does not synchronize.  workspace_bytes < 0 or a misaligned
+ * workspace -> RLCA_EINVAL.
+ *
+ * Failure.  Every argument is validated before the first launch.  Kernel
+ * launches cannot be withdrawn once enqueued, so should the runtime refuse
+ * the second or third launch (RLCA_EHIP, which a launch that the runtime
+ * accepted on the same stream an instant earlier leaves only to a failing
+ * runtime or device), the earlier launches stay enqueued: the workspace and,
+ * after the second, carry_out and carry_map may then hold results, while the
+ * outputs are not written.
  *
  * rlca_split_segments(num_envs, T) returns S (1: no split): the smallest
  * power of two with num_envs * S >= 256, T divisible by S and T / S >= 4096,
  * stopping where either condition would fail; 1 for more than 64 rows and
- * for rows shorter than 32768 steps; -1 (with a message for rlca_last_error) for
- * negative sizes.
+ * for rows shorter than 32768 steps; -1 (with a message for rlca_last_error)
+ * for num_envs < 0 or T < 1.  rlca_split_workspace_bytes(num_envs, T) returns
+ * the workspace a split call needs, 12 * num_envs * S bytes (3 floats per
+ * segment), or 0 when S = 1; -1 as above.
  */
-int rlca_set_workspace(void *workspace, int64_t bytes);
 int rlca_split_segments(int64_t num_envs, int64_t T);
+int64_t rlca_split_workspace_bytes(int64_t num_envs, int64_t T);
 
 int rlca_num_variants(void);
 int rlca_set_variant(int variant);

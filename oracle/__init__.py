@@ -26,7 +26,7 @@ import os
 
 import numpy as np
 
-from .build import LIB, SRC, build_oracle
+from .build import LIB, build_oracle, stale
 
 _lib = None
 _D = ctypes.POINTER(ctypes.c_double)
@@ -36,7 +36,7 @@ _U8 = ctypes.POINTER(ctypes.c_uint8)
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB) or os.path.getmtime(LIB) < os.path.getmtime(SRC):
+        if stale():
             build_oracle()
         lib = ctypes.CDLL(LIB)
         i64, dbl = ctypes.c_int64, ctypes.c_double
@@ -335,3 +335,123 @@ def vtrace_probs(rewards, values, actions, log_pi, log_mu, terminated=None, trun
                                        pg.ctypes.data_as(_D), cip, c.out_p, c.map_p),
            "vtrace_probs")
     return (vs, pg, c.out, c.map) if chunk else (vs, pg)
+
+
+# ------------------------------------------------ the oracle on several threads
+#
+# The benchmark's CPU baseline times the oracle on every host core.  The C
+# drivers of oracle_rows.c cut the rows into one contiguous slice per thread
+# and run the unchanged serial functions above on each slice (OpenMP); one
+# ctypes call covers a whole batch, with the interpreter lock released.
+
+_ROWS_SIGS = None
+
+
+def _rows_lib():
+    global _ROWS_SIGS
+    lib = _load()
+    if _ROWS_SIGS is None:
+        i64, dbl, ci = ctypes.c_int64, ctypes.c_double, ctypes.c_int
+        _I32 = ctypes.POINTER(ctypes.c_int32)
+        sigs = {
+            "returns": [ci, i64, i64, _D, _U8, _U8, _D, _D, dbl, _D],
+            "gae": [ci, i64, i64, _D, _D, _U8, _U8, _D, dbl, dbl, _D, _D],
+            "td_lambda": [ci, i64, i64, _D, _D, _U8, _U8, _D, dbl, dbl, _D],
+            "vtrace": [ci, i64, i64, _D, _D, _D, _U8, _U8, _D, dbl, dbl, dbl, dbl, dbl, _D, _D],
+            "retrace": [ci, i64, i64, _D, _D, _D, _D, _U8, _U8, dbl, dbl, dbl, _D],
+            "eligibility_trace": [ci, i64, i64, _D, _U8, _U8, _D, dbl, dbl, _D],
+            "episodic_cumsum": [ci, i64, i64, _D, _U8, _U8, _D, _D],
+            "retrace_probs": [ci, i64, i64, i64, _D, _D, _I32, _D, _D, ci, _U8, _U8, _D, dbl,
+                              dbl, dbl, _D],
+            "vtrace_probs": [ci, i64, i64, i64, _D, _D, _I32, _D, _D, ci, _U8, _U8, _D, dbl,
+                             dbl, dbl, dbl, dbl, _D, _D],
+        }
+        for name, argtypes in sigs.items():
+            f = getattr(lib, "oracle_rows_" + name)
+            f.argtypes = argtypes
+            f.restype = ctypes.c_int
+        lib.oracle_rows_threads.argtypes = []
+        lib.oracle_rows_threads.restype = ctypes.c_int
+        _ROWS_SIGS = sigs
+    return lib
+
+
+def batch_runner(algo, inputs, params, threads):
+    """A function of no arguments that runs the oracle once over the whole
+    batch ``inputs`` (a dict of the workload's arrays: rewards, values,
+    terminated, ...) on ``threads`` host threads, one contiguous row slice
+    each, and returns the list of its output arrays (float64 [N, T]; the
+    same arrays on every call).  Arrays are widened and outputs allocated
+    here, once.  ``algo`` is
+    one of returns, gae, td_lambda, vtrace, retrace, eligibility_trace,
+    episodic_cumsum, retrace_probs, vtrace_probs; ``params`` holds gamma, lam
+    and the clips the algorithm takes."""
+    lib = _rows_lib()
+    g = inputs.get
+    r, rp = _f64(g("rewards"), np.shape(_as_numpy(g("rewards"))))
+    N, T = r.shape
+    keep = [r]
+
+    def f64(name, shape):
+        a, p = _f64(g(name), shape)
+        keep.append(a)
+        return p
+
+    def u8(name):
+        a, p = _u8(g(name), (N, T))
+        keep.append(a)
+        return p
+
+    outs = []
+
+    def out():
+        a = np.empty((N, T), np.float64)
+        outs.append(a)
+        return a.ctypes.data_as(_D)
+
+    gamma = float(params["gamma"])
+    lam = float(params.get("lam", 1.0))
+    clips = [float(params.get(k, 1.0)) for k in ("rho_bar", "c_bar", "pg_rho_bar")]
+    nt = int(threads)
+    te, tr = u8("terminated"), u8("truncated")
+    if algo == "returns":
+        args = (nt, N, T, rp, te, tr, f64("trunc_values", (N, T)), f64("bootstrap", (N,)),
+                gamma, out())
+    elif algo in ("gae", "td_lambda"):
+        args = (nt, N, T, rp, f64("values", (N, T + 1)), te, tr, f64("trunc_values", (N, T)),
+                gamma, lam, out()) + ((out(),) if algo == "gae" else ())
+    elif algo == "vtrace":
+        args = (nt, N, T, rp, f64("values", (N, T + 1)), f64("log_rhos", (N, T)), te, tr,
+                f64("trunc_values", (N, T)), gamma, lam, *clips, out(), out())
+    elif algo == "retrace":
+        args = (nt, N, T, rp, f64("q_taken", (N, T)), f64("exp_q_next", (N, T)),
+                f64("log_rhos", (N, T)), te, tr, gamma, lam, clips[1], out())
+    elif algo in ("eligibility_trace", "episodic_cumsum"):
+        x = f64("bootstrap", (N,))
+        args = (nt, N, T, rp, te, tr, x) + ((gamma, lam) if algo == "eligibility_trace"
+                                             else ()) + (out(),)
+    elif algo in ("retrace_probs", "vtrace_probs"):
+        A = np.shape(_as_numpy(g("log_pi")))[2]
+        S = T + 1 if algo == "retrace_probs" else T
+        ac, acp = _i32(g("actions"), (N, T))
+        keep.append(ac)
+        mu_taken = len(np.shape(_as_numpy(g("log_mu")))) == 2
+        lm = f64("log_mu", (N, T) if mu_taken else (N, T, A))
+        if algo == "retrace_probs":
+            args = (nt, N, T, A, rp, f64("q_values", (N, S, A)), acp, f64("log_pi", (N, S, A)),
+                    lm, int(mu_taken), te, tr, f64("trunc_eq", (N, T)), gamma, lam, clips[1],
+                    out())
+        else:
+            args = (nt, N, T, A, rp, f64("values", (N, T + 1)), acp, f64("log_pi", (N, S, A)),
+                    lm, int(mu_taken), te, tr, f64("trunc_values", (N, T)), gamma, lam, *clips,
+                    out(), out())
+    else:
+        raise ValueError("unknown algorithm %r" % (algo,))
+    fn = getattr(lib, "oracle_rows_" + algo)
+
+    def run():
+        _check(fn(*args), algo + " (rows)")
+        return outs
+
+    run.inputs = keep
+    return run

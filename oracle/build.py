@@ -8,16 +8,24 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
+# The row-parallel drivers (OpenMP) around oracle.c's serial functions, for
+# the benchmark's all-cores CPU baseline.
+SRC_ROWS = os.path.join(HERE, "oracle_rows.c")
 LIB = os.path.join(HERE, "liboracle.so")
+
+
+def stale() -> bool:
+    return not os.path.exists(LIB) or any(os.path.getmtime(LIB) < os.path.getmtime(s)
+                                          for s in (SRC, SRC_ROWS))
 
 
 def build_oracle(force: bool = True) -> str:
     """Build ``liboracle.so`` next to this file with plain gcc (no fast-math)."""
-    if not force and os.path.exists(LIB) and os.path.getmtime(LIB) >= os.path.getmtime(SRC):
+    if not force and not stale():
         return LIB
     tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC",
-           SRC, "-o", tmp, "-lm"]
+    cmd = ["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", "-fopenmp",
+           SRC, SRC_ROWS, "-o", tmp, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
     return LIB

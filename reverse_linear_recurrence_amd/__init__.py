@@ -14,7 +14,9 @@ their window forms (carry in; carry and carry map out) with the suffix
 _chunk, the generic segmented scan rlca_affine_scan, Retrace and V-trace from
 policy log-probability tables (rlca_retrace_probs, rlca_vtrace_probs), and the
 tiling controls rlca_set_variant, rlca_num_variants,
-rlca_variant_info, rlca_last_variant, plus rlca_version.
+rlca_variant_info, rlca_last_variant, the split-call sizes
+rlca_split_segments and rlca_split_workspace_bytes (split_workspace allocates
+one), plus rlca_version.
 """
 from ._binding import (  # noqa: F401
     ALGO_CODES,
@@ -44,8 +46,8 @@ from ._binding import (  # noqa: F401
     rlca_returns,
     rlca_returns_chunk,
     rlca_set_variant,
-    rlca_set_workspace,
     rlca_split_segments,
+    rlca_split_workspace_bytes,
     rlca_td_lambda,
     rlca_td_lambda_chunk,
     rlca_variant_info,
@@ -54,4 +56,5 @@ from ._binding import (  # noqa: F401
     rlca_vtrace_chunk,
     rlca_vtrace_probs,
     rlca_vtrace_probs_chunk,
+    split_workspace,
 )

@@ -9,7 +9,6 @@ of the tensors' device) and the call returns without synchronizing.
 """
 import ctypes
 import os
-import threading
 
 import torch
 
@@ -41,22 +40,22 @@ _SIGNATURES = {
     "rlca_episodic_cumsum": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _i64,
                              _vp],
     "rlca_returns_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
-                           _f32, _vp, _i64, _vp, _vp, _vp],
+                           _f32, _vp, _i64, _vp, _vp, _vp, _i64, _vp],
     "rlca_gae_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
-                       _f32, _f32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
+                       _f32, _f32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp],
     "rlca_td_lambda_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
-                             _i64, _f32, _f32, _vp, _i64, _vp, _vp, _vp, _vp],
+                             _i64, _f32, _f32, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp],
     "rlca_vtrace_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                           _i64, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _vp, _i64, _vp, _i64,
-                          _vp, _vp, _vp, _vp],
+                          _vp, _vp, _vp, _vp, _i64, _vp],
     "rlca_retrace_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
-                           _i64, _vp, _i64, _f32, _f32, _f32, _vp, _i64, _vp, _vp, _vp, _vp],
+                           _i64, _vp, _i64, _f32, _f32, _f32, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp],
     "rlca_eligibility_trace_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
-                                     _f32, _f32, _vp, _i64, _vp, _vp, _vp],
+                                     _f32, _f32, _vp, _i64, _vp, _vp, _vp, _i64, _vp],
     "rlca_episodic_cumsum_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp,
-                                   _i64, _vp, _vp, _vp],
+                                   _i64, _vp, _vp, _vp, _i64, _vp],
     "rlca_affine_scan": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _int, _vp, _vp, _i64,
-                         _vp, _vp, _vp],
+                         _vp, _vp, _vp, _i64, _vp],
     "rlca_retrace_probs": [_i64, _i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                            _vp, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f32, _f32, _f32,
                            _vp, _i64, _vp],
@@ -72,8 +71,8 @@ _SIGNATURES = {
                                 _vp],
     "rlca_last_error": [],
     "rlca_version": [],
-    "rlca_set_workspace": [_vp, _i64],
     "rlca_split_segments": [_i64, _i64],
+    "rlca_split_workspace_bytes": [_i64, _i64],
     "rlca_num_variants": [],
     "rlca_set_variant": [_int],
     "rlca_variant_info": [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
@@ -105,7 +104,8 @@ def load_library():
         for name, argtypes in _SIGNATURES.items():
             fn = getattr(lib, name)
             fn.argtypes = argtypes
-            fn.restype = ctypes.c_char_p if name == "rlca_last_error" else ctypes.c_int
+            fn.restype = {"rlca_last_error": ctypes.c_char_p,
+                          "rlca_split_workspace_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
         _lib = lib
     return _lib
 
@@ -318,7 +318,18 @@ def rlca_episodic_cumsum(x, terminated=None, truncated=None, s_init=None, *, out
 # (None: 0) is the scan state entering from the neighbouring window;
 # carry_out must not overlap carry_in (use two vectors in turn).
 # ``with_carry_out`` / ``with_map`` False pass NULL for that output (returned
-# as None).
+# as None).  ``workspace`` (a contiguous GPU tensor, e.g. from
+# split_workspace, or None) lets a call on few long rows run split.
+
+
+def _workspace(workspace, device):
+    if workspace is None:
+        return None, 0
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_contiguous()):
+        raise ValueError("workspace must be a contiguous tensor")
+    if workspace.device != device:
+        raise ValueError("workspace is on %s, expected %s" % (workspace.device, device))
+    return workspace.data_ptr(), workspace.numel() * workspace.element_size()
 
 
 def _carry_in(carry_in, N, device):
@@ -348,7 +359,7 @@ def _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, device):
 
 def rlca_returns_chunk(rewards, terminated=None, truncated=None, trunc_values=None, *, gamma,
                        carry_in=None, out=None, carry_out=None, carry_map=None,
-                       with_carry_out=True, with_map=True, stream=None):
+                       with_carry_out=True, with_map=True, workspace=None, stream=None):
     """Window of discounted returns: ``(returns, carry_out, carry_map)``;
     carry_in is G_T, carry_out is G_0."""
     N, T, code, dev = _common(rewards)
@@ -360,8 +371,9 @@ def rlca_returns_chunk(rewards, terminated=None, truncated=None, trunc_values=No
     ci = _carry_in(carry_in, N, dev)
     out, o, ld_o = _output("returns", out, (N, T), dev)
     co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    ws, ws_b = _workspace(workspace, dev)
     _check(load_library().rlca_returns_chunk(N, T, code, r, ld_r, te, ld_te, tr, ld_tr, tv, ld_tv,
-                                             ci, gamma, o, ld_o, co_p, cm_p,
+                                             ci, gamma, o, ld_o, co_p, cm_p, ws, ws_b,
                                              _stream(stream, dev)))
     return out, co, cm
 
@@ -369,7 +381,7 @@ def rlca_returns_chunk(rewards, terminated=None, truncated=None, trunc_values=No
 def rlca_gae_chunk(rewards, values, terminated=None, truncated=None, trunc_values=None, *,
                    gamma, lam, carry_in=None, advantages=None, targets=None, with_targets=True,
                    carry_out=None, carry_map=None, with_carry_out=True, with_map=True,
-                   stream=None):
+                   workspace=None, stream=None):
     """Window of GAE: ``(advantages, targets, carry_out, carry_map)``; carry_in
     is the advantage A_T of the step after the window, carry_out is A_0."""
     N, T, code, dev = _common(rewards)
@@ -385,15 +397,16 @@ def rlca_gae_chunk(rewards, values, terminated=None, truncated=None, trunc_value
     if with_targets or targets is not None:
         targets, g, ld_g = _output("targets", targets, (N, T), dev)
     co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    ws, ws_b = _workspace(workspace, dev)
     _check(load_library().rlca_gae_chunk(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr, ld_tr, tv,
-                                         ld_tv, gamma, lam, a, ld_a, g, ld_g, ci, co_p, cm_p,
-                                         _stream(stream, dev)))
+                                         ld_tv, gamma, lam, a, ld_a, g, ld_g, ci, co_p, cm_p, ws,
+                                         ws_b, _stream(stream, dev)))
     return adv, targets, co, cm
 
 
 def rlca_td_lambda_chunk(rewards, values, terminated=None, truncated=None, trunc_values=None, *,
                          gamma, lam, carry_in=None, out=None, carry_out=None, carry_map=None,
-                         with_carry_out=True, with_map=True, stream=None):
+                         with_carry_out=True, with_map=True, workspace=None, stream=None):
     """Window of TD(lambda) returns: ``(lambda_returns, carry_out, carry_map)``;
     the carry is G^lambda - V (carry_in at step T, carry_out at step 0)."""
     N, T, code, dev = _common(rewards)
@@ -406,8 +419,9 @@ def rlca_td_lambda_chunk(rewards, values, terminated=None, truncated=None, trunc
     ci = _carry_in(carry_in, N, dev)
     out, o, ld_o = _output("lambda_returns", out, (N, T), dev)
     co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    ws, ws_b = _workspace(workspace, dev)
     _check(load_library().rlca_td_lambda_chunk(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr, ld_tr,
-                                               tv, ld_tv, gamma, lam, o, ld_o, ci, co_p, cm_p,
+                                               tv, ld_tv, gamma, lam, o, ld_o, ci, co_p, cm_p, ws, ws_b,
                                                _stream(stream, dev)))
     return out, co, cm
 
@@ -416,7 +430,7 @@ def rlca_vtrace_chunk(rewards, values, log_rhos, terminated=None, truncated=None
                       trunc_values=None, *, gamma, lam=1.0, rho_bar=1.0, c_bar=1.0,
                       pg_rho_bar=1.0, carry_in=None, vs=None, pg_advantages=None, with_pg=True,
                       carry_out=None, carry_map=None, with_carry_out=True, with_map=True,
-                      stream=None):
+                      workspace=None, stream=None):
     """Window of V-trace: ``(vs, pg_advantages, carry_out, carry_map)``; the
     carry is vs - V (carry_in at step T, carry_out at step 0)."""
     N, T, code, dev = _common(rewards)
@@ -433,16 +447,18 @@ def rlca_vtrace_chunk(rewards, values, log_rhos, terminated=None, truncated=None
     if with_pg or pg_advantages is not None:
         pg_advantages, pg, ld_pg = _output("pg_advantages", pg_advantages, (N, T), dev)
     co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    ws, ws_b = _workspace(workspace, dev)
     _check(load_library().rlca_vtrace_chunk(N, T, code, r, ld_r, v, ld_v, lr, ld_lr, te, ld_te,
                                             tr, ld_tr, tv, ld_tv, gamma, lam, rho_bar, c_bar,
-                                            pg_rho_bar, o, ld_o, pg, ld_pg, ci, co_p, cm_p,
+                                            pg_rho_bar, o, ld_o, pg, ld_pg, ci, co_p, cm_p, ws, ws_b,
                                             _stream(stream, dev)))
     return vs, pg_advantages, co, cm
 
 
 def rlca_retrace_chunk(rewards, q_taken, exp_q_next, log_rhos, terminated=None, truncated=None,
                        *, gamma, lam=1.0, c_bar=1.0, carry_in=None, out=None, carry_out=None,
-                       carry_map=None, with_carry_out=True, with_map=True, stream=None):
+                       carry_map=None, with_carry_out=True, with_map=True, workspace=None,
+                       stream=None):
     """Window of Retrace(lambda): ``(q_ret, carry_out, carry_map)``; the carry
     is c_t (q_ret_t - q_taken_t) (carry_in at step T, carry_out at step 0)."""
     N, T, code, dev = _common(rewards)
@@ -456,15 +472,17 @@ def rlca_retrace_chunk(rewards, q_taken, exp_q_next, log_rhos, terminated=None, 
     ci = _carry_in(carry_in, N, dev)
     out, o, ld_o = _output("q_ret", out, (N, T), dev)
     co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    ws, ws_b = _workspace(workspace, dev)
     _check(load_library().rlca_retrace_chunk(N, T, code, r, ld_r, q, ld_q, eq, ld_eq, lr, ld_lr,
                                              te, ld_te, tr, ld_tr, gamma, lam, c_bar, o, ld_o, ci,
-                                             co_p, cm_p, _stream(stream, dev)))
+                                             co_p, cm_p, ws, ws_b, _stream(stream, dev)))
     return out, co, cm
 
 
 def rlca_eligibility_trace_chunk(x, terminated=None, truncated=None, *, gamma, lam,
                                  carry_in=None, out=None, carry_out=None, carry_map=None,
-                                 with_carry_out=True, with_map=True, stream=None):
+                                 with_carry_out=True, with_map=True, workspace=None,
+                                 stream=None):
     """Window of the eligibility trace: ``(traces, carry_out, carry_map)``;
     carry_in is z_{-1}, carry_out is z_{T-1} (0 if an episode ends there)."""
     N, T, code, dev = _common(x)
@@ -475,15 +493,16 @@ def rlca_eligibility_trace_chunk(x, terminated=None, truncated=None, *, gamma, l
     ci = _carry_in(carry_in, N, dev)
     out, o, ld_o = _output("traces", out, (N, T), dev)
     co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    ws, ws_b = _workspace(workspace, dev)
     _check(load_library().rlca_eligibility_trace_chunk(N, T, code, a, ld_a, te, ld_te, tr, ld_tr,
-                                                       ci, gamma, lam, o, ld_o, co_p, cm_p,
+                                                       ci, gamma, lam, o, ld_o, co_p, cm_p, ws, ws_b,
                                                        _stream(stream, dev)))
     return out, co, cm
 
 
 def rlca_episodic_cumsum_chunk(x, terminated=None, truncated=None, *, carry_in=None, out=None,
                                carry_out=None, carry_map=None, with_carry_out=True,
-                               with_map=True, stream=None):
+                               with_map=True, workspace=None, stream=None):
     """Window of the episodic prefix sum: ``(sums, carry_out, carry_map)``;
     carry_in is S_{-1}, carry_out is S_{T-1} (0 if an episode ends there)."""
     N, T, code, dev = _common(x)
@@ -494,15 +513,16 @@ def rlca_episodic_cumsum_chunk(x, terminated=None, truncated=None, *, carry_in=N
     ci = _carry_in(carry_in, N, dev)
     out, o, ld_o = _output("sums", out, (N, T), dev)
     co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    ws, ws_b = _workspace(workspace, dev)
     _check(load_library().rlca_episodic_cumsum_chunk(N, T, code, a, ld_a, te, ld_te, tr, ld_tr,
-                                                     ci, o, ld_o, co_p, cm_p,
+                                                     ci, o, ld_o, co_p, cm_p, ws, ws_b,
                                                      _stream(stream, dev)))
     return out, co, cm
 
 
 def rlca_affine_scan(alpha, beta, reset=None, *, reverse=True, carry_in=None, out=None,
                      carry_out=None, carry_map=None, with_carry_out=True, with_map=True,
-                     stream=None):
+                     workspace=None, stream=None):
     """Segmented affine scan: ``(A, carry_out, carry_map)`` with
     A_t = alpha_t + beta'_t A_{t+1} (reverse; A_T = carry_in) or
     A_t = alpha_t + beta'_t A_{t-1} (forward; A_{-1} = carry_in),
@@ -515,8 +535,9 @@ def rlca_affine_scan(alpha, beta, reset=None, *, reverse=True, carry_in=None, ou
     ci = _carry_in(carry_in, N, dev)
     out, o, ld_o = _output("out", out, (N, T), dev)
     co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    ws, ws_b = _workspace(workspace, dev)
     _check(load_library().rlca_affine_scan(N, T, code, a, ld_a, b, ld_b, rs, ld_rs,
-                                           1 if reverse else 0, ci, o, ld_o, co_p, cm_p,
+                                           1 if reverse else 0, ci, o, ld_o, co_p, cm_p, ws, ws_b,
                                            _stream(stream, dev)))
     return out, co, cm
 
@@ -712,32 +733,31 @@ def rlca_variant_info(variant, dtype=torch.float32, algo="gae"):
     return k.value, l.value, w.value
 
 
-_ws_local = threading.local()
-
-
-def rlca_set_workspace(workspace):
-    """Set the calling thread's workspace for split calls (few long rows):
-    a contiguous tensor on the GPU, or None to switch split calls off.  The
-    tensor is kept alive here until the next call replaces it."""
-    lib = load_library()
-    if workspace is None:
-        _check(lib.rlca_set_workspace(None, 0))
-    else:
-        if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda
-                and workspace.is_contiguous()):
-            raise ValueError("workspace must be a contiguous tensor on a GPU")
-        _check(lib.rlca_set_workspace(workspace.data_ptr(),
-                                      workspace.numel() * workspace.element_size()))
-    _ws_local.tensor = workspace
-
-
 def rlca_split_segments(num_envs, T):
-    """Segments per row a call of num_envs rows of T steps is split into
-    when a workspace is set (1: not split)."""
+    """Segments per row a window call of num_envs rows of T steps is split
+    into when given a workspace (1: not split)."""
     s = load_library().rlca_split_segments(int(num_envs), int(T))
     if s < 0:
         raise ValueError(load_library().rlca_last_error().decode())
     return s
+
+
+def rlca_split_workspace_bytes(num_envs, T):
+    """Workspace bytes a split window call of num_envs rows of T steps needs
+    (0: the call does not split)."""
+    b = load_library().rlca_split_workspace_bytes(int(num_envs), int(T))
+    if b < 0:
+        raise ValueError(load_library().rlca_last_error().decode())
+    return b
+
+
+def split_workspace(num_envs, T, device="cuda"):
+    """A workspace tensor for a window call of num_envs rows of T steps, or
+    None when the call would not split."""
+    b = rlca_split_workspace_bytes(num_envs, T)
+    if b == 0:
+        return None
+    return torch.empty(b // 4, dtype=torch.float32, device=device)
 
 
 def rlca_last_variant():

@@ -5,7 +5,8 @@
 // the kernels of scan_kernels.hpp (instantiated in kernels_plain.hip and
 // kernels_window.hip) and probs_kernels.hpp (kernels_probs.hip).  A call
 // validates its arguments, picks a tiling variant, and enqueues one kernel on
-// the caller's stream (a split call on a few long rows: three, see below).
+// the caller's stream (a window call split over a few long rows: three, see
+// below).
 
 #include <hip/hip_runtime.h>
 
@@ -60,9 +61,6 @@ int auto_variant(int64_t N, int64_t T, bool bf16, bool vtrace) {
 thread_local std::string t_last_error;
 thread_local int t_forced_variant = -1;
 thread_local int t_last_variant = -1;
-// The caller's workspace for split calls (rlca_set_workspace), in floats.
-thread_local float *t_ws = nullptr;
-thread_local int64_t t_ws_floats = 0;
 
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char *fmt, ...) {
@@ -142,9 +140,8 @@ int check_clip(const char *name, float x) {
 }
 
 int check_sizes(int64_t N, int64_t T, int dtype) {
-  if (N < 0 || T < 0)
-    return fail(RLCA_EINVAL, "num_envs = %lld and T = %lld must be >= 0",
-                static_cast<long long>(N), static_cast<long long>(T));
+  if (N < 0) return fail(RLCA_EINVAL, "num_envs = %lld must be >= 0", static_cast<long long>(N));
+  if (T < 1) return fail(RLCA_EINVAL, "T = %lld must be >= 1", static_cast<long long>(T));
   if (N > INT32_MAX) return fail(RLCA_EINVAL, "num_envs = %lld exceeds 2^31-1", static_cast<long long>(N));
   if (T > INT32_MAX - 1)
     return fail(RLCA_EINVAL, "T = %lld exceeds 2^31-2", static_cast<long long>(T));
@@ -243,12 +240,15 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
 
 int64_t esize_of(int dtype) { return dtype == RLCA_BF16 ? 2 : 4; }
 
-// The carry vectors of a window call (all NULL and off for the plain calls).
+// The carry vectors of a window call (all NULL and off for the plain calls),
+// and the caller's workspace for a split call (NULL: never split).
 struct Window {
   bool on;
   const float *cin;
   float *cout;
   float *cmap;
+  void *ws = nullptr;
+  int64_t ws_bytes = 0;
 };
 constexpr Window kNoWindow{false, nullptr, nullptr, nullptr};
 
@@ -269,17 +269,17 @@ int add_window(Arr *arrs, int n, const Window &w, int64_t N) {
 
 // ------------------------------------------------------------- split calls
 //
-// Few long rows leave most CUs idle with one workgroup per row.  A call (plain,
-// window form or generic scan) with at most kSplitMaxRows rows then cuts every
-// row into S segments of T / S steps and runs them as N * S rows of the
-// window kernels, the T-split of the window calls done inside the library:
+// Few long rows leave most CUs idle with one workgroup per row.  A window call
+// (or generic scan) given a workspace, with at most kSplitMaxRows rows, then
+// cuts every row into S segments of T / S steps and runs them as N * S rows of
+// the window kernels, the T-split of the window calls done inside the library:
 //   1. every segment from carry 0, writing only its carry map (a, b);
 //   2. per row, the maps composed from the row's end (forward mirrors: its
-//      start) into the carry entering each segment, and for window calls the
-//      row's carry out and carry map (compose_carries);
+//      start) into the carry entering each segment, and the row's carry out
+//      and carry map (compose_carries);
 //   3. every segment again from that carry, writing the outputs.
-// The inputs are read twice.  Used only while the caller has set a workspace
-// of 3 * N * S floats (rlca_set_workspace).
+// The inputs are read twice.  Used only by window calls given a workspace of
+// at least 3 * N * S floats (rlca_split_workspace_bytes).
 
 constexpr int64_t kSplitMaxRows = 64;    // split calls with at most this many rows
 constexpr int64_t kSplitMinRow = 32768;  // and rows at least this long
@@ -302,23 +302,19 @@ int64_t split_count(int64_t N, int64_t T) {
 }
 
 // The carry entering each segment, from the segments' maps: reverse
-// recurrences compose from the row's last segment (whose carry is the row's
-// bootstrap, or 0), forward ones from its first (the row's initial value).
-// The row's starting carry is the caller's carry_in (window calls, fp32) or
-// the plain call's bootstrap or initial value (input dtype), else 0.  Window
-// calls also get the row's carry_out (the last segment's outgoing carry in
-// composition order) and its carry map (the composite of every segment map).
-// One wavefront per row.  Its lanes load the maps of 64 consecutive segments
-// at once (every chunk's loads are issued before the first is used), and a
-// shuffle scan composes them: lane j ends with the composite of the chunk's
-// maps from its own to the chunk's end in composition order.  Chunks are
-// taken in that order, each starting from the carry the previous one hands
-// on.
-template <typename InT>
+// recurrences compose from the row's last segment, forward ones from its
+// first, starting from the caller's carry_in (NULL: 0).  Also the row's
+// carry_out (the last segment's outgoing carry in composition order) and its
+// carry map (the composite of every segment map).  One wavefront per row.
+// Its lanes load the maps of 64 consecutive segments at once (every chunk's
+// loads are issued before the first is used), and a shuffle scan composes
+// them: lane j ends with the composite of the chunk's maps from its own to
+// the chunk's end in composition order.  Chunks are taken in that order, each
+// starting from the carry the previous one hands on.
 __global__ void __launch_bounds__(64)
-compose_carries(const float *__restrict__ map, const InT *__restrict__ init,
-                const float *__restrict__ init_f32, float *__restrict__ cin, int S,
-                bool forward, float *__restrict__ cout, float *__restrict__ cmap) {
+compose_carries(const float *__restrict__ map, const float *__restrict__ init,
+                float *__restrict__ cin, int S, bool forward, float *__restrict__ cout,
+                float *__restrict__ cmap) {
   constexpr int kMaxChunks = 4;
   static_assert(kSplitTarget <= 64 * kMaxChunks, "S <= kSplitTarget segments per row");
   const int64_t n = blockIdx.x;
@@ -340,9 +336,7 @@ compose_carries(const float *__restrict__ map, const InT *__restrict__ init,
       mb[k] = map[2 * e + 1];
     }
   }
-  float c = init_f32 != nullptr ? init_f32[n]
-             : init != nullptr  ? Bits<InT>::to_float(Bits<InT>::load(init + n))
-                                : 0.f;
+  float c = init != nullptr ? init[n] : 0.f;
   float ta = 0.f, tb = 1.f;  // the composite of the chunks so far
   for (int k = 0; k < nchunks; ++k) {
     // Inclusive scan in composition order: after it, lane j holds
@@ -385,10 +379,24 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
                         const Window &w, Args &a, void *stream) {
   if (n + kExtraArrs > kCap) return fail(RLCA_EINVAL, "internal: argument table too small");
   n = add_window(arrs, n, w, N);
-  if (N == 0 || a.T == 0) return RLCA_OK;
+  if (w.ws != nullptr) {
+    if (w.ws_bytes < 0)
+      return fail(RLCA_EINVAL, "workspace_bytes = %lld is negative",
+                  static_cast<long long>(w.ws_bytes));
+    if (reinterpret_cast<uintptr_t>(w.ws) % 4 != 0)
+      return fail(RLCA_EINVAL, "workspace is not 4-byte aligned");
+  }
+  if (N == 0) return RLCA_OK;
   const int64_t S = split_count(N, a.T);
-  const bool split = S > 1 && t_ws != nullptr && t_ws_floats >= 3 * N * S;
-  if (split) arrs[n++] = Arr{"workspace", t_ws, 3 * N * S, 3 * N * S, 4, false, true, true};
+  const bool split = S > 1 && w.ws != nullptr;
+  if (split) {
+    if (w.ws_bytes < 12 * N * S)
+      return fail(RLCA_EINVAL,
+                  "workspace_bytes = %lld is less than the %lld this call's split needs "
+                  "(rlca_split_workspace_bytes)",
+                  static_cast<long long>(w.ws_bytes), static_cast<long long>(12 * N * S));
+    arrs[n++] = Arr{"workspace", w.ws, 3 * N * S, 3 * N * S, 4, false, true, true};
+  }
   for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], N));
   RLCA_TRY(check_aliasing(arrs, n));
   a.cin = w.cin;
@@ -396,7 +404,8 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   a.cmap = w.cmap;
   if (!split) return launch(algo, dtype, a, stream, w.on);
 
-  float *maps = t_ws, *cins = t_ws + 2 * N * S;
+  float *const ws = static_cast<float *>(w.ws);
+  float *maps = ws, *cins = ws + 2 * N * S;
   Args a1 = a;  // 1. maps only
   a1.T = a.T / S;
   a1.o0 = nullptr;
@@ -405,17 +414,14 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   a1.cout = nullptr;
   a1.cmap = maps;
   RLCA_TRY(launch(algo, dtype, a1, stream, true, static_cast<int>(S)));
-  // 2. compose: from the caller's carry_in (window calls), or the bootstrap of
-  // returns or initial value of the forward mirrors (plain calls)
+  // 2. compose, from the caller's carry_in
   bool forward = algo == kEligibility || algo == kCumsum || algo == kAffineFwd;
-  const void *init = !w.on && (algo == kReturns || forward) ? a.boot : nullptr;
-  const float *cmaps = maps, *init_f32 = w.cin;
+  const float *cmaps = maps, *init = w.cin;
   float *cout = w.cout, *cmap = w.cmap;
   int S32 = static_cast<int>(S);
-  void *kargs[] = {&cmaps, &init, &init_f32, &cins, &S32, &forward, &cout, &cmap};
-  const void *kernel = dtype == RLCA_BF16 ? reinterpret_cast<const void *>(&compose_carries<bf16_t>)
-                                          : reinterpret_cast<const void *>(&compose_carries<float>);
-  const hipError_t e = hipLaunchKernel(kernel, dim3(static_cast<unsigned>(N)), dim3(64), kargs, 0,
+  void *kargs[] = {&cmaps, &init, &cins, &S32, &forward, &cout, &cmap};
+  const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&compose_carries),
+                                       dim3(static_cast<unsigned>(N)), dim3(64), kargs, 0,
                                        static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   Args a2 = a;  // 3. outputs
@@ -656,7 +662,7 @@ int retrace_probs_impl(int64_t num_envs, int64_t T, int64_t num_actions, int dty
       {"q_ret", q_ret, ld_q_ret, T, 4, true, true},
   };
   const int n = add_window(arrs, 9, w, num_envs);
-  if (num_envs == 0 || T == 0) return RLCA_OK;
+  if (num_envs == 0) return RLCA_OK;
   for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], num_envs));
   RLCA_TRY(check_aliasing(arrs, n));
   Args a{};
@@ -716,7 +722,7 @@ int vtrace_probs_impl(int64_t num_envs, int64_t T, int64_t num_actions, int dtyp
       {"pg_advantages", pg_advantages, ld_pg_advantages, T, 4, false, true},
   };
   const int n = add_window(arrs, 10, w, num_envs);
-  if (num_envs == 0 || T == 0) return RLCA_OK;
+  if (num_envs == 0) return RLCA_OK;
   for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], num_envs));
   RLCA_TRY(check_aliasing(arrs, n));
   Args a{};
@@ -737,6 +743,10 @@ int vtrace_probs_impl(int64_t num_envs, int64_t T, int64_t num_actions, int dtyp
   ta.mu_taken = log_mu_taken;
   a.cin = w.cin; a.cout = w.cout; a.cmap = w.cmap;
   return launch_probs(kVtrace, dtype, a, ta, stream, w.on);
+}
+
+Window window_of(const float *cin, float *cout, float *cmap, void *ws, int64_t ws_bytes) {
+  return Window{true, cin, cout, cmap, ws, ws_bytes};
 }
 
 }  // namespace
@@ -825,16 +835,21 @@ int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype, const void *x, 
 }
 
 // ------------------------------------------------------ window entry points
+//
+// `workspace` (nullable) enables the split of few long rows (see
+// validate_and_launch); the plain entry points above never split.
 
 int rlca_returns_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
                        int64_t ld_rewards, const uint8_t *terminated, int64_t ld_terminated,
                        const uint8_t *truncated, int64_t ld_truncated, const void *trunc_values,
                        int64_t ld_trunc_values, const float *carry_in, float gamma,
                        float *returns, int64_t ld_returns, float *carry_out, float *carry_map,
-                       void *stream) {
+                       void *workspace, int64_t workspace_bytes, void *stream) {
   return returns_impl(num_envs, T, dtype, rewards, ld_rewards, terminated, ld_terminated,
                       truncated, ld_truncated, trunc_values, ld_trunc_values, nullptr, gamma,
-                      returns, ld_returns, Window{true, carry_in, carry_out, carry_map}, stream);
+                      returns, ld_returns,
+                      window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes),
+                      stream);
 }
 
 int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
@@ -843,11 +858,11 @@ int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
                    int64_t ld_truncated, const void *trunc_values, int64_t ld_trunc_values,
                    float gamma, float lam, float *advantages, int64_t ld_advantages,
                    float *targets, int64_t ld_targets, const float *carry_in, float *carry_out,
-                   float *carry_map, void *stream) {
+                   float *carry_map, void *workspace, int64_t workspace_bytes, void *stream) {
   return gae_like(kGae, num_envs, T, dtype, rewards, ld_rewards, values, ld_values, terminated,
                   ld_terminated, truncated, ld_truncated, trunc_values, ld_trunc_values, gamma,
                   lam, advantages, ld_advantages, targets, ld_targets, "advantages", "targets",
-                  Window{true, carry_in, carry_out, carry_map}, stream);
+                  window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes), stream);
 }
 
 int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
@@ -857,12 +872,12 @@ int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype, const void *rew
                          const void *trunc_values, int64_t ld_trunc_values, float gamma,
                          float lam, float *lambda_returns, int64_t ld_lambda_returns,
                          const float *carry_in, float *carry_out, float *carry_map,
-                         void *stream) {
+                         void *workspace, int64_t workspace_bytes, void *stream) {
   return gae_like(kTdLambda, num_envs, T, dtype, rewards, ld_rewards, values, ld_values,
                   terminated, ld_terminated, truncated, ld_truncated, trunc_values,
                   ld_trunc_values, gamma, lam, lambda_returns, ld_lambda_returns, nullptr, 0,
-                  "lambda_returns", "unused", Window{true, carry_in, carry_out, carry_map},
-                  stream);
+                  "lambda_returns", "unused",
+                  window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes), stream);
 }
 
 int rlca_vtrace_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
@@ -872,12 +887,14 @@ int rlca_vtrace_chunk(int64_t num_envs, int64_t T, int dtype, const void *reward
                       const void *trunc_values, int64_t ld_trunc_values, float gamma, float lam,
                       float rho_bar, float c_bar, float pg_rho_bar, float *vs, int64_t ld_vs,
                       float *pg_advantages, int64_t ld_pg_advantages, const float *carry_in,
-                      float *carry_out, float *carry_map, void *stream) {
+                      float *carry_out, float *carry_map, void *workspace,
+                      int64_t workspace_bytes, void *stream) {
   return vtrace_impl(num_envs, T, dtype, rewards, ld_rewards, values, ld_values, log_rhos,
                      ld_log_rhos, terminated, ld_terminated, truncated, ld_truncated,
                      trunc_values, ld_trunc_values, gamma, lam, rho_bar, c_bar, pg_rho_bar, vs,
                      ld_vs, pg_advantages, ld_pg_advantages,
-                     Window{true, carry_in, carry_out, carry_map}, stream);
+                     window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes),
+                     stream);
 }
 
 int rlca_retrace_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
@@ -886,11 +903,13 @@ int rlca_retrace_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewar
                        int64_t ld_log_rhos, const uint8_t *terminated, int64_t ld_terminated,
                        const uint8_t *truncated, int64_t ld_truncated, float gamma, float lam,
                        float c_bar, float *q_ret, int64_t ld_q_ret, const float *carry_in,
-                       float *carry_out, float *carry_map, void *stream) {
+                       float *carry_out, float *carry_map, void *workspace,
+                       int64_t workspace_bytes, void *stream) {
   return retrace_impl(num_envs, T, dtype, rewards, ld_rewards, q_taken, ld_q_taken, exp_q_next,
                       ld_exp_q_next, log_rhos, ld_log_rhos, terminated, ld_terminated,
                       truncated, ld_truncated, gamma, lam, c_bar, q_ret, ld_q_ret,
-                      Window{true, carry_in, carry_out, carry_map}, stream);
+                      window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes),
+                      stream);
 }
 
 int rlca_eligibility_trace_chunk(int64_t num_envs, int64_t T, int dtype, const void *x,
@@ -898,26 +917,31 @@ int rlca_eligibility_trace_chunk(int64_t num_envs, int64_t T, int dtype, const v
                                  const uint8_t *truncated, int64_t ld_truncated,
                                  const float *carry_in, float gamma, float lam, float *traces,
                                  int64_t ld_traces, float *carry_out, float *carry_map,
-                                 void *stream) {
+                                 void *workspace, int64_t workspace_bytes, void *stream) {
   return forward_like(kEligibility, num_envs, T, dtype, x, ld_x, terminated, ld_terminated,
                       truncated, ld_truncated, nullptr, gamma, lam, traces, ld_traces, "z_init",
-                      "traces", Window{true, carry_in, carry_out, carry_map}, stream);
+                      "traces",
+                      window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes),
+                      stream);
 }
 
 int rlca_episodic_cumsum_chunk(int64_t num_envs, int64_t T, int dtype, const void *x,
                                int64_t ld_x, const uint8_t *terminated, int64_t ld_terminated,
                                const uint8_t *truncated, int64_t ld_truncated,
                                const float *carry_in, float *sums, int64_t ld_sums,
-                               float *carry_out, float *carry_map, void *stream) {
+                               float *carry_out, float *carry_map, void *workspace,
+                               int64_t workspace_bytes, void *stream) {
   return forward_like(kCumsum, num_envs, T, dtype, x, ld_x, terminated, ld_terminated, truncated,
                       ld_truncated, nullptr, 1.f, 1.f, sums, ld_sums, "s_init", "sums",
-                      Window{true, carry_in, carry_out, carry_map}, stream);
+                      window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes),
+                      stream);
 }
 
 int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype, const void *alpha,
                      int64_t ld_alpha, const void *beta, int64_t ld_beta, const uint8_t *reset,
                      int64_t ld_reset, int reverse, const float *carry_in, float *out,
-                     int64_t ld_out, float *carry_out, float *carry_map, void *stream) {
+                     int64_t ld_out, float *carry_out, float *carry_map, void *workspace,
+                     int64_t workspace_bytes, void *stream) {
   RLCA_TRY(check_sizes(num_envs, T, dtype));
   if (reverse != 0 && reverse != 1)
     return fail(RLCA_EINVAL, "reverse = %d must be 0 or 1", reverse);
@@ -936,7 +960,8 @@ int rlca_affine_scan(int64_t num_envs, int64_t T, int dtype, const void *alpha,
   a.o0 = out; a.ld_o0 = ld_out;
   a.gamma = a.lam = a.rho_bar = a.c_bar = a.pg_rho_bar = 1.f;
   return validate_and_launch(reverse ? kAffine : kAffineFwd, dtype, num_envs, arrs, 4,
-                            Window{true, carry_in, carry_out, carry_map}, a, stream);
+                             window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes),
+                             a, stream);
 }
 
 // ------------------------------------------------ policy-table entry points
@@ -1011,28 +1036,25 @@ int rlca_vtrace_probs_chunk(int64_t num_envs, int64_t T, int64_t num_actions, in
 
 const char *rlca_last_error(void) { return t_last_error.c_str(); }
 
-int rlca_version(void) { return 400; }  // 0.4.0: bf16 long rows at 8 steps per lane; rlca_variant_info takes the algorithm
-
-int rlca_set_workspace(void *workspace, int64_t bytes) {
-  if (workspace == nullptr) {
-    t_ws = nullptr;
-    t_ws_floats = 0;
-    return RLCA_OK;
-  }
-  if (bytes < 0) return fail(RLCA_EINVAL, "workspace size %lld is negative", static_cast<long long>(bytes));
-  if (reinterpret_cast<uintptr_t>(workspace) % 4 != 0)
-    return fail(RLCA_EINVAL, "workspace is not 4-byte aligned");
-  t_ws = static_cast<float *>(workspace);
-  t_ws_floats = bytes / 4;
-  return RLCA_OK;
-}
+// 0.5.0: T < 1 is an error; the split calls' workspace is an argument of the
+// window calls (no per-thread workspace).
+int rlca_version(void) { return 500; }
 
 int rlca_split_segments(int64_t num_envs, int64_t T) {
-  if (num_envs < 0 || T < 0) {
-    fail(RLCA_EINVAL, "num_envs and T must be >= 0");
+  if (num_envs < 0 || T < 1) {
+    fail(RLCA_EINVAL, "num_envs must be >= 0 and T >= 1");
     return -1;
   }
   return static_cast<int>(split_count(num_envs, T));
+}
+
+int64_t rlca_split_workspace_bytes(int64_t num_envs, int64_t T) {
+  if (num_envs < 0 || T < 1) {
+    fail(RLCA_EINVAL, "num_envs must be >= 0 and T >= 1");
+    return -1;
+  }
+  const int64_t S = split_count(num_envs, T);
+  return S > 1 ? 12 * num_envs * S : 0;
 }
 
 int rlca_num_variants(void) { return kNumVariants; }

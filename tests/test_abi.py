@@ -1,6 +1,12 @@
 """C-ABI checks that need no GPU: the library loads, exports every entry point
 that include/rlca.h declares, and rejects bad arguments with the documented
-status before anything is enqueued (validation makes no HIP call)."""
+status before anything is enqueued (validation makes no HIP call).
+
+The arrays here are fake device addresses that nothing may dereference, so
+every call in this file must fail validation: a call that passed it would
+enqueue a kernel on those addresses.  The one check that needs a call to pass
+validation (adjacent arrays do not alias) runs only where no GPU is present,
+where the launch itself fails (RLCA_EHIP)."""
 import ctypes
 import math
 import os
@@ -90,11 +96,24 @@ def err(lib):
 
 def test_empty_inputs_are_ok_without_launch(lib):
     assert gae(lib, N=0) == rl.RLCA_OK
-    assert gae(lib, T=0) == rl.RLCA_OK
     # Nothing is read or written for an empty batch, so no pointer is needed.
     assert gae(lib, N=0, r=None, v=None, adv=None) == rl.RLCA_OK
     # Parameters are still validated.
     assert gae(lib, N=0, gamma=3.0) == rl.RLCA_EINVAL
+
+
+def test_rows_without_steps_are_rejected(lib):
+    # T < 1 is an error, with or without rows.
+    for N in (0, 4):
+        assert gae(lib, N=N, T=0) == rl.RLCA_EINVAL
+        assert "T = 0 must be >= 1" in err(lib)
+    assert lib.rlca_returns(4, 0, 0, R, 8, None, 8, None, 8, None, 8, None, 0.9,
+                            ADV, 8, None) == rl.RLCA_EINVAL
+    assert lib.rlca_affine_scan(0, 0, F32, R, 8, V, 8, None, 8, 1, None, ADV, 8, None, None,
+                                None, 0, None) == rl.RLCA_EINVAL
+    assert lib.rlca_retrace_probs(4, 0, 5, F32, R, 8, V, 45, TE, 8, TR, 45, TV, 40, 0, None, 8,
+                                  None, 8, None, 8, 0.9, 0.9, 1.0, ADV, 8, None) == rl.RLCA_EINVAL
+    assert "T = 0" in err(lib)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
@@ -136,7 +155,16 @@ def test_aliasing_is_rejected(lib):
     assert "targets" in err(lib)
     span = (4 - 1) * 8 + 8  # elements of a [4, 8] array
     assert gae(lib, adv=R - span * 4 + 4) == rl.RLCA_EALIAS
-    assert gae(lib, adv=R - span * 4) != rl.RLCA_EALIAS  # adjacent, not overlapping
+
+
+def test_adjacent_arrays_do_not_alias(lib):
+    # Passing validation enqueues a kernel on the fake addresses: only where
+    # no GPU is present, so that the launch itself fails.
+    if torch.cuda.is_available():
+        pytest.skip("a call that passes validation would launch on fake addresses")
+    span = (4 - 1) * 8 + 8
+    assert gae(lib, adv=R - span * 4) == rl.RLCA_EHIP  # adjacent, not overlapping
+    assert "launch" in err(lib)
 
 
 def test_truncation_without_flags_needs_no_trunc_values(lib):
@@ -202,9 +230,10 @@ def test_binding_refuses_cpu_tensors():
 C_IN, C_OUT, C_MAP = (BASE + (8 + i) * 0x1000000 for i in range(3))
 
 
-def gae_chunk(lib, N=4, T=8, cin=C_IN, cout=C_OUT, cmap=C_MAP, adv=ADV, r=R):
+def gae_chunk(lib, N=4, T=8, cin=C_IN, cout=C_OUT, cmap=C_MAP, adv=ADV, r=R, ws=None,
+              ws_bytes=0):
     return lib.rlca_gae_chunk(N, T, F32, r, T, V, T + 1, TE, T, TR, T, TV, T, 0.9, 0.9,
-                              adv, T, TGT, T, cin, cout, cmap, None)
+                              adv, T, TGT, T, cin, cout, cmap, ws, ws_bytes, None)
 
 
 def test_window_entry_points_validate_carry_vectors(lib):
@@ -222,12 +251,12 @@ def test_window_entry_points_validate_carry_vectors(lib):
     assert gae_chunk(lib, cmap=C_OUT - 2 * 4 * 4 + 4) == rl.RLCA_EALIAS
     ret = lambda **k: lib.rlca_returns_chunk(4, 8, F32, R, 8, None, 8, None, 8, None, 8,
                                               k.get("cin", C_IN), k.get("gamma", 0.9), ADV, 8,
-                                              k.get("cout", C_OUT), None, None)
+                                              k.get("cout", C_OUT), None, None, 0, None)
     assert ret(gamma=1.5) == rl.RLCA_EINVAL
     assert ret(cout=ADV + 4) == rl.RLCA_EALIAS
     el = lambda **k: lib.rlca_eligibility_trace_chunk(4, 8, F32, R, 8, None, 8, None, 8,
                                                        k.get("cin", C_IN), 0.9, k.get("lam", 0.9),
-                                                       ADV, 8, C_OUT, C_MAP, None)
+                                                       ADV, 8, C_OUT, C_MAP, None, 0, None)
     assert el(lam=2.0) == rl.RLCA_EINVAL and "lam" in err(lib)
     assert el(cin=ADV) == rl.RLCA_EALIAS
 
@@ -236,7 +265,7 @@ def test_affine_scan_validates(lib):
     aff = lambda **k: lib.rlca_affine_scan(k.get("N", 4), 8, k.get("dtype", F32), k.get("a", R),
                                            8, k.get("b", V), 8, k.get("rs", None), 8,
                                            k.get("rev", 1), None, k.get("out", ADV), 8, None,
-                                           None, None)
+                                           None, None, 0, None)
     assert aff(N=0) == rl.RLCA_OK
     assert aff(rev=2) == rl.RLCA_EINVAL and "reverse" in err(lib)
     assert aff(b=None) == rl.RLCA_EINVAL and "beta" in err(lib)
@@ -306,32 +335,46 @@ def test_split_segments_rule(lib):
     # T / S >= 4096, stopping where either would fail; no split above 64 rows
     # or below 32768 steps per row
     cases = {(64, 65536): 4, (16, 262144): 16, (1, 32768): 8, (1, 1 << 20): 256,
-             (3, 32768): 8, (65, 65536): 1, (127, 65536): 1, (128, 32768): 1,
-             (3, 16384): 1, (100, 16384): 1, (8, 4096): 1, (2, 3 * 16384): 8,
-             (2, 32769): 1, (2, 2 * 32769): 2, (0, 0): 1}
+             (2, 1 << 19): 128, (3, 32768): 8, (65, 65536): 1, (127, 65536): 1,
+             (128, 32768): 1, (3, 16384): 1, (100, 16384): 1, (8, 4096): 1, (2, 3 * 16384): 8,
+             (2, 32769): 1, (2, 2 * 32769): 2, (0, 1): 1}
     for (N, T), S in cases.items():
         assert rl.rlca_split_segments(N, T) == S, (N, T)
-    with pytest.raises(ValueError):
-        rl.rlca_split_segments(-1, 8)
+        assert rl.rlca_split_workspace_bytes(N, T) == (12 * N * S if S > 1 else 0), (N, T)
+    # at most 64 rows split, into fewer than 512 segments in all
+    assert max(N * rl.rlca_split_segments(N, 1 << 24) for N in range(1, 65)) < 512
+    for bad in ((-1, 8), (4, 0)):
+        with pytest.raises(ValueError):
+            rl.rlca_split_segments(*bad)
+        with pytest.raises(ValueError):
+            rl.rlca_split_workspace_bytes(*bad)
     assert lib.rlca_split_segments(4, -8) == -1 and "T" in err(lib)
+    assert lib.rlca_split_workspace_bytes(4, 0) == -1 and "T >= 1" in err(lib)
+
+
+WS = BASE + 0x40000000  # a fake workspace clear of every array above
 
 
 def test_workspace_is_validated(lib):
-    try:
-        assert lib.rlca_set_workspace(BASE + 0x8000002, 64) == rl.RLCA_EINVAL
-        assert "aligned" in err(lib)
-        assert lib.rlca_set_workspace(BASE + 0x8000000, -4) == rl.RLCA_EINVAL
-        # A call that splits (16 rows of 65536 steps: 16 segments each) checks
-        # its 3 * 16 * 16 floats of workspace against its arrays before any
-        # launch.
-        assert lib.rlca_set_workspace(ADV + 64, 1 << 20) == rl.RLCA_OK
-        assert gae(lib, N=16, T=65536) == rl.RLCA_EALIAS and "workspace" in err(lib)
-        assert lib.rlca_set_workspace(R + 4 * 65536 * 16 - 8, 1 << 20) == rl.RLCA_OK
-        assert gae(lib, N=16, T=65536) == rl.RLCA_EALIAS and "rewards" in err(lib)
-        with pytest.raises(ValueError):
-            rl.rlca_set_workspace(torch.empty(16))  # not on a GPU
-    finally:
-        assert lib.rlca_set_workspace(None, 0) == rl.RLCA_OK
+    # A window call that splits (16 rows of 65536 steps: 16 segments each)
+    # checks its 3 * 16 * 16 floats of workspace before any launch.
+    N, T = 16, 65536
+    need = rl.rlca_split_workspace_bytes(N, T)
+    assert need == 12 * N * 16
+    assert gae_chunk(lib, N=N, T=T, ws=WS + 2, ws_bytes=need) == rl.RLCA_EINVAL
+    assert "aligned" in err(lib)
+    assert gae_chunk(lib, N=N, T=T, ws=WS, ws_bytes=-4) == rl.RLCA_EINVAL
+    assert "negative" in err(lib)
+    assert gae_chunk(lib, N=N, T=T, ws=WS, ws_bytes=need - 4) == rl.RLCA_EINVAL
+    assert "rlca_split_workspace_bytes" in err(lib)
+    # overlapping an output, an input
+    assert gae_chunk(lib, N=N, T=T, ws=ADV + 64, ws_bytes=need) == rl.RLCA_EALIAS
+    assert "workspace" in err(lib)
+    assert gae_chunk(lib, N=N, T=T, ws=R + 4 * 65536 * 16 - 8, ws_bytes=need) == rl.RLCA_EALIAS
+    assert "rewards" in err(lib)
+    with pytest.raises(ValueError):
+        rl.rlca_affine_scan(torch.zeros(2, 4), torch.zeros(2, 4),
+                            workspace=torch.empty(16))  # not on a GPU
 
 
 def test_split_window_call_validates_its_workspace(lib):
@@ -339,14 +382,18 @@ def test_split_window_call_validates_its_workspace(lib):
     # the workspace, all beside its own arrays (the argument table has room
     # for four more entries), before any launch.
     N, T = 16, 65536
-    try:
-        assert lib.rlca_set_workspace(R + 64, 1 << 20) == rl.RLCA_OK
-        for _ in range(3):
-            assert gae_chunk(lib, N=N, T=T, r=R) == rl.RLCA_EALIAS
-            assert "workspace" in err(lib)
-            assert lib.rlca_returns_chunk(N, T, F32, R, T, None, T, None, T, None, T, C_IN, 0.9,
-                                          ADV, T, C_OUT, C_MAP, None) == rl.RLCA_EALIAS
-        assert lib.rlca_set_workspace(C_MAP + 8, 1 << 20) == rl.RLCA_OK
-        assert gae_chunk(lib, N=N, T=T) == rl.RLCA_EALIAS and "carry_map" in err(lib)
-    finally:
-        assert lib.rlca_set_workspace(None, 0) == rl.RLCA_OK
+    need = rl.rlca_split_workspace_bytes(N, T)
+    for _ in range(3):
+        assert gae_chunk(lib, N=N, T=T, r=R, ws=R + 64, ws_bytes=need) == rl.RLCA_EALIAS
+        assert "workspace" in err(lib)
+        assert lib.rlca_returns_chunk(N, T, F32, R, T, None, T, None, T, None, T, C_IN, 0.9,
+                                      ADV, T, C_OUT, C_MAP, R + 64, need,
+                                      None) == rl.RLCA_EALIAS
+        assert lib.rlca_affine_scan(N, T, F32, R, T, V, T, None, T, 0, C_IN, ADV, T, C_OUT,
+                                    C_MAP, V + 8, need, None) == rl.RLCA_EALIAS
+        assert "workspace" in err(lib)
+    assert gae_chunk(lib, N=N, T=T, ws=C_MAP + 8, ws_bytes=need) == rl.RLCA_EALIAS
+    assert "carry_map" in err(lib)
+    # the carry vectors are validated when a workspace is given too
+    assert gae_chunk(lib, N=N, T=T, cin=C_IN + 2, ws=WS, ws_bytes=need) == rl.RLCA_EINVAL
+    assert "carry_in" in err(lib)

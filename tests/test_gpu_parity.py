@@ -179,11 +179,16 @@ def test_rows_past_element_2_to_the_31(algo, dtype):
 
 
 def test_empty_and_nullable():
-    for N, T in ((0, 16), (5, 0), (0, 0)):
+    r = torch.zeros(0, 16, device="cuda")
+    v = torch.zeros(0, 17, device="cuda")
+    adv, tgt = rl.rlca_gae(r, v, gamma=0.9, lam=0.9)
+    assert adv.shape == (0, 16) and tgt.shape == (0, 16)
+    for N, T in ((5, 0), (0, 0)):  # rows without steps: refused, nothing launched
         r = torch.zeros(N, T, device="cuda")
         v = torch.zeros(N, T + 1, device="cuda")
-        adv, tgt = rl.rlca_gae(r, v, gamma=0.9, lam=0.9)
-        assert adv.shape == (N, T) and tgt.shape == (N, T)
+        with pytest.raises(rl.RlcaError, match="T = 0 must be >= 1") as e:
+            rl.rlca_gae(r, v, gamma=0.9, lam=0.9)
+        assert e.value.status == rl.RLCA_EINVAL
     host = random_inputs("gae", 9, 40, 3)
     dev = to_device(host)
     p = params32(DEFAULT_PARAMS)

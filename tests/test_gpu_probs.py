@@ -2,8 +2,11 @@
 (rlca_retrace_probs, rlca_vtrace_probs) against the oracle.
 
 The tables are [N, T(+1), A] (rl-triton, Results: the heavier Retrace workload
-loads the action probabilities at every step).  Cases cover one to 257
-actions, row lengths around the 256-step tile, workgroups with rows past N,
+loads the action probabilities at every step).  Cases cover one to 65536
+actions (the largest table the entry points accept, where a tile's element
+index passes 2^24 and float rounding of it starts: the slice index is then
+a corrected estimate), row lengths around the 256-step tile, workgroups with
+rows past N,
 row strides larger than a row, table rows past element 2^31 of their buffer,
 both input dtypes, the full-size workload, and out-of-range actions (NaN at
 that step and every earlier step of the row).
@@ -82,6 +85,36 @@ def test_vtrace_probs_parity(N, T, A, dtype, mu_taken):
         for a, b in zip(got, ref):
             assert np.all(np.isfinite(a))
             assert rel_err(a, b) <= TOL[dtype], (N, T, A, p_trunc, rel_err(a, b))
+
+
+# Large action sets: slices x A of one tile above 2^24 with A = 65536 (both
+# tilings: 256 steps, one wavefront per row, and 1024-step tiles), and A =
+# 4096 over a ragged second tile.
+LARGE = [(2, 300, 65536), (2, 256, 65536), (3, 1030, 4096), (4, 200, 4096)]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N,T,A", LARGE)
+@pytest.mark.parametrize("algo", ["retrace_probs", "vtrace_probs"])
+def test_large_action_sets(algo, N, T, A, dtype):
+    # Slices one tile streams: its steps (Retrace: and the slice after them).
+    tile = 1024 if T > 256 else 256
+    slices = min(T, tile) + (1 if algo == "retrace_probs" else 0)
+    if A == 65536:
+        assert slices * A >= 1 << 24
+    for mu_taken in ((False, True) if A == 65536 and dtype == "f32" else (False,)):
+        d = make_tables(algo, N, T, A, seed=7000 + T + A + mu_taken, dtype=dtype, p_term=0.01,
+                        p_trunc=0.01, mu_taken=mu_taken)
+        print(algo, dtype, "N", N, "T", T, "A", A, "mu_taken", mu_taken, flush=True)
+        if algo == "retrace_probs":
+            got, ref = (gpu_retrace(d),), (ref_retrace(d),)
+        else:
+            got, ref = gpu_vtrace(d), ref_vtrace(d)
+        for a, b in zip(got, ref):
+            assert np.all(np.isfinite(a))
+            assert rel_err(a, b) <= TOL[dtype], (algo, N, T, A, dtype, rel_err(a, b))
+        del d
+        torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("name", ["retrace_probs_2048x1024x18", "vtrace_probs_2048x1024x18"])

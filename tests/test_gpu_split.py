@@ -1,13 +1,15 @@
 """Split calls (few long rows) on the GPU against the oracle.
 
-With a workspace set, a call (plain, window form or generic scan) on at most
-64 rows of at least 32768 steps cuts each row into S segments and runs them as
-N * S rows of the window kernels (maps only, compose, outputs): the window
-calls' split along T inside one library call.  Window calls also get the
-row's carry_out and carry map from the composition.
+A window call (rlca_X_chunk or the generic scan) given a workspace, on at most
+64 rows of at least 32768 steps, cuts each row into S segments and runs them
+as N * S rows of the window kernels (maps only, compose, outputs): the window
+calls' split along T inside one library call (the operator of the rl-triton
+pages' Method 1 is associative, so the pieces join through their carry maps).
 The results must match the oracle to the same tolerance as an unsplit call,
-for every algorithm, with episode boundaries that fall inside and across
-segment borders and with carries that cross every border (no boundaries).
+for every algorithm, with episode boundaries that fall inside and exactly at
+segment borders and with carries that cross every border (no boundaries),
+from 8 segments per row up to the 256 that rlca_split_segments allows, where
+the composition walks its 64-segment chunks one after another.
 """
 import numpy as np
 import pytest
@@ -16,19 +18,24 @@ import torch
 import oracle
 import reverse_linear_recurrence_amd as rl
 from gpu_common import (ALGOS, DEFAULT_PARAMS, TOL, assert_close, params32, random_inputs,
-                        run_gpu, run_oracle, to_device)
+                        run_oracle, to_device)
 from test_gpu_window import (affine_inputs, check_window, run_gpu_chunk, run_oracle_chunk,
                              window_inputs)
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture
-def workspace():
-    ws = torch.empty(1 << 16, device="cuda")
-    rl.rlca_set_workspace(ws)
-    yield ws
-    rl.rlca_set_workspace(None)
+def workspace_for(N, T):
+    ws = rl.split_workspace(N, T)
+    assert ws is not None, "a call of %d x %d does not split" % (N, T)
+    ws.fill_(float("nan"))
+    return ws
+
+
+def assert_split(ws, N, T):
+    S = rl.rlca_split_segments(N, T)
+    maps = ws[:2 * N * S].cpu().numpy()
+    assert np.all(np.isfinite(maps)), "the call did not split"
 
 
 def padded(d, pad):
@@ -44,105 +51,111 @@ def padded(d, pad):
     return out
 
 
+def plain_by_window(algo, d, p, ws):
+    """The window form with no carries: the plain call's results (returns and
+    the forward mirrors with a zero bootstrap / initial value)."""
+    out, _, _ = run_gpu_chunk(algo, d, p, None, with_carry_out=False, with_map=False,
+                              workspace=ws)
+    return out
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("algo", ALGOS)
-def test_split_call_matches_oracle(algo, dtype, workspace):
+def test_split_call_matches_oracle(algo, dtype):
     p = params32(dict(DEFAULT_PARAMS, gamma=0.999, lam=0.99))
     N, T = 3, 32768
-    S = rl.rlca_split_segments(N, T)
-    assert S == 8
+    assert rl.rlca_split_segments(N, T) == 8
     for seed, p_b in ((71, 0.0), (72, 0.0005), (73, 0.01)):
-        host = random_inputs(algo, N, T, seed, dtype, p_term=p_b, p_trunc=p_b)
+        host = random_inputs(algo, N, T, seed, dtype, p_term=p_b, p_trunc=p_b, bootstrap=False)
         ref = run_oracle(algo, host, p)
-        workspace.fill_(float("nan"))
-        print(algo, dtype, "N", N, "T", T, "S", S, "boundary rate", p_b, flush=True)
-        got = run_gpu(algo, to_device(host), p)
-        # the first pass wrote every segment's carry map
-        maps = workspace[:2 * N * S].cpu().numpy()
-        assert np.all(np.isfinite(maps)), "the call did not split"
+        ws = workspace_for(N, T)
+        print(algo, dtype, "N", N, "T", T, "boundary rate", p_b, flush=True)
+        got = plain_by_window(algo, to_device(host), p, ws)
+        assert_split(ws, N, T)
         assert_close(got, ref, TOL[dtype], "%s/%s/split p=%g" % (algo, dtype, p_b))
 
 
 @pytest.mark.parametrize("algo", ["gae", "retrace", "eligibility"])
-def test_split_call_with_padded_rows(algo, workspace):
+def test_split_call_with_padded_rows(algo):
     p = params32(DEFAULT_PARAMS)
     N, T = 5, 32768
-    S = rl.rlca_split_segments(N, T)
-    assert S == 8
-    host = random_inputs(algo, N, T, 81, "f32", p_term=0.002, p_trunc=0.002)
+    assert rl.rlca_split_segments(N, T) == 8
+    host = random_inputs(algo, N, T, 81, "f32", p_term=0.002, p_trunc=0.002, bootstrap=False)
     ref = run_oracle(algo, host, p)
-    workspace.fill_(float("nan"))
-    got = run_gpu(algo, padded(to_device(host), 37), p)
-    assert np.all(np.isfinite(workspace[:2 * N * S].cpu().numpy()))
+    ws = workspace_for(N, T)
+    got = plain_by_window(algo, padded(to_device(host), 37), p, ws)
+    assert_split(ws, N, T)
     assert_close(got, ref, TOL["f32"], "%s/split/padded" % algo)
 
 
-def test_no_split_without_room_or_divisible_length():
+def test_no_split_for_indivisible_rows_and_small_workspaces():
     p = params32(DEFAULT_PARAMS)
-    ws = torch.full((3 * 3 * 8 - 1,), float("nan"), device="cuda")  # one float short
-    rl.rlca_set_workspace(ws)
-    try:
-        assert rl.rlca_split_segments(3, 32768) == 8
-        host = random_inputs("gae", 3, 32768, 91, "f32", p_term=0.001, p_trunc=0.001)
-        got = run_gpu("gae", to_device(host), p)
-        assert torch.isnan(ws).all(), "a workspace too small for the split was used"
-        assert_close(got, run_oracle("gae", host, p), TOL["f32"], "gae/no room")
-        ws2 = torch.full((1 << 12,), float("nan"), device="cuda")
-        rl.rlca_set_workspace(ws2)
-        assert rl.rlca_split_segments(3, 32767) == 1
-        host = random_inputs("gae", 3, 32767, 92, "f32", p_term=0.001, p_trunc=0.001)
-        got = run_gpu("gae", to_device(host), p)
-        assert torch.isnan(ws2).all()
-        assert_close(got, run_oracle("gae", host, p), TOL["f32"], "gae/odd T")
-    finally:
-        rl.rlca_set_workspace(None)
+    # S = 1: the workspace is not touched, the call runs unsplit.
+    assert rl.rlca_split_segments(3, 32767) == 1
+    assert rl.rlca_split_workspace_bytes(3, 32767) == 0
+    ws = torch.full((1 << 12,), float("nan"), device="cuda")
+    host = random_inputs("gae", 3, 32767, 92, "f32", p_term=0.001, p_trunc=0.001)
+    got = plain_by_window("gae", to_device(host), p, ws)
+    assert torch.isnan(ws).all()
+    assert_close(got, run_oracle("gae", host, p), TOL["f32"], "gae/odd T")
+    # A call that splits, given a workspace one float short: refused before
+    # any launch, nothing written.
+    need = rl.rlca_split_workspace_bytes(3, 32768)
+    assert need == 12 * 3 * 8
+    short = torch.full((need // 4 - 1,), float("nan"), device="cuda")
+    dev = to_device(random_inputs("gae", 3, 32768, 91, "f32"))
+    adv = torch.full((3, 32768), float("nan"), device="cuda")
+    with pytest.raises(rl.RlcaError, match="rlca_split_workspace_bytes"):
+        rl.rlca_gae_chunk(dev["rewards"], dev["values"], dev["terminated"], dev["truncated"],
+                          dev["trunc_values"], gamma=p["gamma"], lam=p["lam"], advantages=adv,
+                          workspace=short)
+    torch.cuda.synchronize()
+    assert torch.isnan(short).all() and torch.isnan(adv).all()
 
 
 def test_split_and_unsplit_calls_agree():
-    # The same call with and without a workspace: equal up to rounding order.
+    # The same window call with and without a workspace: equal up to rounding
+    # order.
     p = params32(DEFAULT_PARAMS)
-    host = random_inputs("td_lambda", 2, 1 << 16, 93, "bf16", p_term=0.0005, p_trunc=0.0002)
+    N, T = 2, 1 << 16
+    host = random_inputs("td_lambda", N, T, 93, "bf16", p_term=0.0005, p_trunc=0.0002)
     dev = to_device(host)
-    plain = run_gpu("td_lambda", dev, p)
-    ws = torch.empty(1 << 12, device="cuda")
-    rl.rlca_set_workspace(ws)
-    try:
-        assert rl.rlca_split_segments(2, 1 << 16) == 16
-        split = run_gpu("td_lambda", dev, p)
-    finally:
-        rl.rlca_set_workspace(None)
-    assert_close(split, plain, TOL["f32"], "td_lambda/split vs unsplit")
+    c = torch.randn(N, generator=torch.Generator().manual_seed(5)).cuda()
+    plain = run_gpu_chunk("td_lambda", dev, p, c)
+    assert rl.rlca_split_segments(N, T) == 16
+    ws = workspace_for(N, T)
+    split = run_gpu_chunk("td_lambda", dev, p, c, workspace=ws)
+    assert_split(ws, N, T)
+    check_window(split, plain, "f32", "td_lambda/split vs unsplit")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("algo", ALGOS)
-def test_split_window_call_matches_oracle(algo, dtype, workspace):
+def test_split_window_call_matches_oracle(algo, dtype):
     # carry in from the caller; carry out and carry map of the whole row
     p = params32(dict(DEFAULT_PARAMS, c_bar=0.95, rho_bar=1.05))
     N, T = 3, 32768
-    S = rl.rlca_split_segments(N, T)
     for sparse in (False, True):
         d, c = window_inputs(algo, N, T, 501 + sparse, dtype, sparse)
-        workspace.fill_(float("nan"))
-        print(algo, dtype, "window N", N, "T", T, "S", S, "sparse", sparse, flush=True)
-        got = run_gpu_chunk(algo, to_device(d), p, c.cuda())
-        assert np.all(np.isfinite(workspace[:2 * N * S].cpu().numpy())), "did not split"
+        ws = workspace_for(N, T)
+        print(algo, dtype, "window N", N, "T", T, "sparse", sparse, flush=True)
+        got = run_gpu_chunk(algo, to_device(d), p, c.cuda(), workspace=ws)
+        assert_split(ws, N, T)
         check_window(got, run_oracle_chunk(algo, d, p, c), dtype,
                      "%s/%s split window sparse=%s" % (algo, dtype, sparse))
 
 
 @pytest.mark.parametrize("reverse", [True, False])
-def test_split_affine_scan_matches_oracle(reverse, workspace):
+def test_split_affine_scan_matches_oracle(reverse):
     N, T = 2, 65536
-    S = rl.rlca_split_segments(N, T)
-    assert S == 16
+    assert rl.rlca_split_segments(N, T) == 16
     for p_reset, with_reset in ((0.0, False), (0.001, True)):
         al, be, rs, c = affine_inputs(N, T, 601, "f32", p_reset)
-        workspace.fill_(float("nan"))
+        ws = workspace_for(N, T)
         A, co, cm = rl.rlca_affine_scan(al.cuda(), be.cuda(), rs.cuda() if with_reset else None,
-                                        reverse=reverse, carry_in=c.cuda())
+                                        reverse=reverse, carry_in=c.cuda(), workspace=ws)
         torch.cuda.synchronize()
-        assert np.all(np.isfinite(workspace[:2 * N * S].cpu().numpy())), "did not split"
+        assert_split(ws, N, T)
         rA, rco, rcm = oracle.affine_scan(al, be, rs if with_reset else None, c,
                                           reverse=reverse)
         got = ({"A": A.double().cpu().numpy()}, co.double().cpu().numpy(),
@@ -151,7 +164,84 @@ def test_split_affine_scan_matches_oracle(reverse, workspace):
                      "affine split rev=%s p_reset=%g" % (reverse, p_reset))
 
 
-def test_split_call_in_a_hip_graph_replays_like_eager_calls(workspace):
+# ------------------------------------------- 128 and 256 segments per row
+
+def border_boundaries(d, algo, T, S, seed):
+    """Sparse random boundaries plus boundaries at and just before several
+    segment borders (the first step of a segment and the last of the one
+    before), of both kinds where the algorithm takes truncations."""
+    L = T // S
+    g = np.random.Generator(np.random.PCG64(seed))
+    term = d["terminated"].numpy().copy()
+    trunc = d["truncated"].numpy().copy() if d.get("truncated") is not None else None
+    for row in range(term.shape[0]):
+        for k in g.choice(np.arange(1, S), size=min(12, S - 1), replace=False):
+            t = int(k) * L - int(g.integers(0, 2))  # a segment's first step or the one before
+            if trunc is not None and g.random() < 0.5:
+                trunc[row, t] = 1
+            else:
+                term[row, t] = 1
+    d["terminated"] = torch.from_numpy(term)
+    if trunc is not None:
+        d["truncated"] = torch.from_numpy(trunc)
+    return d
+
+
+MANY = [(2, 1 << 19, 128), (1, 1 << 20, 256)]
+
+
+@pytest.mark.parametrize("N,T,S", MANY)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ["gae", "retrace", "eligibility"])
+def test_many_segments_match_oracle(algo, dtype, N, T, S):
+    assert rl.rlca_split_segments(N, T) == S
+    p = params32(dict(DEFAULT_PARAMS, gamma=0.999, lam=0.99))
+    for form in ("plain", "window"):
+        d, c = window_inputs(algo, N, T, 801 + S, dtype, sparse=True)
+        d = border_boundaries(d, algo, T, S, 901 + S)
+        ws = workspace_for(N, T)
+        print(algo, dtype, "N", N, "T", T, "S", S, form, flush=True)
+        if form == "plain":
+            got = plain_by_window(algo, to_device(d), p, ws)
+            assert_split(ws, N, T)
+            assert_close(got, run_oracle(algo, d, p), TOL[dtype],
+                         "%s/%s S=%d plain" % (algo, dtype, S))
+        else:
+            got = run_gpu_chunk(algo, to_device(d), p, c.cuda(), workspace=ws)
+            assert_split(ws, N, T)
+            check_window(got, run_oracle_chunk(algo, d, p, c), dtype,
+                         "%s/%s S=%d window" % (algo, dtype, S))
+
+
+@pytest.mark.parametrize("N,T,S", MANY)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reverse", [True, False])
+def test_many_segments_affine_scan(reverse, dtype, N, T, S):
+    assert rl.rlca_split_segments(N, T) == S
+    for p_reset, form in ((0.0, "window"), (0.0005, "plain"), (0.0005, "window")):
+        al, be, rs, c = affine_inputs(N, T, 611 + S, dtype, p_reset)
+        L = T // S
+        if p_reset:  # resets at segment borders too
+            rs = rs.clone()
+            rs[:, torch.as_tensor(L * np.arange(3, S, 7))] = 1
+            rs[:, torch.as_tensor(L * np.arange(5, S, 11) - 1)] = 1
+        cin = c if form == "window" else None
+        ws = workspace_for(N, T)
+        print("affine", dtype, "reverse", reverse, "S", S, form, "p_reset", p_reset, flush=True)
+        A, co, cm = rl.rlca_affine_scan(al.cuda(), be.cuda(), rs.cuda() if p_reset else None,
+                                        reverse=reverse,
+                                        carry_in=None if cin is None else cin.cuda(),
+                                        workspace=ws)
+        torch.cuda.synchronize()
+        assert_split(ws, N, T)
+        rA, rco, rcm = oracle.affine_scan(al, be, rs if p_reset else None, cin, reverse=reverse)
+        got = ({"A": A.double().cpu().numpy()}, co.double().cpu().numpy(),
+               cm.double().cpu().numpy())
+        check_window(got, ({"A": rA}, rco, rcm), dtype,
+                     "affine S=%d rev=%s %s p_reset=%g" % (S, reverse, form, p_reset))
+
+
+def test_split_call_in_a_hip_graph_replays_like_eager_calls():
     # The three launches of a split call (both passes and the compose kernel)
     # captured once; every replay, with eager split calls and in-place input
     # updates in between, equals the eager call bitwise.
@@ -161,19 +251,22 @@ def test_split_call_in_a_hip_graph_replays_like_eager_calls(workspace):
     dev = to_device(random_inputs("gae", N, T, 701, "f32", p_term=0.0005, p_trunc=0.0005))
     args = (dev["rewards"], dev["values"], dev["terminated"], dev["truncated"],
             dev["trunc_values"])
+    ws = workspace_for(N, T)
+    ws_eager = workspace_for(N, T)
     adv = torch.empty(N, T, device="cuda")
     tgt = torch.empty_like(adv)
+    kw = dict(gamma=p["gamma"], lam=p["lam"], with_carry_out=False, with_map=False)
     g = torch.cuda.CUDAGraph()
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         with torch.cuda.graph(g, stream=s):
-            rl.rlca_gae(*args, gamma=p["gamma"], lam=p["lam"], advantages=adv, targets=tgt)
+            rl.rlca_gae_chunk(*args, advantages=adv, targets=tgt, workspace=ws, **kw)
     torch.cuda.synchronize()
     for i in range(4):
         if i == 2:
             dev["rewards"].mul_(-0.5)
-        e_adv, e_tgt = rl.rlca_gae(*args, gamma=p["gamma"], lam=p["lam"])
+        e_adv, e_tgt, _, _ = rl.rlca_gae_chunk(*args, workspace=ws_eager, **kw)
         adv.fill_(float("nan"))
         tgt.fill_(float("nan"))
         torch.cuda.synchronize()
