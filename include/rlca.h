@@ -314,6 +314,32 @@ int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype,
                    const float *carry_in, float *carry_out, float *carry_map,
                    void *workspace, int64_t workspace_bytes,
                    void *stream);
+/*
+ * rlca_gae_chunk_noalloc: rlca_gae_chunk for callers that cannot allocate
+ * device memory or pass a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments without
+ * (workspace, workspace_bytes), same results: a call that would split (see
+ * "Split calls" below) takes its workspace from a 6 KB array that the
+ * library holds on each device until the process ends, room for every split
+ * the library makes (3 floats per segment, at most 512 segments; a larger
+ * need is RLCA_EINVAL).  The array's address on a device is looked up on the
+ * first call there (with that device made current for the lookup); no call
+ * allocates or frees memory.  Every call on one device shares that device's
+ * array, and each split call overwrites it before reading it: calls that
+ * overlap in time on one device (different streams) race and must not be
+ * made; calls on one stream are ordered.  An unsplit call does not touch it.
+ */
+int rlca_gae_chunk_noalloc(int64_t num_envs, int64_t T, int dtype,
+                           const void *rewards, int64_t ld_rewards,
+                           const void *values, int64_t ld_values,
+                           const uint8_t *terminated, int64_t ld_terminated,
+                           const uint8_t *truncated, int64_t ld_truncated,
+                           const void *trunc_values, int64_t ld_trunc_values,
+                           float gamma, float lam,
+                           float *advantages, int64_t ld_advantages,
+                           float *targets, int64_t ld_targets,
+                           const float *carry_in, float *carry_out, float *carry_map,
+                           void *stream);
 int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype,
                          const void *rewards, int64_t ld_rewards,
                          const void *values, int64_t ld_values,

@@ -11,7 +11,8 @@ Functions (same names as the C ABI):
     rlca_returns, rlca_gae, rlca_td_lambda, rlca_vtrace, rlca_retrace,
     rlca_eligibility_trace, rlca_episodic_cumsum,
 their window forms (carry in; carry and carry map out) with the suffix
-_chunk, the generic segmented scan rlca_affine_scan, Retrace and V-trace from
+_chunk (and rlca_gae_chunk_noalloc, which needs no workspace), the generic
+segmented scan rlca_affine_scan, Retrace and V-trace from
 policy log-probability tables (rlca_retrace_probs, rlca_vtrace_probs), and the
 tiling controls rlca_set_variant, rlca_num_variants,
 rlca_variant_info, rlca_last_variant, the split-call sizes
@@ -37,6 +38,7 @@ from ._binding import (  # noqa: F401
     rlca_episodic_cumsum_chunk,
     rlca_gae,
     rlca_gae_chunk,
+    rlca_gae_chunk_noalloc,
     rlca_last_variant,
     rlca_num_variants,
     rlca_retrace,

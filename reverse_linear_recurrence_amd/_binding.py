@@ -43,6 +43,8 @@ _SIGNATURES = {
                            _f32, _vp, _i64, _vp, _vp, _vp, _i64, _vp],
     "rlca_gae_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
                        _f32, _f32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp],
+    "rlca_gae_chunk_noalloc": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                               _vp, _i64, _f32, _f32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
     "rlca_td_lambda_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
                              _i64, _f32, _f32, _vp, _i64, _vp, _vp, _vp, _vp, _i64, _vp],
     "rlca_vtrace_chunk": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
@@ -401,6 +403,34 @@ def rlca_gae_chunk(rewards, values, terminated=None, truncated=None, trunc_value
     _check(load_library().rlca_gae_chunk(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr, ld_tr, tv,
                                          ld_tv, gamma, lam, a, ld_a, g, ld_g, ci, co_p, cm_p, ws,
                                          ws_b, _stream(stream, dev)))
+    return adv, targets, co, cm
+
+
+def rlca_gae_chunk_noalloc(rewards, values, terminated=None, truncated=None, trunc_values=None,
+                           *, gamma, lam, carry_in=None, advantages=None, targets=None,
+                           with_targets=True, carry_out=None, carry_map=None,
+                           with_carry_out=True, with_map=True, stream=None):
+    """rlca_gae_chunk for callers that cannot allocate: a call on few long
+    rows splits with the library's own device scratch array instead of a
+    workspace.  Pass every output (advantages, targets, carry_out, carry_map)
+    to keep this wrapper from allocating them.  Calls that overlap in time on
+    one device race on that array."""
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    ci = _carry_in(carry_in, N, dev)
+    adv, a, ld_a = _output("advantages", advantages, (N, T), dev)
+    g, ld_g = None, 0
+    if with_targets or targets is not None:
+        targets, g, ld_g = _output("targets", targets, (N, T), dev)
+    co, cm, co_p, cm_p = _carry_outputs(carry_out, carry_map, with_carry_out, with_map, N, dev)
+    _check(load_library().rlca_gae_chunk_noalloc(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr,
+                                                 ld_tr, tv, ld_tv, gamma, lam, a, ld_a, g, ld_g,
+                                                 ci, co_p, cm_p, _stream(stream, dev)))
     return adv, targets, co, cm
 
 

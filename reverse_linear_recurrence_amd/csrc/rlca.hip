@@ -15,6 +15,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "probs_kernels.hpp"
@@ -745,6 +746,67 @@ int vtrace_probs_impl(int64_t num_envs, int64_t T, int64_t num_actions, int dtyp
   return launch_probs(kVtrace, dtype, a, ta, stream, w.on);
 }
 
+// ------------------------------------------- the no-allocation entry point
+//
+// Callers that cannot allocate device memory (code under HIP graph capture,
+// tight serving loops, harnesses that forbid allocation) take a split call's
+// workspace from this file-scope array instead of passing one: 3 floats per
+// segment, room for every split the library makes (at most kSplitMaxRows
+// rows, fewer than 2 * kSplitTarget segments in all), 6 KB per device,
+// held until the process ends.  In host code `scratch` only names the
+// symbol; its address on a device comes from hipGetSymbolAddress, made once
+// per device (scratch_on) and used for every kernel argument.
+constexpr int64_t kScratchSegments = 2 * kSplitTarget;
+constexpr int64_t kScratchFloats = 3 * kScratchSegments;
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+float *g_scratch[kMaxDevices];  // the array's address on each device, once known
+
+// The device a stream belongs to (the current device for the NULL stream).
+int device_of(void *stream, int *dev) {
+  hipError_t e;
+  if (stream == nullptr) {
+    e = hipGetDevice(dev);
+  } else {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &d);
+    *dev = static_cast<int>(d);
+  }
+  if (e != hipSuccess) return fail(RLCA_EHIP, "device of the stream: %s", hipGetErrorString(e));
+  return RLCA_OK;
+}
+
+// The scratch array's address on the device of `stream`: looked up on the
+// first call on that device, with that device current, then kept.
+int scratch_on(void *stream, float **out) {
+  int dev = 0;
+  RLCA_TRY(device_of(stream, &dev));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(RLCA_EINVAL, "device %d is beyond the %d devices the scratch table holds", dev,
+                kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch[dev] == nullptr) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+    if (e != hipSuccess) return fail(RLCA_EHIP, "selecting device %d: %s", dev, hipGetErrorString(e));
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (cur != dev) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess || p == nullptr)
+      return fail(RLCA_EHIP, "address of the scratch array on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch[dev] = static_cast<float *>(p);
+  }
+  *out = g_scratch[dev];
+  return RLCA_OK;
+}
+
 Window window_of(const float *cin, float *cout, float *cmap, void *ws, int64_t ws_bytes) {
   return Window{true, cin, cout, cmap, ws, ws_bytes};
 }
@@ -863,6 +925,34 @@ int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
                   ld_terminated, truncated, ld_truncated, trunc_values, ld_trunc_values, gamma,
                   lam, advantages, ld_advantages, targets, ld_targets, "advantages", "targets",
                   window_of(carry_in, carry_out, carry_map, workspace, workspace_bytes), stream);
+}
+
+int rlca_gae_chunk_noalloc(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                           int64_t ld_rewards, const void *values, int64_t ld_values,
+                           const uint8_t *terminated, int64_t ld_terminated,
+                           const uint8_t *truncated, int64_t ld_truncated,
+                           const void *trunc_values, int64_t ld_trunc_values, float gamma,
+                           float lam, float *advantages, int64_t ld_advantages, float *targets,
+                           int64_t ld_targets, const float *carry_in, float *carry_out,
+                           float *carry_map, void *stream) {
+  RLCA_TRY(check_sizes(num_envs, T, dtype));
+  // The library's scratch array replaces the caller's workspace, only for a
+  // call that splits.
+  float *ws = nullptr;
+  const int64_t S = split_count(num_envs, T);
+  if (num_envs > 0 && S > 1) {
+    if (3 * num_envs * S > kScratchFloats)
+      return fail(RLCA_EINVAL, "the split of %lld rows into %lld segments needs %lld bytes, more "
+                  "than the %lld of the library's scratch array",
+                  static_cast<long long>(num_envs), static_cast<long long>(S),
+                  static_cast<long long>(12 * num_envs * S),
+                  static_cast<long long>(4 * kScratchFloats));
+    RLCA_TRY(scratch_on(stream, &ws));
+  }
+  return gae_like(kGae, num_envs, T, dtype, rewards, ld_rewards, values, ld_values, terminated,
+                  ld_terminated, truncated, ld_truncated, trunc_values, ld_trunc_values, gamma,
+                  lam, advantages, ld_advantages, targets, ld_targets, "advantages", "targets",
+                  window_of(carry_in, carry_out, carry_map, ws, 4 * kScratchFloats), stream);
 }
 
 int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
