@@ -77,7 +77,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="approximate CPU time for the oracle baseline (0: skip)")
     ap.add_argument("--no-graph", action="store_true",
-                    help="launch each step from Python instead of replaying a HIP graph")
+                    help="plain eager launches from Python (same as --timing eager)")
+    ap.add_argument("--timing", choices=["auto", "queued", "graph", "eager"], default="auto",
+                    help="how the K steps are timed (auto: queued for K <= %d, else graph)"
+                    % 1000)
     ap.add_argument("--variant", type=int, default=-1, help="force a tiling variant")
     ap.add_argument("--window", action="store_true",
                     help="time the window entry point (carry in; carry and carry map out)")
@@ -86,8 +89,11 @@ def parse():
                          "carries), so that calls on few long rows split every row into "
                          "segments")
     ap.add_argument("--spread-replays", type=int, default=11,
-                    help="after the timed region, replay the graph this many more times, "
-                         "each timed alone, for median / p10 / p90 launch times (0: skip)")
+                    help="after the timed region, time the same K steps this many more "
+                         "times, each block alone, for median / p10 / p90 (0: skip)")
+    ap.add_argument("--body-blocks", type=int, default=30,
+                    help="blocks of steps timed through the instrumented library for the "
+                         "kernel body (0: skip)")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip timing a plain copy kernel of the same byte count")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -212,6 +218,91 @@ def cpu_model():
     except OSError:
         pass
     return None
+
+
+# Timed regions of at most this many steps are timed as eager launches
+# queued behind a spin kernel; longer ones as one HIP graph replay.  A graph
+# replay carries a fixed cost of about 8 us on this runtime, which 20 steps
+# do not amortize; the queue of a stream holds a few thousand launches.
+QUEUED_MAX_STEPS = 1000
+TIMING_DESC = {
+    "queued": "K eager launches queued behind a spin kernel (the GPU runs them back to back; "
+              "events bracket exactly the K launches)",
+    "graph": "HIP graph replay of K launches",
+    "eager": "eager launches from Python",
+}
+
+
+def spin_rate(stream):
+    """Cycles of torch.cuda._sleep per microsecond on this GPU."""
+    import torch
+    torch.cuda._sleep(1000)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    torch.cuda._sleep(2_000_000)
+    b.record(stream)
+    b.synchronize()
+    return 2e6 / (a.elapsed_time(b) * 1e3)
+
+
+def make_timed(fn, K, mode, stream, rate):
+    """A function that runs fn(0) .. fn(K-1) (one launch each) between two
+    events on `stream`, with the device synchronized before and after, and
+    returns the average microseconds per step.
+
+    queued: the launches are enqueued while a spin kernel (torch.cuda._sleep,
+    bounded) keeps the GPU busy, long enough to cover the host's enqueue
+    time, so the GPU runs the K launches back to back and the start event is
+    taken when the spin ends; graph: one replay of a HIP graph of the K
+    launches (captured and replayed once untimed here); eager: plain
+    launches."""
+    import torch
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    if mode == "graph":
+        dev = torch.cuda.current_device()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream(dev)
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(K):
+                    fn(i)
+        torch.cuda.synchronize()
+        g.replay()  # untimed: the first replay uploads the graph
+        torch.cuda.synchronize()
+
+        def once():
+            torch.cuda.synchronize()
+            a.record(stream)
+            g.replay()
+            b.record(stream)
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) * 1e3 / K
+        once.graph = g
+        return once
+    host_us = 0.0
+    if mode == "queued":
+        n = min(K, 50)
+        t0 = time.perf_counter()
+        for i in range(n):
+            fn(i)
+        host_us = (time.perf_counter() - t0) / n * 1e6
+        torch.cuda.synchronize()
+
+    def once():
+        torch.cuda.synchronize()
+        if mode == "queued":
+            torch.cuda._sleep(int((2.0 * K * host_us + 300.0) * rate))
+        a.record(stream)
+        for i in range(K):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / K
+    return once
 
 
 def main():
@@ -429,61 +520,33 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    if args.no_graph:
-        start.record(stream)
-        for i in range(K):
-            step(sets[i % R])
-        end.record(stream)
-        torch.cuda.synchronize()
-        timing = "eager launches from Python"
-    else:
-        g = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream(dev)
-        cap.wait_stream(stream)
-        with torch.cuda.stream(cap):
-            with torch.cuda.graph(g, stream=cap):
-                for i in range(K):
-                    step(sets[i % R])
-        torch.cuda.synchronize()
-        g.replay()  # untimed: first replay uploads the graph
-        torch.cuda.synchronize()
-        start.record(stream)
-        g.replay()
-        end.record(stream)
-        torch.cuda.synchronize()
-        timing = "HIP graph replay of K launches"
-    elapsed_ms = start.elapsed_time(end)
-    ms_per_step = elapsed_ms / K
+    mode = args.timing
+    if mode == "auto":
+        mode = "eager" if args.no_graph else ("queued" if K <= QUEUED_MAX_STEPS else "graph")
+    rate = spin_rate(stream) if mode == "queued" else None
+    once = make_timed(lambda i: step(sets[i % R]), K, mode, stream, rate)
+    torch.cuda.synchronize()
+    ms_per_step = once() / 1e3  # the timed region: exactly K steps
+    timing = TIMING_DESC[mode]
 
-    # ---- spread: after the timed region, replay the same graph a few more
-    # times, each replay timed alone; the average step time of each replay
-    # gives median / p10 / p90 over replays.  (Per-dispatch spreads come from
-    # the kernel trace; single launches are too short to time with events.)
+    # ---- spread: the same K steps timed again, each block alone, for the
+    # median / p10 / p90 of the per-step average over blocks.
     spread = None
-    if not args.no_graph and args.spread_replays > 0:
-        per = []
-        for _ in range(args.spread_replays):
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            g.replay()
-            b.record(stream)
-            b.synchronize()
-            per.append(a.elapsed_time(b) * 1e3 / K)
-        per.sort()
+    if args.spread_replays > 0:
+        per = sorted(once() for _ in range(args.spread_replays))
 
         def pick(f):
             return per[min(len(per) - 1, int(f * len(per)))]
         spread = {"median": pick(0.5), "p10": pick(0.1), "p90": pick(0.9),
-                  "replays": len(per), "steps_per_replay": K}
+                  "blocks": len(per), "steps_per_block": K}
 
-    # ---- practical ceiling: a plain copy kernel (torch's) moving the same
-    # number of bytes (half read, half written), timed the same way.  Under
-    # --no-graph it also serves as the known-size calibration kernel of the
-    # counter runs (see --summarize-pmc).
-    copy = None
+    # ---- floors, timed the same way: a plain copy kernel (torch's) moving
+    # the same number of bytes (half read, half written), the practical
+    # ceiling for one launch of this size, and an almost empty kernel
+    # (torch.cuda._sleep(0)), the per-launch cost of the runtime and the
+    # command processor.  Under --no-graph the copy also serves as the
+    # known-size calibration kernel of the counter runs (see --summarize-pmc).
+    copy = floor = None
     if not args.no_copy_ceiling:
         half = algorithmic_bytes(w, N, T, args.window) // launches_per_step_of(w) // 2 // 16 * 16
         RC = max(2, int(np.ceil(args.rotate_mb * 2 ** 20 / (2 * half))))
@@ -491,35 +554,53 @@ def main():
                  torch.empty(half // 4, dtype=torch.float32, device=dev)) for _ in range(RC)]
         for a, _ in bufs:
             a.fill_(1.0)
-        KC = min(K, 1000)
-        if args.no_graph:
-            c0 = torch.cuda.Event(enable_timing=True)
-            c1 = torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            for i in range(KC):
-                bufs[i % RC][1].copy_(bufs[i % RC][0])
-            c1.record(stream)
-        else:
-            gc = torch.cuda.CUDAGraph()
-            cap = torch.cuda.Stream(dev)
-            cap.wait_stream(stream)
-            with torch.cuda.stream(cap):
-                with torch.cuda.graph(gc, stream=cap):
-                    for i in range(KC):
-                        bufs[i % RC][1].copy_(bufs[i % RC][0])
-            torch.cuda.synchronize()
-            gc.replay()
-            torch.cuda.synchronize()
-            c0 = torch.cuda.Event(enable_timing=True)
-            c1 = torch.cuda.Event(enable_timing=True)
-            c0.record(stream)
-            gc.replay()
-            c1.record(stream)
+        KC = min(K, QUEUED_MAX_STEPS)
+        mode_c = "eager" if mode == "eager" else ("queued" if rate is not None else "graph")
         torch.cuda.synchronize()
-        cus = c0.elapsed_time(c1) * 1e3 / KC
+        cus = make_timed(lambda i: bufs[i % RC][1].copy_(bufs[i % RC][0]), KC, mode_c, stream,
+                         rate)()
         copy = {"bytes_per_launch": 2 * half, "avg_launch_us": cus,
-                "GBps": 2 * half / (cus * 1e-6) / 1e9, "kernel": "torch copy_ (float32)"}
+                "GBps": 2 * half / (cus * 1e-6) / 1e9, "kernel": "torch copy_ (float32)",
+                "timing": TIMING_DESC[mode_c]}
         del bufs
+        fus = make_timed(lambda i: torch.cuda._sleep(0), KC, mode_c, stream, rate)()
+        floor = {"avg_launch_us": fus, "kernel": "torch.cuda._sleep(0), an almost empty kernel",
+                 "timing": TIMING_DESC[mode_c]}
+    # ---- kernel body: the same steps through the instrumented build of the
+    # library (librlca_timed.so: same sources, plus per-wavefront wall-clock
+    # stamps at entry and once all loads and stores are done).  For the last
+    # launch of each block of steps, the body is max(end) - min(start): the
+    # kernel's time on the GPU from its first wavefront's start to its last
+    # wavefront's completed stores, without the runtime's per-launch cost.
+    body = None
+    if args.body_blocks > 0 and mode != "eager" and os.path.exists(rl.TIMED_LIB_PATH):
+        with rl.use_library(rl.TIMED_LIB_PATH):
+            for i in range(min(args.warmup, 50)):
+                step(sets[i % R])
+            torch.cuda.synchronize()
+            KB = min(K, 200)
+            mode_b = "queued" if rate is not None else "graph"
+            once_b = make_timed(lambda i: step(sets[i % R]), KB, mode_b, stream, rate)
+            bodies, waves_us, spreads, steps_b = [], [], [], []
+            for _ in range(args.body_blocks):
+                steps_b.append(once_b())
+                st = rl.rlca_timestamps().astype(np.int64)
+                bodies.append(float(st[:, 1].max() - st[:, 0].min()) * 0.01)
+                waves_us.append(float(np.median(st[:, 1] - st[:, 0])) * 0.01)
+                spreads.append(float(st[:, 0].max() - st[:, 0].min()) * 0.01)
+            n_waves = int(st.shape[0])
+        bodies.sort()
+
+        def q(v, f):
+            v = sorted(v)
+            return v[min(len(v) - 1, int(f * len(v)))]
+        body = {"median_us": q(bodies, 0.5), "p10_us": q(bodies, 0.1), "p90_us": q(bodies, 0.9),
+                "samples": len(bodies), "wavefronts": n_waves,
+                "wave_median_us": q(waves_us, 0.5), "start_spread_us": q(spreads, 0.5),
+                "instrumented_step_us": q(steps_b, 0.5),
+                "method": "librlca_timed.so (the same sources with per-wavefront 100 MHz "
+                          "wall-clock stamps); last launch of each of %d blocks of %d steps, "
+                          "%s" % (len(bodies), KB, TIMING_DESC[mode_b])}
     launches_per_step = launches_per_step_of(w) * (3 if split_segments > 1 else 1)
     env_steps = N * T
     value = env_steps / (ms_per_step * 1e-3)
@@ -618,10 +699,16 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": bytes_per_step / launches_per_step,
-                     "avg_launch_us": ms_per_step * 1e3 / launches_per_step},
+                     "avg_launch_us": ms_per_step * 1e3 / launches_per_step,
+                     "kernel_body_us": body["median_us"] if body else None,
+                     "kernel_only_frac": (bytes_per_step / launches_per_step
+                                          / (body["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS)
+                     if body and launches_per_step == 1 else None},
+        "kernel_body": body,
         "cpu_baseline": cpu,
         "copy_ceiling": copy,
-        "replay_us_per_step": spread,
+        "launch_floor": floor,
+        "step_us_spread": spread,
         "parity_max_rel_err": parity,
         "parity": {"max_rel_err_per_output": per_output, "tolerance": tol,
                    "pass": parity <= tol},

@@ -606,6 +606,23 @@ typedef enum {
 int rlca_split_segments(int64_t num_envs, int64_t T);
 int64_t rlca_split_workspace_bytes(int64_t num_envs, int64_t T);
 
+/*
+ * Kernel timing (instrumented build only; a measurement tool, not part of
+ * the computation).  librlca.so is built without it.  librlca_timed.so, built
+ * from the same sources with RLCA_TIMESTAMPS defined (python -m
+ * reverse_linear_recurrence_amd.build --timestamps), has every wavefront of
+ * a scan kernel record the GPU's 100 MHz wall clock at entry and again once
+ * all of its loads and stores have completed.  rlca_timestamps copies the
+ * (start, end) pairs of the calling thread's last launch, one pair per
+ * wavefront in launch order, for at most max_waves wavefronts (and at most
+ * 65536), into dst (host memory, 2 * max_waves uint64), and sets *waves to
+ * the number copied; the launch's duration on the GPU is then max(end) -
+ * min(start) ticks of 10 ns.  It synchronizes with the device.  Only the
+ * last launch of each device is kept: read it before launching again.
+ * librlca.so: RLCA_EINVAL.
+ */
+int rlca_timestamps(uint64_t *dst, int64_t max_waves, int64_t *waves);
+
 int rlca_num_variants(void);
 int rlca_set_variant(int variant);
 int rlca_variant_info(int variant, int algo, int dtype, int *steps_per_lane, int *lanes_per_row,

@@ -29,6 +29,7 @@ from ._binding import (  # noqa: F401
     RLCA_F32,
     RLCA_OK,
     RlcaError,
+    TIMED_LIB_PATH,
     lib_path,
     load_library,
     rlca_affine_scan,
@@ -52,6 +53,7 @@ from ._binding import (  # noqa: F401
     rlca_split_workspace_bytes,
     rlca_td_lambda,
     rlca_td_lambda_chunk,
+    rlca_timestamps,
     rlca_variant_info,
     rlca_version,
     rlca_vtrace,
@@ -59,4 +61,5 @@ from ._binding import (  # noqa: F401
     rlca_vtrace_probs,
     rlca_vtrace_probs_chunk,
     split_workspace,
+    use_library,
 )

@@ -17,7 +17,12 @@ RLCA_F32, RLCA_BF16 = 0, 1
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "librlca.so")
-_lib = None
+# The instrumented build (per-wavefront wall-clock stamps; see rlca_timestamps).
+TIMED_LIB_PATH = os.path.join(_HERE, "librlca_timed.so")
+# Loaded builds by path; calls go to the current one (librlca.so unless
+# inside use_library).
+_libs = {}
+_current = _LIB_PATH
 
 _i64 = ctypes.c_int64
 _int = ctypes.c_int
@@ -75,6 +80,7 @@ _SIGNATURES = {
     "rlca_version": [],
     "rlca_split_segments": [_i64, _i64],
     "rlca_split_workspace_bytes": [_i64, _i64],
+    "rlca_timestamps": [_vp, _i64, ctypes.POINTER(_i64)],
     "rlca_num_variants": [],
     "rlca_set_variant": [_int],
     "rlca_variant_info": [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
@@ -95,21 +101,47 @@ def lib_path():
     return _LIB_PATH
 
 
-def load_library():
-    """Load librlca.so from the package directory (raises if it is not built)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(_LIB_PATH):
-            raise ImportError("librlca.so is not built: run "
-                              "`python -m reverse_linear_recurrence_amd.build`")
-        lib = ctypes.CDLL(_LIB_PATH)
+def load_library(path=None):
+    """Load librlca.so from the package directory (raises if it is not built)
+    and return it; with ``path``, that build of the same ABI instead
+    (TIMED_LIB_PATH: the instrumented one), without making it current (see
+    use_library)."""
+    path = path or _current
+    lib = _libs.get(path)
+    if lib is None:
+        if not os.path.exists(path):
+            raise ImportError("%s is not built: run `python -m reverse_linear_recurrence_amd.build"
+                              "%s`" % (os.path.basename(path),
+                                       " --timestamps" if path == TIMED_LIB_PATH else ""))
+        lib = ctypes.CDLL(path)
         for name, argtypes in _SIGNATURES.items():
             fn = getattr(lib, name)
             fn.argtypes = argtypes
             fn.restype = {"rlca_last_error": ctypes.c_char_p,
                           "rlca_split_workspace_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
-        _lib = lib
-    return _lib
+        _libs[path] = lib
+    return lib
+
+
+class use_library:
+    """``with use_library(path):`` routes this module's calls to another
+    build of the library (e.g. TIMED_LIB_PATH) on the calling thread's
+    behalf, for the duration of the block (not thread-safe: one current
+    build per process)."""
+
+    def __init__(self, path):
+        self.path = path
+
+    def __enter__(self):
+        global _current
+        load_library(self.path)
+        self.prev, _current = _current, self.path
+        return _libs[self.path]
+
+    def __exit__(self, *exc):
+        global _current
+        _current = self.prev
+        return False
 
 
 def _check(rc):
@@ -788,6 +820,18 @@ def split_workspace(num_envs, T, device="cuda"):
     if b == 0:
         return None
     return torch.empty(b // 4, dtype=torch.float32, device=device)
+
+
+def rlca_timestamps(max_waves=1 << 16):
+    """Instrumented build only: the (start, end) wall-clock stamps, in ticks
+    of 10 ns, of every wavefront of the calling thread's last launch, as a
+    uint64 numpy array [waves, 2].  Synchronizes with the device."""
+    import numpy as np
+    buf = (ctypes.c_uint64 * (2 * max_waves))()
+    n = _i64()
+    _check(load_library().rlca_timestamps(ctypes.cast(buf, _vp), int(max_waves),
+                                          ctypes.byref(n)))
+    return np.frombuffer(buf, dtype=np.uint64, count=2 * n.value).reshape(-1, 2).copy()
 
 
 def rlca_last_variant():

@@ -15,6 +15,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librlca.so")
+# The instrumented build: the same sources with RLCA_TIMESTAMPS defined, so
+# that the scan kernels record per-wavefront wall-clock stamps (a measurement
+# tool for bench.py; never loaded by default).
+LIB_TIMED = os.path.join(PKG, "librlca_timed.so")
 # Host code and the kernel tables, compiled in parallel.
 SOURCES = [os.path.join(CSRC, n) for n in ("rlca.hip", "kernels_plain.hip", "kernels_window.hip",
                                            "kernels_probs.hip")]
@@ -30,8 +34,9 @@ def hipcc():
     return path if os.path.exists(path) else "hipcc"
 
 
-def compile_command(src, obj):
-    return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-c",
+def compile_command(src, obj, timestamps=False):
+    return [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-c"] + (
+        ["-DRLCA_TIMESTAMPS"] if timestamps else []) + [
             # Packed fp32 ops (v_pk_*_f32) stay off: plain scalar fp32 only.
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             # Leading scalar kernel arguments are preloaded into SGPRs.
@@ -62,12 +67,14 @@ def up_to_date():
     return all(os.path.getmtime(d) <= t for d in DEPS)
 
 
-def build(verbose=False):
-    """Compile librlca.so (always) and return its path."""
-    tag = ".tmp%d" % os.getpid()
+def build(verbose=False, timestamps=False):
+    """Compile librlca.so (always; with timestamps, librlca_timed.so) and
+    return its path."""
+    target = LIB_TIMED if timestamps else LIB
+    tag = ".tmp%d%s" % (os.getpid(), "t" if timestamps else "")
     objs = [os.path.join(PKG, os.path.basename(src).replace(".hip", tag + ".o")) for src in SOURCES]
-    cmds = [compile_command(src, obj) for src, obj in zip(SOURCES, objs)]
-    tmp = LIB + tag
+    cmds = [compile_command(src, obj, timestamps) for src, obj in zip(SOURCES, objs)]
+    tmp = target + tag
     try:
         if verbose:
             for c in cmds:
@@ -82,14 +89,14 @@ def build(verbose=False):
         rc, out = _run(link_command(objs, tmp))
         if rc != 0:
             raise RuntimeError("hipcc link failed (%d):\n%s" % (rc, out))
-        os.replace(tmp, LIB)
+        os.replace(tmp, target)
     finally:
         for f in objs + [tmp]:
             if os.path.exists(f):
                 os.remove(f)
-    return LIB
+    return target
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, timestamps="--timestamps" in sys.argv[1:]))
     sys.exit(0)

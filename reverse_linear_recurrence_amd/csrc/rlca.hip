@@ -63,6 +63,7 @@ thread_local std::string t_last_error;
 thread_local int t_forced_variant = -1;
 thread_local int t_last_variant = -1;
 
+
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 int fail(int status, const char *fmt, ...) {
   char buf[512];
@@ -73,6 +74,35 @@ int fail(int status, const char *fmt, ...) {
   t_last_error = buf;
   return status;
 }
+
+#ifdef RLCA_TIMESTAMPS
+// Instrumented build: the wavefronts' wall-clock stamps of the last scan
+// kernel launched on each device (see scan_kernels.hpp), and the number of
+// wavefronts of the calling thread's last launch.
+static __device__ __align__(256) uint64_t stamp_buf[2 * kStampWaves];
+std::mutex g_stamp_mutex;
+uint64_t *g_stamp_buf[64];
+thread_local int64_t t_last_waves = 0;
+thread_local int t_last_device = 0;
+
+int stamp_buffer(int *dev_out, uint64_t **out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(RLCA_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(RLCA_EINVAL, "device %d beyond the stamp table", dev);
+  std::lock_guard<std::mutex> lock(g_stamp_mutex);
+  if (g_stamp_buf[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(stamp_buf));
+    if (e != hipSuccess || p == nullptr)
+      return fail(RLCA_EHIP, "address of the stamp buffer: %s", hipGetErrorString(e));
+    g_stamp_buf[dev] = static_cast<uint64_t *>(p);
+  }
+  *dev_out = dev;
+  *out = g_stamp_buf[dev];
+  return RLCA_OK;
+}
+#endif
 
 // ------------------------------------------------------------- validation
 
@@ -176,6 +206,10 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
   block = dim3(64 * waves);
   Args a = args;
   a.seg_count = S;
+#ifdef RLCA_TIMESTAMPS
+  int stamp_dev = 0;
+  RLCA_TRY(stamp_buffer(&stamp_dev, &a.stamps));
+#endif
   // Truncation bootstraps of the whole call: dense reads for small batches.
   const bool dense_tv = args.N * S * args.T <= kDenseTvMaxSteps;
   // Hot streams (see scan_kernels.hpp), passed again as preloaded scalars.
@@ -236,6 +270,10 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
   if (e != hipSuccess)
     return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   t_last_variant = v;
+#ifdef RLCA_TIMESTAMPS
+  t_last_waves = static_cast<int64_t>(grid.x) * grid.y * waves;
+  t_last_device = stamp_dev;
+#endif
   return RLCA_OK;
 }
 
@@ -1145,6 +1183,29 @@ int64_t rlca_split_workspace_bytes(int64_t num_envs, int64_t T) {
   }
   const int64_t S = split_count(num_envs, T);
   return S > 1 ? 12 * num_envs * S : 0;
+}
+
+int rlca_timestamps(uint64_t *dst, int64_t max_waves, int64_t *waves) {
+#ifdef RLCA_TIMESTAMPS
+  if (dst == nullptr || waves == nullptr || max_waves < 0)
+    return fail(RLCA_EINVAL, "dst and waves must not be NULL, max_waves >= 0");
+  int dev = 0;
+  uint64_t *buf = nullptr;
+  RLCA_TRY(stamp_buffer(&dev, &buf));
+  if (dev != t_last_device) return fail(RLCA_EINVAL, "the last launch ran on another device");
+  int64_t n = t_last_waves < kStampWaves ? t_last_waves : kStampWaves;
+  if (n > max_waves) n = max_waves;
+  const hipError_t e = hipMemcpy(dst, buf, static_cast<size_t>(2 * n) * sizeof(uint64_t),
+                                 hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(RLCA_EHIP, "reading the stamps: %s", hipGetErrorString(e));
+  *waves = n;
+  return RLCA_OK;
+#else
+  (void)dst;
+  (void)max_waves;
+  if (waves != nullptr) *waves = 0;
+  return fail(RLCA_EINVAL, "this build records no timestamps (the instrumented build does)");
+#endif
 }
 
 int rlca_num_variants(void) { return kNumVariants; }

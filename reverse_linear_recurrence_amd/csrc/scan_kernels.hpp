@@ -93,7 +93,42 @@ struct Args {
   float *cout;
   float *cmap;
   int seg_count = 1;  // window instances: segments per row (gridDim.y; 1 unless split)
+#ifdef RLCA_TIMESTAMPS
+  uint64_t *stamps;   // instrumented build: per-wavefront wall-clock stamps
+#endif
 };
+
+#ifdef RLCA_TIMESTAMPS
+// Instrumented build only (compiled with -DRLCA_TIMESTAMPS into a library of
+// its own, never the product library): every wavefront of a scan kernel
+// records the 100 MHz wall clock at entry and again once all of its loads and
+// stores have completed, as (start, end) at stamps[2 * w], w the wavefront's
+// index in the launch (the first kStampWaves wavefronts only).  The launch's
+// duration on the GPU is then max(end) - min(start), without the runtime's
+// per-launch cost around it.
+constexpr int64_t kStampWaves = 1 << 16;
+
+__device__ __forceinline__ uint64_t wall_clock() { return __builtin_amdgcn_s_memrealtime(); }
+
+// Taken at a kernel's entry; its destructor, run at every return, waits for
+// the wavefront's loads and stores and records both stamps.
+struct WaveStamp {
+  uint64_t *stamps;
+  uint64_t start;
+  __device__ ~WaveStamp() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0);  // every load and store of this wavefront done
+    const uint64_t end = wall_clock();
+    const int waves = static_cast<int>(blockDim.x) >> 6;
+    const int64_t w = (static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * waves +
+                      (threadIdx.x >> 6);
+    if ((threadIdx.x & 63) == 0 && w < kStampWaves) {
+      stamps[2 * w] = start;
+      stamps[2 * w + 1] = end;
+    }
+  }
+};
+#endif
 
 // Hot streams: the (up to) five arrays each algorithm reads at the start of a
 // tile.  They are passed again as leading scalar kernel arguments h0..h4,
@@ -964,6 +999,9 @@ __global__ void __launch_bounds__(64 * short_row_waves(WPR, LPR, kChunk))
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
             int N32, int T32, int ldT, int ldX, const Args p) {
   static_assert(WPR == 1 || LPR == 64, "multi-wavefront rows use whole wavefronts");
+#ifdef RLCA_TIMESTAMPS
+  const WaveStamp stamp{p.stamps, wall_clock()};  // written at every return
+#endif
   constexpr int kWaves = short_row_waves(WPR, LPR, kChunk);
   constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
   constexpr int kTile = kGroup * K;
