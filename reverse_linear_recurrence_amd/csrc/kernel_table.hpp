@@ -8,34 +8,43 @@
 
 namespace rlca {
 
-template <int A, typename InT, int V, bool U, bool C>
+template <int A, typename InT, int V, bool U, bool C, bool O>
 const void *kernel_ptr() {
   constexpr Variant v = kVariants[V];
   constexpr int K = steps_per_lane(v, sizeof(InT) == 2, A == kVtrace);
-  return reinterpret_cast<const void *>(&scan_kernel<A, InT, K, v.LPR, v.WPR, U, C>);
+  return reinterpret_cast<const void *>(&scan_kernel<A, InT, K, v.LPR, v.WPR, U, C, O>);
 }
 
-template <int A, typename InT, bool U, bool C>
+template <int A, typename InT, bool U, bool C, bool O>
 const void *kernel_ptr(int v) {
   static_assert(kNumVariants == 9, "one case per variant");
   switch (v) {
-    case 0: return kernel_ptr<A, InT, 0, U, C>();
-    case 1: return kernel_ptr<A, InT, 1, U, C>();
-    case 2: return kernel_ptr<A, InT, 2, U, C>();
-    case 3: return kernel_ptr<A, InT, 3, U, C>();
-    case 4: return kernel_ptr<A, InT, 4, U, C>();
-    case 5: return kernel_ptr<A, InT, 5, U, C>();
-    case 6: return kernel_ptr<A, InT, 6, U, C>();
-    case 7: return kernel_ptr<A, InT, 7, U, C>();
-    default: return kernel_ptr<A, InT, 8, U, C>();
+    case 0: return kernel_ptr<A, InT, 0, U, C, O>();
+    case 1: return kernel_ptr<A, InT, 1, U, C, O>();
+    case 2: return kernel_ptr<A, InT, 2, U, C, O>();
+    case 3: return kernel_ptr<A, InT, 3, U, C, O>();
+    case 4: return kernel_ptr<A, InT, 4, U, C, O>();
+    case 5: return kernel_ptr<A, InT, 5, U, C, O>();
+    case 6: return kernel_ptr<A, InT, 6, U, C, O>();
+    case 7: return kernel_ptr<A, InT, 7, U, C, O>();
+    default: return kernel_ptr<A, InT, 8, U, C, O>();
   }
 }
 
+// one: the one-tile instance (rows of exactly one whole tile); it exists for
+// the plain instances (C false) with a uniform row stride.
 template <int A, bool C>
-const void *kernel_ptr(int dtype, int v, bool uniform) {
+const void *kernel_ptr(int dtype, int v, bool uniform, bool one = false) {
+  if constexpr (!C) {
+    if (uniform && one) {
+      return dtype == RLCA_BF16 ? kernel_ptr<A, bf16_t, true, C, true>(v)
+                                : kernel_ptr<A, float, true, C, true>(v);
+    }
+  }
   if (dtype == RLCA_BF16)
-    return uniform ? kernel_ptr<A, bf16_t, true, C>(v) : kernel_ptr<A, bf16_t, false, C>(v);
-  return uniform ? kernel_ptr<A, float, true, C>(v) : kernel_ptr<A, float, false, C>(v);
+    return uniform ? kernel_ptr<A, bf16_t, true, C, false>(v)
+                   : kernel_ptr<A, bf16_t, false, C, false>(v);
+  return uniform ? kernel_ptr<A, float, true, C, false>(v) : kernel_ptr<A, float, false, C, false>(v);
 }
 
 }  // namespace rlca

@@ -4,15 +4,15 @@
 
 namespace rlca {
 
-const void *plain_kernel(int algo, int dtype, int v, bool uniform) {
+const void *plain_kernel(int algo, int dtype, int v, bool uniform, bool one) {
   switch (algo) {
-    case kReturns: return kernel_ptr<kReturns, false>(dtype, v, uniform);
-    case kGae: return kernel_ptr<kGae, false>(dtype, v, uniform);
-    case kTdLambda: return kernel_ptr<kTdLambda, false>(dtype, v, uniform);
-    case kVtrace: return kernel_ptr<kVtrace, false>(dtype, v, uniform);
-    case kRetrace: return kernel_ptr<kRetrace, false>(dtype, v, uniform);
-    case kEligibility: return kernel_ptr<kEligibility, false>(dtype, v, uniform);
-    case kCumsum: return kernel_ptr<kCumsum, false>(dtype, v, uniform);
+    case kReturns: return kernel_ptr<kReturns, false>(dtype, v, uniform, one);
+    case kGae: return kernel_ptr<kGae, false>(dtype, v, uniform, one);
+    case kTdLambda: return kernel_ptr<kTdLambda, false>(dtype, v, uniform, one);
+    case kVtrace: return kernel_ptr<kVtrace, false>(dtype, v, uniform, one);
+    case kRetrace: return kernel_ptr<kRetrace, false>(dtype, v, uniform, one);
+    case kEligibility: return kernel_ptr<kEligibility, false>(dtype, v, uniform, one);
+    case kCumsum: return kernel_ptr<kCumsum, false>(dtype, v, uniform, one);
     default: return nullptr;
   }
 }

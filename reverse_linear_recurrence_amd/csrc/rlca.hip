@@ -262,8 +262,11 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
   int ldT = static_cast<int>(a.ld_r);
   int ldX = static_cast<int>(ldx);
   void *kargs[] = {&hot[0], &hot[1], &hot[2], &hot[3], &hot[4], &N32, &T32, &ldT, &ldX, &a};
+  // Rows of exactly one whole tile take the one-tile instance (fewer
+  // registers, so more wavefronts per SIMD).
+  const bool one = args.T == tile_steps(var, dtype == RLCA_BF16, algo == kVtrace);
   const void *kernel = window ? window_kernel(algo, dtype, v, uniform)
-                              : plain_kernel(algo, dtype, v, uniform);
+                              : plain_kernel(algo, dtype, v, uniform, one);
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no kernel for algorithm %d", algo);
   const hipError_t e = hipLaunchKernel(kernel, grid, block, kargs, 0,
                                        static_cast<hipStream_t>(stream));

@@ -990,11 +990,16 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 
 // Algo A, input type InT, K steps per lane, LPR lanes per row inside one
 // wavefront (WPR == 1), or WPR wavefronts per row (then LPR must be 64).
+// kOne: an instance for rows of exactly one whole tile (T == K * lanes per
+// row) only.  It holds one tile of loads and no tile loop, so it needs far
+// fewer VGPRs than the general instance (which sizes its registers for the
+// two-buffer loop), and more of its wavefronts fit on a SIMD at once.
 // Workgroup: 64 * short_row_waves(WPR, LPR, kChunk) threads.
 // h0..h4, N32, T32, ldT, ldX: the preloaded hot arguments (see above); they
 // duplicate fields of p.  kChunk: window instance (carry vector in, carry and
 // carry map out).
-template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk>
+template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk,
+          bool kOne = false>
 __global__ void __launch_bounds__(64 * short_row_waves(WPR, LPR, kChunk))
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
             int N32, int T32, int ldT, int ldX, const Args p) {
@@ -1114,9 +1119,9 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
   // (g = 0 owns the latest steps), forward ones along it.
   const int64_t lane_off =
       static_cast<int64_t>(Uses<A>::forward ? g : kGroup - 1 - g) * K;
-  auto t0_of = [&](int64_t c) { return c * kTile + lane_off; };
+  [[maybe_unused]] auto t0_of = [&](int64_t c) { return c * kTile + lane_off; };
 
-  if (ntiles == 1 && T == kTile) {
+  if (kOne || (ntiles == 1 && T == kTile)) {
     // One whole tile: straight-line code.
     Tile<K> x;
     issue_tile<A, InT, K>(p, rp, lane_off, T - lane_off, x);
@@ -1127,95 +1132,97 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
                                                      write_window);
     return;
   }
-  const bool ragged = T % kTile != 0;
-  if constexpr (Uses<A>::forward) {
-    // Tiles from the first to the last; the ragged one comes last.  Same
-    // two-buffer pipeline as below, in increasing c.
-    const int64_t nwhole = ragged ? ntiles - 1 : ntiles;
-    Tile<K> buf_a, buf_b;
-    int64_t c = 0;
-    if (nwhole > 0) {
-      issue_tile<A, InT, K>(p, rp, t0_of(0), T - t0_of(0), buf_a);
-      if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
-      for (;;) {
-        {
-          finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
-          const int64_t cn = c + 1 < nwhole ? c + 1 : c;
-          issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
-          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
-              p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
-              s_agg, m, win, write_window);
+  if constexpr (!kOne) {
+    const bool ragged = T % kTile != 0;
+    if constexpr (Uses<A>::forward) {
+      // Tiles from the first to the last; the ragged one comes last.  Same
+      // two-buffer pipeline as below, in increasing c.
+      const int64_t nwhole = ragged ? ntiles - 1 : ntiles;
+      Tile<K> buf_a, buf_b;
+      int64_t c = 0;
+      if (nwhole > 0) {
+        issue_tile<A, InT, K>(p, rp, t0_of(0), T - t0_of(0), buf_a);
+        if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+        for (;;) {
+          {
+            finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
+            const int64_t cn = c + 1 < nwhole ? c + 1 : c;
+            issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
+            carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+                p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
+                s_agg, m, win, write_window);
+          }
+          if (++c == nwhole) break;
+          {
+            finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
+            const int64_t cn = c + 1 < nwhole ? c + 1 : c;
+            issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
+            carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+                p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
+                s_agg, m, win, write_window);
+          }
+          if (++c == nwhole) break;
         }
-        if (++c == nwhole) break;
-        {
-          finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
-          const int64_t cn = c + 1 < nwhole ? c + 1 : c;
-          issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
-          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
-              p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
-              s_agg, m, win, write_window);
-        }
-        if (++c == nwhole) break;
       }
+      if (ragged) {
+        const int64_t te0 = t0_of(ntiles - 1);
+        const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
+        Tile<K> x;
+        load_edge<A, InT, K>(p, rp, te0, lim, T, x);
+        if constexpr (kChunk) {
+          if (nwhole == 0) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+        }
+        tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok, ntiles - 1,
+                                                        false, lane, wave, carry, s_agg, m, win,
+                                                        write_window);
+      }
+      return;
     }
+    int64_t c = ragged ? ntiles - 2 : ntiles - 1;  // latest whole tile
+    // Two explicit buffers, alternating: tile c is decoded (and its sparse
+    // bootstrap loads issued) before tile c-1's loads are issued into the other
+    // buffer, then tile c is computed.  In-order load completion then lets the
+    // computation of tile c wait for tile c only, and no register copies are
+    // needed between iterations.  The prefetch is unconditional (no branch for
+    // the wait-count analysis to merge): after tile 0 it re-reads tile 0, which
+    // was just loaded (cache hits, never used).
+    Tile<K> buf_a, buf_b;
+    if (c >= 0) issue_tile<A, InT, K>(p, rp, t0_of(c), T - t0_of(c), buf_a);
     if (ragged) {
       const int64_t te0 = t0_of(ntiles - 1);
       const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
       Tile<K> x;
       load_edge<A, InT, K>(p, rp, te0, lim, T, x);
-      if constexpr (kChunk) {
-        if (nwhole == 0) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+      if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+      carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok,
+                                                              ntiles - 1, c >= 0, lane, wave, carry,
+                                                              s_agg, m, win, write_window);
+    } else {
+      if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+    }
+    if (c < 0) return;
+    for (;;) {
+      {
+        finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
+        const int64_t cn = c > 0 ? c - 1 : 0;
+        issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
+        carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+            p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
+            win, write_window);
       }
-      tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok, ntiles - 1,
-                                                      false, lane, wave, carry, s_agg, m, win,
-                                                      write_window);
+      if (c == 0) break;
+      --c;
+      {
+        finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
+        const int64_t cn = c > 0 ? c - 1 : 0;
+        issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
+        carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+            p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
+            win, write_window);
+      }
+      if (c == 0) break;
+      --c;
     }
-    return;
-  }
-  int64_t c = ragged ? ntiles - 2 : ntiles - 1;  // latest whole tile
-  // Two explicit buffers, alternating: tile c is decoded (and its sparse
-  // bootstrap loads issued) before tile c-1's loads are issued into the other
-  // buffer, then tile c is computed.  In-order load completion then lets the
-  // computation of tile c wait for tile c only, and no register copies are
-  // needed between iterations.  The prefetch is unconditional (no branch for
-  // the wait-count analysis to merge): after tile 0 it re-reads tile 0, which
-  // was just loaded (cache hits, never used).
-  Tile<K> buf_a, buf_b;
-  if (c >= 0) issue_tile<A, InT, K>(p, rp, t0_of(c), T - t0_of(c), buf_a);
-  if (ragged) {
-    const int64_t te0 = t0_of(ntiles - 1);
-    const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
-    Tile<K> x;
-    load_edge<A, InT, K>(p, rp, te0, lim, T, x);
-    if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
-    carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok,
-                                                            ntiles - 1, c >= 0, lane, wave, carry,
-                                                            s_agg, m, win, write_window);
-  } else {
-    if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
-  }
-  if (c < 0) return;
-  for (;;) {
-    {
-      finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
-      const int64_t cn = c > 0 ? c - 1 : 0;
-      issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
-      carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
-          p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
-          win, write_window);
-    }
-    if (c == 0) break;
-    --c;
-    {
-      finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
-      const int64_t cn = c > 0 ? c - 1 : 0;
-      issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
-      carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
-          p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
-          win, write_window);
-    }
-    if (c == 0) break;
-    --c;
   }
 }
 
