@@ -84,6 +84,10 @@ def parse():
     ap.add_argument("--variant", type=int, default=-1, help="force a tiling variant")
     ap.add_argument("--window", action="store_true",
                     help="time the window entry point (carry in; carry and carry map out)")
+    ap.add_argument("--materialized", action="store_true",
+                    help="time the materialized doubling scan (rlca_X_materialized, the "
+                         "pages' comparison baseline re-created in HIP) instead of the fused "
+                         "kernel")
     ap.add_argument("--split", action="store_true",
                     help="call the window form with a workspace (and, without --window, no "
                          "carries), so that calls on few long rows split every row into "
@@ -406,7 +410,41 @@ def main():
         else:
             raise ValueError(w.algo)
 
+    mat_ws = None
+    if args.materialized:
+        if args.window or args.split or w.algo not in ("returns", "gae", "td_lambda",
+                                                       "vtrace+retrace"):
+            print("--materialized: a plain call of returns, GAE, TD(lambda), V-trace or "
+                  "Retrace", file=sys.stderr)
+            sys.exit(2)
+        mat_ws = torch.empty(rl.rlca_materialized_workspace_bytes(N, T) // 4,
+                             dtype=torch.float32, device=dev)
+
+    def materialized_step(d):
+        kw = dict(workspace=mat_ws)
+        if w.algo == "gae":
+            rl.rlca_gae_materialized(d["rewards"], d["values"], d["terminated"],
+                                     d.get("truncated"), d.get("trunc_values"), gamma=gamma,
+                                     lam=lam, advantages=d["_o0"], targets=d["_o1"], **kw)
+        elif w.algo == "td_lambda":
+            rl.rlca_td_lambda_materialized(d["rewards"], d["values"], d["terminated"],
+                                           d.get("truncated"), d.get("trunc_values"),
+                                           gamma=gamma, lam=lam, out=d["_o0"], **kw)
+        elif w.algo == "returns":
+            rl.rlca_returns_materialized(d["rewards"], d["terminated"], gamma=gamma,
+                                         out=d["_o0"], **kw)
+        else:
+            rl.rlca_vtrace_materialized(d["rewards"], d["values"], d["log_rhos"],
+                                        d["terminated"], gamma=gamma, lam=lam, vs=d["_o0"],
+                                        pg_advantages=d["_o1"], **clips, **kw)
+            rl.rlca_retrace_materialized(d["rewards"], d["q_taken"], d["exp_q_next"],
+                                         d["log_rhos"], d["terminated"], gamma=gamma, lam=lam,
+                                         c_bar=clips["c_bar"], out=d["_o2"], **kw)
+
     def step(d):
+        if args.materialized:
+            materialized_step(d)
+            return
         if args.window or args.split:
             window_step(d)
             return
@@ -588,7 +626,8 @@ def main():
     # kernel's time on the GPU from its first wavefront's start to its last
     # wavefront's completed stores, without the runtime's per-launch cost.
     body = None
-    if args.body_blocks > 0 and mode != "eager" and os.path.exists(rl.TIMED_LIB_PATH):
+    if (args.body_blocks > 0 and mode != "eager" and not args.materialized
+            and os.path.exists(rl.TIMED_LIB_PATH)):
         with rl.use_library(rl.TIMED_LIB_PATH):
             for i in range(min(args.warmup, 50)):
                 step(sets[i % R])
@@ -617,10 +656,13 @@ def main():
                           "wall-clock stamps); last launch of each of %d blocks of %d steps, "
                           "%s" % (len(bodies), KB, TIMING_DESC[mode_b])}
     launches_per_step = launches_per_step_of(w) * (3 if split_segments > 1 else 1)
+    if args.materialized:
+        launches_per_step = launches_per_step_of(w) * (2 + max(0, (T - 1).bit_length()))
     env_steps = N * T
     value = env_steps / (ms_per_step * 1e-3)
     bytes_per_step = algorithmic_bytes(w, N, T, args.window)
-    traffic_key = w.name + ("/window" if args.window else "")
+    traffic_key = w.name + ("/window" if args.window else "") + (
+        "/materialized" if args.materialized else "")
     achieved = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
     # ---- HBM traffic from the committed counter runs, if they match this kernel
@@ -711,7 +753,8 @@ def main():
                    "launches_per_step": launches_per_step, "variant": variant,
                    "split_segments": split_segments,
                    "entry": "window (carry in; carry and carry map out)" if args.window
-                   else "plain"},
+                   else ("materialized doubling scan (2 + ceil(log2 T) launches through HBM)"
+                         if args.materialized else "plain")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
                      "algorithmic_bytes_per_launch": bytes_per_step / launches_per_step,

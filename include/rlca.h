@@ -243,6 +243,86 @@ int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype,
                          void *stream);
 
 /*
+ * The materialized doubling scan (Problem: the vectorized O(log T) scan that
+ * writes its intermediates to HBM and reads them back at every step, the
+ * baseline the pages measure the fused kernels against; Method 2, Results).
+ * Re-created in HIP so that the comparison can be made on MI355X; a
+ * reference point, not a faster path.  rlca_X_materialized computes what
+ * rlca_X computes (same arguments, same results up to rounding order, same
+ * validation), in 2 + ceil(log2 T) kernel launches instead of one:
+ *   1. (alpha_t, beta_t) of every step, as the coefficient table of rlca_X
+ *      states them, written to the workspace;
+ *   2. for s = 1, 2, 4, ... < T: every step composes its pair with the pair
+ *      s steps later, (a_t, b_t) <- (a_t + b_t a_{t+s}, b_t b_{t+s}) where
+ *      t + s < T, from one pair of arrays into the other;
+ *   3. A_t = a_t + b_t A_T (A_T: returns' bootstrap, else 0) and the outputs.
+ * Each launch streams whole [N, T] arrays through HBM: at T = 128, about 9
+ * times the bytes of the fused call.
+ * Workspace.  Device memory owned by the caller, 4-byte aligned, at least
+ * rlca_materialized_workspace_bytes(N, T) = 16 N T bytes (two pairs of fp32
+ * [N, T] arrays), not overlapping the call's arrays (RLCA_EALIAS); NULL or
+ * smaller -> RLCA_EINVAL.  Calls sharing a workspace must be ordered.
+ * rlca_materialized_workspace_bytes: -1 for num_envs < 0, T < 1, or a size
+ * past 2^63 bytes.
+ */
+int64_t rlca_materialized_workspace_bytes(int64_t num_envs, int64_t T);
+int rlca_returns_materialized(int64_t num_envs, int64_t T, int dtype,
+                              const void *rewards, int64_t ld_rewards,
+                              const uint8_t *terminated, int64_t ld_terminated,
+                              const uint8_t *truncated, int64_t ld_truncated,
+                              const void *trunc_values, int64_t ld_trunc_values,
+                              const void *bootstrap,
+                              float gamma,
+                              float *returns, int64_t ld_returns,
+                              void *workspace, int64_t workspace_bytes,
+                              void *stream);
+int rlca_gae_materialized(int64_t num_envs, int64_t T, int dtype,
+                          const void *rewards, int64_t ld_rewards,
+                          const void *values, int64_t ld_values,
+                          const uint8_t *terminated, int64_t ld_terminated,
+                          const uint8_t *truncated, int64_t ld_truncated,
+                          const void *trunc_values, int64_t ld_trunc_values,
+                          float gamma, float lam,
+                          float *advantages, int64_t ld_advantages,
+                          float *targets, int64_t ld_targets,
+                          void *workspace, int64_t workspace_bytes,
+                          void *stream);
+int rlca_td_lambda_materialized(int64_t num_envs, int64_t T, int dtype,
+                                const void *rewards, int64_t ld_rewards,
+                                const void *values, int64_t ld_values,
+                                const uint8_t *terminated, int64_t ld_terminated,
+                                const uint8_t *truncated, int64_t ld_truncated,
+                                const void *trunc_values, int64_t ld_trunc_values,
+                                float gamma, float lam,
+                                float *lambda_returns, int64_t ld_lambda_returns,
+                                void *workspace, int64_t workspace_bytes,
+                                void *stream);
+int rlca_vtrace_materialized(int64_t num_envs, int64_t T, int dtype,
+                             const void *rewards, int64_t ld_rewards,
+                             const void *values, int64_t ld_values,
+                             const void *log_rhos, int64_t ld_log_rhos,
+                             const uint8_t *terminated, int64_t ld_terminated,
+                             const uint8_t *truncated, int64_t ld_truncated,
+                             const void *trunc_values, int64_t ld_trunc_values,
+                             float gamma, float lam, float rho_bar, float c_bar,
+                             float pg_rho_bar,
+                             float *vs, int64_t ld_vs,
+                             float *pg_advantages, int64_t ld_pg_advantages,
+                             void *workspace, int64_t workspace_bytes,
+                             void *stream);
+int rlca_retrace_materialized(int64_t num_envs, int64_t T, int dtype,
+                              const void *rewards, int64_t ld_rewards,
+                              const void *q_taken, int64_t ld_q_taken,
+                              const void *exp_q_next, int64_t ld_exp_q_next,
+                              const void *log_rhos, int64_t ld_log_rhos,
+                              const uint8_t *terminated, int64_t ld_terminated,
+                              const uint8_t *truncated, int64_t ld_truncated,
+                              float gamma, float lam, float c_bar,
+                              float *q_ret, int64_t ld_q_ret,
+                              void *workspace, int64_t workspace_bytes,
+                              void *stream);
+
+/*
  * Window entry points (Method 3, "rollout windows"; Method 1: the operator is
  * associative, so a rollout can be cut along time and the pieces chained).
  * A rollout longer than one call -- streamed as it is collected, or cut into

@@ -13,7 +13,8 @@ Functions (same names as the C ABI):
 their window forms (carry in; carry and carry map out) with the suffix
 _chunk (and rlca_gae_chunk_noalloc, which needs no workspace), the generic
 segmented scan rlca_affine_scan, Retrace and V-trace from
-policy log-probability tables (rlca_retrace_probs, rlca_vtrace_probs), and the
+policy log-probability tables (rlca_retrace_probs, rlca_vtrace_probs), the
+materialized doubling scan the pages compare against (rlca_X_materialized), and the
 tiling controls rlca_set_variant, rlca_num_variants,
 rlca_variant_info, rlca_last_variant, the split-call sizes
 rlca_split_segments and rlca_split_workspace_bytes (split_workspace allocates
@@ -40,24 +41,30 @@ from ._binding import (  # noqa: F401
     rlca_gae,
     rlca_gae_chunk,
     rlca_gae_chunk_noalloc,
+    rlca_gae_materialized,
     rlca_last_variant,
+    rlca_materialized_workspace_bytes,
     rlca_num_variants,
     rlca_retrace,
     rlca_retrace_chunk,
+    rlca_retrace_materialized,
     rlca_retrace_probs,
     rlca_retrace_probs_chunk,
     rlca_returns,
     rlca_returns_chunk,
+    rlca_returns_materialized,
     rlca_set_variant,
     rlca_split_segments,
     rlca_split_workspace_bytes,
     rlca_td_lambda,
     rlca_td_lambda_chunk,
+    rlca_td_lambda_materialized,
     rlca_timestamps,
     rlca_variant_info,
     rlca_version,
     rlca_vtrace,
     rlca_vtrace_chunk,
+    rlca_vtrace_materialized,
     rlca_vtrace_probs,
     rlca_vtrace_probs_chunk,
     split_workspace,

@@ -76,6 +76,19 @@ _SIGNATURES = {
                                 _i64, _vp, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _f32,
                                 _f32, _f32, _f32, _f32, _vp, _i64, _vp, _i64, _vp, _vp, _vp,
                                 _vp],
+    "rlca_materialized_workspace_bytes": [_i64, _i64],
+    "rlca_returns_materialized": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                  _vp, _f32, _vp, _i64, _vp, _i64, _vp],
+    "rlca_gae_materialized": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp,
+                              _i64, _f32, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _vp],
+    "rlca_td_lambda_materialized": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                    _vp, _i64, _f32, _f32, _vp, _i64, _vp, _i64, _vp],
+    "rlca_vtrace_materialized": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                 _vp, _i64, _vp, _i64, _f32, _f32, _f32, _f32, _f32, _vp, _i64,
+                                 _vp, _i64, _vp, _i64, _vp],
+    "rlca_retrace_materialized": [_i64, _i64, _int, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64,
+                                  _vp, _i64, _vp, _i64, _f32, _f32, _f32, _vp, _i64, _vp, _i64,
+                                  _vp],
     "rlca_last_error": [],
     "rlca_version": [],
     "rlca_split_segments": [_i64, _i64],
@@ -118,7 +131,9 @@ def load_library(path=None):
             fn = getattr(lib, name)
             fn.argtypes = argtypes
             fn.restype = {"rlca_last_error": ctypes.c_char_p,
-                          "rlca_split_workspace_bytes": ctypes.c_int64}.get(name, ctypes.c_int)
+                          "rlca_split_workspace_bytes": ctypes.c_int64,
+                          "rlca_materialized_workspace_bytes": ctypes.c_int64}.get(name,
+                                                                                    ctypes.c_int)
         _libs[path] = lib
     return lib
 
@@ -341,6 +356,128 @@ def rlca_episodic_cumsum(x, terminated=None, truncated=None, s_init=None, *, out
     out, o, ld_o = _output("sums", out, (N, T), dev)
     _check(load_library().rlca_episodic_cumsum(N, T, code, a, ld_a, te, ld_te, tr, ld_tr, s0, o,
                                                ld_o, _stream(stream, dev)))
+    return out
+
+
+# ------------------------------------------------ materialized doubling scan
+#
+# rlca_X_materialized: the results of rlca_X through the materialized O(log T)
+# doubling scan (the pages' comparison baseline, re-created in HIP), with a
+# workspace of rlca_materialized_workspace_bytes(N, T) bytes (allocated here
+# when not given).
+
+
+def rlca_materialized_workspace_bytes(num_envs, T):
+    b = load_library().rlca_materialized_workspace_bytes(int(num_envs), int(T))
+    if b < 0:
+        raise ValueError(load_library().rlca_last_error().decode())
+    return b
+
+
+def _mat_workspace(workspace, N, T, device):
+    if workspace is None:
+        workspace = torch.empty(rlca_materialized_workspace_bytes(N, T) // 4, dtype=torch.float32,
+                                device=device)
+    return (workspace,) + _workspace(workspace, device)
+
+
+def rlca_returns_materialized(rewards, terminated=None, truncated=None, trunc_values=None,
+                              bootstrap=None, *, gamma, out=None, workspace=None, stream=None):
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    b, _ = _float_input("bootstrap", bootstrap, dt, (N,), dev)
+    out, o, ld_o = _output("returns", out, (N, T), dev)
+    ws_t, ws, ws_b = _mat_workspace(workspace, N, T, dev)
+    _check(load_library().rlca_returns_materialized(N, T, code, r, ld_r, te, ld_te, tr, ld_tr,
+                                                    tv, ld_tv, b, gamma, o, ld_o, ws, ws_b,
+                                                    _stream(stream, dev)))
+    return out
+
+
+def rlca_gae_materialized(rewards, values, terminated=None, truncated=None, trunc_values=None,
+                          *, gamma, lam, advantages=None, targets=None, with_targets=True,
+                          workspace=None, stream=None):
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    adv, a, ld_a = _output("advantages", advantages, (N, T), dev)
+    g, ld_g = None, 0
+    if with_targets or targets is not None:
+        targets, g, ld_g = _output("targets", targets, (N, T), dev)
+    ws_t, ws, ws_b = _mat_workspace(workspace, N, T, dev)
+    _check(load_library().rlca_gae_materialized(N, T, code, r, ld_r, v, ld_v, te, ld_te, tr,
+                                                ld_tr, tv, ld_tv, gamma, lam, a, ld_a, g, ld_g,
+                                                ws, ws_b, _stream(stream, dev)))
+    return adv, targets
+
+
+def rlca_td_lambda_materialized(rewards, values, terminated=None, truncated=None,
+                                trunc_values=None, *, gamma, lam, out=None, workspace=None,
+                                stream=None):
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    out, o, ld_o = _output("lambda_returns", out, (N, T), dev)
+    ws_t, ws, ws_b = _mat_workspace(workspace, N, T, dev)
+    _check(load_library().rlca_td_lambda_materialized(N, T, code, r, ld_r, v, ld_v, te, ld_te,
+                                                      tr, ld_tr, tv, ld_tv, gamma, lam, o, ld_o,
+                                                      ws, ws_b, _stream(stream, dev)))
+    return out
+
+
+def rlca_vtrace_materialized(rewards, values, log_rhos, terminated=None, truncated=None,
+                             trunc_values=None, *, gamma, lam=1.0, rho_bar=1.0, c_bar=1.0,
+                             pg_rho_bar=1.0, vs=None, pg_advantages=None, with_pg=True,
+                             workspace=None, stream=None):
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    v, ld_v = _float_input("values", values, dt, (N, T + 1), dev)
+    lr, ld_lr = _float_input("log_rhos", log_rhos, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    tv, ld_tv = _float_input("trunc_values", trunc_values, dt, (N, T), dev)
+    vs, o, ld_o = _output("vs", vs, (N, T), dev)
+    pg, ld_pg = None, 0
+    if with_pg or pg_advantages is not None:
+        pg_advantages, pg, ld_pg = _output("pg_advantages", pg_advantages, (N, T), dev)
+    ws_t, ws, ws_b = _mat_workspace(workspace, N, T, dev)
+    _check(load_library().rlca_vtrace_materialized(N, T, code, r, ld_r, v, ld_v, lr, ld_lr, te,
+                                                   ld_te, tr, ld_tr, tv, ld_tv, gamma, lam,
+                                                   rho_bar, c_bar, pg_rho_bar, o, ld_o, pg,
+                                                   ld_pg, ws, ws_b, _stream(stream, dev)))
+    return vs, pg_advantages
+
+
+def rlca_retrace_materialized(rewards, q_taken, exp_q_next, log_rhos, terminated=None,
+                              truncated=None, *, gamma, lam=1.0, c_bar=1.0, out=None,
+                              workspace=None, stream=None):
+    N, T, code, dev = _common(rewards)
+    dt = rewards.dtype
+    r, ld_r = _float_input("rewards", rewards, dt, (N, T), dev)
+    q, ld_q = _float_input("q_taken", q_taken, dt, (N, T), dev)
+    eq, ld_eq = _float_input("exp_q_next", exp_q_next, dt, (N, T), dev)
+    lr, ld_lr = _float_input("log_rhos", log_rhos, dt, (N, T), dev)
+    te, ld_te = _flag_input("terminated", terminated, (N, T), dev)
+    tr, ld_tr = _flag_input("truncated", truncated, (N, T), dev)
+    out, o, ld_o = _output("q_ret", out, (N, T), dev)
+    ws_t, ws, ws_b = _mat_workspace(workspace, N, T, dev)
+    _check(load_library().rlca_retrace_materialized(N, T, code, r, ld_r, q, ld_q, eq, ld_eq, lr,
+                                                    ld_lr, te, ld_te, tr, ld_tr, gamma, lam,
+                                                    c_bar, o, ld_o, ws, ws_b,
+                                                    _stream(stream, dev)))
     return out
 
 

@@ -21,9 +21,10 @@ LIB = os.path.join(PKG, "librlca.so")
 LIB_TIMED = os.path.join(PKG, "librlca_timed.so")
 # Host code and the kernel tables, compiled in parallel.
 SOURCES = [os.path.join(CSRC, n) for n in ("rlca.hip", "kernels_plain.hip", "kernels_window.hip",
-                                           "kernels_probs.hip")]
+                                           "kernels_probs.hip", "kernels_materialized.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, n) for n in ("scan_kernels.hpp", "kernel_table.hpp",
-                                                   "variants.hpp", "probs_kernels.hpp")] + [
+                                                   "variants.hpp", "probs_kernels.hpp",
+                                                   "materialized.hpp")] + [
     os.path.join(INCLUDE, "rlca.h")]
 ARCH = "gfx950"
 

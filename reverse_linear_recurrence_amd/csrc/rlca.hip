@@ -18,6 +18,7 @@
 #include <mutex>
 #include <string>
 
+#include "materialized.hpp"
 #include "probs_kernels.hpp"
 #include "rlca.h"
 #include "scan_kernels.hpp"
@@ -291,8 +292,45 @@ struct Window {
   float *cmap;
   void *ws = nullptr;
   int64_t ws_bytes = 0;
+  // The materialized doubling scan (materialized.hpp) in ws instead of the
+  // fused kernel.
+  bool materialized = false;
 };
 constexpr Window kNoWindow{false, nullptr, nullptr, nullptr};
+
+// The materialized doubling scan: its pairs (two pairs of [N, T] float
+// arrays) in the caller's workspace; 2 + ceil(log2 T) launches.
+int launch_materialized(int algo, int dtype, const Args &args, float *ws, void *stream) {
+  int64_t N = args.N, T = args.T;
+  const int64_t NT = N * T;
+  float *pa = ws, *pb = ws + NT, *qa = ws + 2 * NT, *qb = ws + 3 * NT;
+  const dim3 grid(static_cast<unsigned>((T + kMatBlock - 1) / kMatBlock),
+                  static_cast<unsigned>(N < kMatMaxGridRows ? N : kMatMaxGridRows));
+  const dim3 block(kMatBlock);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  Args a = args;
+  auto go = [&](const void *kernel, void **kargs) {
+    if (kernel == nullptr) return fail(RLCA_EINVAL, "no materialized kernel for algorithm %d", algo);
+    const hipError_t e = hipLaunchKernel(kernel, grid, block, kargs, 0, s);
+    if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return static_cast<int>(RLCA_OK);
+  };
+  void *k1[] = {&a, &pa, &pb};
+  RLCA_TRY(go(mat_coeffs_kernel(algo, dtype), k1));
+  for (int64_t off = 1; off < T; off *= 2) {
+    void *kd[] = {&pa, &pb, &qa, &qb, &N, &T, &off};
+    RLCA_TRY(go(mat_double_kernel(), kd));
+    float *ta = pa, *tb = pb;
+    pa = qa;
+    pb = qb;
+    qa = ta;
+    qb = tb;
+  }
+  void *k3[] = {&a, &pa, &pb};
+  RLCA_TRY(go(mat_epilogue_kernel(algo, dtype), k3));
+  t_last_variant = -1;
+  return RLCA_OK;
+}
 
 // Room a call's argument table keeps after its own arrays: the window's
 // three carry vectors and a split call's workspace.
@@ -427,6 +465,23 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
                   static_cast<long long>(w.ws_bytes));
     if (reinterpret_cast<uintptr_t>(w.ws) % 4 != 0)
       return fail(RLCA_EINVAL, "workspace is not 4-byte aligned");
+  }
+  if (w.materialized) {
+    if (w.ws == nullptr) return fail(RLCA_EINVAL, "the materialized scan needs a workspace");
+    if (N == 0) return RLCA_OK;
+    if (N > INT64_MAX / 16 / a.T)
+      return fail(RLCA_EINVAL, "%lld x %lld steps are too many for the materialized scan",
+                  static_cast<long long>(N), static_cast<long long>(a.T));
+    const int64_t nt = N * a.T;
+    if (w.ws_bytes < 16 * nt)
+      return fail(RLCA_EINVAL,
+                  "workspace_bytes = %lld is less than the %lld the materialized scan needs "
+                  "(rlca_materialized_workspace_bytes)",
+                  static_cast<long long>(w.ws_bytes), static_cast<long long>(16 * nt));
+    arrs[n++] = Arr{"workspace", w.ws, 4 * nt, 4 * nt, 4, false, true, true};
+    for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], N));
+    RLCA_TRY(check_aliasing(arrs, n));
+    return launch_materialized(algo, dtype, a, static_cast<float *>(w.ws), stream);
   }
   if (N == 0) return RLCA_OK;
   const int64_t S = split_count(N, a.T);
@@ -852,6 +907,10 @@ Window window_of(const float *cin, float *cout, float *cmap, void *ws, int64_t w
   return Window{true, cin, cout, cmap, ws, ws_bytes};
 }
 
+Window materialized_in(void *ws, int64_t ws_bytes) {
+  return Window{false, nullptr, nullptr, nullptr, ws, ws_bytes, true};
+}
+
 }  // namespace
 }  // namespace rlca
 
@@ -935,6 +994,90 @@ int rlca_episodic_cumsum(int64_t num_envs, int64_t T, int dtype, const void *x, 
   return forward_like(kCumsum, num_envs, T, dtype, x, ld_x, terminated, ld_terminated, truncated,
                       ld_truncated, s_init, 1.f, 1.f, sums, ld_sums, "s_init", "sums", kNoWindow,
                       stream);
+}
+
+// ------------------------------------------ materialized doubling scan
+
+int64_t rlca_materialized_workspace_bytes(int64_t num_envs, int64_t T) {
+  if (num_envs < 0 || T < 1) {
+    fail(RLCA_EINVAL, "num_envs must be >= 0 and T >= 1");
+    return -1;
+  }
+  if (num_envs > 0 && num_envs > INT64_MAX / 16 / T) {
+    fail(RLCA_EINVAL, "too many steps for the materialized scan");
+    return -1;
+  }
+  return 16 * num_envs * T;
+}
+
+int rlca_returns_materialized(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                              int64_t ld_rewards, const uint8_t *terminated,
+                              int64_t ld_terminated, const uint8_t *truncated,
+                              int64_t ld_truncated, const void *trunc_values,
+                              int64_t ld_trunc_values, const void *bootstrap, float gamma,
+                              float *returns, int64_t ld_returns, void *workspace,
+                              int64_t workspace_bytes, void *stream) {
+  return returns_impl(num_envs, T, dtype, rewards, ld_rewards, terminated, ld_terminated,
+                      truncated, ld_truncated, trunc_values, ld_trunc_values, bootstrap, gamma,
+                      returns, ld_returns, materialized_in(workspace, workspace_bytes), stream);
+}
+
+int rlca_gae_materialized(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                          int64_t ld_rewards, const void *values, int64_t ld_values,
+                          const uint8_t *terminated, int64_t ld_terminated,
+                          const uint8_t *truncated, int64_t ld_truncated,
+                          const void *trunc_values, int64_t ld_trunc_values, float gamma,
+                          float lam, float *advantages, int64_t ld_advantages, float *targets,
+                          int64_t ld_targets, void *workspace, int64_t workspace_bytes,
+                          void *stream) {
+  return gae_like(kGae, num_envs, T, dtype, rewards, ld_rewards, values, ld_values, terminated,
+                  ld_terminated, truncated, ld_truncated, trunc_values, ld_trunc_values, gamma,
+                  lam, advantages, ld_advantages, targets, ld_targets, "advantages", "targets",
+                  materialized_in(workspace, workspace_bytes), stream);
+}
+
+int rlca_td_lambda_materialized(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                                int64_t ld_rewards, const void *values, int64_t ld_values,
+                                const uint8_t *terminated, int64_t ld_terminated,
+                                const uint8_t *truncated, int64_t ld_truncated,
+                                const void *trunc_values, int64_t ld_trunc_values, float gamma,
+                                float lam, float *lambda_returns, int64_t ld_lambda_returns,
+                                void *workspace, int64_t workspace_bytes, void *stream) {
+  return gae_like(kTdLambda, num_envs, T, dtype, rewards, ld_rewards, values, ld_values,
+                  terminated, ld_terminated, truncated, ld_truncated, trunc_values,
+                  ld_trunc_values, gamma, lam, lambda_returns, ld_lambda_returns, nullptr, 0,
+                  "lambda_returns", "unused", materialized_in(workspace, workspace_bytes),
+                  stream);
+}
+
+int rlca_vtrace_materialized(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                             int64_t ld_rewards, const void *values, int64_t ld_values,
+                             const void *log_rhos, int64_t ld_log_rhos,
+                             const uint8_t *terminated, int64_t ld_terminated,
+                             const uint8_t *truncated, int64_t ld_truncated,
+                             const void *trunc_values, int64_t ld_trunc_values, float gamma,
+                             float lam, float rho_bar, float c_bar, float pg_rho_bar, float *vs,
+                             int64_t ld_vs, float *pg_advantages, int64_t ld_pg_advantages,
+                             void *workspace, int64_t workspace_bytes, void *stream) {
+  return vtrace_impl(num_envs, T, dtype, rewards, ld_rewards, values, ld_values, log_rhos,
+                     ld_log_rhos, terminated, ld_terminated, truncated, ld_truncated,
+                     trunc_values, ld_trunc_values, gamma, lam, rho_bar, c_bar, pg_rho_bar, vs,
+                     ld_vs, pg_advantages, ld_pg_advantages,
+                     materialized_in(workspace, workspace_bytes), stream);
+}
+
+int rlca_retrace_materialized(int64_t num_envs, int64_t T, int dtype, const void *rewards,
+                              int64_t ld_rewards, const void *q_taken, int64_t ld_q_taken,
+                              const void *exp_q_next, int64_t ld_exp_q_next,
+                              const void *log_rhos, int64_t ld_log_rhos,
+                              const uint8_t *terminated, int64_t ld_terminated,
+                              const uint8_t *truncated, int64_t ld_truncated, float gamma,
+                              float lam, float c_bar, float *q_ret, int64_t ld_q_ret,
+                              void *workspace, int64_t workspace_bytes, void *stream) {
+  return retrace_impl(num_envs, T, dtype, rewards, ld_rewards, q_taken, ld_q_taken, exp_q_next,
+                      ld_exp_q_next, log_rhos, ld_log_rhos, terminated, ld_terminated,
+                      truncated, ld_truncated, gamma, lam, c_bar, q_ret, ld_q_ret,
+                      materialized_in(workspace, workspace_bytes), stream);
 }
 
 // ------------------------------------------------------ window entry points

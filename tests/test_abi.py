@@ -21,6 +21,12 @@ from reverse_linear_recurrence_amd import _binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "rlca.h")
 
+# Every array here is a fake address: should a call pass validation where a
+# GPU is present, it would enqueue a kernel on them.  The module runs only
+# where none is (the library then fails any launch with RLCA_EHIP).
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="fake device addresses: run where no GPU is present")
+
 
 def declared_functions():
     text = open(HEADER).read()
@@ -158,10 +164,8 @@ def test_aliasing_is_rejected(lib):
 
 
 def test_adjacent_arrays_do_not_alias(lib):
-    # Passing validation enqueues a kernel on the fake addresses: only where
-    # no GPU is present, so that the launch itself fails.
-    if torch.cuda.is_available():
-        pytest.skip("a call that passes validation would launch on fake addresses")
+    # Passing validation enqueues a kernel on the fake addresses; with no GPU
+    # present (the module's condition) the launch itself fails.
     span = (4 - 1) * 8 + 8
     assert gae(lib, adv=R - span * 4) == rl.RLCA_EHIP  # adjacent, not overlapping
     assert "launch" in err(lib)
@@ -397,3 +401,38 @@ def test_split_window_call_validates_its_workspace(lib):
     # the carry vectors are validated when a workspace is given too
     assert gae_chunk(lib, N=N, T=T, cin=C_IN + 2, ws=WS, ws_bytes=need) == rl.RLCA_EINVAL
     assert "carry_in" in err(lib)
+
+
+def test_materialized_scan_validates_its_workspace(lib):
+    # The materialized doubling scan needs 16 bytes per step of workspace,
+    # checked (with the call's own arrays) before any launch.
+    N, T = 4, 8
+    need = rl.rlca_materialized_workspace_bytes(N, T)
+    assert need == 16 * N * T
+    assert rl.rlca_materialized_workspace_bytes(0, 5) == 0
+    with pytest.raises(ValueError):
+        rl.rlca_materialized_workspace_bytes(2, 0)
+    assert lib.rlca_materialized_workspace_bytes(2 ** 31 - 1, 2 ** 31 - 2) == -1
+
+    def g(ws, nb, **k):
+        return lib.rlca_gae_materialized(k.get("N", N), T, F32, R, T, V, T + 1, TE, T, TR, T, TV,
+                                         T, k.get("gamma", 0.9), 0.9, ADV, T, TGT, T, ws, nb,
+                                         None)
+    assert g(None, 0) == rl.RLCA_EINVAL and "needs a workspace" in err(lib)
+    assert g(WS, need - 4) == rl.RLCA_EINVAL and "rlca_materialized_workspace_bytes" in err(lib)
+    assert g(WS + 2, need) == rl.RLCA_EINVAL and "aligned" in err(lib)
+    assert g(WS, -1) == rl.RLCA_EINVAL
+    assert g(ADV + 16, need) == rl.RLCA_EALIAS and "workspace" in err(lib)
+    assert g(V + 8, need) == rl.RLCA_EALIAS and "values" in err(lib)
+    assert g(WS, need, gamma=2.0) == rl.RLCA_EINVAL and "gamma" in err(lib)
+    assert g(None, 0, N=0) == rl.RLCA_EINVAL  # the workspace is required, rows or not
+    assert g(WS, need, N=0) == rl.RLCA_OK
+    rt = lib.rlca_retrace_materialized(N, T, F32, R, T, V, T, TV, T, TE, T, None, T, None, T,
+                                       0.9, 0.9, 0.0, ADV, T, WS, need, None)
+    assert rt == rl.RLCA_EINVAL and "c_bar" in err(lib)
+    vt = lib.rlca_vtrace_materialized(N, T, F32, R, T, V, T + 1, TE, T, None, T, None, T, None,
+                                      T, 0.9, 0.9, 1.0, 1.0, 1.0, ADV, T, R, T, WS, need, None)
+    assert vt == rl.RLCA_EALIAS and "pg_advantages" in err(lib)
+    ret = lib.rlca_returns_materialized(N, T, F32, R, T, None, T, None, T, None, T,
+                                        WS + need - 4, 0.9, ADV, T, WS, need, None)
+    assert ret == rl.RLCA_EALIAS and "bootstrap" in err(lib)
