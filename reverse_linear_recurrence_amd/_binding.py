@@ -128,6 +128,8 @@ def load_library(path=None):
                                        " --timestamps" if path == TIMED_LIB_PATH else ""))
         lib = ctypes.CDLL(path)
         for name, argtypes in _SIGNATURES.items():
+            if path != _LIB_PATH and not hasattr(lib, name):
+                continue  # another build may predate an entry point
             fn = getattr(lib, name)
             fn.argtypes = argtypes
             fn.restype = {"rlca_last_error": ctypes.c_char_p,

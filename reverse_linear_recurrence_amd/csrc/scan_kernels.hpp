@@ -265,14 +265,22 @@ struct FlagWords {
   uint32_t sh;  // misalignment of p in bits
 };
 
-template <int K>
+// kAligned: p is known to be 4-byte aligned (every flag row of the call is),
+// so the span is exactly its K/4 dwords and no further dword is read.
+template <int K, bool kAligned = false>
 __device__ __forceinline__ void ld_flags_raw(const uint8_t *__restrict__ p, FlagWords<K> &f) {
   static_assert(K % 4 == 0, "K must be a multiple of 4");
-  const int mis = static_cast<int>(reinterpret_cast<uintptr_t>(p) & 3);
-  const uint32_t *base = reinterpret_cast<const uint32_t *>(p - mis);
-  ld_dwords<K / 4, true>(base, f.d);
-  f.extra = base[K / 4 - 1 + (mis != 0)];
-  f.sh = static_cast<uint32_t>(mis) * 8;
+  if constexpr (kAligned) {
+    ld_dwords<K / 4, true>(reinterpret_cast<const uint32_t *>(p), f.d);
+    f.extra = f.d[K / 4 - 1];
+    f.sh = 0;
+  } else {
+    const int mis = static_cast<int>(reinterpret_cast<uintptr_t>(p) & 3);
+    const uint32_t *base = reinterpret_cast<const uint32_t *>(p - mis);
+    ld_dwords<K / 4, true>(base, f.d);
+    f.extra = base[K / 4 - 1 + (mis != 0)];
+    f.sh = static_cast<uint32_t>(mis) * 8;
+  }
 }
 
 template <int K>
@@ -452,7 +460,7 @@ __device__ __forceinline__ float tv_at(const Tile<K> &x, int j) {
 
 // One read of the raw rollout for a lane of a whole tile (Method 2: on-chip
 // construction): unconditional vector loads, all issued before any use.
-template <int A, typename InT, int K>
+template <int A, typename InT, int K, bool kAligned = false>
 __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
                                            int64_t lim, Tile<K> &q) {
   using U = Uses<A>;
@@ -477,8 +485,8 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
   } else {
     trp = rp.has_tr ? rp.tr + f0 : own;
   }
-  ld_flags_raw<K>(trp, q.ftr);
-  ld_flags_raw<K>(rp.has_te ? rp.te + f0 : own, q.fte);
+  ld_flags_raw<K, kAligned>(trp, q.ftr);
+  ld_flags_raw<K, kAligned>(rp.has_te ? rp.te + f0 : own, q.fte);
   Ld<InT>::template vec<K>(rp.r + t0, q.r);
   if constexpr (U::values || U::q || U::affine) {
     float vk[K];
@@ -994,12 +1002,16 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 // row) only.  It holds one tile of loads and no tile loop, so it needs far
 // fewer VGPRs than the general instance (which sizes its registers for the
 // two-buffer loop), and more of its wavefronts fit on a SIMD at once.
+// kAligned (one-tile instances of the reverse recurrences only): every flag
+// row the kernel reads (and, for a missing flag array, its stand-in, the
+// rewards row) is 4-byte aligned, so a lane's flag span is read as exactly
+// its K/4 dwords.
 // Workgroup: 64 * short_row_waves(WPR, LPR, kChunk) threads.
 // h0..h4, N32, T32, ldT, ldX: the preloaded hot arguments (see above); they
 // duplicate fields of p.  kChunk: window instance (carry vector in, carry and
 // carry map out).
 template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk,
-          bool kOne = false>
+          bool kOne = false, bool kAligned = false>
 __global__ void __launch_bounds__(64 * short_row_waves(WPR, LPR, kChunk))
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
             int N32, int T32, int ldT, int ldX, const Args p) {
@@ -1124,7 +1136,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
   if (kOne || (ntiles == 1 && T == kTile)) {
     // One whole tile: straight-line code.
     Tile<K> x;
-    issue_tile<A, InT, K>(p, rp, lane_off, T - lane_off, x);
+    issue_tile<A, InT, K, kAligned>(p, rp, lane_off, T - lane_off, x);
     if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
     finish_tile<A, InT, K>(p, rp, lane_off, x);
     tile_compute<A, InT, K, LPR, WPR, false, kChunk>(p, rp, x, lane_off, T - lane_off, row_ok, 0,
