@@ -8,14 +8,14 @@
 
 namespace rlca {
 
-template <int A, typename InT, int V, bool U, bool C, bool O, bool AL>
+template <int A, typename InT, int V, bool U, bool C, int O, bool AL>
 const void *kernel_ptr() {
   constexpr Variant v = kVariants[V];
   constexpr int K = steps_per_lane(v, sizeof(InT) == 2, A == kVtrace);
   return reinterpret_cast<const void *>(&scan_kernel<A, InT, K, v.LPR, v.WPR, U, C, O, AL>);
 }
 
-template <int A, typename InT, bool U, bool C, bool O = false, bool AL = false>
+template <int A, typename InT, bool U, bool C, int O = 0, bool AL = false>
 const void *kernel_ptr(int v) {
   static_assert(kNumVariants == 9, "one case per variant");
   switch (v) {
@@ -31,30 +31,34 @@ const void *kernel_ptr(int v) {
   }
 }
 
-template <int A, typename InT, bool C>
-const void *one_tile_ptr(int v, bool aligned) {
+template <int A, typename InT, bool C, int O>
+const void *fixed_tiles_ptr(int v, bool aligned) {
   constexpr bool kHasAligned = !Uses<A>::prev_flags;  // forward mirrors read from t - 1
   if constexpr (kHasAligned) {
-    if (aligned) return kernel_ptr<A, InT, true, C, true, true>(v);
+    if (aligned) return kernel_ptr<A, InT, true, C, O, true>(v);
   }
-  return kernel_ptr<A, InT, true, C, true, false>(v);
+  return kernel_ptr<A, InT, true, C, O, false>(v);
 }
 
-// one: the one-tile instance (rows of exactly one whole tile), aligned: its
-// twin for 4-byte aligned flag rows (reverse recurrences); both exist for the
-// plain instances (C false) with a uniform row stride.
+// tiles: 1 or 2 for the instances of rows of exactly one or two whole tiles
+// (0: the general instance), aligned: their twins for 4-byte aligned flag
+// rows (reverse recurrences); they exist for the plain instances (C false)
+// with a uniform row stride.
 template <int A, bool C>
-const void *kernel_ptr(int dtype, int v, bool uniform, bool one = false, bool aligned = false) {
+const void *kernel_ptr(int dtype, int v, bool uniform, int tiles = 0, bool aligned = false) {
   if constexpr (!C) {
-    if (uniform && one) {
-      return dtype == RLCA_BF16 ? one_tile_ptr<A, bf16_t, C>(v, aligned)
-                                : one_tile_ptr<A, float, C>(v, aligned);
+    if (uniform && tiles == 1) {
+      return dtype == RLCA_BF16 ? fixed_tiles_ptr<A, bf16_t, C, 1>(v, aligned)
+                                : fixed_tiles_ptr<A, float, C, 1>(v, aligned);
+    }
+    if (uniform && tiles == 2) {
+      return dtype == RLCA_BF16 ? fixed_tiles_ptr<A, bf16_t, C, 2>(v, aligned)
+                                : fixed_tiles_ptr<A, float, C, 2>(v, aligned);
     }
   }
   if (dtype == RLCA_BF16)
-    return uniform ? kernel_ptr<A, bf16_t, true, C, false>(v)
-                   : kernel_ptr<A, bf16_t, false, C, false>(v);
-  return uniform ? kernel_ptr<A, float, true, C, false>(v) : kernel_ptr<A, float, false, C, false>(v);
+    return uniform ? kernel_ptr<A, bf16_t, true, C>(v) : kernel_ptr<A, bf16_t, false, C>(v);
+  return uniform ? kernel_ptr<A, float, true, C>(v) : kernel_ptr<A, float, false, C>(v);
 }
 
 }  // namespace rlca

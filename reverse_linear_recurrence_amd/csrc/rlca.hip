@@ -263,11 +263,13 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
   int ldT = static_cast<int>(a.ld_r);
   int ldX = static_cast<int>(ldx);
   void *kargs[] = {&hot[0], &hot[1], &hot[2], &hot[3], &hot[4], &N32, &T32, &ldT, &ldX, &a};
-  // Rows of exactly one whole tile take the one-tile instance (fewer
-  // registers, so more wavefronts per SIMD), and its aligned twin when every
-  // flag row the kernel reads is 4-byte aligned: the flag arrays' rows, or,
-  // standing in for a missing one, the rewards' rows.
-  const bool one = args.T == tile_steps(var, dtype == RLCA_BF16, algo == kVtrace);
+  // Rows of exactly one or two whole tiles take the instance for that many
+  // tiles (straight-line code: fewer registers, or no redundant prefetch),
+  // and its aligned twin when every flag row the kernel reads is 4-byte
+  // aligned: the flag arrays' rows, or, standing in for a missing one, the
+  // rewards' rows.
+  const int64_t tile = tile_steps(var, dtype == RLCA_BF16, algo == kVtrace);
+  const int tiles = args.T == tile ? 1 : (args.T == 2 * tile ? 2 : 0);
   auto rows_aligned = [&](const void *ptr, int64_t ld, int64_t esize) {
     return reinterpret_cast<uintptr_t>(ptr) % 4 == 0 && (args.N <= 1 || (ld * esize) % 4 == 0);
   };
@@ -277,7 +279,7 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
       (a.trunc == nullptr || rows_aligned(a.trunc, a.ld_trunc, 1)) &&
       ((a.term != nullptr && a.trunc != nullptr) || rows_aligned(a.r, a.ld_r, es));
   const void *kernel = window ? window_kernel(algo, dtype, v, uniform)
-                              : plain_kernel(algo, dtype, v, uniform, one, flags_aligned);
+                              : plain_kernel(algo, dtype, v, uniform, tiles, flags_aligned);
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no kernel for algorithm %d", algo);
   const hipError_t e = hipLaunchKernel(kernel, grid, block, kargs, 0,
                                        static_cast<hipStream_t>(stream));

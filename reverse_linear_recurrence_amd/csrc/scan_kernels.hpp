@@ -262,7 +262,7 @@ template <int K>
 struct FlagWords {
   uint32_t d[K / 4];
   uint32_t extra;
-  uint32_t sh;  // misalignment of p in bits
+  uint32_t sh;  // misalignment of p in bytes (0-3)
 };
 
 // kAligned: p is known to be 4-byte aligned (every flag row of the call is),
@@ -279,17 +279,21 @@ __device__ __forceinline__ void ld_flags_raw(const uint8_t *__restrict__ p, Flag
     const uint32_t *base = reinterpret_cast<const uint32_t *>(p - mis);
     ld_dwords<K / 4, true>(base, f.d);
     f.extra = base[K / 4 - 1 + (mis != 0)];
-    f.sh = static_cast<uint32_t>(mis) * 8;
+    f.sh = static_cast<uint32_t>(mis);
   }
 }
 
+// Each output dword is the byte pair {hi : lo} moved down by the misalignment,
+// one v_alignbyte_b32.  (A 64-bit shift, v_lshrrev_b64, does the same, but
+// with its shift amount in the last VGPR of a kernel's allocation it has
+// decoded the flags of some wavefronts of 512-thread workgroups unshifted,
+// now and then; the byte align takes no such operand pair.)
 template <int K>
 __device__ __forceinline__ void decode_flags(const FlagWords<K> &f, uint32_t (&w)[K / 4]) {
 #pragma unroll
   for (int i = 0; i < K / 4; ++i) {
     const uint32_t hi = i + 1 < K / 4 ? f.d[i + 1] : f.extra;
-    const uint64_t pair = (static_cast<uint64_t>(hi) << 32) | f.d[i];
-    w[i] = static_cast<uint32_t>(pair >> f.sh);
+    w[i] = __builtin_amdgcn_alignbyte(hi, f.d[i], f.sh);
   }
 }
 
@@ -460,7 +464,11 @@ __device__ __forceinline__ float tv_at(const Tile<K> &x, int j) {
 
 // One read of the raw rollout for a lane of a whole tile (Method 2: on-chip
 // construction): unconditional vector loads, all issued before any use.
-template <int A, typename InT, int K, bool kAligned = false>
+// kVkNeighbour (one-tile instances only, where a lane's span is its row's
+// last exactly when lim <= K): only a wavefront's first lane and a row's
+// last span load V_{t0+K}; the others take it from their neighbour
+// (vk_from_neighbour).
+template <int A, typename InT, int K, bool kAligned = false, bool kVkNeighbour = false>
 __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
                                            int64_t lim, Tile<K> &q) {
   using U = Uses<A>;
@@ -486,8 +494,8 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
     trp = rp.has_tr ? rp.tr + f0 : own;
   }
   if constexpr (kAligned && A == kGae) {
-    // GAE's aligned one-tile instances: a missing flag array's stand-in load
-    // is skipped behind a uniform branch (GAE 4096x128 with the V_{t0+K} form
+    // GAE's aligned instances: a missing flag array's stand-in load is
+    // skipped behind a uniform branch (GAE 4096x128 with the V_{t0+K} form
     // below: 3.42 -> 3.32 us per launch; TD(lambda) 16384x256 with the same
     // two changes: 10.07 -> 10.34 us, so the other algorithms keep the
     // unconditional form).
@@ -511,7 +519,7 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
     Ld<InT>::template vec<K>(rp.v + t0, vk);
 #pragma unroll
     for (int j = 0; j < K; ++j) q.v[j] = vk[j];
-    if constexpr (kAligned && A == kGae) {
+    if constexpr (kVkNeighbour && U::values) {
       // V_{t0+K} is the next span's first value, which the lane before in the
       // wavefront holds (vk_from_neighbour); only a wavefront's first lane
       // and a row's last span load it.
@@ -551,8 +559,8 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// V_{t0+K} of a lane that did not load it (issue_tile, GAE's aligned one-tile
-// instances): the first value of the lane before it in the wavefront, whose
+// V_{t0+K} of a lane that did not load it (issue_tile with kVkNeighbour): the
+// first value of the lane before it in the wavefront, whose
 // span is the next one in time (reverse lane order).  A wavefront's first
 // lane and a row's last span (end_span) loaded their own.
 template <int K>
@@ -1033,20 +1041,25 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 
 // Algo A, input type InT, K steps per lane, LPR lanes per row inside one
 // wavefront (WPR == 1), or WPR wavefronts per row (then LPR must be 64).
-// kOne: an instance for rows of exactly one whole tile (T == K * lanes per
-// row) only.  It holds one tile of loads and no tile loop, so it needs far
-// fewer VGPRs than the general instance (which sizes its registers for the
-// two-buffer loop), and more of its wavefronts fit on a SIMD at once.
-// kAligned (one-tile instances of the reverse recurrences only): every flag
-// row the kernel reads (and, for a missing flag array, its stand-in, the
-// rewards row) is 4-byte aligned, so a lane's flag span is read as exactly
-// its K/4 dwords.
+// kTiles: 0 for the general instance (any T); 1 or 2 for instances that
+// take rows of exactly one or exactly two whole tiles (T == kTiles * K *
+// lanes per row) only, as straight-line code.  The one-tile instance holds
+// one tile of loads and no tile loop, so it needs far fewer VGPRs than the
+// general instance (which sizes its registers for the two-buffer loop), and
+// more of its wavefronts fit on a SIMD at once.  The two-tile instance
+// issues both tiles' loads up front and no more: the general loop's
+// unconditional prefetch would re-read a third tile, half again the loads
+// of such a row (GAE bf16 256x16384: 13.1 -> 11.5 us without it).
+// kAligned (fixed-tile instances of the reverse recurrences only): every
+// flag row the kernel reads (and, for a missing flag array, its stand-in,
+// the rewards row) is 4-byte aligned, so a lane's flag span is read as
+// exactly its K/4 dwords.
 // Workgroup: 64 * short_row_waves(WPR, LPR, kChunk) threads.
 // h0..h4, N32, T32, ldT, ldX: the preloaded hot arguments (see above); they
 // duplicate fields of p.  kChunk: window instance (carry vector in, carry and
 // carry map out).
 template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk,
-          bool kOne = false, bool kAligned = false>
+          int kTiles = 0, bool kAligned = false>
 __global__ void __launch_bounds__(64 * short_row_waves(WPR, LPR, kChunk))
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
             int N32, int T32, int ldT, int ldX, const Args p) {
@@ -1168,108 +1181,138 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
       static_cast<int64_t>(Uses<A>::forward ? g : kGroup - 1 - g) * K;
   [[maybe_unused]] auto t0_of = [&](int64_t c) { return c * kTile + lane_off; };
 
-  if (kOne || (ntiles == 1 && T == kTile)) {
-    // One whole tile: straight-line code.
+  // One whole tile: straight-line code.
+  auto one_tile = [&]() {
+    // GAE's aligned one-tile instances take V_{t0+K} from the neighbouring
+    // lane (with the flag loads of issue_tile: GAE 4096x128 3.42 -> 3.32 us;
+    // TD(lambda) 16384x256 measured slower with the same two changes).
+    constexpr bool kVk = kTiles == 1 && kAligned && A == kGae;
     Tile<K> x;
-    issue_tile<A, InT, K, kAligned>(p, rp, lane_off, T - lane_off, x);
+    issue_tile<A, InT, K, kAligned, kVk>(p, rp, lane_off, T - lane_off, x);
     if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
     finish_tile<A, InT, K>(p, rp, lane_off, x);
-    if constexpr (kAligned && A == kGae) vk_from_neighbour(x, T - lane_off <= K);
+    if constexpr (kVk) vk_from_neighbour(x, T - lane_off <= K);
     tile_compute<A, InT, K, LPR, WPR, false, kChunk>(p, rp, x, lane_off, T - lane_off, row_ok, 0,
                                                      false, lane, wave, carry, s_agg, m, win,
                                                      write_window);
-    return;
-  }
-  if constexpr (!kOne) {
-    const bool ragged = T % kTile != 0;
-    if constexpr (Uses<A>::forward) {
-      // Tiles from the first to the last; the ragged one comes last.  Same
-      // two-buffer pipeline as below, in increasing c.
-      const int64_t nwhole = ragged ? ntiles - 1 : ntiles;
-      Tile<K> buf_a, buf_b;
-      int64_t c = 0;
-      if (nwhole > 0) {
-        issue_tile<A, InT, K>(p, rp, t0_of(0), T - t0_of(0), buf_a);
-        if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
-        for (;;) {
-          {
-            finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
-            const int64_t cn = c + 1 < nwhole ? c + 1 : c;
-            issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
-            carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
-                p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
-                s_agg, m, win, write_window);
+  };
+  if constexpr (kTiles == 1) {
+    one_tile();
+  } else if constexpr (kTiles == 2) {
+    // Two whole tiles, both tiles' loads in flight: the tile computed first
+    // (the later one in time for reverse recurrences, the earlier one for
+    // forward ones) hands its carry to the other.
+    constexpr int64_t kFirst = Uses<A>::forward ? 0 : 1;
+    constexpr int64_t kSecond = 1 - kFirst;
+    Tile<K> xf, xs;
+    issue_tile<A, InT, K, kAligned>(p, rp, t0_of(kFirst), T - t0_of(kFirst), xf);
+    if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+    finish_tile<A, InT, K>(p, rp, t0_of(kFirst), xf);
+    issue_tile<A, InT, K, kAligned>(p, rp, t0_of(kSecond), T - t0_of(kSecond), xs);
+    carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+        p, rp, xf, t0_of(kFirst), T - t0_of(kFirst), row_ok, kFirst, true, lane, wave, carry,
+        s_agg, m, win, write_window);
+    finish_tile<A, InT, K>(p, rp, t0_of(kSecond), xs);
+    tile_compute<A, InT, K, LPR, WPR, false, kChunk>(p, rp, xs, t0_of(kSecond),
+                                                     T - t0_of(kSecond), row_ok, kSecond, false,
+                                                     lane, wave, carry, s_agg, m, win,
+                                                     write_window);
+  } else {
+    if (ntiles == 1 && T == kTile) {
+      one_tile();
+      return;
+    }
+    {
+      const bool ragged = T % kTile != 0;
+      if constexpr (Uses<A>::forward) {
+        // Tiles from the first to the last; the ragged one comes last.  Same
+        // two-buffer pipeline as below, in increasing c.
+        const int64_t nwhole = ragged ? ntiles - 1 : ntiles;
+        Tile<K> buf_a, buf_b;
+        int64_t c = 0;
+        if (nwhole > 0) {
+          issue_tile<A, InT, K>(p, rp, t0_of(0), T - t0_of(0), buf_a);
+          if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+          for (;;) {
+            {
+              finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
+              const int64_t cn = c + 1 < nwhole ? c + 1 : c;
+              issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
+              carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+                  p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
+                  s_agg, m, win, write_window);
+            }
+            if (++c == nwhole) break;
+            {
+              finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
+              const int64_t cn = c + 1 < nwhole ? c + 1 : c;
+              issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
+              carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+                  p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
+                  s_agg, m, win, write_window);
+            }
+            if (++c == nwhole) break;
           }
-          if (++c == nwhole) break;
-          {
-            finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
-            const int64_t cn = c + 1 < nwhole ? c + 1 : c;
-            issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
-            carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
-                p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
-                s_agg, m, win, write_window);
-          }
-          if (++c == nwhole) break;
         }
+        if (ragged) {
+          const int64_t te0 = t0_of(ntiles - 1);
+          const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
+          Tile<K> x;
+          load_edge<A, InT, K>(p, rp, te0, lim, T, x);
+          if constexpr (kChunk) {
+            if (nwhole == 0) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+          }
+          tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok, ntiles - 1,
+                                                          false, lane, wave, carry, s_agg, m, win,
+                                                          write_window);
+        }
+        return;
       }
+      int64_t c = ragged ? ntiles - 2 : ntiles - 1;  // latest whole tile
+      // Two explicit buffers, alternating: tile c is decoded (and its sparse
+      // bootstrap loads issued) before tile c-1's loads are issued into the other
+      // buffer, then tile c is computed.  In-order load completion then lets the
+      // computation of tile c wait for tile c only, and no register copies are
+      // needed between iterations.  The prefetch is unconditional (no branch for
+      // the wait-count analysis to merge): after tile 0 it re-reads tile 0, which
+      // was just loaded (cache hits, never used).
+      Tile<K> buf_a, buf_b;
+      if (c >= 0) issue_tile<A, InT, K>(p, rp, t0_of(c), T - t0_of(c), buf_a);
       if (ragged) {
         const int64_t te0 = t0_of(ntiles - 1);
         const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
         Tile<K> x;
         load_edge<A, InT, K>(p, rp, te0, lim, T, x);
-        if constexpr (kChunk) {
-          if (nwhole == 0) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+        if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+        carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok,
+                                                                ntiles - 1, c >= 0, lane, wave, carry,
+                                                                s_agg, m, win, write_window);
+      } else {
+        if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+      }
+      if (c < 0) return;
+      for (;;) {
+        {
+          finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
+          const int64_t cn = c > 0 ? c - 1 : 0;
+          issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
+          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+              p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
+              win, write_window);
         }
-        tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok, ntiles - 1,
-                                                        false, lane, wave, carry, s_agg, m, win,
-                                                        write_window);
+        if (c == 0) break;
+        --c;
+        {
+          finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
+          const int64_t cn = c > 0 ? c - 1 : 0;
+          issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
+          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+              p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
+              win, write_window);
+        }
+        if (c == 0) break;
+        --c;
       }
-      return;
-    }
-    int64_t c = ragged ? ntiles - 2 : ntiles - 1;  // latest whole tile
-    // Two explicit buffers, alternating: tile c is decoded (and its sparse
-    // bootstrap loads issued) before tile c-1's loads are issued into the other
-    // buffer, then tile c is computed.  In-order load completion then lets the
-    // computation of tile c wait for tile c only, and no register copies are
-    // needed between iterations.  The prefetch is unconditional (no branch for
-    // the wait-count analysis to merge): after tile 0 it re-reads tile 0, which
-    // was just loaded (cache hits, never used).
-    Tile<K> buf_a, buf_b;
-    if (c >= 0) issue_tile<A, InT, K>(p, rp, t0_of(c), T - t0_of(c), buf_a);
-    if (ragged) {
-      const int64_t te0 = t0_of(ntiles - 1);
-      const int64_t lim = row_ok ? (T - te0 > 0 ? T - te0 : 0) : 0;
-      Tile<K> x;
-      load_edge<A, InT, K>(p, rp, te0, lim, T, x);
-      if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
-      carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok,
-                                                              ntiles - 1, c >= 0, lane, wave, carry,
-                                                              s_agg, m, win, write_window);
-    } else {
-      if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
-    }
-    if (c < 0) return;
-    for (;;) {
-      {
-        finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
-        const int64_t cn = c > 0 ? c - 1 : 0;
-        issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
-        carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
-            p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
-            win, write_window);
-      }
-      if (c == 0) break;
-      --c;
-      {
-        finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
-        const int64_t cn = c > 0 ? c - 1 : 0;
-        issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
-        carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
-            p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
-            win, write_window);
-      }
-      if (c == 0) break;
-      --c;
     }
   }
 }

@@ -58,11 +58,11 @@ inline int64_t tile_steps(const Variant &v, bool bf16, bool vtrace) {
 // Host-side address of the kernel instance for an algorithm (Algo), input
 // dtype (rlca_dtype), variant index and stride mode.  plain_kernel: the
 // windowed entry points without carries (every Algo but the generic scan),
-// one: the one-tile instance for rows of exactly one whole tile (uniform
-// strides only; otherwise the general instance), aligned: with every flag
-// row 4-byte aligned (reverse recurrences); window_kernel: carry vector in,
-// carry and carry map out (every Algo).
-const void *plain_kernel(int algo, int dtype, int variant, bool uniform, bool one, bool aligned);
+// tiles: 1 or 2 for the instance of rows of exactly that many whole tiles
+// (uniform strides only; otherwise, and for 0, the general instance),
+// aligned: with every flag row 4-byte aligned (reverse recurrences);
+// window_kernel: carry vector in, carry and carry map out (every Algo).
+const void *plain_kernel(int algo, int dtype, int variant, bool uniform, int tiles, bool aligned);
 const void *window_kernel(int algo, int dtype, int variant, bool uniform);
 // The policy-table kernels (Retrace, V-trace), 256-thread workgroups: 4
 // wavefronts per row (1024-step tiles, one row per workgroup) or 1 (256-step

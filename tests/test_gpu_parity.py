@@ -56,9 +56,24 @@ def variant_lengths(v, dtype="f32", algo="gae"):
                                        algo)
     tile = k * lanes
     # every residue of T mod 4 (the lane holding a row's end has 1..3 steps),
-    # rows shorter than one lane's span, one tile, and several tiles
+    # rows shorter than one lane's span, exactly one, two and three whole
+    # tiles (the one-tile and two-tile instances, and the tile loop), and
+    # ragged rows of several tiles
     return sorted({1, 2, 3, 5, 6, 7, tile // 2 + 3, tile - 4, tile - 2, tile - 1, tile,
-                   tile + 1, tile + 4, 2 * tile + 12, 2 * tile + 14})
+                   tile + 1, tile + 4, 2 * tile, 2 * tile + 12, 2 * tile + 14, 3 * tile})
+
+
+def misaligned_flags(dev):
+    """The same inputs with every flag array moved one byte off 4-byte
+    alignment (the fixed-tile instances' unaligned form)."""
+    out = dict(dev)
+    for k in ("terminated", "truncated"):
+        f = dev.get(k)
+        if f is not None:
+            buf = torch.zeros(f.numel() + 1, dtype=f.dtype, device=f.device)
+            out[k] = buf[1:].view(f.shape)
+            out[k].copy_(f)
+    return out
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -77,6 +92,47 @@ def test_every_variant_ragged_lengths(algo, dtype):
             assert rl.rlca_last_variant() == v
             ref = run_oracle(algo, host, p)
             assert_close(got, ref, TOL[dtype], "%s/%s/v%d/T%d" % (algo, dtype, v, T))
+            k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16"
+                                               else torch.float32, algo)
+            if T in (k * lanes, 2 * k * lanes):  # fixed-tile instances, unaligned flags
+                got = run_gpu(algo, misaligned_flags(dev), p)
+                assert_close(got, ref, TOL[dtype], "%s/%s/v%d/T%d/misaligned flags"
+                             % (algo, dtype, v, T))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_flags_read_by_every_wavefront(dtype):
+    """Regression: in 512-thread workgroups some wavefronts once decoded their
+    flag bytes unaligned, now and then (a reset landed 3 steps late).  Unit
+    rewards, one terminal flag per row placed in turn in every wavefront's
+    span, initial sums present: the episodic sum is then an exact integer
+    (steps since the episode began, plus the initial sum before the first
+    reset), checked bit for bit over repeated calls."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    N = 8
+    for v in range(3, rl.rlca_num_variants()):
+        k, lanes, _ = rl.rlca_variant_info(v, tdt, "cumsum")
+        tile = k * lanes
+        for T in (tile, 2 * tile, 3 * tile):
+            step = max(1, T // 24)
+            for rep in range(2):
+                fpos = [(rep * 7 + 13 * n + step * (n + 3 * rep)) % (T - 1) for n in range(N)]
+                flags = np.zeros((N, T), np.uint8)
+                flags[np.arange(N), fpos] = 1
+                s0 = np.arange(3, 3 + N, dtype=np.float64)
+                t = np.arange(T)[None, :]
+                f = np.array(fpos)[:, None]
+                want = np.where(t <= f, s0[:, None] + t + 1, t - f)
+                rl.rlca_set_variant(v)
+                got = rl.rlca_episodic_cumsum(
+                    torch.ones(N, T, dtype=tdt, device="cuda"),
+                    torch.from_numpy(flags).cuda(), None,
+                    torch.from_numpy(s0).to(tdt).cuda())
+                torch.cuda.synchronize()
+                got = got.double().cpu().numpy()
+                bad = np.nonzero(got != want)
+                assert bad[0].size == 0, "%s v%d T%d rep %d: row %d step %d (flag at %d)" % (
+                    dtype, v, T, rep, bad[0][0], bad[1][0], fpos[bad[0][0]])
 
 
 def boundary_rows(T):

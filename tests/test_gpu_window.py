@@ -134,7 +134,7 @@ def variant_lengths(v, dtype, algo):
     k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16" else torch.float32,
                                        algo)
     tile = k * lanes
-    return sorted({1, 3, 6, tile - 3, tile - 2, tile, 2 * tile + 5, 2 * tile + 7})
+    return sorted({1, 3, 6, tile - 3, tile - 2, tile, 2 * tile, 2 * tile + 5, 2 * tile + 7})
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
