@@ -41,10 +41,14 @@ KERNEL_SOURCES = {
              "kernels_window.hip", "rlca.hip"),
     "probs": ("scan_kernels.hpp", "probs_kernels.hpp", "variants.hpp", "kernels_probs.hip",
               "rlca.hip"),
+    "materialized": ("scan_kernels.hpp", "materialized.hpp", "kernels_materialized.hip",
+                     "rlca.hip"),
 }
 
 
 def kernel_family(workload_key):
+    if workload_key.endswith("/materialized"):
+        return "materialized"
     return "probs" if "_probs_" in workload_key else "scan"
 
 
@@ -103,6 +107,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of this "
                          "script into profiles/traffic.json, then exit")
+    ap.add_argument("--summarize-profile", nargs=2, metavar=("RUN_DIR", "OUT_MD"),
+                    help="write the profile summary of one workload (see summarize_profile), "
+                         "then exit")
     return ap.parse_args()
 
 
@@ -204,6 +211,183 @@ def summarize_pmc(fetch_dir, write_dir):
     print(json.dumps(out[meta["workload"]], indent=1))
 
 
+# The commands of one workload's profile, run from the repository root; {opts}
+# stands for the bench options of the workload, {d} for the run directory.
+PROFILE_COMMANDS = (
+    ("bench", "python3 bench.py {opts} > {d}/bench.json"),
+    ("trace", "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
+              "--output-format csv -d {d}/trace -o t -- python3 <repo>/bench.py {opts} "
+              "--steps 500 --warmup 50 --cpu-seconds 0 --body-blocks 0 --spread-replays 0"),
+    ("fetch", "cd /tmp && export TMPDIR=/tmp && RLCA_BENCH_META_DIR={d}/fetch rocprofv3 --pmc "
+              "FETCH_SIZE --output-format csv -d {d}/fetch -o p -- python3 <repo>/bench.py "
+              "{opts} --steps 20 --warmup 2 --cpu-seconds 0 --no-graph --rotate-mb 64 "
+              "--body-blocks 0 --spread-replays 0"),
+    ("write", "(the same with WRITE_SIZE into {d}/write)"),
+    ("busy", "(the same with SQ_BUSY_CYCLES SQ_WAVES into {d}/busy)"),
+    ("summary", "python3 bench.py --summarize-profile {d} profiles/<this file>"),
+)
+SE_COUNT = 32          # shader engines: 4 per XCD, 8 XCDs
+SCLK_GHZ = 2.4         # MI355X peak engine clock
+
+
+def summarize_profile(run_dir, out_md):
+    """One workload's profile summary (markdown) from a run directory holding
+    args.txt (the bench options), bench.json (the unprofiled bench line),
+    trace/ (rocprofv3 --kernel-trace), fetch/ and write/ (--pmc FETCH_SIZE,
+    WRITE_SIZE; also written to profiles/traffic.json) and busy/ (--pmc
+    SQ_BUSY_CYCLES SQ_WAVES)."""
+    import csv
+    import glob
+    import statistics
+
+    opts = open(os.path.join(run_dir, "args.txt")).read().split()
+    b = json.load(open(os.path.join(run_dir, "bench.json")))
+    traffic = None
+    if os.path.isdir(os.path.join(run_dir, "fetch")):
+        summarize_pmc(os.path.join(run_dir, "fetch"), os.path.join(run_dir, "write"))
+        key = b["config"]["workload"] + {
+            "window (carry in; carry and carry map out)": "/window"}.get(
+                b["config"]["entry"], "/materialized" if b["config"]["entry"].startswith(
+                    "material") else "")
+        traffic = json.load(open(TRAFFIC_FILE))[key]
+
+    def rows_of(d, name):
+        out = []
+        import gzip
+        for f in glob.glob(os.path.join(run_dir, d, "**", name), recursive=True) + glob.glob(
+                os.path.join(run_dir, d, "**", name + ".gz"), recursive=True):
+            out += list(csv.DictReader(gzip.open(f, "rt") if f.endswith(".gz") else open(f)))
+        return out
+
+    def q(v, f):
+        v = sorted(v)
+        return v[min(len(v) - 1, int(f * len(v)))]
+
+    def short(name):
+        name = re.sub(r"\(void const\*.*$", "", name)
+        return name if len(name) < 90 else name[:87] + "..."
+
+    trace = rows_of("trace", "*kernel_trace.csv")
+    groups = {}
+    for r in trace:
+        n = r["Kernel_Name"]
+        if "rlca::" in n:
+            k = short(n)
+        elif "copyBuffer" in n:
+            k = "copy (`__amd_rocclr_copyBuffer`, grid %s)" % r["Grid_Size_X"]
+        elif "spin_kernel" in n:
+            k = "empty kernel (`torch.cuda._sleep`)"
+        else:
+            continue
+        groups.setdefault(k, []).append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    # the calibration copy: the copy grid with the most dispatches
+    copies = sorted((k for k in groups if k.startswith("copy")), key=lambda k: -len(groups[k]))
+    for k in copies[1:]:
+        del groups[k]
+    busy = {}
+    for r in rows_of("busy", "*counter_collection.csv"):
+        if "rlca::" in r["Kernel_Name"]:
+            busy.setdefault((short(r["Kernel_Name"]), r["Counter_Name"]), []).append(
+                float(r["Counter_Value"]))
+
+    rf, kb, fl, cp, sp = (b["roofline"], b.get("kernel_body"), b.get("launch_floor"),
+                          b.get("copy_ceiling"), b.get("step_us_spread"))
+    L = b["config"]["launches_per_step"]
+    d = "<run>"
+    o = " ".join(opts)
+    lines = ["# librlca, workload `%s`%s" % (b["config"]["workload"], {
+                 "plain": ""}.get(b["config"]["entry"], " (%s)" % b["config"]["entry"])), "",
+             "MI355X, one GPU: %d x %d %s inputs, %d launch%s per step." % (
+                            b["config"]["num_envs"], b["config"]["T"],
+                            b["config"]["input_dtype"], L, "" if L == 1 else "es"), "",
+             "Commands (repository root on the GPU box; `<run>` is a scratch directory):", "",
+             "```"]
+    for _, c in PROFILE_COMMANDS:
+        lines.append(c.format(opts=o, d=d))
+    lines += ["```", "",
+              "## Per-launch time, unprofiled (the bench line)", "",
+              "| quantity | median | p10 | p90 |", "|---|---|---|---|"]
+    if sp:
+        per = 1e0 / L
+        lines.append("| library, back to back: µs per launch over %d blocks of %d steps (%s) "
+                     "| %.3f | %.3f | %.3f |" % (sp["blocks"], sp["steps_per_block"],
+                                                 b["config"]["timing"], sp["median"] * per,
+                                                 sp["p10"] * per, sp["p90"] * per))
+    if kb:
+        lines.append("| kernel body, µs: first wavefront's start to the last wavefront's "
+                     "completed stores (instrumented build, %d samples, %d wavefronts) "
+                     "| %.3f | %.3f | %.3f |" % (kb["samples"], kb["wavefronts"],
+                                                 kb["median_us"], kb["p10_us"], kb["p90_us"]))
+    lines += ["", "| quantity | value |", "|---|---|",
+              "| timed region: µs per step (K = %d) | %.3f |" % (b["steps"],
+                                                                  b["ms_per_step"] * 1e3),
+              "| µs per launch | %.3f |" % rf["avg_launch_us"],
+              "| algorithmic bytes per launch | %d |" % rf["algorithmic_bytes_per_launch"],
+              "| achieved (algorithmic bytes / µs per launch) | %.0f GB/s, %.1f%% of 8 TB/s |"
+              % (rf["achieved"], 100 * rf["frac"])]
+    if rf.get("kernel_only_frac"):
+        lines.append("| kernel-only (algorithmic bytes / kernel body) | %.0f GB/s, %.1f%% |"
+                     % (rf["kernel_only_frac"] * HBM_PEAK_GBPS, 100 * rf["kernel_only_frac"]))
+    if fl:
+        lines.append("| launch floor: an almost empty kernel, µs per launch | %.3f |"
+                     % fl["avg_launch_us"])
+    if cp:
+        lines.append("| copy ceiling: torch copy of %d bytes (half read, half written), µs per "
+                     "launch | %.3f (%.0f GB/s) |" % (cp["bytes_per_launch"], cp["avg_launch_us"],
+                                                      cp["GBps"]))
+    lines += ["", "## rocprofv3 kernel trace (durations of single dispatches, ns)", "",
+              "The tracer takes each dispatch alone (start to start about 20 µs apart in "
+              "these runs), so a duration here is one launch's latency from the command "
+              "processor's start of the dispatch to its end-of-kernel signal, with no "
+              "overlap with the launches before and after it: for a short kernel it is "
+              "longer than its share of a back-to-back stream.", "",
+              "| kernel | dispatches | median | p10 | p90 |", "|---|---|---|---|---|"]
+    for k, v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
+        lines.append("| %s | %d | %d | %d | %d |" % (k, len(v), q(v, 0.5), q(v, 0.1), q(v, 0.9)))
+    if busy:
+        lines += ["", "## Shader-engine busy time (rocprofv3 --pmc SQ_BUSY_CYCLES SQ_WAVES)", "",
+                  "SQ_BUSY_CYCLES counts, per shader engine, the cycles in which any "
+                  "wavefront of the dispatch is resident; the sum over the %d engines / %d "
+                  "is the mean engine's busy time, at the %.1f GHz peak clock a lower bound "
+                  "of the kernel's time with waves on the GPU." % (SE_COUNT, SE_COUNT,
+                                                                   SCLK_GHZ), "",
+                  "| kernel | wavefronts | busy cycles per engine | µs at %.1f GHz |" % SCLK_GHZ,
+                  "|---|---|---|---|"]
+        for (k, c), v in sorted(busy.items()):
+            if c != "SQ_BUSY_CYCLES":
+                continue
+            waves = statistics.median(busy.get((k, "SQ_WAVES"), [0]))
+            per_se = statistics.median(v) / SE_COUNT
+            lines.append("| %s | %d | %.0f | %.3f |" % (k, waves, per_se,
+                                                         per_se / SCLK_GHZ / 1e3))
+    if traffic is None:
+        with open(out_md, "w") as f:
+            f.write("\n".join(lines + ["", "(No counter runs for this workload.)", ""]))
+        print("wrote", out_md)
+        return
+    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then WRITE_SIZE)", "",
+              "| quantity | value |", "|---|---|"]
+    for k, v in traffic["fetch_kib_per_launch"].items():
+        lines.append("| FETCH_SIZE per dispatch (KiB), %s | %.1f |" % (short(k), v))
+    for k, v in traffic["write_kib_per_launch"].items():
+        lines.append("| WRITE_SIZE per dispatch (KiB), %s | %.1f |" % (short(k), v))
+    lines += ["| calibration copy bytes read / written | %d / %d |"
+              % (traffic["copy_bytes_read"], traffic["copy_bytes_written"]),
+              "| its FETCH_SIZE / WRITE_SIZE (KiB) | %.1f / %.1f |"
+              % (traffic["copy_fetch_kib"], traffic["copy_write_kib"]),
+              "| scale: FETCH / WRITE | %.3f / %.3f |" % (traffic["fetch_scale"],
+                                                          traffic["write_scale"]),
+              "| HBM bytes per launch (scaled; mean over the library's kernels) | %.0f |"
+              % traffic["bytes_per_launch"],
+              "| algorithmic bytes per launch | %d |" % traffic["algorithmic_bytes_per_launch"],
+              "| ratio | %.3f |" % (traffic["bytes_per_launch"]
+                                   / traffic["algorithmic_bytes_per_launch"]),
+              "| kernel source hash | `%s` |" % traffic["kernel_source_hash"], ""]
+    with open(out_md, "w") as f:
+        f.write("\n".join(lines))
+    print("wrote", out_md)
+
+
 def host_threads():
     """Host cores this process may run on, capped at 16 (one GPU's share)."""
     try:
@@ -229,6 +413,7 @@ def cpu_model():
 # replay carries a fixed cost of about 8 us on this runtime, which 20 steps
 # do not amortize; the queue of a stream holds a few thousand launches.
 QUEUED_MAX_STEPS = 1000
+MAX_SETS = 1024
 TIMING_DESC = {
     "queued": "K eager launches queued behind a spin kernel (the GPU runs them back to back; "
               "events bracket exactly the K launches)",
@@ -321,6 +506,9 @@ def main():
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
+    if args.summarize_profile:
+        summarize_profile(*args.summarize_profile)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only; multi-GPU runs are not part of this "
               "library (rows shard across GPUs with no communication)", file=sys.stderr)
@@ -347,7 +535,10 @@ def main():
     dev = torch.device("cuda:0")
     host = make_workload(w)
     set_bytes = sum(x.numel() * x.element_size() for x in host.values()) + 2 * 4 * N * T
-    R = max(2, int(np.ceil(args.rotate_mb * 2 ** 20 / set_bytes)))
+    # (at most MAX_SETS: a tiny batch would otherwise take tens of thousands of
+    # sets, and as many untimed pre-touch calls; such a batch is latency-bound
+    # and sits in the caches whatever the rotation)
+    R = max(2, min(MAX_SETS, int(np.ceil(args.rotate_mb * 2 ** 20 / set_bytes))))
     print("workload %s: %d x %d %s, %d rotating sets of %.2f MB" %
           (w.name, N, T, w.dtype, R, set_bytes / 2 ** 20), file=sys.stderr, flush=True)
 
@@ -602,7 +793,7 @@ def main():
     copy = floor = None
     if not args.no_copy_ceiling:
         half = algorithmic_bytes(w, N, T, args.window) // launches_per_step_of(w) // 2 // 16 * 16
-        RC = max(2, int(np.ceil(args.rotate_mb * 2 ** 20 / (2 * half))))
+        RC = max(2, min(MAX_SETS, int(np.ceil(args.rotate_mb * 2 ** 20 / (2 * half)))))
         bufs = [(torch.empty(half // 4, dtype=torch.float32, device=dev),
                  torch.empty(half // 4, dtype=torch.float32, device=dev)) for _ in range(RC)]
         for a, _ in bufs:
@@ -639,6 +830,8 @@ def main():
             for _ in range(args.body_blocks):
                 steps_b.append(once_b())
                 st = rl.rlca_timestamps().astype(np.int64)
+                if st.shape[0] == 0:
+                    break  # a kernel without stamps
                 bodies.append(float(st[:, 1].max() - st[:, 0].min()) * 0.01)
                 waves_us.append(float(np.median(st[:, 1] - st[:, 0])) * 0.01)
                 spreads.append(float(st[:, 0].max() - st[:, 0].min()) * 0.01)
@@ -648,13 +841,14 @@ def main():
         def q(v, f):
             v = sorted(v)
             return v[min(len(v) - 1, int(f * len(v)))]
-        body = {"median_us": q(bodies, 0.5), "p10_us": q(bodies, 0.1), "p90_us": q(bodies, 0.9),
-                "samples": len(bodies), "wavefronts": n_waves,
-                "wave_median_us": q(waves_us, 0.5), "start_spread_us": q(spreads, 0.5),
-                "instrumented_step_us": q(steps_b, 0.5),
-                "method": "librlca_timed.so (the same sources with per-wavefront 100 MHz "
-                          "wall-clock stamps); last launch of each of %d blocks of %d steps, "
-                          "%s" % (len(bodies), KB, TIMING_DESC[mode_b])}
+        if bodies:
+            body = {"median_us": q(bodies, 0.5), "p10_us": q(bodies, 0.1),
+                    "p90_us": q(bodies, 0.9), "samples": len(bodies), "wavefronts": n_waves,
+                    "wave_median_us": q(waves_us, 0.5), "start_spread_us": q(spreads, 0.5),
+                    "instrumented_step_us": q(steps_b, 0.5),
+                    "method": "librlca_timed.so (the same sources with per-wavefront 100 MHz "
+                              "wall-clock stamps); last launch of each of %d blocks of %d "
+                              "steps, %s" % (len(bodies), KB, TIMING_DESC[mode_b])}
     launches_per_step = launches_per_step_of(w) * (3 if split_segments > 1 else 1)
     if args.materialized:
         launches_per_step = launches_per_step_of(w) * (2 + max(0, (T - 1).bit_length()))

@@ -273,6 +273,9 @@ __global__ void __launch_bounds__(kProbsThreads)
 probs_kernel(const Args p, const TableArgs ta) {
   static_assert(Algo == kRetrace || Algo == kVtrace, "policy tables: Retrace or V-trace");
   static_assert(WPR == 1 || WPR == 4, "one or four wavefronts per row");
+#ifdef RLCA_TIMESTAMPS
+  const WaveStamp stamp{p.stamps, wall_clock()};  // written at every return
+#endif
   constexpr int K = kProbsK;
   constexpr int kGroup = 64 * WPR;            // threads per row
   constexpr int kTile = kGroup * K;           // steps per tile

@@ -551,6 +551,10 @@ int launch_probs(int algo, int dtype, const Args &args, const TableArgs &tables,
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no policy-table kernel for algorithm %d", algo);
   Args a = args;
   TableArgs ta = tables;
+#ifdef RLCA_TIMESTAMPS
+  int stamp_dev = 0;
+  RLCA_TRY(stamp_buffer(&stamp_dev, &a.stamps));
+#endif
   const int64_t rows_per_block = 4 / wpr;
   const dim3 grid(static_cast<unsigned>((a.N + rows_per_block - 1) / rows_per_block));
   const dim3 block(kProbsBlock);
@@ -559,6 +563,10 @@ int launch_probs(int algo, int dtype, const Args &args, const TableArgs &tables,
       hipLaunchKernel(kernel, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   t_last_variant = -1;
+#ifdef RLCA_TIMESTAMPS
+  t_last_waves = static_cast<int64_t>(grid.x) * (kProbsBlock / 64);
+  t_last_device = stamp_dev;
+#endif
   return RLCA_OK;
 }
 
