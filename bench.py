@@ -148,6 +148,24 @@ def algorithmic_bytes(w, N, T, window=False):
     raise ValueError(w.algo)
 
 
+def stream_mixes(w):
+    """The byte mix of each launch of a step, as (fp32 arrays, 16-bit arrays,
+    byte arrays, fp32 outputs) of N*T elements each, for the streaming-ceiling
+    leg: the arrays the method must read and write (algorithmic_bytes), or None
+    where the ceiling kernel has no such mix."""
+    flags = 2 if w.p_trunc is not None else 1
+    mixes = {"returns": [(1, 0, flags, 1)], "gae": [(2, 0, 2, 2)],
+             "td_lambda": [(2, 0, flags, 1)], "vtrace+retrace": [(3, 0, 1, 2), (4, 0, 1, 1)],
+             "eligibility": [(1, 0, flags, 1)], "cumsum": [(1, 0, flags, 1)]}.get(w.algo)
+    if mixes is None:
+        return None
+    if w.dtype == "bf16":
+        mixes = [(0, nf, nb, no) for nf, _, nb, no in mixes]
+    known = {(1, 0, 1, 1), (2, 0, 2, 2), (2, 0, 1, 1), (2, 0, 2, 1), (3, 0, 1, 2), (4, 0, 1, 1),
+             (0, 2, 2, 2), (1, 0, 2, 1)}
+    return mixes if all(m in known for m in mixes) else None
+
+
 def launches_per_step_of(w):
     return 2 if w.algo == "vtrace+retrace" else 1
 
@@ -335,6 +353,13 @@ def summarize_profile(run_dir, out_md):
         lines.append("| copy ceiling: torch copy of %d bytes (half read, half written), µs per "
                      "launch | %.3f (%.0f GB/s) |" % (cp["bytes_per_launch"], cp["avg_launch_us"],
                                                       cp["GBps"]))
+    sc = b.get("stream_ceiling")
+    if sc:
+        lines.append("| streaming ceiling: the same byte mix streamed with no recurrence "
+                     "(libstream_ceiling.so, best of 9 launch shapes), µs per step | %.3f "
+                     "(%.0f GB/s) |" % (sc["step_us"], sc["GBps"]))
+        lines.append("| this call's speed relative to the streaming ceiling | %.1f%% |"
+                     % (100 * rf["frac_of_stream_ceiling"]))
     lines += ["", "## rocprofv3 kernel trace (durations of single dispatches, ns)", "",
               "The tracer takes each dispatch alone (start to start about 20 µs apart in "
               "these runs), so a duration here is one launch's latency from the command "
@@ -810,6 +835,65 @@ def main():
         fus = make_timed(lambda i: torch.cuda._sleep(0), KC, mode_c, stream, rate)()
         floor = {"avg_launch_us": fus, "kernel": "torch.cuda._sleep(0), an almost empty kernel",
                  "timing": TIMING_DESC[mode_c]}
+    # ---- streaming ceiling: the workload's byte mix (the arrays the method
+    # must read and write, N*T elements each) streamed by a kernel with no
+    # recurrence (libstream_ceiling.so), timed the same way over a few launch
+    # shapes; the best is the practical ceiling of one launch of this size.
+    ceiling = None
+    mixes = stream_mixes(w)
+    from reverse_linear_recurrence_amd import build as hip_build
+    if (not args.no_copy_ceiling and mixes and not args.window
+            and os.path.exists(hip_build.LIB_CEILING)):
+        import ctypes
+        clib = ctypes.CDLL(hip_build.LIB_CEILING)
+        clib.stream_ceiling.restype = ctypes.c_int
+        E = N * T
+        KC = min(K, QUEUED_MAX_STEPS)
+        mode_c = "eager" if mode == "eager" else ("queued" if rate is not None else "graph")
+        per_launch, shapes = [], []
+        for nf, nh, nb, no in mixes:
+            mix_bytes = E * (4 * nf + 2 * nh + nb + 4 * no)
+            RS = max(2, min(MAX_SETS, int(np.ceil(args.rotate_mb * 2 ** 20 / mix_bytes))))
+            P4 = ctypes.c_void_p * 4
+            csets = []
+            for _ in range(RS):
+                arrs = ([torch.empty(E, dtype=torch.float32, device=dev) for _ in range(nf)],
+                        [torch.zeros(E, dtype=torch.int16, device=dev) for _ in range(nh)],
+                        [torch.zeros(E, dtype=torch.uint8, device=dev) for _ in range(nb)],
+                        [torch.empty(E, dtype=torch.float32, device=dev) for _ in range(no)])
+                for a in arrs[0]:
+                    a.fill_(1.0)
+                ptrs = [P4(*([x.data_ptr() for x in group] + [None] * (4 - len(group))))
+                        for group in arrs]
+                csets.append((ptrs, arrs))
+            best = None
+            for u in (1, 2, 4):
+                for blk in (256, 512, 1024):
+                    def cstep(i, u=u, blk=blk):
+                        pt = csets[i % RS][0]
+                        rc = clib.stream_ceiling(nf, nh, nb, no, pt[0], pt[1], pt[2], pt[3],
+                                                 ctypes.c_int64(E), u, blk, ctypes.c_void_p(
+                                                     torch.cuda.current_stream().cuda_stream))
+                        if rc != 0:
+                            raise RuntimeError("stream_ceiling failed (%d)" % rc)
+                    for i in range(RS):
+                        cstep(i)
+                    torch.cuda.synchronize()
+                    us = make_timed(cstep, KC, mode_c, stream, rate)()
+                    if best is None or us < best[0]:
+                        best = (us, u, blk)
+            per_launch.append(best[0])
+            shapes.append({"slots_per_thread": best[1], "workgroup": best[2],
+                           "bytes_per_launch": mix_bytes})
+            del csets
+        torch.cuda.synchronize()
+        ceil_us = sum(per_launch)
+        ceiling = {"step_us": ceil_us, "per_launch_us": per_launch, "launches": shapes,
+                   "GBps": algorithmic_bytes(w, N, T) / (ceil_us * 1e-6) / 1e9,
+                   "kernel": "stream_ceiling (libstream_ceiling.so): the workload's byte mix "
+                             "with non-temporal loads and stores and no recurrence; best of "
+                             "3 x 3 launch shapes",
+                   "timing": TIMING_DESC[mode_c]}
     # ---- kernel body: the same steps through the instrumented build of the
     # library (librlca_timed.so: same sources, plus per-wavefront wall-clock
     # stamps at entry and once all loads and stores are done).  For the last
@@ -956,10 +1040,13 @@ def main():
                      "kernel_body_us": body["median_us"] if body else None,
                      "kernel_only_frac": (bytes_per_step / launches_per_step
                                           / (body["median_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS)
-                     if body and launches_per_step == 1 else None},
+                     if body and launches_per_step == 1 else None,
+                     "frac_of_stream_ceiling": (ceiling["step_us"] / (ms_per_step * 1e3))
+                     if ceiling else None},
         "kernel_body": body,
         "cpu_baseline": cpu,
         "copy_ceiling": copy,
+        "stream_ceiling": ceiling,
         "launch_floor": floor,
         "step_us_spread": spread,
         "parity_max_rel_err": parity,

@@ -19,6 +19,10 @@ LIB = os.path.join(PKG, "librlca.so")
 # that the scan kernels record per-wavefront wall-clock stamps (a measurement
 # tool for bench.py; never loaded by default).
 LIB_TIMED = os.path.join(PKG, "librlca_timed.so")
+# A measurement tool beside the library (not part of it): the streaming
+# ceiling of a workload's byte mix, timed by bench.py.
+CEILING_SRC = os.path.join(CSRC, "stream_ceiling.hip")
+LIB_CEILING = os.path.join(PKG, "libstream_ceiling.so")
 # Host code and the kernel tables, compiled in parallel.
 SOURCES = [os.path.join(CSRC, n) for n in ("rlca.hip", "kernels_plain.hip", "kernels_window.hip",
                                            "kernels_probs.hip", "kernels_materialized.hip")]
@@ -98,6 +102,29 @@ def build(verbose=False, timestamps=False):
     return target
 
 
+def build_ceiling(verbose=False):
+    """Compile libstream_ceiling.so (bench.py's streaming-ceiling leg) and
+    return its path."""
+    tmp = LIB_CEILING + ".tmp%d" % os.getpid()
+    cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall", "-Wextra",
+           CEILING_SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    try:
+        rc, out = _run(cmd)
+        if rc != 0:
+            raise RuntimeError("hipcc failed on %s (%d):\n%s" % (CEILING_SRC, rc, out))
+        os.replace(tmp, LIB_CEILING)
+    finally:
+        if os.path.exists(tmp):
+            os.remove(tmp)
+    return LIB_CEILING
+
+
 if __name__ == "__main__":
-    print(build(verbose=True, timestamps="--timestamps" in sys.argv[1:]))
+    if "--ceiling" in sys.argv[1:]:
+        print(build_ceiling(verbose=True))
+    else:
+        print(build(verbose=True, timestamps="--timestamps" in sys.argv[1:]))
     sys.exit(0)

@@ -39,6 +39,21 @@ def test_algorithmic_bytes(name, expected):
     assert bench.algorithmic_bytes(w, w.num_envs, w.T) == expected
 
 
+@pytest.mark.parametrize("name", [n for n in WORKLOADS if bench.stream_mixes(WORKLOADS[n])])
+def test_stream_ceiling_moves_the_per_step_algorithmic_bytes(name):
+    """The streaming-ceiling leg moves, per step, exactly the algorithmic
+    bytes of every env-step (all but the per-row bootstrap terms)."""
+    w = WORKLOADS[name]
+    per_step = sum(4 * nf + 2 * nh + nb + 4 * no for nf, nh, nb, no in bench.stream_mixes(w))
+    per_row = bench.algorithmic_bytes(w, w.num_envs, 0)
+    assert per_step * w.num_envs * w.T == bench.algorithmic_bytes(w, w.num_envs, w.T) - per_row
+
+
+def test_stream_ceiling_has_a_mix_for_every_scan_workload():
+    for name, w in WORKLOADS.items():
+        assert (bench.stream_mixes(w) is None) == w.algo.endswith("_probs"), name
+
+
 def test_window_bytes_add_the_carry_vectors():
     w = WORKLOADS["gae_4096x128"]
     plain = bench.algorithmic_bytes(w, w.num_envs, w.T)
