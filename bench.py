@@ -38,7 +38,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 _CSRC = os.path.join(ROOT, "reverse_linear_recurrence_amd", "csrc")
 KERNEL_SOURCES = {
     "scan": ("scan_kernels.hpp", "kernel_table.hpp", "variants.hpp", "kernels_plain.hip",
-             "kernels_window.hip", "rlca.hip"),
+             "kernels_window.hip", "kernels_chain.hip", "rlca.hip"),
     "probs": ("scan_kernels.hpp", "probs_kernels.hpp", "variants.hpp", "kernels_probs.hip",
               "rlca.hip"),
     "materialized": ("scan_kernels.hpp", "materialized.hpp", "kernels_materialized.hip",
@@ -96,6 +96,9 @@ def parse():
                     help="call the window form with a workspace (and, without --window, no "
                          "carries), so that calls on few long rows split every row into "
                          "segments")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="with --split: the three-launch form of split calls instead of the "
+                         "chained one (rlca_set_chained(False))")
     ap.add_argument("--spread-replays", type=int, default=11,
                     help="after the timed region, time the same K steps this many more "
                          "times, each block alone, for median / p10 / p90 (0: skip)")
@@ -592,6 +595,8 @@ def main():
             sys.exit(2)
         split_segments = rl.rlca_split_segments(N, T)
         workspace = rl.split_workspace(N, T, dev)
+    if args.no_chain:
+        rl.rlca_set_chained(False)
 
     def window_step(d):
         if args.window:
@@ -703,6 +708,7 @@ def main():
     import oracle
     step(sets[0])
     torch.cuda.synchronize()
+    launches_per_call = rl.rlca_last_launches()  # of the step's (last) library call
     win = dict(carry_in=carry_in, chunk=True) if args.window else {}
     if args.window and w.algo in ("returns",):
         win = dict(chunk=True)
@@ -933,9 +939,12 @@ def main():
                     "method": "librlca_timed.so (the same sources with per-wavefront 100 MHz "
                               "wall-clock stamps); last launch of each of %d blocks of %d "
                               "steps, %s" % (len(bodies), KB, TIMING_DESC[mode_b])}
-    launches_per_step = launches_per_step_of(w) * (3 if split_segments > 1 else 1)
-    if args.materialized:
-        launches_per_step = launches_per_step_of(w) * (2 + max(0, (T - 1).bit_length()))
+    launches_per_step = launches_per_step_of(w) * launches_per_call
+    split_form = None
+    if args.split:
+        split_form = {1: "unsplit", 2: "chained", 3: "three-launch"}.get(launches_per_call)
+        if split_form != "three-launch":
+            split_segments = None if split_form == "chained" else 1
     env_steps = N * T
     value = env_steps / (ms_per_step * 1e-3)
     bytes_per_step = algorithmic_bytes(w, N, T, args.window)
@@ -1029,7 +1038,7 @@ def main():
                    "seed": w.seed, "rotation_sets": R, "timing": timing,
                    "before_warmup": "one untimed call per rotation set",
                    "launches_per_step": launches_per_step, "variant": variant,
-                   "split_segments": split_segments,
+                   "split_segments": split_segments, "split_form": split_form,
                    "entry": "window (carry in; carry and carry map out)" if args.window
                    else ("materialized doubling scan (2 + ceil(log2 T) launches through HBM)"
                          if args.materialized else "plain")},

@@ -399,10 +399,10 @@ int rlca_gae_chunk(int64_t num_envs, int64_t T, int dtype,
  * device memory or pass a workspace (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation).  Same arguments without
  * (workspace, workspace_bytes), same results: a call that would split (see
- * "Split calls" below) takes its workspace from a 6 KB array that the
- * library holds on each device until the process ends, room for every split
- * the library makes (3 floats per segment, at most 512 segments; a larger
- * need is RLCA_EINVAL).  The array's address on a device is looked up on the
+ * "Split calls" below) takes the three-launch form, with its workspace from
+ * a 6 KB array that the library holds on each device until the process
+ * ends, room for every split of that form (3 floats per segment, at most 512
+ * segments; a larger need is RLCA_EINVAL).  The array's address on a device is looked up on the
  * first call there (with that device made current for the lookup); no call
  * allocates or frees memory.  Every call on one device shares that device's
  * array, and each split call overwrites it before reading it: calls that
@@ -650,38 +650,68 @@ typedef enum {
  * least 32768 steps leaves most compute units idle.  A window call of the
  * scan family (rlca_*_chunk of the seven algorithms and rlca_affine_scan; not
  * the policy-table calls) given a workspace then cuts every row into
- * S = rlca_split_segments(N, T) segments of T / S steps and runs three
- * launches on `stream`: the segments from carry 0, writing only their carry
- * maps to the workspace; a small kernel composing, per row, the carry that
- * enters each segment from carry_in, and the row's carry_out and carry_map;
- * and the segments again from those carries, writing the outputs.  It reads
- * the inputs twice and computes the same results up to rounding order.  The
- * plain entry points (rlca_gae, ...) never split: for the same result on few
- * long rows call the window form with NULL carries and a workspace.
+ * segments, in one of two forms, and computes the same results up to
+ * rounding order:
  *
- * Workspace.  Device memory owned by the caller, 4-byte aligned, at least
- * rlca_split_workspace_bytes(N, T) bytes; it must not overlap the call's
- * arrays (RLCA_EALIAS).  It is used only when S > 1 (otherwise the call runs
- * unsplit and never touches it); then a smaller size is RLCA_EINVAL.  Calls
- * that share a workspace must be ordered, for instance issued to one stream:
- * the library does not synchronize.  workspace_bytes < 0 or a misaligned
- * workspace -> RLCA_EINVAL.
+ * Chained (one pass).  Where the row length is a multiple of one or two
+ * whole tiles of a tiling with whole wavefronts per row, with at most 64
+ * segments per row and at least half as many as the three-launch form below
+ * takes, the rows share one row stride, the workspace is 8-byte aligned and
+ * holds 8 bytes plus 32 per segment: two launches, a one-thread
+ * kernel advancing the workspace's epoch word (the call's tag), then one
+ * workgroup per segment that scans its segment, publishes its carry map in
+ * the workspace, composes the maps the segments before it in scan order have
+ * published into the carry entering its own (from the row's end for reverse
+ * recurrences, from its start for the forward mirrors, starting at
+ * carry_in), publishes the map to the carry it hands on, and writes its
+ * outputs.  The inputs are read once.  Published words carry the tag, so the
+ * workspace needs no clearing, before the first call or between calls (also
+ * between replays of a captured graph).  A workgroup waits only for
+ * workgroups launched before it; its wait is bounded all the same, and a
+ * carry not found within the bound (which the hardware's in-order workgroup
+ * dispatch rules out) turns that segment's outputs into NaN.
+ *
+ * Three launches, otherwise: S = rlca_split_segments(N, T) segments of
+ * T / S steps; the segments from carry 0, writing only their carry maps to
+ * the workspace; a small kernel composing, per row, the carry that enters
+ * each segment from carry_in, and the row's carry_out and carry_map; and the
+ * segments again from those carries, writing the outputs.  It reads the
+ * inputs twice.
+ *
+ * rlca_set_chained(0) makes the calling thread's split calls take the
+ * three-launch form (for tests and comparisons); rlca_set_chained(1) restores
+ * the default.  It returns the previous setting.  rlca_last_launches() is
+ * the number of kernel launches the calling thread's last successful call
+ * enqueued.  The plain entry points (rlca_gae, ...) never split: for the same
+ * result on few long rows call the window form with NULL carries and a
+ * workspace.
+ *
+ * Workspace.  Device memory owned by the caller, 4-byte aligned (8 for the
+ * chained form), at least rlca_split_workspace_bytes(N, T) bytes; it must not
+ * overlap the call's arrays (RLCA_EALIAS).  It is used only when the call
+ * splits (otherwise the call runs unsplit and never touches it); then a size
+ * below what the three-launch form needs is RLCA_EINVAL (a size that fits
+ * only that form selects it).  Calls that share a workspace must be ordered,
+ * for instance issued to one stream: the library does not synchronize.
+ * workspace_bytes < 0 or a misaligned workspace -> RLCA_EINVAL.
  *
  * Failure.  Every argument is validated before the first launch.  Kernel
  * launches cannot be withdrawn once enqueued, so should the runtime refuse
- * the second or third launch (RLCA_EHIP, which a launch that the runtime
- * accepted on the same stream an instant earlier leaves only to a failing
- * runtime or device), the earlier launches stay enqueued: the workspace and,
- * after the second, carry_out and carry_map may then hold results, while the
- * outputs are not written.
+ * the second or third launch of the three-launch form (RLCA_EHIP, which a
+ * launch that the runtime accepted on the same stream an instant earlier
+ * leaves only to a failing runtime or device), the earlier launches stay
+ * enqueued: the workspace and, after the second, carry_out and carry_map may
+ * then hold results, while the outputs are not written.
  *
- * rlca_split_segments(num_envs, T) returns S (1: no split): the smallest
- * power of two with num_envs * S >= 256, T divisible by S and T / S >= 4096,
- * stopping where either condition would fail; 1 for more than 64 rows and
- * for rows shorter than 32768 steps; -1 (with a message for rlca_last_error)
- * for num_envs < 0 or T < 1.  rlca_split_workspace_bytes(num_envs, T) returns
- * the workspace a split call needs, 12 * num_envs * S bytes (3 floats per
- * segment), or 0 when S = 1; -1 as above.
+ * rlca_split_segments(num_envs, T) returns the three-launch form's S (1: no
+ * split): the smallest power of two with num_envs * S >= 256, T divisible by
+ * S and T / S >= 4096, stopping where either condition would fail; 1 for
+ * more than 64 rows and for rows shorter than 32768 steps; -1 (with a message
+ * for rlca_last_error) for num_envs < 0 or T < 1.
+ * rlca_split_workspace_bytes(num_envs, T) returns the workspace a split call
+ * may use, the larger of the three-launch form's 12 * num_envs * S bytes (3
+ * floats per segment) and the chained form's 8 bytes plus 32 per segment for
+ * any input dtype, or 0 when neither splits; -1 as above.
  */
 int rlca_split_segments(int64_t num_envs, int64_t T);
 int64_t rlca_split_workspace_bytes(int64_t num_envs, int64_t T);
@@ -708,6 +738,8 @@ int rlca_set_variant(int variant);
 int rlca_variant_info(int variant, int algo, int dtype, int *steps_per_lane, int *lanes_per_row,
                       int *waves_per_row);
 int rlca_last_variant(void);
+int rlca_set_chained(int enable);
+int rlca_last_launches(void);
 
 #ifdef __cplusplus
 }

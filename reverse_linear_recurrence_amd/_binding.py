@@ -99,6 +99,8 @@ _SIGNATURES = {
     "rlca_variant_info": [_int, _int, _int, ctypes.POINTER(_int), ctypes.POINTER(_int),
                           ctypes.POINTER(_int)],
     "rlca_last_variant": [],
+    "rlca_set_chained": [_int],
+    "rlca_last_launches": [],
 }
 
 
@@ -975,3 +977,14 @@ def rlca_timestamps(max_waves=1 << 16):
 
 def rlca_last_variant():
     return load_library().rlca_last_variant()
+
+
+def rlca_set_chained(enable):
+    """Allow (True, the default) or forbid the one-launch chained form of
+    split calls on this thread; returns the previous setting."""
+    return bool(load_library().rlca_set_chained(1 if enable else 0))
+
+
+def rlca_last_launches():
+    """Kernel launches the calling thread's last successful call enqueued."""
+    return load_library().rlca_last_launches()

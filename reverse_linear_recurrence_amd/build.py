@@ -25,7 +25,8 @@ CEILING_SRC = os.path.join(CSRC, "stream_ceiling.hip")
 LIB_CEILING = os.path.join(PKG, "libstream_ceiling.so")
 # Host code and the kernel tables, compiled in parallel.
 SOURCES = [os.path.join(CSRC, n) for n in ("rlca.hip", "kernels_plain.hip", "kernels_window.hip",
-                                           "kernels_probs.hip", "kernels_materialized.hip")]
+                                           "kernels_chain.hip", "kernels_probs.hip",
+                                           "kernels_materialized.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, n) for n in ("scan_kernels.hpp", "kernel_table.hpp",
                                                    "variants.hpp", "probs_kernels.hpp",
                                                    "materialized.hpp")] + [

@@ -61,4 +61,36 @@ const void *kernel_ptr(int dtype, int v, bool uniform, int tiles = 0, bool align
   return uniform ? kernel_ptr<A, float, true, C>(v) : kernel_ptr<A, float, false, C>(v);
 }
 
+// Chained instances (one-launch split calls): window instances with a
+// uniform row stride for segments of exactly one or two whole tiles, in the
+// tilings with whole wavefronts per row (variants 3-8).
+template <int A, typename InT, int V, int O>
+const void *chain_ptr() {
+  constexpr Variant v = kVariants[V];
+  static_assert(v.WPR > 1, "chained instances need whole-wavefront rows");
+  constexpr int K = steps_per_lane(v, sizeof(InT) == 2, A == kVtrace);
+  return reinterpret_cast<const void *>(
+      &scan_kernel<A, InT, K, v.LPR, v.WPR, true, true, O, false, true>);
+}
+
+template <int A, typename InT, int O>
+const void *chain_ptr(int v) {
+  switch (v) {
+    case 3: return chain_ptr<A, InT, 3, O>();
+    case 4: return chain_ptr<A, InT, 4, O>();
+    case 5: return chain_ptr<A, InT, 5, O>();
+    case 6: return chain_ptr<A, InT, 6, O>();
+    case 7: return chain_ptr<A, InT, 7, O>();
+    case 8: return chain_ptr<A, InT, 8, O>();
+    default: return nullptr;
+  }
+}
+
+template <int A>
+const void *chain_ptr(int dtype, int v, int tiles) {
+  if (tiles == 1) return dtype == RLCA_BF16 ? chain_ptr<A, bf16_t, 1>(v) : chain_ptr<A, float, 1>(v);
+  if (tiles == 2) return dtype == RLCA_BF16 ? chain_ptr<A, bf16_t, 2>(v) : chain_ptr<A, float, 2>(v);
+  return nullptr;
+}
+
 }  // namespace rlca

@@ -63,6 +63,8 @@ int auto_variant(int64_t N, int64_t T, bool bf16, bool vtrace) {
 thread_local std::string t_last_error;
 thread_local int t_forced_variant = -1;
 thread_local int t_last_variant = -1;
+thread_local int t_chained = 1;      // rlca_set_chained
+thread_local int t_last_launches = 0;  // rlca_last_launches
 
 
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -187,34 +189,12 @@ int check_sizes(int64_t N, int64_t T, int dtype) {
     if (rc_ != RLCA_OK) return rc_; \
   } while (0)
 
-// window: the instance with carry vectors (Args::cin, cout, cmap).
-// S > 1: segment view (window instances): each of the args.N rows is cut
-// into S segments of args.T steps, segment y taken by grid row y.
-int launch(int algo, int dtype, const Args &args, void *stream, bool window = false, int S = 1) {
-  const int v = t_forced_variant >= 0
-                    ? t_forced_variant
-                    : auto_variant(args.N * S, args.T, dtype == RLCA_BF16, algo == kVtrace);
-  const Variant var = kVariants[v];
-  dim3 grid, block;
-  const int waves = short_row_waves(var.WPR, var.LPR, window);
-  if (var.WPR > 1) {
-    grid = dim3(static_cast<unsigned>(args.N), static_cast<unsigned>(S));
-  } else {
-    const int64_t rows_per_wg = waves * (64 / var.LPR);
-    grid = dim3(static_cast<unsigned>((args.N + rows_per_wg - 1) / rows_per_wg),
-                static_cast<unsigned>(S));
-  }
-  block = dim3(64 * waves);
-  Args a = args;
-  a.seg_count = S;
-#ifdef RLCA_TIMESTAMPS
-  int stamp_dev = 0;
-  RLCA_TRY(stamp_buffer(&stamp_dev, &a.stamps));
-#endif
-  // Truncation bootstraps of the whole call: dense reads for small batches.
-  const bool dense_tv = args.N * S * args.T <= kDenseTvMaxSteps;
-  // Hot streams (see scan_kernels.hpp), passed again as preloaded scalars.
-  const void *hot[5] = {a.r, nullptr, nullptr, nullptr, nullptr};
+// The hot streams of a launch (see scan_kernels.hpp) and the stride of values
+// (or Retrace's truncation switch) in ldx; returns whether the hot [N,T]
+// streams share the rewards' row stride (the kUniform instances).
+bool hot_streams(int algo, const Args &a, bool dense_tv, const void *(&hot)[5], int64_t *ldx_out) {
+  hot[0] = a.r;
+  for (int i = 1; i < 5; ++i) hot[i] = nullptr;
   int64_t hld[5] = {a.ld_r, 0, 0, 0, 0};  // stride of each hot [N,T] stream (0: none)
   int64_t ldx = 0;
   switch (algo) {
@@ -258,6 +238,93 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
   bool uniform = true;
   for (int i = 1; i < 5; ++i)
     if (hot[i] != nullptr && hld[i] != 0 && hld[i] != a.ld_r) uniform = false;
+  *ldx_out = ldx;
+  return uniform;
+}
+
+int64_t esize_of(int dtype) { return dtype == RLCA_BF16 ? 2 : 4; }
+
+// A chained split (one pass over the inputs): the tiling, whole tiles per
+// segment, segments per row, and the workspace (its epoch word, then the
+// words the segments publish).
+struct ChainPlan {
+  int v = -1;  // < 0: none
+  int tiles = 0;
+  int64_t S = 0;
+  unsigned long long *slots = nullptr;
+};
+
+// The chained split's epoch word advanced to its next value, never 0 (its low
+// half is the next call's tag; scan_kernels.hpp).
+__global__ void __launch_bounds__(64) chain_epoch(unsigned long long *epoch) {
+  if (threadIdx.x != 0) return;
+  uint32_t e = static_cast<uint32_t>(
+      __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  e = e + 1 != 0 ? e + 1 : 1;
+  __hip_atomic_store(epoch, static_cast<unsigned long long>(e), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// window: the instance with carry vectors (Args::cin, cout, cmap).
+// S > 1: segment view (window instances): each of the args.N rows is cut
+// into S segments of args.T steps, segment y taken by grid row y.
+// chain: the chained instance for that segment view (S = chain->S).
+int launch(int algo, int dtype, const Args &args, void *stream, bool window = false, int S = 1,
+           const ChainPlan *chain = nullptr) {
+  const int v = chain != nullptr ? chain->v
+                : t_forced_variant >= 0
+                    ? t_forced_variant
+                    : auto_variant(args.N * S, args.T, dtype == RLCA_BF16, algo == kVtrace);
+  const Variant var = kVariants[v];
+  dim3 grid, block;
+  const int waves = short_row_waves(var.WPR, var.LPR, window);
+  if (var.WPR > 1) {
+    grid = dim3(static_cast<unsigned>(args.N), static_cast<unsigned>(S));
+  } else {
+    const int64_t rows_per_wg = waves * (64 / var.LPR);
+    grid = dim3(static_cast<unsigned>((args.N + rows_per_wg - 1) / rows_per_wg),
+                static_cast<unsigned>(S));
+  }
+  block = dim3(64 * waves);
+  Args a = args;
+  a.seg_count = S;
+  if (chain != nullptr) {
+    // the workspace's epoch advances first: this call's tag
+    a.chain = chain->slots;
+    void *ekargs[] = {&a.chain};
+    const hipError_t ee = hipLaunchKernel(reinterpret_cast<const void *>(&chain_epoch), dim3(1),
+                                          dim3(64), ekargs, 0, static_cast<hipStream_t>(stream));
+    if (ee != hipSuccess)
+      return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(ee));
+    if (!(algo == kEligibility || algo == kCumsum || algo == kAffineFwd)) {
+      // Reverse recurrences take the segments from the row's end: every row
+      // pointer moves to the row's last segment (scan_kernels.hpp).
+      const int64_t shift = (S - 1) * args.T;
+      const int64_t es = esize_of(dtype);
+      auto move = [&](const void *ptr, int64_t esize) -> const void * {
+        return ptr == nullptr ? nullptr : static_cast<const char *>(ptr) + shift * esize;
+      };
+      a.r = move(a.r, es);
+      a.v = move(a.v, es);
+      a.lr = move(a.lr, es);
+      a.eq = move(a.eq, es);
+      a.tv = move(a.tv, es);
+      a.term = static_cast<const uint8_t *>(move(a.term, 1));
+      a.trunc = static_cast<const uint8_t *>(move(a.trunc, 1));
+      a.o0 = a.o0 == nullptr ? nullptr : a.o0 + shift;
+      a.o1 = a.o1 == nullptr ? nullptr : a.o1 + shift;
+    }
+  }
+#ifdef RLCA_TIMESTAMPS
+  int stamp_dev = 0;
+  RLCA_TRY(stamp_buffer(&stamp_dev, &a.stamps));
+#endif
+  // Truncation bootstraps of the whole call: dense reads for small batches.
+  const bool dense_tv = args.N * S * args.T <= kDenseTvMaxSteps;
+  // Hot streams (see scan_kernels.hpp), passed again as preloaded scalars.
+  const void *hot[5];
+  int64_t ldx = 0;
+  const bool uniform = hot_streams(algo, a, dense_tv, hot, &ldx);
   int N32 = static_cast<int>(a.N);
   int T32 = static_cast<int>(a.T);
   int ldT = static_cast<int>(a.ld_r);
@@ -278,8 +345,10 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
       (a.term == nullptr || rows_aligned(a.term, a.ld_term, 1)) &&
       (a.trunc == nullptr || rows_aligned(a.trunc, a.ld_trunc, 1)) &&
       ((a.term != nullptr && a.trunc != nullptr) || rows_aligned(a.r, a.ld_r, es));
-  const void *kernel = window ? window_kernel(algo, dtype, v, uniform)
-                              : plain_kernel(algo, dtype, v, uniform, tiles, flags_aligned);
+  const void *kernel = chain != nullptr ? (uniform ? chain_kernel(algo, dtype, v, chain->tiles)
+                                                   : nullptr)
+                       : window ? window_kernel(algo, dtype, v, uniform)
+                                : plain_kernel(algo, dtype, v, uniform, tiles, flags_aligned);
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no kernel for algorithm %d", algo);
   const hipError_t e = hipLaunchKernel(kernel, grid, block, kargs, 0,
                                        static_cast<hipStream_t>(stream));
@@ -292,8 +361,6 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
 #endif
   return RLCA_OK;
 }
-
-int64_t esize_of(int dtype) { return dtype == RLCA_BF16 ? 2 : 4; }
 
 // The carry vectors of a window call (all NULL and off for the plain calls),
 // and the caller's workspace for a split call (NULL: never split).
@@ -391,6 +458,53 @@ int64_t split_count(int64_t N, int64_t T) {
   int64_t S = 1;
   while (N * S < kSplitTarget && T % (2 * S) == 0 && T / (2 * S) >= kSplitMinLen) S *= 2;
   return S;
+}
+
+// The chained form of a split call (one pass; see scan_kernels.hpp): the
+// segments are one or two whole tiles of a whole-wavefront tiling, at most
+// kChainMaxSegments per row, so that each workgroup's segment is scanned in
+// registers before its carry is known.  Tilings are tried from the longest
+// tile down, two tiles per segment before one; the first with
+// N * S >= kSplitTarget is taken, else the one with the most segments.  Same
+// rows as the three-launch split (at most kSplitMaxRows rows of at least
+// kSplitMinRow steps).
+ChainPlan chain_plan(int64_t N, int64_t T, bool bf16, bool vtrace) {
+  ChainPlan best;
+  if (N < 1 || N > kSplitMaxRows || T < kSplitMinRow) return best;
+  for (int v = kNumVariants - 1; v >= 0; --v) {
+    if (kVariants[v].WPR == 1) continue;
+    for (int tiles = 2; tiles >= 1; --tiles) {
+      const int64_t len = tiles * tile_steps(kVariants[v], bf16, vtrace);
+      if (T % len != 0) continue;
+      const int64_t S = T / len;
+      if (S < 2 || S > kChainMaxSegments) continue;
+      if (best.v < 0 || S > best.S) {
+        best.v = v;
+        best.tiles = tiles;
+        best.S = S;
+      }
+      if (N * S >= kSplitTarget) return best;
+    }
+  }
+  return best;
+}
+
+// Workspace bytes of a chained split: the epoch word, then 4 words per
+// segment.
+int64_t chain_bytes(int64_t N, int64_t S) { return 8 + 32 * N * S; }
+
+// The workspace a split call of N rows of T steps may use: the larger of the
+// three-launch split's and the chained form's for any input dtype.
+int64_t split_workspace_bytes(int64_t N, int64_t T) {
+  const int64_t S = split_count(N, T);
+  int64_t need = S > 1 ? 12 * N * S : 0;
+  for (int bf16 = 0; bf16 < 2; ++bf16) {
+    for (int vtrace = 0; vtrace < 2; ++vtrace) {
+      const ChainPlan c = chain_plan(N, T, bf16 != 0, vtrace != 0);
+      if (c.v >= 0 && chain_bytes(N, c.S) > need) need = chain_bytes(N, c.S);
+    }
+  }
+  return need;
 }
 
 // The carry entering each segment, from the segments' maps: reverse
@@ -493,9 +607,40 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
     arrs[n++] = Arr{"workspace", w.ws, 4 * nt, 4 * nt, 4, false, true, true};
     for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], N));
     RLCA_TRY(check_aliasing(arrs, n));
-    return launch_materialized(algo, dtype, a, static_cast<float *>(w.ws), stream);
+    RLCA_TRY(launch_materialized(algo, dtype, a, static_cast<float *>(w.ws), stream));
+    t_last_launches = 2 + static_cast<int>(std::ceil(std::log2(static_cast<double>(a.T))));
+    return RLCA_OK;
   }
   if (N == 0) return RLCA_OK;
+  // The chained split (one pass) where it applies: a workspace large
+  // enough and 8-byte aligned (its words are 64-bit), rows that share one
+  // stride, chaining not switched off for this thread, and at least half as
+  // many segments as the three-launch form would take.  (Where the chained
+  // form has fewer, its segments are long and few workgroups run them: bf16
+  // GAE 1x1048576, 64 against 256 segments, took 13.40 against 12.38 us;
+  // 2x524288, 64 against 128, 10.19 against 10.90 us.)
+  if (w.ws != nullptr && t_chained) {
+    ChainPlan cp = chain_plan(N, a.T, dtype == RLCA_BF16, algo == kVtrace);
+    const void *hot[5];
+    int64_t ldx = 0;
+    if (cp.v >= 0 && 2 * cp.S >= split_count(N, a.T) &&
+        reinterpret_cast<uintptr_t>(w.ws) % 8 == 0 &&
+        w.ws_bytes >= chain_bytes(N, cp.S) && hot_streams(algo, a, false, hot, &ldx)) {
+      const int64_t floats = chain_bytes(N, cp.S) / 4;
+      arrs[n++] = Arr{"workspace", w.ws, floats, floats, 4, false, true, true};
+      for (int i = 0; i < n; ++i) RLCA_TRY(check_array(arrs[i], N));
+      RLCA_TRY(check_aliasing(arrs, n));
+      a.cin = w.cin;
+      a.cout = w.cout;
+      a.cmap = w.cmap;
+      cp.slots = static_cast<unsigned long long *>(w.ws);
+      Args ac = a;
+      ac.T = a.T / cp.S;
+      RLCA_TRY(launch(algo, dtype, ac, stream, true, static_cast<int>(cp.S), &cp));
+      t_last_launches = 2;
+      return RLCA_OK;
+    }
+  }
   const int64_t S = split_count(N, a.T);
   const bool split = S > 1 && w.ws != nullptr;
   if (split) {
@@ -511,7 +656,11 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   a.cin = w.cin;
   a.cout = w.cout;
   a.cmap = w.cmap;
-  if (!split) return launch(algo, dtype, a, stream, w.on);
+  if (!split) {
+    RLCA_TRY(launch(algo, dtype, a, stream, w.on));
+    t_last_launches = 1;
+    return RLCA_OK;
+  }
 
   float *const ws = static_cast<float *>(w.ws);
   float *maps = ws, *cins = ws + 2 * N * S;
@@ -538,7 +687,9 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   a2.cin = cins;
   a2.cout = nullptr;
   a2.cmap = nullptr;
-  return launch(algo, dtype, a2, stream, true, static_cast<int>(S));
+  RLCA_TRY(launch(algo, dtype, a2, stream, true, static_cast<int>(S)));
+  t_last_launches = 3;
+  return RLCA_OK;
 }
 
 // The policy-table kernels: a 256-thread workgroup per row for long rows,
@@ -563,6 +714,7 @@ int launch_probs(int algo, int dtype, const Args &args, const TableArgs &tables,
       hipLaunchKernel(kernel, grid, block, kargs, 0, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   t_last_variant = -1;
+  t_last_launches = 1;
 #ifdef RLCA_TIMESTAMPS
   t_last_waves = static_cast<int64_t>(grid.x) * (kProbsBlock / 64);
   t_last_device = stamp_dev;
@@ -1153,10 +1305,18 @@ int rlca_gae_chunk_noalloc(int64_t num_envs, int64_t T, int dtype, const void *r
                   static_cast<long long>(4 * kScratchFloats));
     RLCA_TRY(scratch_on(stream, &ws));
   }
-  return gae_like(kGae, num_envs, T, dtype, rewards, ld_rewards, values, ld_values, terminated,
-                  ld_terminated, truncated, ld_truncated, trunc_values, ld_trunc_values, gamma,
-                  lam, advantages, ld_advantages, targets, ld_targets, "advantages", "targets",
-                  window_of(carry_in, carry_out, carry_map, ws, 4 * kScratchFloats), stream);
+  // Always the three-launch form of a split (the scratch array is sized for
+  // it).
+  const int chained = t_chained;
+  t_chained = 0;
+  const int rc = gae_like(kGae, num_envs, T, dtype, rewards, ld_rewards, values, ld_values,
+                          terminated, ld_terminated, truncated, ld_truncated, trunc_values,
+                          ld_trunc_values, gamma, lam, advantages, ld_advantages, targets,
+                          ld_targets, "advantages", "targets",
+                          window_of(carry_in, carry_out, carry_map, ws, 4 * kScratchFloats),
+                          stream);
+  t_chained = chained;
+  return rc;
 }
 
 int rlca_td_lambda_chunk(int64_t num_envs, int64_t T, int dtype, const void *rewards,
@@ -1331,8 +1491,9 @@ int rlca_vtrace_probs_chunk(int64_t num_envs, int64_t T, int64_t num_actions, in
 const char *rlca_last_error(void) { return t_last_error.c_str(); }
 
 // 0.5.0: T < 1 is an error; the split calls' workspace is an argument of the
-// window calls (no per-thread workspace).
-int rlca_version(void) { return 500; }
+// window calls (no per-thread workspace).  0.5.1: split calls in one pass (the
+// chained form), rlca_set_chained, rlca_last_launches.
+int rlca_version(void) { return 510; }
 
 int rlca_split_segments(int64_t num_envs, int64_t T) {
   if (num_envs < 0 || T < 1) {
@@ -1347,8 +1508,7 @@ int64_t rlca_split_workspace_bytes(int64_t num_envs, int64_t T) {
     fail(RLCA_EINVAL, "num_envs must be >= 0 and T >= 1");
     return -1;
   }
-  const int64_t S = split_count(num_envs, T);
-  return S > 1 ? 12 * num_envs * S : 0;
+  return split_workspace_bytes(num_envs, T);
 }
 
 int rlca_timestamps(uint64_t *dst, int64_t max_waves, int64_t *waves) {
@@ -1399,5 +1559,13 @@ int rlca_variant_info(int variant, int algo, int dtype, int *steps_per_lane_out,
 }
 
 int rlca_last_variant(void) { return t_last_variant; }
+
+int rlca_set_chained(int enable) {
+  const int prev = t_chained;
+  t_chained = enable != 0;
+  return prev;
+}
+
+int rlca_last_launches(void) { return t_last_launches; }
 
 }  // extern "C"

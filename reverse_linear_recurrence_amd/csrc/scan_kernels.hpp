@@ -93,6 +93,10 @@ struct Args {
   float *cout;
   float *cmap;
   int seg_count = 1;  // window instances: segments per row (gridDim.y; 1 unless split)
+  // Chained instances (split calls in one pass, see chain_lookback): the
+  // workspace, its epoch word (this call's tag) followed by the segments'
+  // published carry maps, 4 words per (row, segment).
+  unsigned long long *chain = nullptr;
 #ifdef RLCA_TIMESTAMPS
   uint64_t *stamps;   // instrumented build: per-wavefront wall-clock stamps
 #endif
@@ -797,13 +801,15 @@ struct WindowIn {
   bool done_last;
 };
 
-template <int A, typename InT, bool kU = false>
+template <int A, typename InT, bool kU = false, bool kReadCarry = true>
 __device__ __forceinline__ WindowIn window_in(const Args &p, const RowPtrs<InT> &rp, int64_t T,
                                               float &carry) {
   WindowIn w{0.f, false};
-  // The carry vectors hold one entry per segment (row-major over segments).
-  const int64_t row = late_row<kU>(rp.row) * late(p.seg_count) + blockIdx.y;
-  if (p.cin != nullptr) carry = p.cin[row];
+  if constexpr (kReadCarry) {
+    // The carry vectors hold one entry per segment (row-major over segments).
+    const int64_t row = late_row<kU>(rp.row) * late(p.seg_count) + blockIdx.y;
+    if (p.cin != nullptr) carry = p.cin[row];
+  }
   if constexpr (A == kRetrace) w.lr0 = Ld<InT>::one(rp.lr);
   if constexpr (Uses<A>::prev_flags)
     w.done_last = (rp.has_te && rp.te[T - 1] != 0) || (rp.has_tr && rp.tr[T - 1] != 0);
@@ -816,14 +822,22 @@ __device__ __forceinline__ WindowIn window_in(const Args &p, const RowPtrs<InT> 
 // recurrences hand on A_0 (Retrace: c_0 * A_0, the trace factor of step 0
 // applied); forward mirrors hand on A_{T-1}, or nothing when an episode ends
 // after step T-1; the generic scan hands on its last state unchanged.
+// The factor between a window's last scan state and the carry it hands on
+// (see window_out).
+template <int A>
+__device__ __forceinline__ float window_factor(const Args &p, const WindowIn &w) {
+  float f = 1.f;
+  if constexpr (A == kRetrace) f = p.lam * fminf(p.c_bar, __expf(w.lr0));
+  if constexpr (Uses<A>::prev_flags) f = w.done_last ? 0.f : 1.f;
+  return f;
+}
+
 template <int A, typename InT, bool kU = false>
 __device__ __forceinline__ void window_out(const Args &p, const RowPtrs<InT> &rp,
                                            const WindowIn &w, bool write, float carry,
                                            CarryMap m) {
   if (!write) return;
-  float f = 1.f;
-  if constexpr (A == kRetrace) f = p.lam * fminf(p.c_bar, __expf(w.lr0));
-  if constexpr (Uses<A>::prev_flags) f = w.done_last ? 0.f : 1.f;
+  const float f = window_factor<A>(p, w);
   const int64_t row = late_row<kU>(rp.row) * late(p.seg_count) + blockIdx.y;
   if (p.cout != nullptr) p.cout[row] = f * carry;
   if (p.cmap != nullptr) {
@@ -832,99 +846,16 @@ __device__ __forceinline__ void window_out(const Args &p, const RowPtrs<InT> &rp
   }
 }
 
-// One tile of one row group, inputs already loaded: build pairs, fold, scan,
-// carry, re-run, store.  Returns the carry for the next tile in scan order
-// (in every lane when need_carry; need_carry is false for the row's last
-// tile).  Window instances also fold the tile's composite into m in the
-// group's last lane in scan order, whose inclusive scan is that composite,
-// and after the row's last tile that lane writes the window results
-// (window_out) before the tile's outputs are stored.
-template <int A, typename InT, int K, int LPR, int WPR, bool kEdge, bool kChunk>
-__device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> &rp,
+// The end of a tile: re-run the lane's steps from the value entering its span
+// (xin) and write the tile's outputs, with the fused epilogue of each
+// algorithm.  al, be: the steps' coefficients; ratio: V-trace's e^{log_rho}.
+template <int A, typename InT, int K, int WPR, bool kEdge, bool kChunk>
+__device__ __forceinline__ void tile_epilogue(const Args &p, const RowPtrs<InT> &rp,
                                               const Tile<K> &x, int64_t t0, int64_t lim,
-                                              bool row_ok, int64_t c, bool need_carry, int lane,
-                                              int wave, float carry, float2 (*s_agg)[WPR],
-                                              CarryMap &m, const WindowIn &win,
-                                              bool write_window) {
-  constexpr int kScanLanes = WPR > 1 ? 64 : LPR;
+                                              bool row_ok, int lane, int wave,
+                                              const float (&al)[K], const float (&be)[K],
+                                              const float (&ratio)[K], float xin) {
   using U = Uses<A>;
-
-  float al[K], be[K], ratio[K];
-  coefficients<A, InT, K, kEdge, kChunk>(x, lim, p, al, be, ratio);
-
-  // Fold the lane's steps into one map of the incoming value: reverse,
-  // (a, b) = f_{t0} o ... o f_{t0+K-1}; forward, f_{t0+K-1} o ... o f_{t0}.
-  float a, b;
-  if constexpr (U::forward) {
-    a = al[0];
-    b = be[0];
-#pragma unroll
-    for (int j = 1; j < K; ++j) {
-      a = fmaf(be[j], a, al[j]);
-      b = be[j] * b;
-    }
-  } else {
-    a = al[K - 1];
-    b = be[K - 1];
-#pragma unroll
-    for (int j = K - 2; j >= 0; --j) {
-      a = fmaf(be[j], a, al[j]);
-      b = be[j] * b;
-    }
-  }
-
-  group_scan<kScanLanes>(a, b);
-
-  // Carry into this lane group's span and out of the tile.
-  float cin = carry;
-  float carry_out = 0.f;
-  if constexpr (WPR > 1) {
-    const int buf = static_cast<int>(c & 1);
-    const float wa = readlane(a, 63), wb = readlane(b, 63);  // whole-wavefront map
-    if (lane == 0) s_agg[buf][wave] = make_float2(wa, wb);
-    __syncthreads();
-    // Wavefront 0 holds the first span of the tile in scan order (reverse:
-    // the latest steps; forward: the earliest): compose from it onward.
-    // Lane w < WPR of every wavefront takes wavefront w's map, and a scan
-    // over those lanes leaves in lane w the composite of wavefronts 0 .. w.
-    const float2 ag = lane < WPR ? s_agg[buf][lane] : make_float2(0.f, 1.f);
-    float sa = ag.x, sb = ag.y;
-    group_scan<WPR>(sa, sb);
-    const int w = __builtin_amdgcn_readfirstlane(wave);
-    const int wp = w > 0 ? w - 1 : 0;
-    const float pa = readlane(sa, wp), pb = readlane(sb, wp);  // wavefronts 0 .. w-1
-    if (w > 0) cin = fmaf(pb, carry, pa);
-    const float ta = readlane(sa, WPR - 1), tb = readlane(sb, WPR - 1);
-    const float xc = fmaf(tb, carry, ta);
-    CarryMap tm{ta, tb};  // the tile's composite
-    carry_out = xc;
-    if constexpr (kChunk) {
-      m.a = fmaf(tm.b, m.a, tm.a);
-      m.b = tm.b * m.b;
-      if (!need_carry) window_out<A, InT, (WPR > 1)>(p, rp, win, write_window, xc, m);
-    }
-  }
-  // A at the far end of this lane's span (reverse: its earliest step;
-  // forward: its latest) ...
-  const float y = fmaf(b, cin, a);
-  // ... and the value entering the lane's span: y of the previous lane in
-  // scan order (lane - 1), the next-later (reverse) or next-earlier (forward)
-  // span.
-  float xin = dpp<0x138, 0xf>(y, cin);  // wave_shr:1
-  if ((lane % kScanLanes) == 0) xin = cin;
-  if constexpr (WPR == 1) {
-    if (need_carry) {
-      if constexpr (LPR == 64) carry_out = readlane(y, 63);
-      else carry_out = lane_shuffle(y, (lane / LPR) * LPR + LPR - 1);
-    }
-    if constexpr (kChunk) {
-      // Meaningful in the group's last lane only (see above).
-      m.a = fmaf(b, m.a, a);
-      m.b = b * m.b;
-      if (!need_carry) window_out<A, InT, (WPR > 1)>(p, rp, win, write_window, y, m);
-    }
-  }
-
   // Re-run the lane's steps from its incoming value; fused epilogue.
   const float gamma = late(p.gamma);
   const float pg_rho_bar = A == kVtrace ? late(p.pg_rho_bar) : 1.f;
@@ -1036,7 +967,262 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
         if (has_o1) o1_row[t0 + e] = o1[e];
       }
   }
+}
+
+// One tile of one row group, inputs already loaded: build pairs, fold, scan,
+// carry, re-run, store.  Returns the carry for the next tile in scan order
+// (in every lane when need_carry; need_carry is false for the row's last
+// tile).  Window instances also fold the tile's composite into m in the
+// group's last lane in scan order, whose inclusive scan is that composite,
+// and after the row's last tile that lane writes the window results
+// (window_out) before the tile's outputs are stored.
+template <int A, typename InT, int K, int LPR, int WPR, bool kEdge, bool kChunk>
+__device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> &rp,
+                                              const Tile<K> &x, int64_t t0, int64_t lim,
+                                              bool row_ok, int64_t c, bool need_carry, int lane,
+                                              int wave, float carry, float2 (*s_agg)[WPR],
+                                              CarryMap &m, const WindowIn &win,
+                                              bool write_window) {
+  constexpr int kScanLanes = WPR > 1 ? 64 : LPR;
+  using U = Uses<A>;
+
+  float al[K], be[K], ratio[K];
+  coefficients<A, InT, K, kEdge, kChunk>(x, lim, p, al, be, ratio);
+
+  // Fold the lane's steps into one map of the incoming value: reverse,
+  // (a, b) = f_{t0} o ... o f_{t0+K-1}; forward, f_{t0+K-1} o ... o f_{t0}.
+  float a, b;
+  if constexpr (U::forward) {
+    a = al[0];
+    b = be[0];
+#pragma unroll
+    for (int j = 1; j < K; ++j) {
+      a = fmaf(be[j], a, al[j]);
+      b = be[j] * b;
+    }
+  } else {
+    a = al[K - 1];
+    b = be[K - 1];
+#pragma unroll
+    for (int j = K - 2; j >= 0; --j) {
+      a = fmaf(be[j], a, al[j]);
+      b = be[j] * b;
+    }
+  }
+
+  group_scan<kScanLanes>(a, b);
+
+  // Carry into this lane group's span and out of the tile.
+  float cin = carry;
+  float carry_out = 0.f;
+  if constexpr (WPR > 1) {
+    const int buf = static_cast<int>(c & 1);
+    const float wa = readlane(a, 63), wb = readlane(b, 63);  // whole-wavefront map
+    if (lane == 0) s_agg[buf][wave] = make_float2(wa, wb);
+    __syncthreads();
+    // Wavefront 0 holds the first span of the tile in scan order (reverse:
+    // the latest steps; forward: the earliest): compose from it onward.
+    // Lane w < WPR of every wavefront takes wavefront w's map, and a scan
+    // over those lanes leaves in lane w the composite of wavefronts 0 .. w.
+    const float2 ag = lane < WPR ? s_agg[buf][lane] : make_float2(0.f, 1.f);
+    float sa = ag.x, sb = ag.y;
+    group_scan<WPR>(sa, sb);
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    const int wp = w > 0 ? w - 1 : 0;
+    const float pa = readlane(sa, wp), pb = readlane(sb, wp);  // wavefronts 0 .. w-1
+    if (w > 0) cin = fmaf(pb, carry, pa);
+    const float ta = readlane(sa, WPR - 1), tb = readlane(sb, WPR - 1);
+    const float xc = fmaf(tb, carry, ta);
+    CarryMap tm{ta, tb};  // the tile's composite
+    carry_out = xc;
+    if constexpr (kChunk) {
+      m.a = fmaf(tm.b, m.a, tm.a);
+      m.b = tm.b * m.b;
+      if (!need_carry) window_out<A, InT, (WPR > 1)>(p, rp, win, write_window, xc, m);
+    }
+  }
+  // A at the far end of this lane's span (reverse: its earliest step;
+  // forward: its latest) ...
+  const float y = fmaf(b, cin, a);
+  // ... and the value entering the lane's span: y of the previous lane in
+  // scan order (lane - 1), the next-later (reverse) or next-earlier (forward)
+  // span.
+  float xin = dpp<0x138, 0xf>(y, cin);  // wave_shr:1
+  if ((lane % kScanLanes) == 0) xin = cin;
+  if constexpr (WPR == 1) {
+    if (need_carry) {
+      if constexpr (LPR == 64) carry_out = readlane(y, 63);
+      else carry_out = lane_shuffle(y, (lane / LPR) * LPR + LPR - 1);
+    }
+    if constexpr (kChunk) {
+      // Meaningful in the group's last lane only (see above).
+      m.a = fmaf(b, m.a, a);
+      m.b = b * m.b;
+      if (!need_carry) window_out<A, InT, (WPR > 1)>(p, rp, win, write_window, y, m);
+    }
+  }
+
+  tile_epilogue<A, InT, K, WPR, kEdge, kChunk>(p, rp, x, t0, lim, row_ok, lane, wave, al, be,
+                                              ratio, xin);
   return carry_out;
+}
+
+// ---------------------------------------------------- chained (one-pass) split
+//
+// A split call's segments in one pass: workgroup (row, k) takes the k-th
+// segment of its row in scan order (from the row's end for reverse
+// recurrences, from its start for forward ones), k = blockIdx.y.  It loads
+// and scans its segment without a carry (tile_scan), publishes the segment's
+// carry map, finds the carry entering its segment from the maps of the
+// segments before it in scan order (chain_lookback), publishes the carry map
+// from the row's incoming carry to its own outgoing one, then writes its
+// outputs (tile_emit).  The inputs are read once; the carry maps are the
+// window calls' (window_out), composed as the split calls compose them.
+//
+// Each published value is one 64-bit word, written and read with relaxed
+// device-scope atomics (coherent across the chip's L2 caches): the value's
+// bits in the low half and the call's tag in the high half, so a word is
+// either wholly this call's or not yet written by it.  The tag is the
+// workspace's epoch word, which a one-thread kernel (chain_epoch, rlca.hip) advances
+// before every chained launch (also on every replay of a captured graph), so
+// that no word an earlier call left is taken for one of this call.  A
+// workgroup reads only the words of workgroups of its row with a smaller k,
+// which have smaller linear workgroup ids and were dispatched no later; the
+// poll is bounded all the same (kChainMaxPolls), and a carry not found by then
+// is NaN.
+
+constexpr int kChainMaxPolls = 1 << 16;
+constexpr int kChainMaxSegments = 64;  // one wavefront composes the look-back
+
+// A lane's state after the carry-free scan of a whole tile (WPR > 1): its
+// inclusive map within the wavefront (a, b), the composite of the wavefronts
+// before it in the tile (pa, pb; first: it is the first), and the tile's
+// composite (ta, tb).
+struct TileScan {
+  float a, b, pa, pb, ta, tb;
+  bool first;
+};
+
+template <int A, typename InT, int K, int WPR>
+__device__ __forceinline__ TileScan tile_scan(const Args &p, const Tile<K> &x, int64_t lim,
+                                              int64_t c, int lane, int wave,
+                                              float2 (*s_agg)[WPR]) {
+  using U = Uses<A>;
+  float al[K], be[K], ratio[K];
+  coefficients<A, InT, K, false, true>(x, lim, p, al, be, ratio);
+  float a, b;
+  if constexpr (U::forward) {
+    a = al[0];
+    b = be[0];
+#pragma unroll
+    for (int j = 1; j < K; ++j) {
+      a = fmaf(be[j], a, al[j]);
+      b = be[j] * b;
+    }
+  } else {
+    a = al[K - 1];
+    b = be[K - 1];
+#pragma unroll
+    for (int j = K - 2; j >= 0; --j) {
+      a = fmaf(be[j], a, al[j]);
+      b = be[j] * b;
+    }
+  }
+  group_scan<64>(a, b);
+  const int buf = static_cast<int>(c & 1);
+  const float wa = readlane(a, 63), wb = readlane(b, 63);
+  if (lane == 0) s_agg[buf][wave] = make_float2(wa, wb);
+  __syncthreads();
+  const float2 ag = lane < WPR ? s_agg[buf][lane] : make_float2(0.f, 1.f);
+  float sa = ag.x, sb = ag.y;
+  group_scan<WPR>(sa, sb);
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  const int wp = w > 0 ? w - 1 : 0;
+  TileScan s;
+  s.a = a;
+  s.b = b;
+  s.pa = readlane(sa, wp);
+  s.pb = readlane(sb, wp);
+  s.ta = readlane(sa, WPR - 1);
+  s.tb = readlane(sb, WPR - 1);
+  s.first = w == 0;
+  return s;
+}
+
+// The outputs of a tile scanned by tile_scan, given the carry entering it;
+// returns the carry it hands on.
+template <int A, typename InT, int K, int WPR>
+__device__ __forceinline__ float tile_emit(const Args &p, const RowPtrs<InT> &rp,
+                                           const Tile<K> &x, int64_t t0, int64_t lim, bool row_ok,
+                                           int lane, int wave, float carry, const TileScan &s) {
+  const float cin = s.first ? carry : fmaf(s.pb, carry, s.pa);
+  const float y = fmaf(s.b, cin, s.a);
+  float xin = dpp<0x138, 0xf>(y, cin);  // wave_shr:1
+  if (lane == 0) xin = cin;
+  float al[K], be[K], ratio[K];
+  coefficients<A, InT, K, false, true>(x, lim, p, al, be, ratio);
+  tile_epilogue<A, InT, K, WPR, false, true>(p, rp, x, t0, lim, row_ok, lane, wave, al, be, ratio,
+                                             xin);
+  return fmaf(s.tb, carry, s.ta);
+}
+
+__device__ __forceinline__ unsigned long long chain_word(float v, uint32_t tag) {
+  return (static_cast<unsigned long long>(tag) << 32) | __float_as_uint(v);
+}
+
+__device__ __forceinline__ void chain_put(unsigned long long *w, float v, uint32_t tag) {
+  __hip_atomic_store(w, chain_word(v, tag), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wavefront 0 of workgroup (row, k > 0): the map from the row's incoming carry
+// to the carry entering segment k, (ra, rb), from the words of segments
+// 0 .. k-1 (slots: the row's first word).  Per segment j: words 0, 1 the
+// segment's own carry map, words 2, 3 the map from the row's incoming carry to
+// the carry it hands on (segment 0 publishes only these).  Lane j < k reads
+// segment j's four words; the latest j whose words 2, 3 are this call's, with
+// words 0, 1 of every later j < k, composes the answer in one scan.  Returns
+// false if the words were not all there within kChainMaxPolls polls.
+__device__ __forceinline__ bool chain_lookback(unsigned long long *slots, uint32_t tag, int k,
+                                               int lane, float &ra, float &rb) {
+  for (int it = 0; it < kChainMaxPolls; ++it) {
+    unsigned long long w0 = 0, w1 = 0, w2 = 0, w3 = 0;
+    if (lane < k) {
+      unsigned long long *s = slots + 4 * lane;
+      w2 = __hip_atomic_load(s + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w3 = __hip_atomic_load(s + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w0 = __hip_atomic_load(s + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      w1 = __hip_atomic_load(s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    auto mine = [&](unsigned long long w) { return static_cast<uint32_t>(w >> 32) == tag; };
+    const bool inc = lane < k && mine(w2) && mine(w3);
+    const bool agg = lane < k && mine(w0) && mine(w1);
+    const unsigned long long inc_mask = __ballot(inc);
+    const unsigned long long agg_mask = __ballot(agg);
+    if (inc_mask != 0) {
+      const int j0 = 63 - __clzll(static_cast<long long>(inc_mask));
+      // lanes j0+1 .. k-1 need their own maps
+      const unsigned long long below_k = k >= 64 ? ~0ull : (1ull << k) - 1;
+      const unsigned long long need = below_k & ~((2ull << j0) - 1);
+      if ((agg_mask & need) == need) {
+        float a = 0.f, b = 1.f;  // identity below j0
+        if (lane == j0) {
+          a = __uint_as_float(static_cast<uint32_t>(w2));
+          b = __uint_as_float(static_cast<uint32_t>(w3));
+        } else if (lane > j0 && lane < k) {
+          a = __uint_as_float(static_cast<uint32_t>(w0));
+          b = __uint_as_float(static_cast<uint32_t>(w1));
+        }
+        group_scan<64>(a, b);  // lane i: f_i o ... o f_0
+        ra = readlane(a, k - 1);
+        rb = readlane(b, k - 1);
+        return true;
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  ra = __int_as_float(0x7fc00000);
+  rb = ra;
+  return false;
 }
 
 // Algo A, input type InT, K steps per lane, LPR lanes per row inside one
@@ -1059,7 +1245,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 // duplicate fields of p.  kChunk: window instance (carry vector in, carry and
 // carry map out).
 template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk,
-          int kTiles = 0, bool kAligned = false>
+          int kTiles = 0, bool kAligned = false, bool kChain = false>
 __global__ void __launch_bounds__(64 * short_row_waves(WPR, LPR, kChunk))
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
             int N32, int T32, int ldT, int ldX, const Args p) {
@@ -1093,7 +1279,13 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
   // grid row per segment, and workgroups of grid row y take segment y, T
   // steps long, of their rows (no argument is read before the loads).
   const int64_t src = rr;
-  const int64_t seg_off = kChunk ? static_cast<int64_t>(blockIdx.y) * T : 0;
+  // Chained instances of reverse recurrences take the segments from the
+  // row's end: the host passes every row pointer moved to the row's last
+  // segment, and segment y starts y segments before it.
+  const int64_t seg_off =
+      kChunk ? (kChain && !Uses<A>::forward ? -static_cast<int64_t>(blockIdx.y) * T
+                                            : static_cast<int64_t>(blockIdx.y) * T)
+             : 0;
   // Row stride of a hot stream: the preloaded common stride, or (mixed
   // strides) the stream's own stride from Args.
   auto ld = [&](int64_t own_ld) -> int64_t { return kUniform ? static_cast<int64_t>(ldT) : own_ld; };
@@ -1196,7 +1388,78 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
                                                      false, lane, wave, carry, s_agg, m, win,
                                                      write_window);
   };
-  if constexpr (kTiles == 1) {
+  if constexpr (kChain) {
+    // One segment of a split call (see chain_lookback): its tiles scanned
+    // without a carry, the segment's carry map published, the carry entering
+    // the segment found, then the outputs.
+    static_assert(kChunk && WPR > 1 && (kTiles == 1 || kTiles == 2),
+                  "chained instances: whole-wavefront rows of one or two tiles");
+    __shared__ float s_chain[2];
+    constexpr int64_t kFirst = kTiles == 1 || Uses<A>::forward ? 0 : 1;
+    constexpr int64_t kSecond = 1 - kFirst;
+    Tile<K> xf, xs;
+    float unused = 0.f;
+    issue_tile<A, InT, K>(p, rp, t0_of(kFirst), T - t0_of(kFirst), xf);
+    win = window_in<A, InT, true, false>(p, rp, T, unused);
+    finish_tile<A, InT, K>(p, rp, t0_of(kFirst), xf);
+    if constexpr (kTiles == 2) issue_tile<A, InT, K>(p, rp, t0_of(kSecond), T - t0_of(kSecond), xs);
+    const TileScan sf = tile_scan<A, InT, K, WPR>(p, xf, T - t0_of(kFirst), kFirst, lane, wave,
+                                                  s_agg);
+    TileScan ss{};
+    if constexpr (kTiles == 2) {
+      finish_tile<A, InT, K>(p, rp, t0_of(kSecond), xs);
+      ss = tile_scan<A, InT, K, WPR>(p, xs, T - t0_of(kSecond), kSecond, lane, wave, s_agg);
+    }
+    // The segment's carry map: its tiles' composites in scan order, times
+    // the factor between its last scan state and the carry it hands on.
+    float ma = sf.ta, mb = sf.tb;
+    if constexpr (kTiles == 2) {
+      ma = fmaf(ss.tb, ma, ss.ta);
+      mb = ss.tb * mb;
+    }
+    const float f = window_factor<A>(p, win);
+    ma *= f;
+    mb *= f;
+    const int k = static_cast<int>(blockIdx.y);
+    const int S = late(p.seg_count);
+    unsigned long long *slots = p.chain + 1 + row * 4 * static_cast<int64_t>(S);
+    const uint32_t tag = static_cast<uint32_t>(
+        __hip_atomic_load(p.chain, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const float c_row = p.cin != nullptr ? p.cin[row] : 0.f;
+    if (wave == 0) {
+      // (ra, rb): the row's incoming carry -> the carry entering this segment
+      float ra = 0.f, rb = 1.f;
+      if (k > 0) {
+        if (lane == 0) {
+          chain_put(slots + 4 * k, ma, tag);
+          chain_put(slots + 4 * k + 1, mb, tag);
+        }
+        chain_lookback(slots, tag, k, lane, ra, rb);
+      }
+      const float pa = fmaf(mb, ra, ma), pb = mb * rb;  // ... -> the carry it hands on
+      if (lane == 0) {
+        chain_put(slots + 4 * k + 2, pa, tag);
+        chain_put(slots + 4 * k + 3, pb, tag);
+        s_chain[0] = ra;
+        s_chain[1] = rb;
+        if (k == S - 1) {
+          if (p.cout != nullptr) p.cout[row] = fmaf(pb, c_row, pa);
+          if (p.cmap != nullptr) {
+            p.cmap[2 * row] = pa;
+            p.cmap[2 * row + 1] = pb;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const float c_seg = fmaf(s_chain[1], c_row, s_chain[0]);
+    const float c_next = tile_emit<A, InT, K, WPR>(p, rp, xf, t0_of(kFirst), T - t0_of(kFirst),
+                                                   row_ok, lane, wave, c_seg, sf);
+    if constexpr (kTiles == 2)
+      tile_emit<A, InT, K, WPR>(p, rp, xs, t0_of(kSecond), T - t0_of(kSecond), row_ok, lane,
+                                wave, c_next, ss);
+    (void)c_next;
+  } else if constexpr (kTiles == 1) {
     one_tile();
   } else if constexpr (kTiles == 2) {
     // Two whole tiles, both tiles' loads in flight: the tile computed first

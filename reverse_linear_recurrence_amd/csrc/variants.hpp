@@ -64,6 +64,10 @@ inline int64_t tile_steps(const Variant &v, bool bf16, bool vtrace) {
 // window_kernel: carry vector in, carry and carry map out (every Algo).
 const void *plain_kernel(int algo, int dtype, int variant, bool uniform, int tiles, bool aligned);
 const void *window_kernel(int algo, int dtype, int variant, bool uniform);
+// chain_kernel: the chained instance (one-launch split call) for segments of
+// `tiles` (1 or 2) whole tiles of a whole-wavefront tiling (variants 3-8,
+// uniform row stride); NULL otherwise.
+const void *chain_kernel(int algo, int dtype, int variant, int tiles);
 // The policy-table kernels (Retrace, V-trace), 256-thread workgroups: 4
 // wavefronts per row (1024-step tiles, one row per workgroup) or 1 (256-step
 // tiles, four rows per workgroup).

@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import reverse_linear_recurrence_amd as rl
+from split_rules import chain_segments
 from reverse_linear_recurrence_amd import _binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -344,7 +345,20 @@ def test_split_segments_rule(lib):
              (2, 32769): 1, (2, 2 * 32769): 2, (0, 1): 1}
     for (N, T), S in cases.items():
         assert rl.rlca_split_segments(N, T) == S, (N, T)
-        assert rl.rlca_split_workspace_bytes(N, T) == (12 * N * S if S > 1 else 0), (N, T)
+        chained = max(8 + 32 * N * chain_segments(N, T, dt, algo) if chain_segments(
+            N, T, dt, algo) else 0 for dt in (torch.float32, torch.bfloat16)
+            for algo in ("gae", "vtrace"))
+        assert rl.rlca_split_workspace_bytes(N, T) == max(12 * N * S if S > 1 else 0,
+                                                          chained), (N, T)
+    # the chained form's segments: one or two whole tiles of a whole-wavefront
+    # tiling, at most 64 per row
+    assert chain_segments(16, 262144, torch.float32, "gae") == 32  # 2 tiles of 4096
+    assert chain_segments(16, 262144, torch.bfloat16, "gae") == 16  # 2 tiles of 8192
+    assert chain_segments(64, 65536, torch.bfloat16, "gae") == 4
+    assert chain_segments(1, 32768, torch.float32, "gae") == 32  # 1 tile of 1024
+    assert chain_segments(1, 1 << 20, torch.bfloat16, "gae") == 64
+    assert chain_segments(65, 65536, torch.float32, "gae") == 0
+    assert chain_segments(2, 32769, torch.float32, "gae") == 0
     # at most 64 rows split, into fewer than 512 segments in all
     assert max(N * rl.rlca_split_segments(N, 1 << 24) for N in range(1, 65)) < 512
     for bad in ((-1, 8), (4, 0)):
@@ -364,12 +378,14 @@ def test_workspace_is_validated(lib):
     # checks its 3 * 16 * 16 floats of workspace before any launch.
     N, T = 16, 65536
     need = rl.rlca_split_workspace_bytes(N, T)
-    assert need == 12 * N * 16
+    assert need == 8 + 32 * N * 16  # the chained form's, above the three-launch form's
     assert gae_chunk(lib, N=N, T=T, ws=WS + 2, ws_bytes=need) == rl.RLCA_EINVAL
     assert "aligned" in err(lib)
     assert gae_chunk(lib, N=N, T=T, ws=WS, ws_bytes=-4) == rl.RLCA_EINVAL
     assert "negative" in err(lib)
-    assert gae_chunk(lib, N=N, T=T, ws=WS, ws_bytes=need - 4) == rl.RLCA_EINVAL
+    # below what the three-launch form needs (a size that fits only that form
+    # selects it)
+    assert gae_chunk(lib, N=N, T=T, ws=WS, ws_bytes=12 * N * 16 - 4) == rl.RLCA_EINVAL
     assert "rlca_split_workspace_bytes" in err(lib)
     # overlapping an output, an input
     assert gae_chunk(lib, N=N, T=T, ws=ADV + 64, ws_bytes=need) == rl.RLCA_EALIAS

@@ -1,15 +1,19 @@
 """Split calls (few long rows) on the GPU against the oracle.
 
 A window call (rlca_X_chunk or the generic scan) given a workspace, on at most
-64 rows of at least 32768 steps, cuts each row into S segments and runs them
-as N * S rows of the window kernels (maps only, compose, outputs): the window
+64 rows of at least 32768 steps, cuts each row into segments: the window
 calls' split along T inside one library call (the operator of the rl-triton
 pages' Method 1 is associative, so the pieces join through their carry maps).
-The results must match the oracle to the same tolerance as an unsplit call,
-for every algorithm, with episode boundaries that fall inside and exactly at
-segment borders and with carries that cross every border (no boundaries),
-from 8 segments per row up to the 256 that rlca_split_segments allows, where
-the composition walks its 64-segment chunks one after another.
+Every test runs both forms: the chained one (one pass: each segment's
+workgroup publishes its carry map and composes the published maps of the
+segments before it; up to 64 segments per row) and the three-launch one (maps
+only, compose, outputs; rlca_set_chained(False)), which takes over where the
+chained one does not apply.  The results must match the oracle to the same
+tolerance as an unsplit call, for every algorithm, with episode boundaries
+that fall inside and exactly at segment borders and with carries that cross
+every border (no boundaries), from 8 segments per row up to the 256 that
+rlca_split_segments allows, where the composition walks its 64-segment chunks
+one after another.
 """
 import numpy as np
 import pytest
@@ -19,10 +23,18 @@ import oracle
 import reverse_linear_recurrence_amd as rl
 from gpu_common import (ALGOS, DEFAULT_PARAMS, TOL, assert_close, params32, random_inputs,
                         run_oracle, to_device)
+from split_rules import takes_chained
 from test_gpu_window import (affine_inputs, check_window, run_gpu_chunk, run_oracle_chunk,
                              window_inputs)
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["chained", "three"], autouse=True)
+def form(request):
+    prev = rl.rlca_set_chained(request.param == "chained")
+    yield request.param
+    rl.rlca_set_chained(prev)
 
 
 def workspace_for(N, T):
@@ -32,10 +44,19 @@ def workspace_for(N, T):
     return ws
 
 
-def assert_split(ws, N, T):
-    S = rl.rlca_split_segments(N, T)
-    maps = ws[:2 * N * S].cpu().numpy()
-    assert np.all(np.isfinite(maps)), "the call did not split"
+def assert_split(ws, N, T, dtype="f32", algo="gae"):
+    """The call split, in the form the thread's setting and the shape select."""
+    chained = rl.rlca_set_chained(True)
+    rl.rlca_set_chained(chained)
+    if chained and takes_chained(N, T, dtype, "vtrace" if algo == "vtrace" else "gae"):
+        assert rl.rlca_last_launches() == 2, "the call did not take the chained form"
+        epoch = ws[:2].view(torch.int32).cpu().numpy()
+        assert epoch[0] != 0 and epoch[1] == 0, "the chained call did not advance its epoch"
+    else:
+        assert rl.rlca_last_launches() == 3, "the call did not take the three-launch form"
+        S = rl.rlca_split_segments(N, T)
+        maps = ws[:2 * N * S].cpu().numpy()
+        assert np.all(np.isfinite(maps)), "the call did not split"
 
 
 def padded(d, pad):
@@ -71,7 +92,7 @@ def test_split_call_matches_oracle(algo, dtype):
         ws = workspace_for(N, T)
         print(algo, dtype, "N", N, "T", T, "boundary rate", p_b, flush=True)
         got = plain_by_window(algo, to_device(host), p, ws)
-        assert_split(ws, N, T)
+        assert_split(ws, N, T, dtype, algo)
         assert_close(got, ref, TOL[dtype], "%s/%s/split p=%g" % (algo, dtype, p_b))
 
 
@@ -84,7 +105,7 @@ def test_split_call_with_padded_rows(algo):
     ref = run_oracle(algo, host, p)
     ws = workspace_for(N, T)
     got = plain_by_window(algo, padded(to_device(host), 37), p, ws)
-    assert_split(ws, N, T)
+    assert_split(ws, N, T, "f32", algo)
     assert_close(got, ref, TOL["f32"], "%s/split/padded" % algo)
 
 
@@ -98,10 +119,11 @@ def test_no_split_for_indivisible_rows_and_small_workspaces():
     got = plain_by_window("gae", to_device(host), p, ws)
     assert torch.isnan(ws).all()
     assert_close(got, run_oracle("gae", host, p), TOL["f32"], "gae/odd T")
-    # A call that splits, given a workspace one float short: refused before
-    # any launch, nothing written.
-    need = rl.rlca_split_workspace_bytes(3, 32768)
-    assert need == 12 * 3 * 8
+    # A call that splits, given a workspace one float short of the
+    # three-launch form's (the smaller form's): refused before any launch,
+    # nothing written.
+    need = 12 * 3 * rl.rlca_split_segments(3, 32768)
+    assert need == 12 * 3 * 8 and rl.rlca_split_workspace_bytes(3, 32768) >= need
     short = torch.full((need // 4 - 1,), float("nan"), device="cuda")
     dev = to_device(random_inputs("gae", 3, 32768, 91, "f32"))
     adv = torch.full((3, 32768), float("nan"), device="cuda")
@@ -125,7 +147,7 @@ def test_split_and_unsplit_calls_agree():
     assert rl.rlca_split_segments(N, T) == 16
     ws = workspace_for(N, T)
     split = run_gpu_chunk("td_lambda", dev, p, c, workspace=ws)
-    assert_split(ws, N, T)
+    assert_split(ws, N, T, "bf16", "td_lambda")
     check_window(split, plain, "f32", "td_lambda/split vs unsplit")
 
 
@@ -140,7 +162,7 @@ def test_split_window_call_matches_oracle(algo, dtype):
         ws = workspace_for(N, T)
         print(algo, dtype, "window N", N, "T", T, "sparse", sparse, flush=True)
         got = run_gpu_chunk(algo, to_device(d), p, c.cuda(), workspace=ws)
-        assert_split(ws, N, T)
+        assert_split(ws, N, T, dtype, algo)
         check_window(got, run_oracle_chunk(algo, d, p, c), dtype,
                      "%s/%s split window sparse=%s" % (algo, dtype, sparse))
 
@@ -203,12 +225,12 @@ def test_many_segments_match_oracle(algo, dtype, N, T, S):
         print(algo, dtype, "N", N, "T", T, "S", S, form, flush=True)
         if form == "plain":
             got = plain_by_window(algo, to_device(d), p, ws)
-            assert_split(ws, N, T)
+            assert_split(ws, N, T, dtype, algo)
             assert_close(got, run_oracle(algo, d, p), TOL[dtype],
                          "%s/%s S=%d plain" % (algo, dtype, S))
         else:
             got = run_gpu_chunk(algo, to_device(d), p, c.cuda(), workspace=ws)
-            assert_split(ws, N, T)
+            assert_split(ws, N, T, dtype, algo)
             check_window(got, run_oracle_chunk(algo, d, p, c), dtype,
                          "%s/%s S=%d window" % (algo, dtype, S))
 
@@ -233,7 +255,7 @@ def test_many_segments_affine_scan(reverse, dtype, N, T, S):
                                         carry_in=None if cin is None else cin.cuda(),
                                         workspace=ws)
         torch.cuda.synchronize()
-        assert_split(ws, N, T)
+        assert_split(ws, N, T, dtype)
         rA, rco, rcm = oracle.affine_scan(al, be, rs if p_reset else None, cin, reverse=reverse)
         got = ({"A": A.double().cpu().numpy()}, co.double().cpu().numpy(),
                cm.double().cpu().numpy())

@@ -6,7 +6,8 @@ Two calls in a row on one device, the second on a smaller input, both large
 enough to split (the library's scratch array then holds the first call's
 segment maps when the second begins); then a call too short to split.  Each
 result must equal rlca_gae_chunk's bitwise (the same kernels run the same
-split) and match the oracle at the fp32 bar (max|err| <= 1e-4 max|ref|).
+three-launch split, which the no-allocation call always takes) and match the
+oracle at the fp32 bar (max|err| <= 1e-4 max|ref|).
 """
 import numpy as np
 import pytest
@@ -44,7 +45,11 @@ def test_noalloc_call_equals_the_workspace_call_twice_in_a_row():
               flush=True)
         got = call(rl.rlca_gae_chunk_noalloc, d, p, cin.cuda())
         ws = rl.split_workspace(N, T)
-        ref_gpu = call(rl.rlca_gae_chunk, d, p, cin.cuda(), workspace=ws)
+        prev = rl.rlca_set_chained(False)  # the form the no-allocation call takes
+        try:
+            ref_gpu = call(rl.rlca_gae_chunk, d, p, cin.cuda(), workspace=ws)
+        finally:
+            rl.rlca_set_chained(prev)
         for k in got:
             assert torch.equal(got[k], ref_gpu[k]), "call %d: %s differs from rlca_gae_chunk" % (i, k)
         a, t, co, cm = oracle.gae(host["rewards"], host["values"], host["terminated"],
