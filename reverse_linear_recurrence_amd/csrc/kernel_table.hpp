@@ -42,19 +42,17 @@ const void *fixed_tiles_ptr(int v, bool aligned) {
 
 // tiles: 1 or 2 for the instances of rows of exactly one or two whole tiles
 // (0: the general instance), aligned: their twins for 4-byte aligned flag
-// rows (reverse recurrences); they exist for the plain instances (C false)
-// with a uniform row stride.
+// rows (reverse recurrences and the generic scan); they exist for the plain
+// and the window instances with a uniform row stride.
 template <int A, bool C>
 const void *kernel_ptr(int dtype, int v, bool uniform, int tiles = 0, bool aligned = false) {
-  if constexpr (!C) {
-    if (uniform && tiles == 1) {
-      return dtype == RLCA_BF16 ? fixed_tiles_ptr<A, bf16_t, C, 1>(v, aligned)
-                                : fixed_tiles_ptr<A, float, C, 1>(v, aligned);
-    }
-    if (uniform && tiles == 2) {
-      return dtype == RLCA_BF16 ? fixed_tiles_ptr<A, bf16_t, C, 2>(v, aligned)
-                                : fixed_tiles_ptr<A, float, C, 2>(v, aligned);
-    }
+  if (uniform && tiles == 1) {
+    return dtype == RLCA_BF16 ? fixed_tiles_ptr<A, bf16_t, C, 1>(v, aligned)
+                              : fixed_tiles_ptr<A, float, C, 1>(v, aligned);
+  }
+  if (uniform && tiles == 2) {
+    return dtype == RLCA_BF16 ? fixed_tiles_ptr<A, bf16_t, C, 2>(v, aligned)
+                              : fixed_tiles_ptr<A, float, C, 2>(v, aligned);
   }
   if (dtype == RLCA_BF16)
     return uniform ? kernel_ptr<A, bf16_t, true, C>(v) : kernel_ptr<A, bf16_t, false, C>(v);

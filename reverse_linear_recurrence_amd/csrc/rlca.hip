@@ -347,7 +347,7 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
       ((a.term != nullptr && a.trunc != nullptr) || rows_aligned(a.r, a.ld_r, es));
   const void *kernel = chain != nullptr ? (uniform ? chain_kernel(algo, dtype, v, chain->tiles)
                                                    : nullptr)
-                       : window ? window_kernel(algo, dtype, v, uniform)
+                       : window ? window_kernel(algo, dtype, v, uniform, tiles, flags_aligned)
                                 : plain_kernel(algo, dtype, v, uniform, tiles, flags_aligned);
   if (kernel == nullptr) return fail(RLCA_EINVAL, "no kernel for algorithm %d", algo);
   const hipError_t e = hipLaunchKernel(kernel, grid, block, kargs, 0,

@@ -60,10 +60,12 @@ inline int64_t tile_steps(const Variant &v, bool bf16, bool vtrace) {
 // windowed entry points without carries (every Algo but the generic scan),
 // tiles: 1 or 2 for the instance of rows of exactly that many whole tiles
 // (uniform strides only; otherwise, and for 0, the general instance),
-// aligned: with every flag row 4-byte aligned (reverse recurrences);
-// window_kernel: carry vector in, carry and carry map out (every Algo).
+// aligned: with every flag row 4-byte aligned (reverse recurrences and the
+// generic scan); window_kernel: carry vector in, carry and carry map out
+// (every Algo), with the same choices.
 const void *plain_kernel(int algo, int dtype, int variant, bool uniform, int tiles, bool aligned);
-const void *window_kernel(int algo, int dtype, int variant, bool uniform);
+const void *window_kernel(int algo, int dtype, int variant, bool uniform, int tiles,
+                          bool aligned);
 // chain_kernel: the chained instance (one-launch split call) for segments of
 // `tiles` (1 or 2) whole tiles of a whole-wavefront tiling (variants 3-8,
 // uniform row stride); NULL otherwise.

@@ -18,6 +18,7 @@ import oracle
 import reverse_linear_recurrence_amd as rl
 from gpu_common import (ALGOS, DEFAULT_PARAMS, FORWARD, TOL, assert_close, params32,
                         random_inputs, rel_err, run_gpu, to_device)
+from test_gpu_parity import misaligned_flags
 
 pytestmark = pytest.mark.gpu
 
@@ -154,6 +155,16 @@ def test_window_parity_every_variant(algo, dtype):
                 assert rl.rlca_last_variant() == v
                 ref = run_oracle_chunk(algo, d, p, c)
                 check_window(got, ref, dtype, "%s v%d T=%d sparse=%s" % (algo, v, T, sparse))
+                k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16"
+                                                   else torch.float32, algo)
+                if T in (k * lanes, 2 * k * lanes) and not sparse:
+                    # the fixed-tile instances with flag rows off 4-byte alignment
+                    prev = rl.rlca_set_variant(v)
+                    try:
+                        got = run_gpu_chunk(algo, misaligned_flags(to_device(d)), p, c.cuda())
+                    finally:
+                        rl.rlca_set_variant(prev)
+                    check_window(got, ref, dtype, "%s v%d T=%d misaligned flags" % (algo, v, T))
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -293,6 +304,24 @@ def test_affine_scan_parity_every_variant(reverse, dtype):
                        cm.double().cpu().numpy())
                 check_window(got, ({"A": rA}, rco, rcm), dtype,
                              "affine rev=%s v%d T=%d p_reset=%g" % (reverse, v, T, p_reset))
+                k, lanes, _ = rl.rlca_variant_info(v, torch.bfloat16 if dtype == "bf16"
+                                                   else torch.float32, "affine")
+                if with_reset and T in (k * lanes, 2 * k * lanes):
+                    # reset flags off 4-byte alignment (the fixed-tile instances)
+                    buf = torch.zeros(rs.numel() + 1, dtype=rs.dtype, device="cuda")
+                    rs_mis = buf[1:].view(rs.shape)
+                    rs_mis.copy_(rs.cuda())
+                    prev = rl.rlca_set_variant(v)
+                    try:
+                        A, co, cm = rl.rlca_affine_scan(al.cuda(), be.cuda(), rs_mis,
+                                                        reverse=reverse, carry_in=c.cuda())
+                        torch.cuda.synchronize()
+                    finally:
+                        rl.rlca_set_variant(prev)
+                    got = ({"A": A.double().cpu().numpy()}, co.double().cpu().numpy(),
+                           cm.double().cpu().numpy())
+                    check_window(got, ({"A": rA}, rco, rcm), dtype,
+                                 "affine rev=%s v%d T=%d misaligned resets" % (reverse, v, T))
 
 
 def test_affine_scan_reproduces_gae_and_eligibility_calls():
