@@ -176,8 +176,9 @@ typedef uint32_t NU2 __attribute__((ext_vector_type(2), aligned(4)));
 typedef float NF4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // kNT: non-temporal loads, for streams that nothing reads again (flags, the
-// truncation bootstraps, Retrace's expectations, the policy tables).  The
-// rewards, values and log-ratios stay ordinary loads: the step-(t0+K)
+// truncation bootstraps, Retrace's expectations, the policy tables, and the
+// values where V_{t0+K} comes from the neighbouring lane).  The rewards,
+// log-ratios and otherwise the values stay ordinary loads: the step-(t0+K)
 // neighbour of values and log-ratios, and a missing flag array's stand-in
 // (the lane's own reward bytes), re-read lines they bring in, and measured
 // slower (TD(lambda) 16384x256 +5%) when those streams were non-temporal too.
@@ -519,8 +520,11 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
   }
   Ld<InT>::template vec<K>(rp.r + t0, q.r);
   if constexpr (U::values || U::q || U::affine) {
+    // Values are non-temporal where most lanes take V_{t0+K} from their
+    // neighbour, so that nothing re-reads their lines (GAE 4096x128: 3.355 ->
+    // 3.316 us per launch); elsewhere the V_{t0+K} loads re-read them.
     float vk[K];
-    Ld<InT>::template vec<K>(rp.v + t0, vk);
+    Ld<InT>::template vec<K, kVkNeighbour>(rp.v + t0, vk);
 #pragma unroll
     for (int j = 0; j < K; ++j) q.v[j] = vk[j];
     if constexpr (kVkNeighbour && U::values) {
