@@ -238,7 +238,7 @@ PROFILE_COMMANDS = (
     ("bench", "python3 bench.py {opts} > {d}/bench.json"),
     ("trace", "cd /tmp && export TMPDIR=/tmp && rocprofv3 --kernel-trace --stats "
               "--output-format csv -d {d}/trace -o t -- python3 <repo>/bench.py {opts} "
-              "--steps 500 --warmup 50 --cpu-seconds 0 --body-blocks 0 --spread-replays 0"),
+              "--steps 2000 --warmup 100 --cpu-seconds 0 --body-blocks 0 --spread-replays 0"),
     ("fetch", "cd /tmp && export TMPDIR=/tmp && RLCA_BENCH_META_DIR={d}/fetch rocprofv3 --pmc "
               "FETCH_SIZE --output-format csv -d {d}/fetch -o p -- python3 <repo>/bench.py "
               "{opts} --steps 20 --warmup 2 --cpu-seconds 0 --no-graph --rotate-mb 64 "
@@ -269,7 +269,8 @@ def summarize_profile(run_dir, out_md):
         key = b["config"]["workload"] + {
             "window (carry in; carry and carry map out)": "/window"}.get(
                 b["config"]["entry"], "/materialized" if b["config"]["entry"].startswith(
-                    "material") else "")
+                    "material") else "") + (
+            "/three-launch" if b["config"].get("split_form") == "three-launch" else "")
         traffic = json.load(open(TRAFFIC_FILE))[key]
 
     def rows_of(d, name):
@@ -364,11 +365,12 @@ def summarize_profile(run_dir, out_md):
         lines.append("| this call's speed relative to the streaming ceiling | %.1f%% |"
                      % (100 * rf["frac_of_stream_ceiling"]))
     lines += ["", "## rocprofv3 kernel trace (durations of single dispatches, ns)", "",
-              "The tracer takes each dispatch alone (start to start about 20 µs apart in "
-              "these runs), so a duration here is one launch's latency from the command "
-              "processor's start of the dispatch to its end-of-kernel signal, with no "
-              "overlap with the launches before and after it: for a short kernel it is "
-              "longer than its share of a back-to-back stream.", "",
+              "The timed region of the traced run is one HIP graph replay of 2000 steps. "
+              "The tracer takes each dispatch alone, so a duration here is one launch's "
+              "latency from the command processor's start of the dispatch to its "
+              "end-of-kernel signal, with no overlap with the launches before and after "
+              "it: for a short kernel it is longer than its share of a back-to-back "
+              "stream, and so are the copy and empty kernels of the same run.", "",
               "| kernel | dispatches | median | p10 | p90 |", "|---|---|---|---|---|"]
     for k, v in sorted(groups.items(), key=lambda kv: -len(kv[1])):
         lines.append("| %s | %d | %d | %d | %d |" % (k, len(v), q(v, 0.5), q(v, 0.1), q(v, 0.9)))
@@ -949,7 +951,8 @@ def main():
     value = env_steps / (ms_per_step * 1e-3)
     bytes_per_step = algorithmic_bytes(w, N, T, args.window)
     traffic_key = w.name + ("/window" if args.window else "") + (
-        "/materialized" if args.materialized else "")
+        "/materialized" if args.materialized else "") + (
+        "/three-launch" if split_form == "three-launch" else "")
     achieved = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
     # ---- HBM traffic from the committed counter runs, if they match this kernel
