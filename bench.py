@@ -711,6 +711,7 @@ def main():
     step(sets[0])
     torch.cuda.synchronize()
     launches_per_call = rl.rlca_last_launches()  # of the step's (last) library call
+    segments_per_row = rl.rlca_last_segments()
     win = dict(carry_in=carry_in, chunk=True) if args.window else {}
     if args.window and w.algo in ("returns",):
         win = dict(chunk=True)
@@ -944,9 +945,9 @@ def main():
     launches_per_step = launches_per_step_of(w) * launches_per_call
     split_form = None
     if args.split:
-        split_form = {1: "unsplit", 2: "chained", 3: "three-launch"}.get(launches_per_call)
-        if split_form != "three-launch":
-            split_segments = None if split_form == "chained" else 1
+        split_form = ("unsplit" if segments_per_row == 1 else
+                      "three-launch" if launches_per_call == 3 else "chained")
+        split_segments = segments_per_row
     env_steps = N * T
     value = env_steps / (ms_per_step * 1e-3)
     bytes_per_step = algorithmic_bytes(w, N, T, args.window)

@@ -657,19 +657,21 @@ typedef enum {
  * whole tiles of a tiling with whole wavefronts per row, with at most 64
  * segments per row and at least half as many as the three-launch form below
  * takes, the rows share one row stride, the workspace is 8-byte aligned and
- * holds 8 bytes plus 32 per segment: two launches, a one-thread
- * kernel advancing the workspace's epoch word (the call's tag), then one
- * workgroup per segment that scans its segment, publishes its carry map in
- * the workspace, composes the maps the segments before it in scan order have
- * published into the carry entering its own (from the row's end for reverse
- * recurrences, from its start for the forward mirrors, starting at
- * carry_in), publishes the map to the carry it hands on, and writes its
- * outputs.  The inputs are read once.  Published words carry the tag, so the
- * workspace needs no clearing, before the first call or between calls (also
- * between replays of a captured graph).  A workgroup waits only for
- * workgroups launched before it; its wait is bounded all the same, and a
- * carry not found within the bound (which the hardware's in-order workgroup
- * dispatch rules out) turns that segment's outputs into NaN.
+ * holds 8 bytes plus 32 per segment: one launch, one workgroup per segment
+ * that reads the workspace's epoch word (the previous call's tag; this
+ * call's is the next value, never 0), scans its segment, publishes its carry
+ * map in the workspace, composes the maps the segments before it in scan
+ * order have published into the carry entering its own (from the row's end
+ * for reverse recurrences, from its start for the forward mirrors, starting
+ * at carry_in), publishes the map to the carry it hands on, and writes its
+ * outputs; the launch's last workgroup then stores the call's tag in the
+ * epoch word, once every workgroup has read it.  The inputs are read once.
+ * Published words carry the tag, so the workspace needs no clearing, before
+ * the first call or between calls (also between replays of a captured
+ * graph).  A workgroup waits only for workgroups launched before it; its
+ * wait is bounded all the same, and a carry not found within the bound
+ * (which the hardware's in-order workgroup dispatch rules out) turns
+ * that segment's outputs into NaN.
  *
  * Three launches, otherwise: S = rlca_split_segments(N, T) segments of
  * T / S steps; the segments from carry 0, writing only their carry maps to
@@ -682,7 +684,8 @@ typedef enum {
  * three-launch form (for tests and comparisons); rlca_set_chained(1) restores
  * the default.  It returns the previous setting.  rlca_last_launches() is
  * the number of kernel launches the calling thread's last successful call
- * enqueued.  The plain entry points (rlca_gae, ...) never split: for the same
+ * enqueued, rlca_last_segments() the number of segments it cut each row into
+ * (1: not split; a chained call is one launch of more than one segment).  The plain entry points (rlca_gae, ...) never split: for the same
  * result on few long rows call the window form with NULL carries and a
  * workspace.
  *
@@ -740,6 +743,7 @@ int rlca_variant_info(int variant, int algo, int dtype, int *steps_per_lane, int
 int rlca_last_variant(void);
 int rlca_set_chained(int enable);
 int rlca_last_launches(void);
+int rlca_last_segments(void);
 
 #ifdef __cplusplus
 }

@@ -18,7 +18,8 @@ materialized doubling scan the pages compare against (rlca_X_materialized), and 
 tiling controls rlca_set_variant, rlca_num_variants,
 rlca_variant_info, rlca_last_variant, the split-call sizes
 rlca_split_segments and rlca_split_workspace_bytes (split_workspace allocates
-one), the split form control rlca_set_chained, rlca_last_launches, plus
+one), the split form control rlca_set_chained, rlca_last_launches,
+rlca_last_segments, plus
 rlca_version.
 """
 from ._binding import (  # noqa: F401
@@ -44,6 +45,7 @@ from ._binding import (  # noqa: F401
     rlca_gae_chunk_noalloc,
     rlca_gae_materialized,
     rlca_last_launches,
+    rlca_last_segments,
     rlca_last_variant,
     rlca_materialized_workspace_bytes,
     rlca_num_variants,

@@ -101,6 +101,7 @@ _SIGNATURES = {
     "rlca_last_variant": [],
     "rlca_set_chained": [_int],
     "rlca_last_launches": [],
+    "rlca_last_segments": [],
 }
 
 
@@ -988,3 +989,8 @@ def rlca_set_chained(enable):
 def rlca_last_launches():
     """Kernel launches the calling thread's last successful call enqueued."""
     return load_library().rlca_last_launches()
+
+
+def rlca_last_segments():
+    """Segments per row of the calling thread's last successful call (1: not split)."""
+    return load_library().rlca_last_segments()

@@ -65,6 +65,7 @@ thread_local int t_forced_variant = -1;
 thread_local int t_last_variant = -1;
 thread_local int t_chained = 1;      // rlca_set_chained
 thread_local int t_last_launches = 0;  // rlca_last_launches
+thread_local int t_last_segments = 0;  // rlca_last_segments
 
 
 int fail(int status, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
@@ -254,17 +255,6 @@ struct ChainPlan {
   unsigned long long *slots = nullptr;
 };
 
-// The chained split's epoch word advanced to its next value, never 0 (its low
-// half is the next call's tag; scan_kernels.hpp).
-__global__ void __launch_bounds__(64) chain_epoch(unsigned long long *epoch) {
-  if (threadIdx.x != 0) return;
-  uint32_t e = static_cast<uint32_t>(
-      __hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-  e = e + 1 != 0 ? e + 1 : 1;
-  __hip_atomic_store(epoch, static_cast<unsigned long long>(e), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // window: the instance with carry vectors (Args::cin, cout, cmap).
 // S > 1: segment view (window instances): each of the args.N rows is cut
 // into S segments of args.T steps, segment y taken by grid row y.
@@ -289,13 +279,7 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
   Args a = args;
   a.seg_count = S;
   if (chain != nullptr) {
-    // the workspace's epoch advances first: this call's tag
     a.chain = chain->slots;
-    void *ekargs[] = {&a.chain};
-    const hipError_t ee = hipLaunchKernel(reinterpret_cast<const void *>(&chain_epoch), dim3(1),
-                                          dim3(64), ekargs, 0, static_cast<hipStream_t>(stream));
-    if (ee != hipSuccess)
-      return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(ee));
     if (!(algo == kEligibility || algo == kCumsum || algo == kAffineFwd)) {
       // Reverse recurrences take the segments from the row's end: every row
       // pointer moves to the row's last segment (scan_kernels.hpp).
@@ -609,6 +593,7 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
     RLCA_TRY(check_aliasing(arrs, n));
     RLCA_TRY(launch_materialized(algo, dtype, a, static_cast<float *>(w.ws), stream));
     t_last_launches = 2 + static_cast<int>(std::ceil(std::log2(static_cast<double>(a.T))));
+    t_last_segments = 1;
     return RLCA_OK;
   }
   if (N == 0) return RLCA_OK;
@@ -637,7 +622,8 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
       Args ac = a;
       ac.T = a.T / cp.S;
       RLCA_TRY(launch(algo, dtype, ac, stream, true, static_cast<int>(cp.S), &cp));
-      t_last_launches = 2;
+      t_last_launches = 1;
+      t_last_segments = static_cast<int>(cp.S);
       return RLCA_OK;
     }
   }
@@ -659,6 +645,7 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   if (!split) {
     RLCA_TRY(launch(algo, dtype, a, stream, w.on));
     t_last_launches = 1;
+    t_last_segments = 1;
     return RLCA_OK;
   }
 
@@ -689,6 +676,7 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   a2.cmap = nullptr;
   RLCA_TRY(launch(algo, dtype, a2, stream, true, static_cast<int>(S)));
   t_last_launches = 3;
+  t_last_segments = S32;
   return RLCA_OK;
 }
 
@@ -715,6 +703,7 @@ int launch_probs(int algo, int dtype, const Args &args, const TableArgs &tables,
   if (e != hipSuccess) return fail(RLCA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   t_last_variant = -1;
   t_last_launches = 1;
+  t_last_segments = 1;
 #ifdef RLCA_TIMESTAMPS
   t_last_waves = static_cast<int64_t>(grid.x) * (kProbsBlock / 64);
   t_last_device = stamp_dev;
@@ -1492,8 +1481,9 @@ const char *rlca_last_error(void) { return t_last_error.c_str(); }
 
 // 0.5.0: T < 1 is an error; the split calls' workspace is an argument of the
 // window calls (no per-thread workspace).  0.5.1: split calls in one pass (the
-// chained form), rlca_set_chained, rlca_last_launches.
-int rlca_version(void) { return 510; }
+// chained form), rlca_set_chained, rlca_last_launches.  0.5.2: the chained
+// form in one launch (its last workgroup advances the epoch), rlca_last_segments.
+int rlca_version(void) { return 520; }
 
 int rlca_split_segments(int64_t num_envs, int64_t T) {
   if (num_envs < 0 || T < 1) {
@@ -1567,5 +1557,7 @@ int rlca_set_chained(int enable) {
 }
 
 int rlca_last_launches(void) { return t_last_launches; }
+
+int rlca_last_segments(void) { return t_last_segments; }
 
 }  // extern "C"

@@ -1086,14 +1086,17 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 // Each published value is one 64-bit word, written and read with relaxed
 // device-scope atomics (coherent across the chip's L2 caches): the value's
 // bits in the low half and the call's tag in the high half, so a word is
-// either wholly this call's or not yet written by it.  The tag is the
-// workspace's epoch word, which a one-thread kernel (chain_epoch, rlca.hip) advances
-// before every chained launch (also on every replay of a captured graph), so
-// that no word an earlier call left is taken for one of this call.  A
-// workgroup reads only the words of workgroups of its row with a smaller k,
-// which have smaller linear workgroup ids and were dispatched no later; the
-// poll is bounded all the same (kChainMaxPolls), and a carry not found by then
-// is NaN.
+// either wholly this call's or not yet written by it.  The workspace's epoch
+// word holds the previous call's tag, and this call's is the next value
+// (never 0): every workgroup reads the word once, before it publishes
+// anything, and the launch's last workgroup stores the new tag there once no
+// workgroup of this call can still read it (chain_advance; also on every
+// replay of a captured graph), so that no word an earlier call left is taken
+// for one of this call.  (A fresh workspace filled with any one 32-bit
+// pattern holds no word with the first call's tag.)  A workgroup reads only the words of
+// workgroups with smaller linear ids, which were dispatched no later; the
+// poll is bounded all the same (kChainMaxPolls), and a carry not found by
+// then is NaN.
 
 constexpr int kChainMaxPolls = 1 << 16;
 constexpr int kChainMaxSegments = 64;  // one wavefront composes the look-back
@@ -1227,6 +1230,34 @@ __device__ __forceinline__ bool chain_lookback(unsigned long long *slots, uint32
   ra = __int_as_float(0x7fc00000);
   rb = ra;
   return false;
+}
+
+// Wavefront 0 of the launch's last workgroup (row N-1, segment S-1; the
+// highest linear id), after its own outputs: waits until the last segment of
+// every row (lane r: row r < N <= 64) has published its words 2, 3 with this
+// call's tag, then stores that tag in the epoch word for the next call.  A
+// segment publishes words 2, 3 only after its look-back has found words of
+// every earlier segment of its row, directly or through the words 2, 3 of a
+// segment that had itself found them, so by then every workgroup of the call
+// has read the epoch word (each reads it before publishing anything).  Were
+// the wait to run out, the epoch advances all the same.
+__device__ __forceinline__ void chain_advance(unsigned long long *epoch, uint32_t tag, int N,
+                                              int S, int lane) {
+  const unsigned long long rows = N >= 64 ? ~0ull : (1ull << N) - 1;
+  for (int it = 0; it < kChainMaxPolls; ++it) {
+    bool done = true;
+    if (lane < N) {
+      const unsigned long long w = __hip_atomic_load(
+          epoch + 1 + (static_cast<int64_t>(lane) * S + (S - 1)) * 4 + 2, __ATOMIC_RELAXED,
+          __HIP_MEMORY_SCOPE_AGENT);
+      done = static_cast<uint32_t>(w >> 32) == tag;
+    }
+    if ((__ballot(done) & rows) == rows) break;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (lane == 0)
+    __hip_atomic_store(epoch, static_cast<unsigned long long>(tag), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Algo A, input type InT, K steps per lane, LPR lanes per row inside one
@@ -1427,8 +1458,9 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     const int k = static_cast<int>(blockIdx.y);
     const int S = late(p.seg_count);
     unsigned long long *slots = p.chain + 1 + row * 4 * static_cast<int64_t>(S);
-    const uint32_t tag = static_cast<uint32_t>(
+    const uint32_t epoch = static_cast<uint32_t>(
         __hip_atomic_load(p.chain, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const uint32_t tag = epoch + 1 != 0 ? epoch + 1 : 1;
     const float c_row = p.cin != nullptr ? p.cin[row] : 0.f;
     if (wave == 0) {
       // (ra, rb): the row's incoming carry -> the carry entering this segment
@@ -1463,6 +1495,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
       tile_emit<A, InT, K, WPR>(p, rp, xs, t0_of(kSecond), T - t0_of(kSecond), row_ok, lane,
                                 wave, c_next, ss);
     (void)c_next;
+    if (wave == 0 && k == S - 1 && row == N32 - 1) chain_advance(p.chain, tag, N32, S, lane);
   } else if constexpr (kTiles == 1) {
     one_tile();
   } else if constexpr (kTiles == 2) {
