@@ -913,6 +913,9 @@ def main():
     if (args.body_blocks > 0 and mode != "eager" and not args.materialized
             and os.path.exists(rl.TIMED_LIB_PATH)):
         with rl.use_library(rl.TIMED_LIB_PATH):
+            # the per-thread settings of the timed build: the same as the library's
+            rl.rlca_set_chained(not args.no_chain)
+            rl.rlca_set_variant(args.variant)
             for i in range(min(args.warmup, 50)):
                 step(sets[i % R])
             torch.cuda.synchronize()
