@@ -94,7 +94,7 @@ struct Args {
   float *cmap;
   int seg_count = 1;  // window instances: segments per row (gridDim.y; 1 unless split)
   // Chained instances (split calls in one pass, see chain_lookback): the
-  // workspace, its epoch word (this call's tag) followed by the segments'
+  // workspace, its epoch word (the previous call's tag) followed by the segments'
   // published carry maps, 4 words per (row, segment).
   unsigned long long *chain = nullptr;
 #ifdef RLCA_TIMESTAMPS

@@ -263,37 +263,6 @@ def test_many_segments_affine_scan(reverse, dtype, N, T, S):
                      "affine S=%d rev=%s %s p_reset=%g" % (S, reverse, form, p_reset))
 
 
-@pytest.mark.parametrize("fill", [0x00000000, 0x7FC00000, 0xFFFFFFFF, 0x3F800000])
-def test_chained_calls_advance_the_epoch_from_any_fill(form, fill):
-    # A fresh workspace filled with one 32-bit pattern (zeros, NaN, all ones,
-    # 1.0f): the first chained call's tag is the pattern plus one (0 skipped),
-    # each later call's the previous plus one, and every call on the same
-    # workspace gives the same results.
-    if form != "chained":
-        pytest.skip("the epoch word belongs to the chained form")
-    p = params32(DEFAULT_PARAMS)
-    N, T = 2, 65536
-    host = random_inputs("gae", N, T, 811, "f32", p_term=0.001, p_trunc=0.001, bootstrap=False)
-    dev = to_device(host)
-    ref = run_oracle("gae", host, p)
-    ws = rl.split_workspace(N, T)
-    ws.view(torch.int32).fill_(np.array(fill, dtype=np.uint32).view(np.int32).item())
-    expect = fill
-    first = None
-    for i in range(3):
-        expect = expect + 1 if expect + 1 < (1 << 32) else 1
-        got = plain_by_window("gae", dev, p, ws)
-        assert_split(ws, N, T, "f32", "gae")
-        epoch = ws[:2].view(torch.int32).cpu().numpy().view(np.uint32)
-        assert epoch[0] == expect and epoch[1] == 0, (i, hex(epoch[0]), hex(expect))
-        if first is None:
-            first = got
-            assert_close(got, ref, TOL["f32"], "gae/chained fill %#x" % fill)
-        else:
-            for k in first:
-                assert np.array_equal(got[k], first[k]), (i, k)
-
-
 def test_split_call_in_a_hip_graph_replays_like_eager_calls():
     # The three launches of a split call (both passes and the compose kernel)
     # captured once; every replay, with eager split calls and in-place input
