@@ -267,7 +267,7 @@ int launch(int algo, int dtype, const Args &args, void *stream, bool window = fa
                     : auto_variant(args.N * S, args.T, dtype == RLCA_BF16, algo == kVtrace);
   const Variant var = kVariants[v];
   dim3 grid, block;
-  const int waves = short_row_waves(var.WPR, var.LPR, window);
+  const int waves = short_row_waves(var.WPR, var.LPR, window, algo);
   if (var.WPR > 1) {
     grid = dim3(static_cast<unsigned>(args.N), static_cast<unsigned>(S));
   } else {

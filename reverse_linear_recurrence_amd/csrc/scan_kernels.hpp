@@ -51,15 +51,6 @@
 
 namespace rlca {
 
-enum Algo : int {
-  kReturns = 0, kGae = 1, kTdLambda = 2, kVtrace = 3, kRetrace = 4,
-  // forward-time mirrors: A_t = alpha_t + beta_t * A_{t-1}
-  kEligibility = 5, kCumsum = 6,
-  // the generic segmented scan over caller-given (alpha, beta), reverse and
-  // forward in time
-  kAffine = 7, kAffineFwd = 8
-};
-
 using bf16_t = uint16_t;  // raw bfloat16 bits
 
 // Everything a launch needs, passed by value in the kernel argument segment.
@@ -1275,20 +1266,20 @@ __device__ __forceinline__ void chain_advance(unsigned long long *epoch, uint32_
 // flag row the kernel reads (and, for a missing flag array, its stand-in,
 // the rewards row) is 4-byte aligned, so a lane's flag span is read as
 // exactly its K/4 dwords.
-// Workgroup: 64 * short_row_waves(WPR, LPR, kChunk) threads.
+// Workgroup: 64 * short_row_waves(WPR, LPR, kChunk, A) threads.
 // h0..h4, N32, T32, ldT, ldX: the preloaded hot arguments (see above); they
 // duplicate fields of p.  kChunk: window instance (carry vector in, carry and
 // carry map out).
 template <int A, typename InT, int K, int LPR, int WPR, bool kUniform, bool kChunk,
           int kTiles = 0, bool kAligned = false, bool kChain = false>
-__global__ void __launch_bounds__(64 * short_row_waves(WPR, LPR, kChunk))
+__global__ void __launch_bounds__(64 * short_row_waves(WPR, LPR, kChunk, A))
 scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, const void *h4,
             int N32, int T32, int ldT, int ldX, const Args p) {
   static_assert(WPR == 1 || LPR == 64, "multi-wavefront rows use whole wavefronts");
 #ifdef RLCA_TIMESTAMPS
   const WaveStamp stamp{p.stamps, wall_clock()};  // written at every return
 #endif
-  constexpr int kWaves = short_row_waves(WPR, LPR, kChunk);
+  constexpr int kWaves = short_row_waves(WPR, LPR, kChunk, A);
   constexpr int kGroup = WPR > 1 ? 64 * WPR : LPR;
   constexpr int kTile = kGroup * K;
 

@@ -6,6 +6,15 @@
 
 namespace rlca {
 
+enum Algo : int {
+  kReturns = 0, kGae = 1, kTdLambda = 2, kVtrace = 3, kRetrace = 4,
+  // forward-time mirrors: A_t = alpha_t + beta_t * A_{t-1}
+  kEligibility = 5, kCumsum = 6,
+  // the generic segmented scan over caller-given (alpha, beta), reverse and
+  // forward in time
+  kAffine = 7, kAffineFwd = 8
+};
+
 struct Variant {
   int LPR;    // lanes per row inside a wavefront (64 when WPR > 1)
   int WPR;    // wavefronts per row
@@ -13,8 +22,8 @@ struct Variant {
 };
 
 constexpr Variant kVariants[] = {
-    {16, 1, false},  // 0: tile    64 steps, 16 rows per 256-thread workgroup (window: 32 per 512)
-    {32, 1, false},  // 1: tile   128,  8 rows per workgroup (window: 16 per 512 threads)
+    {16, 1, false},  // 0: tile    64 steps, 16 rows per 256-thread workgroup (window, GAE: 32 per 512)
+    {32, 1, false},  // 1: tile   128,  8 rows per workgroup (window, GAE: 16 per 512 threads)
     {64, 1, false},  // 2: tile   256,  4 rows per workgroup
     {64, 4, false},  // 3: tile  1024,  1 row per 256-thread workgroup
     {64, 8, false},  // 4: tile  2048,  1 row per 512-thread workgroup
@@ -41,14 +50,16 @@ constexpr int steps_per_lane(const Variant &v, bool bf16, bool vtrace) {
 }
 
 // Wavefronts per workgroup: WPR for rows of whole wavefronts; otherwise 4,
-// or 8 for window instances whose rows take part of a wavefront (LPR < 64).
-// Larger workgroups write the per-row carry vectors in longer runs: the GAE
-// 4096x128 window call took 3.66 instead of 3.97 us, eligibility 2.91
-// instead of 2.99; with one row per wavefront they were slower (TD(lambda)
-// 16384x256 window 11.93 against 11.52 us), and the plain calls gained
-// nothing.
-constexpr int short_row_waves(int WPR, int LPR, bool window) {
-  return WPR > 1 ? WPR : (window && LPR < 64 ? 8 : 4);
+// or 8 for window instances and GAE when rows take part of a wavefront
+// (LPR < 64).  Larger workgroups write the per-row carry vectors in longer
+// runs: the GAE 4096x128 window call took 3.66 instead of 3.97 us,
+// eligibility 2.91 instead of 2.99; with one row per wavefront they were
+// slower (TD(lambda) 16384x256 window 11.93 against 11.52 us).  Of the plain
+// calls, GAE 4096x128 (two outputs) took 3.29 against 3.31 us with 8, while
+// the eligibility trace and the episodic sum at 4096x128 took 2.54 against
+// 2.52 us and keep 4 (2 wavefronts: 3.45, 2.53 us).
+constexpr int short_row_waves(int WPR, int LPR, bool window, int algo) {
+  return WPR > 1 ? WPR : (LPR < 64 && (window || algo == kGae) ? 8 : 4);
 }
 
 inline int64_t tile_steps(const Variant &v, bool bf16, bool vtrace) {
