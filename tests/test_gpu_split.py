@@ -23,7 +23,7 @@ import oracle
 import reverse_linear_recurrence_amd as rl
 from gpu_common import (ALGOS, DEFAULT_PARAMS, TOL, assert_close, params32, random_inputs,
                         run_oracle, to_device)
-from split_rules import takes_chained
+from split_rules import chain_segments, takes_chained, torch_dtype
 from test_gpu_window import (affine_inputs, check_window, run_gpu_chunk, run_oracle_chunk,
                              window_inputs)
 
@@ -50,11 +50,14 @@ def assert_split(ws, N, T, dtype="f32", algo="gae"):
     rl.rlca_set_chained(chained)
     if chained and takes_chained(N, T, dtype, "vtrace" if algo == "vtrace" else "gae"):
         assert rl.rlca_last_launches() == 1, "the call did not take the chained form"
+        assert rl.rlca_last_segments() == chain_segments(
+            N, T, torch_dtype(dtype), "vtrace" if algo == "vtrace" else "gae")
         epoch = ws[:2].view(torch.int32).cpu().numpy()
         assert epoch[0] != 0 and epoch[1] == 0, "the chained call did not advance its epoch"
     else:
         assert rl.rlca_last_launches() == 3, "the call did not take the three-launch form"
         S = rl.rlca_split_segments(N, T)
+        assert rl.rlca_last_segments() == S
         maps = ws[:2 * N * S].cpu().numpy()
         assert np.all(np.isfinite(maps)), "the call did not split"
 
@@ -117,6 +120,7 @@ def test_no_split_for_indivisible_rows_and_small_workspaces():
     ws = torch.full((1 << 12,), float("nan"), device="cuda")
     host = random_inputs("gae", 3, 32767, 92, "f32", p_term=0.001, p_trunc=0.001)
     got = plain_by_window("gae", to_device(host), p, ws)
+    assert rl.rlca_last_launches() == 1 and rl.rlca_last_segments() == 1
     assert torch.isnan(ws).all()
     assert_close(got, run_oracle("gae", host, p), TOL["f32"], "gae/odd T")
     # A call that splits, given a workspace one float short of the
