@@ -655,23 +655,22 @@ typedef enum {
  *
  * Chained (one pass).  Where the row length is a multiple of one or two
  * whole tiles of a tiling with whole wavefronts per row, with at most 64
- * segments per row and at least half as many as the three-launch form below
- * takes, the rows share one row stride, the workspace is 8-byte aligned and
- * holds 8 bytes plus 32 per segment: one launch, one workgroup per segment
- * that reads the workspace's epoch word (the previous call's tag; this
- * call's is the next value, never 0), scans its segment, publishes its carry
- * map in the workspace, composes the maps the segments before it in scan
- * order have published into the carry entering its own (from the row's end
- * for reverse recurrences, from its start for the forward mirrors, starting
- * at carry_in), publishes the map to the carry it hands on, and writes its
- * outputs; the launch's last workgroup then stores the call's tag in the
- * epoch word, once every workgroup has read it.  The inputs are read once.
- * Published words carry the tag, so the workspace needs no clearing, before
- * the first call or between calls (also between replays of a captured
- * graph).  A workgroup waits only for workgroups launched before it; its
- * wait is bounded all the same, and a carry not found within the bound
- * (which the hardware's in-order workgroup dispatch rules out) turns
- * that segment's outputs into NaN.
+ * segments per row, the rows share one row stride, the workspace is 8-byte
+ * aligned and holds 8 bytes plus 32 per segment: one launch, one workgroup
+ * per segment that reads the workspace's epoch word (the previous call's
+ * tag; this call's is the next value, never 0), scans its segment,
+ * publishes its carry map in the workspace, composes the maps the segments
+ * before it in scan order have published into the carry entering its own
+ * (from the row's end for reverse recurrences, from its start for the
+ * forward mirrors, starting at carry_in), publishes the map to the carry it
+ * hands on, and writes its outputs; the launch's last workgroup then stores
+ * the call's tag in the epoch word, once every workgroup has read it.  The
+ * inputs are read once.  Published words carry the tag, so the workspace
+ * needs no clearing, before the first call or between calls (also between
+ * replays of a captured graph).  A workgroup waits only for workgroups
+ * launched before it; its wait is bounded all the same, and a carry not
+ * found within the bound (which the hardware's in-order workgroup dispatch
+ * rules out) turns that segment's outputs into NaN.
  *
  * Three launches, otherwise: S = rlca_split_segments(N, T) segments of
  * T / S steps; the segments from carry 0, writing only their carry maps to

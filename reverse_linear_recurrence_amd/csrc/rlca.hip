@@ -599,16 +599,15 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   if (N == 0) return RLCA_OK;
   // The chained split (one pass) where it applies: a workspace large
   // enough and 8-byte aligned (its words are 64-bit), rows that share one
-  // stride, chaining not switched off for this thread, and at least half as
-  // many segments as the three-launch form would take.  (Where the chained
-  // form has fewer, its segments are long and few workgroups run them: bf16
-  // GAE 1x1048576, 64 against 256 segments, took 13.40 against 12.38 us;
-  // 2x524288, 64 against 128, 10.19 against 10.90 us.)
+  // stride, and chaining not switched off for this thread.  (It wins also
+  // where it has fewer segments than the three-launch form: bf16 GAE
+  // 1x1048576, 64 against 256 segments, took 11.77 against 12.37 us;
+  // 2x524288, 64 against 128, 8.47 against 10.76 us.)
   if (w.ws != nullptr && t_chained) {
     ChainPlan cp = chain_plan(N, a.T, dtype == RLCA_BF16, algo == kVtrace);
     const void *hot[5];
     int64_t ldx = 0;
-    if (cp.v >= 0 && 2 * cp.S >= split_count(N, a.T) &&
+    if (cp.v >= 0 &&
         reinterpret_cast<uintptr_t>(w.ws) % 8 == 0 &&
         w.ws_bytes >= chain_bytes(N, cp.S) && hot_streams(algo, a, false, hot, &ldx)) {
       const int64_t floats = chain_bytes(N, cp.S) / 4;

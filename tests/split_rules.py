@@ -36,7 +36,6 @@ def torch_dtype(dtype):
 
 def takes_chained(N, T, dtype, algo):
     """Whether a split window call (workspace large enough, 8-byte aligned,
-    rows sharing one stride, chaining on) takes the chained form: a chained
-    plan with at least half the three-launch form's segments."""
-    S = chain_segments(N, T, torch_dtype(dtype), algo)
-    return S > 0 and 2 * S >= rl.rlca_split_segments(N, T)
+    rows sharing one stride, chaining on) takes the chained form: whenever a
+    chained plan exists."""
+    return chain_segments(N, T, torch_dtype(dtype), algo) > 0
