@@ -654,7 +654,7 @@ typedef enum {
  * rounding order:
  *
  * Chained (one pass).  Where the row length is a multiple of one or two
- * whole tiles of a tiling with whole wavefronts per row, with at most 64
+ * whole tiles of a tiling with whole wavefronts per row, with at most 256
  * segments per row, the rows share one row stride, the workspace is 8-byte
  * aligned and holds 8 bytes plus 32 per segment: one launch, one workgroup
  * per segment that reads the workspace's epoch word (the previous call's

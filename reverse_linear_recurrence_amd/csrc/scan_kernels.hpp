@@ -1090,7 +1090,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 // then is NaN.
 
 constexpr int kChainMaxPolls = 1 << 16;
-constexpr int kChainMaxSegments = 64;  // one wavefront composes the look-back
+constexpr int kChainMaxSegments = 256;  // segments per row (look-back: a window of 64)
 
 // A lane's state after the carry-free scan of a whole tile (WPR > 1): its
 // inclusive map within the wavefront (a, b), the composite of the wavefronts
@@ -1173,46 +1173,53 @@ __device__ __forceinline__ void chain_put(unsigned long long *w, float v, uint32
 }
 
 // Wavefront 0 of workgroup (row, k > 0): the map from the row's incoming carry
-// to the carry entering segment k, (ra, rb), from the words of segments
-// 0 .. k-1 (slots: the row's first word).  Per segment j: words 0, 1 the
-// segment's own carry map, words 2, 3 the map from the row's incoming carry to
-// the carry it hands on (segment 0 publishes only these).  Lane j < k reads
-// segment j's four words; the latest j whose words 2, 3 are this call's, with
-// words 0, 1 of every later j < k, composes the answer in one scan.  Returns
-// false if the words were not all there within kChainMaxPolls polls.
+// to the carry entering segment k, (ra, rb), from the words of the (at most
+// 64) segments before it, k0 = max(0, k - 64) .. k-1 (slots: the row's first
+// word).  Per segment j: words 0, 1 the segment's own carry map, words 2, 3
+// the map from the row's incoming carry to the carry it hands on (segment 0
+// publishes only these).  Lane i reads segment k0 + i's four words; the
+// latest segment j0 of the window whose words 2, 3 are this call's, with
+// words 0, 1 of every later one, composes the answer in one scan.  Beyond 64
+// segments the window holds no segment 0: the words 2, 3 of one of its
+// segments must appear first, which each publishes once its own look-back
+// has ended (the segments below the window come no later in dispatch, so one
+// always does).  Returns false if the words were not all there within
+// kChainMaxPolls polls.
 __device__ __forceinline__ bool chain_lookback(unsigned long long *slots, uint32_t tag, int k,
                                                int lane, float &ra, float &rb) {
+  const int k0 = k > 64 ? k - 64 : 0;
+  const int n = k - k0;  // window length, 1 .. 64
   for (int it = 0; it < kChainMaxPolls; ++it) {
     unsigned long long w0 = 0, w1 = 0, w2 = 0, w3 = 0;
-    if (lane < k) {
-      unsigned long long *s = slots + 4 * lane;
+    if (lane < n) {
+      unsigned long long *s = slots + 4 * (k0 + lane);
       w2 = __hip_atomic_load(s + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       w3 = __hip_atomic_load(s + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       w0 = __hip_atomic_load(s + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       w1 = __hip_atomic_load(s + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     auto mine = [&](unsigned long long w) { return static_cast<uint32_t>(w >> 32) == tag; };
-    const bool inc = lane < k && mine(w2) && mine(w3);
-    const bool agg = lane < k && mine(w0) && mine(w1);
+    const bool inc = lane < n && mine(w2) && mine(w3);
+    const bool agg = lane < n && mine(w0) && mine(w1);
     const unsigned long long inc_mask = __ballot(inc);
     const unsigned long long agg_mask = __ballot(agg);
     if (inc_mask != 0) {
-      const int j0 = 63 - __clzll(static_cast<long long>(inc_mask));
-      // lanes j0+1 .. k-1 need their own maps
-      const unsigned long long below_k = k >= 64 ? ~0ull : (1ull << k) - 1;
-      const unsigned long long need = below_k & ~((2ull << j0) - 1);
+      const int j0 = 63 - __clzll(static_cast<long long>(inc_mask));  // window lane
+      // lanes j0+1 .. n-1 need their own maps
+      const unsigned long long below_n = n >= 64 ? ~0ull : (1ull << n) - 1;
+      const unsigned long long need = below_n & ~((2ull << j0) - 1);
       if ((agg_mask & need) == need) {
         float a = 0.f, b = 1.f;  // identity below j0
         if (lane == j0) {
           a = __uint_as_float(static_cast<uint32_t>(w2));
           b = __uint_as_float(static_cast<uint32_t>(w3));
-        } else if (lane > j0 && lane < k) {
+        } else if (lane > j0 && lane < n) {
           a = __uint_as_float(static_cast<uint32_t>(w0));
           b = __uint_as_float(static_cast<uint32_t>(w1));
         }
         group_scan<64>(a, b);  // lane i: f_i o ... o f_0
-        ra = readlane(a, k - 1);
-        rb = readlane(b, k - 1);
+        ra = readlane(a, n - 1);
+        rb = readlane(b, n - 1);
         return true;
       }
     }

@@ -8,7 +8,7 @@ import reverse_linear_recurrence_amd as rl
 def chain_segments(N, T, dtype, algo):
     """The chained split's segments per row (0: none), by its stated rule:
     tilings with whole wavefronts per row from the longest tile down, two
-    tiles per segment before one, at most 64 segments per row; the first
+    tiles per segment before one, at most 256 segments per row; the first
     choice with N * S >= 256, else the one with the most segments."""
     if N < 1 or N > 64 or T < 32768:
         return 0
@@ -22,7 +22,7 @@ def chain_segments(N, T, dtype, algo):
             if T % length:
                 continue
             S = T // length
-            if S < 2 or S > 64:
+            if S < 2 or S > 256:
                 continue
             best = max(best, S)
             if N * S >= 256:

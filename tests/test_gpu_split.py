@@ -5,15 +5,15 @@ A window call (rlca_X_chunk or the generic scan) given a workspace, on at most
 calls' split along T inside one library call (the operator of the rl-triton
 pages' Method 1 is associative, so the pieces join through their carry maps).
 Every test runs both forms: the chained one (one pass: each segment's
-workgroup publishes its carry map and composes the published maps of the
-segments before it; up to 64 segments per row) and the three-launch one (maps
-only, compose, outputs; rlca_set_chained(False)), which takes over where the
-chained one does not apply.  The results must match the oracle to the same
-tolerance as an unsplit call, for every algorithm, with episode boundaries
-that fall inside and exactly at segment borders and with carries that cross
-every border (no boundaries), from 8 segments per row up to the 256 that
-rlca_split_segments allows, where the composition walks its 64-segment chunks
-one after another.
+workgroup publishes its carry map and composes the published maps of the up
+to 64 segments before it; up to 256 segments per row) and the three-launch
+one (maps only, compose, outputs; rlca_set_chained(False)), which takes over
+where the chained one does not apply.  The results must match the oracle to
+the same tolerance as an unsplit call, for every algorithm, with episode
+boundaries that fall inside and exactly at segment borders and with carries
+that cross every border (no boundaries), from 8 segments per row up to 256:
+the three-launch composition then walks its 64-segment chunks one after
+another, and the chained look-back its 64-segment windows.
 """
 import numpy as np
 import pytest
