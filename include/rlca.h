@@ -683,9 +683,10 @@ typedef enum {
  * three-launch form (for tests and comparisons); rlca_set_chained(1) restores
  * the default.  It returns the previous setting.  rlca_last_launches() is
  * the number of kernel launches the calling thread's last successful call
- * enqueued, rlca_last_segments() the number of segments it cut each row into
- * (1: not split; a chained call is one launch of more than one segment).  The plain entry points (rlca_gae, ...) never split: for the same
- * result on few long rows call the window form with NULL carries and a
+ * enqueued, rlca_last_segments() the number of segments it cut each row
+ * into (1: not split; a chained call is one launch of more than one
+ * segment).  The plain entry points (rlca_gae, ...) never split: for the
+ * same result on few long rows call the window form with NULL carries and a
  * workspace.
  *
  * Workspace.  Device memory owned by the caller, 4-byte aligned (8 for the
