@@ -1084,10 +1084,10 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
 // workgroup of this call can still read it (chain_advance; also on every
 // replay of a captured graph), so that no word an earlier call left is taken
 // for one of this call.  (A fresh workspace filled with any one 32-bit
-// pattern holds no word with the first call's tag.)  A workgroup reads only the words of
-// workgroups with smaller linear ids, which were dispatched no later; the
-// poll is bounded all the same (kChainMaxPolls), and a carry not found by
-// then is NaN.
+// pattern holds no word with the first call's tag.)  A workgroup reads only
+// the words of workgroups with smaller linear ids, which were dispatched no
+// later; the poll is bounded all the same (kChainMaxPolls), and a carry not
+// found by then is NaN.
 
 constexpr int kChainMaxPolls = 1 << 16;
 constexpr int kChainMaxSegments = 256;  // segments per row (look-back: a window of 64)
