@@ -2,8 +2,9 @@
 the same seeded inputs.  Covers the five measured workloads at full size (in
 the tiling the benchmark uses), every tiling variant on ragged lengths, the
 exhaustive boundary enumeration, strided and misaligned rows, rows that
-start past element 2^31 of their buffer, empty inputs, and bitwise invariants (no leak across a boundary, window end, determinism,
-row permutation, power-of-two scaling)."""
+start past element 2^31 of their buffer, empty inputs, parameter extremes, and
+bitwise invariants (no leak across a boundary, window end, determinism, row
+permutation, power-of-two scaling)."""
 import itertools
 
 import numpy as np
@@ -533,3 +534,34 @@ def test_forward_no_leak_across_boundary_bitwise(algo, kind):
             b = run_gpu(algo, to_device(pert), p)
             for k in a:
                 assert np.array_equal(a[k][:, s + 1:], b[k][:, s + 1:]), (algo, kind, T, v, k)
+
+
+# Parameter extremes: no discount propagation (gamma 0), undiscounted sums
+# (gamma = lambda = 1), one-step TD (lambda 0), no clipping (infinite clips) and
+# tight clips with a policy-gradient clip above the others.  Every algorithm
+# uses the parameters it takes; the episodic sum takes none.
+INF = float("inf")
+EXTREMES = [
+    dict(gamma=0.0, lam=0.9),
+    dict(gamma=1.0, lam=1.0),
+    dict(gamma=1.0, lam=0.0),
+    dict(gamma=0.5, lam=1.0),
+    dict(gamma=0.99, lam=0.95, rho_bar=INF, c_bar=INF, pg_rho_bar=INF),
+    dict(gamma=0.99, lam=0.95, rho_bar=0.5, c_bar=0.1, pg_rho_bar=2.0),
+]
+
+
+EXTREME_CASES = [(algo, i) for algo in ALGOS for i in range(len(EXTREMES))
+                 if (algo != "cumsum" or i == 0) and (algo in ("vtrace", "retrace") or i < 4)]
+
+
+@pytest.mark.parametrize("T", [300, 2100])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo,which", EXTREME_CASES)
+def test_parameter_extremes(algo, which, dtype, T):
+    p = params32(dict(DEFAULT_PARAMS, **EXTREMES[which]))
+    N = 24
+    host = random_inputs(algo, N, T, 900 + which, dtype, p_term=0.01, p_trunc=0.005)
+    got = run_gpu(algo, to_device(host), p)
+    assert_close(got, run_oracle(algo, host, p), TOL[dtype],
+                 "%s/%s T=%d %s" % (algo, dtype, T, EXTREMES[which]))
