@@ -330,3 +330,32 @@ def test_policy_table_windows_chain_like_one_window(algo):
     for j, w in enumerate(whole):
         got = np.concatenate([pieces[lo][j] for lo in cuts[:-1]], axis=1)
         assert rel_err(got, w) <= TOL["f32"], (algo, j, rel_err(got, w))
+
+
+# Parameter extremes: gamma 0 and 1, lambda 0 and 1, no clipping (infinite
+# clips) and tight clips, on both tilings (rows of at most 256 steps, one
+# wavefront each; longer rows, 1024-step tiles).
+INF = float("inf")
+PROB_EXTREMES = [
+    dict(gamma=0.0, lam=0.9),
+    dict(gamma=1.0, lam=1.0),
+    dict(gamma=1.0, lam=0.0),
+    dict(gamma=0.99, lam=0.95, c_bar=INF, rho_bar=INF, pg_rho_bar=INF),
+    dict(gamma=0.99, lam=0.95, c_bar=0.1, rho_bar=0.5, pg_rho_bar=2.0),
+]
+
+
+@pytest.mark.parametrize("T", [200, 1100])
+@pytest.mark.parametrize("which", range(len(PROB_EXTREMES)))
+@pytest.mark.parametrize("algo", ["retrace_probs", "vtrace_probs"])
+def test_parameter_extremes(algo, which, T):
+    e = {k: fp32_param(v) if v != INF else v for k, v in PROB_EXTREMES[which].items()}
+    d = make_tables(algo, 6, T, 9, seed=700 + which, dtype="f32", p_term=0.01, p_trunc=0.005)
+    if algo == "retrace_probs":
+        e.pop("rho_bar", None)
+        e.pop("pg_rho_bar", None)
+        got, ref = gpu_retrace(d, **e), ref_retrace(d, **e)
+        assert np.all(np.isfinite(got)) and rel_err(got, ref) <= TOL["f32"], (which, T)
+    else:
+        for a, b in zip(gpu_vtrace(d, **e), ref_vtrace(d, **e)):
+            assert np.all(np.isfinite(a)) and rel_err(a, b) <= TOL["f32"], (which, T)

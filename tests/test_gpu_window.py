@@ -18,7 +18,7 @@ import oracle
 import reverse_linear_recurrence_amd as rl
 from gpu_common import (ALGOS, DEFAULT_PARAMS, FORWARD, TOL, assert_close, params32,
                         random_inputs, rel_err, run_gpu, to_device)
-from test_gpu_parity import misaligned_flags
+from test_gpu_parity import EXTREME_CASES, EXTREMES, misaligned_flags
 
 pytestmark = pytest.mark.gpu
 
@@ -396,3 +396,17 @@ def test_window_calls_in_a_hip_graph_chain_like_eager_calls():
         for got, want in zip((a_late, t_late, a_early, t_early), eager):
             assert torch.equal(got, want), "replay %d" % i
         assert torch.equal(c2, e_c2)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo,which", EXTREME_CASES)
+def test_window_parameter_extremes(algo, which, dtype):
+    # The window calls (carry in; carry and carry map out) at the parameter
+    # extremes of the plain calls' test, on rows with few boundaries so that
+    # the carries reach far into the window.
+    p = params32(dict(DEFAULT_PARAMS, **EXTREMES[which]))
+    N, T = 24, 700
+    d, c = window_inputs(algo, N, T, 950 + which, dtype, True)
+    got = run_gpu_chunk(algo, to_device(d), p, c.cuda())
+    check_window(got, run_oracle_chunk(algo, d, p, c), dtype,
+                 "%s/%s window %s" % (algo, dtype, EXTREMES[which]))
