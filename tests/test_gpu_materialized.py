@@ -16,6 +16,7 @@ import reverse_linear_recurrence_amd as rl
 from gpu_common import (DEFAULT_PARAMS, TOL, assert_close, params32, random_inputs, run_gpu,
                         run_oracle, to_device)
 from reverse_linear_recurrence_amd.synth import WORKLOADS, fp32_param, make_workload
+from test_gpu_parity import EXTREME_CASES, EXTREMES
 
 pytestmark = pytest.mark.gpu
 
@@ -107,3 +108,14 @@ def test_materialized_full_size_configs(name):
         got = run_mat(algo, dev, p)
         assert_close(got, run_oracle(algo, host, p), TOL[w.dtype],
                      "%s/%s materialized full size" % (name, algo))
+
+
+@pytest.mark.parametrize("algo,which", [c for c in EXTREME_CASES if c[0] in ALGOS5])
+def test_materialized_parameter_extremes(algo, which):
+    # The parameter extremes of the fused calls' test (gamma 0 and 1, lambda 0
+    # and 1, infinite and tight ratio clips) through the doubling passes.
+    p = params32(dict(DEFAULT_PARAMS, **EXTREMES[which]))
+    host = random_inputs(algo, 12, 700, 3300 + which, "f32", p_term=0.01, p_trunc=0.005)
+    got = run_mat(algo, to_device(host), p)
+    assert_close(got, run_oracle(algo, host, p), TOL["f32"],
+                 "%s materialized %s" % (algo, EXTREMES[which]))
