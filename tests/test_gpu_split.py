@@ -24,6 +24,7 @@ import reverse_linear_recurrence_amd as rl
 from gpu_common import (ALGOS, DEFAULT_PARAMS, TOL, assert_close, params32, random_inputs,
                         run_oracle, to_device)
 from split_rules import chain_segments, takes_chained, torch_dtype
+from test_gpu_parity import EXTREME_CASES, EXTREMES
 from test_gpu_window import (affine_inputs, check_window, run_gpu_chunk, run_oracle_chunk,
                              window_inputs)
 
@@ -302,3 +303,20 @@ def test_split_call_in_a_hip_graph_replays_like_eager_calls():
     ref = run_oracle("gae", {k: v.cpu() for k, v in dev.items()}, p)
     assert_close({"advantages": adv.double().cpu().numpy()}, {"advantages": ref["advantages"]},
                  TOL["f32"], "gae/split graph")
+
+
+@pytest.mark.parametrize("algo,which", [c for c in EXTREME_CASES
+                                        if c[0] in ("gae", "vtrace", "retrace", "eligibility")])
+def test_split_parameter_extremes(algo, which):
+    # Split calls (both forms) at the parameter extremes of the unsplit calls'
+    # test: undiscounted carries cross every segment border, gamma 0 cuts
+    # every map to its first step, and unclipped ratios grow the maps past 1.
+    p = params32(dict(DEFAULT_PARAMS, **EXTREMES[which]))
+    N, T = 3, 32768
+    host = random_inputs(algo, N, T, 4100 + which, "f32", p_term=0.0005, p_trunc=0.0005,
+                         bootstrap=False)
+    ws = workspace_for(N, T)
+    got = plain_by_window(algo, to_device(host), p, ws)
+    assert_split(ws, N, T, "f32", algo)
+    assert_close(got, run_oracle(algo, host, p), TOL["f32"],
+                 "%s/split %s" % (algo, EXTREMES[which]))
