@@ -565,3 +565,38 @@ def test_parameter_extremes(algo, which, dtype, T):
     got = run_gpu(algo, to_device(host), p)
     assert_close(got, run_oracle(algo, host, p), TOL[dtype],
                  "%s/%s T=%d %s" % (algo, dtype, T, EXTREMES[which]))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("algo", ALGOS)
+def test_non_finite_inputs(algo, dtype):
+    # NaN and infinite rewards: the scan evaluates each step as alpha + beta *
+    # A with beta = 0 at an episode boundary, and 0 * NaN is NaN, so a
+    # non-finite value reaches every step on the far side of it in scan order,
+    # across boundaries too, where the oracle's loop restarts the episode with
+    # a branch and stops it there.  Every output the oracle makes non-finite is
+    # non-finite here, the others lie in rows with a non-finite input on the
+    # near side of them, and every output finite on both sides matches.
+    p = params32(DEFAULT_PARAMS)
+    N, T = 16, 700
+    host = random_inputs(algo, N, T, 1200, dtype, p_term=0.01, p_trunc=0.005)
+    r = host["rewards"].clone()
+    bad = {3: 500, 7: 10, 11: 350, 12: 699}
+    for row, col in bad.items():
+        r[row, col] = float("inf") if row == 11 else float("nan")
+    host["rewards"] = r
+    got = run_gpu(algo, to_device(host), p)
+    ref = run_oracle(algo, host, p)
+    forward = algo in FORWARD
+    for k in ref:
+        gn, rn = ~np.isfinite(got[k]), ~np.isfinite(ref[k])
+        assert np.all(gn[rn]), (k, "the oracle's non-finite outputs must be non-finite")
+        for row, col in np.argwhere(gn & ~rn):
+            assert row in bad, (k, row, col)
+            # V-trace's pg reads the next step's vs: one step past the input
+            assert (col >= bad[row]) if forward else (col <= bad[row] + 1), (k, row, col)
+        fin = ~gn
+        assert rel_err(got[k][fin], ref[k][fin]) <= TOL[dtype], k
+    # the NaN of row 3 reaches every step on its far side, boundaries included
+    first = got[next(iter(ref))][3]
+    assert np.isnan(first[500:] if forward else first[:501]).all()
