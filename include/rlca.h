@@ -56,6 +56,12 @@
  *   synchronizes, and returns as soon as the work is enqueued on `stream`.
  * Nullable inputs.  terminated == NULL means no terminations; truncated ==
  *   NULL means no truncations (trunc_values is then ignored and may be NULL).
+ * Non-finite inputs.  Episode boundaries cut the recurrence with a zero
+ *   factor (A_t = alpha_t + 0 * A_{t+1}), and 0 * NaN = 0 * inf = NaN: a NaN
+ *   or infinite input the recurrence reaches makes every output on its far
+ *   side in scan order (earlier steps; later ones for the forward mirrors)
+ *   of its row non-finite, across episode boundaries too.  Finite values
+ *   never cross a boundary.
  * Errors.  Arguments are validated before anything is enqueued; on any
  *   non-OK status nothing is launched and no output is written (the one
  *   exception, a launch refused in the middle of a split call, is stated
