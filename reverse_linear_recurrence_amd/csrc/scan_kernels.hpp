@@ -726,7 +726,7 @@ __device__ __forceinline__ void load_edge(const Args &p, const RowPtrs<InT> &rp,
 
 // (alpha_t, beta_t) per step (Method 1 coefficients, Method 3 masks).  Steps
 // outside the row get the identity map (0, 1).
-template <int A, typename InT, int K, bool kEdge, bool kChunk>
+template <int A, typename InT, int K, bool kEdge, bool kChunk, bool kEarly = true>
 __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, const Args &p,
                                              float (&al)[K], float (&be)[K], float (&ratio)[K]) {
   const float gamma = late(p.gamma);
@@ -734,13 +734,14 @@ __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, cons
   const float gl = gamma * lam;
   const float rho_bar = A == kVtrace ? late(p.rho_bar) : 1.f;
   const float c_bar = A == kVtrace || A == kRetrace ? late(p.c_bar) : 1.f;
-  if constexpr (A == kReturns || A == kGae || A == kTdLambda || Uses<A>::prev_flags) {
+  if constexpr (kEarly && (A == kReturns || A == kGae || A == kTdLambda || Uses<A>::prev_flags)) {
     // The factors need the flags only, which arrive first: they are formed
     // before the wait for the tile's other loads, and the work left once the
     // data is in is shorter (GAE 4096x128 3.27 -> 3.23 us, TD(lambda)
     // 16384x256 10.07 -> 10.01 us, GAE bf16 256x16384 11.75 -> 11.46 us).
     // Forward mirrors: te, tr are the flags of step t-1, and a boundary there
-    // restarts at step t.
+    // restarts at step t.  (kEarly is off in the general instances' two-buffer
+    // tile loop at 8 steps per lane, whose registers would then spill.)
 #pragma unroll
     for (int j = 0; j < K; ++j) {
       const bool done = flag<K>(x.te, j) || flag<K>(x.tr, j);
@@ -773,7 +774,14 @@ __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, cons
     const bool done = te || tr;
     float a_j, b_j;
     ratio[j] = 0.f;
-    if constexpr (A == kVtrace) {
+    if constexpr (A == kReturns) {
+      a_j = (tr && !te) ? fmaf(gamma, tv_at<InT, K>(x, j), x.r[j]) : x.r[j];
+      b_j = done ? 0.f : gamma;
+    } else if constexpr (A == kGae || A == kTdLambda) {
+      const float nv = te ? 0.f : (tr ? tv_at<InT, K>(x, j) : x.v[j + 1]);
+      a_j = fmaf(gamma, nv, x.r[j]) - x.v[j];
+      b_j = done ? 0.f : gl;
+    } else if constexpr (A == kVtrace) {
       const float e = __expf(x.lr[j]);
       ratio[j] = e;
       const float nv = te ? 0.f : (tr ? tv_at<InT, K>(x, j) : x.v[j + 1]);
@@ -783,6 +791,10 @@ __device__ __forceinline__ void coefficients(const Tile<K> &x, int64_t lim, cons
       // te: reset flag of step t itself.
       a_j = x.r[j];
       b_j = te ? 0.f : x.v[j];
+    } else if constexpr (Uses<A>::forward) {
+      // te, tr: flags of step t-1; a boundary there restarts at step t.
+      a_j = x.r[j];
+      b_j = done ? 0.f : (A == kCumsum ? 1.f : gl);
     } else {  // kRetrace
       a_j = (te ? x.r[j] : fmaf(gamma, x.eq[j], x.r[j])) - x.v[j];
       const bool has_next = j + 1 < lim;  // step t+1 lies inside the row
@@ -1004,7 +1016,8 @@ __device__ __forceinline__ void tile_epilogue(const Args &p, const RowPtrs<InT> 
 // group's last lane in scan order, whose inclusive scan is that composite,
 // and after the row's last tile that lane writes the window results
 // (window_out) before the tile's outputs are stored.
-template <int A, typename InT, int K, int LPR, int WPR, bool kEdge, bool kChunk>
+template <int A, typename InT, int K, int LPR, int WPR, bool kEdge, bool kChunk,
+          bool kEarly = true>
 __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> &rp,
                                               const Tile<K> &x, int64_t t0, int64_t lim,
                                               bool row_ok, int64_t c, bool need_carry, int lane,
@@ -1015,7 +1028,7 @@ __device__ __forceinline__ float tile_compute(const Args &p, const RowPtrs<InT> 
   using U = Uses<A>;
 
   float al[K], be[K], ratio[K];
-  coefficients<A, InT, K, kEdge, kChunk>(x, lim, p, al, be, ratio);
+  coefficients<A, InT, K, kEdge, kChunk, kEarly>(x, lim, p, al, be, ratio);
 
   // Fold the lane's steps into one map of the incoming value: reverse,
   // (a, b) = f_{t0} o ... o f_{t0+K-1}; forward, f_{t0+K-1} o ... o f_{t0}.
@@ -1439,6 +1452,10 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
       static_cast<int64_t>(Uses<A>::forward ? g : kGroup - 1 - g) * K;
   [[maybe_unused]] auto t0_of = [&](int64_t c) { return c * kTile + lane_off; };
 
+  // The general instances' tile loop forms the factors early (coefficients)
+  // at 4 steps per lane only.
+  constexpr bool kLoopEarly = K == 4;
+
   // One whole tile: straight-line code.
   auto one_tile = [&]() {
     // GAE's aligned one-tile instances take V_{t0+K} from the neighbouring
@@ -1571,7 +1588,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
               finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
               const int64_t cn = c + 1 < nwhole ? c + 1 : c;
               issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
-              carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+              carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk, kLoopEarly>(
                   p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
                   s_agg, m, win, write_window);
             }
@@ -1580,7 +1597,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
               finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
               const int64_t cn = c + 1 < nwhole ? c + 1 : c;
               issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
-              carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+              carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk, kLoopEarly>(
                   p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c + 1 < ntiles, lane, wave, carry,
                   s_agg, m, win, write_window);
             }
@@ -1595,7 +1612,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
           if constexpr (kChunk) {
             if (nwhole == 0) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
           }
-          tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok, ntiles - 1,
+          tile_compute<A, InT, K, LPR, WPR, true, kChunk, kLoopEarly>(p, rp, x, te0, lim, row_ok, ntiles - 1,
                                                           false, lane, wave, carry, s_agg, m, win,
                                                           write_window);
         }
@@ -1617,7 +1634,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
         Tile<K> x;
         load_edge<A, InT, K>(p, rp, te0, lim, T, x);
         if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
-        carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk>(p, rp, x, te0, lim, row_ok,
+        carry = tile_compute<A, InT, K, LPR, WPR, true, kChunk, kLoopEarly>(p, rp, x, te0, lim, row_ok,
                                                                 ntiles - 1, c >= 0, lane, wave, carry,
                                                                 s_agg, m, win, write_window);
       } else {
@@ -1629,7 +1646,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
           finish_tile<A, InT, K>(p, rp, t0_of(c), buf_a);
           const int64_t cn = c > 0 ? c - 1 : 0;
           issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_b);
-          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk, kLoopEarly>(
               p, rp, buf_a, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
               win, write_window);
         }
@@ -1639,7 +1656,7 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
           finish_tile<A, InT, K>(p, rp, t0_of(c), buf_b);
           const int64_t cn = c > 0 ? c - 1 : 0;
           issue_tile<A, InT, K>(p, rp, t0_of(cn), T - t0_of(cn), buf_a);
-          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk>(
+          carry = tile_compute<A, InT, K, LPR, WPR, false, kChunk, kLoopEarly>(
               p, rp, buf_b, t0_of(c), T - t0_of(c), row_ok, c, c > 0, lane, wave, carry, s_agg, m,
               win, write_window);
         }
