@@ -936,8 +936,13 @@ __device__ __forceinline__ void tile_epilogue(const Args &p, const RowPtrs<InT> 
   // One write of the outputs.
   const bool has_o1 = U::two_outputs && late(p.o1) != nullptr;
   const int64_t orow = late_row<(WPR > 1)>(rp.src);
-  float *o0_row = p.o0 + orow * p.ld_o0 + rp.seg_off;
-  float *o1_row = p.o1 + orow * p.ld_o1 + rp.seg_off;
+  // Rows and strides are below 2^31: one 32 x 32 -> 64-bit multiply each.
+  auto row_off = [&](int64_t ld) {
+    return static_cast<int64_t>(static_cast<uint64_t>(static_cast<uint32_t>(orow)) *
+                                static_cast<uint32_t>(ld));
+  };
+  float *o0_row = p.o0 + row_off(p.ld_o0) + rp.seg_off;
+  float *o1_row = p.o1 + row_off(p.ld_o1) + rp.seg_off;
   // Window instances with no outputs (the first pass of a split call) write
   // only the carry vectors.
   const bool store = row_ok && (!kChunk || p.o0 != nullptr);
