@@ -463,10 +463,14 @@ __device__ __forceinline__ float tv_at(const Tile<K> &x, int j) {
 // kVkNeighbour (one-tile instances only, where a lane's span is its row's
 // last exactly when lim <= K): only a wavefront's first lane and a row's
 // last span load V_{t0+K}; the others take it from their neighbour
-// (vk_from_neighbour).
-template <int A, typename InT, int K, bool kAligned = false, bool kVkNeighbour = false>
+// (vk_from_neighbour).  mid runs between the flag loads and the others.
+struct NoMid {
+  __device__ void operator()() const {}
+};
+template <int A, typename InT, int K, bool kAligned = false, bool kVkNeighbour = false,
+          typename Mid = NoMid>
 __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp, int64_t t0,
-                                           int64_t lim, Tile<K> &q) {
+                                           int64_t lim, Tile<K> &q, Mid mid = Mid()) {
   using U = Uses<A>;
 #pragma unroll
   for (int j = 0; j < K; ++j) { q.v[j] = 0.f; q.lr[j] = 0.f; q.eq[j] = 0.f; q.tv[j] = 0.f; }
@@ -509,6 +513,7 @@ __device__ __forceinline__ void issue_tile(const Args &p, const RowPtrs<InT> &rp
     ld_flags_raw<K, kAligned>(trp, q.ftr);
     ld_flags_raw<K, kAligned>(rp.has_te ? rp.te + f0 : own, q.fte);
   }
+  mid();
   Ld<InT>::template vec<K>(rp.r + t0, q.r);
   if constexpr (U::values || U::q || U::affine) {
     // Values are non-temporal where most lanes take V_{t0+K} from their
@@ -1468,8 +1473,20 @@ scan_kernel(const void *h0, const void *h1, const void *h2, const void *h3, cons
     // TD(lambda) 16384x256 measured slower with the same two changes).
     constexpr bool kVk = kTiles == 1 && kAligned && A == kGae;
     Tile<K> x;
-    issue_tile<A, InT, K, kAligned, kVk>(p, rp, lane_off, T - lane_off, x);
-    if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+    if constexpr (kChunk && LPR < 64 && A == kGae) {
+      // GAE's window calls on rows that share a wavefront read the carry
+      // entering the window between the flags and the other loads, so that
+      // it is not the last load to arrive (GAE 4096x128 window call 3.45 ->
+      // 3.36 us; with one row per wavefront, TD(lambda) 16384x256, it cost
+      // 1.4 us, and the forward mirrors, whose window_in also reads flags,
+      // 0.25 us at 4096x128).
+      issue_tile<A, InT, K, kAligned, kVk>(p, rp, lane_off, T - lane_off, x, [&]() {
+        win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+      });
+    } else {
+      issue_tile<A, InT, K, kAligned, kVk>(p, rp, lane_off, T - lane_off, x);
+      if constexpr (kChunk) win = window_in<A, InT, (WPR > 1)>(p, rp, T, carry);
+    }
     pin_epilogue_args<kChunk>(p);
     finish_tile<A, InT, K>(p, rp, lane_off, x);
     if constexpr (kVk) vk_from_neighbour(x, T - lane_off <= K);
