@@ -652,17 +652,24 @@ typedef enum {
 /*
  * Split calls: few long rows (Method 1: the operator is associative, so a
  * row can be cut along time, its pieces scanned apart and joined by their
- * carry maps).  With one workgroup per row, a call on at most 64 rows of at
- * least 32768 steps leaves most compute units idle.  A window call of the
- * scan family (rlca_*_chunk of the seven algorithms and rlca_affine_scan; not
- * the policy-table calls) given a workspace then cuts every row into
- * segments, in one of two forms, and computes the same results up to
- * rounding order:
+ * carry maps).  With one workgroup per row, a call on fewer rows than the
+ * GPU's 256 compute units leaves some of them idle, and long rows keep the
+ * others busy for long.  A window call of the scan family (rlca_*_chunk of
+ * the seven algorithms and rlca_affine_scan; not the policy-table calls)
+ * given a workspace then cuts every row into segments, in one of two forms,
+ * and computes the same results up to rounding order:
  *
- * Chained (one pass).  Where the row length is a multiple of one or two
- * whole tiles of a tiling with whole wavefronts per row, with at most 256
- * segments per row, the rows share one row stride, the workspace is 8-byte
- * aligned and holds 8 bytes plus 32 per segment: one launch, one workgroup
+ * Chained (one pass), for N <= 224 rows of T >= 32768 steps.  The segment
+ * length L is one or two whole tiles of a tiling with whole wavefronts per
+ * row (rlca_variant_info: K x lanes per row steps per tile) with
+ * T % L == 0 and 2 <= T / L <= 256; of those, with S = T / L, the one with
+ * the least ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096, ties
+ * going to the longer, where r is 1 for the 16-wavefront two-tile segments
+ * of returns, GAE and TD(lambda) at K = 8, of V-trace, and of Retrace at
+ * K = 8 or on bf16 inputs (a compute unit holds one such workgroup at once),
+ * else 2.
+ * Where such an L exists, the rows share one row stride, the workspace is
+ * 8-byte aligned and holds 8 bytes plus 32 per segment: one launch, one workgroup
  * per segment that reads the workspace's epoch word (the previous call's
  * tag; this call's is the next value, never 0), scans its segment,
  * publishes its carry map in the workspace, composes the maps the segments
@@ -720,7 +727,7 @@ typedef enum {
  * rlca_split_workspace_bytes(num_envs, T) returns the workspace a split call
  * may use, the larger of the three-launch form's 12 * num_envs * S bytes (3
  * floats per segment) and the chained form's 8 bytes plus 32 per segment for
- * any input dtype, or 0 when neither splits; -1 as above.
+ * any input dtype and algorithm, or 0 when neither splits; -1 as above.
  */
 int rlca_split_segments(int64_t num_envs, int64_t T);
 int64_t rlca_split_workspace_bytes(int64_t num_envs, int64_t T);

@@ -413,7 +413,8 @@ int add_window(Arr *arrs, int n, const Window &w, int64_t N) {
 // ------------------------------------------------------------- split calls
 //
 // Few long rows leave most CUs idle with one workgroup per row.  A window call
-// (or generic scan) given a workspace, with at most kSplitMaxRows rows, then
+// (or generic scan) given a workspace takes the chained form below where it
+// applies; otherwise, with at most kSplitMaxRows rows, it
 // cuts every row into S segments of T / S steps and runs them as N * S rows of
 // the window kernels, the T-split of the window calls done inside the library:
 //   1. every segment from carry 0, writing only its carry map (a, b);
@@ -447,27 +448,74 @@ int64_t split_count(int64_t N, int64_t T) {
 // The chained form of a split call (one pass; see scan_kernels.hpp): the
 // segments are one or two whole tiles of a whole-wavefront tiling, at most
 // kChainMaxSegments per row, so that each workgroup's segment is scanned in
-// registers before its carry is known.  Tilings are tried from the longest
-// tile down, two tiles per segment before one; the first with
-// N * S >= kSplitTarget is taken, else the one with the most segments.  Same
-// rows as the three-launch split (at most kSplitMaxRows rows of at least
-// kSplitMinRow steps).
-ChainPlan chain_plan(int64_t N, int64_t T, bool bf16, bool vtrace) {
+// registers before its carry is known.  Taken for at most kChainMaxRows rows
+// of at least kSplitMinRow steps: with more rows, one workgroup per row
+// already keeps nearly every CU busy (bf16 GAE 240x32768: 24.8 us unsplit,
+// 25.1 chained; 208x49152: 34.9 unsplit, 31.7 chained; fp32 224x32768 still
+// 28.2 unsplit, 29.4 chained).
+//
+// Of the plans, the one with the least
+//   ceil(N * S / kSplitTarget) * L + ceil(N * S / (kSplitTarget * r)) * kChainSegmentCost,
+// ties going to the longer segment: the rounds of one segment per CU the
+// grid needs times a segment's L steps, plus a fixed cost per segment (its
+// start, its look-back and its drain) that a second workgroup resident on
+// the same CU hides; r = chain_residency (1 or 2).  Measured on GAE (us
+// per call):
+// bf16 16x262144 15.4 with two tiles of 8192 per segment, 15.4 with one;
+// 176x131072, 74.7 and 68.8; 160x32768, 22.0 and 18.5 (unsplit 22.2); fp32
+// 96x32768, 14.6 with two tiles of 4096, 14.1 with two of 2048 (the best),
+// 16.2 with one of 4096.  A rule on the segment count alone misses one way
+// or the other: the fewer, longer segments win where they fill the CUs
+// once, the shorter ones where the longer would leave a second round half
+// empty.
+constexpr int64_t kChainMaxRows = 224;
+constexpr int64_t kChainSegmentCost = 4096;
+
+// Workgroups of a chained instance that one CU holds at once, counted up to
+// 2.  Every chained instance holds at least two, but for the 16-wavefront
+// instances of two tiles that need more than 64 VGPRs (more than 4
+// wavefronts per SIMD): returns, GAE and TD(lambda) at 8 steps per lane
+// (70 to 87 VGPRs), V-trace (66), and Retrace at 8 steps per lane or on bf16
+// inputs (67 to 101).  These counts are those of the compiled code; a CPU
+// test checks the table against it.
+int chain_residency(int algo, const Variant &v, int tiles, bool bf16) {
+  if (v.WPR != 16 || tiles != 2) return 2;
+  const int K = steps_per_lane(v, bf16, algo == kVtrace);
+  switch (algo) {
+    case kReturns:
+    case kGae:
+    case kTdLambda:
+      return K == 8 ? 1 : 2;
+    case kVtrace:
+      return 1;
+    case kRetrace:
+      return K == 8 || bf16 ? 1 : 2;
+    default:
+      return 2;
+  }
+}
+
+ChainPlan chain_plan(int64_t N, int64_t T, bool bf16, int algo) {
   ChainPlan best;
-  if (N < 1 || N > kSplitMaxRows || T < kSplitMinRow) return best;
+  if (N < 1 || N > kChainMaxRows || T < kSplitMinRow) return best;
+  int64_t best_cost = 0, best_len = 0;
   for (int v = kNumVariants - 1; v >= 0; --v) {
     if (kVariants[v].WPR == 1) continue;
     for (int tiles = 2; tiles >= 1; --tiles) {
-      const int64_t len = tiles * tile_steps(kVariants[v], bf16, vtrace);
+      const int64_t len = tiles * tile_steps(kVariants[v], bf16, algo == kVtrace);
       if (T % len != 0) continue;
       const int64_t S = T / len;
       if (S < 2 || S > kChainMaxSegments) continue;
-      if (best.v < 0 || S > best.S) {
+      const int64_t r = chain_residency(algo, kVariants[v], tiles, bf16);
+      const int64_t cost = (N * S + kSplitTarget - 1) / kSplitTarget * len +
+                           (N * S + kSplitTarget * r - 1) / (kSplitTarget * r) * kChainSegmentCost;
+      if (best.v < 0 || cost < best_cost || (cost == best_cost && len > best_len)) {
         best.v = v;
         best.tiles = tiles;
         best.S = S;
+        best_cost = cost;
+        best_len = len;
       }
-      if (N * S >= kSplitTarget) return best;
     }
   }
   return best;
@@ -478,13 +526,13 @@ ChainPlan chain_plan(int64_t N, int64_t T, bool bf16, bool vtrace) {
 int64_t chain_bytes(int64_t N, int64_t S) { return 8 + 32 * N * S; }
 
 // The workspace a split call of N rows of T steps may use: the larger of the
-// three-launch split's and the chained form's for any input dtype.
+// three-launch split's and the chained form's for any input dtype and algorithm.
 int64_t split_workspace_bytes(int64_t N, int64_t T) {
   const int64_t S = split_count(N, T);
   int64_t need = S > 1 ? 12 * N * S : 0;
   for (int bf16 = 0; bf16 < 2; ++bf16) {
-    for (int vtrace = 0; vtrace < 2; ++vtrace) {
-      const ChainPlan c = chain_plan(N, T, bf16 != 0, vtrace != 0);
+    for (int algo = kReturns; algo <= kAffineFwd; ++algo) {
+      const ChainPlan c = chain_plan(N, T, bf16 != 0, algo);
       if (c.v >= 0 && chain_bytes(N, c.S) > need) need = chain_bytes(N, c.S);
     }
   }
@@ -604,7 +652,7 @@ int validate_and_launch(int algo, int dtype, int64_t N, Arr (&arrs)[kCap], int n
   // 1x1048576, 64 against 256 segments, took 11.77 against 12.37 us;
   // 2x524288, 64 against 128, 8.47 against 10.76 us.)
   if (w.ws != nullptr && t_chained) {
-    ChainPlan cp = chain_plan(N, a.T, dtype == RLCA_BF16, algo == kVtrace);
+    ChainPlan cp = chain_plan(N, a.T, dtype == RLCA_BF16, algo);
     const void *hot[5];
     int64_t ldx = 0;
     if (cp.v >= 0 &&

@@ -1288,8 +1288,9 @@ __device__ __forceinline__ bool chain_lookback(unsigned long long *slots, uint32
 
 // Wavefront 0 of the launch's last workgroup (row N-1, segment S-1; the
 // highest linear id), after its own outputs: waits until the last segment of
-// every row (lane r: row r < N <= 64) has published its words 2, 3 with this
-// call's tag, then stores that tag in the epoch word for the next call.  A
+// every row (lane i: rows i, i + 64, ... below N) has published its words 2,
+// 3 with this call's tag, then stores that tag in the epoch word for the next
+// call.  A
 // segment publishes words 2, 3 only after its look-back has found words of
 // every earlier segment of its row, directly or through the words 2, 3 of a
 // segment that had itself found them, so by then every workgroup of the call
@@ -1297,16 +1298,15 @@ __device__ __forceinline__ bool chain_lookback(unsigned long long *slots, uint32
 // the wait to run out, the epoch advances all the same.
 __device__ __forceinline__ void chain_advance(unsigned long long *epoch, uint32_t tag, int N,
                                               int S, int lane) {
-  const unsigned long long rows = N >= 64 ? ~0ull : (1ull << N) - 1;
   for (int it = 0; it < kChainMaxPolls; ++it) {
     bool done = true;
-    if (lane < N) {
+    for (int r = lane; r < N; r += 64) {
       const unsigned long long w = __hip_atomic_load(
-          epoch + 1 + (static_cast<int64_t>(lane) * S + (S - 1)) * 4 + 2, __ATOMIC_RELAXED,
+          epoch + 1 + (static_cast<int64_t>(r) * S + (S - 1)) * 4 + 2, __ATOMIC_RELAXED,
           __HIP_MEMORY_SCOPE_AGENT);
-      done = static_cast<uint32_t>(w >> 32) == tag;
+      done = done && static_cast<uint32_t>(w >> 32) == tag;
     }
-    if ((__ballot(done) & rows) == rows) break;
+    if (__ballot(!done) == 0) break;
     __builtin_amdgcn_s_sleep(2);
   }
   if (lane == 0)

@@ -5,29 +5,51 @@ import torch
 import reverse_linear_recurrence_amd as rl
 
 
+def residency(algo, k, waves, tiles, bf16):
+    """Workgroups of a chained instance one compute unit holds at once,
+    counted up to 2: 1 for the 16-wavefront two-tile segments of returns,
+    GAE and TD(lambda) at K = 8, of V-trace, and of Retrace at K = 8 or on
+    bf16 inputs; 2 otherwise."""
+    if waves != 16 or tiles != 2:
+        return 2
+    if algo in ("returns", "gae", "td_lambda"):
+        return 1 if k == 8 else 2
+    if algo == "vtrace":
+        return 1
+    if algo == "retrace":
+        return 1 if k == 8 or bf16 else 2
+    return 2
+
+
 def chain_segments(N, T, dtype, algo):
     """The chained split's segments per row (0: none), by its stated rule:
-    tilings with whole wavefronts per row from the longest tile down, two
-    tiles per segment before one, at most 256 segments per row; the first
-    choice with N * S >= 256, else the one with the most segments."""
-    if N < 1 or N > 64 or T < 32768:
+    at most 224 rows of at least 32768 steps; segments of L steps, one or two
+    whole tiles of a tiling with whole wavefronts per row, 2 to 256 per row;
+    of those, the one with the least
+    ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096 (r: residency),
+    ties going to the longer segment.  algo: a key of rl.ALGO_CODES (the
+    affine scan: "affine", either direction)."""
+    if N < 1 or N > 224 or T < 32768:
         return 0
-    best = 0
-    for v in reversed(range(rl.rlca_num_variants())):
+    bf16 = torch_dtype(dtype) == torch.bfloat16
+    best = None
+    for v in range(rl.rlca_num_variants()):
         k, lanes, waves = rl.rlca_variant_info(v, dtype, algo)
         if waves == 1:
             continue
-        for tiles in (2, 1):
+        for tiles in (1, 2):
             length = tiles * k * lanes
             if T % length:
                 continue
             S = T // length
             if S < 2 or S > 256:
                 continue
-            best = max(best, S)
-            if N * S >= 256:
-                return best
-    return best
+            r = residency(algo, k, waves, tiles, bf16)
+            cost = -(-N * S // 256) * length + -(-N * S // (256 * r)) * 4096
+            key = (cost, -length)
+            if best is None or key < best[0]:
+                best = (key, S)
+    return 0 if best is None else best[1]
 
 
 def torch_dtype(dtype):

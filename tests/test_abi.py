@@ -347,11 +347,12 @@ def test_split_segments_rule(lib):
         assert rl.rlca_split_segments(N, T) == S, (N, T)
         chained = max(8 + 32 * N * chain_segments(N, T, dt, algo) if chain_segments(
             N, T, dt, algo) else 0 for dt in (torch.float32, torch.bfloat16)
-            for algo in ("gae", "vtrace"))
+            for algo in rl.ALGO_CODES)
         assert rl.rlca_split_workspace_bytes(N, T) == max(12 * N * S if S > 1 else 0,
                                                           chained), (N, T)
     # the chained form's segments: one or two whole tiles of a whole-wavefront
-    # tiling, at most 256 per row
+    # tiling, at most 256 per row, the least
+    # ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096
     assert chain_segments(16, 262144, torch.float32, "gae") == 32  # 2 tiles of 4096
     assert chain_segments(16, 262144, torch.bfloat16, "gae") == 16  # 2 tiles of 8192
     assert chain_segments(64, 65536, torch.bfloat16, "gae") == 4
@@ -359,7 +360,11 @@ def test_split_segments_rule(lib):
     assert chain_segments(1, 1 << 20, torch.bfloat16, "gae") == 256  # 1 tile of 4096
     assert chain_segments(1, 1 << 21, torch.float32, "gae") == 256  # 2 tiles of 4096
     assert chain_segments(1, 1 << 22, torch.float32, "gae") == 0  # 512 segments at least
-    assert chain_segments(65, 65536, torch.float32, "gae") == 0
+    assert chain_segments(65, 65536, torch.float32, "gae") == 8  # 2 tiles of 4096 (tie: longer)
+    assert chain_segments(160, 32768, torch.bfloat16, "gae") == 4  # 1 tile of 8192 (tie)
+    assert chain_segments(224, 32768, torch.bfloat16, "gae") == 2  # 2 tiles of 8192
+    assert chain_segments(225, 65536, torch.bfloat16, "gae") == 0
+    assert chain_segments(100, 32768, torch.float32, "vtrace") == 4
     assert chain_segments(2, 32769, torch.float32, "gae") == 0
     # at most 64 rows split, into fewer than 512 segments in all
     assert max(N * rl.rlca_split_segments(N, 1 << 24) for N in range(1, 65)) < 512

@@ -26,14 +26,15 @@ def chained():
     rl.rlca_set_chained(prev)
 
 
+@pytest.mark.parametrize("N,T", [(2, 65536), (130, 32768)])
 @pytest.mark.parametrize("fill", [0x00000000, 0x7FC00000, 0xFFFFFFFF, 0x3F800000])
-def test_chained_calls_advance_the_epoch_from_any_fill(fill):
+def test_chained_calls_advance_the_epoch_from_any_fill(fill, N, T):
     # A fresh workspace filled with one 32-bit pattern (zeros, NaN, all ones,
     # 1.0f): the first chained call's tag is the pattern plus one (0 skipped),
     # each later call's the previous plus one, and every call on the same
-    # workspace gives the same results.
+    # workspace gives the same results.  130 rows: the last workgroup waits
+    # on the rows in chunks of 64 (two whole, one of 2).
     p = params32(DEFAULT_PARAMS)
-    N, T = 2, 65536
     host = random_inputs("gae", N, T, 811, "f32", p_term=0.001, p_trunc=0.001, bootstrap=False)
     dev = to_device(host)
     ref = run_oracle("gae", host, p)

@@ -1,14 +1,15 @@
 """Split calls (few long rows) on the GPU against the oracle.
 
-A window call (rlca_X_chunk or the generic scan) given a workspace, on at most
-64 rows of at least 32768 steps, cuts each row into segments: the window
-calls' split along T inside one library call (the operator of the rl-triton
-pages' Method 1 is associative, so the pieces join through their carry maps).
+A window call (rlca_X_chunk or the generic scan) given a workspace, on few
+rows of at least 32768 steps, cuts each row into segments: the window calls'
+split along T inside one library call (the operator of the rl-triton pages'
+Method 1 is associative, so the pieces join through their carry maps).
 Every test runs both forms: the chained one (one pass: each segment's
 workgroup publishes its carry map and composes the published maps of the up
-to 64 segments before it; up to 256 segments per row) and the three-launch
-one (maps only, compose, outputs; rlca_set_chained(False)), which takes over
-where the chained one does not apply.  The results must match the oracle to
+to 64 segments before it; up to 256 segments per row, up to 224 rows) and
+the three-launch one (maps only, compose, outputs; rlca_set_chained(False);
+up to 64 rows, beyond which the call runs unsplit), which takes over where
+the chained one does not apply.  The results must match the oracle to
 the same tolerance as an unsplit call, for every algorithm, with episode
 boundaries that fall inside and exactly at segment borders and with carries
 that cross every border (no boundaries), from 8 segments per row up to 256:
@@ -49,15 +50,17 @@ def assert_split(ws, N, T, dtype="f32", algo="gae"):
     """The call split, in the form the thread's setting and the shape select."""
     chained = rl.rlca_set_chained(True)
     rl.rlca_set_chained(chained)
-    if chained and takes_chained(N, T, dtype, "vtrace" if algo == "vtrace" else "gae"):
+    if chained and takes_chained(N, T, dtype, algo):
         assert rl.rlca_last_launches() == 1, "the call did not take the chained form"
-        assert rl.rlca_last_segments() == chain_segments(
-            N, T, torch_dtype(dtype), "vtrace" if algo == "vtrace" else "gae")
+        assert rl.rlca_last_segments() == chain_segments(N, T, torch_dtype(dtype), algo)
         epoch = ws[:2].view(torch.int32).cpu().numpy()
         assert epoch[0] != 0 and epoch[1] == 0, "the chained call did not advance its epoch"
     else:
-        assert rl.rlca_last_launches() == 3, "the call did not take the three-launch form"
         S = rl.rlca_split_segments(N, T)
+        if S == 1:  # more rows than the three-launch form takes: unsplit
+            assert rl.rlca_last_launches() == 1 and rl.rlca_last_segments() == 1
+            return
+        assert rl.rlca_last_launches() == 3, "the call did not take the three-launch form"
         assert rl.rlca_last_segments() == S
         maps = ws[:2 * N * S].cpu().numpy()
         assert np.all(np.isfinite(maps)), "the call did not split"
@@ -182,7 +185,7 @@ def test_split_affine_scan_matches_oracle(reverse):
         A, co, cm = rl.rlca_affine_scan(al.cuda(), be.cuda(), rs.cuda() if with_reset else None,
                                         reverse=reverse, carry_in=c.cuda(), workspace=ws)
         torch.cuda.synchronize()
-        assert_split(ws, N, T)
+        assert_split(ws, N, T, "f32", "affine")
         rA, rco, rcm = oracle.affine_scan(al, be, rs if with_reset else None, c,
                                           reverse=reverse)
         got = ({"A": A.double().cpu().numpy()}, co.double().cpu().numpy(),
@@ -240,6 +243,59 @@ def test_many_segments_match_oracle(algo, dtype, N, T, S):
                          "%s/%s S=%d window" % (algo, dtype, S))
 
 
+ROWS = [(algo, 100, 32768) for algo in ALGOS] + [(algo, 200, 32768)
+                                                  for algo in ("gae", "retrace", "eligibility")]
+
+
+@pytest.mark.parametrize("algo,N,T", ROWS)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_many_rows_match_oracle(algo, dtype, N, T):
+    # 65 to 224 rows: the chained form only (the three-launch form runs such
+    # calls unsplit); the launch's last workgroup waits on the rows in
+    # 64-row chunks before it advances the epoch.
+    S = chain_segments(N, T, torch_dtype(dtype), algo)
+    assert rl.rlca_split_segments(N, T) == 1 and S > 1
+    p = params32(dict(DEFAULT_PARAMS, gamma=0.999, lam=0.99))
+    for form in ("plain", "window"):
+        d, c = window_inputs(algo, N, T, 1701 + N, dtype, sparse=True)
+        d = border_boundaries(d, algo, T, S, 1801 + N)
+        ws = workspace_for(N, T)
+        print(algo, dtype, "N", N, "T", T, "S", S, form, flush=True)
+        if form == "plain":
+            got = plain_by_window(algo, to_device(d), p, ws)
+            assert_split(ws, N, T, dtype, algo)
+            assert_close(got, run_oracle(algo, d, p), TOL[dtype],
+                         "%s/%s %dx%d plain" % (algo, dtype, N, T))
+        else:
+            got = run_gpu_chunk(algo, to_device(d), p, c.cuda(), workspace=ws)
+            assert_split(ws, N, T, dtype, algo)
+            check_window(got, run_oracle_chunk(algo, d, p, c), dtype,
+                         "%s/%s %dx%d window" % (algo, dtype, N, T))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("reverse", [True, False])
+def test_many_rows_affine_scan(reverse, dtype):
+    N, T = 100, 32768
+    S = chain_segments(N, T, torch_dtype(dtype), "affine")
+    assert rl.rlca_split_segments(N, T) == 1 and S > 1
+    al, be, rs, c = affine_inputs(N, T, 1901, dtype, 0.0005)
+    L = T // S
+    rs = rs.clone()
+    rs[::2, torch.as_tensor(L * np.arange(1, S))] = 1  # resets at segment borders, even rows
+    ws = workspace_for(N, T)
+    print("affine", dtype, "reverse", reverse, "N", N, "S", S, flush=True)
+    A, co, cm = rl.rlca_affine_scan(al.cuda(), be.cuda(), rs.cuda(), reverse=reverse,
+                                    carry_in=c.cuda(), workspace=ws)
+    torch.cuda.synchronize()
+    assert_split(ws, N, T, dtype, "affine")
+    rA, rco, rcm = oracle.affine_scan(al, be, rs, c, reverse=reverse)
+    got = ({"A": A.double().cpu().numpy()}, co.double().cpu().numpy(),
+           cm.double().cpu().numpy())
+    check_window(got, ({"A": rA}, rco, rcm), dtype,
+                 "affine %dx%d rev=%s" % (N, T, reverse))
+
+
 @pytest.mark.parametrize("N,T,S", MANY)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("reverse", [True, False])
@@ -260,7 +316,7 @@ def test_many_segments_affine_scan(reverse, dtype, N, T, S):
                                         carry_in=None if cin is None else cin.cuda(),
                                         workspace=ws)
         torch.cuda.synchronize()
-        assert_split(ws, N, T, dtype)
+        assert_split(ws, N, T, dtype, "affine")
         rA, rco, rcm = oracle.affine_scan(al, be, rs if p_reset else None, cin, reverse=reverse)
         got = ({"A": A.double().cpu().numpy()}, co.double().cpu().numpy(),
                cm.double().cpu().numpy())
