@@ -62,6 +62,11 @@ def code_text(src):
     return " ".join(_COMMENT.sub(" ", src).split())
 
 
+# The traffic.json key of a workload names the split form a --split run took
+# (an unsplit call has none).
+SPLIT_KEY = {"chained": "/chained", "three-launch": "/three-launch"}
+
+
 def kernel_source_hash(family="scan"):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[family]:
@@ -269,8 +274,7 @@ def summarize_profile(run_dir, out_md):
         key = b["config"]["workload"] + {
             "window (carry in; carry and carry map out)": "/window"}.get(
                 b["config"]["entry"], "/materialized" if b["config"]["entry"].startswith(
-                    "material") else "") + (
-            "/three-launch" if b["config"].get("split_form") == "three-launch" else "")
+                    "material") else "") + SPLIT_KEY.get(b["config"].get("split_form"), "")
         traffic = json.load(open(TRAFFIC_FILE))[key]
 
     def rows_of(d, name):
@@ -955,8 +959,7 @@ def main():
     value = env_steps / (ms_per_step * 1e-3)
     bytes_per_step = algorithmic_bytes(w, N, T, args.window)
     traffic_key = w.name + ("/window" if args.window else "") + (
-        "/materialized" if args.materialized else "") + (
-        "/three-launch" if split_form == "three-launch" else "")
+        "/materialized" if args.materialized else "") + SPLIT_KEY.get(split_form, "")
     achieved = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
     # ---- HBM traffic from the committed counter runs, if they match this kernel

@@ -1300,11 +1300,15 @@ __device__ __forceinline__ void chain_advance(unsigned long long *epoch, uint32_
                                               int S, int lane) {
   for (int it = 0; it < kChainMaxPolls; ++it) {
     bool done = true;
-    for (int r = lane; r < N; r += 64) {
-      const unsigned long long w = __hip_atomic_load(
-          epoch + 1 + (static_cast<int64_t>(r) * S + (S - 1)) * 4 + 2, __ATOMIC_RELAXED,
-          __HIP_MEMORY_SCOPE_AGENT);
-      done = done && static_cast<uint32_t>(w >> 32) == tag;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {  // rows lane + 64 c, N <= 256
+      const int r = lane + 64 * c;
+      if (r < N) {
+        const unsigned long long w = __hip_atomic_load(
+            epoch + 1 + (static_cast<int64_t>(r) * S + (S - 1)) * 4 + 2, __ATOMIC_RELAXED,
+            __HIP_MEMORY_SCOPE_AGENT);
+        done = done && static_cast<uint32_t>(w >> 32) == tag;
+      }
     }
     if (__ballot(!done) == 0) break;
     __builtin_amdgcn_s_sleep(2);

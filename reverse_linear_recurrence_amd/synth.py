@@ -60,6 +60,10 @@ WORKLOADS = {
     # workload's rates.
     "gae_bf16_16x262144": Workload("gae_bf16_16x262144", "gae", 16, 262144, "bf16", 110,
                                    gamma=0.999, lam=0.97, p_term=0.0005, p_trunc=0.0002),
+    # Fewer rows than CUs but more than a few: 160 rows leave 96 CUs idle
+    # unsplit.
+    "gae_bf16_160x32768": Workload("gae_bf16_160x32768", "gae", 160, 32768, "bf16", 111,
+                                   gamma=0.999, lam=0.97, p_term=0.0005, p_trunc=0.0002),
     # Forward-time mirrors, at the GAE workload's shape and boundary rates.
     "eligibility_4096x128": Workload("eligibility_4096x128", "eligibility", 4096, 128, "f32",
                                      106, gamma=0.99, lam=0.95, p_term=0.005, p_trunc=0.002),
