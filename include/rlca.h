@@ -667,7 +667,8 @@ typedef enum {
  * going to the longer, where r is 1 for the 16-wavefront two-tile segments
  * of returns, GAE and TD(lambda) at K = 8, of V-trace, and of Retrace at
  * K = 8 or on bf16 inputs (a compute unit holds one such workgroup at once),
- * else 2.
+ * else 2.  On bf16 inputs (but for V-trace) the wide tilings (K = 8) are
+ * taken where any of them gives such an L, the others only otherwise.
  * Where such an L exists, the rows share one row stride, the workspace is
  * 8-byte aligned and holds 8 bytes plus 32 per segment: one launch, one workgroup
  * per segment that reads the workspace's epoch word (the previous call's

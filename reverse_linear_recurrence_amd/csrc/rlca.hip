@@ -499,25 +499,34 @@ ChainPlan chain_plan(int64_t N, int64_t T, bool bf16, int algo) {
   ChainPlan best;
   if (N < 1 || N > kChainMaxRows || T < kSplitMinRow) return best;
   int64_t best_cost = 0, best_len = 0;
-  for (int v = kNumVariants - 1; v >= 0; --v) {
-    if (kVariants[v].WPR == 1) continue;
-    for (int tiles = 2; tiles >= 1; --tiles) {
-      const int64_t len = tiles * tile_steps(kVariants[v], bf16, algo == kVtrace);
-      if (T % len != 0) continue;
-      const int64_t S = T / len;
-      if (S < 2 || S > kChainMaxSegments) continue;
-      const int64_t r = chain_residency(algo, kVariants[v], tiles, bf16);
-      const int64_t cost = (N * S + kSplitTarget - 1) / kSplitTarget * len +
-                           (N * S + kSplitTarget * r - 1) / (kSplitTarget * r) * kChainSegmentCost;
-      if (best.v < 0 || cost < best_cost || (cost == best_cost && len > best_len)) {
-        best.v = v;
-        best.tiles = tiles;
-        best.S = S;
-        best_cost = cost;
-        best_len = len;
+  auto consider = [&](bool wide_only) {
+    for (int v = kNumVariants - 1; v >= 0; --v) {
+      if (kVariants[v].WPR == 1 || (wide_only && !kVariants[v].wide)) continue;
+      for (int tiles = 2; tiles >= 1; --tiles) {
+        const int64_t len = tiles * tile_steps(kVariants[v], bf16, algo == kVtrace);
+        if (T % len != 0) continue;
+        const int64_t S = T / len;
+        if (S < 2 || S > kChainMaxSegments) continue;
+        const int64_t r = chain_residency(algo, kVariants[v], tiles, bf16);
+        const int64_t cost =
+            (N * S + kSplitTarget - 1) / kSplitTarget * len +
+            (N * S + kSplitTarget * r - 1) / (kSplitTarget * r) * kChainSegmentCost;
+        if (best.v < 0 || cost < best_cost || (cost == best_cost && len > best_len)) {
+          best.v = v;
+          best.tiles = tiles;
+          best.S = S;
+          best_cost = cost;
+          best_len = len;
+        }
       }
     }
-  }
+  };
+  // On bf16 inputs the wide tilings (8 steps per lane: one 16-byte vector
+  // per lane and array) come before the narrow ones (8-byte vectors), which
+  // serve only rows that no wide tile divides (bf16 GAE 4x65536: 5.2 us in
+  // 128 segments of 2048 steps, 5.7 us in 256 of 1024).
+  if (bf16 && algo != kVtrace) consider(true);
+  if (best.v < 0) consider(false);
   return best;
 }
 

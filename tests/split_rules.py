@@ -27,29 +27,38 @@ def chain_segments(N, T, dtype, algo):
     whole tiles of a tiling with whole wavefronts per row, 2 to 256 per row;
     of those, the one with the least
     ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096 (r: residency),
-    ties going to the longer segment.  algo: a key of rl.ALGO_CODES (the
-    affine scan: "affine", either direction)."""
+    ties going to the longer segment; on bf16 inputs (but for V-trace) the
+    tilings with K = 8 first, the others only where none of those fits.
+    algo: a key of rl.ALGO_CODES (the affine scan: "affine", either
+    direction)."""
     if N < 1 or N > 224 or T < 32768:
         return 0
     bf16 = torch_dtype(dtype) == torch.bfloat16
-    best = None
-    for v in range(rl.rlca_num_variants()):
-        k, lanes, waves = rl.rlca_variant_info(v, dtype, algo)
-        if waves == 1:
-            continue
-        for tiles in (1, 2):
-            length = tiles * k * lanes
-            if T % length:
+
+    def best_of(wide_only):
+        best = None
+        for v in range(rl.rlca_num_variants()):
+            k, lanes, waves = rl.rlca_variant_info(v, dtype, algo)
+            if waves == 1 or (wide_only and k != 8):
                 continue
-            S = T // length
-            if S < 2 or S > 256:
-                continue
-            r = residency(algo, k, waves, tiles, bf16)
-            cost = -(-N * S // 256) * length + -(-N * S // (256 * r)) * 4096
-            key = (cost, -length)
-            if best is None or key < best[0]:
-                best = (key, S)
-    return 0 if best is None else best[1]
+            for tiles in (1, 2):
+                length = tiles * k * lanes
+                if T % length:
+                    continue
+                S = T // length
+                if S < 2 or S > 256:
+                    continue
+                r = residency(algo, k, waves, tiles, bf16)
+                cost = -(-N * S // 256) * length + -(-N * S // (256 * r)) * 4096
+                key = (cost, -length)
+                if best is None or key < best[0]:
+                    best = (key, S)
+        return None if best is None else best[1]
+
+    S = best_of(True) if bf16 and algo != "vtrace" else None
+    if S is None:
+        S = best_of(False)
+    return S or 0
 
 
 def torch_dtype(dtype):

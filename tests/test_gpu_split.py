@@ -273,6 +273,28 @@ def test_many_rows_match_oracle(algo, dtype, N, T):
                          "%s/%s %dx%d window" % (algo, dtype, N, T))
 
 
+@pytest.mark.parametrize("N,chained", [(224, True), (225, False)])
+def test_row_limit_of_the_chained_split(N, chained):
+    # 224 rows split chained (the epoch advance waits on four 64-row
+    # chunks, the last one partial); from 225 rows the call runs unsplit
+    # and leaves the workspace untouched.
+    T = 32768
+    p = params32(DEFAULT_PARAMS)
+    host = random_inputs("gae", N, T, 2001 + N, "f32", p_term=0.001, p_trunc=0.001,
+                         bootstrap=False)
+    assert (rl.split_workspace(N, T) is not None) == chained
+    ws = workspace_for(N, T) if chained else torch.full((1 << 12,), float("nan"),
+                                                        device="cuda")
+    print("gae f32 N", N, "T", T, "chained", chained, flush=True)
+    got = plain_by_window("gae", to_device(host), p, ws)
+    if chained:
+        assert_split(ws, N, T, "f32", "gae")
+    else:
+        assert rl.rlca_last_launches() == 1 and rl.rlca_last_segments() == 1
+        assert torch.isnan(ws).all()
+    assert_close(got, run_oracle("gae", host, p), TOL["f32"], "gae/%d rows" % N)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("reverse", [True, False])
 def test_many_rows_affine_scan(reverse, dtype):
