@@ -1063,9 +1063,10 @@ int vtrace_probs_impl(int64_t num_envs, int64_t T, int64_t num_actions, int dtyp
 //
 // Callers that cannot allocate device memory (code under HIP graph capture,
 // tight serving loops, harnesses that forbid allocation) take a split call's
-// workspace from this file-scope array instead of passing one: 3 floats per
-// segment, room for every split the library makes (at most kSplitMaxRows
-// rows, fewer than 2 * kSplitTarget segments in all), 6 KB per device,
+// workspace from this file-scope array instead of passing one, and always
+// take the three-launch form: 3 floats per segment, room for every such
+// split (at most kSplitMaxRows rows, fewer than 2 * kSplitTarget segments in
+// all), 6 KB per device,
 // held until the process ends.  In host code `scratch` only names the
 // symbol; its address on a device comes from hipGetSymbolAddress, made once
 // per device (scratch_on) and used for every kernel argument.

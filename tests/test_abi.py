@@ -369,7 +369,7 @@ def test_split_segments_rule(lib):
     assert chain_segments(8, 32768, torch.bfloat16, "gae") == 16  # wide: 1 tile of 2048
     assert chain_segments(1, 33 * 1024, torch.bfloat16, "gae") == 33  # no wide tile divides T
     assert chain_segments(1, 33 * 1024, torch.bfloat16, "vtrace") == 33
-    # at most 64 rows split, into fewer than 512 segments in all
+    # the three-launch form: at most 64 rows, fewer than 512 segments in all
     assert max(N * rl.rlca_split_segments(N, 1 << 24) for N in range(1, 65)) < 512
     for bad in ((-1, 8), (4, 0)):
         with pytest.raises(ValueError):
