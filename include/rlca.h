@@ -659,8 +659,9 @@ typedef enum {
  * given a workspace then cuts every row into segments, in one of two forms,
  * and computes the same results up to rounding order:
  *
- * Chained (one pass), for N <= 224 rows of T >= 32768 steps.  The segment
- * length L is one or two whole tiles of a tiling with whole wavefronts per
+ * Chained (one pass), for N rows of T >= 8192 steps with N <= 224 and
+ * N <= T / 128 (16384 steps: up to 128 rows; 32768 and more: 224).  The
+ * segment length L is one or two whole tiles of a tiling with whole wavefronts per
  * row (rlca_variant_info: K x lanes per row steps per tile) with
  * T % L == 0 and 2 <= T / L <= 256; of those, with S = T / L, the one with
  * the least ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096, ties

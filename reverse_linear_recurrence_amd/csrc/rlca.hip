@@ -448,11 +448,14 @@ int64_t split_count(int64_t N, int64_t T) {
 // The chained form of a split call (one pass; see scan_kernels.hpp): the
 // segments are one or two whole tiles of a whole-wavefront tiling, at most
 // kChainMaxSegments per row, so that each workgroup's segment is scanned in
-// registers before its carry is known.  Taken for at most kChainMaxRows rows
-// of at least kSplitMinRow steps: with more rows, one workgroup per row
-// already keeps nearly every CU busy (bf16 GAE 240x32768: 24.8 us unsplit,
-// 25.1 chained; 208x49152: 34.9 unsplit, 31.7 chained; fp32 224x32768 still
-// 28.2 unsplit, 29.4 chained).
+// registers before its carry is known.  Taken for N rows of T steps with
+// T >= kChainMinRow and N <= min(kChainMaxRows, T / kChainStepsPerRow):
+// with more rows, one workgroup per row already keeps enough CUs busy for
+// long enough that the look-back, a latency the unsplit call does not have,
+// costs more than the split saves.  Measured on GAE (us per call, unsplit
+// against chained): bf16 240x32768 24.8 / 25.1, 208x49152 34.9 / 31.7, fp32
+// 224x32768 28.2 / 29.4; bf16 128x16384 8.9 / 7.9, 200x16384 10.2 / 12.9;
+// bf16 64x8192 5.5 / 4.9, 128x8192 5.9 / 6.4; bf16 32x4096 3.8 / 4.6.
 //
 // Of the plans, the one with the least
 //   ceil(N * S / kSplitTarget) * L + ceil(N * S / (kSplitTarget * r)) * kChainSegmentCost,
@@ -469,6 +472,8 @@ int64_t split_count(int64_t N, int64_t T) {
 // once, the shorter ones where the longer would leave a second round half
 // empty.
 constexpr int64_t kChainMaxRows = 224;
+constexpr int64_t kChainMinRow = 8192;
+constexpr int64_t kChainStepsPerRow = 128;
 constexpr int64_t kChainSegmentCost = 4096;
 
 // Workgroups of a chained instance that one CU holds at once, counted up to
@@ -497,7 +502,7 @@ int chain_residency(int algo, const Variant &v, int tiles, bool bf16) {
 
 ChainPlan chain_plan(int64_t N, int64_t T, bool bf16, int algo) {
   ChainPlan best;
-  if (N < 1 || N > kChainMaxRows || T < kSplitMinRow) return best;
+  if (N < 1 || N > kChainMaxRows || T < kChainMinRow || N * kChainStepsPerRow > T) return best;
   int64_t best_cost = 0, best_len = 0;
   auto consider = [&](bool wide_only) {
     for (int v = kNumVariants - 1; v >= 0; --v) {

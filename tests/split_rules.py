@@ -23,15 +23,15 @@ def residency(algo, k, waves, tiles, bf16):
 
 def chain_segments(N, T, dtype, algo):
     """The chained split's segments per row (0: none), by its stated rule:
-    at most 224 rows of at least 32768 steps; segments of L steps, one or two
-    whole tiles of a tiling with whole wavefronts per row, 2 to 256 per row;
-    of those, the one with the least
+    N rows of T >= 8192 steps with N <= 224 and N <= T / 128; segments of L
+    steps, one or two whole tiles of a tiling with whole wavefronts per row,
+    2 to 256 per row; of those, the one with the least
     ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096 (r: residency),
     ties going to the longer segment; on bf16 inputs (but for V-trace) the
     tilings with K = 8 first, the others only where none of those fits.
     algo: a key of rl.ALGO_CODES (the affine scan: "affine", either
     direction)."""
-    if N < 1 or N > 224 or T < 32768:
+    if N < 1 or N > 224 or T < 8192 or 128 * N > T:
         return 0
     bf16 = torch_dtype(dtype) == torch.bfloat16
 

@@ -364,6 +364,11 @@ def test_split_segments_rule(lib):
     assert chain_segments(160, 32768, torch.bfloat16, "gae") == 4  # 1 tile of 8192 (tie)
     assert chain_segments(224, 32768, torch.bfloat16, "gae") == 2  # 2 tiles of 8192
     assert chain_segments(225, 65536, torch.bfloat16, "gae") == 0
+    assert chain_segments(128, 16384, torch.bfloat16, "gae") == 2  # N <= T / 128
+    assert chain_segments(129, 16384, torch.bfloat16, "gae") == 0
+    assert chain_segments(16, 8192, torch.bfloat16, "gae") == 4  # 1 tile of 2048
+    assert chain_segments(64, 8192, torch.float32, "gae") == 4  # segments of 2048 steps
+    assert chain_segments(32, 4096, torch.bfloat16, "gae") == 0  # T < 8192
     assert chain_segments(100, 32768, torch.float32, "vtrace") == 4
     assert chain_segments(2, 32769, torch.float32, "gae") == 0
     assert chain_segments(8, 32768, torch.bfloat16, "gae") == 16  # wide: 1 tile of 2048

@@ -1,20 +1,21 @@
 """Split calls (few long rows) on the GPU against the oracle.
 
 A window call (rlca_X_chunk or the generic scan) given a workspace, on few
-rows of at least 32768 steps, cuts each row into segments: the window calls'
-split along T inside one library call (the operator of the rl-triton pages'
-Method 1 is associative, so the pieces join through their carry maps).
-Every test runs both forms: the chained one (one pass: each segment's
-workgroup publishes its carry map and composes the published maps of the up
-to 64 segments before it; up to 256 segments per row, up to 224 rows) and
-the three-launch one (maps only, compose, outputs; rlca_set_chained(False);
-up to 64 rows, beyond which the call runs unsplit), which takes over where
-the chained one does not apply.  The results must match the oracle to
-the same tolerance as an unsplit call, for every algorithm, with episode
-boundaries that fall inside and exactly at segment borders and with carries
-that cross every border (no boundaries), from 8 segments per row up to 256:
-the three-launch composition then walks its 64-segment chunks one after
-another, and the chained look-back its 64-segment windows.
+long rows, cuts each row into segments: the window calls' split along T
+inside one library call (the operator of the rl-triton pages' Method 1 is
+associative, so the pieces join through their carry maps).  Every test runs
+both forms: the chained one (one pass: each segment's workgroup publishes
+its carry map and composes the published maps of the up to 64 segments
+before it; up to 256 segments per row, up to 224 rows of at least 8192
+steps) and the three-launch one (maps only, compose, outputs;
+rlca_set_chained(False); up to 64 rows of at least 32768 steps, the call
+runs unsplit otherwise), which takes over where the chained one does not
+apply.  The results must match the oracle to the same tolerance as an
+unsplit call, for every algorithm, with episode boundaries that fall inside
+and exactly at segment borders and with carries that cross every border (no
+boundaries), from 8 segments per row up to 256: the three-launch
+composition then walks its 64-segment chunks one after another, and the
+chained look-back its 64-segment windows.
 """
 import numpy as np
 import pytest
@@ -243,16 +244,19 @@ def test_many_segments_match_oracle(algo, dtype, N, T, S):
                          "%s/%s S=%d window" % (algo, dtype, S))
 
 
-ROWS = [(algo, 100, 32768) for algo in ALGOS] + [(algo, 200, 32768)
-                                                  for algo in ("gae", "retrace", "eligibility")]
+ROWS = ([(algo, 100, 32768) for algo in ALGOS]
+        + [(algo, 200, 32768) for algo in ("gae", "retrace", "eligibility")]
+        + [(algo, 16, 16384) for algo in ("gae", "vtrace", "retrace", "eligibility")]
+        + [(algo, 64, 8192) for algo in ("gae", "td_lambda", "cumsum")])
 
 
 @pytest.mark.parametrize("algo,N,T", ROWS)
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_many_rows_match_oracle(algo, dtype, N, T):
-    # 65 to 224 rows: the chained form only (the three-launch form runs such
-    # calls unsplit); the launch's last workgroup waits on the rows in
-    # 64-row chunks before it advances the epoch.
+def test_chained_only_shapes_match_oracle(algo, dtype, N, T):
+    # Shapes only the chained form splits (the three-launch form runs them
+    # unsplit): 65 to 224 rows, where the launch's last workgroup waits on
+    # the rows in 64-row chunks before it advances the epoch, and rows of
+    # 8192 to 32767 steps.
     S = chain_segments(N, T, torch_dtype(dtype), algo)
     assert rl.rlca_split_segments(N, T) == 1 and S > 1
     p = params32(dict(DEFAULT_PARAMS, gamma=0.999, lam=0.99))
