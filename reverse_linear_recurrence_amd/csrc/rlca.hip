@@ -478,11 +478,12 @@ constexpr int64_t kChainSegmentCost = 4096;
 
 // Workgroups of a chained instance that one CU holds at once, counted up to
 // 2.  Every chained instance holds at least two, but for the 16-wavefront
-// instances of two tiles that need more than 64 VGPRs (more than 4
-// wavefronts per SIMD): returns, GAE and TD(lambda) at 8 steps per lane
-// (70 to 87 VGPRs), V-trace (66), and Retrace at 8 steps per lane or on bf16
-// inputs (67 to 101).  These counts are those of the compiled code; a CPU
-// test checks the table against it.
+// instances of two tiles that need more than 64 VGPRs (two such workgroups
+// put 8 wavefronts on each SIMD, which then has room for fewer): returns,
+// GAE and TD(lambda) at 8 steps per lane (70 to 87 VGPRs), V-trace (66),
+// and Retrace at 8 steps per lane or on bf16 inputs (67 to 101).  These
+// counts are those of the compiled code; a CPU test checks the table
+// against it.
 int chain_residency(int algo, const Variant &v, int tiles, bool bf16) {
   if (v.WPR != 16 || tiles != 2) return 2;
   const int K = steps_per_lane(v, bf16, algo == kVtrace);
