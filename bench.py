@@ -62,9 +62,13 @@ def code_text(src):
     return " ".join(_COMMENT.sub(" ", src).split())
 
 
-# The traffic.json key of a workload names the split form a --split run took
-# (an unsplit call has none).
-SPLIT_KEY = {"chained": "/chained", "three-launch": "/three-launch"}
+def traffic_key(workload, window=False, materialized=False, split_form=None):
+    """The profiles/traffic.json key of a timed configuration: the workload,
+    then the entry point (window or materialized form) and the form a split
+    call took (chained or three-launch; an unsplit call adds nothing)."""
+    return workload + ("/window" if window else "") + (
+        "/materialized" if materialized else "") + {
+        "chained": "/chained", "three-launch": "/three-launch"}.get(split_form, "")
 
 
 def kernel_source_hash(family="scan"):
@@ -271,10 +275,9 @@ def summarize_profile(run_dir, out_md):
     traffic = None
     if os.path.isdir(os.path.join(run_dir, "fetch")):
         summarize_pmc(os.path.join(run_dir, "fetch"), os.path.join(run_dir, "write"))
-        key = b["config"]["workload"] + {
-            "window (carry in; carry and carry map out)": "/window"}.get(
-                b["config"]["entry"], "/materialized" if b["config"]["entry"].startswith(
-                    "material") else "") + SPLIT_KEY.get(b["config"].get("split_form"), "")
+        entry = b["config"]["entry"]
+        key = traffic_key(b["config"]["workload"], entry.startswith("window"),
+                          entry.startswith("material"), b["config"].get("split_form"))
         traffic = json.load(open(TRAFFIC_FILE))[key]
 
     def rows_of(d, name):
@@ -958,8 +961,7 @@ def main():
     env_steps = N * T
     value = env_steps / (ms_per_step * 1e-3)
     bytes_per_step = algorithmic_bytes(w, N, T, args.window)
-    traffic_key = w.name + ("/window" if args.window else "") + (
-        "/materialized" if args.materialized else "") + SPLIT_KEY.get(split_form, "")
+    tkey = traffic_key(w.name, args.window, args.materialized, split_form)
     achieved = bytes_per_step / (ms_per_step * 1e-3) / 1e9
 
     # ---- HBM traffic from the committed counter runs, if they match this kernel
@@ -967,8 +969,8 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             tr = json.load(f)
-        entry = tr.get(traffic_key)
-        if entry and entry.get("kernel_source_hash") == kernel_source_hash(kernel_family(traffic_key)):
+        entry = tr.get(tkey)
+        if entry and entry.get("kernel_source_hash") == kernel_source_hash(kernel_family(tkey)):
             traffic = entry.get("bytes_per_launch")
 
     # ---- CPU oracle on the host cores (bounded sample of the same workload):
@@ -1026,7 +1028,7 @@ def main():
     if meta_dir:
         os.makedirs(meta_dir, exist_ok=True)
         with open(os.path.join(meta_dir, "bench_meta.json"), "w") as f:
-            json.dump({"workload": traffic_key, "algorithmic_bytes_per_launch":
+            json.dump({"workload": tkey, "algorithmic_bytes_per_launch":
                        bytes_per_step / launches_per_step,
                        "copy_bytes_per_launch": copy["bytes_per_launch"] if copy else None}, f)
 

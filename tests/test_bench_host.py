@@ -8,6 +8,7 @@ column, done flags and the outputs, each read or written once): GAE 18 B per
 fp32 env-step plus the bootstrap column, and so on.
 """
 import hashlib
+import json
 import os
 import subprocess
 import sys
@@ -94,3 +95,19 @@ def test_host_threads_is_bounded_by_affinity_and_one_gpu_share():
 def test_cpu_model_is_text_or_absent():
     m = bench.cpu_model()
     assert m is None or (isinstance(m, str) and m)
+
+
+def test_traffic_keys_name_the_entry_point_and_split_form():
+    assert bench.traffic_key("gae_4096x128") == "gae_4096x128"
+    assert bench.traffic_key("gae_4096x128", window=True) == "gae_4096x128/window"
+    assert bench.traffic_key("gae_4096x128", materialized=True) == "gae_4096x128/materialized"
+    w = "gae_bf16_16x262144"
+    assert bench.traffic_key(w, split_form="chained") == w + "/chained"
+    assert bench.traffic_key(w, split_form="three-launch") == w + "/three-launch"
+    assert bench.traffic_key(w, split_form="unsplit") == w
+    # every committed entry is keyed by a workload and a form bench.py produces
+    forms = {bench.traffic_key(n, win, mat, s) for n in WORKLOADS for win in (False, True)
+             for mat in (False, True) for s in (None, "chained", "three-launch")}
+    with open(bench.TRAFFIC_FILE) as f:
+        committed = json.load(f)
+    assert committed and set(committed) <= forms
