@@ -350,13 +350,15 @@ def test_many_segments_affine_scan(reverse, dtype, N, T, S):
                      "affine S=%d rev=%s %s p_reset=%g" % (S, reverse, form, p_reset))
 
 
-def test_split_call_in_a_hip_graph_replays_like_eager_calls():
-    # The three launches of a split call (both passes and the compose kernel)
-    # captured once; every replay, with eager split calls and in-place input
+@pytest.mark.parametrize("N,T,S3", [(4, 65536, 16), (100, 32768, 1)])
+def test_split_call_in_a_hip_graph_replays_like_eager_calls(N, T, S3):
+    # A split call captured once (chained: one launch that advances the
+    # workspace's epoch on every replay; three launches: both passes and the
+    # compose kernel; 100 rows: chained only, unsplit in the three-launch
+    # setting); every replay, with eager split calls and in-place input
     # updates in between, equals the eager call bitwise.
     p = params32(DEFAULT_PARAMS)
-    N, T = 4, 65536
-    assert rl.rlca_split_segments(N, T) == 16
+    assert rl.rlca_split_segments(N, T) == S3
     dev = to_device(random_inputs("gae", N, T, 701, "f32", p_term=0.0005, p_trunc=0.0005))
     args = (dev["rewards"], dev["values"], dev["terminated"], dev["truncated"],
             dev["trunc_values"])
