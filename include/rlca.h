@@ -661,19 +661,20 @@ typedef enum {
  *
  * Chained (one pass), for N rows of T >= 8192 steps with N <= 224 and
  * N <= T / 128 (16384 steps: up to 128 rows; 32768 and more: 224).  The
- * segment length L is one or two whole tiles of a tiling with whole wavefronts per
- * row (rlca_variant_info: K x lanes per row steps per tile) with
- * T % L == 0 and 2 <= T / L <= 256; of those, with S = T / L, the one with
- * the least ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096, ties
- * going to the longer, where r is 1 for the 16-wavefront two-tile segments
- * of returns, GAE and TD(lambda) at K = 8, of V-trace, and of Retrace at
- * K = 8 or on bf16 inputs (a compute unit holds one such workgroup at once),
- * else 2.  On bf16 inputs (but for V-trace) the wide tilings (K = 8) are
- * taken where any of them gives such an L, the others only otherwise.
- * Where such an L exists, the rows share one row stride, the workspace is
- * 8-byte aligned and holds 8 bytes plus 32 per segment: one launch, one workgroup
- * per segment that reads the workspace's epoch word (the previous call's
- * tag; this call's is the next value, never 0), scans its segment,
+ * segment length L is one or two whole tiles of a tiling with whole
+ * wavefronts per row (rlca_variant_info: K x lanes per row steps per tile)
+ * with T % L == 0 and 2 <= T / L <= 256; of those, with S = T / L, the one
+ * with the least ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096,
+ * ties going to the longer, where r is 1 for the 16-wavefront two-tile
+ * segments of returns, GAE and TD(lambda) at K = 8, of V-trace, and of
+ * Retrace at K = 8 or on bf16 inputs (a compute unit holds one such
+ * workgroup at once), else 2.  On bf16 inputs (but for V-trace) the wide
+ * tilings (K = 8) are taken where any of them gives such an L, the others
+ * only otherwise.  Where such an L exists, the rows share one row stride,
+ * and the workspace is 8-byte aligned and holds 8 bytes plus 32 per
+ * segment: one launch, one workgroup per segment that reads the
+ * workspace's epoch word (the previous call's tag; this call's is the next
+ * value, never 0), scans its segment,
  * publishes its carry map in the workspace, composes the maps the segments
  * before it in scan order have published into the carry entering its own
  * (from the row's end for reverse recurrences, from its start for the
@@ -687,8 +688,8 @@ typedef enum {
  * found within the bound (which the hardware's in-order workgroup dispatch
  * rules out) turns that segment's outputs into NaN.
  *
- * Three launches, otherwise: S = rlca_split_segments(N, T) segments of
- * T / S steps; the segments from carry 0, writing only their carry maps to
+ * Three launches, otherwise, on at most 64 rows of at least 32768 steps:
+ * S = rlca_split_segments(N, T) segments of T / S steps; the segments from carry 0, writing only their carry maps to
  * the workspace; a small kernel composing, per row, the carry that enters
  * each segment from carry_in, and the row's carry_out and carry_map; and the
  * segments again from those carries, writing the outputs.  It reads the
