@@ -664,10 +664,10 @@ typedef enum {
  * segment length L is one or two whole tiles of a tiling with whole
  * wavefronts per row (rlca_variant_info: K x lanes per row steps per tile)
  * with T % L == 0 and 2 <= T / L <= 256; of those, with S = T / L, the one
- * with the least ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096,
- * ties going to the longer, where r is 1 for the 16-wavefront two-tile
- * segments of returns, GAE and TD(lambda) at K = 8, of V-trace, and of
- * Retrace at K = 8 or on bf16 inputs (a compute unit holds one such
+ * with the least ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096
+ * + 32 * S, ties going to the longer, where r is 1 for the 16-wavefront
+ * two-tile segments of returns, GAE and TD(lambda) at K = 8, of V-trace,
+ * and of Retrace at K = 8 or on bf16 inputs (a compute unit holds one such
  * workgroup at once), else 2.  On bf16 inputs (but for V-trace) the wide
  * tilings (K = 8) are taken where any of them gives such an L, the others
  * only otherwise.  Where such an L exists, the rows share one row stride,

@@ -458,12 +458,15 @@ int64_t split_count(int64_t N, int64_t T) {
 // bf16 64x8192 5.5 / 4.9, 128x8192 5.9 / 6.4; bf16 32x4096 3.8 / 4.6.
 //
 // Of the plans, the one with the least
-//   ceil(N * S / kSplitTarget) * L + ceil(N * S / (kSplitTarget * r)) * kChainSegmentCost,
+//   ceil(N * S / kSplitTarget) * L + ceil(N * S / (kSplitTarget * r)) * kChainSegmentCost
+//     + S * kChainLinkCost,
 // ties going to the longer segment: the rounds of one segment per CU the
 // grid needs times a segment's L steps, plus a fixed cost per segment (its
 // start, its look-back and its drain) that a second workgroup resident on
-// the same CU hides; r = chain_residency (1 or 2).  Measured on GAE (us
-// per call):
+// the same CU hides (r = chain_residency, 1 or 2), plus a cost per link of
+// a row's chain (beyond 64 segments a look-back waits for a segment 64
+// back to have found its own carry; bf16 2x262144: 7.2 us in 128 segments
+// of 2048 steps per row, 6.3 in 64 of 4096).  Measured on GAE (us per call):
 // bf16 16x262144 15.4 with two tiles of 8192 per segment, 15.4 with one;
 // 176x131072, 74.7 and 68.8; 160x32768, 22.0 and 18.5 (unsplit 22.2); fp32
 // 96x32768, 14.6 with two tiles of 4096, 14.1 with two of 2048 (the best),
@@ -475,6 +478,7 @@ constexpr int64_t kChainMaxRows = 224;
 constexpr int64_t kChainMinRow = 8192;
 constexpr int64_t kChainStepsPerRow = 128;
 constexpr int64_t kChainSegmentCost = 4096;
+constexpr int64_t kChainLinkCost = 32;
 
 // Workgroups of a chained instance that one CU holds at once, counted up to
 // 2.  Every chained instance holds at least two, but for the 16-wavefront
@@ -516,7 +520,8 @@ ChainPlan chain_plan(int64_t N, int64_t T, bool bf16, int algo) {
         const int64_t r = chain_residency(algo, kVariants[v], tiles, bf16);
         const int64_t cost =
             (N * S + kSplitTarget - 1) / kSplitTarget * len +
-            (N * S + kSplitTarget * r - 1) / (kSplitTarget * r) * kChainSegmentCost;
+            (N * S + kSplitTarget * r - 1) / (kSplitTarget * r) * kChainSegmentCost +
+            S * kChainLinkCost;
         if (best.v < 0 || cost < best_cost || (cost == best_cost && len > best_len)) {
           best.v = v;
           best.tiles = tiles;

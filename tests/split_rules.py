@@ -26,7 +26,8 @@ def chain_segments(N, T, dtype, algo):
     N rows of T >= 8192 steps with N <= 224 and N <= T / 128; segments of L
     steps, one or two whole tiles of a tiling with whole wavefronts per row,
     2 to 256 per row; of those, the one with the least
-    ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096 (r: residency),
+    ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096 + 32 * S (r:
+    residency),
     ties going to the longer segment; on bf16 inputs (but for V-trace) the
     tilings with K = 8 first, the others only where none of those fits.
     algo: a key of rl.ALGO_CODES (the affine scan: "affine", either
@@ -49,7 +50,7 @@ def chain_segments(N, T, dtype, algo):
                 if S < 2 or S > 256:
                     continue
                 r = residency(algo, k, waves, tiles, bf16)
-                cost = -(-N * S // 256) * length + -(-N * S // (256 * r)) * 4096
+                cost = -(-N * S // 256) * length + -(-N * S // (256 * r)) * 4096 + 32 * S
                 key = (cost, -length)
                 if best is None or key < best[0]:
                     best = (key, S)

@@ -352,12 +352,12 @@ def test_split_segments_rule(lib):
                                                           chained), (N, T)
     # the chained form's segments: one or two whole tiles of a whole-wavefront
     # tiling, at most 256 per row, the least
-    # ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096
+    # ceil(N * S / 256) * L + ceil(N * S / (256 * r)) * 4096 + 32 * S
     assert chain_segments(16, 262144, torch.float32, "gae") == 32  # 2 tiles of 4096
     assert chain_segments(16, 262144, torch.bfloat16, "gae") == 16  # 2 tiles of 8192
     assert chain_segments(64, 65536, torch.bfloat16, "gae") == 4
     assert chain_segments(1, 32768, torch.float32, "gae") == 32  # 1 tile of 1024
-    assert chain_segments(1, 1 << 20, torch.bfloat16, "gae") == 256  # 1 tile of 4096
+    assert chain_segments(1, 1 << 20, torch.bfloat16, "gae") == 128  # 1 tile of 8192
     assert chain_segments(1, 1 << 21, torch.float32, "gae") == 256  # 2 tiles of 4096
     assert chain_segments(1, 1 << 22, torch.float32, "gae") == 0  # 512 segments at least
     assert chain_segments(65, 65536, torch.float32, "gae") == 8  # 2 tiles of 4096 (tie: longer)
